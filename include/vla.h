@@ -1,0 +1,233 @@
+/* vla.h -- C ABI of the KV-cached GQA decoder library for MI355X (gfx950).
+ *
+ * One model instance ("handle") holds seeded random-init weights, a block-paged
+ * KV cache with a LIFO free-list, per-frame mean keys, and scratch buffers, all
+ * on the HIP device that was current when the handle was created. Every entry
+ * point is plain C: plain pointers and sizes, no C++ or framework types.
+ *
+ * What is computed (cited by page title and section):
+ *  - the pre-norm decoder layer: RMSNorm, fused q/k/v projection, RoPE at
+ *    absolute positions, grouped-query attention over the cached keys,
+ *    output projection, RMSNorm, gated (SwiGLU) feed-forward
+ *    ("Can an LLM Forget the Right Things?", section 6; "CSR: Infinite-Horizon
+ *    Real-Time Policies with Massive Cached State Representations", III-A);
+ *  - chunked prefill reading KV blocks in place, causal inside the chunk, RoPE
+ *    positions continuing after the cached tokens
+ *    ("Rebuilding Kshipra Around Memory", section 4);
+ *  - a block arena reserved once with a LIFO free-list
+ *    ("Rebuilding Kshipra Around Memory", section 1);
+ *  - redundant-frame scoring by cosine similarity and eviction of the most
+ *    redundant frame ("Can an LLM Forget the Right Things?", section 5).
+ *
+ * Conventions shared by all calls
+ *  - Return value: VLA_OK (0) or a negative vla_status. On failure the model
+ *    state is unchanged and vla_last_error() holds a message (thread local).
+ *    No C++ exception crosses this boundary.
+ *  - Streams: `stream` is a hipStream_t passed as void* (NULL = the null
+ *    stream). Work is enqueued on it; pointers passed in must stay valid until
+ *    the stream has reached the call.
+ *  - Synchronisation: a call that returns a host value computed on the device
+ *    (out_next_token, the frame id of an eviction, out_score) synchronises the
+ *    stream before returning. Everything else is asynchronous.
+ *  - Ownership: the library owns everything it allocates (weights, KV pool,
+ *    tables, scratch); the caller owns every pointer it passes.
+ *  - Threading: a handle must not be used from two threads at once.
+ *  - Frames: a frame is the unit of eviction: one vla_prefill_chunk or one
+ *    vla_kv_append_raw call. It starts on a fresh block. Decode tokens form a
+ *    non-evictable tail that also starts on a fresh block.
+ *  - Positions: a monotonic counter; every appended token takes the next
+ *    position and positions are never reused (vla_kv_rollback excepted).
+ */
+#ifndef VLA_H
+#define VLA_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct vla_model vla_model;   /* opaque, owned by the library */
+typedef struct vla_pool vla_pool;     /* opaque host-only block pool */
+
+typedef enum {
+  VLA_OK = 0,
+  VLA_E_INVALID = -1,          /* bad configuration, shape or argument */
+  VLA_E_NO_BLOCKS = -2,        /* not enough free KV blocks (or frame slots) */
+  VLA_E_NOTHING_TO_EVICT = -3, /* fewer than two evictable frames */
+  VLA_E_HIP = -4,              /* a HIP runtime call failed */
+  VLA_E_STATE = -5             /* call not valid in the current state */
+} vla_status;
+
+typedef enum { VLA_F32 = 0, VLA_BF16 = 1, VLA_INT4_G128 = 2 } vla_dtype;
+typedef enum { VLA_SWIGLU = 0 } vla_ffn_kind;
+
+/* Model configuration. Sizes in elements. */
+typedef struct {
+  int32_t n_layers;     /* decoder layers L */
+  int32_t hidden;       /* H, multiple of 64 */
+  int32_t n_heads;      /* query heads Hq */
+  int32_t n_kv_heads;   /* KV heads Hkv, divides Hq (Hq/Hkv = group size g) */
+  int32_t head_dim;     /* d, even, <= 256, multiple of 16 */
+  int32_t ffn;          /* F, multiple of 16 */
+  int32_t vocab;        /* V */
+  float rms_eps;        /* RMSNorm epsilon */
+  double rope_theta;    /* RoPE base */
+  int32_t wdtype;       /* projection weights: VLA_F32 or VLA_BF16 */
+  int32_t act_dtype;    /* activations and KV cache: VLA_F32 or VLA_BF16 (= wdtype) */
+  int32_t ffn_kind;     /* VLA_SWIGLU */
+  int32_t block_tokens; /* tokens per KV block: 16 */
+  int32_t num_blocks;   /* KV budget in blocks (the fixed memory budget) */
+  int32_t max_frames;   /* most frames resident at once (mean-key table rows) */
+  int32_t max_chunk;    /* longest prefill chunk / raw append, in tokens */
+  uint64_t seed;        /* weight seed */
+  double init_std;      /* weights ~ N(0, init_std^2); norm weights are 1 */
+} vla_config;
+
+/* Create a model: validates cfg, allocates weights, KV pool (K and V, each
+ * [L][num_blocks][Hkv][block_tokens][d] in act_dtype), the mean-key table
+ * ([L][max_frames][Hkv*d] fp64) and scratch on the current device, and fills
+ * the weights from the seeded splitmix64 -> Box-Muller generator
+ * ("Can an LLM Forget the Right Things?", section 6: untrained weights from a
+ * seeded PRNG). Element i (row-major, logical (out, in) layout) of tensor
+ * stream s is init_std * N(seed, s, i) rounded to nearest-even into wdtype.
+ * Synchronises the device. Errors: VLA_E_INVALID (bad cfg, out == NULL),
+ * VLA_E_HIP (allocation or launch failure). */
+vla_status vla_model_create(const vla_config* cfg, vla_model** out);
+
+/* Free everything the handle owns (synchronises the device). NULL is a no-op. */
+void vla_model_destroy(vla_model* m);
+
+/* Append one frame of n tokens at the next n positions and run the whole
+ * forward over it ("Rebuilding Kshipra Around Memory", section 4).
+ * Exactly one of:
+ *   tokens  host int32[n], ids in [0, vocab): rows of the embedding table;
+ *   embeds  device pointer to [n][hidden] in act_dtype: caller embeddings
+ *           (e.g. visual tokens), used as given.
+ * Writes the new frame id to *out_frame_id (host, nullable; ids count up from
+ * 0 in arrival order). The last row's logits are kept (vla_logits_out).
+ * Errors: VLA_E_INVALID (n < 1, n > max_chunk, both/neither input, id out of
+ * range), VLA_E_NO_BLOCKS (ceil(n/block_tokens) blocks not free, or
+ * max_frames frames resident). */
+vla_status vla_prefill_chunk(vla_model* m, const int32_t* tokens, const void* embeds,
+                             int32_t n, int32_t* out_frame_id, void* stream);
+
+/* One decode token at the next position: embedding row `token`, full forward,
+ * logits kept, and the greedy next token (argmax over the vocabulary, ties to
+ * the lowest id) written to *out_next_token (host, nullable; non-NULL
+ * synchronises the stream). Errors: VLA_E_INVALID (token out of range),
+ * VLA_E_NO_BLOCKS (the tail needs a new block and none is free). */
+vla_status vla_decode_step(vla_model* m, int32_t token, int32_t* out_next_token, void* stream);
+
+/* Score the resident frames on `layer` and evict the most redundant one
+ * ("Can an LLM Forget the Right Things?", section 5). Each frame is represented
+ * by its mean key on that layer (fp64 mean over its tokens of the stored,
+ * post-RoPE keys, all KV heads concatenated: Hkv*d values). For every
+ * unordered pair of frames s = dot / (sqrt(|a|^2) sqrt(|b|^2)) in fp64 (0 when
+ * that denominator is below 1e-8), computed once per pair; each frame's score
+ * is its largest similarity to any other frame; the frame with the highest
+ * score is evicted, ties to the lowest frame id (the oldest). Its blocks are
+ * pushed onto the free-list in logical order and its mean keys dropped.
+ * Writes the evicted frame id and its score (both host, nullable).
+ * Synchronises the stream. Errors: VLA_E_INVALID (layer out of range),
+ * VLA_E_NOTHING_TO_EVICT (fewer than two frames resident). */
+vla_status vla_kv_score_and_evict(vla_model* m, int32_t layer, int32_t* out_frame_id,
+                                  double* out_score, void* stream);
+
+/* Same scoring as vla_kv_score_and_evict without evicting (state unchanged). */
+vla_status vla_kv_score(vla_model* m, int32_t layer, int32_t* out_frame_id, double* out_score,
+                        void* stream);
+
+/* Copy the last computed logits (fp32[vocab], from the last prefill row or
+ * decode step) into `out` (host or device memory; n must equal vocab).
+ * Synchronises the stream. Errors: VLA_E_INVALID (n != vocab, out NULL),
+ * VLA_E_STATE (no forward has run yet). */
+vla_status vla_logits_out(vla_model* m, float* out, int32_t n, void* stream);
+
+/* Message of the last failure on this thread ("" if none). Owned by the library. */
+const char* vla_last_error(void);
+
+/* Append a frame whose keys and values are given: k, v are device pointers to
+ * [n_layers][n][n_kv_heads][head_dim] in act_dtype, stored as given (already
+ * rotated; no RoPE is applied). The frame takes the next n positions and its
+ * mean keys are computed. Errors: as vla_prefill_chunk. */
+vla_status vla_kv_append_raw(vla_model* m, const void* k, const void* v, int32_t n,
+                             int32_t* out_frame_id, void* stream);
+
+/* Drop every frame and decode tail created after frame keep_frame_id, newest
+ * first, returning their blocks in reverse allocation order (this restores the
+ * free-list exactly when nothing was evicted since), and reset the position
+ * and frame-id counters to their values right after that frame. Host-only
+ * bookkeeping; enqueues no work. Errors: VLA_E_INVALID (no such frame). */
+vla_status vla_kv_rollback(vla_model* m, int32_t keep_frame_id);
+
+/* Recompute every resident frame's mean keys on every layer from the stored
+ * keys (a full refresh; reads the whole key cache once). */
+vla_status vla_kv_refresh_mean_keys(vla_model* m, void* stream);
+
+/* Host-side view of the state. */
+typedef struct {
+  int64_t next_position;    /* position the next token will take */
+  int32_t next_frame_id;
+  int32_t n_frames;         /* resident frames */
+  int32_t resident_tokens;  /* frames + decode tail */
+  int32_t free_blocks;
+  int32_t logical_blocks;   /* entries of the logical block table */
+} vla_state;
+vla_status vla_get_state(const vla_model* m, vla_state* out);
+
+/* Logical block table (creation order of frames/tails, blocks in order within
+ * each): physical block ids and valid tokens per block, host arrays of `cap`
+ * entries; *n_out receives the number of entries. */
+vla_status vla_kv_block_table(const vla_model* m, int32_t* blocks, int32_t* ntok, int32_t cap,
+                              int32_t* n_out);
+
+/* Resident frame ids in arrival order (host array of cap entries). */
+vla_status vla_kv_frames(const vla_model* m, int32_t* frame_ids, int32_t cap, int32_t* n_out);
+
+/* Copy layer `layer`'s mean keys of the resident frames, in arrival order, to
+ * host memory out[cap_frames][n_kv_heads*head_dim] (fp64). Synchronises. */
+vla_status vla_mean_keys_out(vla_model* m, int32_t layer, double* out, int32_t cap_frames,
+                             int32_t* n_out, void* stream);
+
+/* Copy the resident keys and values of `layer` in logical order to device
+ * memory k_out, v_out: [cap_tokens][n_kv_heads][head_dim] in act_dtype. */
+vla_status vla_kv_gather(vla_model* m, int32_t layer, void* k_out, void* v_out,
+                         int32_t cap_tokens, int32_t* n_out, void* stream);
+
+/* Copy one weight tensor in its logical (out, in) row-major layout and storage
+ * type to device memory `out` of `bytes` bytes. kind: 1 q, 2 k, 3 v, 4 o,
+ * 5 gate, 6 up, 7 down (per layer), 8 embedding, 9 output head (layer ignored). */
+vla_status vla_weight_out(vla_model* m, int32_t kind, int32_t layer, void* out, int64_t bytes,
+                          void* stream);
+
+/* Kernel timing with HIP events on the launch stream. When enabled for a
+ * kernel class, each launch of that class is bracketed by an event pair;
+ * vla_profile_read synchronises and returns the summed duration (ms) and
+ * launch count since the last enable. Classes: see VLA_K_* below. */
+enum {
+  VLA_K_NONE = 0, VLA_K_GEMV_QKV = 1, VLA_K_GEMV_O = 2, VLA_K_GEMV_GATEUP = 3,
+  VLA_K_GEMV_DOWN = 4, VLA_K_GEMV_HEAD = 5, VLA_K_ATTN_DECODE = 6, VLA_K_GEMM_QKV = 7,
+  VLA_K_GEMM_O = 8, VLA_K_GEMM_GATEUP = 9, VLA_K_GEMM_DOWN = 10, VLA_K_ATTN_PREFILL = 11,
+  VLA_K_MEANKEYS = 12, VLA_K_SCORE = 13, VLA_K_RMSNORM = 14, VLA_K_COUNT = 15
+};
+vla_status vla_profile_enable(vla_model* m, int32_t kernel_class);
+vla_status vla_profile_read(vla_model* m, double* total_ms, int32_t* launches);
+
+/* Host-only LIFO block pool ("Rebuilding Kshipra Around Memory", section 1):
+ * the free-list starts as [0 .. n-1] so the first pop returns n-1; released
+ * blocks are pushed in the order given and popped first. The model uses the
+ * same pool. No HIP calls; usable without a GPU. */
+vla_status vla_pool_create(int32_t num_blocks, vla_pool** out);
+void vla_pool_destroy(vla_pool* p);
+/* Pop n blocks into out[n]; VLA_E_NO_BLOCKS (pool unchanged) if fewer are free. */
+vla_status vla_pool_alloc(vla_pool* p, int32_t n, int32_t* out);
+/* Push n blocks in the order given; VLA_E_INVALID for an id out of range or already free. */
+vla_status vla_pool_release(vla_pool* p, const int32_t* blocks, int32_t n);
+int32_t vla_pool_free_count(const vla_pool* p);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* VLA_H */

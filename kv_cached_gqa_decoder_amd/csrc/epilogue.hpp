@@ -1,0 +1,63 @@
+// Epilogues shared by the projection kernels (matrix-core GEMM, fp32 GEMM, GEMV).
+#pragma once
+
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace vla {
+
+// One RoPE pair of the fused q/k/v projection for token row t.
+// `col` is the even physical column of the pair (LAYOUT_QKV): logical dims
+// j and j + d/2 of head col/d, with j = (col % d) / 2. q and k are rotated by
+// the angle pos * theta^(-2j/d), evaluated in fp64 ("Rebuilding Kshipra Around
+// Memory", section 4: RoPE at absolute positions; rotate-half pairing); q goes
+// to the query buffer, k and v to the paged pool at the token's block and slot
+// (the cache stores post-RoPE keys).
+template <typename T>
+__device__ __forceinline__ void epi_qkv_pair(const FwdCtx& c, int t, int col, float lo, float hi) {
+  const int d = c.g.d;
+  const int head = col / d;
+  const int j = (col % d) >> 1;
+  const int hkv = c.g.hkv;
+  if (head < c.hq + hkv) {
+    const double ang = (double)(c.pos0 + t) * c.inv_freq[j];
+    const float cs = (float)cos(ang), sn = (float)sin(ang);
+    const float rlo = lo * cs - hi * sn;
+    const float rhi = hi * cs + lo * sn;
+    lo = rlo;
+    hi = rhi;
+  }
+  if (head < c.hq) {
+    T* q = (T*)c.qbuf + ((size_t)t * c.hq + head) * d;
+    St<T>::st(q, j, lo);
+    St<T>::st(q, j + d / 2, hi);
+    return;
+  }
+  const int ls = c.cslot0 + t;
+  const int b = c.blk_table[c.cb0 + ls / c.g.bt];
+  const int s = ls % c.g.bt;
+  if (head < c.hq + hkv) {
+    const int h = head - c.hq;
+    T* kp = (T*)c.kpool;
+    St<T>::st(kp, c.g.kidx(c.layer, b, h, s, j), lo);
+    St<T>::st(kp, c.g.kidx(c.layer, b, h, s, j + d / 2), hi);
+  } else {
+    const int h = head - c.hq - hkv;
+    T* vp = (T*)c.vpool;
+    St<T>::st(vp, c.g.vidx(c.layer, b, h, s, j), lo);
+    St<T>::st(vp, c.g.vidx(c.layer, b, h, s, j + d / 2), hi);
+  }
+}
+
+// order-preserving map of an fp32 value to uint32 (larger float -> larger key)
+__device__ __forceinline__ uint32_t f32_order_key(float v) {
+  const uint32_t u = __float_as_uint(v);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+// argmax key: value in the high word, (0xffffffff - index) in the low word, so the
+// largest key is the largest value and, among equal values, the lowest index
+__device__ __forceinline__ unsigned long long argmax_key(float v, uint32_t idx) {
+  return ((unsigned long long)f32_order_key(v) << 32) | (unsigned long long)(0xffffffffu - idx);
+}
+
+}  // namespace vla

@@ -1,0 +1,123 @@
+// Host-side launch interface of the HIP kernels (internal to the library).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace vla {
+
+enum Dtype { DT_F32 = 0, DT_BF16 = 1 };
+
+// Physical weight layouts (all generated in place from the counter-based generator).
+//  PLAIN   row-major [rows][cols], one stream.
+//  QKV     rows = (Hq + 2 Hkv) d: q heads, then k heads, then v heads; inside each
+//          head the two members (j, j + d/2) of a RoPE pair sit on adjacent rows
+//          2j and 2j+1, so one output tile holds both halves of a rotation.
+//  GATEUP  rows = 2F in blocks of 32: 16 gate rows f..f+15 then the 16 matching up
+//          rows, so one 32-column tile holds both operands of the gated product.
+enum Layout { LAYOUT_PLAIN = 0, LAYOUT_QKV = 1, LAYOUT_GATEUP = 2 };
+
+// Paged KV pool geometry. K element (l, b, h, s, i) lives at
+// (((l*nb + b)*hkv + h)*bt + s)*d + i; V is stored transposed inside a block,
+// element (l, b, h, s, i) at (((l*nb + b)*hkv + h)*d + i)*bt + s, so that a
+// 4-key run of one head dimension is contiguous (the operand order of the
+// P*V matrix-core product).
+struct KvGeom {
+  int L, nb, hkv, bt, d;
+  __host__ __device__ size_t kidx(int l, int b, int h, int s, int i) const {
+    return ((((size_t)l * nb + b) * hkv + h) * bt + s) * d + i;
+  }
+  __host__ __device__ size_t vidx(int l, int b, int h, int s, int i) const {
+    return ((((size_t)l * nb + b) * hkv + h) * d + i) * bt + s;
+  }
+};
+
+// Where the rows of the current pass go: row t (0..n-1) is the token at
+// absolute position pos0 + t, stored at logical chunk slot cslot0 + t of the
+// blocks starting at logical block cb0.
+struct FwdCtx {
+  int layer = 0;
+  int64_t pos0 = 0;
+  const double* inv_freq = nullptr;  // [d/2] theta^(-2j/d), fp64
+  void* kpool = nullptr;
+  void* vpool = nullptr;
+  KvGeom g{};
+  const int* blk_table = nullptr;    // logical block -> physical block
+  int cb0 = 0;
+  int cslot0 = 0;
+  void* qbuf = nullptr;              // [n][Hq][d] activations
+  int hq = 0;
+};
+
+enum Epi { EPI_STORE = 0, EPI_RESID = 1, EPI_QKV = 2, EPI_SWIGLU = 3, EPI_HEAD = 4 };
+
+struct GemmArgs {
+  const void* A = nullptr;  // [M][K] activations
+  const void* W = nullptr;  // [N][K] weights (physical layout)
+  int M = 0, N = 0, K = 0;
+  int epi = EPI_STORE;
+  void* C = nullptr;        // STORE [M][N]; RESID x [M][N] (+=); SWIGLU [M][N/2]
+  FwdCtx ctx;
+};
+
+struct GemvArgs {
+  const void* x = nullptr;      // [K] input row (activations)
+  const float* norm_g = nullptr;  // non-null: RMSNorm the input first
+  float eps = 0.f;
+  const void* W = nullptr;      // [N][K]
+  int N = 0, K = 0;
+  int epi = EPI_STORE;
+  void* out = nullptr;          // RESID x[N] (+=); SWIGLU act[N/2]; HEAD logits fp32[N]
+  unsigned long long* argmax_part = nullptr;  // HEAD: one key per workgroup
+  FwdCtx ctx;
+};
+
+struct AttnArgs {
+  const void* q = nullptr;   // [n][Hq][d]
+  void* out = nullptr;       // [n][Hq][d]
+  const void* kpool = nullptr;
+  const void* vpool = nullptr;
+  KvGeom g{};
+  int layer = 0;
+  const int* blk_table = nullptr;  // logical -> physical
+  const int* blk_ntok = nullptr;   // valid tokens per logical block
+  int nlb = 0;                     // logical blocks visible to this pass
+  int last_ntok = 0;               // valid tokens of logical block nlb-1 (overrides the table)
+  int cb0 = 0, cslot0 = 0;         // first token of the causal region (the chunk)
+  int n = 0, hq = 0;
+  int splits = 1;
+  float* part_o = nullptr;         // [units][16][d] (splits > 1)
+  float* part_ml = nullptr;        // [units][2][16]
+  float scale = 1.f;
+};
+
+// ---- launches (all return the launch status) ----
+hipError_t launch_init_weight(void* out, int dt, int layout, int64_t rows, int64_t cols,
+                              uint64_t seed, uint64_t sa, uint64_t sb, uint64_t sc, int hq,
+                              int hkv, int d, double stdv, hipStream_t s);
+hipError_t launch_weight_logical(const void* phys, void* out, int dt, int layout, int which,
+                                 int64_t rows, int64_t cols, int hq, int hkv, int d,
+                                 hipStream_t s);
+hipError_t launch_fill_f32(float* p, float v, int64_t n, hipStream_t s);
+hipError_t launch_embed(const int* tokens, int token_scalar, int n, const void* E, void* x,
+                        int H, int dt, unsigned long long* reset_cell, hipStream_t s);
+hipError_t launch_rmsnorm(const void* x, const float* g, void* u, int rows, int H, float eps,
+                          int dt, hipStream_t s);
+hipError_t launch_gemm(const GemmArgs& a, int dt, hipStream_t s);
+hipError_t launch_gemv(const GemvArgs& a, int dt, hipStream_t s, int* grid_out);
+hipError_t launch_argmax_final(const unsigned long long* part, int nparts,
+                               unsigned long long* result, hipStream_t s);
+hipError_t launch_attention(const AttnArgs& a, int dt, hipStream_t s);
+hipError_t launch_kv_scatter(const void* k, const void* v, int n, void* kpool, void* vpool,
+                             KvGeom g, const int* blk_table, int cb0, int dt, hipStream_t s);
+hipError_t launch_kv_gather(const void* kpool, const void* vpool, KvGeom g, int layer,
+                            const int* blk_table, const int* blk_ntok, const int* tok_base,
+                            int nlb, void* k_out, void* v_out, int dt, hipStream_t s);
+hipError_t launch_meankeys(const void* kpool, KvGeom g, const int* blk_table,
+                           const int* fr_blk0, const int* fr_nblk, const int* fr_ntok,
+                           const int* fr_slot, int nframes, int layer0, int nlayers,
+                           double* table, int max_frames, int dt, hipStream_t s);
+hipError_t launch_score(const double* table_layer, const int* fr_slot, int nframes, int D,
+                        double* m_out, double* result, hipStream_t s);
+
+}  // namespace vla

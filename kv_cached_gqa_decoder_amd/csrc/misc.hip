@@ -1,0 +1,263 @@
+// Weight generation, embedding gather, RMSNorm, raw KV scatter / gather.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace vla {
+
+// ---------------------------------------------------------------------------
+// Seeded generator ("Can an LLM Forget the Right Things?", section 6: weights
+// from splitmix64 feeding Box-Muller). splitmix64 is the generator of Steele,
+// Lea and Flood (2014); counter based here: element i of stream s under seed k
+// draws the two outputs at key + 2i and key + 2i + 1 with key = sm(k ^ sm(s)).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint64_t sm64(uint64_t x) {
+  x += 0x9E3779B97F4A7C15ull;
+  uint64_t z = (x ^ (x >> 30)) * 0xBF58476D1CE4E5B9ull;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+  return z ^ (z >> 31);
+}
+__device__ __forceinline__ double u53(uint64_t x) { return (double)(x >> 11) * 0x1.0p-53; }
+
+__device__ __forceinline__ double normal_at(uint64_t key, uint64_t i) {
+  const double u1 = u53(sm64(key + 2 * i));
+  const double u2 = u53(sm64(key + 2 * i + 1));
+  return sqrt(-2.0 * log(1.0 - u1)) * cos(6.283185307179586 * u2);
+}
+
+// nearest-even rounding of a double to 8 significant bits (bfloat16), normal range
+__device__ __forceinline__ double round_bf16_d(double v) {
+  int e;
+  const double m = frexp(v, &e);
+  return ldexp(rint(m * 256.0) / 256.0, e);
+}
+
+// physical row -> (stream selector 0/1/2, logical row) for the three layouts
+__device__ __forceinline__ void phys_to_logical(int layout, int64_t r, int hq, int hkv, int d,
+                                                int* which, int64_t* lr) {
+  if (layout == LAYOUT_QKV) {
+    const int64_t head = r / d;
+    const int w = (int)(r % d);
+    const int j = (w >> 1) + (w & 1) * (d / 2);
+    if (head < hq) { *which = 0; *lr = head * d + j; }
+    else if (head < hq + hkv) { *which = 1; *lr = (head - hq) * d + j; }
+    else { *which = 2; *lr = (head - hq - hkv) * d + j; }
+  } else if (layout == LAYOUT_GATEUP) {
+    const int64_t b = r / 32;
+    const int w = (int)(r % 32);
+    *which = w < 16 ? 0 : 1;
+    *lr = b * 16 + (w & 15);
+  } else {
+    *which = 0;
+    *lr = r;
+  }
+}
+
+template <typename T>
+__global__ void init_weight_kernel(T* out, int layout, int64_t rows, int64_t cols, uint64_t seed,
+                                   uint64_t sa, uint64_t sb, uint64_t sc, int hq, int hkv, int d,
+                                   double stdv) {
+  const uint64_t keys[3] = {sm64(seed ^ sm64(sa)), sm64(seed ^ sm64(sb)), sm64(seed ^ sm64(sc))};
+  const int64_t total = rows * cols;
+  for (int64_t p = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; p < total;
+       p += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t r = p / cols, c = p % cols;
+    int which;
+    int64_t lr;
+    phys_to_logical(layout, r, hq, hkv, d, &which, &lr);
+    const double v = stdv * normal_at(keys[which], (uint64_t)(lr * cols + c));
+    if constexpr (sizeof(T) == 4) {
+      out[p] = (float)v;
+    } else {
+      out[p] = (bf16_t)(__float_as_uint((float)round_bf16_d(v)) >> 16);
+    }
+  }
+}
+
+// logical (out, in) element (lr, c) of sub-tensor `which` -> physical row
+__device__ __forceinline__ int64_t logical_to_phys(int layout, int which, int64_t lr, int hq,
+                                                   int hkv, int d) {
+  if (layout == LAYOUT_QKV) {
+    const int64_t head = lr / d + (which == 0 ? 0 : which == 1 ? hq : hq + hkv);
+    const int j = (int)(lr % d);
+    const int w = j < d / 2 ? 2 * j : 2 * (j - d / 2) + 1;
+    return head * d + w;
+  }
+  if (layout == LAYOUT_GATEUP) return (lr / 16) * 32 + (lr % 16) + (which ? 16 : 0);
+  return lr;
+}
+
+template <typename T>
+__global__ void weight_logical_kernel(const T* phys, T* out, int layout, int which, int64_t rows,
+                                      int64_t cols, int hq, int hkv, int d) {
+  const int64_t total = rows * cols;
+  for (int64_t p = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; p < total;
+       p += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t lr = p / cols, c = p % cols;
+    out[p] = phys[logical_to_phys(layout, which, lr, hq, hkv, d) * cols + c];
+  }
+}
+
+static int grid_for(int64_t n, int block) {
+  int64_t g = (n + block - 1) / block;
+  if (g > 65536) g = 65536;
+  if (g < 1) g = 1;
+  return (int)g;
+}
+
+hipError_t launch_weight_logical(const void* phys, void* out, int dt, int layout, int which,
+                                 int64_t rows, int64_t cols, int hq, int hkv, int d,
+                                 hipStream_t s) {
+  const int g = grid_for(rows * cols, 256);
+  if (dt == DT_F32)
+    weight_logical_kernel<float><<<g, 256, 0, s>>>((const float*)phys, (float*)out, layout, which,
+                                                    rows, cols, hq, hkv, d);
+  else
+    weight_logical_kernel<bf16_t><<<g, 256, 0, s>>>((const bf16_t*)phys, (bf16_t*)out, layout,
+                                                     which, rows, cols, hq, hkv, d);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+__global__ void fill_f32_kernel(float* p, float v, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+       i += (int64_t)gridDim.x * blockDim.x)
+    p[i] = v;
+}
+hipError_t launch_fill_f32(float* p, float v, int64_t n, hipStream_t s) {
+  fill_f32_kernel<<<grid_for(n, 256), 256, 0, s>>>(p, v, n);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// embedding rows; block 0 also clears the argmax cell of this pass
+template <typename T>
+__global__ void embed_kernel(const int* tokens, int token_scalar, int n, const T* E, T* x, int H,
+                             unsigned long long* reset_cell) {
+  if (reset_cell && blockIdx.x == 0 && threadIdx.x == 0) *reset_cell = 0ull;
+  for (int t = blockIdx.x; t < n; t += gridDim.x) {
+    const int64_t id = tokens ? tokens[t] : token_scalar;
+    for (int i = threadIdx.x; i < H; i += blockDim.x) x[(int64_t)t * H + i] = E[id * H + i];
+  }
+}
+hipError_t launch_embed(const int* tokens, int token_scalar, int n, const void* E, void* x, int H,
+                        int dt, unsigned long long* reset_cell, hipStream_t s) {
+  const int g = n < 1024 ? n : 1024;
+  if (dt == DT_F32)
+    embed_kernel<float><<<g, 256, 0, s>>>(tokens, token_scalar, n, (const float*)E, (float*)x, H,
+                                          reset_cell);
+  else
+    embed_kernel<bf16_t><<<g, 256, 0, s>>>(tokens, token_scalar, n, (const bf16_t*)E, (bf16_t*)x,
+                                           H, reset_cell);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// RMSNorm, one wavefront per row, fp32 statistics: u = x * (mean(x^2) + eps)^-1/2 * g
+template <typename T>
+__global__ __launch_bounds__(256) void rmsnorm_kernel(const T* x, const float* g, T* u, int rows,
+                                                      int H, float eps) {
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= rows) return;
+  const T* xr = x + (int64_t)row * H;
+  float ss = 0.f;
+  for (int i = lane; i < H; i += 64) {
+    const float v = St<T>::ld(xr, i);
+    ss += v * v;
+  }
+  ss = wave_sum(ss);
+  const float r = rsqrtf(ss / (float)H + eps);
+  T* ur = u + (int64_t)row * H;
+  for (int i = lane; i < H; i += 64) St<T>::st(ur, i, St<T>::ld(xr, i) * r * g[i]);
+}
+hipError_t launch_rmsnorm(const void* x, const float* g, void* u, int rows, int H, float eps,
+                          int dt, hipStream_t s) {
+  const int grid = (rows + 3) / 4;
+  if (dt == DT_F32)
+    rmsnorm_kernel<float><<<grid, 256, 0, s>>>((const float*)x, g, (float*)u, rows, H, eps);
+  else
+    rmsnorm_kernel<bf16_t><<<grid, 256, 0, s>>>((const bf16_t*)x, g, (bf16_t*)u, rows, H, eps);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// raw frame append: k, v [L][n][Hkv][d] -> the paged pool at the frame's blocks
+template <typename T>
+__global__ void kv_scatter_kernel(const T* k, const T* v, int n, T* kp, T* vp, KvGeom g,
+                                  const int* blk_table, int cb0) {
+  const int64_t total = (int64_t)g.L * n * g.hkv * g.d;
+  for (int64_t p = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; p < total;
+       p += (int64_t)gridDim.x * blockDim.x) {
+    const int i = (int)(p % g.d);
+    int64_t r = p / g.d;
+    const int h = (int)(r % g.hkv);
+    r /= g.hkv;
+    const int t = (int)(r % n);
+    const int l = (int)(r / n);
+    const int b = blk_table[cb0 + t / g.bt];
+    const int sl = t % g.bt;
+    kp[g.kidx(l, b, h, sl, i)] = k[p];
+    vp[g.vidx(l, b, h, sl, i)] = v[p];
+  }
+}
+hipError_t launch_kv_scatter(const void* k, const void* v, int n, void* kpool, void* vpool,
+                             KvGeom g, const int* blk_table, int cb0, int dt, hipStream_t s) {
+  const int grid = grid_for((int64_t)g.L * n * g.hkv * g.d, 256);
+  if (dt == DT_F32)
+    kv_scatter_kernel<float><<<grid, 256, 0, s>>>((const float*)k, (const float*)v, n,
+                                                  (float*)kpool, (float*)vpool, g, blk_table, cb0);
+  else
+    kv_scatter_kernel<bf16_t><<<grid, 256, 0, s>>>((const bf16_t*)k, (const bf16_t*)v, n,
+                                                   (bf16_t*)kpool, (bf16_t*)vpool, g, blk_table,
+                                                   cb0);
+  return hipGetLastError();
+}
+
+// resident K/V of one layer in logical order -> [tokens][Hkv][d]
+template <typename T>
+__global__ void kv_gather_kernel(const T* kp, const T* vp, KvGeom g, int layer,
+                                 const int* blk_table, const int* blk_ntok, const int* tok_base,
+                                 T* ko, T* vo) {
+  const int lb = blockIdx.x;
+  const int b = blk_table[lb];
+  const int nt = blk_ntok[lb];
+  const int base = tok_base[lb];
+  const int per = g.hkv * g.d;
+  for (int e = threadIdx.x; e < nt * per; e += blockDim.x) {
+    const int sl = e / per;
+    const int h = (e % per) / g.d;
+    const int i = e % g.d;
+    const int64_t o = (int64_t)(base + sl) * per + h * g.d + i;
+    ko[o] = kp[g.kidx(layer, b, h, sl, i)];
+    vo[o] = vp[g.vidx(layer, b, h, sl, i)];
+  }
+}
+hipError_t launch_kv_gather(const void* kpool, const void* vpool, KvGeom g, int layer,
+                            const int* blk_table, const int* blk_ntok, const int* tok_base,
+                            int nlb, void* k_out, void* v_out, int dt, hipStream_t s) {
+  if (nlb <= 0) return hipSuccess;
+  if (dt == DT_F32)
+    kv_gather_kernel<float><<<nlb, 256, 0, s>>>((const float*)kpool, (const float*)vpool, g, layer,
+                                                blk_table, blk_ntok, tok_base, (float*)k_out,
+                                                (float*)v_out);
+  else
+    kv_gather_kernel<bf16_t><<<nlb, 256, 0, s>>>((const bf16_t*)kpool, (const bf16_t*)vpool, g,
+                                                 layer, blk_table, blk_ntok, tok_base,
+                                                 (bf16_t*)k_out, (bf16_t*)v_out);
+  return hipGetLastError();
+}
+
+hipError_t launch_init_weight(void* out, int dt, int layout, int64_t rows, int64_t cols,
+                              uint64_t seed, uint64_t sa, uint64_t sb, uint64_t sc, int hq,
+                              int hkv, int d, double stdv, hipStream_t s) {
+  const int g = grid_for(rows * cols, 256);
+  if (dt == DT_F32)
+    init_weight_kernel<float><<<g, 256, 0, s>>>((float*)out, layout, rows, cols, seed, sa, sb, sc,
+                                                hq, hkv, d, stdv);
+  else
+    init_weight_kernel<bf16_t><<<g, 256, 0, s>>>((bf16_t*)out, layout, rows, cols, seed, sa, sb,
+                                                 sc, hq, hkv, d, stdv);
+  return hipGetLastError();
+}
+
+}  // namespace vla

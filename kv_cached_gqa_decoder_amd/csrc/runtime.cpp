@@ -1,0 +1,978 @@
+// Host runtime behind the C ABI of include/vla.h: model state, frame registry,
+// block tables, and the launch sequences of prefill, decode and scoring.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <string.h>
+
+#include <algorithm>
+#include <cmath>
+#include <string>
+#include <vector>
+
+#include "../../include/vla.h"
+#include "block_pool.hpp"
+#include "kernels.hpp"
+
+using namespace vla;
+
+namespace {
+
+thread_local std::string g_err;
+
+struct Err {
+  vla_status st;
+  std::string msg;
+};
+
+#define HIPCHK(expr)                                                                      \
+  do {                                                                                    \
+    hipError_t e_ = (expr);                                                               \
+    if (e_ != hipSuccess)                                                                 \
+      throw Err{VLA_E_HIP, std::string(#expr) + " failed: " + hipGetErrorString(e_)};     \
+  } while (0)
+
+[[noreturn]] void raise(vla_status st, const std::string& msg) { throw Err{st, msg}; }
+
+constexpr int kPartUnits = 4096;   // attention split partials capacity (wavefront units)
+constexpr int kArgmaxParts = 2048; // head GEMV workgroups at most
+
+struct Segment {
+  bool frame = true;
+  int frame_id = -1;
+  int64_t start_pos = 0;
+  int ntok = 0;
+  int slot = -1;               // mean-key table row (frames only)
+  std::vector<int> blocks;
+};
+
+// pinned host staging buffer for uploads; an event guards its reuse
+struct Staging {
+  void* host = nullptr;
+  size_t cap = 0;
+  hipEvent_t ev = nullptr;
+  bool pending = false;
+};
+
+}  // namespace
+
+struct vla_pool {
+  BlockPool p;
+};
+
+struct vla_model {
+  vla_config cfg{};
+  int dev = 0;
+  int dt = DT_BF16;
+  size_t esz = 2;
+  KvGeom geom{};
+
+  // weights (physical layouts, see kernels.hpp)
+  void* embed = nullptr;
+  void* head = nullptr;
+  std::vector<void*> wqkv, wo, wgu, wdown;
+  float* norm_ones = nullptr;   // all RMSNorm weights are 1
+  double* inv_freq = nullptr;
+
+  // cache
+  void* kpool = nullptr;
+  void* vpool = nullptr;
+  double* meankeys = nullptr;   // [L][max_frames][Hkv*d]
+
+  // scratch
+  void* x = nullptr;
+  void* u = nullptr;
+  void* qbuf = nullptr;
+  void* ao = nullptr;
+  void* act = nullptr;
+  float* logits = nullptr;
+  unsigned long long* amax_part = nullptr;
+  unsigned long long* amax_res = nullptr;
+  float* part_o = nullptr;
+  float* part_ml = nullptr;
+  int* d_meta = nullptr;        // blk | ntok | tokbase (nb each) | fr_slot | fr_blk0 | fr_nblk | fr_ntok
+  int* d_tokens = nullptr;
+  double* d_score_m = nullptr;
+  double* d_score_res = nullptr;
+  Staging st_meta, st_tok, st_read;
+
+  // host state
+  BlockPool pool;
+  std::vector<Segment> segs;
+  std::vector<int> free_slots;
+  int64_t next_pos = 0;
+  int next_frame_id = 0;
+  bool meta_dirty = true;
+  bool have_logits = false;
+
+  // profiling
+  int prof_cls = VLA_K_NONE;
+  std::vector<hipEvent_t> prof_ev;
+  int prof_used = 0;
+
+  std::vector<void*> allocs;
+
+  int* d_blk() const { return d_meta; }
+  int* d_ntok() const { return d_meta + cfg.num_blocks; }
+  int* d_tokbase() const { return d_meta + 2 * cfg.num_blocks; }
+  int* d_fr_slot() const { return d_meta + 3 * cfg.num_blocks; }
+  int* d_fr_blk0() const { return d_fr_slot() + cfg.max_frames; }
+  int* d_fr_nblk() const { return d_fr_blk0() + cfg.max_frames; }
+  int* d_fr_ntok() const { return d_fr_nblk() + cfg.max_frames; }
+  size_t meta_ints() const { return 3 * (size_t)cfg.num_blocks + 4 * (size_t)cfg.max_frames; }
+};
+
+namespace {
+
+template <typename F>
+vla_status guarded(F&& f) {
+  try {
+    f();
+    g_err.clear();
+    return VLA_OK;
+  } catch (const Err& e) {
+    g_err = e.msg;
+    return e.st;
+  } catch (const std::exception& e) {
+    g_err = e.what();
+    return VLA_E_STATE;
+  } catch (...) {
+    g_err = "unknown error";
+    return VLA_E_STATE;
+  }
+}
+
+void* dalloc(vla_model* m, size_t bytes) {
+  void* p = nullptr;
+  HIPCHK(hipMalloc(&p, bytes < 256 ? 256 : bytes));
+  m->allocs.push_back(p);
+  return p;
+}
+
+void staging_init(Staging& s, size_t bytes) {
+  HIPCHK(hipHostMalloc(&s.host, bytes, hipHostMallocDefault));
+  s.cap = bytes;
+  HIPCHK(hipEventCreateWithFlags(&s.ev, hipEventDisableTiming));
+}
+void staging_free(Staging& s) {
+  if (s.ev) (void)hipEventSynchronize(s.ev);
+  if (s.host) (void)hipHostFree(s.host);
+  if (s.ev) (void)hipEventDestroy(s.ev);
+  s = Staging{};
+}
+void* staging_acquire(Staging& s) {
+  if (s.pending) HIPCHK(hipEventSynchronize(s.ev));
+  s.pending = false;
+  return s.host;
+}
+void staging_upload(Staging& s, void* dst, size_t bytes, hipStream_t st) {
+  HIPCHK(hipMemcpyAsync(dst, s.host, bytes, hipMemcpyHostToDevice, st));
+  HIPCHK(hipEventRecord(s.ev, st));
+  s.pending = true;
+}
+
+// ---- profiling (HIP events on the launch stream) ----
+void prof_mark(vla_model* m, int cls, hipStream_t st) {
+  if (m->prof_cls != cls || cls == VLA_K_NONE) return;
+  if (m->prof_used == (int)m->prof_ev.size()) {
+    hipEvent_t e;
+    HIPCHK(hipEventCreate(&e));
+    m->prof_ev.push_back(e);
+  }
+  HIPCHK(hipEventRecord(m->prof_ev[m->prof_used++], st));
+}
+
+#define LAUNCH(m, cls, st, expr)          \
+  do {                                    \
+    prof_mark(m, cls, st);                \
+    HIPCHK(expr);                         \
+    prof_mark(m, cls, st);                \
+  } while (0)
+
+// ---- bookkeeping ----
+int bt_of(const vla_model* m) { return m->cfg.block_tokens; }
+
+int logical_blocks(const vla_model* m) {
+  int n = 0;
+  for (const auto& s : m->segs) n += (int)s.blocks.size();
+  return n;
+}
+int resident_tokens(const vla_model* m) {
+  int n = 0;
+  for (const auto& s : m->segs) n += s.ntok;
+  return n;
+}
+int n_frames(const vla_model* m) {
+  int n = 0;
+  for (const auto& s : m->segs) n += s.frame ? 1 : 0;
+  return n;
+}
+// logical index of segment i's first block
+int seg_blk0(const vla_model* m, size_t i) {
+  int n = 0;
+  for (size_t k = 0; k < i; ++k) n += (int)m->segs[k].blocks.size();
+  return n;
+}
+
+// rebuild and upload the logical block table and the frame list
+void sync_meta(vla_model* m, hipStream_t st) {
+  if (!m->meta_dirty) return;
+  const int nb = m->cfg.num_blocks, mf = m->cfg.max_frames, bt = bt_of(m);
+  int* h = (int*)staging_acquire(m->st_meta);
+  memset(h, 0, m->meta_ints() * sizeof(int));
+  int* blk = h;
+  int* ntok = h + nb;
+  int* base = h + 2 * nb;
+  int* fslot = h + 3 * nb;
+  int* fblk0 = fslot + mf;
+  int* fnblk = fblk0 + mf;
+  int* fntok = fnblk + mf;
+  int lb = 0, tok = 0, f = 0;
+  for (const auto& s : m->segs) {
+    if (s.frame) {
+      fslot[f] = s.slot;
+      fblk0[f] = lb;
+      fnblk[f] = (int)s.blocks.size();
+      fntok[f] = s.ntok;
+      ++f;
+    }
+    for (size_t i = 0; i < s.blocks.size(); ++i) {
+      blk[lb] = s.blocks[i];
+      ntok[lb] = std::min(bt, s.ntok - (int)i * bt);
+      base[lb] = tok;
+      tok += ntok[lb];
+      ++lb;
+    }
+  }
+  staging_upload(m->st_meta, m->d_meta, m->meta_ints() * sizeof(int), st);
+  m->meta_dirty = false;
+}
+
+int last_block_ntok(const vla_model* m) {
+  for (auto it = m->segs.rbegin(); it != m->segs.rend(); ++it)
+    if (!it->blocks.empty()) return it->ntok - ((int)it->blocks.size() - 1) * bt_of(m);
+  return 0;
+}
+
+FwdCtx make_ctx(vla_model* m, int layer, int64_t pos0, int cb0, int cslot0) {
+  FwdCtx c;
+  c.layer = layer;
+  c.pos0 = pos0;
+  c.inv_freq = m->inv_freq;
+  c.kpool = m->kpool;
+  c.vpool = m->vpool;
+  c.g = m->geom;
+  c.blk_table = m->d_blk();
+  c.cb0 = cb0;
+  c.cslot0 = cslot0;
+  c.qbuf = m->qbuf;
+  c.hq = m->cfg.n_heads;
+  return c;
+}
+
+int attn_splits(const vla_model* m, int n, int nlb) {
+  if (m->dt == DT_F32) return 1;
+  const int grp = m->cfg.n_heads / m->cfg.n_kv_heads;
+  const int units = m->cfg.n_kv_heads * ((n * grp + 15) / 16);
+  const int target = n == 1 ? 512 : 1024;
+  int s = target / units;
+  s = std::min(s, (nlb + 1) / 2);
+  s = std::min(s, kPartUnits / units);
+  return std::max(s, 1);
+}
+
+// the per-layer launches of one pass over n rows whose K/V go to logical slots
+// (cb0, cslot0 ...); rows = prefill chunk (n >= 1, matrix path) or decode (GEMV path)
+void run_layers(vla_model* m, int n, int64_t pos0, int cb0, int cslot0, bool decode,
+                hipStream_t st) {
+  const vla_config& c = m->cfg;
+  const int H = c.hidden, qd = c.n_heads * c.head_dim;
+  const int nqkv = (c.n_heads + 2 * c.n_kv_heads) * c.head_dim;
+  const int nlb = logical_blocks(m);
+  AttnArgs at;
+  at.q = m->qbuf;
+  at.out = m->ao;
+  at.kpool = m->kpool;
+  at.vpool = m->vpool;
+  at.g = m->geom;
+  at.blk_table = m->d_blk();
+  at.blk_ntok = m->d_ntok();
+  at.nlb = nlb;
+  at.last_ntok = last_block_ntok(m);
+  at.cb0 = cb0;
+  at.cslot0 = cslot0;
+  at.n = n;
+  at.hq = c.n_heads;
+  at.splits = attn_splits(m, n, nlb);
+  at.part_o = m->part_o;
+  at.part_ml = m->part_ml;
+  at.scale = (float)(1.0 / std::sqrt((double)c.head_dim));
+
+  for (int l = 0; l < c.n_layers; ++l) {
+    at.layer = l;
+    const FwdCtx ctx = make_ctx(m, l, pos0, cb0, cslot0);
+    if (decode) {
+      GemvArgs g;
+      g.x = m->x;
+      g.norm_g = m->norm_ones;
+      g.eps = c.rms_eps;
+      g.W = m->wqkv[l];
+      g.N = nqkv;
+      g.K = H;
+      g.epi = EPI_QKV;
+      g.ctx = ctx;
+      LAUNCH(m, VLA_K_GEMV_QKV, st, launch_gemv(g, m->dt, st, nullptr));
+      LAUNCH(m, VLA_K_ATTN_DECODE, st, launch_attention(at, m->dt, st));
+      GemvArgs o;
+      o.x = m->ao;
+      o.W = m->wo[l];
+      o.N = H;
+      o.K = qd;
+      o.epi = EPI_RESID;
+      o.out = m->x;
+      LAUNCH(m, VLA_K_GEMV_O, st, launch_gemv(o, m->dt, st, nullptr));
+      GemvArgs gu;
+      gu.x = m->x;
+      gu.norm_g = m->norm_ones;
+      gu.eps = c.rms_eps;
+      gu.W = m->wgu[l];
+      gu.N = 2 * c.ffn;
+      gu.K = H;
+      gu.epi = EPI_SWIGLU;
+      gu.out = m->act;
+      LAUNCH(m, VLA_K_GEMV_GATEUP, st, launch_gemv(gu, m->dt, st, nullptr));
+      GemvArgs dn;
+      dn.x = m->act;
+      dn.W = m->wdown[l];
+      dn.N = H;
+      dn.K = c.ffn;
+      dn.epi = EPI_RESID;
+      dn.out = m->x;
+      LAUNCH(m, VLA_K_GEMV_DOWN, st, launch_gemv(dn, m->dt, st, nullptr));
+    } else {
+      LAUNCH(m, VLA_K_RMSNORM, st,
+             launch_rmsnorm(m->x, m->norm_ones, m->u, n, H, c.rms_eps, m->dt, st));
+      GemmArgs q;
+      q.A = m->u;
+      q.W = m->wqkv[l];
+      q.M = n;
+      q.N = nqkv;
+      q.K = H;
+      q.epi = EPI_QKV;
+      q.ctx = ctx;
+      LAUNCH(m, VLA_K_GEMM_QKV, st, launch_gemm(q, m->dt, st));
+      LAUNCH(m, VLA_K_ATTN_PREFILL, st, launch_attention(at, m->dt, st));
+      GemmArgs o;
+      o.A = m->ao;
+      o.W = m->wo[l];
+      o.M = n;
+      o.N = H;
+      o.K = qd;
+      o.epi = EPI_RESID;
+      o.C = m->x;
+      LAUNCH(m, VLA_K_GEMM_O, st, launch_gemm(o, m->dt, st));
+      LAUNCH(m, VLA_K_RMSNORM, st,
+             launch_rmsnorm(m->x, m->norm_ones, m->u, n, H, c.rms_eps, m->dt, st));
+      GemmArgs gu;
+      gu.A = m->u;
+      gu.W = m->wgu[l];
+      gu.M = n;
+      gu.N = 2 * c.ffn;
+      gu.K = H;
+      gu.epi = EPI_SWIGLU;
+      gu.C = m->act;
+      LAUNCH(m, VLA_K_GEMM_GATEUP, st, launch_gemm(gu, m->dt, st));
+      GemmArgs dn;
+      dn.A = m->act;
+      dn.W = m->wdown[l];
+      dn.M = n;
+      dn.N = H;
+      dn.K = c.ffn;
+      dn.epi = EPI_RESID;
+      dn.C = m->x;
+      LAUNCH(m, VLA_K_GEMM_DOWN, st, launch_gemm(dn, m->dt, st));
+    }
+  }
+}
+
+// final RMSNorm of the last row, output head, argmax
+void run_head(vla_model* m, int row, hipStream_t st) {
+  const vla_config& c = m->cfg;
+  GemvArgs h;
+  h.x = (const char*)m->x + (size_t)row * c.hidden * m->esz;
+  h.norm_g = m->norm_ones;
+  h.eps = c.rms_eps;
+  h.W = m->head;
+  h.N = c.vocab;
+  h.K = c.hidden;
+  h.epi = EPI_HEAD;
+  h.out = m->logits;
+  h.argmax_part = m->amax_part;
+  int grid = 0;
+  LAUNCH(m, VLA_K_GEMV_HEAD, st, launch_gemv(h, m->dt, st, &grid));
+  HIPCHK(launch_argmax_final(m->amax_part, grid, m->amax_res, st));
+  m->have_logits = true;
+}
+
+int read_argmax(vla_model* m, hipStream_t st) {
+  unsigned long long* h = (unsigned long long*)staging_acquire(m->st_read);
+  HIPCHK(hipMemcpyAsync(h, m->amax_res, sizeof(unsigned long long), hipMemcpyDeviceToHost, st));
+  HIPCHK(hipStreamSynchronize(st));
+  return (int)(0xffffffffu - (uint32_t)(*h & 0xffffffffull));
+}
+
+void mean_keys_for(vla_model* m, int frame_index, hipStream_t st) {
+  LAUNCH(m, VLA_K_MEANKEYS, st,
+         launch_meankeys(m->kpool, m->geom, m->d_blk(), m->d_fr_blk0() + frame_index,
+                         m->d_fr_nblk() + frame_index, m->d_fr_ntok() + frame_index,
+                         m->d_fr_slot() + frame_index, 1, 0, m->cfg.n_layers, m->meankeys,
+                         m->cfg.max_frames, m->dt, st));
+}
+
+// register a new frame of n tokens (blocks, slot, positions); returns its segment index
+size_t new_frame(vla_model* m, int n) {
+  const int bt = bt_of(m);
+  if (n < 1 || n > m->cfg.max_chunk)
+    raise(VLA_E_INVALID, "chunk length " + std::to_string(n) + " outside [1, max_chunk=" +
+                             std::to_string(m->cfg.max_chunk) + "]");
+  if (m->free_slots.empty()) raise(VLA_E_NO_BLOCKS, "max_frames frames already resident");
+  const int need = (n + bt - 1) / bt;
+  Segment s;
+  if (!m->pool.alloc(need, &s.blocks))
+    raise(VLA_E_NO_BLOCKS, "need " + std::to_string(need) + " blocks, " +
+                               std::to_string(m->pool.free_count()) + " free");
+  s.frame = true;
+  s.frame_id = m->next_frame_id++;
+  s.start_pos = m->next_pos;
+  s.ntok = n;
+  s.slot = m->free_slots.back();
+  m->free_slots.pop_back();
+  m->next_pos += n;
+  m->segs.push_back(s);
+  m->meta_dirty = true;
+  return m->segs.size() - 1;
+}
+
+int frame_index_of(const vla_model* m, size_t seg_index) {
+  int f = 0;
+  for (size_t i = 0; i < seg_index; ++i) f += m->segs[i].frame ? 1 : 0;
+  return f;
+}
+
+void validate_cfg(const vla_config* c) {
+  auto bad = [](const std::string& s) { raise(VLA_E_INVALID, "invalid config: " + s); };
+  if (!c) bad("null");
+  if (c->n_layers < 1 || c->hidden < 64 || c->n_heads < 1 || c->n_kv_heads < 1 ||
+      c->head_dim < 2 || c->ffn < 16 || c->vocab < 2)
+    bad("non-positive size");
+  if (c->n_heads % c->n_kv_heads) bad("n_heads must be a multiple of n_kv_heads");
+  if (c->head_dim % 16 || c->head_dim > 256) bad("head_dim must be a multiple of 16, <= 256");
+  if (c->ffn % 16) bad("ffn must be a multiple of 16");
+  if (c->hidden % 64) bad("hidden must be a multiple of 64");
+  if (c->block_tokens != 16) bad("block_tokens must be 16");
+  if (c->num_blocks < 1 || c->max_frames < 1 || c->max_chunk < 1) bad("budget sizes");
+  if (c->wdtype != c->act_dtype || (c->wdtype != VLA_F32 && c->wdtype != VLA_BF16))
+    bad("wdtype must equal act_dtype, VLA_F32 or VLA_BF16");
+  if (c->ffn_kind != VLA_SWIGLU) bad("ffn_kind");
+  if (!(c->rope_theta > 1.0)) bad("rope_theta");
+  const int qd = c->n_heads * c->head_dim;
+  if (c->wdtype == VLA_BF16) {
+    if (c->head_dim != 64 && c->head_dim != 128 && c->head_dim != 256)
+      bad("bf16 path: head_dim 64, 128 or 256");
+    if (qd % 64 || c->ffn % 64) bad("bf16 path: n_heads*head_dim and ffn multiples of 64");
+  } else {
+    if (c->num_blocks * c->block_tokens > 2048) bad("fp32 path: at most 2048 cached tokens");
+    if (qd % 8 || c->ffn % 8) bad("multiples of 8");
+  }
+  if ((int64_t)c->vocab * c->hidden > ((int64_t)1 << 40)) bad("vocab*hidden too large");
+}
+
+void init_weights(vla_model* m) {
+  const vla_config& c = m->cfg;
+  const int H = c.hidden, d = c.head_dim, hq = c.n_heads, hkv = c.n_kv_heads;
+  const hipStream_t st = nullptr;
+  auto sid = [](int layer, int kind) { return (uint64_t)(((layer + 1) << 8) | kind); };
+  HIPCHK(launch_init_weight(m->embed, m->dt, LAYOUT_PLAIN, c.vocab, H, c.seed, 1, 1, 1, hq, hkv,
+                            d, c.init_std, st));
+  HIPCHK(launch_init_weight(m->head, m->dt, LAYOUT_PLAIN, c.vocab, H, c.seed, 2, 2, 2, hq, hkv, d,
+                            c.init_std, st));
+  for (int l = 0; l < c.n_layers; ++l) {
+    HIPCHK(launch_init_weight(m->wqkv[l], m->dt, LAYOUT_QKV, (int64_t)(hq + 2 * hkv) * d, H,
+                              c.seed, sid(l, 1), sid(l, 2), sid(l, 3), hq, hkv, d, c.init_std, st));
+    HIPCHK(launch_init_weight(m->wo[l], m->dt, LAYOUT_PLAIN, H, (int64_t)hq * d, c.seed,
+                              sid(l, 4), sid(l, 4), sid(l, 4), hq, hkv, d, c.init_std, st));
+    HIPCHK(launch_init_weight(m->wgu[l], m->dt, LAYOUT_GATEUP, 2 * (int64_t)c.ffn, H, c.seed,
+                              sid(l, 5), sid(l, 6), sid(l, 6), hq, hkv, d, c.init_std, st));
+    HIPCHK(launch_init_weight(m->wdown[l], m->dt, LAYOUT_PLAIN, H, c.ffn, c.seed, sid(l, 7),
+                              sid(l, 7), sid(l, 7), hq, hkv, d, c.init_std, st));
+  }
+  HIPCHK(launch_fill_f32(m->norm_ones, 1.0f, H, st));
+  std::vector<double> inv(d / 2);
+  for (int j = 0; j < d / 2; ++j) inv[j] = std::pow(c.rope_theta, -2.0 * j / d);
+  HIPCHK(hipMemcpy(m->inv_freq, inv.data(), inv.size() * sizeof(double), hipMemcpyHostToDevice));
+  HIPCHK(hipDeviceSynchronize());
+}
+
+void destroy(vla_model* m) {
+  if (!m) return;
+  (void)hipSetDevice(m->dev);
+  (void)hipDeviceSynchronize();
+  for (void* p : m->allocs) (void)hipFree(p);
+  staging_free(m->st_meta);
+  staging_free(m->st_tok);
+  staging_free(m->st_read);
+  for (hipEvent_t e : m->prof_ev) (void)hipEventDestroy(e);
+  delete m;
+}
+
+}  // namespace
+
+// ============================================================================
+// C ABI
+// ============================================================================
+extern "C" {
+
+const char* vla_last_error(void) { return g_err.c_str(); }
+
+vla_status vla_model_create(const vla_config* cfg, vla_model** out) {
+  vla_model* m = nullptr;
+  vla_status st = guarded([&] {
+    if (!out) raise(VLA_E_INVALID, "out is NULL");
+    *out = nullptr;
+    validate_cfg(cfg);
+    m = new vla_model();
+    m->cfg = *cfg;
+    HIPCHK(hipGetDevice(&m->dev));
+    const vla_config& c = m->cfg;
+    m->dt = c.act_dtype == VLA_F32 ? DT_F32 : DT_BF16;
+    m->esz = m->dt == DT_F32 ? 4 : 2;
+    m->geom = KvGeom{c.n_layers, c.num_blocks, c.n_kv_heads, c.block_tokens, c.head_dim};
+    const size_t H = c.hidden, d = c.head_dim, hq = c.n_heads, hkv = c.n_kv_heads;
+    const size_t e = m->esz;
+    m->embed = dalloc(m, (size_t)c.vocab * H * e);
+    m->head = dalloc(m, (size_t)c.vocab * H * e);
+    for (int l = 0; l < c.n_layers; ++l) {
+      m->wqkv.push_back(dalloc(m, (hq + 2 * hkv) * d * H * e));
+      m->wo.push_back(dalloc(m, H * hq * d * e));
+      m->wgu.push_back(dalloc(m, 2 * (size_t)c.ffn * H * e));
+      m->wdown.push_back(dalloc(m, H * (size_t)c.ffn * e));
+    }
+    m->norm_ones = (float*)dalloc(m, H * sizeof(float));
+    m->inv_freq = (double*)dalloc(m, d / 2 * sizeof(double));
+    const size_t pool_bytes = (size_t)c.n_layers * c.num_blocks * hkv * c.block_tokens * d * e;
+    m->kpool = dalloc(m, pool_bytes);
+    m->vpool = dalloc(m, pool_bytes);
+    // stale slots of partial blocks meet zero probabilities in P*V: keep them finite
+    HIPCHK(hipMemset(m->kpool, 0, pool_bytes));
+    HIPCHK(hipMemset(m->vpool, 0, pool_bytes));
+    m->meankeys = (double*)dalloc(m, (size_t)c.n_layers * c.max_frames * hkv * d * sizeof(double));
+    const size_t mc = c.max_chunk;
+    m->x = dalloc(m, mc * H * e);
+    m->u = dalloc(m, mc * H * e);
+    m->qbuf = dalloc(m, mc * hq * d * e);
+    m->ao = dalloc(m, mc * hq * d * e);
+    m->act = dalloc(m, mc * (size_t)c.ffn * e);
+    m->logits = (float*)dalloc(m, (size_t)c.vocab * sizeof(float));
+    m->amax_part = (unsigned long long*)dalloc(m, kArgmaxParts * sizeof(unsigned long long));
+    m->amax_res = (unsigned long long*)dalloc(m, sizeof(unsigned long long));
+    if (m->dt == DT_BF16) {
+      m->part_o = (float*)dalloc(m, (size_t)kPartUnits * 16 * d * sizeof(float));
+      m->part_ml = (float*)dalloc(m, (size_t)kPartUnits * 32 * sizeof(float));
+    }
+    m->d_meta = (int*)dalloc(m, m->meta_ints() * sizeof(int));
+    m->d_tokens = (int*)dalloc(m, mc * sizeof(int));
+    m->d_score_m = (double*)dalloc(m, (size_t)c.max_frames * sizeof(double));
+    m->d_score_res = (double*)dalloc(m, 2 * sizeof(double));
+    staging_init(m->st_meta, m->meta_ints() * sizeof(int));
+    staging_init(m->st_tok, mc * sizeof(int));
+    staging_init(m->st_read, 64);
+    m->pool.reset(c.num_blocks);
+    for (int i = c.max_frames - 1; i >= 0; --i) m->free_slots.push_back(i);
+    init_weights(m);
+    *out = m;
+  });
+  if (st != VLA_OK && m) {
+    std::string keep = g_err;
+    destroy(m);
+    g_err = keep;
+  }
+  return st;
+}
+
+void vla_model_destroy(vla_model* m) { destroy(m); }
+
+vla_status vla_prefill_chunk(vla_model* m, const int32_t* tokens, const void* embeds, int32_t n,
+                             int32_t* out_frame_id, void* stream) {
+  return guarded([&] {
+    if (!m) raise(VLA_E_INVALID, "null model");
+    if ((tokens == nullptr) == (embeds == nullptr))
+      raise(VLA_E_INVALID, "exactly one of tokens / embeds must be given");
+    if (n < 1 || n > m->cfg.max_chunk) raise(VLA_E_INVALID, "chunk length out of range");
+    if (tokens)
+      for (int i = 0; i < n; ++i)
+        if (tokens[i] < 0 || tokens[i] >= m->cfg.vocab) raise(VLA_E_INVALID, "token id out of range");
+    HIPCHK(hipSetDevice(m->dev));
+    const hipStream_t st = (hipStream_t)stream;
+    const size_t si = new_frame(m, n);
+    const Segment seg = m->segs[si];
+    try {
+      sync_meta(m, st);
+      if (tokens) {
+        int* h = (int*)staging_acquire(m->st_tok);
+        memcpy(h, tokens, (size_t)n * sizeof(int));
+        staging_upload(m->st_tok, m->d_tokens, (size_t)n * sizeof(int), st);
+        HIPCHK(launch_embed(m->d_tokens, 0, n, m->embed, m->x, m->cfg.hidden, m->dt, nullptr, st));
+      } else {
+        HIPCHK(hipMemcpyAsync(m->x, embeds, (size_t)n * m->cfg.hidden * m->esz,
+                              hipMemcpyDeviceToDevice, st));
+      }
+      run_layers(m, n, seg.start_pos, seg_blk0(m, si), 0, /*decode=*/false, st);
+      run_head(m, n - 1, st);
+      mean_keys_for(m, frame_index_of(m, si), st);
+    } catch (...) {
+      // undo the registration (blocks back in reverse pop order)
+      std::vector<int> rb(seg.blocks.rbegin(), seg.blocks.rend());
+      m->pool.release(rb.data(), (int)rb.size());
+      m->free_slots.push_back(seg.slot);
+      m->segs.erase(m->segs.begin() + si);
+      m->next_pos = seg.start_pos;
+      m->next_frame_id = seg.frame_id;
+      m->meta_dirty = true;
+      throw;
+    }
+    if (out_frame_id) *out_frame_id = seg.frame_id;
+  });
+}
+
+vla_status vla_decode_step(vla_model* m, int32_t token, int32_t* out_next_token, void* stream) {
+  return guarded([&] {
+    if (!m) raise(VLA_E_INVALID, "null model");
+    if (token < 0 || token >= m->cfg.vocab) raise(VLA_E_INVALID, "token id out of range");
+    HIPCHK(hipSetDevice(m->dev));
+    const hipStream_t st = (hipStream_t)stream;
+    const int bt = bt_of(m);
+    // place the token in the decode tail (a tail starts on a fresh block)
+    bool new_seg = false, new_block = false;
+    if (m->segs.empty() || m->segs.back().frame) {
+      Segment s;
+      s.frame = false;
+      s.start_pos = m->next_pos;
+      if (!m->pool.alloc(1, &s.blocks)) raise(VLA_E_NO_BLOCKS, "no free block for the decode tail");
+      m->segs.push_back(s);
+      new_seg = true;
+    } else if (m->segs.back().ntok == (int)m->segs.back().blocks.size() * bt) {
+      if (!m->pool.alloc(1, &m->segs.back().blocks))
+        raise(VLA_E_NO_BLOCKS, "no free block for the decode tail");
+      new_block = true;
+    }
+    Segment& tail = m->segs.back();
+    const int off = tail.ntok;
+    tail.ntok += 1;
+    const int64_t pos = m->next_pos++;
+    if (new_seg || new_block) m->meta_dirty = true;
+    try {
+      sync_meta(m, st);
+      const int cb0 = logical_blocks(m) - 1;
+      HIPCHK(launch_embed(nullptr, token, 1, m->embed, m->x, m->cfg.hidden, m->dt, nullptr, st));
+      run_layers(m, 1, pos, cb0, off % bt, /*decode=*/true, st);
+      run_head(m, 0, st);
+    } catch (...) {
+      tail.ntok -= 1;
+      m->next_pos -= 1;
+      if (new_seg) {
+        m->pool.release(tail.blocks.data(), 1);
+        m->segs.pop_back();
+      } else if (new_block) {
+        m->pool.release(&tail.blocks.back(), 1);
+        tail.blocks.pop_back();
+      }
+      m->meta_dirty = true;
+      throw;
+    }
+    if (out_next_token) *out_next_token = read_argmax(m, st);
+  });
+}
+
+static vla_status score_impl(vla_model* m, int32_t layer, int32_t* out_frame_id, double* out_score,
+                             void* stream, bool evict) {
+  return guarded([&] {
+    if (!m) raise(VLA_E_INVALID, "null model");
+    if (layer < 0 || layer >= m->cfg.n_layers) raise(VLA_E_INVALID, "layer out of range");
+    const int F = n_frames(m);
+    if (F < 2) raise(VLA_E_NOTHING_TO_EVICT, "fewer than 2 frames resident");
+    HIPCHK(hipSetDevice(m->dev));
+    const hipStream_t st = (hipStream_t)stream;
+    sync_meta(m, st);
+    const int D = m->cfg.n_kv_heads * m->cfg.head_dim;
+    const double* tab = m->meankeys + (size_t)layer * m->cfg.max_frames * D;
+    LAUNCH(m, VLA_K_SCORE, st, launch_score(tab, m->d_fr_slot(), F, D, m->d_score_m,
+                                            m->d_score_res, st));
+    double* h = (double*)staging_acquire(m->st_read);
+    HIPCHK(hipMemcpyAsync(h, m->d_score_res, 2 * sizeof(double), hipMemcpyDeviceToHost, st));
+    HIPCHK(hipStreamSynchronize(st));
+    const int idx = (int)h[0];
+    const double score = h[1];
+    if (idx < 0 || idx >= F) raise(VLA_E_STATE, "scoring returned an invalid index");
+    // idx-th resident frame in arrival order
+    size_t si = 0;
+    for (int f = -1; si < m->segs.size(); ++si)
+      if (m->segs[si].frame && ++f == idx) break;
+    const int fid = m->segs[si].frame_id;
+    if (evict) {
+      Segment s = m->segs[si];
+      if (!m->pool.release(s.blocks.data(), (int)s.blocks.size()))
+        raise(VLA_E_STATE, "block bookkeeping corrupted");
+      m->free_slots.push_back(s.slot);
+      m->segs.erase(m->segs.begin() + si);
+      m->meta_dirty = true;
+    }
+    if (out_frame_id) *out_frame_id = fid;
+    if (out_score) *out_score = score;
+  });
+}
+
+vla_status vla_kv_score_and_evict(vla_model* m, int32_t layer, int32_t* out_frame_id,
+                                  double* out_score, void* stream) {
+  return score_impl(m, layer, out_frame_id, out_score, stream, true);
+}
+
+vla_status vla_kv_score(vla_model* m, int32_t layer, int32_t* out_frame_id, double* out_score,
+                        void* stream) {
+  return score_impl(m, layer, out_frame_id, out_score, stream, false);
+}
+
+vla_status vla_logits_out(vla_model* m, float* out, int32_t n, void* stream) {
+  return guarded([&] {
+    if (!m || !out) raise(VLA_E_INVALID, "null argument");
+    if (n != m->cfg.vocab) raise(VLA_E_INVALID, "n must equal vocab");
+    if (!m->have_logits) raise(VLA_E_STATE, "no forward has run yet");
+    HIPCHK(hipSetDevice(m->dev));
+    const hipStream_t st = (hipStream_t)stream;
+    HIPCHK(hipMemcpyAsync(out, m->logits, (size_t)n * sizeof(float), hipMemcpyDefault, st));
+    HIPCHK(hipStreamSynchronize(st));
+  });
+}
+
+vla_status vla_kv_append_raw(vla_model* m, const void* k, const void* v, int32_t n,
+                             int32_t* out_frame_id, void* stream) {
+  return guarded([&] {
+    if (!m || !k || !v) raise(VLA_E_INVALID, "null argument");
+    HIPCHK(hipSetDevice(m->dev));
+    const hipStream_t st = (hipStream_t)stream;
+    const size_t si = new_frame(m, n);
+    const Segment seg = m->segs[si];
+    try {
+      sync_meta(m, st);
+      HIPCHK(launch_kv_scatter(k, v, n, m->kpool, m->vpool, m->geom, m->d_blk(), seg_blk0(m, si),
+                               m->dt, st));
+      mean_keys_for(m, frame_index_of(m, si), st);
+    } catch (...) {
+      std::vector<int> rb(seg.blocks.rbegin(), seg.blocks.rend());
+      m->pool.release(rb.data(), (int)rb.size());
+      m->free_slots.push_back(seg.slot);
+      m->segs.erase(m->segs.begin() + si);
+      m->next_pos = seg.start_pos;
+      m->next_frame_id = seg.frame_id;
+      m->meta_dirty = true;
+      throw;
+    }
+    if (out_frame_id) *out_frame_id = seg.frame_id;
+  });
+}
+
+vla_status vla_kv_rollback(vla_model* m, int32_t keep_frame_id) {
+  return guarded([&] {
+    if (!m) raise(VLA_E_INVALID, "null model");
+    size_t keep = m->segs.size();
+    for (size_t i = 0; i < m->segs.size(); ++i)
+      if (m->segs[i].frame && m->segs[i].frame_id == keep_frame_id) keep = i;
+    if (keep == m->segs.size()) raise(VLA_E_INVALID, "no such resident frame");
+    while (m->segs.size() > keep + 1) {
+      Segment s = m->segs.back();
+      std::vector<int> rb(s.blocks.rbegin(), s.blocks.rend());
+      if (!m->pool.release(rb.data(), (int)rb.size()))
+        raise(VLA_E_STATE, "block bookkeeping corrupted");
+      if (s.frame) m->free_slots.push_back(s.slot);
+      m->segs.pop_back();
+    }
+    const Segment& k = m->segs[keep];
+    m->next_pos = k.start_pos + k.ntok;
+    m->next_frame_id = keep_frame_id + 1;
+    m->meta_dirty = true;
+  });
+}
+
+vla_status vla_kv_refresh_mean_keys(vla_model* m, void* stream) {
+  return guarded([&] {
+    if (!m) raise(VLA_E_INVALID, "null model");
+    HIPCHK(hipSetDevice(m->dev));
+    const hipStream_t st = (hipStream_t)stream;
+    sync_meta(m, st);
+    const int F = n_frames(m);
+    LAUNCH(m, VLA_K_MEANKEYS, st,
+           launch_meankeys(m->kpool, m->geom, m->d_blk(), m->d_fr_blk0(), m->d_fr_nblk(),
+                           m->d_fr_ntok(), m->d_fr_slot(), F, 0, m->cfg.n_layers, m->meankeys,
+                           m->cfg.max_frames, m->dt, st));
+  });
+}
+
+vla_status vla_get_state(const vla_model* m, vla_state* out) {
+  return guarded([&] {
+    if (!m || !out) raise(VLA_E_INVALID, "null argument");
+    out->next_position = m->next_pos;
+    out->next_frame_id = m->next_frame_id;
+    out->n_frames = n_frames(m);
+    out->resident_tokens = resident_tokens(m);
+    out->free_blocks = m->pool.free_count();
+    out->logical_blocks = logical_blocks(m);
+  });
+}
+
+vla_status vla_kv_block_table(const vla_model* m, int32_t* blocks, int32_t* ntok, int32_t cap,
+                              int32_t* n_out) {
+  return guarded([&] {
+    if (!m || !n_out) raise(VLA_E_INVALID, "null argument");
+    const int bt = m->cfg.block_tokens;
+    int n = 0;
+    for (const auto& s : m->segs)
+      for (size_t i = 0; i < s.blocks.size(); ++i, ++n)
+        if (n < cap) {
+          if (blocks) blocks[n] = s.blocks[i];
+          if (ntok) ntok[n] = std::min(bt, s.ntok - (int)i * bt);
+        }
+    *n_out = n;
+  });
+}
+
+vla_status vla_kv_frames(const vla_model* m, int32_t* frame_ids, int32_t cap, int32_t* n_out) {
+  return guarded([&] {
+    if (!m || !n_out) raise(VLA_E_INVALID, "null argument");
+    int n = 0;
+    for (const auto& s : m->segs)
+      if (s.frame) {
+        if (frame_ids && n < cap) frame_ids[n] = s.frame_id;
+        ++n;
+      }
+    *n_out = n;
+  });
+}
+
+vla_status vla_mean_keys_out(vla_model* m, int32_t layer, double* out, int32_t cap_frames,
+                             int32_t* n_out, void* stream) {
+  return guarded([&] {
+    if (!m || !out || !n_out) raise(VLA_E_INVALID, "null argument");
+    if (layer < 0 || layer >= m->cfg.n_layers) raise(VLA_E_INVALID, "layer out of range");
+    HIPCHK(hipSetDevice(m->dev));
+    const hipStream_t st = (hipStream_t)stream;
+    const int D = m->cfg.n_kv_heads * m->cfg.head_dim;
+    int f = 0;
+    for (const auto& s : m->segs) {
+      if (!s.frame) continue;
+      if (f < cap_frames)
+        HIPCHK(hipMemcpyAsync(out + (size_t)f * D,
+                              m->meankeys + ((size_t)layer * m->cfg.max_frames + s.slot) * D,
+                              D * sizeof(double), hipMemcpyDeviceToHost, st));
+      ++f;
+    }
+    HIPCHK(hipStreamSynchronize(st));
+    *n_out = f;
+  });
+}
+
+vla_status vla_kv_gather(vla_model* m, int32_t layer, void* k_out, void* v_out,
+                         int32_t cap_tokens, int32_t* n_out, void* stream) {
+  return guarded([&] {
+    if (!m || !k_out || !v_out || !n_out) raise(VLA_E_INVALID, "null argument");
+    if (layer < 0 || layer >= m->cfg.n_layers) raise(VLA_E_INVALID, "layer out of range");
+    const int T = resident_tokens(m);
+    *n_out = T;
+    if (T > cap_tokens) raise(VLA_E_INVALID, "cap_tokens smaller than the resident tokens");
+    HIPCHK(hipSetDevice(m->dev));
+    const hipStream_t st = (hipStream_t)stream;
+    m->meta_dirty = true;  // the device copy of the last block's count may be stale
+    sync_meta(m, st);
+    HIPCHK(launch_kv_gather(m->kpool, m->vpool, m->geom, layer, m->d_blk(), m->d_ntok(),
+                            m->d_tokbase(), logical_blocks(m), k_out, v_out, m->dt, st));
+  });
+}
+
+vla_status vla_weight_out(vla_model* m, int32_t kind, int32_t layer, void* out, int64_t bytes,
+                          void* stream) {
+  return guarded([&] {
+    if (!m || !out) raise(VLA_E_INVALID, "null argument");
+    const vla_config& c = m->cfg;
+    if (kind < 1 || kind > 9) raise(VLA_E_INVALID, "kind");
+    if (kind <= 7 && (layer < 0 || layer >= c.n_layers)) raise(VLA_E_INVALID, "layer");
+    HIPCHK(hipSetDevice(m->dev));
+    const hipStream_t st = (hipStream_t)stream;
+    const int64_t H = c.hidden, d = c.head_dim, qd = (int64_t)c.n_heads * d,
+                  kd = (int64_t)c.n_kv_heads * d;
+    int64_t rows = 0, cols = H;
+    const void* src = nullptr;
+    int layout = LAYOUT_PLAIN, which = 0;
+    switch (kind) {
+      case 1: rows = qd; src = m->wqkv[layer]; layout = LAYOUT_QKV; which = 0; break;
+      case 2: rows = kd; src = m->wqkv[layer]; layout = LAYOUT_QKV; which = 1; break;
+      case 3: rows = kd; src = m->wqkv[layer]; layout = LAYOUT_QKV; which = 2; break;
+      case 4: rows = H; cols = qd; src = m->wo[layer]; break;
+      case 5: rows = c.ffn; src = m->wgu[layer]; layout = LAYOUT_GATEUP; which = 0; break;
+      case 6: rows = c.ffn; src = m->wgu[layer]; layout = LAYOUT_GATEUP; which = 1; break;
+      case 7: rows = H; cols = c.ffn; src = m->wdown[layer]; break;
+      case 8: rows = c.vocab; src = m->embed; break;
+      case 9: rows = c.vocab; src = m->head; break;
+    }
+    if (bytes < rows * cols * (int64_t)m->esz) raise(VLA_E_INVALID, "output buffer too small");
+    HIPCHK(launch_weight_logical(src, out, m->dt, layout, which, rows, cols, c.n_heads,
+                                 c.n_kv_heads, (int)d, st));
+  });
+}
+
+vla_status vla_profile_enable(vla_model* m, int32_t kernel_class) {
+  return guarded([&] {
+    if (!m) raise(VLA_E_INVALID, "null model");
+    if (kernel_class < 0 || kernel_class >= VLA_K_COUNT) raise(VLA_E_INVALID, "kernel class");
+    m->prof_cls = kernel_class;
+    m->prof_used = 0;
+  });
+}
+
+vla_status vla_profile_read(vla_model* m, double* total_ms, int32_t* launches) {
+  return guarded([&] {
+    if (!m) raise(VLA_E_INVALID, "null model");
+    double tot = 0.0;
+    for (int i = 0; i + 1 < m->prof_used; i += 2) {
+      HIPCHK(hipEventSynchronize(m->prof_ev[i + 1]));
+      float ms = 0.f;
+      HIPCHK(hipEventElapsedTime(&ms, m->prof_ev[i], m->prof_ev[i + 1]));
+      tot += ms;
+    }
+    if (total_ms) *total_ms = tot;
+    if (launches) *launches = m->prof_used / 2;
+  });
+}
+
+// ---- host-only pool ----
+vla_status vla_pool_create(int32_t num_blocks, vla_pool** out) {
+  return guarded([&] {
+    if (!out || num_blocks < 0) raise(VLA_E_INVALID, "bad argument");
+    *out = new vla_pool();
+    (*out)->p.reset(num_blocks);
+  });
+}
+void vla_pool_destroy(vla_pool* p) { delete p; }
+vla_status vla_pool_alloc(vla_pool* p, int32_t n, int32_t* out) {
+  return guarded([&] {
+    if (!p || (!out && n > 0) || n < 0) raise(VLA_E_INVALID, "bad argument");
+    std::vector<int> got;
+    if (!p->p.alloc(n, &got)) raise(VLA_E_NO_BLOCKS, "not enough free blocks");
+    for (int i = 0; i < n; ++i) out[i] = got[i];
+  });
+}
+vla_status vla_pool_release(vla_pool* p, const int32_t* blocks, int32_t n) {
+  return guarded([&] {
+    if (!p || (!blocks && n > 0) || n < 0) raise(VLA_E_INVALID, "bad argument");
+    if (!p->p.release(blocks, n)) raise(VLA_E_INVALID, "block id out of range or already free");
+  });
+}
+int32_t vla_pool_free_count(const vla_pool* p) { return p ? p->p.free_count() : 0; }
+
+}  // extern "C"

@@ -1,0 +1,129 @@
+// Redundant-frame scoring ("Can an LLM Forget the Right Things?", section 5:
+// evict the frame most similar to another one, by cosine similarity; the
+// cosine is a dot product over two norms, 0 below a 1e-8 denominator).
+//
+// mean keys   fp64 mean over a frame's tokens of its stored keys, per layer,
+//             all KV heads concatenated. A sum of bf16 or fp32 values in fp64
+//             is exact here, so the result does not depend on the order.
+// scoring     one workgroup per frame i computes s_ij for every j != i and
+//             m_i = max_j s_ij; the pair value is a pure function of the
+//             unordered pair (same operand order, same reduction tree for
+//             (i, j) and (j, i)), so s_ij == s_ji bit for bit. A second
+//             kernel takes argmax_i m_i with ties to the lowest index.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace vla {
+
+template <typename T>
+__global__ __launch_bounds__(256) void meankeys_kernel(const T* kp, KvGeom g, const int* blk_table,
+                                                       const int* fr_blk0, const int* fr_nblk,
+                                                       const int* fr_ntok, const int* fr_slot,
+                                                       int layer0, double* table, int max_frames) {
+  const int f = blockIdx.x;
+  const int layer = layer0 + blockIdx.y;
+  const int D = g.hkv * g.d;
+  const int blk0 = fr_blk0[f], nblk = fr_nblk[f], ntok = fr_ntok[f];
+  double* out = table + ((size_t)layer * max_frames + fr_slot[f]) * D;
+  for (int i = threadIdx.x; i < D; i += blockDim.x) {
+    const int h = i / g.d, dd = i % g.d;
+    double s = 0.0;
+    for (int k = 0; k < nblk; ++k) {
+      const int b = blk_table[blk0 + k];
+      const int nt = min(g.bt, ntok - k * g.bt);
+      for (int sl = 0; sl < nt; ++sl) s += (double)St<T>::ld(kp, g.kidx(layer, b, h, sl, dd));
+    }
+    out[i] = s / (double)ntok;
+  }
+}
+
+hipError_t launch_meankeys(const void* kpool, KvGeom g, const int* blk_table, const int* fr_blk0,
+                           const int* fr_nblk, const int* fr_ntok, const int* fr_slot, int nframes,
+                           int layer0, int nlayers, double* table, int max_frames, int dt,
+                           hipStream_t s) {
+  if (nframes <= 0 || nlayers <= 0) return hipSuccess;
+  dim3 grid(nframes, nlayers);
+  if (dt == DT_F32)
+    meankeys_kernel<float><<<grid, 256, 0, s>>>((const float*)kpool, g, blk_table, fr_blk0,
+                                                fr_nblk, fr_ntok, fr_slot, layer0, table,
+                                                max_frames);
+  else
+    meankeys_kernel<bf16_t><<<grid, 256, 0, s>>>((const bf16_t*)kpool, g, blk_table, fr_blk0,
+                                                 fr_nblk, fr_ntok, fr_slot, layer0, table,
+                                                 max_frames);
+  return hipGetLastError();
+}
+
+// dot product of two fp64 rows by one wavefront: lane sums k = lane, lane+64, ...
+// in order, then a fixed xor-tree across lanes
+__device__ __forceinline__ double wave_dot(const double* x, const double* y, int D, int lane) {
+  double s = 0.0;
+  for (int k = lane; k < D; k += 64) s = fma(x[k], y[k], s);
+  return wave_sum_d(s);
+}
+
+__global__ __launch_bounds__(256) void score_rows_kernel(const double* tab, const int* fr_slot,
+                                                         int F, int D, double* m_out) {
+  __shared__ double wmax[4];
+  const int i = blockIdx.x;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  double best = -INFINITY;
+  for (int j = wave; j < F; j += 4) {
+    if (j == i) continue;
+    const int lo = min(i, j), hi = max(i, j);
+    const double* a = tab + (size_t)fr_slot[lo] * D;
+    const double* b = tab + (size_t)fr_slot[hi] * D;
+    const double dot = wave_dot(a, b, D, lane);
+    const double na = wave_dot(a, a, D, lane);
+    const double nb = wave_dot(b, b, D, lane);
+    const double den = sqrt(na) * sqrt(nb);
+    const double sij = den < 1e-8 ? 0.0 : dot / den;
+    best = sij > best ? sij : best;
+  }
+  if (lane == 0) wmax[wave] = best;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    double m = wmax[0];
+    for (int w = 1; w < 4; ++w) m = wmax[w] > m ? wmax[w] : m;
+    m_out[i] = m;
+  }
+}
+
+// argmax over m[0..F), ties to the lowest index; result[0] = index, result[1] = value
+__global__ __launch_bounds__(256) void score_argmax_kernel(const double* m, int F, double* result) {
+  __shared__ double sv[256];
+  __shared__ int si[256];
+  double bv = -INFINITY;
+  int bi = 0x7fffffff;
+  for (int i = threadIdx.x; i < F; i += 256) {
+    if (m[i] > bv) { bv = m[i]; bi = i; }  // ascending i: strict > keeps the lowest
+  }
+  sv[threadIdx.x] = bv;
+  si[threadIdx.x] = bi;
+  __syncthreads();
+  for (int o = 128; o > 0; o >>= 1) {
+    if ((int)threadIdx.x < o) {
+      const double v2 = sv[threadIdx.x + o];
+      const int i2 = si[threadIdx.x + o];
+      if (v2 > sv[threadIdx.x] || (v2 == sv[threadIdx.x] && i2 < si[threadIdx.x])) {
+        sv[threadIdx.x] = v2;
+        si[threadIdx.x] = i2;
+      }
+    }
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    result[0] = (double)si[0];
+    result[1] = sv[0];
+  }
+}
+
+hipError_t launch_score(const double* table_layer, const int* fr_slot, int nframes, int D,
+                        double* m_out, double* result, hipStream_t s) {
+  if (nframes < 2) return hipErrorInvalidValue;
+  score_rows_kernel<<<nframes, 256, 0, s>>>(table_layer, fr_slot, nframes, D, m_out);
+  score_argmax_kernel<<<1, 256, 0, s>>>(m_out, nframes, result);
+  return hipGetLastError();
+}
+
+}  // namespace vla

@@ -1,0 +1,387 @@
+"""ctypes binding of libvla.so: the C entry points of include/vla.h under the same names.
+
+Argument marshalling only: every step of the path runs in the library's HIP
+kernels. Device pointers are passed as integers or as objects with a
+``data_ptr()`` method (torch tensors); streams as integers (a hipStream_t, e.g.
+``torch.cuda.current_stream().cuda_stream``) or None for the null stream.
+Failures raise ``VlaError`` carrying the status code and vla_last_error().
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from ctypes import POINTER, byref, c_double, c_int32, c_int64, c_uint64, c_void_p
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libvla.so")
+
+VLA_OK, VLA_E_INVALID, VLA_E_NO_BLOCKS, VLA_E_NOTHING_TO_EVICT, VLA_E_HIP, VLA_E_STATE = \
+    0, -1, -2, -3, -4, -5
+VLA_F32, VLA_BF16, VLA_INT4_G128 = 0, 1, 2
+VLA_SWIGLU = 0
+
+# kernel classes for vla_profile_enable
+K_CLASSES = {
+    "gemv_qkv": 1, "gemv_o": 2, "gemv_gateup": 3, "gemv_down": 4, "gemv_head": 5,
+    "attn_decode": 6, "gemm_qkv": 7, "gemm_o": 8, "gemm_gateup": 9, "gemm_down": 10,
+    "attn_prefill": 11, "meankeys": 12, "score": 13, "rmsnorm": 14,
+}
+
+
+class VlaError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"vla status {status}: {msg}")
+        self.status = status
+
+
+class vla_config(ctypes.Structure):
+    _fields_ = [
+        ("n_layers", c_int32), ("hidden", c_int32), ("n_heads", c_int32),
+        ("n_kv_heads", c_int32), ("head_dim", c_int32), ("ffn", c_int32), ("vocab", c_int32),
+        ("rms_eps", ctypes.c_float), ("rope_theta", c_double),
+        ("wdtype", c_int32), ("act_dtype", c_int32), ("ffn_kind", c_int32),
+        ("block_tokens", c_int32), ("num_blocks", c_int32), ("max_frames", c_int32),
+        ("max_chunk", c_int32), ("seed", c_uint64), ("init_std", c_double),
+    ]
+
+
+class vla_state(ctypes.Structure):
+    _fields_ = [("next_position", c_int64), ("next_frame_id", c_int32), ("n_frames", c_int32),
+                ("resident_tokens", c_int32), ("free_blocks", c_int32),
+                ("logical_blocks", c_int32)]
+
+
+_SIGS = {
+    "vla_model_create": (c_int32, [POINTER(vla_config), POINTER(c_void_p)]),
+    "vla_model_destroy": (None, [c_void_p]),
+    "vla_prefill_chunk": (c_int32, [c_void_p, c_void_p, c_void_p, c_int32, POINTER(c_int32),
+                                    c_void_p]),
+    "vla_decode_step": (c_int32, [c_void_p, c_int32, POINTER(c_int32), c_void_p]),
+    "vla_kv_score_and_evict": (c_int32, [c_void_p, c_int32, POINTER(c_int32), POINTER(c_double),
+                                         c_void_p]),
+    "vla_kv_score": (c_int32, [c_void_p, c_int32, POINTER(c_int32), POINTER(c_double), c_void_p]),
+    "vla_logits_out": (c_int32, [c_void_p, c_void_p, c_int32, c_void_p]),
+    "vla_last_error": (ctypes.c_char_p, []),
+    "vla_kv_append_raw": (c_int32, [c_void_p, c_void_p, c_void_p, c_int32, POINTER(c_int32),
+                                    c_void_p]),
+    "vla_kv_rollback": (c_int32, [c_void_p, c_int32]),
+    "vla_kv_refresh_mean_keys": (c_int32, [c_void_p, c_void_p]),
+    "vla_get_state": (c_int32, [c_void_p, POINTER(vla_state)]),
+    "vla_kv_block_table": (c_int32, [c_void_p, c_void_p, c_void_p, c_int32, POINTER(c_int32)]),
+    "vla_kv_frames": (c_int32, [c_void_p, c_void_p, c_int32, POINTER(c_int32)]),
+    "vla_mean_keys_out": (c_int32, [c_void_p, c_int32, c_void_p, c_int32, POINTER(c_int32),
+                                    c_void_p]),
+    "vla_kv_gather": (c_int32, [c_void_p, c_int32, c_void_p, c_void_p, c_int32,
+                                POINTER(c_int32), c_void_p]),
+    "vla_weight_out": (c_int32, [c_void_p, c_int32, c_int32, c_void_p, c_int64, c_void_p]),
+    "vla_profile_enable": (c_int32, [c_void_p, c_int32]),
+    "vla_profile_read": (c_int32, [c_void_p, POINTER(c_double), POINTER(c_int32)]),
+    "vla_pool_create": (c_int32, [c_int32, POINTER(c_void_p)]),
+    "vla_pool_destroy": (None, [c_void_p]),
+    "vla_pool_alloc": (c_int32, [c_void_p, c_int32, c_void_p]),
+    "vla_pool_release": (c_int32, [c_void_p, c_void_p, c_int32]),
+    "vla_pool_free_count": (c_int32, [c_void_p]),
+}
+
+_lib = None
+
+
+def load(path: str = LIB_PATH):
+    """Load libvla.so (raises if it has not been built: there is no fallback path)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(path):
+            raise ImportError(f"{path} is missing: build it with "
+                              "`python kv_cached_gqa_decoder_amd/build.py` (hipcc, gfx950)")
+        lib = ctypes.CDLL(path)
+        for name, (res, args) in _SIGS.items():
+            fn = getattr(lib, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = lib
+    return _lib
+
+
+def _ptr(x):
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    return x.data_ptr()
+
+
+def _stream(s):
+    if s is None:
+        return None
+    if isinstance(s, int):
+        return s
+    return s.cuda_stream
+
+
+def _check(st: int):
+    if st != VLA_OK:
+        raise VlaError(st, load().vla_last_error().decode())
+
+
+# ---- the C entry points ----------------------------------------------------
+def vla_model_create(cfg: vla_config) -> int:
+    h = c_void_p()
+    _check(load().vla_model_create(byref(cfg), byref(h)))
+    return h.value
+
+
+def vla_model_destroy(m: int) -> None:
+    load().vla_model_destroy(m)
+
+
+def vla_prefill_chunk(m: int, tokens=None, embeds=None, n: int = 0, stream=None) -> int:
+    """tokens: host int32 buffer (numpy array or ctypes array) or None; embeds: device pointer."""
+    fid = c_int32(-1)
+    tok_ptr = None
+    if tokens is not None:
+        import numpy as np
+        tokens = np.ascontiguousarray(tokens, dtype=np.int32)
+        tok_ptr = tokens.ctypes.data
+        n = n or tokens.size
+    _check(load().vla_prefill_chunk(m, tok_ptr, _ptr(embeds), n, byref(fid), _stream(stream)))
+    return fid.value
+
+
+def vla_decode_step(m: int, token: int, stream=None, want_token: bool = True):
+    nxt = c_int32(-1)
+    _check(load().vla_decode_step(m, int(token), byref(nxt) if want_token else None,
+                                  _stream(stream)))
+    return nxt.value if want_token else None
+
+
+def vla_kv_score_and_evict(m: int, layer: int = 0, stream=None):
+    fid, sc = c_int32(-1), c_double(0.0)
+    _check(load().vla_kv_score_and_evict(m, layer, byref(fid), byref(sc), _stream(stream)))
+    return fid.value, sc.value
+
+
+def vla_kv_score(m: int, layer: int = 0, stream=None):
+    fid, sc = c_int32(-1), c_double(0.0)
+    _check(load().vla_kv_score(m, layer, byref(fid), byref(sc), _stream(stream)))
+    return fid.value, sc.value
+
+
+def vla_logits_out(m: int, out, n: int, stream=None) -> None:
+    _check(load().vla_logits_out(m, _ptr(out) if not hasattr(out, "ctypes") else out.ctypes.data,
+                                 n, _stream(stream)))
+
+
+def vla_last_error() -> str:
+    return load().vla_last_error().decode()
+
+
+def vla_kv_append_raw(m: int, k, v, n: int, stream=None) -> int:
+    fid = c_int32(-1)
+    _check(load().vla_kv_append_raw(m, _ptr(k), _ptr(v), n, byref(fid), _stream(stream)))
+    return fid.value
+
+
+def vla_kv_rollback(m: int, keep_frame_id: int) -> None:
+    _check(load().vla_kv_rollback(m, keep_frame_id))
+
+
+def vla_kv_refresh_mean_keys(m: int, stream=None) -> None:
+    _check(load().vla_kv_refresh_mean_keys(m, _stream(stream)))
+
+
+def vla_get_state(m: int) -> dict:
+    s = vla_state()
+    _check(load().vla_get_state(m, byref(s)))
+    return {k: getattr(s, k) for k, _ in vla_state._fields_}
+
+
+def vla_kv_block_table(m: int):
+    import numpy as np
+    n = c_int32(0)
+    _check(load().vla_kv_block_table(m, None, None, 0, byref(n)))
+    blocks = np.zeros(max(n.value, 1), dtype=np.int32)
+    ntok = np.zeros(max(n.value, 1), dtype=np.int32)
+    _check(load().vla_kv_block_table(m, blocks.ctypes.data, ntok.ctypes.data, n.value, byref(n)))
+    return blocks[: n.value], ntok[: n.value]
+
+
+def vla_kv_frames(m: int):
+    import numpy as np
+    n = c_int32(0)
+    _check(load().vla_kv_frames(m, None, 0, byref(n)))
+    ids = np.zeros(max(n.value, 1), dtype=np.int32)
+    _check(load().vla_kv_frames(m, ids.ctypes.data, n.value, byref(n)))
+    return ids[: n.value]
+
+
+def vla_mean_keys_out(m: int, layer: int, cap_frames: int, dim: int, stream=None):
+    import numpy as np
+    out = np.zeros((max(cap_frames, 1), dim), dtype=np.float64)
+    n = c_int32(0)
+    _check(load().vla_mean_keys_out(m, layer, out.ctypes.data, cap_frames, byref(n),
+                                    _stream(stream)))
+    return out[: min(n.value, cap_frames)]
+
+
+def vla_kv_gather(m: int, layer: int, k_out, v_out, cap_tokens: int, stream=None) -> int:
+    n = c_int32(0)
+    _check(load().vla_kv_gather(m, layer, _ptr(k_out), _ptr(v_out), cap_tokens, byref(n),
+                                _stream(stream)))
+    return n.value
+
+
+def vla_weight_out(m: int, kind: int, layer: int, out, nbytes: int, stream=None) -> None:
+    _check(load().vla_weight_out(m, kind, layer, _ptr(out), nbytes, _stream(stream)))
+
+
+def vla_profile_enable(m: int, kernel_class: int) -> None:
+    _check(load().vla_profile_enable(m, kernel_class))
+
+
+def vla_profile_read(m: int):
+    ms, n = c_double(0.0), c_int32(0)
+    _check(load().vla_profile_read(m, byref(ms), byref(n)))
+    return ms.value, n.value
+
+
+def vla_pool_create(num_blocks: int) -> int:
+    h = c_void_p()
+    _check(load().vla_pool_create(num_blocks, byref(h)))
+    return h.value
+
+
+def vla_pool_destroy(p: int) -> None:
+    load().vla_pool_destroy(p)
+
+
+def vla_pool_alloc(p: int, n: int):
+    import numpy as np
+    out = np.zeros(max(n, 1), dtype=np.int32)
+    _check(load().vla_pool_alloc(p, n, out.ctypes.data))
+    return [int(v) for v in out[:n]]
+
+
+def vla_pool_release(p: int, blocks) -> None:
+    import numpy as np
+    b = np.ascontiguousarray(blocks, dtype=np.int32)
+    _check(load().vla_pool_release(p, b.ctypes.data, b.size))
+
+
+def vla_pool_free_count(p: int) -> int:
+    return load().vla_pool_free_count(p)
+
+
+# ---- configurations of the workloads --------------------------------------
+PRESETS = {
+    # tiny GQA decoder, fp32: 64-token prompt then 16 greedy decodes
+    "c1_tiny_f32": dict(n_layers=2, hidden=256, n_heads=4, n_kv_heads=2, head_dim=64, ffn=688,
+                        vocab=1024, rope_theta=1e4, wdtype=VLA_F32, num_blocks=8,
+                        max_frames=8, max_chunk=64, seed=1235),
+    # Qwen2.5-1.5B-shaped GQA decoder, bf16: 1024 cached + 256-token chunk + 16 decodes
+    "c2_qwen1p5b_bf16": dict(n_layers=28, hidden=1536, n_heads=12, n_kv_heads=2, head_dim=128,
+                             ffn=8960, vocab=151936, rope_theta=1e6, wdtype=VLA_BF16,
+                             num_blocks=96, max_frames=16, max_chunk=256, seed=1236),
+    # same shape, 128 frames of 64 tokens at a 512-block budget, 32 eviction cycles
+    "c3_semantic_eviction": dict(n_layers=28, hidden=1536, n_heads=12, n_kv_heads=2,
+                                 head_dim=128, ffn=8960, vocab=151936, rope_theta=1e6,
+                                 wdtype=VLA_BF16, num_blocks=512, max_frames=128, max_chunk=64,
+                                 seed=1237),
+}
+
+
+def make_config(**kw) -> vla_config:
+    c = vla_config()
+    c.n_layers = kw["n_layers"]
+    c.hidden = kw["hidden"]
+    c.n_heads = kw["n_heads"]
+    c.n_kv_heads = kw["n_kv_heads"]
+    c.head_dim = kw["head_dim"]
+    c.ffn = kw["ffn"]
+    c.vocab = kw["vocab"]
+    c.rms_eps = kw.get("rms_eps", 1e-6)
+    c.rope_theta = kw.get("rope_theta", 1e4)
+    c.wdtype = kw.get("wdtype", VLA_BF16)
+    c.act_dtype = kw.get("act_dtype", c.wdtype)
+    c.ffn_kind = VLA_SWIGLU
+    c.block_tokens = kw.get("block_tokens", 16)
+    c.num_blocks = kw["num_blocks"]
+    c.max_frames = kw["max_frames"]
+    c.max_chunk = kw["max_chunk"]
+    c.seed = kw["seed"]
+    c.init_std = kw.get("init_std", 0.02)
+    return c
+
+
+def preset(name: str, **overrides) -> vla_config:
+    kw = dict(PRESETS[name])
+    kw.update(overrides)
+    return make_config(**kw)
+
+
+class Model:
+    """Owns one handle; methods forward to the C entry points of the same names."""
+
+    def __init__(self, cfg: vla_config):
+        self.cfg = cfg
+        self.h = vla_model_create(cfg)
+
+    def close(self):
+        if self.h:
+            vla_model_destroy(self.h)
+            self.h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def prefill_chunk(self, tokens=None, embeds=None, n=0, stream=None):
+        return vla_prefill_chunk(self.h, tokens, embeds, n, stream)
+
+    def decode_step(self, token, stream=None, want_token=True):
+        return vla_decode_step(self.h, token, stream, want_token)
+
+    def kv_score_and_evict(self, layer=0, stream=None):
+        return vla_kv_score_and_evict(self.h, layer, stream)
+
+    def kv_score(self, layer=0, stream=None):
+        return vla_kv_score(self.h, layer, stream)
+
+    def logits_out(self, out, stream=None):
+        vla_logits_out(self.h, out, self.cfg.vocab, stream)
+
+    def kv_append_raw(self, k, v, n, stream=None):
+        return vla_kv_append_raw(self.h, k, v, n, stream)
+
+    def kv_rollback(self, keep_frame_id):
+        vla_kv_rollback(self.h, keep_frame_id)
+
+    def kv_refresh_mean_keys(self, stream=None):
+        vla_kv_refresh_mean_keys(self.h, stream)
+
+    def state(self):
+        return vla_get_state(self.h)
+
+    def block_table(self):
+        return vla_kv_block_table(self.h)
+
+    def frames(self):
+        return vla_kv_frames(self.h)
+
+    def mean_keys(self, layer, stream=None):
+        return vla_mean_keys_out(self.h, layer, self.cfg.max_frames,
+                                 self.cfg.n_kv_heads * self.cfg.head_dim, stream)
+
+    def kv_gather(self, layer, k_out, v_out, cap_tokens, stream=None):
+        return vla_kv_gather(self.h, layer, k_out, v_out, cap_tokens, stream)
+
+    def weight_out(self, kind, layer, out, nbytes, stream=None):
+        vla_weight_out(self.h, kind, layer, out, nbytes, stream)
+
+    def profile_enable(self, kernel_class):
+        vla_profile_enable(self.h, K_CLASSES.get(kernel_class, kernel_class)
+                           if isinstance(kernel_class, str) else kernel_class)
+
+    def profile_read(self):
+        return vla_profile_read(self.h)
