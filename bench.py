@@ -1,0 +1,372 @@
+#!/usr/bin/env python3
+"""Benchmark of the KV-cached GQA decoder hot path on one MI355X.
+
+One step is one frame step of the Qwen2.5-1.5B-shaped decoder (28 layers,
+hidden 1536, 12 query heads, 2 KV heads, head dim 128, SwiGLU 8960, vocab
+151936, bf16) with a 1024-token context already cached in 16-token blocks:
+
+  1. roll the cache back to the 1024-token context (host bookkeeping only);
+  2. prefill a 256-token visual chunk (N(0,1) embeddings, resident in HBM);
+  3. 16 greedy decode steps (each returns its next token to the host);
+  4. score the resident frames on layer 0 (fp64 mean keys, all-pairs cosine).
+
+Printed: one JSON line. ``value`` is the prefill throughput in tokens/s
+(HIP events around the prefill calls of the timed steps); ``ms_per_step`` is
+the wall time of a whole frame step. ``phases`` holds the decode-step latency,
+the frame-step time, the eviction leg (semantic eviction workload: 128 cached
+frames of 64 tokens, 32 score-and-evict cycles each followed by a 64-token
+prefill) and roofline fractions. ``roofline`` covers the dominant kernel (the
+decode gate/up projection); ``cpu_baseline`` times the CPU oracle on a bounded
+sample of the same prefill.
+
+Usage: python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "prefill tok/s + decode ms/step at Qwen2.5-1.5B shape; % MFMA/HBM peak"
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, published
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
+
+# Qwen2.5-1.5B-shaped decoder
+L, H, HQ, HKV, D, F, V = 28, 1536, 12, 2, 128, 8960, 151936
+CONTEXT, CHUNK, DECODES = 1024, 256, 16
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+# ---------------------------------------------------------------------------
+# algorithmic work (weights-only GEMM traffic plus KV reads; FLOPs of the GEMMs
+# and the attention products)
+# ---------------------------------------------------------------------------
+def layer_weight_params():
+    return (HQ + 2 * HKV) * D * H + H * HQ * D + 2 * F * H + H * F
+
+
+def prefill_flops(n=CHUNK, ctx=CONTEXT):
+    lin = 2 * n * layer_weight_params() * L + 2 * V * H          # last row through W_Y
+    # q.k and p.v over the visible keys: ctx + causal part of the chunk
+    keys = n * ctx + n * (n + 1) // 2
+    attn = L * HQ * 2 * 2 * D * keys
+    return lin + attn
+
+
+def decode_bytes(ctx_tokens):
+    w = 2 * (layer_weight_params() * L + V * H)
+    kv = L * 2 * HKV * D * 2 * ctx_tokens
+    return w + kv
+
+
+def gateup_bytes():
+    # the decode gate/up projection: both weight matrices, the input row, the gated output
+    return 2 * F * H * 2 + H * 2 + F * 2
+
+
+def file_sha(path):
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def read_traffic(kernel_src):
+    """HBM traffic per launch of the gate/up GEMV from the committed counter summary,
+    or None when the summary is missing or the kernel source changed since."""
+    path = os.path.join(ROOT, "profiles", "gemv_gateup_qwen1p5b_decode_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    txt = open(path).read()
+    m_sha = re.search(r"^kernel_source_sha256_16:\s*(\S+)", txt, re.M)
+    m_b = re.search(r"^hbm_bytes_per_launch:\s*([0-9.eE+]+)", txt, re.M)
+    if not m_sha or not m_b or m_sha.group(1) != file_sha(kernel_src):
+        return None
+    return float(m_b.group(1))
+
+
+# ---------------------------------------------------------------------------
+def gpu_leg(args):
+    import numpy as np
+    import torch
+
+    import kv_cached_gqa_decoder_amd as vla
+    import synth
+
+    torch.cuda.set_device(0)
+    stream = torch.cuda.current_stream()
+    sh = stream.cuda_stream
+    p = vla.PRESETS["c2_qwen1p5b_bf16"]
+    log(f"[bench] creating the Qwen2.5-1.5B-shaped model (seed {p['seed']})")
+    m = vla.Model(vla.make_config(**p))
+    # context: 1024 uniform ids, prefilled untimed in 4 chunks of 256
+    ctx_fid = -1
+    for c in range(CONTEXT // CHUNK):
+        ids = synth.token_ids(p["seed"], c, CHUNK, V)
+        ctx_fid = m.prefill_chunk(tokens=ids, stream=sh)
+    _, xs = synth.embeddings(p["seed"], 0, CHUNK, H, "bf16")
+    chunk = torch.from_numpy(np.ascontiguousarray(xs).view(np.int16)).view(torch.bfloat16).cuda()
+    torch.cuda.synchronize()
+
+    def step(ev=None):
+        m.kv_rollback(ctx_fid)
+        if ev:
+            ev[0].record(stream)
+        m.prefill_chunk(embeds=chunk, n=CHUNK, stream=sh)
+        if ev:
+            ev[1].record(stream)
+        tok = m.decode_step(1, stream=sh)
+        for _ in range(DECODES - 1):
+            tok = m.decode_step(tok, stream=sh)
+        if ev:
+            ev[2].record(stream)
+        m.kv_score(0, stream=sh)
+        if ev:
+            ev[3].record(stream)
+
+    log(f"[bench] warmup {args.warmup} steps")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    m.profile_enable("gemv_gateup")
+    log(f"[bench] timing {args.steps} steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    gu_ms, gu_n = m.profile_read()
+    m.profile_enable(0)
+
+    pre = [e[0].elapsed_time(e[1]) for e in evs]
+    dec = [e[1].elapsed_time(e[2]) / DECODES for e in evs]
+    sco = [e[2].elapsed_time(e[3]) for e in evs]
+    pre_ms = statistics.mean(pre)
+    dec_ms = statistics.mean(dec)
+
+    # per-decode-step latency distribution (separate short pass, events per step)
+    m.kv_rollback(ctx_fid)
+    m.prefill_chunk(embeds=chunk, n=CHUNK, stream=sh)
+    de = [torch.cuda.Event(enable_timing=True) for _ in range(DECODES + 1)]
+    tok = 1
+    de[0].record(stream)
+    for i in range(DECODES):
+        tok = m.decode_step(tok, stream=sh)
+        de[i + 1].record(stream)
+    torch.cuda.synchronize()
+    per_dec = [de[i].elapsed_time(de[i + 1]) for i in range(DECODES)]
+    m.close()
+    del chunk
+    torch.cuda.synchronize()
+
+    ev_leg = eviction_leg(args) if not args.no_eviction else None
+
+    fl = prefill_flops()
+    dbytes = decode_bytes(CONTEXT + CHUNK + DECODES // 2)
+    gu_avg = gu_ms / max(gu_n, 1)
+    gu_gbs = gateup_bytes() / (gu_avg * 1e-3) / 1e9
+    kernel_src = os.path.join(ROOT, "kv_cached_gqa_decoder_amd", "csrc", "gemv.hip")
+    traffic = read_traffic(kernel_src)
+    res = {
+        "metric": METRIC,
+        "value": round(CHUNK / (pre_ms * 1e-3), 1),
+        "unit": "tok/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall * 1e3 / args.steps, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded random-init weights N(0,0.02); uniform context ids; "
+                "N(0,1) visual-token embeddings)",
+        "config": {
+            "workload": "Qwen2.5-1.5B-shaped GQA decoder frame step: 1024-token cached context, "
+                        "256-token visual-chunk prefill, 16 greedy decode steps, layer-0 frame "
+                        "scoring; batch 1, 16-token KV blocks",
+            "layers": L, "hidden": H, "q_heads": HQ, "kv_heads": HKV, "head_dim": D,
+            "ffn": F, "vocab": V, "context": CONTEXT, "chunk": CHUNK, "decode_steps": DECODES,
+            "batch": 1, "parallelism": "single GPU",
+        },
+        "phases": {
+            "prefill_ms": round(pre_ms, 4),
+            "prefill_tok_s": round(CHUNK / (pre_ms * 1e-3), 1),
+            "prefill_mfma_frac": round(fl / (pre_ms * 1e-3) / (PEAK_BF16_TFLOPS * 1e12), 4),
+            "prefill_flop": fl,
+            "decode_ms_per_step": round(dec_ms, 4),
+            "decode_ms_per_step_median": round(statistics.median(per_dec), 4),
+            "decode_ms_per_step_max": round(max(per_dec), 4),
+            "decode_hbm_frac": round(dbytes / (dec_ms * 1e-3) / (PEAK_HBM_GBS * 1e9), 4),
+            "decode_bytes_per_step": dbytes,
+            "frame_step_ms": round(pre_ms + DECODES * dec_ms, 4),
+            "frame_budget_ms": 33.0,
+            "score_ms": round(statistics.mean(sco), 4),
+        },
+        "roofline": {
+            "kernel": "gemv gate/up + SwiGLU (decode)",
+            "bound": "hbm",
+            "achieved": round(gu_gbs, 1),
+            "peak": PEAK_HBM_GBS,
+            "unit": "GB/s",
+            "frac": round(gu_gbs / PEAK_HBM_GBS, 4),
+            "traffic": traffic,
+            "algorithmic_bytes_per_launch": gateup_bytes(),
+            "avg_launch_us": round(gu_avg * 1e3, 3),
+            "launches": gu_n,
+        },
+    }
+    if ev_leg:
+        res["phases"].update(ev_leg)
+    return res
+
+
+def eviction_leg(args):
+    """Semantic eviction workload: 128 raw frames of 64 tokens (layer-0 keys clustered
+    around 16 centres, sigma 0.1), 512-block budget, 32 cycles of score-and-evict followed
+    by a 64-token prefill of N(0,1) embeddings; plus a full mean-key refresh."""
+    import numpy as np
+    import torch
+
+    import kv_cached_gqa_decoder_amd as vla
+    import synth
+
+    stream = torch.cuda.current_stream()
+    sh = stream.cuda_stream
+    p = vla.PRESETS["c3_semantic_eviction"]
+    log("[bench] eviction leg: creating the model and 128 raw frames")
+    m = vla.Model(vla.make_config(**p))
+    for f in range(128):
+        _, (ks, vs) = synth.clustered_frame(p["seed"], f, L, 64, HKV, D)
+        kt = torch.from_numpy(ks.view(np.int16)).view(torch.bfloat16).cuda()
+        vt = torch.from_numpy(vs.view(np.int16)).view(torch.bfloat16).cuda()
+        m.kv_append_raw(kt, vt, 64, stream=sh)
+    embeds = []
+    for c in range(32):
+        _, xs = synth.embeddings(p["seed"], c, 64, H, "bf16")
+        embeds.append(torch.from_numpy(xs.view(np.int16)).view(torch.bfloat16).cuda())
+    torch.cuda.synchronize()
+    sc_us, pf_ms = [], []
+    for c in range(32):
+        t0 = time.perf_counter()
+        m.kv_score_and_evict(0, stream=sh)          # synchronises (returns the frame id)
+        sc_us.append((time.perf_counter() - t0) * 1e6)
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        m.prefill_chunk(embeds=embeds[c], n=64, stream=sh)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        pf_ms.append(e0.elapsed_time(e1))
+    # device time of the scoring kernels alone
+    m.profile_enable("score")
+    for _ in range(10):
+        m.kv_score(0, stream=sh)
+    s_ms, s_n = m.profile_read()
+    # full refresh of every frame's mean keys on all 28 layers (reads the whole key cache)
+    m.profile_enable("meankeys")
+    for _ in range(5):
+        m.kv_refresh_mean_keys(stream=sh)
+    r_ms, r_n = m.profile_read()
+    m.profile_enable(0)
+    m.close()
+    torch.cuda.synchronize()
+    refresh_bytes = L * 128 * 64 * HKV * D * 2
+    r_avg = r_ms / max(r_n, 1)
+    return {
+        "evict_score_us_median": round(statistics.median(sc_us), 2),
+        "evict_score_kernel_us": round(s_ms / max(s_n, 1) * 1e3, 2),
+        "evict_cycle_prefill64_ms_median": round(statistics.median(pf_ms), 4),
+        "meankey_refresh_us": round(r_avg * 1e3, 2),
+        "meankey_refresh_gbs": round(refresh_bytes / (r_avg * 1e-3) / 1e9, 1),
+        "meankey_refresh_hbm_frac": round(refresh_bytes / (r_avg * 1e-3) / (PEAK_HBM_GBS * 1e9), 4),
+    }
+
+
+# ---------------------------------------------------------------------------
+def cpu_baseline(layers_sample: int):
+    """The oracle (fp64 numpy) on a bounded sample of the prefill: the same 1024-token
+    context and 256-token chunk, through the first `layers_sample` of the 28 layers, then
+    the output head on the last row; scaled per layer to 28 layers for tokens/s."""
+    import numpy as np
+
+    import synth
+    from oracle import decoder as D_
+    from oracle import rng
+
+    if not rng.have_c():
+        from oracle import build as ob
+        ob.build()
+    try:
+        import threadpoolctl
+        threads = max(i["num_threads"] for i in threadpoolctl.threadpool_info()
+                      if i.get("user_api") == "blas")
+    except Exception:
+        threads = len(os.sched_getaffinity(0))
+    cfg = D_.C2.with_(n_layers=layers_sample)
+    log(f"[bench] cpu baseline: oracle, {layers_sample} of {L} layers, {threads} BLAS threads")
+    sess = D_.Session(cfg)
+    for c in range(CONTEXT // CHUNK):
+        sess.prefill_chunk(tokens=synth.token_ids(cfg.seed, c, CHUNK, V))
+    x32, _ = synth.embeddings(cfg.seed, 0, CHUNK, H, "bf16")
+    ctx_fid = sess.frames()[-1].frame_id
+    runs = []
+    for _ in range(3):
+        sess.rollback(ctx_fid)
+        t0 = time.perf_counter()
+        sess.prefill_chunk(embeds=x32)
+        runs.append(time.perf_counter() - t0)
+    t_all = statistics.median(runs)
+    h = np.asarray(x32[-1], dtype=np.float64)
+    t0 = time.perf_counter()
+    sess._logits(h)
+    t_head = time.perf_counter() - t0
+    per_layer = (t_all - t_head) / layers_sample
+    est = per_layer * L + t_head
+    return {
+        "value": round(CHUNK / est, 3),
+        "unit": "tok/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": f"256-token chunk prefill over a 1024-token cached context through "
+                  f"{layers_sample} of {L} layers plus the output head (median of 3: "
+                  f"{t_all:.2f} s); scaled per layer to {L} layers: est. {est:.2f} s",
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-eviction", action="store_true")
+    ap.add_argument("--cpu-layers", type=int, default=2)
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the decoder's hot path here runs on a single "
+              "MI355X (no multi-GPU path is built); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+    res = gpu_leg(args)
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(args.cpu_layers)
+    else:
+        res["cpu_baseline"] = None
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()
