@@ -201,10 +201,13 @@ vla_status vla_kv_gather(vla_model* m, int32_t layer, void* k_out, void* v_out,
 vla_status vla_weight_out(vla_model* m, int32_t kind, int32_t layer, void* out, int64_t bytes,
                           void* stream);
 
-/* Kernel timing with HIP events on the launch stream. When enabled for a
- * kernel class, each launch of that class is bracketed by an event pair;
- * vla_profile_read synchronises and returns the summed duration (ms) and
- * launch count since the last enable. Classes: see VLA_K_* below. */
+/* Kernel timing with HIP events. While a kernel class is enabled, every
+ * kernel that a call of that class launches carries a start/stop event pair
+ * in its own dispatch on the launch stream (so the span is the kernel's
+ * execution, as a kernel trace reports it). vla_profile_read synchronises and
+ * returns the summed kernel time (ms) and the number of profiled calls since
+ * the last enable (a call of VLA_K_SCORE launches two kernels; every other
+ * class one). VLA_K_NONE disables. Errors: VLA_E_INVALID (bad class). */
 enum {
   VLA_K_NONE = 0, VLA_K_GEMV_QKV = 1, VLA_K_GEMV_O = 2, VLA_K_GEMV_GATEUP = 3,
   VLA_K_GEMV_DOWN = 4, VLA_K_GEMV_HEAD = 5, VLA_K_ATTN_DECODE = 6, VLA_K_GEMM_QKV = 7,

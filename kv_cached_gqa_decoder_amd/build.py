@@ -28,6 +28,8 @@ def hipcc() -> str:
 
 def _flags():
     return ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC",
+            # a variable read in its own initialiser is undefined behaviour: refuse to build
+            "-Wall", "-Werror=uninitialized", "-Werror=shadow",
             # packed fp32 instructions are kept out of every kernel
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
             "-I", os.path.join(HERE, "..", "include")]

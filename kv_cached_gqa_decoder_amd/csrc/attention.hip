@@ -5,24 +5,39 @@
 // ("Rebuilding Kshipra Around Memory", section 4), computed as an online
 // softmax (m, l, o) over KV blocks read in place from the pool (same section).
 //
-// bf16 path (matrix cores). One wavefront owns (KV head, 16 query rows, key
-// split). Query rows are (token, q head of the group) pairs, so the g heads
-// sharing a KV head consume each K/V block together and a block is read once
-// per KV-head group rather than once per query head. Per 32-key step:
-//   S^T = K Q^T        v_mfma_f32_16x16x32_bf16, A = 16 keys x 32 dims (K rows,
-//                      contiguous), B = Q^T held in registers for the whole loop;
-//                      the accumulator gives each lane 4 keys of one query.
-//   online softmax     per query column: in-lane max/sum + 2 cross-lane steps.
-//   O^T += V^T P^T     A = V^T (the pool stores V transposed inside a block, so a
-//                      lane reads 4 consecutive keys of one dimension), B = P^T,
-//                      which is exactly the lane's own probabilities: P never
-//                      leaves registers.
-// With several key splits each wavefront writes (o, m, l) and a merge kernel
-// combines the splits deterministically in split order.
+// bf16 path (matrix cores). Query rows are (token, q head of the group) pairs,
+// so the g heads sharing a KV head consume each K/V block together and a block
+// is read once per KV-head group rather than once per query head. One 16-row
+// tile is one wavefront's set of query columns. Per 32-key step (two blocks):
+//   S^T = K Q^T        v_mfma_f32_16x16x32_bf16, A = 16 keys x 32 dims (K rows),
+//                      B = Q^T held in registers for the whole loop; the
+//                      accumulator gives each lane 4 keys of one query.
+//   online softmax     per query column: in-lane max/sum + 2 cross-lane steps,
+//                      in base 2 (scores pre-multiplied by log2 e / sqrt(d)).
+//   O^T += V^T P^T     A = V^T (the pool stores V transposed inside a block, so
+//                      4 consecutive keys of one dimension are contiguous),
+//                      B = P^T, which is exactly the lane's own probabilities.
+// Two workgroup shapes (4 wavefronts each):
+//   key split (decode, <= 16 query rows): the 4 wavefronts share one row tile
+//     and take interleaved block pairs straight from memory; their partial
+//     (m, l, o) are merged through LDS.
+//   row tiles (prefill): each wavefront owns 16 rows; the workgroup stages each
+//     block pair in LDS once (double buffered) for all 64 rows.
+// The resident blocks are split over workgroups (split-K). Each workgroup
+// writes its partial (m, l, o); the last one to finish (an agent-scope ticket
+// counter) merges all splits in split order, so the result does not depend on
+// which workgroup finished last, and resets the counter for the next launch.
+#include <algorithm>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
 namespace vla {
+
+constexpr int kAttnWaves = 4;
+constexpr int kMaxSplitsKey = 128;  // key-split shape: 16 rows per workgroup
+constexpr int kMaxSplitsRow = 32;   // row-tile shape: 64 rows per workgroup
+constexpr float kLog2e = 1.4426950408889634f;
 
 __device__ __forceinline__ bool key_visible(const AttnArgs& a, int b, int slot, int ntok, int tq) {
   if (slot >= ntok) return false;
@@ -31,162 +46,381 @@ __device__ __forceinline__ bool key_visible(const AttnArgs& a, int b, int slot, 
   return ck <= tq;
 }
 
-template <int D>
-__global__ __launch_bounds__(256) void attn_bf16_kernel(AttnArgs a, int rtiles) {
-  const int last_ntok = a.last_ntok;
-  const int lane = threadIdx.x & 63;
-  const int unit = blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int hkv = a.g.hkv;
-  if (unit >= hkv * rtiles * a.splits) return;
-  const int split = unit % a.splits;
-  const int rest = unit / a.splits;
-  const int rt = rest % rtiles;
-  const int kvh = rest / rtiles;
-  const int grp = a.hq / hkv;
-  const int R = a.n * grp;
-  const int jq = lane >> 4;   // lane group: 4 keys / dims per lane
-  const int cq = lane & 15;   // this lane's query column / key row / dim row
+__device__ __forceinline__ int block_ntok(const AttnArgs& a, int b) {
+  return b == a.nlb - 1 ? a.last_ntok : a.blk_ntok[b];
+}
 
-  // query column of this lane
-  const int r = rt * 16 + cq;
-  const bool qvalid = r < R;
-  const int tq = qvalid ? r / grp : 0;
-  const int hq = kvh * grp + (qvalid ? r % grp : 0);
-  const bf16_t* qrow = (const bf16_t*)a.q + ((size_t)tq * a.hq + hq) * D;
-  bf16x8_t qf[D / 32];
+// Operands of one 32-key step held by a lane: K rows (A of S^T = K Q^T) for the
+// two blocks, and V^T rows (A of O^T += V^T P^T), 8 keys per lane in the order
+// {block 0 keys 4jq..4jq+3, block 1 keys 4jq..4jq+3}.
+template <int D>
+struct PairFrags {
+  bf16x8_t k0[D / 32], k1[D / 32];
+  bf16x8_t v[D / 16];
+};
+
+template <int D>
+struct SoftmaxState {
+  float m, l;        // running max (base 2) and sum of the query column
+  f32x4_t o[D / 16]; // O^T[dim dt*16 + 4jq + e][column]
+};
+
+template <int D>
+__device__ __forceinline__ void state_init(SoftmaxState<D>& st) {
+  st.m = -INFINITY;
+  st.l = 0.f;
+#pragma unroll
+  for (int i = 0; i < D / 16; ++i) st.o[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+}
+
+// one online-softmax step over blocks b (and b+1 when has1) for query column (tq)
+template <int D>
+__device__ __forceinline__ void attn_step(const AttnArgs& a, SoftmaxState<D>& st,
+                                          const bf16x8_t* qf, const PairFrags<D>& f, int b,
+                                          bool has1, int tq, int jq, float sl2) {
+  f32x4_t s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int ds = 0; ds < D / 32; ++ds) {
-    u32x4_t v = qvalid ? *(const u32x4_t*)(qrow + ds * 32 + 8 * jq) : u32x4_t{0, 0, 0, 0};
-    qf[ds] = __builtin_bit_cast(bf16x8_t, v);
+    s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f.k0[ds], qf[ds], s0, 0, 0, 0);
+    s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f.k1[ds], qf[ds], s1, 0, 0, 0);
   }
+  const int nt0 = block_ntok(a, b);
+  const int nt1 = has1 ? block_ntok(a, b + 1) : 0;
+  float p0[4], p1[4];
+  float mx = -INFINITY;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int ks = 4 * jq + e;
+    p0[e] = key_visible(a, b, ks, nt0, tq) ? s0[e] * sl2 : -INFINITY;
+    p1[e] = (has1 && key_visible(a, b + 1, ks, nt1, tq)) ? s1[e] * sl2 : -INFINITY;
+    mx = fmaxf(mx, fmaxf(p0[e], p1[e]));
+  }
+  mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+  mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+  const float m_new = fmaxf(st.m, mx);
+  const float m_use = m_new == -INFINITY ? 0.f : m_new;
+  const float alpha = st.m == -INFINITY ? 0.f : exp2f(st.m - m_use);
+  // probabilities rounded to bf16 once; the sum uses the rounded values
+  u32x4_t pw;
+  float sum = 0.f;
+#pragma unroll
+  for (int e = 0; e < 2; ++e) {
+    const bf16_t a0 = f32_to_bf16(exp2f(p0[2 * e] - m_use));
+    const bf16_t a1 = f32_to_bf16(exp2f(p0[2 * e + 1] - m_use));
+    const bf16_t b0 = f32_to_bf16(exp2f(p1[2 * e] - m_use));
+    const bf16_t b1 = f32_to_bf16(exp2f(p1[2 * e + 1] - m_use));
+    sum += bf16_to_f32(a0) + bf16_to_f32(a1) + bf16_to_f32(b0) + bf16_to_f32(b1);
+    pw[e] = (uint32_t)a0 | ((uint32_t)a1 << 16);
+    pw[2 + e] = (uint32_t)b0 | ((uint32_t)b1 << 16);
+  }
+  sum += __shfl_xor(sum, 16, 64);
+  sum += __shfl_xor(sum, 32, 64);
+  st.l = st.l * alpha + sum;
+  st.m = m_new;
+  const bf16x8_t pf = __builtin_bit_cast(bf16x8_t, pw);
+#pragma unroll
+  for (int dt = 0; dt < D / 16; ++dt) {
+    st.o[dt] *= alpha;
+    st.o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f.v[dt], pf, st.o[dt], 0, 0, 0);
+  }
+}
 
-  const int bps = (a.nlb + a.splits - 1) / a.splits;
-  const int b_begin = split * bps;
-  const int b_end = min(a.nlb, b_begin + bps);
-
+// operands of blocks (b, b+1) straight from the pool (key-split shape)
+template <int D>
+__device__ __forceinline__ void load_pair_global(const AttnArgs& a, PairFrags<D>& f, int b,
+                                                 bool has1, int kvh, int cq, int jq) {
   const bf16_t* kp = (const bf16_t*)a.kpool;
   const bf16_t* vp = (const bf16_t*)a.vpool;
-  float m_run = -INFINITY, l_run = 0.f;
-  f32x4_t o[D / 16];
+  const int pb0 = a.blk_table[b];
+  const int pb1 = has1 ? a.blk_table[b + 1] : pb0;
+  const bf16_t* k0 = kp + a.g.kidx(a.layer, pb0, kvh, cq, 0) + 8 * jq;
+  const bf16_t* k1 = kp + a.g.kidx(a.layer, pb1, kvh, cq, 0) + 8 * jq;
 #pragma unroll
-  for (int i = 0; i < D / 16; ++i) o[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
-  for (int b = b_begin; b < b_end; b += 2) {
-    const bool has1 = b + 1 < b_end;
-    const int pb0 = a.blk_table[b];
-    const int pb1 = has1 ? a.blk_table[b + 1] : pb0;
-    const int nt0 = (b == a.nlb - 1) ? last_ntok : a.blk_ntok[b];
-    const int nt1 = has1 ? ((b + 1 == a.nlb - 1) ? last_ntok : a.blk_ntok[b + 1]) : 0;
-
-    f32x4_t s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
-    const bf16_t* k0 = kp + a.g.kidx(a.layer, pb0, kvh, cq, 0);
-    const bf16_t* k1 = kp + a.g.kidx(a.layer, pb1, kvh, cq, 0);
-#pragma unroll
-    for (int ds = 0; ds < D / 32; ++ds) {
-      const bf16x8_t kf0 = __builtin_bit_cast(bf16x8_t, *(const u32x4_t*)(k0 + ds * 32 + 8 * jq));
-      const bf16x8_t kf1 = __builtin_bit_cast(bf16x8_t, *(const u32x4_t*)(k1 + ds * 32 + 8 * jq));
-      s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf0, qf[ds], s0, 0, 0, 0);
-      s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf1, qf[ds], s1, 0, 0, 0);
-    }
-    // lane holds S^T[key 4*jq+e][query cq] for block b (s0) and block b+1 (s1)
-    float p0[4], p1[4];
-    float mx = -INFINITY;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int ks = 4 * jq + e;
-      p0[e] = key_visible(a, b, ks, nt0, tq) ? s0[e] * a.scale : -INFINITY;
-      p1[e] = (has1 && key_visible(a, b + 1, ks, nt1, tq)) ? s1[e] * a.scale : -INFINITY;
-      mx = fmaxf(mx, fmaxf(p0[e], p1[e]));
-    }
-    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    const float m_new = fmaxf(m_run, mx);
-    const float m_use = m_new == -INFINITY ? 0.f : m_new;
-    const float alpha = m_run == -INFINITY ? 0.f : __expf(m_run - m_use);
-    float sum = 0.f;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      p0[e] = __expf(p0[e] - m_use);
-      p1[e] = __expf(p1[e] - m_use);
-      sum += p0[e] + p1[e];
-    }
-    sum += __shfl_xor(sum, 16, 64);
-    sum += __shfl_xor(sum, 32, 64);
-    l_run = l_run * alpha + sum;
-    m_run = m_new;
-
-    u32x4_t pw;
-#pragma unroll
-    for (int e = 0; e < 2; ++e) {
-      pw[e] = (uint32_t)f32_to_bf16(p0[2 * e]) | ((uint32_t)f32_to_bf16(p0[2 * e + 1]) << 16);
-      pw[2 + e] = (uint32_t)f32_to_bf16(p1[2 * e]) | ((uint32_t)f32_to_bf16(p1[2 * e + 1]) << 16);
-    }
-    const bf16x8_t pf = __builtin_bit_cast(bf16x8_t, pw);
-    const bf16_t* v0 = vp + a.g.vidx(a.layer, pb0, kvh, 4 * jq, 0);
-    const bf16_t* v1 = vp + a.g.vidx(a.layer, pb1, kvh, 4 * jq, 0);
-#pragma unroll
-    for (int dt = 0; dt < D / 16; ++dt) {
-      o[dt] *= alpha;
-      const int dim = dt * 16 + cq;
-      const u32x2_t lo = *(const u32x2_t*)(v0 + (size_t)dim * a.g.bt);
-      const u32x2_t hi = has1 ? *(const u32x2_t*)(v1 + (size_t)dim * a.g.bt) : u32x2_t{0, 0};
-      const u32x4_t vv = {lo[0], lo[1], hi[0], hi[1]};
-      o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, vv), pf, o[dt],
-                                                      0, 0, 0);
-    }
+  for (int ds = 0; ds < D / 32; ++ds) {
+    f.k0[ds] = __builtin_bit_cast(bf16x8_t, *(const u32x4_t*)(k0 + ds * 32));
+    f.k1[ds] = __builtin_bit_cast(bf16x8_t, *(const u32x4_t*)(k1 + ds * 32));
   }
-  // lane holds O^T[dim dt*16 + 4*jq + e][query cq]
-  if (a.splits == 1) {
-    if (qvalid) {
-      const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
-      bf16_t* orow = (bf16_t*)a.out + ((size_t)tq * a.hq + hq) * D;
+  const bf16_t* v0 = vp + a.g.vidx(a.layer, pb0, kvh, 4 * jq, 0);
+  const bf16_t* v1 = vp + a.g.vidx(a.layer, pb1, kvh, 4 * jq, 0);
 #pragma unroll
-      for (int dt = 0; dt < D / 16; ++dt) {
-        u32x2_t w;
-        w[0] = (uint32_t)f32_to_bf16(o[dt][0] * inv) | ((uint32_t)f32_to_bf16(o[dt][1] * inv) << 16);
-        w[1] = (uint32_t)f32_to_bf16(o[dt][2] * inv) | ((uint32_t)f32_to_bf16(o[dt][3] * inv) << 16);
-        *(u32x2_t*)(orow + dt * 16 + 4 * jq) = w;
-      }
-    }
-  } else {
-    float* po = a.part_o + ((size_t)unit * 16 + cq) * D;
+  for (int dt = 0; dt < D / 16; ++dt) {
+    const size_t off = (size_t)(dt * 16 + cq) * a.g.bt;
+    const u32x2_t lo = *(const u32x2_t*)(v0 + off);
+    const u32x2_t hi = has1 ? *(const u32x2_t*)(v1 + off) : u32x2_t{0, 0};
+    f.v[dt] = __builtin_bit_cast(bf16x8_t, u32x4_t{lo[0], lo[1], hi[0], hi[1]});
+  }
+}
+
+// LDS image of one block pair (row-tile shape). K rows: [32 keys][D + 8];
+// V^T rows: [D][40], where dim i holds at 8jq + 4blk + e the key 4jq + e of block blk.
+template <int D>
+struct PairLds {
+  static constexpr int KP = D + 8;
+  static constexpr int VP = 40;
+  static constexpr int KELEMS = 32 * KP;
+  static constexpr int VELEMS = D * VP;
+  static constexpr int ELEMS = KELEMS + VELEMS;
+  static constexpr int KCH = 32 * D / 8;   // 16-byte chunks of K per pair
+  static constexpr int VCH = 2 * D * 2;    // 16-byte chunks of V per pair
+  static constexpr int CH = (KCH + VCH) / (kAttnWaves * 64);
+};
+
+template <int D>
+__device__ __forceinline__ void stage_load(const AttnArgs& a, u32x4_t* r, int b, bool has1,
+                                           int kvh) {
+  using P = PairLds<D>;
+  const bf16_t* kp = (const bf16_t*)a.kpool;
+  const bf16_t* vp = (const bf16_t*)a.vpool;
+  const int pb0 = a.blk_table[b];
+  const int pb1 = has1 ? a.blk_table[b + 1] : pb0;
 #pragma unroll
-    for (int dt = 0; dt < D / 16; ++dt) *(f32x4_t*)(po + dt * 16 + 4 * jq) = o[dt];
-    if (jq == 0) {
-      a.part_ml[(size_t)unit * 32 + cq] = m_run;
-      a.part_ml[(size_t)unit * 32 + 16 + cq] = l_run;
+  for (int i = 0; i < P::CH; ++i) {
+    const int c = threadIdx.x + i * kAttnWaves * 64;
+    if (c < P::KCH) {
+      const int blk = c / (16 * D / 8);
+      const int row = (c / (D / 8)) % 16;
+      const int col8 = c % (D / 8);
+      r[i] = *(const u32x4_t*)(kp + a.g.kidx(a.layer, blk ? pb1 : pb0, kvh, row, col8 * 8));
+    } else {
+      const int cv = c - P::KCH;
+      const int blk = cv / (2 * D);
+      const int dim = (cv % (2 * D)) / 2;
+      const int h = cv % 2;
+      r[i] = (blk && !has1) ? u32x4_t{0, 0, 0, 0}
+                            : *(const u32x4_t*)(vp + a.g.vidx(a.layer, blk ? pb1 : pb0, kvh,
+                                                               8 * h, dim));
     }
   }
 }
 
-// combine the splits of one (KV head, row tile): o = sum_s e^(m_s - M) o_s / sum_s e^(m_s - M) l_s
 template <int D>
-__global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a, int rtiles) {
-  const int tile = blockIdx.x;  // kvh * rtiles + rt
-  const int rt = tile % rtiles, kvh = tile / rtiles;
+__device__ __forceinline__ void stage_store(bf16_t* lds, const u32x4_t* r) {
+  using P = PairLds<D>;
+  bf16_t* Ks = lds;
+  bf16_t* Vs = lds + P::KELEMS;
+#pragma unroll
+  for (int i = 0; i < P::CH; ++i) {
+    const int c = threadIdx.x + i * kAttnWaves * 64;
+    if (c < P::KCH) {
+      const int blk = c / (16 * D / 8);
+      const int row = (c / (D / 8)) % 16;
+      const int col8 = c % (D / 8);
+      *(u32x4_t*)(Ks + (blk * 16 + row) * P::KP + col8 * 8) = r[i];
+    } else {
+      const int cv = c - P::KCH;
+      const int blk = cv / (2 * D);
+      const int dim = (cv % (2 * D)) / 2;
+      const int h = cv % 2;
+      bf16_t* row = Vs + dim * P::VP + blk * 4;
+      *(u32x2_t*)(row + (2 * h) * 8) = u32x2_t{r[i][0], r[i][1]};
+      *(u32x2_t*)(row + (2 * h + 1) * 8) = u32x2_t{r[i][2], r[i][3]};
+    }
+  }
+}
+
+template <int D>
+__device__ __forceinline__ void load_pair_lds(const bf16_t* lds, PairFrags<D>& f, int cq, int jq) {
+  using P = PairLds<D>;
+  const bf16_t* Ks = lds;
+  const bf16_t* Vs = lds + P::KELEMS;
+#pragma unroll
+  for (int ds = 0; ds < D / 32; ++ds) {
+    f.k0[ds] = *(const bf16x8_t*)(Ks + cq * P::KP + ds * 32 + 8 * jq);
+    f.k1[ds] = *(const bf16x8_t*)(Ks + (16 + cq) * P::KP + ds * 32 + 8 * jq);
+  }
+#pragma unroll
+  for (int dt = 0; dt < D / 16; ++dt)
+    f.v[dt] = *(const bf16x8_t*)(Vs + (dt * 16 + cq) * P::VP + 8 * jq);
+}
+
+template <int D, bool KEYSPLIT>
+struct AttnShape {
+  static constexpr int ROWS = KEYSPLIT ? 16 : 16 * kAttnWaves;
+  static constexpr int MAXS = KEYSPLIT ? kMaxSplitsKey : kMaxSplitsRow;
+  // LDS: key split -> per-wave partials (4 x 16 x D fp32 + m, l); row tiles -> 2 pair images
+  static constexpr int LDS_BYTES =
+      KEYSPLIT ? kAttnWaves * 16 * (D + 2) * 4 : 2 * PairLds<D>::ELEMS * 2;
+};
+
+// partial layout: part_o[unit][ROWS][D], part_ml[unit][2][ROWS] with
+// unit = (kvh * rgroups + rg) * splits + split
+template <int D, bool KEYSPLIT>
+__global__ __launch_bounds__(256) void attn_bf16_kernel(AttnArgs a, int rgroups) {
+  using S = AttnShape<D, KEYSPLIT>;
+  constexpr int ROWS = S::ROWS;
+  __shared__ __attribute__((aligned(16))) unsigned char smem[S::LDS_BYTES];
+  __shared__ float mw[ROWS * S::MAXS];  // merge weights
+  __shared__ float linv[ROWS];
+  __shared__ int s_ticket;
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int split = blockIdx.x, rg = blockIdx.y, kvh = blockIdx.z;
+  const int splits = a.splits;
   const int grp = a.hq / a.g.hkv;
   const int R = a.n * grp;
-  for (int e = threadIdx.x; e < 16 * D; e += blockDim.x) {
-    const int c = e / D, dim = e % D;
-    const int r = rt * 16 + c;
-    if (r >= R) continue;
-    float M = -INFINITY;
-    for (int s = 0; s < a.splits; ++s)
-      M = fmaxf(M, a.part_ml[((size_t)tile * a.splits + s) * 32 + c]);
-    float L = 0.f, acc = 0.f;
-    if (M != -INFINITY) {
-      for (int s = 0; s < a.splits; ++s) {
-        const size_t u = (size_t)tile * a.splits + s;
-        const float m = a.part_ml[u * 32 + c];
-        if (m == -INFINITY) continue;
-        const float w = __expf(m - M);
-        L += w * a.part_ml[u * 32 + 16 + c];
-        acc += w * a.part_o[(u * 16 + c) * D + dim];
+  const int jq = lane >> 4, cq = lane & 15;
+  const float sl2 = a.scale * kLog2e;
+
+  const int wrow0 = rg * ROWS + (KEYSPLIT ? 0 : wave * 16);
+  const int r = wrow0 + cq;
+  const bool qvalid = r < R;
+  const int tq = qvalid ? r / grp : 0;
+  const int hq = kvh * grp + (qvalid ? r % grp : 0);
+  bf16x8_t qf[D / 32];
+  {
+    const bf16_t* qrow = (const bf16_t*)a.q + ((size_t)tq * a.hq + hq) * D;
+#pragma unroll
+    for (int ds = 0; ds < D / 32; ++ds) {
+      const u32x4_t v = qvalid ? *(const u32x4_t*)(qrow + ds * 32 + 8 * jq) : u32x4_t{0, 0, 0, 0};
+      qf[ds] = __builtin_bit_cast(bf16x8_t, v);
+    }
+  }
+
+  // blocks of this split; blocks past the workgroup's last causal key are skipped
+  const int bps = (a.nlb + splits - 1) / splits;
+  const int b_begin = split * bps;
+  int b_end = min(a.nlb, b_begin + bps);
+  {
+    const int rlast = min(R, rg * ROWS + ROWS) - 1;
+    const int tmax = rlast / grp;
+    b_end = min(b_end, a.cb0 + (tmax + a.cslot0) / a.g.bt + 1);
+  }
+
+  SoftmaxState<D> st;
+  state_init(st);
+  if constexpr (KEYSPLIT) {
+    PairFrags<D> cur, nxt;
+    int b = b_begin + 2 * wave;
+    if (b < b_end) load_pair_global(a, cur, b, b + 1 < b_end, kvh, cq, jq);
+    for (; b < b_end; b += 2 * kAttnWaves) {
+      const int bn = b + 2 * kAttnWaves;
+      if (bn < b_end) load_pair_global(a, nxt, bn, bn + 1 < b_end, kvh, cq, jq);
+      attn_step(a, st, qf, cur, b, b + 1 < b_end, tq, jq, sl2);
+      cur = nxt;
+    }
+    // merge the 4 wavefronts' states through LDS
+    float* Lo = (float*)smem;                       // [wave][16][D]
+    float* Lml = Lo + kAttnWaves * 16 * D;           // [wave][2][16]
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) Lo[(wave * 16 + cq) * D + dt * 16 + 4 * jq + e] = st.o[dt][e];
+    if (jq == 0) {
+      Lml[wave * 32 + cq] = st.m;
+      Lml[wave * 32 + 16 + cq] = st.l;
+    }
+    __syncthreads();
+    const int unit = (kvh * rgroups + rg) * splits + split;
+    for (int e = threadIdx.x; e < 16 * D; e += kAttnWaves * 64) {
+      const int c = e / D, dim = e % D;
+      float M = -INFINITY;
+#pragma unroll
+      for (int w = 0; w < kAttnWaves; ++w) M = fmaxf(M, Lml[w * 32 + c]);
+      float L = 0.f, acc = 0.f;
+      if (M != -INFINITY) {
+#pragma unroll
+        for (int w = 0; w < kAttnWaves; ++w) {
+          const float mw_ = Lml[w * 32 + c];
+          const float wt = mw_ == -INFINITY ? 0.f : exp2f(mw_ - M);
+          L += wt * Lml[w * 32 + 16 + c];
+          acc += wt * Lo[(w * 16 + c) * D + dim];
+        }
+      }
+      const int rr = rg * 16 + c;
+      if (splits == 1) {
+        if (rr < R)
+          ((bf16_t*)a.out)[((size_t)(rr / grp) * a.hq + kvh * grp + rr % grp) * D + dim] =
+              f32_to_bf16(L > 0.f ? acc / L : 0.f);
+      } else {
+        a.part_o[((size_t)unit * 16 + c) * D + dim] = acc;
+        if (dim == 0) {
+          a.part_ml[(size_t)unit * 32 + c] = M;
+          a.part_ml[(size_t)unit * 32 + 16 + c] = L;
+        }
       }
     }
-    const int t = r / grp, h = kvh * grp + r % grp;
-    ((bf16_t*)a.out)[((size_t)t * a.hq + h) * D + dim] = f32_to_bf16(L > 0.f ? acc / L : 0.f);
+  } else {
+    using P = PairLds<D>;
+    bf16_t* buf = (bf16_t*)smem;
+    u32x4_t rs[P::CH];
+    const int npairs = b_end > b_begin ? (b_end - b_begin + 1) / 2 : 0;
+    if (npairs > 0) {
+      stage_load<D>(a, rs, b_begin, b_begin + 1 < b_end, kvh);
+      stage_store<D>(buf, rs);
+    }
+    __syncthreads();
+    for (int p = 0; p < npairs; ++p) {
+      const int b = b_begin + 2 * p;
+      const bool more = p + 1 < npairs;
+      if (more) stage_load<D>(a, rs, b + 2, b + 3 < b_end, kvh);
+      PairFrags<D> f;
+      load_pair_lds<D>(buf + (p & 1) * P::ELEMS, f, cq, jq);
+      attn_step(a, st, qf, f, b, b + 1 < b_end, tq, jq, sl2);
+      if (more) stage_store<D>(buf + ((p + 1) & 1) * P::ELEMS, rs);
+      __syncthreads();
+    }
+    const int unit = (kvh * rgroups + rg) * splits + split;
+    if (splits == 1) {
+      if (qvalid) {
+        const float inv = st.l > 0.f ? 1.f / st.l : 0.f;
+        bf16_t* orow = (bf16_t*)a.out + ((size_t)tq * a.hq + hq) * D;
+#pragma unroll
+        for (int dt = 0; dt < D / 16; ++dt) {
+          u32x2_t w;
+          w[0] = (uint32_t)f32_to_bf16(st.o[dt][0] * inv) |
+                 ((uint32_t)f32_to_bf16(st.o[dt][1] * inv) << 16);
+          w[1] = (uint32_t)f32_to_bf16(st.o[dt][2] * inv) |
+                 ((uint32_t)f32_to_bf16(st.o[dt][3] * inv) << 16);
+          *(u32x2_t*)(orow + dt * 16 + 4 * jq) = w;
+        }
+      }
+    } else {
+      const int c = wave * 16 + cq;  // row inside the workgroup
+      float* po = a.part_o + ((size_t)unit * ROWS + c) * D;
+#pragma unroll
+      for (int dt = 0; dt < D / 16; ++dt) *(f32x4_t*)(po + dt * 16 + 4 * jq) = st.o[dt];
+      if (jq == 0) {
+        a.part_ml[(size_t)unit * 2 * ROWS + c] = st.m;
+        a.part_ml[(size_t)unit * 2 * ROWS + ROWS + c] = st.l;
+      }
+    }
   }
+  if (splits == 1) return;
+
+  // ---- the last workgroup of this (KV head, row group) merges the splits ----
+  __threadfence();
+  __syncthreads();
+  int* counter = a.counters + kvh * rgroups + rg;
+  if (threadIdx.x == 0)
+    s_ticket = __hip_atomic_fetch_add(counter, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
+  if (s_ticket != splits - 1) return;
+  __threadfence();
+  const size_t unit0 = (size_t)(kvh * rgroups + rg) * splits;
+  for (int c = threadIdx.x; c < ROWS; c += kAttnWaves * 64) {
+    float M = -INFINITY;
+    for (int s = 0; s < splits; ++s) M = fmaxf(M, a.part_ml[(unit0 + s) * 2 * ROWS + c]);
+    float L = 0.f;
+    for (int s = 0; s < splits; ++s) {
+      const float m = a.part_ml[(unit0 + s) * 2 * ROWS + c];
+      const float w = (m == -INFINITY) ? 0.f : exp2f(m - M);
+      mw[c * S::MAXS + s] = w;
+      L += w * a.part_ml[(unit0 + s) * 2 * ROWS + ROWS + c];
+    }
+    linv[c] = L > 0.f ? 1.f / L : 0.f;
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < ROWS * D; e += kAttnWaves * 64) {
+    const int c = e / D, dim = e % D;
+    const int rr = rg * ROWS + c;
+    if (rr >= R) continue;
+    float acc = 0.f;
+    for (int s = 0; s < splits; ++s)
+      acc += mw[c * S::MAXS + s] * a.part_o[((unit0 + s) * ROWS + c) * D + dim];
+    ((bf16_t*)a.out)[((size_t)(rr / grp) * a.hq + kvh * grp + rr % grp) * D + dim] =
+        f32_to_bf16(acc * linv[c]);
+  }
+  if (threadIdx.x == 0) *counter = 0;
 }
 
 // ---------------------------------------------------------------------------
@@ -243,26 +477,48 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(AttnArgs a) {
   }
 }
 
-template <int D>
-static void attn_bf16_launch(const AttnArgs& a, int rtiles, hipStream_t s) {
-  const int units = a.g.hkv * rtiles * a.splits;
-  attn_bf16_kernel<D><<<(units + 3) / 4, 256, 0, s>>>(a, rtiles);
-  if (a.splits > 1) attn_merge_kernel<D><<<a.g.hkv * rtiles, 256, 0, s>>>(a, rtiles);
+template <int D, bool KEYSPLIT>
+static void attn_bf16_launch(const AttnArgs& a, int rgroups, hipStream_t s) {
+  const dim3 grid(a.splits, rgroups, a.g.hkv);
+  launch_k(attn_bf16_kernel<D, KEYSPLIT>, grid, dim3(kAttnWaves * 64), 0, s, a, rgroups);
 }
 
-hipError_t launch_attention(const AttnArgs& a, int dt, hipStream_t s) {
-  if (a.nlb <= 0 || a.n <= 0) return hipErrorInvalidValue;
+template <int D>
+static void attn_bf16_dispatch(const AttnArgs& a, bool keysplit, int rgroups, hipStream_t s) {
+  if (keysplit) attn_bf16_launch<D, true>(a, rgroups, s);
+  else attn_bf16_launch<D, false>(a, rgroups, s);
+}
+
+hipError_t launch_attention(const AttnArgs& args, int dt, hipStream_t s) {
+  if (args.nlb <= 0 || args.n <= 0) return hipErrorInvalidValue;
   if (dt == DT_F32) {
-    if (a.nlb * a.g.bt > kF32MaxKeys) return hipErrorInvalidValue;
-    attn_f32_kernel<<<(a.n * a.hq + 3) / 4, 256, 0, s>>>(a);
+    if (args.nlb * args.g.bt > kF32MaxKeys) return hipErrorInvalidValue;
+    launch_k(attn_f32_kernel, dim3((args.n * args.hq + 3) / 4), dim3(256), 0, s, args);
     return hipGetLastError();
   }
-  if (a.splits > 1 && (a.part_o == nullptr || a.part_ml == nullptr)) return hipErrorInvalidValue;
-  const int rtiles = (a.n * (a.hq / a.g.hkv) + 15) / 16;
+  AttnArgs a = args;
+  // workgroup shape and split count: at least 8 blocks (4 pairs) per workgroup,
+  // about 4 (decode) or 2 (prefill) workgroups per CU at most, within the
+  // partial-buffer and counter capacities
+  const int R = a.n * (a.hq / a.g.hkv);
+  const bool keysplit = R <= 16;
+  const int rows = keysplit ? 16 : 16 * kAttnWaves;
+  const int rgroups = (R + rows - 1) / rows;
+  const int base = a.g.hkv * rgroups;
+  int splits = (a.nlb + 7) / 8;
+  splits = std::min(splits, std::max(1, (keysplit ? 1024 : 512) / base));
+  splits = std::min(splits, keysplit ? kMaxSplitsKey : kMaxSplitsRow);
+  splits = std::min(splits, std::max(1, a.part_rows / (base * rows)));
+  splits = std::max(splits, 1);
+  const int bps = (a.nlb + splits - 1) / splits;
+  a.splits = (a.nlb + bps - 1) / bps;
+  if (a.splits > 1 && (a.part_o == nullptr || a.part_ml == nullptr || a.counters == nullptr ||
+                       base > a.counter_cap || base * rows * a.splits > a.part_rows))
+    return hipErrorInvalidValue;
   switch (a.g.d) {
-    case 64: attn_bf16_launch<64>(a, rtiles, s); break;
-    case 128: attn_bf16_launch<128>(a, rtiles, s); break;
-    case 256: attn_bf16_launch<256>(a, rtiles, s); break;
+    case 64: attn_bf16_dispatch<64>(a, keysplit, rgroups, s); break;
+    case 128: attn_bf16_dispatch<128>(a, keysplit, rgroups, s); break;
+    case 256: attn_bf16_dispatch<256>(a, keysplit, rgroups, s); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

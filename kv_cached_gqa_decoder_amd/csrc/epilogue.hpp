@@ -20,8 +20,11 @@ __device__ __forceinline__ void epi_qkv_pair(const FwdCtx& c, int t, int col, fl
   const int j = (col % d) >> 1;
   const int hkv = c.g.hkv;
   if (head < c.hq + hkv) {
+    // angle in fp64, reduced to [-pi, pi] in fp64, then an fp32 sine/cosine
     const double ang = (double)(c.pos0 + t) * c.inv_freq[j];
-    const float cs = (float)cos(ang), sn = (float)sin(ang);
+    const double red = fma(-rint(ang * 0.15915494309189535), 6.283185307179586, ang);
+    float sn, cs;
+    sincosf((float)red, &sn, &cs);
     const float rlo = lo * cs - hi * sn;
     const float rhi = hi * cs + lo * sn;
     lo = rlo;

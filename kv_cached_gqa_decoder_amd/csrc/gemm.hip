@@ -210,15 +210,15 @@ template <int EPI>
 static hipError_t gemm_launch(const GemmArgs& a, int dt, hipStream_t s) {
   if (dt == DT_F32) {
     dim3 grid((a.N + 63) / 64, (a.M + 63) / 64);
-    gemm_f32_kernel<EPI><<<grid, 256, 0, s>>>(a);
+    launch_k(gemm_f32_kernel<EPI>, grid, dim3(256), 0, s, a);
   } else {
     if (a.K % kBK != 0 || a.N % 64 != 0) return hipErrorInvalidValue;
     if (a.M > 64) {
       dim3 grid(a.N / 64, (a.M + 127) / 128);
-      gemm_bf16_kernel<EPI, 128><<<grid, 256, 0, s>>>(a);
+      launch_k(gemm_bf16_kernel<EPI, 128>, grid, dim3(256), 0, s, a);
     } else {
       dim3 grid(a.N / 64, (a.M + 63) / 64);
-      gemm_bf16_kernel<EPI, 64><<<grid, 256, 0, s>>>(a);
+      launch_k(gemm_bf16_kernel<EPI, 64>, grid, dim3(256), 0, s, a);
     }
   }
   return hipGetLastError();

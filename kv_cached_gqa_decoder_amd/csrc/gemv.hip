@@ -133,7 +133,7 @@ static hipError_t gemv_launch(const GemvArgs& a, hipStream_t s, int* grid_out) {
   int grid = ngroups < 2048 ? ngroups : 2048;
   if (grid_out) *grid_out = grid;
   const size_t lds = (size_t)a.K * sizeof(float);
-  gemv_kernel<T, EPI><<<grid, kGemvThreads, lds, s>>>(a, ngroups);
+  launch_k(gemv_kernel<T, EPI>, dim3(grid), dim3(kGemvThreads), (uint32_t)lds, s, a, ngroups);
   return hipGetLastError();
 }
 

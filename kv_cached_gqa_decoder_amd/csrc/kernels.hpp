@@ -1,10 +1,30 @@
 // Host-side launch interface of the HIP kernels (internal to the library).
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
 namespace vla {
+
+// Kernel timing hook. While the runtime profiles a kernel class it points
+// g_prof_sink at its event pool; every launch made through launch_k() then
+// carries a start/stop event pair in its dispatch (hipExtLaunchKernelGGL), so
+// the measured span is the kernel's own execution.
+struct ProfSink;
+extern thread_local ProfSink* g_prof_sink;
+bool prof_take_pair(ProfSink* sink, hipEvent_t* start, hipEvent_t* stop);
+
+template <typename... KArgs, typename... Args>
+inline void launch_k(void (*kernel)(KArgs...), dim3 grid, dim3 block, uint32_t lds,
+                     hipStream_t s, Args... args) {
+  hipEvent_t e0, e1;
+  if (g_prof_sink && prof_take_pair(g_prof_sink, &e0, &e1)) {
+    hipExtLaunchKernelGGL(kernel, grid, block, lds, s, e0, e1, 0u, static_cast<KArgs>(args)...);
+    return;
+  }
+  kernel<<<grid, block, lds, s>>>(static_cast<KArgs>(args)...);
+}
 
 enum Dtype { DT_F32 = 0, DT_BF16 = 1 };
 
@@ -85,9 +105,12 @@ struct AttnArgs {
   int last_ntok = 0;               // valid tokens of logical block nlb-1 (overrides the table)
   int cb0 = 0, cslot0 = 0;         // first token of the causal region (the chunk)
   int n = 0, hq = 0;
-  int splits = 1;
-  float* part_o = nullptr;         // [units][16][d] (splits > 1)
-  float* part_ml = nullptr;        // [units][2][16]
+  int splits = 1;                  // chosen by launch_attention
+  float* part_o = nullptr;         // split partials, part_rows rows of d fp32
+  float* part_ml = nullptr;        // part_rows x 2 fp32 (running max, sum)
+  int part_rows = 0;
+  int* counters = nullptr;         // per (KV head, row group) ticket counters, zero between launches
+  int counter_cap = 0;
   float scale = 1.f;
 };
 

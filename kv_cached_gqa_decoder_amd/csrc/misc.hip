@@ -152,31 +152,56 @@ hipError_t launch_embed(const int* tokens, int token_scalar, int n, const void* 
 }
 
 // ---------------------------------------------------------------------------
-// RMSNorm, one wavefront per row, fp32 statistics: u = x * (mean(x^2) + eps)^-1/2 * g
+// RMSNorm, one wavefront per row, fp32 statistics: u = x * (mean(x^2) + eps)^-1/2 * g.
+// 16-byte loads: 8 bf16 or 4 fp32 values per lane per step; H is a multiple of 64.
 template <typename T>
 __global__ __launch_bounds__(256) void rmsnorm_kernel(const T* x, const float* g, T* u, int rows,
                                                       int H, float eps) {
+  constexpr int CH = 16 / sizeof(T);
   const int lane = threadIdx.x & 63;
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (row >= rows) return;
   const T* xr = x + (int64_t)row * H;
+  T* ur = u + (int64_t)row * H;
   float ss = 0.f;
-  for (int i = lane; i < H; i += 64) {
-    const float v = St<T>::ld(xr, i);
-    ss += v * v;
+  for (int c = lane; c < H / CH; c += 64) {
+    const u32x4_t w = *(const u32x4_t*)(xr + c * CH);
+    float f[CH];
+    if constexpr (CH == 8) unpack8(w, f);
+    else
+#pragma unroll
+      for (int i = 0; i < 4; ++i) f[i] = __uint_as_float(w[i]);
+#pragma unroll
+    for (int i = 0; i < CH; ++i) ss += f[i] * f[i];
   }
   ss = wave_sum(ss);
   const float r = rsqrtf(ss / (float)H + eps);
-  T* ur = u + (int64_t)row * H;
-  for (int i = lane; i < H; i += 64) St<T>::st(ur, i, St<T>::ld(xr, i) * r * g[i]);
+  for (int c = lane; c < H / CH; c += 64) {
+    const u32x4_t w = *(const u32x4_t*)(xr + c * CH);
+    float f[CH];
+    u32x4_t o;
+    if constexpr (CH == 8) {
+      unpack8(w, f);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        o[i] = (uint32_t)f32_to_bf16(f[2 * i] * r * g[c * CH + 2 * i]) |
+               ((uint32_t)f32_to_bf16(f[2 * i + 1] * r * g[c * CH + 2 * i + 1]) << 16);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) o[i] = __float_as_uint(__uint_as_float(w[i]) * r * g[c * CH + i]);
+    }
+    *(u32x4_t*)(ur + c * CH) = o;
+  }
 }
 hipError_t launch_rmsnorm(const void* x, const float* g, void* u, int rows, int H, float eps,
                           int dt, hipStream_t s) {
   const int grid = (rows + 3) / 4;
   if (dt == DT_F32)
-    rmsnorm_kernel<float><<<grid, 256, 0, s>>>((const float*)x, g, (float*)u, rows, H, eps);
+    launch_k(rmsnorm_kernel<float>, dim3(grid), dim3(256), 0, s, (const float*)x, g, (float*)u, rows,
+             H, eps);
   else
-    rmsnorm_kernel<bf16_t><<<grid, 256, 0, s>>>((const bf16_t*)x, g, (bf16_t*)u, rows, H, eps);
+    launch_k(rmsnorm_kernel<bf16_t>, dim3(grid), dim3(256), 0, s, (const bf16_t*)x, g, (bf16_t*)u,
+             rows, H, eps);
   return hipGetLastError();
 }
 

@@ -33,7 +33,7 @@ struct Err {
 
 [[noreturn]] void raise(vla_status st, const std::string& msg) { throw Err{st, msg}; }
 
-constexpr int kPartUnits = 4096;   // attention split partials capacity (wavefront units)
+constexpr int kPartRows = 32768;   // attention split partials capacity (query rows x splits)
 constexpr int kArgmaxParts = 2048; // head GEMV workgroups at most
 
 struct Segment {
@@ -58,6 +58,27 @@ struct Staging {
 struct vla_pool {
   BlockPool p;
 };
+
+namespace vla {
+// event pairs of the profiled kernel launches since the last enable
+struct ProfSink {
+  std::vector<hipEvent_t> ev;
+  int used = 0;     // events handed out (two per kernel launch)
+  int calls = 0;    // profiled calls (one call may launch several kernels)
+};
+thread_local ProfSink* g_prof_sink = nullptr;
+bool prof_take_pair(ProfSink* s, hipEvent_t* a, hipEvent_t* b) {
+  while ((int)s->ev.size() < s->used + 2) {
+    hipEvent_t e;
+    if (hipEventCreate(&e) != hipSuccess) return false;
+    s->ev.push_back(e);
+  }
+  *a = s->ev[s->used];
+  *b = s->ev[s->used + 1];
+  s->used += 2;
+  return true;
+}
+}  // namespace vla
 
 struct vla_model {
   vla_config cfg{};
@@ -89,6 +110,8 @@ struct vla_model {
   unsigned long long* amax_res = nullptr;
   float* part_o = nullptr;
   float* part_ml = nullptr;
+  int* attn_counters = nullptr;
+  int attn_counter_cap = 0;
   int* d_meta = nullptr;        // blk | ntok | tokbase (nb each) | fr_slot | fr_blk0 | fr_nblk | fr_ntok
   int* d_tokens = nullptr;
   double* d_score_m = nullptr;
@@ -106,8 +129,7 @@ struct vla_model {
 
   // profiling
   int prof_cls = VLA_K_NONE;
-  std::vector<hipEvent_t> prof_ev;
-  int prof_used = 0;
+  ProfSink prof;
 
   std::vector<void*> allocs;
 
@@ -170,22 +192,17 @@ void staging_upload(Staging& s, void* dst, size_t bytes, hipStream_t st) {
   s.pending = true;
 }
 
-// ---- profiling (HIP events on the launch stream) ----
-void prof_mark(vla_model* m, int cls, hipStream_t st) {
-  if (m->prof_cls != cls || cls == VLA_K_NONE) return;
-  if (m->prof_used == (int)m->prof_ev.size()) {
-    hipEvent_t e;
-    HIPCHK(hipEventCreate(&e));
-    m->prof_ev.push_back(e);
-  }
-  HIPCHK(hipEventRecord(m->prof_ev[m->prof_used++], st));
-}
-
-#define LAUNCH(m, cls, st, expr)          \
-  do {                                    \
-    prof_mark(m, cls, st);                \
-    HIPCHK(expr);                         \
-    prof_mark(m, cls, st);                \
+// ---- profiling: start/stop events carried by the profiled kernels' dispatches ----
+#define LAUNCH(m, cls, st, expr)                                     \
+  do {                                                               \
+    const bool on_ = (m)->prof_cls == (cls) && (cls) != VLA_K_NONE; \
+    if (on_) {                                                       \
+      g_prof_sink = &(m)->prof;                                      \
+      ++(m)->prof.calls;                                             \
+    }                                                                \
+    const hipError_t launch_err_ = (expr);                           \
+    g_prof_sink = nullptr;                                           \
+    HIPCHK(launch_err_);                                             \
   } while (0)
 
 // ---- bookkeeping ----
@@ -269,17 +286,6 @@ FwdCtx make_ctx(vla_model* m, int layer, int64_t pos0, int cb0, int cslot0) {
   return c;
 }
 
-int attn_splits(const vla_model* m, int n, int nlb) {
-  if (m->dt == DT_F32) return 1;
-  const int grp = m->cfg.n_heads / m->cfg.n_kv_heads;
-  const int units = m->cfg.n_kv_heads * ((n * grp + 15) / 16);
-  const int target = n == 1 ? 512 : 1024;
-  int s = target / units;
-  s = std::min(s, (nlb + 1) / 2);
-  s = std::min(s, kPartUnits / units);
-  return std::max(s, 1);
-}
-
 // the per-layer launches of one pass over n rows whose K/V go to logical slots
 // (cb0, cslot0 ...); rows = prefill chunk (n >= 1, matrix path) or decode (GEMV path)
 void run_layers(vla_model* m, int n, int64_t pos0, int cb0, int cslot0, bool decode,
@@ -302,9 +308,11 @@ void run_layers(vla_model* m, int n, int64_t pos0, int cb0, int cslot0, bool dec
   at.cslot0 = cslot0;
   at.n = n;
   at.hq = c.n_heads;
-  at.splits = attn_splits(m, n, nlb);
   at.part_o = m->part_o;
   at.part_ml = m->part_ml;
+  at.part_rows = m->part_o ? kPartRows : 0;
+  at.counters = m->attn_counters;
+  at.counter_cap = m->attn_counter_cap;
   at.scale = (float)(1.0 / std::sqrt((double)c.head_dim));
 
   for (int l = 0; l < c.n_layers; ++l) {
@@ -520,7 +528,7 @@ void destroy(vla_model* m) {
   staging_free(m->st_meta);
   staging_free(m->st_tok);
   staging_free(m->st_read);
-  for (hipEvent_t e : m->prof_ev) (void)hipEventDestroy(e);
+  for (hipEvent_t e : m->prof.ev) (void)hipEventDestroy(e);
   delete m;
 }
 
@@ -575,8 +583,12 @@ vla_status vla_model_create(const vla_config* cfg, vla_model** out) {
     m->amax_part = (unsigned long long*)dalloc(m, kArgmaxParts * sizeof(unsigned long long));
     m->amax_res = (unsigned long long*)dalloc(m, sizeof(unsigned long long));
     if (m->dt == DT_BF16) {
-      m->part_o = (float*)dalloc(m, (size_t)kPartUnits * 16 * d * sizeof(float));
-      m->part_ml = (float*)dalloc(m, (size_t)kPartUnits * 32 * sizeof(float));
+      m->part_o = (float*)dalloc(m, (size_t)kPartRows * d * sizeof(float));
+      m->part_ml = (float*)dalloc(m, (size_t)kPartRows * 2 * sizeof(float));
+      // one ticket counter per (KV head, 16-row group) of the longest chunk
+      m->attn_counter_cap = (int)(hkv * ((mc * (hq / hkv) + 15) / 16) + 16);
+      m->attn_counters = (int*)dalloc(m, (size_t)m->attn_counter_cap * sizeof(int));
+      HIPCHK(hipMemset(m->attn_counters, 0, (size_t)m->attn_counter_cap * sizeof(int)));
     }
     m->d_meta = (int*)dalloc(m, m->meta_ints() * sizeof(int));
     m->d_tokens = (int*)dalloc(m, mc * sizeof(int));
@@ -931,7 +943,8 @@ vla_status vla_profile_enable(vla_model* m, int32_t kernel_class) {
     if (!m) raise(VLA_E_INVALID, "null model");
     if (kernel_class < 0 || kernel_class >= VLA_K_COUNT) raise(VLA_E_INVALID, "kernel class");
     m->prof_cls = kernel_class;
-    m->prof_used = 0;
+    m->prof.used = 0;
+    m->prof.calls = 0;
   });
 }
 
@@ -939,14 +952,14 @@ vla_status vla_profile_read(vla_model* m, double* total_ms, int32_t* launches) {
   return guarded([&] {
     if (!m) raise(VLA_E_INVALID, "null model");
     double tot = 0.0;
-    for (int i = 0; i + 1 < m->prof_used; i += 2) {
-      HIPCHK(hipEventSynchronize(m->prof_ev[i + 1]));
+    for (int i = 0; i + 1 < m->prof.used; i += 2) {
+      HIPCHK(hipEventSynchronize(m->prof.ev[i + 1]));
       float ms = 0.f;
-      HIPCHK(hipEventElapsedTime(&ms, m->prof_ev[i], m->prof_ev[i + 1]));
+      HIPCHK(hipEventElapsedTime(&ms, m->prof.ev[i], m->prof.ev[i + 1]));
       tot += ms;
     }
     if (total_ms) *total_ms = tot;
-    if (launches) *launches = m->prof_used / 2;
+    if (launches) *launches = m->prof.calls;
   });
 }
 

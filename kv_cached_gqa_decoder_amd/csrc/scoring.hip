@@ -44,11 +44,11 @@ hipError_t launch_meankeys(const void* kpool, KvGeom g, const int* blk_table, co
   if (nframes <= 0 || nlayers <= 0) return hipSuccess;
   dim3 grid(nframes, nlayers);
   if (dt == DT_F32)
-    meankeys_kernel<float><<<grid, 256, 0, s>>>((const float*)kpool, g, blk_table, fr_blk0,
+    launch_k(meankeys_kernel<float>, grid, dim3(256), 0, s, (const float*)kpool, g, blk_table, fr_blk0,
                                                 fr_nblk, fr_ntok, fr_slot, layer0, table,
                                                 max_frames);
   else
-    meankeys_kernel<bf16_t><<<grid, 256, 0, s>>>((const bf16_t*)kpool, g, blk_table, fr_blk0,
+    launch_k(meankeys_kernel<bf16_t>, grid, dim3(256), 0, s, (const bf16_t*)kpool, g, blk_table, fr_blk0,
                                                  fr_nblk, fr_ntok, fr_slot, layer0, table,
                                                  max_frames);
   return hipGetLastError();
@@ -121,8 +121,9 @@ __global__ __launch_bounds__(256) void score_argmax_kernel(const double* m, int 
 hipError_t launch_score(const double* table_layer, const int* fr_slot, int nframes, int D,
                         double* m_out, double* result, hipStream_t s) {
   if (nframes < 2) return hipErrorInvalidValue;
-  score_rows_kernel<<<nframes, 256, 0, s>>>(table_layer, fr_slot, nframes, D, m_out);
-  score_argmax_kernel<<<1, 256, 0, s>>>(m_out, nframes, result);
+  launch_k(score_rows_kernel, dim3(nframes), dim3(256), 0, s, table_layer, fr_slot, nframes, D,
+           m_out);
+  launch_k(score_argmax_kernel, dim3(1), dim3(256), 0, s, (const double*)m_out, nframes, result);
   return hipGetLastError();
 }
 

@@ -231,3 +231,33 @@ def test_rollback_repeats_bit_identically():
     assert np.array_equal(runs[0][0], runs[1][0]) and runs[0][1] == runs[1][1]
     assert runs[0][2] == runs[1][2]
     m.close()
+
+
+# ---------------------------------------------------------------------------
+def test_bf16_long_context_split_attention():
+    """A 1,920-token cached context (30 raw frames, 120 blocks) so that both the
+    prefill and the decode attention split the keys over many workgroups and merge
+    the partials; then a 200-token prefill and 6 greedy decodes."""
+    p = dict(TINY_BF16, num_blocks=160, max_frames=40, max_chunk=200)
+    init_std = 0.08
+    ocfg = oracle_config(p, init_std=init_std)
+    sess = D.Session(ocfg)
+    m = _model(p, init_std)
+    L, hkv, d = p["n_layers"], p["n_kv_heads"], p["head_dim"]
+    for f in range(30):
+        (k32, v32), (ks, vs) = synth.raw_kv_frame(11, f, L, 64, hkv, d, "bf16")
+        fid = m.kv_append_raw(dev_from_storage(ks, "bf16"), dev_from_storage(vs, "bf16"), 64)
+        assert fid == sess.append_raw(k32, v32)
+    x32, xs = synth.embeddings(p["seed"], 0, 200, p["hidden"], "bf16")
+    m.prefill_chunk(embeds=dev_from_storage(xs, "bf16"), n=200)
+    _, ref = sess.prefill_chunk(embeds=x32)
+    log("long ctx prefill cos %.6f rel %.2e" % metrics(logits_of(m), ref))
+    check_logits(logits_of(m), ref, "bf16", "long-context prefill")
+    tok = int(np.argmax(ref))
+    for i in range(6):
+        g = m.decode_step(tok)
+        nxt, ref = sess.decode_step(tok)
+        check_logits(logits_of(m), ref, "bf16", f"long-context decode {i}")
+        check_argmax(g, ref, "bf16", f"long-context decode {i}")
+        tok = nxt
+    m.close()
