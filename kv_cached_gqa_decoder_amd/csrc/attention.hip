@@ -24,9 +24,10 @@
 //   row tiles (prefill): each wavefront owns 16 rows; the workgroup stages each
 //     block pair in LDS once (double buffered) for all 64 rows.
 // The resident blocks are split over workgroups (split-K). Each workgroup
-// writes its partial (m, l, o); the last one to finish (an agent-scope ticket
-// counter) merges all splits in split order, so the result does not depend on
-// which workgroup finished last, and resets the counter for the next launch.
+// writes its partial (m, l, o); a second kernel merges the splits in split
+// order (deterministic). Merging inside the first kernel would need an
+// agent-scope release/acquire per workgroup, which on this chip writes back
+// and invalidates the whole L2 of the workgroup's XCD.
 #include <algorithm>
 
 #include "common.hpp"
@@ -236,7 +237,6 @@ __device__ __forceinline__ void load_pair_lds(const bf16_t* lds, PairFrags<D>& f
 template <int D, bool KEYSPLIT>
 struct AttnShape {
   static constexpr int ROWS = KEYSPLIT ? 16 : 16 * kAttnWaves;
-  static constexpr int MAXS = KEYSPLIT ? kMaxSplitsKey : kMaxSplitsRow;
   // LDS: key split -> per-wave partials (4 x 16 x D fp32 + m, l); row tiles -> 2 pair images
   static constexpr int LDS_BYTES =
       KEYSPLIT ? kAttnWaves * 16 * (D + 2) * 4 : 2 * PairLds<D>::ELEMS * 2;
@@ -249,9 +249,6 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(AttnArgs a, int rgroups)
   using S = AttnShape<D, KEYSPLIT>;
   constexpr int ROWS = S::ROWS;
   __shared__ __attribute__((aligned(16))) unsigned char smem[S::LDS_BYTES];
-  __shared__ float mw[ROWS * S::MAXS];  // merge weights
-  __shared__ float linv[ROWS];
-  __shared__ int s_ticket;
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int split = blockIdx.x, rg = blockIdx.y, kvh = blockIdx.z;
@@ -385,42 +382,55 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(AttnArgs a, int rgroups)
       }
     }
   }
-  if (splits == 1) return;
+}
 
-  // ---- the last workgroup of this (KV head, row group) merges the splits ----
-  __threadfence();
-  __syncthreads();
-  int* counter = a.counters + kvh * rgroups + rg;
-  if (threadIdx.x == 0)
-    s_ticket = __hip_atomic_fetch_add(counter, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-  __syncthreads();
-  if (s_ticket != splits - 1) return;
-  __threadfence();
-  const size_t unit0 = (size_t)(kvh * rgroups + rg) * splits;
-  for (int c = threadIdx.x; c < ROWS; c += kAttnWaves * 64) {
-    float M = -INFINITY;
-    for (int s = 0; s < splits; ++s) M = fmaxf(M, a.part_ml[(unit0 + s) * 2 * ROWS + c]);
-    float L = 0.f;
-    for (int s = 0; s < splits; ++s) {
-      const float m = a.part_ml[(unit0 + s) * 2 * ROWS + c];
-      const float w = (m == -INFINITY) ? 0.f : exp2f(m - M);
-      mw[c * S::MAXS + s] = w;
-      L += w * a.part_ml[(unit0 + s) * 2 * ROWS + ROWS + c];
+// Combines the splits of one (KV head, row group): with per-split running max
+// m_s (base 2), sum l_s and unnormalised o_s, o = sum_s 2^(m_s - M) o_s /
+// sum_s 2^(m_s - M) l_s, M = max_s m_s, taken in split order. One thread per
+// output element; the splits are read 8 at a time (24 loads in flight).
+template <int D, bool KEYSPLIT>
+__global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a, int rgroups) {
+  using S = AttnShape<D, KEYSPLIT>;
+  constexpr int ROWS = S::ROWS;
+  constexpr int CHUNK = 8;
+  const int tile = blockIdx.x;  // kvh * rgroups + rg
+  const int rg = tile % rgroups, kvh = tile / rgroups;
+  const int e = blockIdx.y * 256 + threadIdx.x;
+  if (e >= ROWS * D) return;
+  const int c = e / D, dim = e % D;
+  const int grp = a.hq / a.g.hkv;
+  const int rr = rg * ROWS + c;
+  if (rr >= a.n * grp) return;
+  const int splits = a.splits;
+  const size_t unit0 = (size_t)tile * splits;
+  float M = -INFINITY, L = 0.f, acc = 0.f;
+  for (int s0 = 0; s0 < splits; s0 += CHUNK) {
+    float m[CHUNK], l[CHUNK], o[CHUNK];
+#pragma unroll
+    for (int i = 0; i < CHUNK; ++i) {
+      const size_t u = unit0 + s0 + i;
+      const bool ok = s0 + i < splits;
+      m[i] = ok ? a.part_ml[u * 2 * ROWS + c] : -INFINITY;
+      l[i] = ok ? a.part_ml[u * 2 * ROWS + ROWS + c] : 0.f;
+      o[i] = ok ? a.part_o[(u * ROWS + c) * D + dim] : 0.f;
     }
-    linv[c] = L > 0.f ? 1.f / L : 0.f;
+    float mc = M;
+#pragma unroll
+    for (int i = 0; i < CHUNK; ++i) mc = fmaxf(mc, m[i]);
+    if (mc == -INFINITY) continue;
+    const float sc = M == -INFINITY ? 0.f : exp2f(M - mc);
+    L *= sc;
+    acc *= sc;
+#pragma unroll
+    for (int i = 0; i < CHUNK; ++i) {
+      const float w = m[i] == -INFINITY ? 0.f : exp2f(m[i] - mc);
+      L += w * l[i];
+      acc += w * o[i];
+    }
+    M = mc;
   }
-  __syncthreads();
-  for (int e = threadIdx.x; e < ROWS * D; e += kAttnWaves * 64) {
-    const int c = e / D, dim = e % D;
-    const int rr = rg * ROWS + c;
-    if (rr >= R) continue;
-    float acc = 0.f;
-    for (int s = 0; s < splits; ++s)
-      acc += mw[c * S::MAXS + s] * a.part_o[((unit0 + s) * ROWS + c) * D + dim];
-    ((bf16_t*)a.out)[((size_t)(rr / grp) * a.hq + kvh * grp + rr % grp) * D + dim] =
-        f32_to_bf16(acc * linv[c]);
-  }
-  if (threadIdx.x == 0) *counter = 0;
+  ((bf16_t*)a.out)[((size_t)(rr / grp) * a.hq + kvh * grp + rr % grp) * D + dim] =
+      f32_to_bf16(L > 0.f ? acc / L : 0.f);
 }
 
 // ---------------------------------------------------------------------------
@@ -481,6 +491,11 @@ template <int D, bool KEYSPLIT>
 static void attn_bf16_launch(const AttnArgs& a, int rgroups, hipStream_t s) {
   const dim3 grid(a.splits, rgroups, a.g.hkv);
   launch_k(attn_bf16_kernel<D, KEYSPLIT>, grid, dim3(kAttnWaves * 64), 0, s, a, rgroups);
+  if (a.splits > 1) {
+    constexpr int ROWS = AttnShape<D, KEYSPLIT>::ROWS;
+    const dim3 mgrid(a.g.hkv * rgroups, (ROWS * D + 255) / 256);
+    launch_k(attn_merge_kernel<D, KEYSPLIT>, mgrid, dim3(256), 0, s, a, rgroups);
+  }
 }
 
 template <int D>
@@ -499,7 +514,7 @@ hipError_t launch_attention(const AttnArgs& args, int dt, hipStream_t s) {
   AttnArgs a = args;
   // workgroup shape and split count: at least 8 blocks (4 pairs) per workgroup,
   // about 4 (decode) or 2 (prefill) workgroups per CU at most, within the
-  // partial-buffer and counter capacities
+  // partial-buffer capacity
   const int R = a.n * (a.hq / a.g.hkv);
   const bool keysplit = R <= 16;
   const int rows = keysplit ? 16 : 16 * kAttnWaves;
@@ -512,8 +527,8 @@ hipError_t launch_attention(const AttnArgs& args, int dt, hipStream_t s) {
   splits = std::max(splits, 1);
   const int bps = (a.nlb + splits - 1) / splits;
   a.splits = (a.nlb + bps - 1) / bps;
-  if (a.splits > 1 && (a.part_o == nullptr || a.part_ml == nullptr || a.counters == nullptr ||
-                       base > a.counter_cap || base * rows * a.splits > a.part_rows))
+  if (a.splits > 1 &&
+      (a.part_o == nullptr || a.part_ml == nullptr || base * rows * a.splits > a.part_rows))
     return hipErrorInvalidValue;
   switch (a.g.d) {
     case 64: attn_bf16_dispatch<64>(a, keysplit, rgroups, s); break;

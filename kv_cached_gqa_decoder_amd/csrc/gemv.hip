@@ -1,7 +1,7 @@
 // Decode projections (one token row): weight-streaming GEMV with fused input
 // RMSNorm and fused epilogues (RoPE + paged KV write, residual add, SwiGLU,
 // output head with argmax). HBM-bound: every weight byte is read once with
-// 16-byte loads; the input row lives in LDS as fp32.
+// 16-byte loads, many independent loads in flight per lane.
 #include "common.hpp"
 #include "epilogue.hpp"
 #include "kernels.hpp"
@@ -9,132 +9,186 @@
 namespace vla {
 
 constexpr int kGemvThreads = 256;
-constexpr int kGemvRows = 4;  // output rows per workgroup step
+constexpr int kGemvWaves = kGemvThreads / 64;
+constexpr int kGemvMaxGrid = 2048;  // also the capacity of the argmax partials
 
-// physical rows handled by row group `grp`
-template <int EPI>
-__device__ __forceinline__ void gemv_rows(int grp, int64_t* rows) {
+// Row group g of a wave: RW physical rows. For the gated projection the group
+// is RW/2 gate rows f0 .. f0+RW/2-1 and their RW/2 up rows (LAYOUT_GATEUP puts
+// 16 gate rows, then the 16 matching up rows, in each block of 32).
+template <int EPI, int RW>
+__device__ __forceinline__ int64_t gemv_row(int g, int r) {
   if constexpr (EPI == EPI_SWIGLU) {
-    // gate rows of f = 2grp, 2grp+1 and their up rows (LAYOUT_GATEUP)
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int f = 2 * grp + i;
-      rows[i] = (int64_t)(f / 16) * 32 + (f % 16);
-      rows[2 + i] = rows[i] + 16;
-    }
+    const int f = g * (RW / 2) + (r % (RW / 2));
+    return (int64_t)(f / 16) * 32 + (f % 16) + (r >= RW / 2 ? 16 : 0);
   } else {
-#pragma unroll
-    for (int i = 0; i < kGemvRows; ++i) rows[i] = (int64_t)grp * kGemvRows + i;
+    return (int64_t)g * RW + r;
   }
 }
 
-template <typename T, int EPI>
+__device__ __forceinline__ float dot8(const u32x4_t& w, const u32x4_t& x) {
+  float wf[8], xf[8];
+  unpack8(w, wf);
+  unpack8(x, xf);
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) s += wf[i] * xf[i];
+  return s;
+}
+__device__ __forceinline__ float dot4f(const u32x4_t& w, const u32x4_t& x) {
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) s += __uint_as_float(w[i]) * __uint_as_float(x[i]);
+  return s;
+}
+
+// One workgroup = 4 wavefronts; a wavefront owns RW whole rows at a time and
+// streams them with 16-byte loads, UNR chunks per lane per step (RW * UNR
+// independent loads in flight per lane). The input row (RMSNorm applied when
+// norm_g is given, rounded to the storage type as the prefill path does) sits
+// in LDS; partial sums are reduced across the wavefront with xor shuffles, so
+// the epilogue of a row group needs no workgroup barrier.
+template <typename T, int EPI, int RW>
 __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(GemvArgs a, int ngroups) {
-  extern __shared__ float xs[];  // the input row, fp32
-  __shared__ float red[kGemvThreads / 64][kGemvRows];
-  __shared__ float ys[kGemvRows];
-  __shared__ float ssq[kGemvThreads / 64];
+  extern __shared__ __attribute__((aligned(16))) unsigned char gsmem[];
+  T* xs = (T*)gsmem;
+  __shared__ float ssq[kGemvWaves];
+  __shared__ unsigned long long wbest[kGemvWaves];
+  constexpr int CH = 16 / sizeof(T);   // elements per 16-byte chunk
+  constexpr int UNR = RW >= 8 ? 2 : (RW >= 4 ? 4 : 8);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int K = a.K;
+  const int nch = K / CH;
   const T* x = (const T*)a.x;
 
+  // input row -> LDS (optionally normalised)
   float ss = 0.f;
-  for (int i = tid; i < K; i += kGemvThreads) {
-    const float v = St<T>::ld(x, i);
-    xs[i] = v;
-    ss += v * v;
+  for (int c = tid; c < nch; c += kGemvThreads) {
+    const u32x4_t v = *(const u32x4_t*)(x + (size_t)c * CH);
+    *(u32x4_t*)(xs + (size_t)c * CH) = v;
+    if constexpr (sizeof(T) == 2) {
+      float f[8];
+      unpack8(v, f);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) ss += f[i] * f[i];
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) ss += __uint_as_float(v[i]) * __uint_as_float(v[i]);
+    }
   }
   if (a.norm_g) {  // RMSNorm of the input row (fp32 statistics)
     ss = wave_sum(ss);
     if (lane == 0) ssq[wave] = ss;
     __syncthreads();
-    const float r = rsqrtf((ssq[0] + ssq[1] + ssq[2] + ssq[3]) / (float)K + a.eps);
-    for (int i = tid; i < K; i += kGemvThreads) xs[i] = xs[i] * r * a.norm_g[i];
+    float tot = 0.f;
+#pragma unroll
+    for (int w = 0; w < kGemvWaves; ++w) tot += ssq[w];
+    const float r = rsqrtf(tot / (float)K + a.eps);
+    for (int i = tid; i < K; i += kGemvThreads)
+      St<T>::st(xs, i, St<T>::ld(xs, i) * r * a.norm_g[i]);
   }
   __syncthreads();
 
-  constexpr int CH = 16 / sizeof(T);  // elements per 16-byte load
-  const int nch = K / CH;
   const T* W = (const T*)a.W;
   unsigned long long best = 0ull;
-
-  for (int grp = blockIdx.x; grp < ngroups; grp += gridDim.x) {
-    int64_t rows[kGemvRows];
-    gemv_rows<EPI>(grp, rows);
-    bool ok[kGemvRows];
+  for (int g = blockIdx.x * kGemvWaves + wave; g < ngroups; g += gridDim.x * kGemvWaves) {
+    const T* wr[RW];
 #pragma unroll
-    for (int r = 0; r < kGemvRows; ++r) ok[r] = rows[r] < a.N;
-    float acc[kGemvRows];
+    for (int r = 0; r < RW; ++r) {  // rows past N (a partial last group) re-read row N-1
+      const int64_t row = gemv_row<EPI, RW>(g, r);
+      wr[r] = W + (row < a.N ? row : (int64_t)a.N - 1) * K;
+    }
+    float acc[RW];
 #pragma unroll
-    for (int r = 0; r < kGemvRows; ++r) acc[r] = 0.f;
-
-    for (int c = tid; c < nch; c += kGemvThreads) {
-      float xv[CH];
+    for (int r = 0; r < RW; ++r) acc[r] = 0.f;
+    for (int c0 = lane; c0 < nch; c0 += 64 * UNR) {
+      u32x4_t w[UNR][RW];
 #pragma unroll
-      for (int i = 0; i < CH; ++i) xv[i] = xs[c * CH + i];
+      for (int u = 0; u < UNR; ++u) {
+        const int c = c0 + 64 * u;
 #pragma unroll
-      for (int r = 0; r < kGemvRows; ++r) {
-        if (!ok[r]) continue;
-        const u32x4_t w = *(const u32x4_t*)(W + rows[r] * K + (int64_t)c * CH);
-        float wf[CH];
-        if constexpr (sizeof(T) == 2) {
-          unpack8(w, wf);
-        } else {
+        for (int r = 0; r < RW; ++r)
+          w[u][r] = c < nch ? *(const u32x4_t*)(wr[r] + (size_t)c * CH) : u32x4_t{0, 0, 0, 0};
+      }
 #pragma unroll
-          for (int i = 0; i < 4; ++i) wf[i] = __uint_as_float(w[i]);
+      for (int u = 0; u < UNR; ++u) {
+        const int c = c0 + 64 * u;
+        const u32x4_t xv = c < nch ? *(const u32x4_t*)(xs + (size_t)c * CH) : u32x4_t{0, 0, 0, 0};
+#pragma unroll
+        for (int r = 0; r < RW; ++r) {
+          if constexpr (sizeof(T) == 2) acc[r] += dot8(w[u][r], xv);
+          else acc[r] += dot4f(w[u][r], xv);
         }
-#pragma unroll
-        for (int i = 0; i < CH; ++i) acc[r] += wf[i] * xv[i];
       }
     }
 #pragma unroll
-    for (int r = 0; r < kGemvRows; ++r) acc[r] = wave_sum(acc[r]);
-    if (lane == 0) {
-#pragma unroll
-      for (int r = 0; r < kGemvRows; ++r) red[wave][r] = acc[r];
-    }
-    __syncthreads();
-    if (tid < kGemvRows) ys[tid] = red[0][tid] + red[1][tid] + red[2][tid] + red[3][tid];
-    __syncthreads();
+    for (int r = 0; r < RW; ++r) acc[r] = wave_sum(acc[r]);
 
     if constexpr (EPI == EPI_QKV) {
-      if (tid < kGemvRows / 2)
-        epi_qkv_pair<T>(a.ctx, 0, (int)rows[2 * tid], ys[2 * tid], ys[2 * tid + 1]);
+#pragma unroll
+      for (int p = 0; p < RW / 2; ++p)
+        if (lane == p) epi_qkv_pair<T>(a.ctx, 0, (int)gemv_row<EPI, RW>(g, 2 * p), acc[2 * p],
+                                       acc[2 * p + 1]);
     } else if constexpr (EPI == EPI_RESID) {
-      if (tid < kGemvRows && ok[tid]) {
-        T* xo = (T*)a.out;
-        St<T>::st(xo, rows[tid], St<T>::ld(xo, rows[tid]) + ys[tid]);
+#pragma unroll
+      for (int r = 0; r < RW; ++r) {
+        const int64_t row = gemv_row<EPI, RW>(g, r);
+        if (lane == r && row < a.N) {
+          T* xo = (T*)a.out;
+          St<T>::st(xo, row, St<T>::ld(xo, row) + acc[r]);
+        }
       }
     } else if constexpr (EPI == EPI_SWIGLU) {
-      if (tid < 2) St<T>::st((T*)a.out, 2 * grp + tid, silu(ys[tid]) * ys[2 + tid]);
-    } else if constexpr (EPI == EPI_HEAD) {
-      if (tid == 0) {
 #pragma unroll
-        for (int r = 0; r < kGemvRows; ++r) {
-          if (!ok[r]) continue;
-          ((float*)a.out)[rows[r]] = ys[r];
-          const unsigned long long k = argmax_key(ys[r], (uint32_t)rows[r]);
+      for (int i = 0; i < RW / 2; ++i)
+        if (lane == i) St<T>::st((T*)a.out, g * (RW / 2) + i, silu(acc[i]) * acc[RW / 2 + i]);
+    } else if constexpr (EPI == EPI_HEAD) {
+#pragma unroll
+      for (int r = 0; r < RW; ++r) {
+        const int64_t row = gemv_row<EPI, RW>(g, r);
+        if (row < a.N) {
+          if (lane == r) ((float*)a.out)[row] = acc[r];
+          const unsigned long long k = argmax_key(acc[r], (uint32_t)row);
           best = k > best ? k : best;
         }
       }
     }
-    __syncthreads();
   }
   if constexpr (EPI == EPI_HEAD) {
-    if (tid == 0) a.argmax_part[blockIdx.x] = best;
+    if (lane == 0) wbest[wave] = best;
+    __syncthreads();
+    if (tid == 0) {
+      unsigned long long b = wbest[0];
+#pragma unroll
+      for (int w = 1; w < kGemvWaves; ++w) b = wbest[w] > b ? wbest[w] : b;
+      a.argmax_part[blockIdx.x] = b;
+    }
   }
 }
 
+template <typename T, int EPI, int RW>
+static hipError_t gemv_launch_rw(const GemvArgs& a, hipStream_t s, int* grid_out) {
+  // rows of the residual and head projections may end in a partial group
+  const int ngroups = (EPI == EPI_SWIGLU) ? a.N / RW : (a.N + RW - 1) / RW;
+  int grid = (ngroups + kGemvWaves - 1) / kGemvWaves;
+  grid = grid < kGemvMaxGrid ? grid : kGemvMaxGrid;
+  if (grid_out) *grid_out = grid;
+  const uint32_t lds = (uint32_t)((size_t)a.K * sizeof(T));
+  launch_k(gemv_kernel<T, EPI, RW>, dim3(grid), dim3(kGemvThreads), lds, s, a, ngroups);
+  return hipGetLastError();
+}
+
+// rows per wavefront: 8 when that still gives >= 2048 wavefronts, else 4 when
+// >= 1024, else 2 (small projections spread over more of the chip)
 template <typename T, int EPI>
 static hipError_t gemv_launch(const GemvArgs& a, hipStream_t s, int* grid_out) {
-  int ngroups;
-  if (EPI == EPI_SWIGLU) ngroups = a.N / 4;  // N = 2F physical rows, two f per group
-  else ngroups = (a.N + kGemvRows - 1) / kGemvRows;
-  int grid = ngroups < 2048 ? ngroups : 2048;
-  if (grid_out) *grid_out = grid;
-  const size_t lds = (size_t)a.K * sizeof(float);
-  launch_k(gemv_kernel<T, EPI>, dim3(grid), dim3(kGemvThreads), (uint32_t)lds, s, a, ngroups);
-  return hipGetLastError();
+  if constexpr (EPI == EPI_QKV) {
+    if (a.N % 8) return hipErrorInvalidValue;
+  } else if constexpr (EPI == EPI_SWIGLU) {
+    if (a.N % 32) return hipErrorInvalidValue;
+  }
+  if (a.N / 8 >= 2048) return gemv_launch_rw<T, EPI, 8>(a, s, grid_out);
+  if (a.N / 4 >= 1024) return gemv_launch_rw<T, EPI, 4>(a, s, grid_out);
+  return gemv_launch_rw<T, EPI, 2>(a, s, grid_out);
 }
 
 template <typename T>
@@ -149,7 +203,7 @@ static hipError_t gemv_dispatch(const GemvArgs& a, hipStream_t s, int* grid_out)
 }
 
 hipError_t launch_gemv(const GemvArgs& a, int dt, hipStream_t s, int* grid_out) {
-  if (a.K % 8 != 0) return hipErrorInvalidValue;
+  if (a.K % 8 != 0 || a.K > 32768) return hipErrorInvalidValue;
   return dt == DT_F32 ? gemv_dispatch<float>(a, s, grid_out)
                       : gemv_dispatch<bf16_t>(a, s, grid_out);
 }

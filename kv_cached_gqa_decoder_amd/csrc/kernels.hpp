@@ -69,7 +69,8 @@ struct FwdCtx {
   int hq = 0;
 };
 
-enum Epi { EPI_STORE = 0, EPI_RESID = 1, EPI_QKV = 2, EPI_SWIGLU = 3, EPI_HEAD = 4 };
+enum Epi { EPI_STORE = 0, EPI_RESID = 1, EPI_QKV = 2, EPI_SWIGLU = 3, EPI_HEAD = 4,
+           EPI_PARTIAL = 5 };
 
 struct GemmArgs {
   const void* A = nullptr;  // [M][K] activations
@@ -78,6 +79,14 @@ struct GemmArgs {
   int epi = EPI_STORE;
   void* C = nullptr;        // STORE [M][N]; RESID x [M][N] (+=); SWIGLU [M][N/2]
   FwdCtx ctx;
+  // bf16 RESID: split-K partials (fp32, [splits][M][N]) reduced by a second
+  // kernel that adds them to x and, when norm_out is set, writes
+  // norm_out = RMSNorm(x) (weights norm_g, epsilon eps) for the next projection
+  float* ws = nullptr;
+  size_t ws_elems = 0;
+  void* norm_out = nullptr;
+  const float* norm_g = nullptr;
+  float eps = 0.f;
 };
 
 struct GemvArgs {
@@ -109,8 +118,6 @@ struct AttnArgs {
   float* part_o = nullptr;         // split partials, part_rows rows of d fp32
   float* part_ml = nullptr;        // part_rows x 2 fp32 (running max, sum)
   int part_rows = 0;
-  int* counters = nullptr;         // per (KV head, row group) ticket counters, zero between launches
-  int counter_cap = 0;
   float scale = 1.f;
 };
 

@@ -34,6 +34,7 @@ struct Err {
 [[noreturn]] void raise(vla_status st, const std::string& msg) { throw Err{st, msg}; }
 
 constexpr int kPartRows = 32768;   // attention split partials capacity (query rows x splits)
+constexpr int kGemmSplitsMax = 8;  // split-K partial capacity of the prefill residual projections
 constexpr int kArgmaxParts = 2048; // head GEMV workgroups at most
 
 struct Segment {
@@ -110,8 +111,8 @@ struct vla_model {
   unsigned long long* amax_res = nullptr;
   float* part_o = nullptr;
   float* part_ml = nullptr;
-  int* attn_counters = nullptr;
-  int attn_counter_cap = 0;
+  float* gemm_ws = nullptr;     // split-K partials of the residual projections
+  size_t gemm_ws_elems = 0;
   int* d_meta = nullptr;        // blk | ntok | tokbase (nb each) | fr_slot | fr_blk0 | fr_nblk | fr_ntok
   int* d_tokens = nullptr;
   double* d_score_m = nullptr;
@@ -311,8 +312,7 @@ void run_layers(vla_model* m, int n, int64_t pos0, int cb0, int cslot0, bool dec
   at.part_o = m->part_o;
   at.part_ml = m->part_ml;
   at.part_rows = m->part_o ? kPartRows : 0;
-  at.counters = m->attn_counters;
-  at.counter_cap = m->attn_counter_cap;
+
   at.scale = (float)(1.0 / std::sqrt((double)c.head_dim));
 
   for (int l = 0; l < c.n_layers; ++l) {
@@ -357,8 +357,13 @@ void run_layers(vla_model* m, int n, int64_t pos0, int cb0, int cslot0, bool dec
       dn.out = m->x;
       LAUNCH(m, VLA_K_GEMV_DOWN, st, launch_gemv(dn, m->dt, st, nullptr));
     } else {
-      LAUNCH(m, VLA_K_RMSNORM, st,
-             launch_rmsnorm(m->x, m->norm_ones, m->u, n, H, c.rms_eps, m->dt, st));
+      // bf16: the residual projections reduce their split-K partials into x and
+      // write the next projection's normalised input u in the same pass; only
+      // the first layer's input norm is a kernel of its own. fp32: plain norms.
+      const bool bf16 = m->dt == DT_BF16;
+      if (!bf16 || l == 0)
+        LAUNCH(m, VLA_K_RMSNORM, st,
+               launch_rmsnorm(m->x, m->norm_ones, m->u, n, H, c.rms_eps, m->dt, st));
       GemmArgs q;
       q.A = m->u;
       q.W = m->wqkv[l];
@@ -377,9 +382,15 @@ void run_layers(vla_model* m, int n, int64_t pos0, int cb0, int cslot0, bool dec
       o.K = qd;
       o.epi = EPI_RESID;
       o.C = m->x;
+      o.ws = m->gemm_ws;
+      o.ws_elems = m->gemm_ws_elems;
+      o.norm_out = m->u;
+      o.norm_g = m->norm_ones;
+      o.eps = c.rms_eps;
       LAUNCH(m, VLA_K_GEMM_O, st, launch_gemm(o, m->dt, st));
-      LAUNCH(m, VLA_K_RMSNORM, st,
-             launch_rmsnorm(m->x, m->norm_ones, m->u, n, H, c.rms_eps, m->dt, st));
+      if (!bf16)
+        LAUNCH(m, VLA_K_RMSNORM, st,
+               launch_rmsnorm(m->x, m->norm_ones, m->u, n, H, c.rms_eps, m->dt, st));
       GemmArgs gu;
       gu.A = m->u;
       gu.W = m->wgu[l];
@@ -397,6 +408,11 @@ void run_layers(vla_model* m, int n, int64_t pos0, int cb0, int cslot0, bool dec
       dn.K = c.ffn;
       dn.epi = EPI_RESID;
       dn.C = m->x;
+      dn.ws = m->gemm_ws;
+      dn.ws_elems = m->gemm_ws_elems;
+      dn.norm_out = l + 1 < c.n_layers ? m->u : nullptr;
+      dn.norm_g = m->norm_ones;
+      dn.eps = c.rms_eps;
       LAUNCH(m, VLA_K_GEMM_DOWN, st, launch_gemm(dn, m->dt, st));
     }
   }
@@ -476,6 +492,7 @@ void validate_cfg(const vla_config* c) {
   if (c->head_dim % 16 || c->head_dim > 256) bad("head_dim must be a multiple of 16, <= 256");
   if (c->ffn % 16) bad("ffn must be a multiple of 16");
   if (c->hidden % 64) bad("hidden must be a multiple of 64");
+  if (c->hidden > 8192) bad("hidden must be <= 8192");
   if (c->block_tokens != 16) bad("block_tokens must be 16");
   if (c->num_blocks < 1 || c->max_frames < 1 || c->max_chunk < 1) bad("budget sizes");
   if (c->wdtype != c->act_dtype || (c->wdtype != VLA_F32 && c->wdtype != VLA_BF16))
@@ -585,10 +602,9 @@ vla_status vla_model_create(const vla_config* cfg, vla_model** out) {
     if (m->dt == DT_BF16) {
       m->part_o = (float*)dalloc(m, (size_t)kPartRows * d * sizeof(float));
       m->part_ml = (float*)dalloc(m, (size_t)kPartRows * 2 * sizeof(float));
-      // one ticket counter per (KV head, 16-row group) of the longest chunk
-      m->attn_counter_cap = (int)(hkv * ((mc * (hq / hkv) + 15) / 16) + 16);
-      m->attn_counters = (int*)dalloc(m, (size_t)m->attn_counter_cap * sizeof(int));
-      HIPCHK(hipMemset(m->attn_counters, 0, (size_t)m->attn_counter_cap * sizeof(int)));
+      m->gemm_ws_elems = (size_t)kGemmSplitsMax * mc * H;
+      m->gemm_ws = (float*)dalloc(m, m->gemm_ws_elems * sizeof(float));
+
     }
     m->d_meta = (int*)dalloc(m, m->meta_ints() * sizeof(int));
     m->d_tokens = (int*)dalloc(m, mc * sizeof(int));
