@@ -9,10 +9,11 @@ namespace vla {
 // One RoPE pair of the fused q/k/v projection for token row t.
 // `col` is the even physical column of the pair (LAYOUT_QKV): logical dims
 // j and j + d/2 of head col/d, with j = (col % d) / 2. q and k are rotated by
-// the angle pos * theta^(-2j/d), evaluated in fp64 ("Rebuilding Kshipra Around
-// Memory", section 4: RoPE at absolute positions; rotate-half pairing); q goes
-// to the query buffer, k and v to the paged pool at the token's block and slot
-// (the cache stores post-RoPE keys).
+// the angle of row t's absolute position times theta^(-2j/d) ("Rebuilding
+// Kshipra Around Memory", section 4: RoPE at absolute positions; rotate-half
+// pairing), read from the pass's (cos, sin) table; q goes to the query buffer,
+// k and v to the paged pool at the token's block and slot (the cache stores
+// post-RoPE keys).
 template <typename T>
 __device__ __forceinline__ void epi_qkv_pair(const FwdCtx& c, int t, int col, float lo, float hi) {
   const int d = c.g.d;
@@ -20,13 +21,9 @@ __device__ __forceinline__ void epi_qkv_pair(const FwdCtx& c, int t, int col, fl
   const int j = (col % d) >> 1;
   const int hkv = c.g.hkv;
   if (head < c.hq + hkv) {
-    // angle in fp64, reduced to [-pi, pi] in fp64, then an fp32 sine/cosine
-    const double ang = (double)(c.pos0 + t) * c.inv_freq[j];
-    const double red = fma(-rint(ang * 0.15915494309189535), 6.283185307179586, ang);
-    float sn, cs;
-    sincosf((float)red, &sn, &cs);
-    const float rlo = lo * cs - hi * sn;
-    const float rhi = hi * cs + lo * sn;
+    const float2 cs = c.rope[(size_t)t * (d / 2) + j];
+    const float rlo = lo * cs.x - hi * cs.y;
+    const float rhi = hi * cs.x + lo * cs.y;
     lo = rlo;
     hi = rhi;
   }

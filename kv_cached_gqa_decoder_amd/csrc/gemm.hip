@@ -18,33 +18,68 @@ namespace vla {
 // ---------------------------------------------------------------------------
 // bf16 matrix-core GEMM. Block tile BM x BN (64 or 128 each), 4 wavefronts in a
 // 2 x 2 grid, each wavefront (BM/2) x (BN/2) = MT x NT tiles of 16 x 16 on
-// v_mfma_f32_16x16x32_bf16. 64-deep K steps staged through a double-buffered
-// LDS image (register prefetch of the next step, one barrier per step).
+// v_mfma_f32_16x16x32_bf16, fp32 accumulation.
+//
+// Operands stream straight from memory into an NS-stage LDS ring with
+// global_load_lds_dwordx4 (no register staging): a stage is one 64-deep K
+// step of the A tile (BM rows) and the W tile (BN rows), 128 bytes per row.
+// One such load fills 1 KiB of LDS (8 rows); lane i writes the 16-byte chunk
+// at position i % 8 of row i / 8, and fetches the K chunk (i % 8) ^ (row % 8)
+// of that row, so the matrix-core operand reads (16 rows, one chunk column)
+// fall in distinct LDS banks. NS-1 stages are in flight while one is used.
+//
 // Tiles are ordered so that each XCD (workgroup L runs on XCD L % 8) walks a
 // contiguous run of tiles with the M tiles of one weight tile adjacent: the
 // weight tile is fetched from HBM once and re-read from that XCD's L2.
-// Split-K (blockIdx over splits) writes fp32 partials for the residual
-// projections; a reduction kernel adds them to the residual in split order.
+// Split-K (over blockIdx) writes fp32 partials for the residual projections;
+// a reduction kernel adds them to the residual in split order.
 // ---------------------------------------------------------------------------
-constexpr int kBK = 64;
-constexpr int kPitch = kBK + 8;  // LDS row pitch in bf16 elements (144 B)
 constexpr int kXcds = 8;
 
-template <int BM, int BN>
+template <int BM, int BN, int BK, int NS>
 struct GemmTile {
   static constexpr int WM = BM / 2, WN = BN / 2;
   static constexpr int MT = WM / 16, NT = WN / 16;
-  static constexpr int ACH = BM * kBK / 8 / 256;  // 16-byte chunks per thread per step
-  static constexpr int WCH = BN * kBK / 8 / 256;
-  static constexpr int STAGE = (BM + BN) * kPitch;
+  static constexpr int ROWB = BK * 2;                // bytes of one LDS row (one K step)
+  static constexpr int CPR = BK / 8;                 // 16-byte chunks per row
+  static constexpr int RPI = 64 / CPR;               // rows filled by one DMA load
+  static constexpr int ROWS = BM + BN;               // LDS rows per stage
+  static constexpr int STAGE = ROWS * ROWB;          // bytes
+  static constexpr int LOADS = ROWS / RPI / 4;       // DMA loads per wavefront per stage
+  static constexpr int LDS = NS * STAGE;
+  // chunk position of K chunk kc in LDS row r: 8 consecutive rows read at one chunk
+  // column land in 8 distinct 16-byte bank groups (32 or 64 banks)
+  static __device__ __forceinline__ int pos(int r, int kc) {
+    return BK == 64 ? (kc ^ (r & 7)) : (kc ^ ((r >> 1) & 3));
+  }
 };
 
-template <int EPI, int BM, int BN>
+// wait until at most n of this wavefront's vector-memory operations are outstanding
+template <int STEP>
+__device__ __forceinline__ void wait_vmcnt_steps(int steps) {
+  // s_waitcnt simm16: vmcnt[3:0], expcnt[6:4] (7 = no wait), lgkmcnt[11:8] (15 = no
+  // wait), vmcnt[5:4] in [15:14]
+#define VLA_WAITVM(v) __builtin_amdgcn_s_waitcnt(((v) & 0xF) | 0x70 | 0xF00 | (((v) >> 4) << 14))
+  switch (steps) {
+    case 0: VLA_WAITVM(0); break;
+    case 1: VLA_WAITVM(STEP); break;
+    case 2: VLA_WAITVM(2 * STEP); break;
+    case 3: VLA_WAITVM(3 * STEP); break;
+    case 4: VLA_WAITVM(4 * STEP); break;
+    case 5: VLA_WAITVM(5 * STEP); break;
+    case 6: VLA_WAITVM(6 * STEP); break;
+    default: VLA_WAITVM(0); break;
+  }
+#undef VLA_WAITVM
+}
+
+template <int EPI, int BM, int BN, int BK, int NS>
 __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs a, int tiles_m, int tiles,
                                                         int ksteps) {
-  using G = GemmTile<BM, BN>;
-  constexpr int MT = G::MT, NT = G::NT;
-  __shared__ __attribute__((aligned(16))) bf16_t smem[2 * G::STAGE];
+  using G = GemmTile<BM, BN, BK, NS>;
+  constexpr int MT = G::MT, NT = G::NT, LOADS = G::LOADS;
+  static_assert(LOADS * (NS - 1) <= 63 && NS - 2 <= 6, "vmcnt range");
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[G::LDS];
 
   const int per_xcd = (tiles + kXcds - 1) / kXcds;
   const int slot = blockIdx.x % (kXcds * per_xcd);
@@ -54,12 +89,32 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs a, int tiles_m,
   const int m0 = (t % tiles_m) * BM, n0 = (t / tiles_m) * BN;
   const int M = a.M, K = a.K;
   const int kt0 = z * ksteps;
-  const int nk = min(K / kBK - kt0, ksteps);
+  const int nk = min(K / BK - kt0, ksteps);
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
-  const bf16_t* A = (const bf16_t*)a.A;
-  const bf16_t* W = (const bf16_t*)a.W;
+
+  // this lane's source pointers for its LOADS DMA loads (rows past M re-read row M-1)
+  const bf16_t* src[LOADS];
+#pragma unroll
+  for (int j = 0; j < LOADS; ++j) {
+    const int row = (wave * LOADS + j) * G::RPI + lane / G::CPR;
+    const int kc = G::pos(row, lane % G::CPR);  // pos() is an involution in kc
+    if (row < BM) {
+      const int ar = min(m0 + row, M - 1);
+      src[j] = (const bf16_t*)a.A + (int64_t)ar * K + (int64_t)kt0 * BK + kc * 8;
+    } else {
+      src[j] = (const bf16_t*)a.W + (int64_t)(n0 + row - BM) * K + (int64_t)kt0 * BK + kc * 8;
+    }
+  }
+  auto issue = [&](int kt) {
+    unsigned char* st = smem + (kt % NS) * G::STAGE + wave * LOADS * 1024;
+#pragma unroll
+    for (int j = 0; j < LOADS; ++j)
+      __builtin_amdgcn_global_load_lds((const void*)(src[j] + kt * BK),
+                                       (__attribute__((address_space(3))) void*)(st + j * 1024),
+                                       16, 0, 0);
+  };
 
   f32x4_t acc[MT][NT];
 #pragma unroll
@@ -67,62 +122,36 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs a, int tiles_m,
 #pragma unroll
     for (int j = 0; j < NT; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  u32x4_t ra[G::ACH], rw[G::WCH];
-  auto gload = [&](int kt) {
-    const int k0 = (kt0 + kt) * kBK;
 #pragma unroll
-    for (int i = 0; i < G::ACH; ++i) {
-      const int c = tid + 256 * i;
-      const int row = m0 + (c >> 3), kc = (c & 7) * 8;
-      ra[i] = row < M ? *(const u32x4_t*)(A + (int64_t)row * K + k0 + kc) : u32x4_t{0, 0, 0, 0};
-    }
-#pragma unroll
-    for (int i = 0; i < G::WCH; ++i) {
-      const int c = tid + 256 * i;
-      rw[i] = *(const u32x4_t*)(W + (int64_t)(n0 + (c >> 3)) * K + k0 + (c & 7) * 8);
-    }
-  };
-  auto lstore = [&](bf16_t* st) {
-#pragma unroll
-    for (int i = 0; i < G::ACH; ++i) {
-      const int c = tid + 256 * i;
-      *(u32x4_t*)(st + (c >> 3) * kPitch + (c & 7) * 8) = ra[i];
-    }
-#pragma unroll
-    for (int i = 0; i < G::WCH; ++i) {
-      const int c = tid + 256 * i;
-      *(u32x4_t*)(st + (BM + (c >> 3)) * kPitch + (c & 7) * 8) = rw[i];
-    }
-  };
-
-  if (nk > 0) {
-    gload(0);
-    lstore(smem);
-  }
-  __syncthreads();
+  for (int s = 0; s < NS - 1; ++s)
+    if (s < nk) issue(s);
   for (int kt = 0; kt < nk; ++kt) {
-    const bool more = kt + 1 < nk;
-    if (more) gload(kt + 1);
-    const bf16_t* As = smem + (kt & 1) * G::STAGE;
-    const bf16_t* Ws = As + BM * kPitch;
+    // stage kt has landed once at most (issued - kt - 1) stages are outstanding
+    wait_vmcnt_steps<LOADS>(min(nk, NS - 1 + kt) - kt - 1);
+    // every wavefront's loads of stage kt are in LDS, and every wavefront's reads of
+    // stage kt-1 have returned (lgkmcnt), so that stage may be refilled. A bare
+    // barrier: a fenced one would also drain the loads still in flight.
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    if (kt + NS - 1 < nk) issue(kt + NS - 1);
+    const unsigned char* st = smem + (kt % NS) * G::STAGE;
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      const int kk = ks * 32 + 8 * (lane >> 4);
+    for (int ks = 0; ks < BK / 32; ++ks) {
+      const int kc = ks * 4 + (lane >> 4);
       bf16x8_t bf[NT];
 #pragma unroll
-      for (int ni = 0; ni < NT; ++ni)
-        bf[ni] = *(const bf16x8_t*)(Ws + (wn * G::WN + ni * 16 + (lane & 15)) * kPitch + kk);
+      for (int ni = 0; ni < NT; ++ni) {
+        const int r = BM + wn * G::WN + ni * 16 + (lane & 15);
+        bf[ni] = *(const bf16x8_t*)(st + r * G::ROWB + (G::pos(r, kc) << 4));
+      }
 #pragma unroll
       for (int mi = 0; mi < MT; ++mi) {
-        const bf16x8_t af =
-            *(const bf16x8_t*)(As + (wm * G::WM + mi * 16 + (lane & 15)) * kPitch + kk);
+        const int r = wm * G::WM + mi * 16 + (lane & 15);
+        const bf16x8_t af = *(const bf16x8_t*)(st + r * G::ROWB + (G::pos(r, kc) << 4));
 #pragma unroll
         for (int ni = 0; ni < NT; ++ni)
           acc[mi][ni] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bf[ni], acc[mi][ni], 0, 0, 0);
       }
     }
-    if (more) lstore(smem + ((kt + 1) & 1) * G::STAGE);
-    __syncthreads();
   }
 
   // accumulator element e of tile (mi, ni): row 4*(lane/16)+e, column lane%16
@@ -157,12 +186,12 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs a, int tiles_m,
   }
 }
 
-// x[row] += sum over splits of the partials (split order), rounded to bf16;
-// then, if u is given, u[row] = RMSNorm(x[row]) with fp32 statistics. One
-// workgroup per row; each thread keeps up to 4 chunks of 8 columns in registers.
+// x[row] += sum over splits of the partials (split order), x the fp32 residual;
+// then, if u is given, u[row] = RMSNorm(x[row]) in bf16 with fp32 statistics.
+// One workgroup per row; each thread keeps up to 4 chunks of 8 columns in registers.
 constexpr int kResidMaxChunks = 4;
 __global__ __launch_bounds__(256) void resid_norm_kernel(const float* ws, int splits, int M, int N,
-                                                         bf16_t* x, bf16_t* u, const float* g,
+                                                         float* x, bf16_t* u, const float* g,
                                                          float eps) {
   __shared__ float red[4];
   const int row = blockIdx.x, tid = threadIdx.x;
@@ -173,8 +202,13 @@ __global__ __launch_bounds__(256) void resid_norm_kernel(const float* ws, int sp
   for (int j = 0; j < kResidMaxChunks; ++j) {
     const int c = tid + 256 * j;
     if (c >= nch) continue;
-    bf16_t* xp = x + (size_t)row * N + c * 8;
-    unpack8(*(const u32x4_t*)xp, v[j]);
+    float* xp = x + (size_t)row * N + c * 8;
+    const f32x4_t x0 = *(const f32x4_t*)xp, x1 = *(const f32x4_t*)(xp + 4);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[j][i] = x0[i];
+      v[j][4 + i] = x1[i];
+    }
     for (int s = 0; s < splits; ++s) {
       const float* p = ws + ((size_t)s * M + row) * N + c * 8;
       const f32x4_t p0 = *(const f32x4_t*)p, p1 = *(const f32x4_t*)(p + 4);
@@ -184,16 +218,10 @@ __global__ __launch_bounds__(256) void resid_norm_kernel(const float* ws, int sp
         v[j][4 + i] += p1[i];
       }
     }
-    u32x4_t o;
+    *(f32x4_t*)xp = f32x4_t{v[j][0], v[j][1], v[j][2], v[j][3]};
+    *(f32x4_t*)(xp + 4) = f32x4_t{v[j][4], v[j][5], v[j][6], v[j][7]};
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const bf16_t lo = f32_to_bf16(v[j][2 * i]), hi = f32_to_bf16(v[j][2 * i + 1]);
-      o[i] = (uint32_t)lo | ((uint32_t)hi << 16);
-      v[j][2 * i] = bf16_to_f32(lo);
-      v[j][2 * i + 1] = bf16_to_f32(hi);
-      ss += v[j][2 * i] * v[j][2 * i] + v[j][2 * i + 1] * v[j][2 * i + 1];
-    }
-    *(u32x4_t*)xp = o;
+    for (int i = 0; i < 8; ++i) ss += v[j][i] * v[j][i];
   }
   if (u == nullptr) return;
   ss = wave_sum(ss);
@@ -296,59 +324,71 @@ static hipError_t gemm_f32_launch(const GemmArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <int EPI, int BM, int BN>
+// q/k/v split-K reduction: sums the partials of each RoPE pair (split order) and
+// applies the same epilogue as the unsplit kernel (rotation, query buffer, paged
+// K/V). One workgroup per row.
+__global__ __launch_bounds__(256) void qkv_reduce_kernel(GemmArgs a, int splits) {
+  const int row = blockIdx.x;
+  for (int cp = threadIdx.x; cp < a.N / 2; cp += 256) {
+    float lo = 0.f, hi = 0.f;
+    for (int s = 0; s < splits; ++s) {
+      const float2 v = *(const float2*)(a.ws + ((size_t)s * a.M + row) * a.N + 2 * cp);
+      lo += v.x;
+      hi += v.y;
+    }
+    epi_qkv_pair<bf16_t>(a.ctx, row, 2 * cp, lo, hi);
+  }
+}
+
+template <int EPI, int BM, int BN, int BK, int NS>
 static void gemm_bf16_go(const GemmArgs& a, int splits, int ksteps, hipStream_t s) {
   const int tiles_m = (a.M + BM - 1) / BM;
   const int tiles = tiles_m * (a.N / BN);
   const int per_xcd = (tiles + kXcds - 1) / kXcds;
-  launch_k(gemm_bf16_kernel<EPI, BM, BN>, dim3(kXcds * per_xcd * splits), dim3(256), 0, s, a,
-           tiles_m, tiles, ksteps);
+  launch_k(gemm_bf16_kernel<EPI, BM, BN, BK, NS>, dim3(kXcds * per_xcd * splits), dim3(256), 0,
+           s, a, tiles_m, tiles, ksteps);
 }
 
-template <int EPI>
-static void gemm_bf16_shape(const GemmArgs& a, int bm, int bn, int splits, int ksteps,
-                            hipStream_t s) {
-  if (bm == 128 && bn == 128) gemm_bf16_go<EPI, 128, 128>(a, splits, ksteps, s);
-  else if (bm == 128) gemm_bf16_go<EPI, 128, 64>(a, splits, ksteps, s);
-  else if (bn == 128) gemm_bf16_go<EPI, 64, 128>(a, splits, ksteps, s);
-  else gemm_bf16_go<EPI, 64, 64>(a, splits, ksteps, s);
-}
-
-// Tile shape: start from 128 x 128 (64 rows for short chunks) and narrow N, then
-// M, while fewer than 192 tiles would run. Residual projections also split K so
-// that about 256 workgroups run, each with at least 4 K steps.
+// Shapes, measured at the 256-row chunks of the Qwen2.5-1.5B shape: the wide gated
+// projection takes 128 x 128 tiles with 32-deep K steps in a 4-stage ring (one
+// weight read per two 128-row tiles, sharing an XCD's L2); every other
+// projection takes 64 x 64 tiles with 64-deep K steps in a 4-stage ring and, when
+// that leaves fewer than about 384 workgroups, splits K (at least 4 steps per
+// split). Split projections reduce their fp32 partials in a second kernel: the
+// residual add (+ next RMSNorm), or RoPE + K/V write for q/k/v.
 static hipError_t gemm_bf16(const GemmArgs& a, hipStream_t s) {
-  if (a.K % kBK != 0 || a.N % 64 != 0 || a.M < 1) return hipErrorInvalidValue;
-  int bm = a.M > 64 ? 128 : 64;
-  int bn = a.N % 128 == 0 ? 128 : 64;
-  auto ntiles = [&](int m, int n) { return ((a.M + m - 1) / m) * (a.N / n); };
-  if (ntiles(bm, bn) < 192 && bn == 128) bn = 64;
-  if (ntiles(bm, bn) < 192 && bm == 128) bm = 64;
-  const int tiles = ntiles(bm, bn);
-  const int ksteps_all = a.K / kBK;
-  int splits = 1;
-  if (a.epi == EPI_RESID) {
-    splits = std::max(1, std::min(16, (256 + tiles - 1) / tiles));
-    while (splits > 1 && ksteps_all / splits < 4) --splits;
-    while (splits > 1 && (size_t)splits * a.M * a.N > a.ws_elems) --splits;
-    if ((size_t)a.M * a.N > a.ws_elems || a.ws == nullptr) return hipErrorInvalidValue;
-    if (a.N % 8 != 0 || a.N / 8 > 256 * kResidMaxChunks) return hipErrorInvalidValue;
+  if (a.K % 64 != 0 || a.N % 64 != 0 || a.M < 1) return hipErrorInvalidValue;
+  if (a.epi == EPI_SWIGLU) {
+    if (a.M > 64 && a.N % 128 == 0)
+      gemm_bf16_go<EPI_SWIGLU, 128, 128, 32, 4>(a, 1, a.K / 32, s);
+    else
+      gemm_bf16_go<EPI_SWIGLU, 64, 64, 64, 4>(a, 1, a.K / 64, s);
+    return hipGetLastError();
   }
+  if (a.epi != EPI_QKV && a.epi != EPI_RESID) return hipErrorInvalidValue;
+  const int tiles = ((a.M + 63) / 64) * (a.N / 64);
+  const int ksteps_all = a.K / 64;
+  int splits = std::max(1, std::min(8, (384 + tiles - 1) / tiles));
+  while (splits > 1 && ksteps_all / splits < 4) --splits;
+  while (splits > 1 && (size_t)splits * a.M * a.N > a.ws_elems) --splits;
+  if (a.ws == nullptr || (size_t)a.M * a.N > a.ws_elems) splits = 1;
   const int ksteps = (ksteps_all + splits - 1) / splits;
   splits = (ksteps_all + ksteps - 1) / ksteps;
-  switch (a.epi) {
-    case EPI_QKV: gemm_bf16_shape<EPI_QKV>(a, bm, bn, 1, ksteps, s); break;
-    case EPI_SWIGLU:
-      if (a.N % 64 != 0) return hipErrorInvalidValue;
-      gemm_bf16_shape<EPI_SWIGLU>(a, bm, bn, 1, ksteps, s);
-      break;
-    case EPI_RESID:
-      gemm_bf16_shape<EPI_PARTIAL>(a, bm, bn, splits, ksteps, s);
-      launch_k(resid_norm_kernel, dim3(a.M), dim3(256), 0, s, (const float*)a.ws, splits, a.M,
-               a.N, (bf16_t*)a.C, (bf16_t*)a.norm_out, a.norm_g, a.eps);
-      break;
-    default: return hipErrorInvalidValue;
+  if (a.epi == EPI_QKV) {
+    if (splits == 1) {
+      gemm_bf16_go<EPI_QKV, 64, 64, 64, 4>(a, 1, ksteps_all, s);
+    } else {
+      gemm_bf16_go<EPI_PARTIAL, 64, 64, 64, 4>(a, splits, ksteps, s);
+      launch_k(qkv_reduce_kernel, dim3(a.M), dim3(256), 0, s, a, splits);
+    }
+    return hipGetLastError();
   }
+  // residual projection: always through the partial buffer and the reduction kernel
+  if (a.ws == nullptr || (size_t)a.M * a.N > a.ws_elems) return hipErrorInvalidValue;
+  if (a.N % 8 != 0 || a.N / 8 > 256 * kResidMaxChunks) return hipErrorInvalidValue;
+  gemm_bf16_go<EPI_PARTIAL, 64, 64, 64, 4>(a, splits, ksteps, s);
+  launch_k(resid_norm_kernel, dim3(a.M), dim3(256), 0, s, (const float*)a.ws, splits, a.M, a.N,
+           (float*)a.C, (bf16_t*)a.norm_out, a.norm_g, a.eps);
   return hipGetLastError();
 }
 

@@ -25,27 +25,11 @@ __device__ __forceinline__ int64_t gemv_row(int g, int r) {
   }
 }
 
-__device__ __forceinline__ float dot8(const u32x4_t& w, const u32x4_t& x) {
-  float wf[8], xf[8];
-  unpack8(w, wf);
-  unpack8(x, xf);
-  float s = 0.f;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) s += wf[i] * xf[i];
-  return s;
-}
-__device__ __forceinline__ float dot4f(const u32x4_t& w, const u32x4_t& x) {
-  float s = 0.f;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) s += __uint_as_float(w[i]) * __uint_as_float(x[i]);
-  return s;
-}
-
 // One workgroup = 4 wavefronts; a wavefront owns RW whole rows at a time and
 // streams them with 16-byte loads, UNR chunks per lane per step (RW * UNR
-// independent loads in flight per lane). The input row (RMSNorm applied when
-// norm_g is given, rounded to the storage type as the prefill path does) sits
-// in LDS; partial sums are reduced across the wavefront with xor shuffles, so
+// independent loads in flight per lane). The input row sits in LDS (fp32 when
+// it is the normalised residual); partial sums are reduced across the wavefront
+// with xor shuffles, so
 // the epilogue of a row group needs no workgroup barrier.
 template <typename T, int EPI, int RW>
 __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(GemvArgs a, int ngroups) {
@@ -58,33 +42,36 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(GemvArgs a, int ngro
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int K = a.K;
   const int nch = K / CH;
-  const T* x = (const T*)a.x;
 
-  // input row -> LDS (optionally normalised)
-  float ss = 0.f;
-  for (int c = tid; c < nch; c += kGemvThreads) {
-    const u32x4_t v = *(const u32x4_t*)(x + (size_t)c * CH);
-    *(u32x4_t*)(xs + (size_t)c * CH) = v;
-    if constexpr (sizeof(T) == 2) {
-      float f[8];
-      unpack8(v, f);
+  // input row -> LDS. Every epilogue but the residual one reads the fp32 residual
+  // stream, normalises it (RMSNorm, fp32 statistics) and keeps it in fp32 (these
+  // projections run on the vector ALUs, so the input need not be rounded); the
+  // residual projections read activations already in the weight type.
+  if constexpr (EPI != EPI_RESID) {
+    f32x4_t* xs4 = (f32x4_t*)gsmem;
+    const f32x4_t* xf4 = (const f32x4_t*)a.x;
+    float ss = 0.f;
+    for (int i = tid; i < K / 4; i += kGemvThreads) {
+      const f32x4_t v = xf4[i];
+      xs4[i] = v;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) ss += f[i] * f[i];
-    } else {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) ss += __uint_as_float(v[i]) * __uint_as_float(v[i]);
+      for (int e = 0; e < 4; ++e) ss += v[e] * v[e];
     }
-  }
-  if (a.norm_g) {  // RMSNorm of the input row (fp32 statistics)
-    ss = wave_sum(ss);
-    if (lane == 0) ssq[wave] = ss;
-    __syncthreads();
-    float tot = 0.f;
+    if (a.norm_g) {
+      ss = wave_sum(ss);
+      if (lane == 0) ssq[wave] = ss;
+      __syncthreads();
+      float tot = 0.f;
 #pragma unroll
-    for (int w = 0; w < kGemvWaves; ++w) tot += ssq[w];
-    const float r = rsqrtf(tot / (float)K + a.eps);
-    for (int i = tid; i < K; i += kGemvThreads)
-      St<T>::st(xs, i, St<T>::ld(xs, i) * r * a.norm_g[i]);
+      for (int w = 0; w < kGemvWaves; ++w) tot += ssq[w];
+      const float rn = rsqrtf(tot / (float)K + a.eps);
+      const f32x4_t* g4 = (const f32x4_t*)a.norm_g;
+      for (int i = tid; i < K / 4; i += kGemvThreads) xs4[i] = xs4[i] * rn * g4[i];  // own elements
+    }
+  } else {
+    const T* x = (const T*)a.x;
+    for (int c = tid; c < nch; c += kGemvThreads)
+      *(u32x4_t*)(xs + (size_t)c * CH) = *(const u32x4_t*)(x + (size_t)c * CH);
   }
   __syncthreads();
 
@@ -112,11 +99,33 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(GemvArgs a, int ngro
 #pragma unroll
       for (int u = 0; u < UNR; ++u) {
         const int c = c0 + 64 * u;
-        const u32x4_t xv = c < nch ? *(const u32x4_t*)(xs + (size_t)c * CH) : u32x4_t{0, 0, 0, 0};
+        float xv[CH];
+        if constexpr (EPI != EPI_RESID) {
+          const f32x4_t* xp = (const f32x4_t*)gsmem + (size_t)c * (CH / 4);
+#pragma unroll
+          for (int i = 0; i < CH / 4; ++i) {
+            const f32x4_t q = c < nch ? xp[i] : f32x4_t{0.f, 0.f, 0.f, 0.f};
+            xv[4 * i] = q[0];
+            xv[4 * i + 1] = q[1];
+            xv[4 * i + 2] = q[2];
+            xv[4 * i + 3] = q[3];
+          }
+        } else {
+          const u32x4_t xr = c < nch ? *(const u32x4_t*)(xs + (size_t)c * CH) : u32x4_t{0, 0, 0, 0};
+          if constexpr (sizeof(T) == 2) unpack8(xr, xv);
+          else
+#pragma unroll
+            for (int i = 0; i < 4; ++i) xv[i] = __uint_as_float(xr[i]);
+        }
 #pragma unroll
         for (int r = 0; r < RW; ++r) {
-          if constexpr (sizeof(T) == 2) acc[r] += dot8(w[u][r], xv);
-          else acc[r] += dot4f(w[u][r], xv);
+          float wf[CH];
+          if constexpr (sizeof(T) == 2) unpack8(w[u][r], wf);
+          else
+#pragma unroll
+            for (int i = 0; i < 4; ++i) wf[i] = __uint_as_float(w[u][r][i]);
+#pragma unroll
+          for (int i = 0; i < CH; ++i) acc[r] += wf[i] * xv[i];
         }
       }
     }
@@ -132,10 +141,7 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(GemvArgs a, int ngro
 #pragma unroll
       for (int r = 0; r < RW; ++r) {
         const int64_t row = gemv_row<EPI, RW>(g, r);
-        if (lane == r && row < a.N) {
-          T* xo = (T*)a.out;
-          St<T>::st(xo, row, St<T>::ld(xo, row) + acc[r]);
-        }
+        if (lane == r && row < a.N) ((float*)a.out)[row] += acc[r];
       }
     } else if constexpr (EPI == EPI_SWIGLU) {
 #pragma unroll
@@ -172,7 +178,7 @@ static hipError_t gemv_launch_rw(const GemvArgs& a, hipStream_t s, int* grid_out
   int grid = (ngroups + kGemvWaves - 1) / kGemvWaves;
   grid = grid < kGemvMaxGrid ? grid : kGemvMaxGrid;
   if (grid_out) *grid_out = grid;
-  const uint32_t lds = (uint32_t)((size_t)a.K * sizeof(T));
+  const uint32_t lds = (uint32_t)((size_t)a.K * (EPI == EPI_RESID ? sizeof(T) : sizeof(float)));
   launch_k(gemv_kernel<T, EPI, RW>, dim3(grid), dim3(kGemvThreads), lds, s, a, ngroups);
   return hipGetLastError();
 }
@@ -203,7 +209,8 @@ static hipError_t gemv_dispatch(const GemvArgs& a, hipStream_t s, int* grid_out)
 }
 
 hipError_t launch_gemv(const GemvArgs& a, int dt, hipStream_t s, int* grid_out) {
-  if (a.K % 8 != 0 || a.K > 32768) return hipErrorInvalidValue;
+  // the input row lives in LDS: fp32 (residual inputs) or 16-bit, at most 64 KiB
+  if (a.K % 8 != 0 || a.K > (a.epi == EPI_RESID ? 32768 : 16384)) return hipErrorInvalidValue;
   return dt == DT_F32 ? gemv_dispatch<float>(a, s, grid_out)
                       : gemv_dispatch<bf16_t>(a, s, grid_out);
 }

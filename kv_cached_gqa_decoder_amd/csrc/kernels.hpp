@@ -57,8 +57,7 @@ struct KvGeom {
 // blocks starting at logical block cb0.
 struct FwdCtx {
   int layer = 0;
-  int64_t pos0 = 0;
-  const double* inv_freq = nullptr;  // [d/2] theta^(-2j/d), fp64
+  const float2* rope = nullptr;      // [n][d/2] (cos, sin) of row t's angles (launch_rope_table)
   void* kpool = nullptr;
   void* vpool = nullptr;
   KvGeom g{};
@@ -77,7 +76,7 @@ struct GemmArgs {
   const void* W = nullptr;  // [N][K] weights (physical layout)
   int M = 0, N = 0, K = 0;
   int epi = EPI_STORE;
-  void* C = nullptr;        // STORE [M][N]; RESID x [M][N] (+=); SWIGLU [M][N/2]
+  void* C = nullptr;        // STORE [M][N]; RESID fp32 x [M][N] (+=); SWIGLU [M][N/2]
   FwdCtx ctx;
   // bf16 RESID: split-K partials (fp32, [splits][M][N]) reduced by a second
   // kernel that adds them to x and, when norm_out is set, writes
@@ -90,13 +89,14 @@ struct GemmArgs {
 };
 
 struct GemvArgs {
-  const void* x = nullptr;      // [K] input row (activations)
+  const void* x = nullptr;      // [K] input row: the fp32 residual when norm_g is set,
+                                // else activations in the weight type
   const float* norm_g = nullptr;  // non-null: RMSNorm the input first
   float eps = 0.f;
   const void* W = nullptr;      // [N][K]
   int N = 0, K = 0;
   int epi = EPI_STORE;
-  void* out = nullptr;          // RESID x[N] (+=); SWIGLU act[N/2]; HEAD logits fp32[N]
+  void* out = nullptr;          // RESID fp32 x[N] (+=); SWIGLU act[N/2]; HEAD logits fp32[N]
   unsigned long long* argmax_part = nullptr;  // HEAD: one key per workgroup
   FwdCtx ctx;
 };
@@ -129,6 +129,12 @@ hipError_t launch_weight_logical(const void* phys, void* out, int dt, int layout
                                  int64_t rows, int64_t cols, int hq, int hkv, int d,
                                  hipStream_t s);
 hipError_t launch_fill_f32(float* p, float v, int64_t n, hipStream_t s);
+// (cos, sin) of pos * inv_freq[j] for rows t = 0..n-1 at positions pos0 + t: the
+// angle is formed in fp64 and reduced to [-pi, pi] in fp64, then fp32 sin/cos
+hipError_t launch_rope_table(int64_t pos0, int n, const double* inv_freq, int half,
+                             float2* tab, hipStream_t s);
+// x: the fp32 residual rows [n][H]; E and u in the activation type
+hipError_t launch_to_f32(const void* in, float* out, int64_t n, int dt, hipStream_t s);
 hipError_t launch_embed(const int* tokens, int token_scalar, int n, const void* E, void* x,
                         int H, int dt, unsigned long long* reset_cell, hipStream_t s);
 hipError_t launch_rmsnorm(const void* x, const float* g, void* u, int rows, int H, float eps,

@@ -118,6 +118,26 @@ hipError_t launch_weight_logical(const void* phys, void* out, int dt, int layout
 }
 
 // ---------------------------------------------------------------------------
+__global__ void rope_table_kernel(int64_t pos0, int n, const double* inv_freq, int half,
+                                  float2* tab) {
+  const int64_t total = (int64_t)n * half;
+  for (int64_t p = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; p < total;
+       p += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t t = p / half;
+    const int j = (int)(p % half);
+    const double ang = (double)(pos0 + t) * inv_freq[j];
+    const double red = fma(-rint(ang * 0.15915494309189535), 6.283185307179586, ang);
+    float sn, cs;
+    sincosf((float)red, &sn, &cs);
+    tab[p] = make_float2(cs, sn);
+  }
+}
+hipError_t launch_rope_table(int64_t pos0, int n, const double* inv_freq, int half, float2* tab,
+                             hipStream_t s) {
+  rope_table_kernel<<<grid_for((int64_t)n * half, 256), 256, 0, s>>>(pos0, n, inv_freq, half, tab);
+  return hipGetLastError();
+}
+
 __global__ void fill_f32_kernel(float* p, float v, int64_t n) {
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
        i += (int64_t)gridDim.x * blockDim.x)
@@ -129,14 +149,16 @@ hipError_t launch_fill_f32(float* p, float v, int64_t n, hipStream_t s) {
 }
 
 // ---------------------------------------------------------------------------
-// embedding rows; block 0 also clears the argmax cell of this pass
+// embedding rows (activation type) -> fp32 residual rows; block 0 also clears
+// the argmax cell of this pass
 template <typename T>
-__global__ void embed_kernel(const int* tokens, int token_scalar, int n, const T* E, T* x, int H,
-                             unsigned long long* reset_cell) {
+__global__ void embed_kernel(const int* tokens, int token_scalar, int n, const T* E, float* x,
+                             int H, unsigned long long* reset_cell) {
   if (reset_cell && blockIdx.x == 0 && threadIdx.x == 0) *reset_cell = 0ull;
   for (int t = blockIdx.x; t < n; t += gridDim.x) {
     const int64_t id = tokens ? tokens[t] : token_scalar;
-    for (int i = threadIdx.x; i < H; i += blockDim.x) x[(int64_t)t * H + i] = E[id * H + i];
+    for (int i = threadIdx.x; i < H; i += blockDim.x)
+      x[(int64_t)t * H + i] = St<T>::ld(E, id * H + i);
   }
 }
 hipError_t launch_embed(const int* tokens, int token_scalar, int n, const void* E, void* x, int H,
@@ -146,61 +168,57 @@ hipError_t launch_embed(const int* tokens, int token_scalar, int n, const void* 
     embed_kernel<float><<<g, 256, 0, s>>>(tokens, token_scalar, n, (const float*)E, (float*)x, H,
                                           reset_cell);
   else
-    embed_kernel<bf16_t><<<g, 256, 0, s>>>(tokens, token_scalar, n, (const bf16_t*)E, (bf16_t*)x,
+    embed_kernel<bf16_t><<<g, 256, 0, s>>>(tokens, token_scalar, n, (const bf16_t*)E, (float*)x,
                                            H, reset_cell);
   return hipGetLastError();
 }
 
-// ---------------------------------------------------------------------------
-// RMSNorm, one wavefront per row, fp32 statistics: u = x * (mean(x^2) + eps)^-1/2 * g.
-// 16-byte loads: 8 bf16 or 4 fp32 values per lane per step; H is a multiple of 64.
 template <typename T>
-__global__ __launch_bounds__(256) void rmsnorm_kernel(const T* x, const float* g, T* u, int rows,
-                                                      int H, float eps) {
-  constexpr int CH = 16 / sizeof(T);
+__global__ void to_f32_kernel(const T* in, float* out, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+       i += (int64_t)gridDim.x * blockDim.x)
+    out[i] = St<T>::ld(in, i);
+}
+hipError_t launch_to_f32(const void* in, float* out, int64_t n, int dt, hipStream_t s) {
+  const int g = grid_for(n, 256);
+  if (dt == DT_F32) to_f32_kernel<float><<<g, 256, 0, s>>>((const float*)in, out, n);
+  else to_f32_kernel<bf16_t><<<g, 256, 0, s>>>((const bf16_t*)in, out, n);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// RMSNorm of fp32 residual rows into the activation type, one wavefront per
+// row, fp32 statistics: u = x * (mean(x^2) + eps)^-1/2 * g. H is a multiple of 64.
+template <typename T>
+__global__ __launch_bounds__(256) void rmsnorm_kernel(const float* x, const float* g, T* u,
+                                                      int rows, int H, float eps) {
   const int lane = threadIdx.x & 63;
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (row >= rows) return;
-  const T* xr = x + (int64_t)row * H;
+  const float* xr = x + (int64_t)row * H;
   T* ur = u + (int64_t)row * H;
   float ss = 0.f;
-  for (int c = lane; c < H / CH; c += 64) {
-    const u32x4_t w = *(const u32x4_t*)(xr + c * CH);
-    float f[CH];
-    if constexpr (CH == 8) unpack8(w, f);
-    else
+  for (int c = lane; c < H / 4; c += 64) {
+    const f32x4_t v = *(const f32x4_t*)(xr + c * 4);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) f[i] = __uint_as_float(w[i]);
-#pragma unroll
-    for (int i = 0; i < CH; ++i) ss += f[i] * f[i];
+    for (int i = 0; i < 4; ++i) ss += v[i] * v[i];
   }
   ss = wave_sum(ss);
   const float r = rsqrtf(ss / (float)H + eps);
-  for (int c = lane; c < H / CH; c += 64) {
-    const u32x4_t w = *(const u32x4_t*)(xr + c * CH);
-    float f[CH];
-    u32x4_t o;
-    if constexpr (CH == 8) {
-      unpack8(w, f);
+  for (int c = lane; c < H / 4; c += 64) {
+    const f32x4_t v = *(const f32x4_t*)(xr + c * 4);
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        o[i] = (uint32_t)f32_to_bf16(f[2 * i] * r * g[c * CH + 2 * i]) |
-               ((uint32_t)f32_to_bf16(f[2 * i + 1] * r * g[c * CH + 2 * i + 1]) << 16);
-    } else {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) o[i] = __float_as_uint(__uint_as_float(w[i]) * r * g[c * CH + i]);
-    }
-    *(u32x4_t*)(ur + c * CH) = o;
+    for (int i = 0; i < 4; ++i) St<T>::st(ur, (size_t)c * 4 + i, v[i] * r * g[c * 4 + i]);
   }
 }
 hipError_t launch_rmsnorm(const void* x, const float* g, void* u, int rows, int H, float eps,
                           int dt, hipStream_t s) {
   const int grid = (rows + 3) / 4;
   if (dt == DT_F32)
-    launch_k(rmsnorm_kernel<float>, dim3(grid), dim3(256), 0, s, (const float*)x, g, (float*)u, rows,
-             H, eps);
+    launch_k(rmsnorm_kernel<float>, dim3(grid), dim3(256), 0, s, (const float*)x, g, (float*)u,
+             rows, H, eps);
   else
-    launch_k(rmsnorm_kernel<bf16_t>, dim3(grid), dim3(256), 0, s, (const bf16_t*)x, g, (bf16_t*)u,
+    launch_k(rmsnorm_kernel<bf16_t>, dim3(grid), dim3(256), 0, s, (const float*)x, g, (bf16_t*)u,
              rows, H, eps);
   return hipGetLastError();
 }

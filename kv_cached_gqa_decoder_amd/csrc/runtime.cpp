@@ -94,6 +94,7 @@ struct vla_model {
   std::vector<void*> wqkv, wo, wgu, wdown;
   float* norm_ones = nullptr;   // all RMSNorm weights are 1
   double* inv_freq = nullptr;
+  float2* rope_tab = nullptr;   // (cos, sin) of the current pass's rows, [max_chunk][d/2]
 
   // cache
   void* kpool = nullptr;
@@ -271,11 +272,10 @@ int last_block_ntok(const vla_model* m) {
   return 0;
 }
 
-FwdCtx make_ctx(vla_model* m, int layer, int64_t pos0, int cb0, int cslot0) {
+FwdCtx make_ctx(vla_model* m, int layer, int cb0, int cslot0) {
   FwdCtx c;
   c.layer = layer;
-  c.pos0 = pos0;
-  c.inv_freq = m->inv_freq;
+  c.rope = m->rope_tab;
   c.kpool = m->kpool;
   c.vpool = m->vpool;
   c.g = m->geom;
@@ -295,6 +295,8 @@ void run_layers(vla_model* m, int n, int64_t pos0, int cb0, int cslot0, bool dec
   const int H = c.hidden, qd = c.n_heads * c.head_dim;
   const int nqkv = (c.n_heads + 2 * c.n_kv_heads) * c.head_dim;
   const int nlb = logical_blocks(m);
+  // the rows' RoPE (cos, sin), shared by every layer of this pass
+  HIPCHK(launch_rope_table(pos0, n, m->inv_freq, c.head_dim / 2, m->rope_tab, st));
   AttnArgs at;
   at.q = m->qbuf;
   at.out = m->ao;
@@ -317,7 +319,7 @@ void run_layers(vla_model* m, int n, int64_t pos0, int cb0, int cslot0, bool dec
 
   for (int l = 0; l < c.n_layers; ++l) {
     at.layer = l;
-    const FwdCtx ctx = make_ctx(m, l, pos0, cb0, cslot0);
+    const FwdCtx ctx = make_ctx(m, l, cb0, cslot0);
     if (decode) {
       GemvArgs g;
       g.x = m->x;
@@ -372,6 +374,8 @@ void run_layers(vla_model* m, int n, int64_t pos0, int cb0, int cslot0, bool dec
       q.K = H;
       q.epi = EPI_QKV;
       q.ctx = ctx;
+      q.ws = m->gemm_ws;
+      q.ws_elems = m->gemm_ws_elems;
       LAUNCH(m, VLA_K_GEMM_QKV, st, launch_gemm(q, m->dt, st));
       LAUNCH(m, VLA_K_ATTN_PREFILL, st, launch_attention(at, m->dt, st));
       GemmArgs o;
@@ -422,7 +426,7 @@ void run_layers(vla_model* m, int n, int64_t pos0, int cb0, int cslot0, bool dec
 void run_head(vla_model* m, int row, hipStream_t st) {
   const vla_config& c = m->cfg;
   GemvArgs h;
-  h.x = (const char*)m->x + (size_t)row * c.hidden * m->esz;
+  h.x = (const float*)m->x + (size_t)row * c.hidden;
   h.norm_g = m->norm_ones;
   h.eps = c.rms_eps;
   h.W = m->head;
@@ -583,6 +587,7 @@ vla_status vla_model_create(const vla_config* cfg, vla_model** out) {
     }
     m->norm_ones = (float*)dalloc(m, H * sizeof(float));
     m->inv_freq = (double*)dalloc(m, d / 2 * sizeof(double));
+    m->rope_tab = (float2*)dalloc(m, (size_t)c.max_chunk * (d / 2) * sizeof(float2));
     const size_t pool_bytes = (size_t)c.n_layers * c.num_blocks * hkv * c.block_tokens * d * e;
     m->kpool = dalloc(m, pool_bytes);
     m->vpool = dalloc(m, pool_bytes);
@@ -591,7 +596,7 @@ vla_status vla_model_create(const vla_config* cfg, vla_model** out) {
     HIPCHK(hipMemset(m->vpool, 0, pool_bytes));
     m->meankeys = (double*)dalloc(m, (size_t)c.n_layers * c.max_frames * hkv * d * sizeof(double));
     const size_t mc = c.max_chunk;
-    m->x = dalloc(m, mc * H * e);
+    m->x = dalloc(m, mc * H * sizeof(float));  // the residual stream is fp32
     m->u = dalloc(m, mc * H * e);
     m->qbuf = dalloc(m, mc * hq * d * e);
     m->ao = dalloc(m, mc * hq * d * e);
@@ -602,7 +607,7 @@ vla_status vla_model_create(const vla_config* cfg, vla_model** out) {
     if (m->dt == DT_BF16) {
       m->part_o = (float*)dalloc(m, (size_t)kPartRows * d * sizeof(float));
       m->part_ml = (float*)dalloc(m, (size_t)kPartRows * 2 * sizeof(float));
-      m->gemm_ws_elems = (size_t)kGemmSplitsMax * mc * H;
+      m->gemm_ws_elems = (size_t)kGemmSplitsMax * mc * std::max(H, (hq + 2 * hkv) * d);
       m->gemm_ws = (float*)dalloc(m, m->gemm_ws_elems * sizeof(float));
 
     }
@@ -650,8 +655,7 @@ vla_status vla_prefill_chunk(vla_model* m, const int32_t* tokens, const void* em
         staging_upload(m->st_tok, m->d_tokens, (size_t)n * sizeof(int), st);
         HIPCHK(launch_embed(m->d_tokens, 0, n, m->embed, m->x, m->cfg.hidden, m->dt, nullptr, st));
       } else {
-        HIPCHK(hipMemcpyAsync(m->x, embeds, (size_t)n * m->cfg.hidden * m->esz,
-                              hipMemcpyDeviceToDevice, st));
+        HIPCHK(launch_to_f32(embeds, (float*)m->x, (int64_t)n * m->cfg.hidden, m->dt, st));
       }
       run_layers(m, n, seg.start_pos, seg_blk0(m, si), 0, /*decode=*/false, st);
       run_head(m, n - 1, st);

@@ -20,3 +20,19 @@ def oracle_c_built():
     if not rng.have_c():
         build.build()
     return True
+
+
+@pytest.fixture(autouse=True)
+def _report_worst_logits(request):
+    """After each GPU test, print the worst logits cosine / max relative error it saw."""
+    yield
+    if request.node.get_closest_marker("gpu") is None:
+        return
+    try:
+        from tests import gpu_util
+    except Exception:
+        return
+    for kind, (cos, rel) in sorted(gpu_util.WORST.items()):
+        print(f"[{request.node.name}] worst {kind}: cos {cos:.7f} rel {rel:.3e}", file=sys.stderr,
+              flush=True)
+    gpu_util.WORST.clear()
