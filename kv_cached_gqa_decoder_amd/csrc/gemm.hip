@@ -7,6 +7,8 @@
 // ("Running VLAs at Real-time Speed", section 4.2: both gated projections in
 // one GEMM, only the gated product written back; section 4.4: bias-free
 // residual and activation fused into the GEMM epilogue).
+#include <hip/hip_fp16.h>
+
 #include <algorithm>
 
 #include "common.hpp"
@@ -71,6 +73,43 @@ __device__ __forceinline__ void wait_vmcnt_steps(int steps) {
     default: VLA_WAITVM(0); break;
   }
 #undef VLA_WAITVM
+}
+
+// Epilogue of a wavefront's (MT x NT) tiles. Accumulator element e of tile
+// (mi, ni) is row 4*(lane/16)+e, column lane%16 of that 16 x 16 tile.
+template <int EPI, int MT, int NT, int WM, int WN>
+__device__ __forceinline__ void gemm_epilogue(const GemmArgs& a, f32x4_t (&acc)[MT][NT], int m0,
+                                              int n0, int z, int wm, int wn, int lane) {
+  const int M = a.M;
+#pragma unroll
+  for (int mi = 0; mi < MT; ++mi) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int row = m0 + wm * WM + mi * 16 + 4 * (lane >> 4) + e;
+      if constexpr (EPI == EPI_SWIGLU) {
+        // tiles (ni, ni+1), ni even: gate rows f and the matching up rows (LAYOUT_GATEUP)
+#pragma unroll
+        for (int ni = 0; ni < NT; ni += 2) {
+          const int f = (n0 + wn * WN + ni * 16) / 2 + (lane & 15);
+          if (row < M)
+            St<bf16_t>::st((bf16_t*)a.C, (size_t)row * (a.N / 2) + f,
+                           silu(acc[mi][ni][e]) * acc[mi][ni + 1][e]);
+        }
+      } else {
+#pragma unroll
+        for (int ni = 0; ni < NT; ++ni) {
+          const int col = n0 + wn * WN + ni * 16 + (lane & 15);
+          const float v = acc[mi][ni][e];
+          if constexpr (EPI == EPI_QKV) {
+            const float partner = __shfl_xor(v, 1, 64);
+            if (row < M && (col & 1) == 0) epi_qkv_pair<bf16_t>(a.ctx, row, col, v, partner);
+          } else {  // EPI_PARTIAL
+            if (row < M) a.ws[((size_t)z * M + row) * a.N + col] = v;
+          }
+        }
+      }
+    }
+  }
 }
 
 template <int EPI, int BM, int BN, int BK, int NS>
@@ -154,36 +193,7 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs a, int tiles_m,
     }
   }
 
-  // accumulator element e of tile (mi, ni): row 4*(lane/16)+e, column lane%16
-#pragma unroll
-  for (int mi = 0; mi < MT; ++mi) {
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int row = m0 + wm * G::WM + mi * 16 + 4 * (lane >> 4) + e;
-      if constexpr (EPI == EPI_SWIGLU) {
-        // tiles (ni, ni+1), ni even: gate rows f and the matching up rows (LAYOUT_GATEUP)
-#pragma unroll
-        for (int ni = 0; ni < NT; ni += 2) {
-          const int f = (n0 + wn * G::WN + ni * 16) / 2 + (lane & 15);
-          if (row < M)
-            St<bf16_t>::st((bf16_t*)a.C, (size_t)row * (a.N / 2) + f,
-                           silu(acc[mi][ni][e]) * acc[mi][ni + 1][e]);
-        }
-      } else {
-#pragma unroll
-        for (int ni = 0; ni < NT; ++ni) {
-          const int col = n0 + wn * G::WN + ni * 16 + (lane & 15);
-          const float v = acc[mi][ni][e];
-          if constexpr (EPI == EPI_QKV) {
-            const float partner = __shfl_xor(v, 1, 64);
-            if (row < M && (col & 1) == 0) epi_qkv_pair<bf16_t>(a.ctx, row, col, v, partner);
-          } else {  // EPI_PARTIAL
-            if (row < M) a.ws[((size_t)z * M + row) * a.N + col] = v;
-          }
-        }
-      }
-    }
-  }
+  gemm_epilogue<EPI, MT, NT, G::WM, G::WN>(a, acc, m0, n0, z, wm, wn, lane);
 }
 
 // x[row] += sum over splits of the partials (split order), x the fp32 residual;
@@ -324,6 +334,179 @@ static hipError_t gemm_f32_launch(const GemmArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// INT4 group-128 weights ("Rebuilding Kshipra Around Memory", section 2), the
+// prefill projections: C = sum over groups g of s[g][n] * (A_g q_g^T) (scales
+// stored [K/128][N]). Each K step is one group of 128; its 64 column scales ride
+// in the same DMA ring as the operands. The A tile (BM rows of 256 bytes, 16-byte chunk kc
+// of row r at position kc ^ (r % 16)) and the packed W tile (BN rows of 64 bytes
+// of codes, chunk kc at kc ^ ((r / 2) % 4)) stream into an NS-stage LDS ring by
+// DMA; once per step the workgroup widens the W codes to bf16 (exact: integers
+// in [-8, 7]) into a padded LDS tile; the matrix cores accumulate the group's
+// products into a temporary, and s (fp16, widened) scales it into the fp32 sum,
+// so no product q * s is ever rounded to bf16.
+// ---------------------------------------------------------------------------
+template <int BM, int BN, int NS>
+struct GemmW4Tile {
+  static constexpr int WM = BM / 2, WN = BN / 2;
+  static constexpr int MT = WM / 16, NT = WN / 16;
+  // a stage: A tile, W codes, and one 1 KiB slot whose first BN * 2 bytes are the
+  // group's scales for the tile's columns (8 copies of the 128 bytes)
+  static constexpr int ASTAGE = BM * 256, WSTAGE = BN * 64, STAGE = ASTAGE + WSTAGE + 1024;
+  static constexpr int ALOADS = BM / 4 / 4, WLOADS = BN / 16 / 4;  // DMA loads per wavefront
+  static constexpr int LOADS = ALOADS + WLOADS;  // wavefront 0 adds the scale load
+  static_assert(BN == 64, "one scale DMA covers 64 columns");
+  static constexpr int WBP = 128 + 8;  // bf16 pitch of the widened W tile
+  static constexpr int LDS = NS * STAGE + BN * WBP * 2;
+};
+
+template <int EPI, int BM, int BN, int NS>
+__global__ __launch_bounds__(256) void gemm_w4_kernel(GemmArgs a, int tiles_m, int tiles,
+                                                      int ksteps) {
+  using G = GemmW4Tile<BM, BN, NS>;
+  constexpr int MT = G::MT, NT = G::NT, LOADS = G::LOADS;
+  static_assert(LOADS * (NS - 1) <= 63 && NS - 2 <= 6 && G::WLOADS >= 1, "shape");
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[G::LDS];
+  bf16_t* wb = (bf16_t*)(smem + NS * G::STAGE);
+
+  const int per_xcd = (tiles + kXcds - 1) / kXcds;
+  const int slot = blockIdx.x % (kXcds * per_xcd);
+  const int z = blockIdx.x / (kXcds * per_xcd);
+  const int t = (slot % kXcds) * per_xcd + slot / kXcds;
+  if (t >= tiles) return;
+  const int m0 = (t % tiles_m) * BM, n0 = (t / tiles_m) * BN;
+  const int M = a.M, K = a.K, ngk = K / 128;
+  const int kt0 = z * ksteps;
+  const int nk = min(ngk - kt0, ksteps);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const uint8_t* Wq = (const uint8_t*)a.W;
+  const __half* Sc = (const __half*)(Wq + (size_t)a.N * K / 2);  // [K/128][N]
+
+  // DMA sources: A rows (4 per load, 16 chunks of 16 bytes each), W code rows (16 per load)
+  const unsigned char* srcA[G::ALOADS];
+  const unsigned char* srcW[G::WLOADS];
+#pragma unroll
+  for (int j = 0; j < G::ALOADS; ++j) {
+    const int row = (wave * G::ALOADS + j) * 4 + (lane >> 4);
+    const int kc = (lane & 15) ^ (row & 15);
+    srcA[j] = (const unsigned char*)((const bf16_t*)a.A + (int64_t)min(m0 + row, M - 1) * K +
+                                     (int64_t)kt0 * 128) + kc * 16;
+  }
+#pragma unroll
+  for (int j = 0; j < G::WLOADS; ++j) {
+    const int row = (wave * G::WLOADS + j) * 16 + (lane >> 2);
+    const int kc = (lane & 3) ^ ((row >> 1) & 3);
+    srcW[j] = Wq + (int64_t)(n0 + row) * (K / 2) + (int64_t)kt0 * 64 + kc * 16;
+  }
+  // stage kt goes to ring slot kt % NS. Past the last stage the DMA re-loads that
+  // stage's data into the slot just freed (no later step reads it): every step
+  // then issues the same loads, so every wait below has one constant depth.
+  // scale source: group (kt0 + kd), columns n0 .. n0+63 (lane % 8 picks a 16-byte piece)
+  const unsigned char* srcS = (const unsigned char*)(Sc + (size_t)kt0 * a.N + n0) + (lane & 7) * 16;
+  auto issue = [&](int kt) {
+    unsigned char* st = smem + (kt % NS) * G::STAGE;
+    const int kd = kt < nk ? kt : nk - 1;
+#pragma unroll
+    for (int j = 0; j < G::ALOADS; ++j)
+      __builtin_amdgcn_global_load_lds(
+          (const void*)(srcA[j] + (size_t)kd * 256),
+          (__attribute__((address_space(3))) void*)(st + (wave * G::ALOADS + j) * 1024), 16, 0,
+          0);
+#pragma unroll
+    for (int j = 0; j < G::WLOADS; ++j)
+      __builtin_amdgcn_global_load_lds(
+          (const void*)(srcW[j] + (size_t)kd * 64),
+          (__attribute__((address_space(3))) void*)(st + G::ASTAGE + (wave * G::WLOADS + j) * 1024),
+          16, 0, 0);
+    if (wave == 0)
+      __builtin_amdgcn_global_load_lds(
+          (const void*)(srcS + (size_t)kd * a.N * 2),
+          (__attribute__((address_space(3))) void*)(st + G::ASTAGE + G::WSTAGE), 16, 0, 0);
+  };
+
+  f32x4_t acc[MT][NT];
+#pragma unroll
+  for (int i = 0; i < MT; ++i)
+#pragma unroll
+    for (int j = 0; j < NT; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  if (nk <= 0) {
+    gemm_epilogue<EPI, MT, NT, G::WM, G::WN>(a, acc, m0, n0, z, wm, wn, lane);
+    return;
+  }
+#pragma unroll
+  for (int s0 = 0; s0 < NS - 1; ++s0) issue(s0);
+  for (int kt = 0; kt < nk; ++kt) {
+    // stage kt landed: at most NS-2 younger stages in flight (wavefront 0, which also
+    // loads the scales, waits for a little more than it must)
+    wait_vmcnt_steps<LOADS>(NS - 2);
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    // this step's group scales for the lane's output columns (from the stage)
+    const unsigned char* st = smem + (kt % NS) * G::STAGE;
+    float sc[NT];
+#pragma unroll
+    for (int ni = 0; ni < NT; ++ni)
+      sc[ni] = __half2float(
+          *(const __half*)(st + G::ASTAGE + G::WSTAGE + (wn * G::WN + ni * 16 + (lane & 15)) * 2));
+    issue(kt + NS - 1);
+    // widen the stage's W codes to bf16 (one 16-byte chunk = 32 codes per thread per pass)
+    for (int c = tid; c < BN * 4; c += 256) {
+      const int r = c >> 2, kc = c & 3;
+      const u32x4_t w = *(const u32x4_t*)(st + G::ASTAGE + r * 64 + ((kc ^ ((r >> 1) & 3)) << 4));
+      u32x4_t o[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int q0 = (int)(w[i] << (28 - 8 * j)) >> 28;
+          const int q1 = (int)(w[i] << (24 - 8 * j)) >> 28;
+          o[i][j] = (__float_as_uint((float)q0) >> 16) | (__float_as_uint((float)q1) & 0xffff0000u);
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) *(u32x4_t*)(wb + r * G::WBP + kc * 32 + 8 * i) = o[i];
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    f32x4_t tmp[MT][NT];
+#pragma unroll
+    for (int i = 0; i < MT; ++i)
+#pragma unroll
+      for (int j = 0; j < NT; ++j) tmp[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const int kc = ks * 4 + (lane >> 4);
+      bf16x8_t bf[NT];
+#pragma unroll
+      for (int ni = 0; ni < NT; ++ni)
+        bf[ni] = *(const bf16x8_t*)(wb + (wn * G::WN + ni * 16 + (lane & 15)) * G::WBP + kc * 8);
+#pragma unroll
+      for (int mi = 0; mi < MT; ++mi) {
+        const int r = wm * G::WM + mi * 16 + (lane & 15);
+        const bf16x8_t af = *(const bf16x8_t*)(st + r * 256 + ((kc ^ (r & 15)) << 4));
+#pragma unroll
+        for (int ni = 0; ni < NT; ++ni)
+          tmp[mi][ni] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bf[ni], tmp[mi][ni], 0, 0, 0);
+      }
+    }
+#pragma unroll
+    for (int mi = 0; mi < MT; ++mi)
+#pragma unroll
+      for (int ni = 0; ni < NT; ++ni) acc[mi][ni] += sc[ni] * tmp[mi][ni];
+  }
+  gemm_epilogue<EPI, MT, NT, G::WM, G::WN>(a, acc, m0, n0, z, wm, wn, lane);
+}
+
+template <int EPI>
+static void gemm_w4_go(const GemmArgs& a, int splits, int ksteps, hipStream_t s) {
+  constexpr int BM = 64, BN = 64, NS = 3;
+  const int tiles_m = (a.M + BM - 1) / BM;
+  const int tiles = tiles_m * (a.N / BN);
+  const int per_xcd = (tiles + kXcds - 1) / kXcds;
+  launch_k(gemm_w4_kernel<EPI, BM, BN, NS>, dim3(kXcds * per_xcd * splits), dim3(256), 0, s, a,
+           tiles_m, tiles, ksteps);
+}
+
 // q/k/v split-K reduction: sums the partials of each RoPE pair (split order) and
 // applies the same epilogue as the unsplit kernel (rotation, query buffer, paged
 // K/V). One workgroup per row.
@@ -349,6 +532,35 @@ static void gemm_bf16_go(const GemmArgs& a, int splits, int ksteps, hipStream_t 
            s, a, tiles_m, tiles, ksteps);
 }
 
+// INT4 projections: 64 x 64 tiles over 128-wide groups; residual projections split
+// the groups when fewer than about 384 workgroups would run (at least 4 groups per
+// split) and reduce like the 16-bit path
+static hipError_t gemm_w4(const GemmArgs& a, hipStream_t s) {
+  if (a.K % 128 != 0 || a.N % 64 != 0) return hipErrorInvalidValue;
+  const int ngk = a.K / 128;
+  if (a.epi == EPI_SWIGLU) {
+    gemm_w4_go<EPI_SWIGLU>(a, 1, ngk, s);
+    return hipGetLastError();
+  }
+  if (a.epi == EPI_QKV) {
+    gemm_w4_go<EPI_QKV>(a, 1, ngk, s);
+    return hipGetLastError();
+  }
+  if (a.epi != EPI_RESID) return hipErrorInvalidValue;
+  if (a.ws == nullptr || (size_t)a.M * a.N > a.ws_elems) return hipErrorInvalidValue;
+  if (a.N % 8 != 0 || a.N / 8 > 256 * kResidMaxChunks) return hipErrorInvalidValue;
+  const int tiles = ((a.M + 63) / 64) * (a.N / 64);
+  int splits = std::max(1, std::min(8, (384 + tiles - 1) / tiles));
+  while (splits > 1 && ngk / splits < 4) --splits;
+  while (splits > 1 && (size_t)splits * a.M * a.N > a.ws_elems) --splits;
+  const int ksteps = (ngk + splits - 1) / splits;
+  splits = (ngk + ksteps - 1) / ksteps;
+  gemm_w4_go<EPI_PARTIAL>(a, splits, ksteps, s);
+  launch_k(resid_norm_kernel, dim3(a.M), dim3(256), 0, s, (const float*)a.ws, splits, a.M, a.N,
+           (float*)a.C, (bf16_t*)a.norm_out, a.norm_g, a.eps);
+  return hipGetLastError();
+}
+
 // Shapes, measured at the 256-row chunks of the Qwen2.5-1.5B shape: the wide gated
 // projection takes 128 x 128 tiles with 32-deep K steps in a 4-stage ring (one
 // weight read per two 128-row tiles, sharing an XCD's L2); every other
@@ -358,6 +570,7 @@ static void gemm_bf16_go(const GemmArgs& a, int splits, int ksteps, hipStream_t 
 // residual add (+ next RMSNorm), or RoPE + K/V write for q/k/v.
 static hipError_t gemm_bf16(const GemmArgs& a, hipStream_t s) {
   if (a.K % 64 != 0 || a.N % 64 != 0 || a.M < 1) return hipErrorInvalidValue;
+  if (a.wf == WF_INT4) return gemm_w4(a, s);
   if (a.epi == EPI_SWIGLU) {
     if (a.M > 64 && a.N % 128 == 0)
       gemm_bf16_go<EPI_SWIGLU, 128, 128, 32, 4>(a, 1, a.K / 32, s);

@@ -2,6 +2,8 @@
 // RMSNorm and fused epilogues (RoPE + paged KV write, residual add, SwiGLU,
 // output head with argmax). HBM-bound: every weight byte is read once with
 // 16-byte loads, many independent loads in flight per lane.
+#include <hip/hip_fp16.h>
+
 #include "common.hpp"
 #include "epilogue.hpp"
 #include "kernels.hpp"
@@ -197,6 +199,189 @@ static hipError_t gemv_launch(const GemvArgs& a, hipStream_t s, int* grid_out) {
   return gemv_launch_rw<T, EPI, 2>(a, s, grid_out);
 }
 
+// ---------------------------------------------------------------------------
+// INT4 group-128 weights: a 16-byte chunk holds the 32 codes of K positions
+// 32c .. 32c+31 (even k in the low nibble), inside group c / 4 whose fp16 scale
+// (scales stored [K/128][N]) multiplies the chunk's partial sum in fp32.
+// Same row groups, grid and epilogues as the 16-bit kernel; the input row is
+// always kept in fp32 in LDS.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float dot32_w4(const u32x4_t& w, const float* x) {
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int q = (int)(w[i] << (28 - 4 * j)) >> 28;  // sign-extended nibble j
+      s += (float)q * x[8 * i + j];
+    }
+  }
+  return s;
+}
+
+template <int EPI, int RW>
+__global__ __launch_bounds__(kGemvThreads) void gemv_w4_kernel(GemvArgs a, int ngroups) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char gsmem[];
+  f32x4_t* xs4 = (f32x4_t*)gsmem;
+  __shared__ float ssq[kGemvWaves];
+  __shared__ unsigned long long wbest[kGemvWaves];
+  constexpr int UNR = RW >= 8 ? 1 : (RW >= 4 ? 2 : 4);  // 8 chunk loads (256 codes) in flight
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int K = a.K;
+  const int nch = K / 32;
+
+  // input row -> LDS in fp32 (the normalised residual, or the bf16 activations widened)
+  if constexpr (EPI != EPI_RESID) {
+    const f32x4_t* xf4 = (const f32x4_t*)a.x;
+    float ss = 0.f;
+    for (int i = tid; i < K / 4; i += kGemvThreads) {
+      const f32x4_t v = xf4[i];
+      xs4[i] = v;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) ss += v[e] * v[e];
+    }
+    if (a.norm_g) {
+      ss = wave_sum(ss);
+      if (lane == 0) ssq[wave] = ss;
+      __syncthreads();
+      float tot = 0.f;
+#pragma unroll
+      for (int w = 0; w < kGemvWaves; ++w) tot += ssq[w];
+      const float rn = rsqrtf(tot / (float)K + a.eps);
+      const f32x4_t* g4 = (const f32x4_t*)a.norm_g;
+      for (int i = tid; i < K / 4; i += kGemvThreads) xs4[i] = xs4[i] * rn * g4[i];  // own elements
+    }
+  } else {
+    const bf16_t* x = (const bf16_t*)a.x;
+    for (int c = tid; c < K / 8; c += kGemvThreads) {
+      float f[8];
+      unpack8(*(const u32x4_t*)(x + (size_t)c * 8), f);
+      xs4[2 * c] = f32x4_t{f[0], f[1], f[2], f[3]};
+      xs4[2 * c + 1] = f32x4_t{f[4], f[5], f[6], f[7]};
+    }
+  }
+  __syncthreads();
+
+  const uint8_t* W = (const uint8_t*)a.W;
+  const __half* Sc = (const __half*)(W + (size_t)a.N * K / 2);
+  unsigned long long best = 0ull;
+  for (int g = blockIdx.x * kGemvWaves + wave; g < ngroups; g += gridDim.x * kGemvWaves) {
+    int64_t prow[RW];
+#pragma unroll
+    for (int r = 0; r < RW; ++r) {  // rows past N (a partial last group) re-read row N-1
+      const int64_t row = gemv_row<EPI, RW>(g, r);
+      prow[r] = row < a.N ? row : (int64_t)a.N - 1;
+    }
+    float acc[RW];
+#pragma unroll
+    for (int r = 0; r < RW; ++r) acc[r] = 0.f;
+    for (int c0 = lane; c0 < nch; c0 += 64 * UNR) {
+      u32x4_t w[UNR][RW];
+      float sc[UNR][RW];
+#pragma unroll
+      for (int u = 0; u < UNR; ++u) {
+        const int c = c0 + 64 * u;
+#pragma unroll
+        for (int r = 0; r < RW; ++r) {
+          w[u][r] = c < nch ? *(const u32x4_t*)(W + prow[r] * (K / 2) + (size_t)c * 16)
+                            : u32x4_t{0, 0, 0, 0};
+          sc[u][r] = c < nch ? __half2float(Sc[(size_t)(c / 4) * a.N + prow[r]]) : 0.f;
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < UNR; ++u) {
+        const int c = c0 + 64 * u;
+        float xv[32];
+        const f32x4_t* xp = xs4 + (size_t)c * 8;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const f32x4_t q = c < nch ? xp[i] : f32x4_t{0.f, 0.f, 0.f, 0.f};
+          xv[4 * i] = q[0];
+          xv[4 * i + 1] = q[1];
+          xv[4 * i + 2] = q[2];
+          xv[4 * i + 3] = q[3];
+        }
+#pragma unroll
+        for (int r = 0; r < RW; ++r) acc[r] += sc[u][r] * dot32_w4(w[u][r], xv);
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < RW; ++r) acc[r] = wave_sum(acc[r]);
+
+    if constexpr (EPI == EPI_QKV) {
+#pragma unroll
+      for (int p = 0; p < RW / 2; ++p)
+        if (lane == p) epi_qkv_pair<bf16_t>(a.ctx, 0, (int)gemv_row<EPI, RW>(g, 2 * p), acc[2 * p],
+                                            acc[2 * p + 1]);
+    } else if constexpr (EPI == EPI_RESID) {
+#pragma unroll
+      for (int r = 0; r < RW; ++r) {
+        const int64_t row = gemv_row<EPI, RW>(g, r);
+        if (lane == r && row < a.N) ((float*)a.out)[row] += acc[r];
+      }
+    } else if constexpr (EPI == EPI_SWIGLU) {
+#pragma unroll
+      for (int i = 0; i < RW / 2; ++i)
+        if (lane == i)
+          St<bf16_t>::st((bf16_t*)a.out, g * (RW / 2) + i, silu(acc[i]) * acc[RW / 2 + i]);
+    } else if constexpr (EPI == EPI_HEAD) {
+#pragma unroll
+      for (int r = 0; r < RW; ++r) {
+        const int64_t row = gemv_row<EPI, RW>(g, r);
+        if (row < a.N) {
+          if (lane == r) ((float*)a.out)[row] = acc[r];
+          const unsigned long long k = argmax_key(acc[r], (uint32_t)row);
+          best = k > best ? k : best;
+        }
+      }
+    }
+  }
+  if constexpr (EPI == EPI_HEAD) {
+    if (lane == 0) wbest[wave] = best;
+    __syncthreads();
+    if (tid == 0) {
+      unsigned long long b = wbest[0];
+#pragma unroll
+      for (int w = 1; w < kGemvWaves; ++w) b = wbest[w] > b ? wbest[w] : b;
+      a.argmax_part[blockIdx.x] = b;
+    }
+  }
+}
+
+template <int EPI, int RW>
+static hipError_t gemv_w4_launch_rw(const GemvArgs& a, hipStream_t s, int* grid_out) {
+  const int ngroups = (EPI == EPI_SWIGLU) ? a.N / RW : (a.N + RW - 1) / RW;
+  int grid = (ngroups + kGemvWaves - 1) / kGemvWaves;
+  grid = grid < kGemvMaxGrid ? grid : kGemvMaxGrid;
+  if (grid_out) *grid_out = grid;
+  launch_k(gemv_w4_kernel<EPI, RW>, dim3(grid), dim3(kGemvThreads), (uint32_t)(a.K * 4), s, a,
+           ngroups);
+  return hipGetLastError();
+}
+
+template <int EPI>
+static hipError_t gemv_w4_launch(const GemvArgs& a, hipStream_t s, int* grid_out) {
+  if (a.K % 128 != 0 || a.K > 16384) return hipErrorInvalidValue;
+  if constexpr (EPI == EPI_QKV) {
+    if (a.N % 8) return hipErrorInvalidValue;
+  } else if constexpr (EPI == EPI_SWIGLU) {
+    if (a.N % 32) return hipErrorInvalidValue;
+  }
+  if (a.N / 8 >= 2048) return gemv_w4_launch_rw<EPI, 8>(a, s, grid_out);
+  if (a.N / 4 >= 1024) return gemv_w4_launch_rw<EPI, 4>(a, s, grid_out);
+  return gemv_w4_launch_rw<EPI, 2>(a, s, grid_out);
+}
+
+static hipError_t gemv_w4_dispatch(const GemvArgs& a, hipStream_t s, int* grid_out) {
+  switch (a.epi) {
+    case EPI_QKV: return gemv_w4_launch<EPI_QKV>(a, s, grid_out);
+    case EPI_RESID: return gemv_w4_launch<EPI_RESID>(a, s, grid_out);
+    case EPI_SWIGLU: return gemv_w4_launch<EPI_SWIGLU>(a, s, grid_out);
+    case EPI_HEAD: return gemv_w4_launch<EPI_HEAD>(a, s, grid_out);
+    default: return hipErrorInvalidValue;
+  }
+}
+
 template <typename T>
 static hipError_t gemv_dispatch(const GemvArgs& a, hipStream_t s, int* grid_out) {
   switch (a.epi) {
@@ -209,6 +394,7 @@ static hipError_t gemv_dispatch(const GemvArgs& a, hipStream_t s, int* grid_out)
 }
 
 hipError_t launch_gemv(const GemvArgs& a, int dt, hipStream_t s, int* grid_out) {
+  if (a.wf == WF_INT4) return dt == DT_BF16 ? gemv_w4_dispatch(a, s, grid_out) : hipErrorInvalidValue;
   // the input row lives in LDS: fp32 (residual inputs) or 16-bit, at most 64 KiB
   if (a.K % 8 != 0 || a.K > (a.epi == EPI_RESID ? 32768 : 16384)) return hipErrorInvalidValue;
   return dt == DT_F32 ? gemv_dispatch<float>(a, s, grid_out)

@@ -71,9 +71,12 @@ struct FwdCtx {
 enum Epi { EPI_STORE = 0, EPI_RESID = 1, EPI_QKV = 2, EPI_SWIGLU = 3, EPI_HEAD = 4,
            EPI_PARTIAL = 5 };
 
+enum WeightFmt { WF_ACT = 0, WF_INT4 = 1 };  // weights in the activation type / INT4 g128
+
 struct GemmArgs {
   const void* A = nullptr;  // [M][K] activations
-  const void* W = nullptr;  // [N][K] weights (physical layout)
+  const void* W = nullptr;  // [N][K] weights (physical layout); INT4: codes then scales
+  int wf = WF_ACT;
   int M = 0, N = 0, K = 0;
   int epi = EPI_STORE;
   void* C = nullptr;        // STORE [M][N]; RESID fp32 x [M][N] (+=); SWIGLU [M][N/2]
@@ -93,7 +96,8 @@ struct GemvArgs {
                                 // else activations in the weight type
   const float* norm_g = nullptr;  // non-null: RMSNorm the input first
   float eps = 0.f;
-  const void* W = nullptr;      // [N][K]
+  const void* W = nullptr;      // [N][K]; INT4: packed codes [N][K/2] then scales [K/128][N]
+  int wf = WF_ACT;
   int N = 0, K = 0;
   int epi = EPI_STORE;
   void* out = nullptr;          // RESID fp32 x[N] (+=); SWIGLU act[N/2]; HEAD logits fp32[N]
@@ -125,6 +129,13 @@ struct AttnArgs {
 hipError_t launch_init_weight(void* out, int dt, int layout, int64_t rows, int64_t cols,
                               uint64_t seed, uint64_t sa, uint64_t sb, uint64_t sc, int hq,
                               int hkv, int d, double stdv, hipStream_t s);
+// INT4 group-128 tensors: packed codes [rows][cols/2] then fp16 scales [cols/128][rows]
+hipError_t launch_init_weight_w4(void* out, int layout, int64_t rows, int64_t cols, uint64_t seed,
+                                 uint64_t sa, uint64_t sb, uint64_t sc, int hq, int hkv, int d,
+                                 double stdv, hipStream_t s);
+hipError_t launch_weight_logical_w4(const void* phys, float* out, int layout, int which,
+                                    int64_t rows, int64_t cols, int64_t prows, int hq, int hkv,
+                                    int d, hipStream_t s);
 hipError_t launch_weight_logical(const void* phys, void* out, int dt, int layout, int which,
                                  int64_t rows, int64_t cols, int hq, int hkv, int d,
                                  hipStream_t s);

@@ -1,8 +1,17 @@
 // Weight generation, embedding gather, RMSNorm, raw KV scatter / gather.
+#include <hip/hip_fp16.h>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
 namespace vla {
+
+static int grid_for(int64_t n, int block) {
+  int64_t g = (n + block - 1) / block;
+  if (g > 65536) g = 65536;
+  if (g < 1) g = 1;
+  return (int)g;
+}
 
 // ---------------------------------------------------------------------------
 // Seeded generator ("Can an LLM Forget the Right Things?", section 6: weights
@@ -73,6 +82,60 @@ __global__ void init_weight_kernel(T* out, int layout, int64_t rows, int64_t col
   }
 }
 
+// Group-128 INT4 weights ("Rebuilding Kshipra Around Memory", section 2: 4-bit
+// codes in groups of 128 along a row, two per byte, one fp16 scale per group,
+// and the same fp16 scale used to encode and to decode so |w - q s| <= s / 2).
+// One thread per (physical row, group): the 128 master values are drawn like
+// the other weights and rounded to fp32; s = fp16(max|w| / 7) with the division
+// in fp32; q = clamp(round-half-even(w / s), -8, 7) with the division in fp32 by
+// s widened to fp32 (q = 0 when s = 0); even k in the low nibble.
+// Storage of an N x K tensor: packed bytes [N][K/2], then scales [K/128][N]
+// (group-major: the scales of one group for consecutive rows are contiguous).
+__global__ void init_weight_w4_kernel(uint8_t* out, int layout, int64_t rows, int64_t cols,
+                                      uint64_t seed, uint64_t sa, uint64_t sb, uint64_t sc,
+                                      int hq, int hkv, int d, double stdv) {
+  const uint64_t keys[3] = {sm64(seed ^ sm64(sa)), sm64(seed ^ sm64(sb)), sm64(seed ^ sm64(sc))};
+  const int64_t groups = cols / 128;
+  const int64_t total = rows * groups;
+  __half* scales = (__half*)(out + rows * cols / 2);
+  for (int64_t p = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; p < total;
+       p += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t r = p / groups, g = p % groups;
+    int which;
+    int64_t lr;
+    phys_to_logical(layout, r, hq, hkv, d, &which, &lr);
+    // pass 1: the group's max |w|; pass 2: regenerate and encode (no 128-value array)
+    const uint64_t base = (uint64_t)(lr * cols + g * 128);
+    float amax = 0.f;
+    for (int k = 0; k < 128; ++k)
+      amax = fmaxf(amax, fabsf((float)(stdv * normal_at(keys[which], base + k))));
+    const __half s16 = __float2half_rn(__fdiv_rn(amax, 7.0f));
+    const float s32 = __half2float(s16);
+    scales[g * rows + r] = s16;
+    uint8_t* o = out + r * (cols / 2) + g * 64;
+    for (int k = 0; k < 128; k += 2) {
+      int q[2] = {0, 0};
+      if (s32 != 0.f) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const float w = (float)(stdv * normal_at(keys[which], base + k + h));
+          q[h] = (int)fminf(fmaxf(rintf(__fdiv_rn(w, s32)), -8.f), 7.f);
+        }
+      }
+      o[k / 2] = (uint8_t)((q[0] & 0xF) | ((q[1] & 0xF) << 4));
+    }
+  }
+}
+
+hipError_t launch_init_weight_w4(void* out, int layout, int64_t rows, int64_t cols, uint64_t seed,
+                                 uint64_t sa, uint64_t sb, uint64_t sc, int hq, int hkv, int d,
+                                 double stdv, hipStream_t s) {
+  if (cols % 128) return hipErrorInvalidValue;
+  init_weight_w4_kernel<<<grid_for(rows * (cols / 128), 64), 64, 0, s>>>(
+      (uint8_t*)out, layout, rows, cols, seed, sa, sb, sc, hq, hkv, d, stdv);
+  return hipGetLastError();
+}
+
 // logical (out, in) element (lr, c) of sub-tensor `which` -> physical row
 __device__ __forceinline__ int64_t logical_to_phys(int layout, int which, int64_t lr, int hq,
                                                    int hkv, int d) {
@@ -97,11 +160,28 @@ __global__ void weight_logical_kernel(const T* phys, T* out, int layout, int whi
   }
 }
 
-static int grid_for(int64_t n, int block) {
-  int64_t g = (n + block - 1) / block;
-  if (g > 65536) g = 65536;
-  if (g < 1) g = 1;
-  return (int)g;
+
+// INT4 tensor element (lr, c) of sub-tensor `which`, dequantised: q * s (exact in fp32)
+__global__ void weight_logical_w4_kernel(const uint8_t* phys, float* out, int layout, int which,
+                                         int64_t rows, int64_t cols, int64_t prows, int hq,
+                                         int hkv, int d) {
+  const int64_t total = rows * cols;
+  const __half* scales = (const __half*)(phys + prows * cols / 2);
+  for (int64_t p = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; p < total;
+       p += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t lr = p / cols, c = p % cols;
+    const int64_t r = logical_to_phys(layout, which, lr, hq, hkv, d);
+    const uint8_t b = phys[r * (cols / 2) + c / 2];
+    const int q = (int)((int8_t)((c & 1) ? (b & 0xF0) : (uint8_t)(b << 4)) >> 4);
+    out[p] = (float)q * __half2float(scales[(c / 128) * prows + r]);
+  }
+}
+hipError_t launch_weight_logical_w4(const void* phys, float* out, int layout, int which,
+                                    int64_t rows, int64_t cols, int64_t prows, int hq, int hkv,
+                                    int d, hipStream_t s) {
+  weight_logical_w4_kernel<<<grid_for(rows * cols, 256), 256, 0, s>>>(
+      (const uint8_t*)phys, out, layout, which, rows, cols, prows, hq, hkv, d);
+  return hipGetLastError();
 }
 
 hipError_t launch_weight_logical(const void* phys, void* out, int dt, int layout, int which,

@@ -85,6 +85,7 @@ struct vla_model {
   vla_config cfg{};
   int dev = 0;
   int dt = DT_BF16;
+  int wf = WF_ACT;   // projection weights: activation type or INT4 group-128
   size_t esz = 2;
   KvGeom geom{};
 
@@ -326,6 +327,7 @@ void run_layers(vla_model* m, int n, int64_t pos0, int cb0, int cslot0, bool dec
       g.norm_g = m->norm_ones;
       g.eps = c.rms_eps;
       g.W = m->wqkv[l];
+      g.wf = m->wf;
       g.N = nqkv;
       g.K = H;
       g.epi = EPI_QKV;
@@ -335,6 +337,7 @@ void run_layers(vla_model* m, int n, int64_t pos0, int cb0, int cslot0, bool dec
       GemvArgs o;
       o.x = m->ao;
       o.W = m->wo[l];
+      o.wf = m->wf;
       o.N = H;
       o.K = qd;
       o.epi = EPI_RESID;
@@ -345,6 +348,7 @@ void run_layers(vla_model* m, int n, int64_t pos0, int cb0, int cslot0, bool dec
       gu.norm_g = m->norm_ones;
       gu.eps = c.rms_eps;
       gu.W = m->wgu[l];
+      gu.wf = m->wf;
       gu.N = 2 * c.ffn;
       gu.K = H;
       gu.epi = EPI_SWIGLU;
@@ -353,6 +357,7 @@ void run_layers(vla_model* m, int n, int64_t pos0, int cb0, int cslot0, bool dec
       GemvArgs dn;
       dn.x = m->act;
       dn.W = m->wdown[l];
+      dn.wf = m->wf;
       dn.N = H;
       dn.K = c.ffn;
       dn.epi = EPI_RESID;
@@ -369,6 +374,7 @@ void run_layers(vla_model* m, int n, int64_t pos0, int cb0, int cslot0, bool dec
       GemmArgs q;
       q.A = m->u;
       q.W = m->wqkv[l];
+      q.wf = m->wf;
       q.M = n;
       q.N = nqkv;
       q.K = H;
@@ -381,6 +387,7 @@ void run_layers(vla_model* m, int n, int64_t pos0, int cb0, int cslot0, bool dec
       GemmArgs o;
       o.A = m->ao;
       o.W = m->wo[l];
+      o.wf = m->wf;
       o.M = n;
       o.N = H;
       o.K = qd;
@@ -398,6 +405,7 @@ void run_layers(vla_model* m, int n, int64_t pos0, int cb0, int cslot0, bool dec
       GemmArgs gu;
       gu.A = m->u;
       gu.W = m->wgu[l];
+      gu.wf = m->wf;
       gu.M = n;
       gu.N = 2 * c.ffn;
       gu.K = H;
@@ -407,6 +415,7 @@ void run_layers(vla_model* m, int n, int64_t pos0, int cb0, int cslot0, bool dec
       GemmArgs dn;
       dn.A = m->act;
       dn.W = m->wdown[l];
+      dn.wf = m->wf;
       dn.M = n;
       dn.N = H;
       dn.K = c.ffn;
@@ -430,6 +439,7 @@ void run_head(vla_model* m, int row, hipStream_t st) {
   h.norm_g = m->norm_ones;
   h.eps = c.rms_eps;
   h.W = m->head;
+  h.wf = m->wf;
   h.N = c.vocab;
   h.K = c.hidden;
   h.epi = EPI_HEAD;
@@ -499,12 +509,18 @@ void validate_cfg(const vla_config* c) {
   if (c->hidden > 8192) bad("hidden must be <= 8192");
   if (c->block_tokens != 16) bad("block_tokens must be 16");
   if (c->num_blocks < 1 || c->max_frames < 1 || c->max_chunk < 1) bad("budget sizes");
-  if (c->wdtype != c->act_dtype || (c->wdtype != VLA_F32 && c->wdtype != VLA_BF16))
-    bad("wdtype must equal act_dtype, VLA_F32 or VLA_BF16");
+  if (c->act_dtype != VLA_F32 && c->act_dtype != VLA_BF16) bad("act_dtype must be VLA_F32 or VLA_BF16");
+  if (c->wdtype == VLA_INT4_G128) {
+    if (c->act_dtype != VLA_BF16) bad("INT4 weights need bf16 activations");
+    if (c->hidden % 128 || (c->n_heads * c->head_dim) % 128 || c->ffn % 128)
+      bad("INT4 weights: hidden, n_heads*head_dim and ffn must be multiples of 128");
+  } else if (c->wdtype != c->act_dtype) {
+    bad("wdtype must equal act_dtype (VLA_F32 or VLA_BF16) or be VLA_INT4_G128");
+  }
   if (c->ffn_kind != VLA_SWIGLU) bad("ffn_kind");
   if (!(c->rope_theta > 1.0)) bad("rope_theta");
   const int qd = c->n_heads * c->head_dim;
-  if (c->wdtype == VLA_BF16) {
+  if (c->act_dtype == VLA_BF16) {
     if (c->head_dim != 64 && c->head_dim != 128 && c->head_dim != 256)
       bad("bf16 path: head_dim 64, 128 or 256");
     if (qd % 64 || c->ffn % 64) bad("bf16 path: n_heads*head_dim and ffn multiples of 64");
@@ -520,19 +536,24 @@ void init_weights(vla_model* m) {
   const int H = c.hidden, d = c.head_dim, hq = c.n_heads, hkv = c.n_kv_heads;
   const hipStream_t st = nullptr;
   auto sid = [](int layer, int kind) { return (uint64_t)(((layer + 1) << 8) | kind); };
+  // a projection: in the activation type, or INT4 group-128 (codes + scales)
+  auto proj = [&](void* out, int layout, int64_t rows, int64_t cols, uint64_t sa, uint64_t sb,
+                  uint64_t sc) {
+    if (m->wf == WF_INT4)
+      HIPCHK(launch_init_weight_w4(out, layout, rows, cols, c.seed, sa, sb, sc, hq, hkv, d,
+                                   c.init_std, st));
+    else
+      HIPCHK(launch_init_weight(out, m->dt, layout, rows, cols, c.seed, sa, sb, sc, hq, hkv, d,
+                                c.init_std, st));
+  };
   HIPCHK(launch_init_weight(m->embed, m->dt, LAYOUT_PLAIN, c.vocab, H, c.seed, 1, 1, 1, hq, hkv,
                             d, c.init_std, st));
-  HIPCHK(launch_init_weight(m->head, m->dt, LAYOUT_PLAIN, c.vocab, H, c.seed, 2, 2, 2, hq, hkv, d,
-                            c.init_std, st));
+  proj(m->head, LAYOUT_PLAIN, c.vocab, H, 2, 2, 2);
   for (int l = 0; l < c.n_layers; ++l) {
-    HIPCHK(launch_init_weight(m->wqkv[l], m->dt, LAYOUT_QKV, (int64_t)(hq + 2 * hkv) * d, H,
-                              c.seed, sid(l, 1), sid(l, 2), sid(l, 3), hq, hkv, d, c.init_std, st));
-    HIPCHK(launch_init_weight(m->wo[l], m->dt, LAYOUT_PLAIN, H, (int64_t)hq * d, c.seed,
-                              sid(l, 4), sid(l, 4), sid(l, 4), hq, hkv, d, c.init_std, st));
-    HIPCHK(launch_init_weight(m->wgu[l], m->dt, LAYOUT_GATEUP, 2 * (int64_t)c.ffn, H, c.seed,
-                              sid(l, 5), sid(l, 6), sid(l, 6), hq, hkv, d, c.init_std, st));
-    HIPCHK(launch_init_weight(m->wdown[l], m->dt, LAYOUT_PLAIN, H, c.ffn, c.seed, sid(l, 7),
-                              sid(l, 7), sid(l, 7), hq, hkv, d, c.init_std, st));
+    proj(m->wqkv[l], LAYOUT_QKV, (int64_t)(hq + 2 * hkv) * d, H, sid(l, 1), sid(l, 2), sid(l, 3));
+    proj(m->wo[l], LAYOUT_PLAIN, H, (int64_t)hq * d, sid(l, 4), sid(l, 4), sid(l, 4));
+    proj(m->wgu[l], LAYOUT_GATEUP, 2 * (int64_t)c.ffn, H, sid(l, 5), sid(l, 6), sid(l, 6));
+    proj(m->wdown[l], LAYOUT_PLAIN, H, c.ffn, sid(l, 7), sid(l, 7), sid(l, 7));
   }
   HIPCHK(launch_fill_f32(m->norm_ones, 1.0f, H, st));
   std::vector<double> inv(d / 2);
@@ -573,17 +594,22 @@ vla_status vla_model_create(const vla_config* cfg, vla_model** out) {
     HIPCHK(hipGetDevice(&m->dev));
     const vla_config& c = m->cfg;
     m->dt = c.act_dtype == VLA_F32 ? DT_F32 : DT_BF16;
+    m->wf = c.wdtype == VLA_INT4_G128 ? WF_INT4 : WF_ACT;
     m->esz = m->dt == DT_F32 ? 4 : 2;
     m->geom = KvGeom{c.n_layers, c.num_blocks, c.n_kv_heads, c.block_tokens, c.head_dim};
     const size_t H = c.hidden, d = c.head_dim, hq = c.n_heads, hkv = c.n_kv_heads;
     const size_t e = m->esz;
+    // projection bytes: activation type, or INT4 codes (half a byte) + one fp16 per 128
+    auto wbytes = [&](size_t rows, size_t cols) {
+      return m->wf == WF_INT4 ? rows * cols / 2 + rows * (cols / 128) * 2 : rows * cols * e;
+    };
     m->embed = dalloc(m, (size_t)c.vocab * H * e);
-    m->head = dalloc(m, (size_t)c.vocab * H * e);
+    m->head = dalloc(m, wbytes(c.vocab, H));
     for (int l = 0; l < c.n_layers; ++l) {
-      m->wqkv.push_back(dalloc(m, (hq + 2 * hkv) * d * H * e));
-      m->wo.push_back(dalloc(m, H * hq * d * e));
-      m->wgu.push_back(dalloc(m, 2 * (size_t)c.ffn * H * e));
-      m->wdown.push_back(dalloc(m, H * (size_t)c.ffn * e));
+      m->wqkv.push_back(dalloc(m, wbytes((hq + 2 * hkv) * d, H)));
+      m->wo.push_back(dalloc(m, wbytes(H, hq * d)));
+      m->wgu.push_back(dalloc(m, wbytes(2 * (size_t)c.ffn, H)));
+      m->wdown.push_back(dalloc(m, wbytes(H, c.ffn)));
     }
     m->norm_ones = (float*)dalloc(m, H * sizeof(float));
     m->inv_freq = (double*)dalloc(m, d / 2 * sizeof(double));
@@ -951,6 +977,15 @@ vla_status vla_weight_out(vla_model* m, int32_t kind, int32_t layer, void* out, 
       case 7: rows = H; cols = c.ffn; src = m->wdown[layer]; break;
       case 8: rows = c.vocab; src = m->embed; break;
       case 9: rows = c.vocab; src = m->head; break;
+    }
+    if (m->wf == WF_INT4 && kind != 8) {  // INT4 projection: dequantised q * s in fp32
+      if (bytes < rows * cols * 4) raise(VLA_E_INVALID, "output buffer too small");
+      int64_t prows = rows;  // physical rows of the whole tensor
+      if (kind <= 3) prows = qd + 2 * kd;
+      else if (kind == 5 || kind == 6) prows = 2 * (int64_t)c.ffn;
+      HIPCHK(launch_weight_logical_w4(src, (float*)out, layout, which, rows, cols, prows, c.n_heads,
+                                      c.n_kv_heads, (int)d, st));
+      return;
     }
     if (bytes < rows * cols * (int64_t)m->esz) raise(VLA_E_INVALID, "output buffer too small");
     HIPCHK(launch_weight_logical(src, out, m->dt, layout, which, rows, cols, c.n_heads,

@@ -286,6 +286,12 @@ PRESETS = {
                                  head_dim=128, ffn=8960, vocab=151936, rope_theta=1e6,
                                  wdtype=VLA_BF16, num_blocks=512, max_frames=128, max_chunk=64,
                                  seed=1237),
+    # Llama-3-8B-shaped decoder, INT4 group-128 weights, bf16 activations: a 120,000-token
+    # cached prefix (raw frames of up to 512 tokens), a 512-token chunk, 32 decodes
+    "c5_llama3_8b_int4": dict(n_layers=32, hidden=4096, n_heads=32, n_kv_heads=8, head_dim=128,
+                              ffn=14336, vocab=128256, rope_theta=5e5, wdtype=VLA_INT4_G128,
+                              act_dtype=VLA_BF16, num_blocks=7534, max_frames=256,
+                              max_chunk=512, seed=1239),
 }
 
 
@@ -301,7 +307,7 @@ def make_config(**kw) -> vla_config:
     c.rms_eps = kw.get("rms_eps", 1e-6)
     c.rope_theta = kw.get("rope_theta", 1e4)
     c.wdtype = kw.get("wdtype", VLA_BF16)
-    c.act_dtype = kw.get("act_dtype", c.wdtype)
+    c.act_dtype = kw.get("act_dtype", VLA_BF16 if c.wdtype == VLA_INT4_G128 else c.wdtype)
     c.ffn_kind = VLA_SWIGLU
     c.block_tokens = kw.get("block_tokens", 16)
     c.num_blocks = kw["num_blocks"]

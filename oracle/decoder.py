@@ -90,7 +90,7 @@ C2 = Config("c2_qwen1p5b_bf16", 28, 1536, 12, 2, 128, 8960, 151936, rope_theta=1
             wdtype="bf16", act="bf16", num_blocks=96, max_frames=16, seed=1236)
 C3 = C2.with_(name="c3_semantic_eviction", num_blocks=512, max_frames=128, seed=1237)
 C5 = Config("c5_llama3_8b_int4", 32, 4096, 32, 8, 128, 14336, 128256, rope_theta=5e5,
-            wdtype="int4", act="bf16", num_blocks=7534, max_frames=8, seed=1239)
+            wdtype="int4", act="bf16", num_blocks=7534, max_frames=256, seed=1239)
 CONFIGS = {c.name: c for c in (C1, C2, C3, C5)}
 
 

@@ -29,8 +29,9 @@ def quantize_g128(w: np.ndarray):
     s16 = (amax / np.float32(7.0)).astype(np.float16)
     s32 = s16.astype(np.float32)[..., None]
     safe = np.where(s32 == 0, np.float32(1.0), s32)
-    q = np.clip(np.rint(g / safe), -8, 7)
-    q = np.where(s32 == 0, 0.0, q).astype(np.int8)
+    # fp32 throughout (integer values: the clamp and the zero case are exact)
+    q = np.clip(np.rint(g / safe), np.float32(-8.0), np.float32(7.0))
+    q = np.where(s32 == 0, np.float32(0.0), q).astype(np.int8)
     w_hat = (q.astype(np.float32) * s32).reshape(n, k)
     qn = (q.reshape(n, k).astype(np.int16) & 0xF).astype(np.uint8)
     packed = (qn[:, 0::2] | (qn[:, 1::2] << 4)).astype(np.uint8)

@@ -69,9 +69,10 @@ def check_argmax(gpu_tok: int, ref_logits: np.ndarray, kind: str, what: str = ""
 
 
 def oracle_config(preset: dict, name="custom", init_std=0.02) -> D.Config:
-    wd = {vla.VLA_F32: "f32", vla.VLA_BF16: "bf16"}[preset["wdtype"]]
+    wd = {vla.VLA_F32: "f32", vla.VLA_BF16: "bf16", vla.VLA_INT4_G128: "int4"}[preset["wdtype"]]
+    act = "bf16" if wd == "int4" else wd
     return D.Config(name, preset["n_layers"], preset["hidden"], preset["n_heads"],
                     preset["n_kv_heads"], preset["head_dim"], preset["ffn"], preset["vocab"],
                     rms_eps=preset.get("rms_eps", 1e-6), rope_theta=preset["rope_theta"],
-                    wdtype=wd, act=wd, num_blocks=preset["num_blocks"],
+                    wdtype=wd, act=act, num_blocks=preset["num_blocks"],
                     max_frames=preset["max_frames"], seed=preset["seed"], init_std=init_std)

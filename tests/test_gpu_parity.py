@@ -22,14 +22,21 @@ TINY_BF16 = dict(n_layers=2, hidden=256, n_heads=6, n_kv_heads=2, head_dim=128, 
                  max_chunk=160, seed=99)
 
 
+# INT4 group-128 projections with bf16 activations (every K a multiple of 128)
+TINY_INT4 = dict(TINY_BF16, n_heads=4, wdtype=vla.VLA_INT4_G128, seed=98)
+
+
 def _model(p, init_std=0.02):
     return vla.Model(vla.make_config(**p, init_std=init_std))
 
 
 # ---------------------------------------------------------------------------
-@pytest.mark.parametrize("which", ["c1", "tiny_bf16"])
+@pytest.mark.parametrize("which", ["c1", "tiny_bf16", "tiny_int4"])
 def test_device_weights_equal_oracle_weights(which):
-    p = vla.PRESETS["c1_tiny_f32"] if which == "c1" else TINY_BF16
+    """Device-generated weights equal the oracle's bit for bit; INT4 projections are
+    compared dequantised (q * s is exact in fp32, so equal values mean equal codes
+    and equal fp16 scales wherever a group is not all zero)."""
+    p = {"c1": vla.PRESETS["c1_tiny_f32"], "tiny_bf16": TINY_BF16, "tiny_int4": TINY_INT4}[which]
     ocfg = oracle_config(p)
     w = D.Weights(ocfg, cache_f64=False)
     m = _model(p)
@@ -38,7 +45,8 @@ def test_device_weights_equal_oracle_weights(which):
     for kind, name in kinds.items():
         for layer in ([0, p["n_layers"] - 1] if kind <= 7 else [-1]):
             ref = w.f32(name, layer)
-            dt = torch.float32 if which == "c1" else torch.bfloat16
+            dt = torch.float32 if which == "c1" or (which == "tiny_int4" and kind != 8) \
+                else torch.bfloat16
             out = torch.empty(ref.shape, dtype=dt, device="cuda")
             m.weight_out(kind, max(layer, 0), out, out.numel() * out.element_size())
             got = out.float().cpu().numpy()
