@@ -15,11 +15,14 @@ Printed: one JSON line. ``value`` is the prefill throughput in tokens/s
 the wall time of a whole frame step. ``phases`` holds the decode-step latency,
 the frame-step time, the eviction leg (semantic eviction workload: 128 cached
 frames of 64 tokens, 32 score-and-evict cycles each followed by a 64-token
-prefill) and roofline fractions. ``roofline`` covers the dominant kernel (the
-decode gate/up projection); ``cpu_baseline`` times the CPU oracle on a bounded
-sample of the same prefill.
+prefill), the long-context leg (Llama-3-8B-shaped decoder with INT4 group-128
+weights: a 120,000-token cached prefix, a 512-token chunk, 32 decodes) and
+roofline fractions. ``roofline`` covers the dominant kernel of the frame step
+(the decode gate/up projection); ``cpu_baseline`` times the CPU oracle on a
+bounded sample of the same prefill.
 
 Usage: python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
+                       [--no-eviction] [--no-longctx]
 """
 from __future__ import annotations
 
@@ -173,6 +176,7 @@ def gpu_leg(args):
     torch.cuda.synchronize()
 
     ev_leg = eviction_leg(args) if not args.no_eviction else None
+    lc_leg = longctx_leg(args) if not args.no_longctx else None
 
     fl = prefill_flops()
     dbytes = decode_bytes(CONTEXT + CHUNK + DECODES // 2)
@@ -231,6 +235,8 @@ def gpu_leg(args):
     }
     if ev_leg:
         res["phases"].update(ev_leg)
+    if lc_leg:
+        res["phases"].update(lc_leg)
     return res
 
 
@@ -297,6 +303,119 @@ def eviction_leg(args):
 
 
 # ---------------------------------------------------------------------------
+# Llama-3-8B-shaped long-context workload: INT4 group-128 weights, bf16 activations
+C5_L, C5_H, C5_HQ, C5_HKV, C5_D, C5_F, C5_V = 32, 4096, 32, 8, 128, 14336, 128256
+C5_PREFIX, C5_CHUNK, C5_DECODES, C5_FRAME = 120000, 512, 32, 512
+
+
+def c5_layer_params():
+    return (C5_HQ + 2 * C5_HKV) * C5_D * C5_H + C5_H * C5_HQ * C5_D + 3 * C5_F * C5_H
+
+
+def c5_prefill_flops():
+    lin = 2 * C5_CHUNK * c5_layer_params() * C5_L + 2 * C5_V * C5_H
+    keys = C5_CHUNK * C5_PREFIX + C5_CHUNK * (C5_CHUNK + 1) // 2
+    return lin, C5_L * C5_HQ * 2 * 2 * C5_D * keys
+
+
+def c5_kv_bytes_per_token():
+    return C5_L * 2 * C5_HKV * C5_D * 2
+
+
+def c5_decode_bytes(ctx_tokens):
+    int4 = lambda n: n // 2 + n // 128 * 2      # codes + one fp16 scale per 128
+    w = int4(c5_layer_params()) * C5_L + int4(C5_V * C5_H) + C5_H * 2
+    return w + c5_kv_bytes_per_token() * ctx_tokens
+
+
+def longctx_leg(args):
+    """120,000-token cached prefix (raw bf16 K/V ~ N(0,1) per layer, appended as frames of
+    512 tokens), a 512-token chunk of uniform ids, then 32 greedy decodes."""
+    import torch
+
+    import kv_cached_gqa_decoder_amd as vla
+    import synth
+
+    stream = torch.cuda.current_stream()
+    sh = stream.cuda_stream
+    p = vla.PRESETS["c5_llama3_8b_int4"]
+    log("[bench] long-context leg: creating the Llama-3-8B-shaped INT4 model")
+    m = vla.Model(vla.make_config(**p))
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(p["seed"])
+    done, fid = 0, -1
+    while done < C5_PREFIX:
+        n = min(C5_FRAME, C5_PREFIX - done)
+        shape = (C5_L, n, C5_HKV, C5_D)
+        k = torch.randn(shape, generator=gen, device="cuda").to(torch.bfloat16)
+        v = torch.randn(shape, generator=gen, device="cuda").to(torch.bfloat16)
+        fid = m.kv_append_raw(k, v, n, stream=sh)
+        done += n
+    del k, v
+    ids = synth.token_ids(p["seed"], 0, C5_CHUNK, C5_V)
+    torch.cuda.synchronize()
+    log(f"[bench] long-context leg: {done}-token prefix resident in {fid + 1} frames")
+
+    def run(ev=None):
+        m.kv_rollback(fid)
+        if ev:
+            ev[0].record(stream)
+        m.prefill_chunk(tokens=ids, stream=sh)
+        if ev:
+            ev[1].record(stream)
+        tok = m.decode_step(1, stream=sh)
+        for _ in range(C5_DECODES - 1):
+            tok = m.decode_step(tok, stream=sh)
+        if ev:
+            ev[2].record(stream)
+
+    run()
+    torch.cuda.synchronize()
+    reps = max(2, min(args.steps, 4))
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(reps)]
+    for i in range(reps):
+        run(evs[i])
+    torch.cuda.synchronize()
+    pre_ms = statistics.median(e[0].elapsed_time(e[1]) for e in evs)
+    dec_ms = statistics.median(e[1].elapsed_time(e[2]) / C5_DECODES for e in evs)
+    # kernel time of the attention alone (split pass + merge), prefill then decode
+    m.kv_rollback(fid)
+    m.profile_enable("attn_prefill")
+    m.prefill_chunk(tokens=ids, stream=sh)
+    ap_ms, ap_n = m.profile_read()
+    m.profile_enable("attn_decode")
+    tok = m.decode_step(1, stream=sh)
+    for _ in range(C5_DECODES - 1):
+        tok = m.decode_step(tok, stream=sh)
+    ad_ms, ad_n = m.profile_read()
+    m.profile_enable(0)
+    m.close()
+    torch.cuda.synchronize()
+
+    lin, attn = c5_prefill_flops()
+    ctx_mid = C5_PREFIX + C5_CHUNK + C5_DECODES // 2
+    dbytes = c5_decode_bytes(ctx_mid)
+    attn_layer_bytes = 2 * C5_HKV * C5_D * 2 * ctx_mid        # K and V of one layer
+    ad_avg = ad_ms / max(ad_n, 1)
+    return {
+        "longctx_prefill_ms": round(pre_ms, 3),
+        "longctx_prefill_tok_s": round(C5_CHUNK / (pre_ms * 1e-3), 1),
+        "longctx_prefill_flop": lin + attn,
+        "longctx_prefill_mfma_frac": round((lin + attn) / (pre_ms * 1e-3)
+                                           / (PEAK_BF16_TFLOPS * 1e12), 4),
+        "longctx_prefill_attention_ms": round(ap_ms, 3),
+        "longctx_prefill_attention_mfma_frac": round(attn / (ap_ms * 1e-3)
+                                                     / (PEAK_BF16_TFLOPS * 1e12), 4),
+        "longctx_decode_ms_per_step": round(dec_ms, 4),
+        "longctx_decode_bytes_per_step": dbytes,
+        "longctx_decode_hbm_frac": round(dbytes / (dec_ms * 1e-3) / (PEAK_HBM_GBS * 1e9), 4),
+        "longctx_decode_attention_us_per_layer": round(ad_avg * 1e3, 2),
+        "longctx_decode_attention_hbm_frac": round(attn_layer_bytes / (ad_avg * 1e-3)
+                                                   / (PEAK_HBM_GBS * 1e9), 4),
+    }
+
+
+# ---------------------------------------------------------------------------
 def cpu_baseline(layers_sample: int):
     """The oracle (fp64 numpy) on a bounded sample of the prefill: the same 1024-token
     context and 256-token chunk, through the first `layers_sample` of the 28 layers, then
@@ -354,6 +473,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-eviction", action="store_true")
+    ap.add_argument("--no-longctx", action="store_true")
     ap.add_argument("--cpu-layers", type=int, default=2)
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:

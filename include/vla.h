@@ -73,8 +73,10 @@ typedef struct {
   int32_t vocab;        /* V */
   float rms_eps;        /* RMSNorm epsilon */
   double rope_theta;    /* RoPE base */
-  int32_t wdtype;       /* projection weights: VLA_F32 or VLA_BF16 */
-  int32_t act_dtype;    /* activations and KV cache: VLA_F32 or VLA_BF16 (= wdtype) */
+  int32_t wdtype;       /* projection weights: VLA_F32, VLA_BF16 (both = act_dtype) or
+                           VLA_INT4_G128 (with act_dtype VLA_BF16; hidden, n_heads*head_dim
+                           and ffn multiples of 128) */
+  int32_t act_dtype;    /* activations, embedding table and KV cache: VLA_F32 or VLA_BF16 */
   int32_t ffn_kind;     /* VLA_SWIGLU */
   int32_t block_tokens; /* tokens per KV block: 16 */
   int32_t num_blocks;   /* KV budget in blocks (the fixed memory budget) */
@@ -91,6 +93,15 @@ typedef struct {
  * ("Can an LLM Forget the Right Things?", section 6: untrained weights from a
  * seeded PRNG). Element i (row-major, logical (out, in) layout) of tensor
  * stream s is init_std * N(seed, s, i) rounded to nearest-even into wdtype.
+ * VLA_INT4_G128 ("Rebuilding Kshipra Around Memory", section 2: INT4 weights
+ * in groups of 128 with one fp16 scale, used both to encode and to decode):
+ * every projection and the output head (the embedding table stays in
+ * act_dtype) is drawn as above, rounded to fp32, and quantised per group of
+ * 128 consecutive inputs of one output row: s = fp16(max|w| / 7) (fp32
+ * division, nearest-even), q = clamp(nearest-even(w / s), -8, 7) (q = 0 when
+ * s = 0). Device layout of an N x K tensor: codes [N][K/2] (two per byte, the
+ * even input in the low nibble), then scales [K/128][N] fp16. Inside the
+ * projections the weight is q * s, exact in fp32.
  * Synchronises the device. Errors: VLA_E_INVALID (bad cfg, out == NULL),
  * VLA_E_HIP (allocation or launch failure). */
 vla_status vla_model_create(const vla_config* cfg, vla_model** out);
@@ -197,7 +208,8 @@ vla_status vla_kv_gather(vla_model* m, int32_t layer, void* k_out, void* v_out,
 
 /* Copy one weight tensor in its logical (out, in) row-major layout and storage
  * type to device memory `out` of `bytes` bytes. kind: 1 q, 2 k, 3 v, 4 o,
- * 5 gate, 6 up, 7 down (per layer), 8 embedding, 9 output head (layer ignored). */
+ * 5 gate, 6 up, 7 down (per layer), 8 embedding, 9 output head (layer ignored).
+ * INT4 models: kinds 1-7 and 9 are written dequantised (q * s, fp32). */
 vla_status vla_weight_out(vla_model* m, int32_t kind, int32_t layer, void* out, int64_t bytes,
                           void* stream);
 
@@ -206,8 +218,10 @@ vla_status vla_weight_out(vla_model* m, int32_t kind, int32_t layer, void* out, 
  * in its own dispatch on the launch stream (so the span is the kernel's
  * execution, as a kernel trace reports it). vla_profile_read synchronises and
  * returns the summed kernel time (ms) and the number of profiled calls since
- * the last enable (a call of VLA_K_SCORE launches two kernels; every other
- * class one). VLA_K_NONE disables. Errors: VLA_E_INVALID (bad class). */
+ * the last enable; a call may launch several kernels, all summed (VLA_K_SCORE:
+ * two; attention: the split pass plus, when the keys are split, the merge;
+ * residual projections: the product plus the split reduction). VLA_K_NONE
+ * disables. Errors: VLA_E_INVALID (bad class). */
 enum {
   VLA_K_NONE = 0, VLA_K_GEMV_QKV = 1, VLA_K_GEMV_O = 2, VLA_K_GEMV_GATEUP = 3,
   VLA_K_GEMV_DOWN = 4, VLA_K_GEMV_HEAD = 5, VLA_K_ATTN_DECODE = 6, VLA_K_GEMM_QKV = 7,

@@ -30,6 +30,9 @@ Modules:
   kvpool    LIFO block free-list + frame registry (block tables).
   scoring   per-frame mean keys, all-pairs cosine, argmax eviction.
   int4      group-128 symmetric INT4 quantiser with one fp16 scale.
+  pi0       the two-part policy step: GeGLU prefix model with a K/V-only last
+            layer, the action expert attending to its cache and to itself in
+            both directions, the time embedding and the Euler loop.
 
 Every function here is "parity pinned" by a CPU test in tests/test_oracle_*.py
 unless its docstring says "parity unpinned".

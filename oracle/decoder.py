@@ -22,6 +22,12 @@ Final: logits = W_Y RMSNorm(x_last) ("CSR ...", §III-A output head W_Y; the
 final norm is the pre-norm reading), greedy next token = argmax, ties to the
 lowest id.
 
+Variants used by the pi0-style prefix model ("Running VLAs at Real-time
+Speed", §2 and §4.1-4.2): GeGLU instead of SwiGLU (exact-erf GELU on the gate
+branch); the last layer reduced to its input norm and K/V projection (its K/V
+are all the action expert reads); no vocabulary (vocab 0: caller embeddings
+only, no output head).
+
 Readings where the pages are silent (each listed in the design notes): pre-norm
 RMSNorm with weight 1 and eps 1e-6; HF-style rotate-half RoPE pairing
 (j, j + d/2) with inv_freq_j = theta^(-2j/d), angles in fp64; scale 1/sqrt(d);
@@ -65,6 +71,9 @@ class Config:
     max_frames: int = 64
     seed: int = 1234
     init_std: float = 0.02
+    ffn_kind: str = "swiglu"    # swiglu | geglu
+    kv_only_last: bool = False  # last layer: input norm + K/V only
+    stream_base: int = 0        # added to the per-layer weight streams
 
     @property
     def group(self) -> int:
@@ -137,7 +146,7 @@ class Weights:
             return rng.STREAM_EMBED
         if name == "head":
             return rng.STREAM_HEAD
-        return rng.layer_stream(layer, self._KIND[name])
+        return self.cfg.stream_base + rng.layer_stream(layer, self._KIND[name])
 
     def _make(self, name: str, layer: int) -> np.ndarray:
         c = self.cfg
@@ -235,6 +244,21 @@ def silu(z: np.ndarray) -> np.ndarray:
 def swiglu_ffn(u: np.ndarray, wg: np.ndarray, wu: np.ndarray, wd: np.ndarray) -> np.ndarray:
     """Wdown-map of silu(u Wgate^T) * (u Wup^T)."""
     return (silu(u @ wg.T) * (u @ wu.T)) @ wd.T
+
+
+def gelu_erf(z: np.ndarray) -> np.ndarray:
+    """Exact GELU: z * Phi(z) = z/2 * (1 + erf(z / sqrt 2))."""
+    from scipy.special import erf
+    return 0.5 * z * (1.0 + erf(z / math.sqrt(2.0)))
+
+
+def geglu_ffn(u: np.ndarray, wg: np.ndarray, wu: np.ndarray, wd: np.ndarray) -> np.ndarray:
+    """Wdown-map of gelu(u Wgate^T) * (u Wup^T)."""
+    return (gelu_erf(u @ wg.T) * (u @ wu.T)) @ wd.T
+
+
+def ffn(cfg: "Config", u: np.ndarray, wg: np.ndarray, wu: np.ndarray, wd: np.ndarray):
+    return (geglu_ffn if cfg.ffn_kind == "geglu" else swiglu_ffn)(u, wg, wu, wd)
 
 
 # ----------------------------------------------------------------------------
@@ -392,6 +416,8 @@ class Session:
             q = apply_rope(q, ang)
             k = apply_rope(k, ang)
             place(l, k, v)
+            if c.kv_only_last and l == c.n_layers - 1:
+                break                               # only this layer's K/V are used
             K, V = self.gather(l)
             T = K.shape[0]
             visible = np.ones((n, T), dtype=bool)
@@ -401,11 +427,13 @@ class Session:
             o = gqa_attention(q, K, V, visible)
             x = x + o.reshape(n, -1) @ self.w.f64("o", l).T
             u2 = rmsnorm(x, self.w.norm(l), c.rms_eps)
-            x = x + swiglu_ffn(u2, self.w.f64("gate", l), self.w.f64("up", l),
-                               self.w.f64("down", l))
+            x = x + ffn(c, u2, self.w.f64("gate", l), self.w.f64("up", l),
+                        self.w.f64("down", l))
         return x
 
-    def _logits(self, h_last: np.ndarray) -> np.ndarray:
+    def _logits(self, h_last: np.ndarray):
+        if self.cfg.vocab == 0:
+            return None                             # no output head
         u = rmsnorm(h_last, self.w.norm(), self.cfg.rms_eps)
         return self.w.f64("head") @ u
 
@@ -522,6 +550,6 @@ def dense_forward(cfg: Config, w: Weights, x: np.ndarray, positions) -> np.ndarr
         o = gqa_attention(q, k, v, causal)
         x = x + o.reshape(T, -1) @ w.f64("o", l).T
         u2 = rmsnorm(x, w.norm(l), cfg.rms_eps)
-        x = x + swiglu_ffn(u2, w.f64("gate", l), w.f64("up", l), w.f64("down", l))
+        x = x + ffn(cfg, u2, w.f64("gate", l), w.f64("up", l), w.f64("down", l))
     u = rmsnorm(x, w.norm(), cfg.rms_eps)
     return u @ w.f64("head").T

@@ -17,6 +17,7 @@ STREAM_EMBEDS = 0x20000
 STREAM_RAW_KV = 0x30000
 STREAM_CENTRES = 0x40000
 STREAM_NOISE = 0x41000
+STREAM_ACTION_NOISE = 0x50000
 
 
 def _gen(seed: int, stream: int, call: int = 0) -> np.random.Generator:
@@ -55,6 +56,11 @@ def embeddings(seed: int, call: int, n: int, hidden: int, storage: str):
     """n visual-token embeddings drawn N(0, 1) per element: (float32 values, storage array)."""
     x = _gen(seed, STREAM_EMBEDS, call).standard_normal((n, hidden), dtype=np.float32)
     return encode(x, storage)
+
+
+def action_noise(seed: int, call: int, n: int, width: int) -> np.ndarray:
+    """An action chunk's starting noise, N(0, 1) per element, float32 [n][width]."""
+    return _gen(seed, STREAM_ACTION_NOISE, call).standard_normal((n, width), dtype=np.float32)
 
 
 def raw_kv_frame(seed: int, frame: int, n_layers: int, ntok: int, n_kv_heads: int,

@@ -27,8 +27,12 @@ def rel(a, b):
 
 
 def _hf_model(cfg, w, exact_angles):
+    """HF Llama on the oracle's weights (hidden_act "gelu" = exact GELU for GeGLU configs;
+    a config without vocabulary gets a one-row dummy embedding and head)."""
     from transformers import LlamaConfig, LlamaForCausalLM
-    hc = LlamaConfig(vocab_size=cfg.vocab, hidden_size=cfg.hidden, intermediate_size=cfg.ffn,
+    act = {"swiglu": "silu", "geglu": "gelu"}[cfg.ffn_kind]
+    hc = LlamaConfig(vocab_size=max(cfg.vocab, 1), hidden_act=act,
+                     hidden_size=cfg.hidden, intermediate_size=cfg.ffn,
                      num_hidden_layers=cfg.n_layers, num_attention_heads=cfg.n_heads,
                      num_key_value_heads=cfg.n_kv_heads, head_dim=cfg.head_dim,
                      rms_norm_eps=cfg.rms_eps,
@@ -39,8 +43,9 @@ def _hf_model(cfg, w, exact_angles):
     m = LlamaForCausalLM(hc).double().eval()
     t = lambda a: torch.from_numpy(np.asarray(a, dtype=np.float64))
     with torch.no_grad():
-        m.model.embed_tokens.weight.copy_(t(w.f64("embed")))
-        m.lm_head.weight.copy_(t(w.f64("head")))
+        if cfg.vocab:
+            m.model.embed_tokens.weight.copy_(t(w.f64("embed")))
+            m.lm_head.weight.copy_(t(w.f64("head")))
         m.model.norm.weight.fill_(1.0)
         for l, layer in enumerate(m.model.layers):
             a, f = layer.self_attn, layer.mlp
@@ -90,6 +95,17 @@ def test_c1_shape_matches_hf_llama():
     w = D.Weights(cfg)
     ids = np.random.default_rng(2).integers(0, cfg.vocab, 80)
     ours = D.dense_forward(cfg, w, w.f64("embed")[ids], np.arange(80))
+    m = _hf_model(cfg, w, exact_angles=True)
+    with torch.no_grad():
+        ref = m(torch.from_numpy(ids)[None]).logits[0].numpy()
+    assert rel(ours, ref) < 1e-10
+
+
+def test_geglu_dense_forward_matches_hf_llama_with_exact_gelu():
+    cfg = T1.with_(name="t1g", ffn_kind="geglu", seed=78)
+    w = D.Weights(cfg)
+    ids = np.random.default_rng(6).integers(0, cfg.vocab, 30)
+    ours = D.dense_forward(cfg, w, w.f64("embed")[ids], np.arange(30))
     m = _hf_model(cfg, w, exact_angles=True)
     with torch.no_grad():
         ref = m(torch.from_numpy(ids)[None]).logits[0].numpy()
