@@ -60,7 +60,9 @@ typedef enum {
 } vla_status;
 
 typedef enum { VLA_F32 = 0, VLA_BF16 = 1, VLA_INT4_G128 = 2 } vla_dtype;
-typedef enum { VLA_SWIGLU = 0 } vla_ffn_kind;
+/* Gated FFN: SwiGLU silu(x Wg^T) * (x Wu^T), or GeGLU with the exact-erf GELU
+ * ("Running VLAs at Real-time Speed", section 4.2: the gated pair, fused). */
+typedef enum { VLA_SWIGLU = 0, VLA_GEGLU = 1 } vla_ffn_kind;
 
 /* Model configuration. Sizes in elements. */
 typedef struct {
@@ -70,21 +72,29 @@ typedef struct {
   int32_t n_kv_heads;   /* KV heads Hkv, divides Hq (Hq/Hkv = group size g) */
   int32_t head_dim;     /* d, even, <= 256, multiple of 16 */
   int32_t ffn;          /* F, multiple of 16 */
-  int32_t vocab;        /* V */
+  int32_t vocab;        /* V; 0: no embedding table and no output head (embeddings
+                           in, K/V out: a prefix model), and no logits */
   float rms_eps;        /* RMSNorm epsilon */
   double rope_theta;    /* RoPE base */
   int32_t wdtype;       /* projection weights: VLA_F32, VLA_BF16 (both = act_dtype) or
                            VLA_INT4_G128 (with act_dtype VLA_BF16; hidden, n_heads*head_dim
                            and ffn multiples of 128) */
   int32_t act_dtype;    /* activations, embedding table and KV cache: VLA_F32 or VLA_BF16 */
-  int32_t ffn_kind;     /* VLA_SWIGLU */
+  int32_t ffn_kind;     /* VLA_SWIGLU or VLA_GEGLU */
   int32_t block_tokens; /* tokens per KV block: 16 */
   int32_t num_blocks;   /* KV budget in blocks (the fixed memory budget) */
   int32_t max_frames;   /* most frames resident at once (mean-key table rows) */
   int32_t max_chunk;    /* longest prefill chunk / raw append, in tokens */
   uint64_t seed;        /* weight seed */
   double init_std;      /* weights ~ N(0, init_std^2); norm weights are 1 */
+  int32_t kv_only_last; /* 1: the last layer computes only its input norm and K/V
+                           ("Running VLAs at Real-time Speed", section 4.1: only the
+                           cache of that layer is used); needs vocab 0 */
+  uint32_t stream_base; /* added to every per-layer weight stream (two models built
+                           from one seed, e.g. a prefix model and its expert) */
 } vla_config;
+
+typedef struct vla_expert vla_expert;
 
 /* Create a model: validates cfg, allocates weights, KV pool (K and V, each
  * [L][num_blocks][Hkv][block_tokens][d] in act_dtype), the mean-key table
@@ -93,6 +103,8 @@ typedef struct {
  * ("Can an LLM Forget the Right Things?", section 6: untrained weights from a
  * seeded PRNG). Element i (row-major, logical (out, in) layout) of tensor
  * stream s is init_std * N(seed, s, i) rounded to nearest-even into wdtype.
+ * Streams: embedding 1, output head 2, layer l's tensors stream_base +
+ * ((l + 1) << 8 | kind), kinds q 1, k 2, v 3, o 4, gate 5, up 6, down 7.
  * VLA_INT4_G128 ("Rebuilding Kshipra Around Memory", section 2: INT4 weights
  * in groups of 128 with one fp16 scale, used both to encode and to decode):
  * every projection and the output head (the embedding table stays in
@@ -230,6 +242,31 @@ enum {
 };
 vla_status vla_profile_enable(vla_model* m, int32_t kernel_class);
 vla_status vla_profile_read(vla_model* m, double* total_ms, int32_t* launches);
+
+/* Action expert of a pi0-style policy ("Running VLAs at Real-time Speed",
+ * section 2: a vision-language prefix model plus an expert that predicts an
+ * action chunk by flow matching). The expert is a decoder of its own (cfg:
+ * vocab 0, all layers full; n_layers, n_kv_heads, head_dim, act_dtype and
+ * block_tokens equal to the prefix model's) whose layer l attends to the
+ * prefix model's layer-l cache plus the n_actions tokens of the chunk, every
+ * key visible to every chunk row (no causal mask inside the chunk). The
+ * chunk's K/V live in ceil(n_actions / block_tokens) blocks popped from the
+ * prefix model's free-list at creation and pushed back by destroy (destroy
+ * every expert of a model before the model). Errors: VLA_E_INVALID (cfg or
+ * shapes), VLA_E_NO_BLOCKS (no room in the prefix pool), VLA_E_HIP. */
+vla_status vla_expert_create(vla_model* prefix, const vla_config* cfg, int32_t n_actions,
+                             vla_expert** out);
+void vla_expert_destroy(vla_expert* e);
+
+/* Flow-matching Euler loop on the action chunk x (device fp32 [n_actions][hidden],
+ * updated in place): for k = 0 .. n_steps-1, tau = k * dt,
+ *   h = x + temb(tau)  (temb: sin(tau w_j) for j < hidden/2, then cos(tau w_j),
+ *                       w_j = 2 pi / p_j, p_j = 0.004 * 1000^(j / (hidden/2 - 1)))
+ *   h = the expert's layers over the chunk at positions P .. P+n_actions-1,
+ *       P = the prefix model's next position (the prefix state is unchanged)
+ *   x += dt * RMSNorm(h)   (the velocity: the final norm, no output projection)
+ * Asynchronous on `stream`. Errors: VLA_E_INVALID (null x, n_steps < 1, dt <= 0). */
+vla_status vla_expert_denoise(vla_expert* e, float* x, int32_t n_steps, double dt, void* stream);
 
 /* Host-only LIFO block pool ("Rebuilding Kshipra Around Memory", section 1):
  * the free-list starts as [0 .. n-1] so the first pop returns n-1; released

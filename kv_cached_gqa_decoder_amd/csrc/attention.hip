@@ -2,7 +2,9 @@
 //
 // softmax(q k^T / sqrt(d)) v over every visible key ("CSR ...", III-A), with
 // the keys of the current chunk causal and every other resident key visible
-// ("Rebuilding Kshipra Around Memory", section 4), computed as an online
+// ("Rebuilding Kshipra Around Memory", section 4) -- or, for the action chunk
+// of a pi0-style expert ("Running VLAs at Real-time Speed", section 2), every
+// key of the chunk visible to every row of it -- computed as an online
 // softmax (m, l, o) over KV blocks read in place from the pool (same section).
 //
 // bf16 path (matrix cores). Query rows are (token, q head of the group) pairs,
@@ -42,7 +44,7 @@ constexpr float kLog2e = 1.4426950408889634f;
 
 __device__ __forceinline__ bool key_visible(const AttnArgs& a, int b, int slot, int ntok, int tq) {
   if (slot >= ntok) return false;
-  if (b < a.cb0) return true;
+  if (b < a.cb0 || !a.causal) return true;
   const int ck = (b - a.cb0) * a.g.bt + slot - a.cslot0;  // index inside the causal region
   return ck <= tq;
 }
@@ -277,7 +279,7 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(AttnArgs a, int rgroups)
   const int bps = (a.nlb + splits - 1) / splits;
   const int b_begin = split * bps;
   int b_end = min(a.nlb, b_begin + bps);
-  {
+  if (a.causal) {
     const int rlast = min(R, rg * ROWS + ROWS) - 1;
     const int tmax = rlast / grp;
     b_end = min(b_end, a.cb0 + (tmax + a.cslot0) / a.g.bt + 1);

@@ -56,6 +56,12 @@ __device__ __forceinline__ double wave_sum_d(double v) {
 }
 
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + __expf(-z)); }
+// exact GELU: z * Phi(z) = z/2 * (1 + erf(z / sqrt 2))
+__device__ __forceinline__ float gelu_erf(float z) { return 0.5f * z * (1.0f + erff(z * 0.70710678118654752f)); }
+// gated FFN activation of a (gate, up) pair: SwiGLU (glu 0) or GeGLU (glu 1)
+__device__ __forceinline__ float glu_act(int glu, float gate, float up) {
+  return (glu ? gelu_erf(gate) : silu(gate)) * up;
+}
 
 // 8 bf16 values held in a 16-byte register quad, unpacked to fp32
 __device__ __forceinline__ void unpack8(const u32x4_t& w, float* f) {

@@ -93,7 +93,7 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& a, f32x4_t (&acc)[
           const int f = (n0 + wn * WN + ni * 16) / 2 + (lane & 15);
           if (row < M)
             St<bf16_t>::st((bf16_t*)a.C, (size_t)row * (a.N / 2) + f,
-                           silu(acc[mi][ni][e]) * acc[mi][ni + 1][e]);
+                           glu_act(a.glu, acc[mi][ni][e], acc[mi][ni + 1][e]));
         }
       } else {
 #pragma unroll
@@ -307,7 +307,7 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs a) {
       const int row = m0 + r;
       if (row < M && n0 + blk * 32 < N)
         ((float*)a.C)[(size_t)row * (N / 2) + (n0 + blk * 32) / 2 + cc] =
-            silu(Cs[r][blk * 32 + cc]) * Cs[r][blk * 32 + 16 + cc];
+            glu_act(a.glu, Cs[r][blk * 32 + cc], Cs[r][blk * 32 + 16 + cc]);
     }
   } else if constexpr (EPI == EPI_QKV) {
     for (int e = tid; e < BM * 32; e += 256) {

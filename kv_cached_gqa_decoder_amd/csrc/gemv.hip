@@ -148,7 +148,7 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(GemvArgs a, int ngro
     } else if constexpr (EPI == EPI_SWIGLU) {
 #pragma unroll
       for (int i = 0; i < RW / 2; ++i)
-        if (lane == i) St<T>::st((T*)a.out, g * (RW / 2) + i, silu(acc[i]) * acc[RW / 2 + i]);
+        if (lane == i) St<T>::st((T*)a.out, g * (RW / 2) + i, glu_act(a.glu, acc[i], acc[RW / 2 + i]));
     } else if constexpr (EPI == EPI_HEAD) {
 #pragma unroll
       for (int r = 0; r < RW; ++r) {
@@ -323,7 +323,7 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_w4_kernel(GemvArgs a, int n
 #pragma unroll
       for (int i = 0; i < RW / 2; ++i)
         if (lane == i)
-          St<bf16_t>::st((bf16_t*)a.out, g * (RW / 2) + i, silu(acc[i]) * acc[RW / 2 + i]);
+          St<bf16_t>::st((bf16_t*)a.out, g * (RW / 2) + i, glu_act(a.glu, acc[i], acc[RW / 2 + i]));
     } else if constexpr (EPI == EPI_HEAD) {
 #pragma unroll
       for (int r = 0; r < RW; ++r) {

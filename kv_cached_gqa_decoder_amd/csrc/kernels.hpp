@@ -79,6 +79,7 @@ struct GemmArgs {
   int wf = WF_ACT;
   int M = 0, N = 0, K = 0;
   int epi = EPI_STORE;
+  int glu = 0;              // SWIGLU epilogue: 0 silu(gate) * up, 1 gelu(gate) * up
   void* C = nullptr;        // STORE [M][N]; RESID fp32 x [M][N] (+=); SWIGLU [M][N/2]
   FwdCtx ctx;
   // bf16 RESID: split-K partials (fp32, [splits][M][N]) reduced by a second
@@ -100,6 +101,7 @@ struct GemvArgs {
   int wf = WF_ACT;
   int N = 0, K = 0;
   int epi = EPI_STORE;
+  int glu = 0;                  // SWIGLU epilogue: 0 silu(gate) * up, 1 gelu(gate) * up
   void* out = nullptr;          // RESID fp32 x[N] (+=); SWIGLU act[N/2]; HEAD logits fp32[N]
   unsigned long long* argmax_part = nullptr;  // HEAD: one key per workgroup
   FwdCtx ctx;
@@ -116,7 +118,8 @@ struct AttnArgs {
   const int* blk_ntok = nullptr;   // valid tokens per logical block
   int nlb = 0;                     // logical blocks visible to this pass
   int last_ntok = 0;               // valid tokens of logical block nlb-1 (overrides the table)
-  int cb0 = 0, cslot0 = 0;         // first token of the causal region (the chunk)
+  int cb0 = 0, cslot0 = 0;         // first token of the chunk (its own keys)
+  int causal = 1;                  // 1: the chunk's own keys causal; 0: all visible
   int n = 0, hq = 0;
   int splits = 1;                  // chosen by launch_attention
   float* part_o = nullptr;         // split partials, part_rows rows of d fp32
@@ -146,6 +149,11 @@ hipError_t launch_rope_table(int64_t pos0, int n, const double* inv_freq, int ha
                              float2* tab, hipStream_t s);
 // x: the fp32 residual rows [n][H]; E and u in the activation type
 hipError_t launch_to_f32(const void* in, float* out, int64_t n, int dt, hipStream_t s);
+// action expert: h = x + time embedding of tau; then x += dt * RMSNorm(h)
+hipError_t launch_action_begin(const float* xa, float* h, int rows, int H, double tau,
+                               hipStream_t s);
+hipError_t launch_euler_step(float* xa, const float* h, const float* g, int rows, int H,
+                             float eps, float dt, hipStream_t s);
 hipError_t launch_embed(const int* tokens, int token_scalar, int n, const void* E, void* x,
                         int H, int dt, unsigned long long* reset_cell, hipStream_t s);
 hipError_t launch_rmsnorm(const void* x, const float* g, void* u, int rows, int H, float eps,

@@ -304,6 +304,52 @@ hipError_t launch_rmsnorm(const void* x, const float* g, void* u, int rows, int 
 }
 
 // ---------------------------------------------------------------------------
+// action expert ("Running VLAs at Real-time Speed", section 2: flow matching on
+// the action chunk). Time embedding of tau, width H: sin(tau w_j) for j < H/2,
+// cos(tau w_{j-H/2}) after, w_j = 2 pi / p_j, p_j = 0.004 * 1000^(j / (H/2 - 1)),
+// evaluated in fp64. h = x + temb(tau), fp32 [rows][H].
+__global__ void action_begin_kernel(const float* xa, float* h, int rows, int H, double tau) {
+  const int half = H / 2;
+  const int64_t total = (int64_t)rows * H;
+  for (int64_t p = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; p < total;
+       p += (int64_t)gridDim.x * blockDim.x) {
+    const int j = (int)(p % H);
+    const int jj = j < half ? j : j - half;
+    const double period = 0.004 * pow(1000.0, (double)jj / (double)(half - 1));
+    const double ang = tau * (6.283185307179586 / period);
+    h[p] = xa[p] + (float)(j < half ? sin(ang) : cos(ang));
+  }
+}
+hipError_t launch_action_begin(const float* xa, float* h, int rows, int H, double tau,
+                               hipStream_t s) {
+  if (H < 4 || H % 2) return hipErrorInvalidValue;
+  launch_k(action_begin_kernel, dim3(grid_for((int64_t)rows * H, 256)), dim3(256), 0, s, xa, h,
+           rows, H, tau);
+  return hipGetLastError();
+}
+
+// Euler step x += dt * v with the velocity v = RMSNorm(h) (the expert's final
+// norm, no output projection); one wavefront per row, fp32
+__global__ __launch_bounds__(256) void euler_step_kernel(float* xa, const float* h, const float* g,
+                                                         int rows, int H, float eps, float dt) {
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= rows) return;
+  const float* hr = h + (int64_t)row * H;
+  float* xr = xa + (int64_t)row * H;
+  float ss = 0.f;
+  for (int c = lane; c < H; c += 64) ss += hr[c] * hr[c];
+  ss = wave_sum(ss);
+  const float r = rsqrtf(ss / (float)H + eps);
+  for (int c = lane; c < H; c += 64) xr[c] += dt * (hr[c] * r * g[c]);
+}
+hipError_t launch_euler_step(float* xa, const float* h, const float* g, int rows, int H,
+                             float eps, float dt, hipStream_t s) {
+  launch_k(euler_step_kernel, dim3((rows + 3) / 4), dim3(256), 0, s, xa, h, g, rows, H, eps, dt);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
 // raw frame append: k, v [L][n][Hkv][d] -> the paged pool at the frame's blocks
 template <typename T>
 __global__ void kv_scatter_kernel(const T* k, const T* v, int n, T* kp, T* vp, KvGeom g,

@@ -81,6 +81,16 @@ bool prof_take_pair(ProfSink* s, hipEvent_t* a, hipEvent_t* b) {
 }
 }  // namespace vla
 
+struct vla_model;
+struct vla_expert {
+  vla_model* m = nullptr;        // the expert's weights and scratch (pool borrowed)
+  vla_model* prefix = nullptr;   // the model whose cache it reads and writes into
+  std::vector<int> reserved;     // prefix-pool blocks holding the action chunk's K/V
+  int n_actions = 0;
+  int* d_view = nullptr;         // block list of a pass: blk | ntok (num_blocks each)
+  Staging st_view;
+};
+
 struct vla_model {
   vla_config cfg{};
   int dev = 0;
@@ -273,14 +283,33 @@ int last_block_ntok(const vla_model* m) {
   return 0;
 }
 
-FwdCtx make_ctx(vla_model* m, int layer, int cb0, int cslot0) {
+// the blocks a pass reads: logical block list (device), valid tokens per block,
+// and whether the pass's own keys are causal
+struct KvView {
+  const int* blk = nullptr;
+  const int* ntok = nullptr;
+  int nlb = 0;
+  int last_ntok = 0;
+  int causal = 1;
+};
+
+KvView model_view(vla_model* m) {
+  KvView v;
+  v.blk = m->d_blk();
+  v.ntok = m->d_ntok();
+  v.nlb = logical_blocks(m);
+  v.last_ntok = last_block_ntok(m);
+  return v;
+}
+
+FwdCtx make_ctx(vla_model* m, const KvView& v, int layer, int cb0, int cslot0) {
   FwdCtx c;
   c.layer = layer;
   c.rope = m->rope_tab;
   c.kpool = m->kpool;
   c.vpool = m->vpool;
   c.g = m->geom;
-  c.blk_table = m->d_blk();
+  c.blk_table = v.blk;
   c.cb0 = cb0;
   c.cslot0 = cslot0;
   c.qbuf = m->qbuf;
@@ -290,12 +319,12 @@ FwdCtx make_ctx(vla_model* m, int layer, int cb0, int cslot0) {
 
 // the per-layer launches of one pass over n rows whose K/V go to logical slots
 // (cb0, cslot0 ...); rows = prefill chunk (n >= 1, matrix path) or decode (GEMV path)
-void run_layers(vla_model* m, int n, int64_t pos0, int cb0, int cslot0, bool decode,
-                hipStream_t st) {
+void run_layers(vla_model* m, const KvView& view, int n, int64_t pos0, int cb0, int cslot0,
+                bool decode, hipStream_t st) {
   const vla_config& c = m->cfg;
   const int H = c.hidden, qd = c.n_heads * c.head_dim;
   const int nqkv = (c.n_heads + 2 * c.n_kv_heads) * c.head_dim;
-  const int nlb = logical_blocks(m);
+  const int glu = c.ffn_kind == VLA_GEGLU ? 1 : 0;
   // the rows' RoPE (cos, sin), shared by every layer of this pass
   HIPCHK(launch_rope_table(pos0, n, m->inv_freq, c.head_dim / 2, m->rope_tab, st));
   AttnArgs at;
@@ -304,10 +333,11 @@ void run_layers(vla_model* m, int n, int64_t pos0, int cb0, int cslot0, bool dec
   at.kpool = m->kpool;
   at.vpool = m->vpool;
   at.g = m->geom;
-  at.blk_table = m->d_blk();
-  at.blk_ntok = m->d_ntok();
-  at.nlb = nlb;
-  at.last_ntok = last_block_ntok(m);
+  at.blk_table = view.blk;
+  at.blk_ntok = view.ntok;
+  at.nlb = view.nlb;
+  at.last_ntok = view.last_ntok;
+  at.causal = view.causal;
   at.cb0 = cb0;
   at.cslot0 = cslot0;
   at.n = n;
@@ -320,7 +350,9 @@ void run_layers(vla_model* m, int n, int64_t pos0, int cb0, int cslot0, bool dec
 
   for (int l = 0; l < c.n_layers; ++l) {
     at.layer = l;
-    const FwdCtx ctx = make_ctx(m, l, cb0, cslot0);
+    const FwdCtx ctx = make_ctx(m, view, l, cb0, cslot0);
+    // a K/V-only last layer: its input norm and q/k/v projection (K/V written), nothing more
+    const bool kv_only = c.kv_only_last && l == c.n_layers - 1;
     if (decode) {
       GemvArgs g;
       g.x = m->x;
@@ -333,6 +365,7 @@ void run_layers(vla_model* m, int n, int64_t pos0, int cb0, int cslot0, bool dec
       g.epi = EPI_QKV;
       g.ctx = ctx;
       LAUNCH(m, VLA_K_GEMV_QKV, st, launch_gemv(g, m->dt, st, nullptr));
+      if (kv_only) break;
       LAUNCH(m, VLA_K_ATTN_DECODE, st, launch_attention(at, m->dt, st));
       GemvArgs o;
       o.x = m->ao;
@@ -352,6 +385,7 @@ void run_layers(vla_model* m, int n, int64_t pos0, int cb0, int cslot0, bool dec
       gu.N = 2 * c.ffn;
       gu.K = H;
       gu.epi = EPI_SWIGLU;
+      gu.glu = glu;
       gu.out = m->act;
       LAUNCH(m, VLA_K_GEMV_GATEUP, st, launch_gemv(gu, m->dt, st, nullptr));
       GemvArgs dn;
@@ -383,6 +417,7 @@ void run_layers(vla_model* m, int n, int64_t pos0, int cb0, int cslot0, bool dec
       q.ws = m->gemm_ws;
       q.ws_elems = m->gemm_ws_elems;
       LAUNCH(m, VLA_K_GEMM_QKV, st, launch_gemm(q, m->dt, st));
+      if (kv_only) break;
       LAUNCH(m, VLA_K_ATTN_PREFILL, st, launch_attention(at, m->dt, st));
       GemmArgs o;
       o.A = m->ao;
@@ -410,6 +445,7 @@ void run_layers(vla_model* m, int n, int64_t pos0, int cb0, int cslot0, bool dec
       gu.N = 2 * c.ffn;
       gu.K = H;
       gu.epi = EPI_SWIGLU;
+      gu.glu = glu;
       gu.C = m->act;
       LAUNCH(m, VLA_K_GEMM_GATEUP, st, launch_gemm(gu, m->dt, st));
       GemmArgs dn;
@@ -500,7 +536,7 @@ void validate_cfg(const vla_config* c) {
   auto bad = [](const std::string& s) { raise(VLA_E_INVALID, "invalid config: " + s); };
   if (!c) bad("null");
   if (c->n_layers < 1 || c->hidden < 64 || c->n_heads < 1 || c->n_kv_heads < 1 ||
-      c->head_dim < 2 || c->ffn < 16 || c->vocab < 2)
+      c->head_dim < 2 || c->ffn < 16 || c->vocab < 0 || c->vocab == 1)
     bad("non-positive size");
   if (c->n_heads % c->n_kv_heads) bad("n_heads must be a multiple of n_kv_heads");
   if (c->head_dim % 16 || c->head_dim > 256) bad("head_dim must be a multiple of 16, <= 256");
@@ -517,7 +553,10 @@ void validate_cfg(const vla_config* c) {
   } else if (c->wdtype != c->act_dtype) {
     bad("wdtype must equal act_dtype (VLA_F32 or VLA_BF16) or be VLA_INT4_G128");
   }
-  if (c->ffn_kind != VLA_SWIGLU) bad("ffn_kind");
+  if (c->ffn_kind != VLA_SWIGLU && c->ffn_kind != VLA_GEGLU) bad("ffn_kind");
+  if (c->kv_only_last != 0 && c->kv_only_last != 1) bad("kv_only_last must be 0 or 1");
+  if (c->kv_only_last && c->vocab != 0) bad("a K/V-only last layer leaves no output for a head");
+  if (c->stream_base > 0xFFFFFF) bad("stream_base");
   if (!(c->rope_theta > 1.0)) bad("rope_theta");
   const int qd = c->n_heads * c->head_dim;
   if (c->act_dtype == VLA_BF16) {
@@ -535,7 +574,8 @@ void init_weights(vla_model* m) {
   const vla_config& c = m->cfg;
   const int H = c.hidden, d = c.head_dim, hq = c.n_heads, hkv = c.n_kv_heads;
   const hipStream_t st = nullptr;
-  auto sid = [](int layer, int kind) { return (uint64_t)(((layer + 1) << 8) | kind); };
+  const uint64_t base = c.stream_base;
+  auto sid = [base](int layer, int kind) { return base + (uint64_t)(((layer + 1) << 8) | kind); };
   // a projection: in the activation type, or INT4 group-128 (codes + scales)
   auto proj = [&](void* out, int layout, int64_t rows, int64_t cols, uint64_t sa, uint64_t sb,
                   uint64_t sc) {
@@ -546,9 +586,11 @@ void init_weights(vla_model* m) {
       HIPCHK(launch_init_weight(out, m->dt, layout, rows, cols, c.seed, sa, sb, sc, hq, hkv, d,
                                 c.init_std, st));
   };
-  HIPCHK(launch_init_weight(m->embed, m->dt, LAYOUT_PLAIN, c.vocab, H, c.seed, 1, 1, 1, hq, hkv,
-                            d, c.init_std, st));
-  proj(m->head, LAYOUT_PLAIN, c.vocab, H, 2, 2, 2);
+  if (c.vocab > 0) {
+    HIPCHK(launch_init_weight(m->embed, m->dt, LAYOUT_PLAIN, c.vocab, H, c.seed, 1, 1, 1, hq, hkv,
+                              d, c.init_std, st));
+    proj(m->head, LAYOUT_PLAIN, c.vocab, H, 2, 2, 2);
+  }
   for (int l = 0; l < c.n_layers; ++l) {
     proj(m->wqkv[l], LAYOUT_QKV, (int64_t)(hq + 2 * hkv) * d, H, sid(l, 1), sid(l, 2), sid(l, 3));
     proj(m->wo[l], LAYOUT_PLAIN, H, (int64_t)hq * d, sid(l, 4), sid(l, 4), sid(l, 4));
@@ -574,6 +616,73 @@ void destroy(vla_model* m) {
   delete m;
 }
 
+// allocate and initialise a model; `borrow` (non-null): the KV pool and its
+// geometry belong to that model (an action expert writing into its prefix's pool)
+void build_model(vla_model* m, const vla_config& cfg, const vla_model* borrow) {
+  m->cfg = cfg;
+  HIPCHK(hipGetDevice(&m->dev));
+  const vla_config& c = m->cfg;
+  m->dt = c.act_dtype == VLA_F32 ? DT_F32 : DT_BF16;
+  m->wf = c.wdtype == VLA_INT4_G128 ? WF_INT4 : WF_ACT;
+  m->esz = m->dt == DT_F32 ? 4 : 2;
+  m->geom = borrow ? borrow->geom
+                   : KvGeom{c.n_layers, c.num_blocks, c.n_kv_heads, c.block_tokens, c.head_dim};
+  const size_t H = c.hidden, d = c.head_dim, hq = c.n_heads, hkv = c.n_kv_heads;
+  const size_t e = m->esz;
+  // projection bytes: activation type, or INT4 codes (half a byte) + one fp16 per 128
+  auto wbytes = [&](size_t rows, size_t cols) {
+    return m->wf == WF_INT4 ? rows * cols / 2 + rows * (cols / 128) * 2 : rows * cols * e;
+  };
+  m->embed = dalloc(m, (size_t)c.vocab * H * e);
+  m->head = dalloc(m, wbytes(c.vocab, H));
+  for (int l = 0; l < c.n_layers; ++l) {
+    m->wqkv.push_back(dalloc(m, wbytes((hq + 2 * hkv) * d, H)));
+    m->wo.push_back(dalloc(m, wbytes(H, hq * d)));
+    m->wgu.push_back(dalloc(m, wbytes(2 * (size_t)c.ffn, H)));
+    m->wdown.push_back(dalloc(m, wbytes(H, c.ffn)));
+  }
+  m->norm_ones = (float*)dalloc(m, H * sizeof(float));
+  m->inv_freq = (double*)dalloc(m, d / 2 * sizeof(double));
+  m->rope_tab = (float2*)dalloc(m, (size_t)c.max_chunk * (d / 2) * sizeof(float2));
+  if (borrow) {
+    m->kpool = borrow->kpool;
+    m->vpool = borrow->vpool;
+  } else {
+    const size_t pool_bytes = (size_t)c.n_layers * c.num_blocks * hkv * c.block_tokens * d * e;
+    m->kpool = dalloc(m, pool_bytes);
+    m->vpool = dalloc(m, pool_bytes);
+    // stale slots of partial blocks meet zero probabilities in P*V: keep them finite
+    HIPCHK(hipMemset(m->kpool, 0, pool_bytes));
+    HIPCHK(hipMemset(m->vpool, 0, pool_bytes));
+  }
+  m->meankeys = (double*)dalloc(m, (size_t)c.n_layers * c.max_frames * hkv * d * sizeof(double));
+  const size_t mc = c.max_chunk;
+  m->x = dalloc(m, mc * H * sizeof(float));  // the residual stream is fp32
+  m->u = dalloc(m, mc * H * e);
+  m->qbuf = dalloc(m, mc * hq * d * e);
+  m->ao = dalloc(m, mc * hq * d * e);
+  m->act = dalloc(m, mc * (size_t)c.ffn * e);
+  m->logits = (float*)dalloc(m, (size_t)c.vocab * sizeof(float));
+  m->amax_part = (unsigned long long*)dalloc(m, kArgmaxParts * sizeof(unsigned long long));
+  m->amax_res = (unsigned long long*)dalloc(m, sizeof(unsigned long long));
+  if (m->dt == DT_BF16) {
+    m->part_o = (float*)dalloc(m, (size_t)kPartRows * d * sizeof(float));
+    m->part_ml = (float*)dalloc(m, (size_t)kPartRows * 2 * sizeof(float));
+    m->gemm_ws_elems = (size_t)kGemmSplitsMax * mc * std::max(H, (hq + 2 * hkv) * d);
+    m->gemm_ws = (float*)dalloc(m, m->gemm_ws_elems * sizeof(float));
+  }
+  m->d_meta = (int*)dalloc(m, m->meta_ints() * sizeof(int));
+  m->d_tokens = (int*)dalloc(m, mc * sizeof(int));
+  m->d_score_m = (double*)dalloc(m, (size_t)c.max_frames * sizeof(double));
+  m->d_score_res = (double*)dalloc(m, 2 * sizeof(double));
+  staging_init(m->st_meta, m->meta_ints() * sizeof(int));
+  staging_init(m->st_tok, mc * sizeof(int));
+  staging_init(m->st_read, 64);
+  m->pool.reset(c.num_blocks);
+  for (int i = c.max_frames - 1; i >= 0; --i) m->free_slots.push_back(i);
+  init_weights(m);
+}
+
 }  // namespace
 
 // ============================================================================
@@ -590,63 +699,7 @@ vla_status vla_model_create(const vla_config* cfg, vla_model** out) {
     *out = nullptr;
     validate_cfg(cfg);
     m = new vla_model();
-    m->cfg = *cfg;
-    HIPCHK(hipGetDevice(&m->dev));
-    const vla_config& c = m->cfg;
-    m->dt = c.act_dtype == VLA_F32 ? DT_F32 : DT_BF16;
-    m->wf = c.wdtype == VLA_INT4_G128 ? WF_INT4 : WF_ACT;
-    m->esz = m->dt == DT_F32 ? 4 : 2;
-    m->geom = KvGeom{c.n_layers, c.num_blocks, c.n_kv_heads, c.block_tokens, c.head_dim};
-    const size_t H = c.hidden, d = c.head_dim, hq = c.n_heads, hkv = c.n_kv_heads;
-    const size_t e = m->esz;
-    // projection bytes: activation type, or INT4 codes (half a byte) + one fp16 per 128
-    auto wbytes = [&](size_t rows, size_t cols) {
-      return m->wf == WF_INT4 ? rows * cols / 2 + rows * (cols / 128) * 2 : rows * cols * e;
-    };
-    m->embed = dalloc(m, (size_t)c.vocab * H * e);
-    m->head = dalloc(m, wbytes(c.vocab, H));
-    for (int l = 0; l < c.n_layers; ++l) {
-      m->wqkv.push_back(dalloc(m, wbytes((hq + 2 * hkv) * d, H)));
-      m->wo.push_back(dalloc(m, wbytes(H, hq * d)));
-      m->wgu.push_back(dalloc(m, wbytes(2 * (size_t)c.ffn, H)));
-      m->wdown.push_back(dalloc(m, wbytes(H, c.ffn)));
-    }
-    m->norm_ones = (float*)dalloc(m, H * sizeof(float));
-    m->inv_freq = (double*)dalloc(m, d / 2 * sizeof(double));
-    m->rope_tab = (float2*)dalloc(m, (size_t)c.max_chunk * (d / 2) * sizeof(float2));
-    const size_t pool_bytes = (size_t)c.n_layers * c.num_blocks * hkv * c.block_tokens * d * e;
-    m->kpool = dalloc(m, pool_bytes);
-    m->vpool = dalloc(m, pool_bytes);
-    // stale slots of partial blocks meet zero probabilities in P*V: keep them finite
-    HIPCHK(hipMemset(m->kpool, 0, pool_bytes));
-    HIPCHK(hipMemset(m->vpool, 0, pool_bytes));
-    m->meankeys = (double*)dalloc(m, (size_t)c.n_layers * c.max_frames * hkv * d * sizeof(double));
-    const size_t mc = c.max_chunk;
-    m->x = dalloc(m, mc * H * sizeof(float));  // the residual stream is fp32
-    m->u = dalloc(m, mc * H * e);
-    m->qbuf = dalloc(m, mc * hq * d * e);
-    m->ao = dalloc(m, mc * hq * d * e);
-    m->act = dalloc(m, mc * (size_t)c.ffn * e);
-    m->logits = (float*)dalloc(m, (size_t)c.vocab * sizeof(float));
-    m->amax_part = (unsigned long long*)dalloc(m, kArgmaxParts * sizeof(unsigned long long));
-    m->amax_res = (unsigned long long*)dalloc(m, sizeof(unsigned long long));
-    if (m->dt == DT_BF16) {
-      m->part_o = (float*)dalloc(m, (size_t)kPartRows * d * sizeof(float));
-      m->part_ml = (float*)dalloc(m, (size_t)kPartRows * 2 * sizeof(float));
-      m->gemm_ws_elems = (size_t)kGemmSplitsMax * mc * std::max(H, (hq + 2 * hkv) * d);
-      m->gemm_ws = (float*)dalloc(m, m->gemm_ws_elems * sizeof(float));
-
-    }
-    m->d_meta = (int*)dalloc(m, m->meta_ints() * sizeof(int));
-    m->d_tokens = (int*)dalloc(m, mc * sizeof(int));
-    m->d_score_m = (double*)dalloc(m, (size_t)c.max_frames * sizeof(double));
-    m->d_score_res = (double*)dalloc(m, 2 * sizeof(double));
-    staging_init(m->st_meta, m->meta_ints() * sizeof(int));
-    staging_init(m->st_tok, mc * sizeof(int));
-    staging_init(m->st_read, 64);
-    m->pool.reset(c.num_blocks);
-    for (int i = c.max_frames - 1; i >= 0; --i) m->free_slots.push_back(i);
-    init_weights(m);
+    build_model(m, *cfg, nullptr);
     *out = m;
   });
   if (st != VLA_OK && m) {
@@ -666,6 +719,7 @@ vla_status vla_prefill_chunk(vla_model* m, const int32_t* tokens, const void* em
     if ((tokens == nullptr) == (embeds == nullptr))
       raise(VLA_E_INVALID, "exactly one of tokens / embeds must be given");
     if (n < 1 || n > m->cfg.max_chunk) raise(VLA_E_INVALID, "chunk length out of range");
+    if (tokens && m->cfg.vocab == 0) raise(VLA_E_INVALID, "no vocabulary: pass embeddings");
     if (tokens)
       for (int i = 0; i < n; ++i)
         if (tokens[i] < 0 || tokens[i] >= m->cfg.vocab) raise(VLA_E_INVALID, "token id out of range");
@@ -683,8 +737,8 @@ vla_status vla_prefill_chunk(vla_model* m, const int32_t* tokens, const void* em
       } else {
         HIPCHK(launch_to_f32(embeds, (float*)m->x, (int64_t)n * m->cfg.hidden, m->dt, st));
       }
-      run_layers(m, n, seg.start_pos, seg_blk0(m, si), 0, /*decode=*/false, st);
-      run_head(m, n - 1, st);
+      run_layers(m, model_view(m), n, seg.start_pos, seg_blk0(m, si), 0, /*decode=*/false, st);
+      if (m->cfg.vocab > 0) run_head(m, n - 1, st);
       mean_keys_for(m, frame_index_of(m, si), st);
     } catch (...) {
       // undo the registration (blocks back in reverse pop order)
@@ -731,7 +785,7 @@ vla_status vla_decode_step(vla_model* m, int32_t token, int32_t* out_next_token,
       sync_meta(m, st);
       const int cb0 = logical_blocks(m) - 1;
       HIPCHK(launch_embed(nullptr, token, 1, m->embed, m->x, m->cfg.hidden, m->dt, nullptr, st));
-      run_layers(m, 1, pos, cb0, off % bt, /*decode=*/true, st);
+      run_layers(m, model_view(m), 1, pos, cb0, off % bt, /*decode=*/true, st);
       run_head(m, 0, st);
     } catch (...) {
       tail.ntok -= 1;
@@ -960,6 +1014,7 @@ vla_status vla_weight_out(vla_model* m, int32_t kind, int32_t layer, void* out, 
     const vla_config& c = m->cfg;
     if (kind < 1 || kind > 9) raise(VLA_E_INVALID, "kind");
     if (kind <= 7 && (layer < 0 || layer >= c.n_layers)) raise(VLA_E_INVALID, "layer");
+    if (kind >= 8 && c.vocab == 0) raise(VLA_E_INVALID, "no vocabulary");
     HIPCHK(hipSetDevice(m->dev));
     const hipStream_t st = (hipStream_t)stream;
     const int64_t H = c.hidden, d = c.head_dim, qd = (int64_t)c.n_heads * d,
@@ -1015,6 +1070,102 @@ vla_status vla_profile_read(vla_model* m, double* total_ms, int32_t* launches) {
     }
     if (total_ms) *total_ms = tot;
     if (launches) *launches = m->prof.calls;
+  });
+}
+
+// ---- action expert ("Running VLAs at Real-time Speed", section 2) ----
+vla_status vla_expert_create(vla_model* prefix, const vla_config* cfg, int32_t n_actions,
+                             vla_expert** out) {
+  vla_expert* e = nullptr;
+  vla_status st = guarded([&] {
+    if (!out) raise(VLA_E_INVALID, "out is NULL");
+    *out = nullptr;
+    if (!prefix || !cfg) raise(VLA_E_INVALID, "null argument");
+    if (n_actions < 1) raise(VLA_E_INVALID, "n_actions must be >= 1");
+    const vla_config& pc = prefix->cfg;
+    vla_config c = *cfg;
+    if (c.vocab != 0 || c.kv_only_last)
+      raise(VLA_E_INVALID, "invalid config: an expert has no vocabulary and all layers full");
+    if (c.n_layers != pc.n_layers || c.n_kv_heads != pc.n_kv_heads ||
+        c.head_dim != pc.head_dim || c.act_dtype != pc.act_dtype ||
+        c.block_tokens != pc.block_tokens)
+      raise(VLA_E_INVALID, "invalid config: layers, KV heads, head_dim, act_dtype and "
+                           "block_tokens must match the prefix model");
+    c.num_blocks = pc.num_blocks;
+    c.max_frames = 1;
+    c.max_chunk = n_actions;
+    validate_cfg(&c);
+    HIPCHK(hipSetDevice(prefix->dev));
+    e = new vla_expert();
+    e->prefix = prefix;
+    e->n_actions = n_actions;
+    e->m = new vla_model();
+    build_model(e->m, c, prefix);
+    const int nres = (n_actions + c.block_tokens - 1) / c.block_tokens;
+    if (!prefix->pool.alloc(nres, &e->reserved))
+      raise(VLA_E_NO_BLOCKS, "no free blocks in the prefix pool for the action chunk's K/V");
+    e->d_view = (int*)dalloc(e->m, 2 * (size_t)pc.num_blocks * sizeof(int));
+    staging_init(e->st_view, 2 * (size_t)pc.num_blocks * sizeof(int));
+    *out = e;
+  });
+  if (st != VLA_OK && e) {
+    std::string keep = g_err;
+    vla_expert_destroy(e);
+    g_err = keep;
+  }
+  return st;
+}
+
+void vla_expert_destroy(vla_expert* e) {
+  if (!e) return;
+  if (e->m) destroy(e->m);
+  staging_free(e->st_view);
+  if (!e->reserved.empty()) {
+    std::vector<int> rb(e->reserved.rbegin(), e->reserved.rend());
+    e->prefix->pool.release(rb.data(), (int)rb.size());
+  }
+  delete e;
+}
+
+vla_status vla_expert_denoise(vla_expert* e, float* x, int32_t n_steps, double dt, void* stream) {
+  return guarded([&] {
+    if (!e || !x) raise(VLA_E_INVALID, "null argument");
+    if (n_steps < 1 || !(dt > 0.0) || !std::isfinite(dt))
+      raise(VLA_E_INVALID, "need n_steps >= 1 and a finite dt > 0");
+    vla_model* p = e->prefix;
+    vla_model* m = e->m;
+    HIPCHK(hipSetDevice(m->dev));
+    const hipStream_t st = (hipStream_t)stream;
+    const int bt = bt_of(p), n = e->n_actions, H = m->cfg.hidden, cap = p->cfg.num_blocks;
+    // the blocks of every pass: the prefix's resident blocks in logical order, then
+    // the chunk's own (its K/V are rewritten by every pass)
+    int* h = (int*)staging_acquire(e->st_view);
+    int nb = 0;
+    for (const auto& sg : p->segs)
+      for (size_t i = 0; i < sg.blocks.size(); ++i) {
+        h[nb] = sg.blocks[i];
+        h[cap + nb] = std::min(bt, sg.ntok - (int)i * bt);
+        ++nb;
+      }
+    const int cb0 = nb;
+    for (size_t i = 0; i < e->reserved.size(); ++i) {
+      h[nb] = e->reserved[i];
+      h[cap + nb] = std::min(bt, n - (int)i * bt);
+      ++nb;
+    }
+    KvView v;
+    v.blk = e->d_view;
+    v.ntok = e->d_view + cap;
+    v.nlb = nb;
+    v.last_ntok = h[cap + nb - 1];
+    v.causal = 0;
+    staging_upload(e->st_view, e->d_view, 2 * (size_t)cap * sizeof(int), st);
+    for (int k = 0; k < n_steps; ++k) {
+      HIPCHK(launch_action_begin(x, (float*)m->x, n, H, k * dt, st));
+      run_layers(m, v, n, p->next_pos, cb0, 0, /*decode=*/false, st);
+      HIPCHK(launch_euler_step(x, (const float*)m->x, m->norm_ones, n, H, m->cfg.rms_eps,
+                               (float)dt, st));
+    }
   });
 }
 

@@ -18,7 +18,7 @@ LIB_PATH = os.path.join(HERE, "libvla.so")
 VLA_OK, VLA_E_INVALID, VLA_E_NO_BLOCKS, VLA_E_NOTHING_TO_EVICT, VLA_E_HIP, VLA_E_STATE = \
     0, -1, -2, -3, -4, -5
 VLA_F32, VLA_BF16, VLA_INT4_G128 = 0, 1, 2
-VLA_SWIGLU = 0
+VLA_SWIGLU, VLA_GEGLU = 0, 1
 
 # kernel classes for vla_profile_enable
 K_CLASSES = {
@@ -42,6 +42,7 @@ class vla_config(ctypes.Structure):
         ("wdtype", c_int32), ("act_dtype", c_int32), ("ffn_kind", c_int32),
         ("block_tokens", c_int32), ("num_blocks", c_int32), ("max_frames", c_int32),
         ("max_chunk", c_int32), ("seed", c_uint64), ("init_std", c_double),
+        ("kv_only_last", c_int32), ("stream_base", ctypes.c_uint32),
     ]
 
 
@@ -76,6 +77,9 @@ _SIGS = {
     "vla_weight_out": (c_int32, [c_void_p, c_int32, c_int32, c_void_p, c_int64, c_void_p]),
     "vla_profile_enable": (c_int32, [c_void_p, c_int32]),
     "vla_profile_read": (c_int32, [c_void_p, POINTER(c_double), POINTER(c_int32)]),
+    "vla_expert_create": (c_int32, [c_void_p, POINTER(vla_config), c_int32, POINTER(c_void_p)]),
+    "vla_expert_destroy": (None, [c_void_p]),
+    "vla_expert_denoise": (c_int32, [c_void_p, c_void_p, c_int32, c_double, c_void_p]),
     "vla_pool_create": (c_int32, [c_int32, POINTER(c_void_p)]),
     "vla_pool_destroy": (None, [c_void_p]),
     "vla_pool_alloc": (c_int32, [c_void_p, c_int32, c_void_p]),
@@ -244,6 +248,20 @@ def vla_profile_read(m: int):
     return ms.value, n.value
 
 
+def vla_expert_create(prefix: int, cfg: vla_config, n_actions: int) -> int:
+    h = c_void_p()
+    _check(load().vla_expert_create(prefix, byref(cfg), n_actions, byref(h)))
+    return h.value
+
+
+def vla_expert_destroy(e: int) -> None:
+    load().vla_expert_destroy(e)
+
+
+def vla_expert_denoise(e: int, x, n_steps: int, dt: float, stream=None) -> None:
+    _check(load().vla_expert_denoise(e, _ptr(x), n_steps, dt, _stream(stream)))
+
+
 def vla_pool_create(num_blocks: int) -> int:
     h = c_void_p()
     _check(load().vla_pool_create(num_blocks, byref(h)))
@@ -292,6 +310,16 @@ PRESETS = {
                               ffn=14336, vocab=128256, rope_theta=5e5, wdtype=VLA_INT4_G128,
                               act_dtype=VLA_BF16, num_blocks=7534, max_frames=256,
                               max_chunk=512, seed=1239),
+    # pi0-style policy: Gemma-2B-shaped prefix (17 GeGLU layers + a K/V-only 18th, MQA,
+    # head dim 256) over 2 x 256 image tokens, and the 300M action expert (18 layers,
+    # hidden 1024) denoising a 63-token action chunk in 10 Euler steps
+    "c4_pi0_vlm": dict(n_layers=18, hidden=2048, n_heads=8, n_kv_heads=1, head_dim=256,
+                       ffn=16384, vocab=0, rope_theta=1e4, wdtype=VLA_BF16, ffn_kind=VLA_GEGLU,
+                       kv_only_last=1, num_blocks=40, max_frames=4, max_chunk=512, seed=1238),
+    "c4_pi0_action_expert": dict(n_layers=18, hidden=1024, n_heads=8, n_kv_heads=1,
+                                 head_dim=256, ffn=4096, vocab=0, rope_theta=1e4,
+                                 wdtype=VLA_BF16, ffn_kind=VLA_GEGLU, stream_base=0x8000,
+                                 num_blocks=0, max_frames=0, max_chunk=63, seed=1238),
 }
 
 
@@ -308,13 +336,15 @@ def make_config(**kw) -> vla_config:
     c.rope_theta = kw.get("rope_theta", 1e4)
     c.wdtype = kw.get("wdtype", VLA_BF16)
     c.act_dtype = kw.get("act_dtype", VLA_BF16 if c.wdtype == VLA_INT4_G128 else c.wdtype)
-    c.ffn_kind = VLA_SWIGLU
+    c.ffn_kind = kw.get("ffn_kind", VLA_SWIGLU)
     c.block_tokens = kw.get("block_tokens", 16)
     c.num_blocks = kw["num_blocks"]
     c.max_frames = kw["max_frames"]
     c.max_chunk = kw["max_chunk"]
     c.seed = kw["seed"]
     c.init_std = kw.get("init_std", 0.02)
+    c.kv_only_last = int(kw.get("kv_only_last", 0))
+    c.stream_base = int(kw.get("stream_base", 0))
     return c
 
 
@@ -391,3 +421,27 @@ class Model:
 
     def profile_read(self):
         return vla_profile_read(self.h)
+
+
+class Expert:
+    """An action expert bound to a prefix Model; forwards to the vla_expert_* entry points."""
+
+    def __init__(self, prefix: Model, cfg: vla_config, n_actions: int):
+        self.prefix = prefix
+        self.cfg = cfg
+        self.n_actions = n_actions
+        self.h = vla_expert_create(prefix.h, cfg, n_actions)
+
+    def close(self):
+        if self.h:
+            vla_expert_destroy(self.h)
+            self.h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def denoise(self, x, n_steps=10, dt=None, stream=None):
+        vla_expert_denoise(self.h, x, n_steps, 1.0 / n_steps if dt is None else dt, stream)

@@ -93,8 +93,13 @@ def test_host_pool_rejects_double_free_and_bad_ids(vla):
 
 def test_config_presets_match_the_oracle_shapes(vla):
     from oracle import decoder as D
+    from oracle import pi0
+    configs = dict(D.CONFIGS, **{c.name: c for c in (pi0.C4_VLM, pi0.C4_AE)})
     for name, p in vla.PRESETS.items():
-        c = D.CONFIGS[name]
+        c = configs[name]
+        assert (p.get("ffn_kind", vla.VLA_SWIGLU) == vla.VLA_GEGLU) == (c.ffn_kind == "geglu")
+        assert bool(p.get("kv_only_last", 0)) == c.kv_only_last
+        assert p.get("stream_base", 0) == c.stream_base
         assert (p["n_layers"], p["hidden"], p["n_heads"], p["n_kv_heads"], p["head_dim"],
                 p["ffn"], p["vocab"], p["num_blocks"], p["max_frames"], p["seed"]) == \
             (c.n_layers, c.hidden, c.n_heads, c.n_kv_heads, c.head_dim, c.ffn, c.vocab,

@@ -1,0 +1,126 @@
+"""GPU parity of the pi0-style policy step against the CPU oracle, through the C ABI.
+
+The prefix model (GeGLU, MQA, head dim 256, a K/V-only last layer, no
+vocabulary) prefills caller embeddings; the action expert denoises an action
+chunk with Euler steps, attending to the prefix model's cache and to its own
+chunk in both directions ("Running VLAs at Real-time Speed", sections 2 and
+4.1-4.2). The final action chunk is compared with the oracle's by cosine and
+max relative error, the bf16 tolerances.
+"""
+import numpy as np
+import pytest
+import torch
+
+import kv_cached_gqa_decoder_amd as vla
+import synth
+from oracle import decoder as D
+from oracle import pi0
+from tests.gpu_util import (check_argmax, check_logits, dev_from_storage, log, logits_of,
+                            metrics)
+
+pytestmark = pytest.mark.gpu
+
+TINY_VLM = dict(n_layers=3, hidden=256, n_heads=2, n_kv_heads=1, head_dim=256, ffn=512, vocab=0,
+                rope_theta=1e4, wdtype=vla.VLA_BF16, ffn_kind=vla.VLA_GEGLU, kv_only_last=1,
+                num_blocks=12, max_frames=4, max_chunk=64, seed=61)
+TINY_AE = dict(n_layers=3, hidden=128, n_heads=2, n_kv_heads=1, head_dim=256, ffn=256, vocab=0,
+               rope_theta=1e4, wdtype=vla.VLA_BF16, ffn_kind=vla.VLA_GEGLU, stream_base=0x8000,
+               num_blocks=0, max_frames=0, max_chunk=19, seed=61)
+
+
+def _ocfg(p, name, init_std):
+    wd = {vla.VLA_F32: "f32", vla.VLA_BF16: "bf16"}[p["wdtype"]]
+    return D.Config(name, p["n_layers"], p["hidden"], p["n_heads"], p["n_kv_heads"],
+                    p["head_dim"], p["ffn"], p["vocab"], rope_theta=p["rope_theta"], wdtype=wd,
+                    act=wd, num_blocks=max(p["num_blocks"], 1), max_frames=max(p["max_frames"], 1),
+                    seed=p["seed"], init_std=init_std,
+                    ffn_kind="geglu" if p.get("ffn_kind") == vla.VLA_GEGLU else "swiglu",
+                    kv_only_last=bool(p.get("kv_only_last", 0)),
+                    stream_base=p.get("stream_base", 0))
+
+
+def _check_actions(got, ref, what):
+    cos, rel = metrics(got.ravel(), ref.ravel())
+    log(f"  {what}: cos {cos:.6f} rel {rel:.3e}")
+    assert np.all(np.isfinite(got)), what
+    assert cos >= 0.9995 and rel <= 2e-2, f"{what}: cos {cos:.6f} rel {rel:.3e}"
+
+
+def _policy(vp, ap, init_std, chunks, n_actions, steps, seed_call=0, cache_f64=True):
+    """Prefill `chunks` (token counts) of embeddings on both sides, then denoise."""
+    ovlm = _ocfg(vp, "vlm", init_std)
+    oae = _ocfg(ap, "ae", init_std)
+    sess = D.Session(ovlm, D.Weights(ovlm, cache_f64=cache_f64))
+    m = vla.Model(vla.make_config(**vp, init_std=init_std))
+    for i, n in enumerate(chunks):
+        x32, xs = synth.embeddings(vp["seed"], i, n, vp["hidden"], "bf16")
+        fid = m.prefill_chunk(embeds=dev_from_storage(xs, "bf16"), n=n)
+        assert fid == sess.prefill_chunk(embeds=x32)[0]
+    e = vla.Expert(m, vla.make_config(**ap, init_std=init_std), n_actions)
+    x0 = synth.action_noise(vp["seed"], seed_call, n_actions, ap["hidden"])
+    x = torch.from_numpy(x0.copy()).cuda()
+    e.denoise(x, n_steps=steps)
+    torch.cuda.synchronize()
+    got = x.cpu().numpy().astype(np.float64)
+    ref = pi0.ActionExpert(oae, sess).denoise(x0, steps=steps)
+    return m, e, sess, got, ref
+
+
+def test_pi0_tiny_prefix_cache_and_denoise():
+    """Two prefix frames (40 + 24 tokens), a 19-token action chunk (a ragged second
+    block of its own), 4 Euler steps; the prefix model's stored K/V, including the
+    K/V-only last layer, match the oracle's."""
+    m, e, sess, got, ref = _policy(TINY_VLM, TINY_AE, 0.08, [40, 24], 19, 4)
+    _check_actions(got, ref, "tiny pi0 actions")
+    T = sess.resident_tokens()
+    for layer in range(TINY_VLM["n_layers"]):
+        k = torch.empty((T, 1, 256), dtype=torch.bfloat16, device="cuda")
+        v = torch.empty_like(k)
+        assert m.kv_gather(layer, k, v, T) == T
+        K, V = sess.gather(layer)
+        assert metrics(k.float().cpu().numpy().ravel(), K.ravel())[1] < 2e-2
+        assert metrics(v.float().cpu().numpy().ravel(), V.ravel())[1] < 2e-2
+    # the expert's blocks came from the prefix pool and go back on destroy
+    free = m.state()["free_blocks"]
+    e.close()
+    assert m.state()["free_blocks"] == free + 2
+    # a prefix model has no vocabulary: token input and logits are refused
+    with pytest.raises(vla.VlaError) as err:
+        m.prefill_chunk(tokens=np.array([1, 2], dtype=np.int32))
+    assert err.value.status == vla.VLA_E_INVALID
+    m.close()
+
+
+def test_geglu_head_dim_256_prefill_and_decode():
+    """GeGLU FFN and head dim 256 with a vocabulary: prefill, then greedy decodes (the
+    decode attention's key-split shape at d = 256). Weights N(0, 0.05^2): at 0.08 this
+    two-head model's logits amplify the bf16 rounding of its activations to about the
+    tolerance band on some steps."""
+    p = dict(TINY_VLM, vocab=800, kv_only_last=0, num_blocks=16, seed=62)
+    ocfg = _ocfg(p, "geglu", 0.05)
+    sess = D.Session(ocfg)
+    m = vla.Model(vla.make_config(**p, init_std=0.05))
+    ids = synth.token_ids(p["seed"], 0, 45, p["vocab"])
+    m.prefill_chunk(tokens=ids)
+    _, ref = sess.prefill_chunk(tokens=ids)
+    check_logits(logits_of(m), ref, "bf16", "geglu prefill")
+    tok = int(np.argmax(ref))
+    for i in range(20):
+        g = m.decode_step(tok)
+        nxt, ref = sess.decode_step(tok)
+        check_logits(logits_of(m), ref, "bf16", f"geglu decode {i}")
+        check_argmax(g, ref, "bf16", f"geglu decode {i}")
+        tok = nxt
+    m.close()
+
+
+def test_pi0_full_shape_policy_step():
+    """The workload's own shapes: Gemma-2B-shaped prefix (17 layers + K/V-only 18th)
+    over 2 x 256 image-token embeddings, the 300M expert on a 63-token chunk, 10
+    Euler steps."""
+    vp = vla.PRESETS["c4_pi0_vlm"]
+    ap = vla.PRESETS["c4_pi0_action_expert"]
+    m, e, sess, got, ref = _policy(vp, ap, 0.02, [512], 63, 10, cache_f64=False)
+    _check_actions(got, ref, "pi0 policy step actions")
+    e.close()
+    m.close()
