@@ -16,13 +16,15 @@ the wall time of a whole frame step. ``phases`` holds the decode-step latency,
 the frame-step time, the eviction leg (semantic eviction workload: 128 cached
 frames of 64 tokens, 32 score-and-evict cycles each followed by a 64-token
 prefill), the long-context leg (Llama-3-8B-shaped decoder with INT4 group-128
-weights: a 120,000-token cached prefix, a 512-token chunk, 32 decodes) and
-roofline fractions. ``roofline`` covers the dominant kernel of the frame step
+weights: a 120,000-token cached prefix, a 512-token chunk, 32 decodes), the
+pi0-style policy leg (Gemma-2B-shaped prefix model over 512 image tokens, then
+10 Euler steps of the 300M action expert on a 63-token chunk) and roofline
+fractions. ``roofline`` covers the dominant kernel of the frame step
 (the decode gate/up projection); ``cpu_baseline`` times the CPU oracle on a
 bounded sample of the same prefill.
 
 Usage: python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
-                       [--no-eviction] [--no-longctx]
+                       [--no-eviction] [--no-longctx] [--no-pi0]
 """
 from __future__ import annotations
 
@@ -177,6 +179,7 @@ def gpu_leg(args):
 
     ev_leg = eviction_leg(args) if not args.no_eviction else None
     lc_leg = longctx_leg(args) if not args.no_longctx else None
+    p0_leg = pi0_leg(args) if not args.no_pi0 else None
 
     fl = prefill_flops()
     dbytes = decode_bytes(CONTEXT + CHUNK + DECODES // 2)
@@ -237,6 +240,8 @@ def gpu_leg(args):
         res["phases"].update(ev_leg)
     if lc_leg:
         res["phases"].update(lc_leg)
+    if p0_leg:
+        res["phases"].update(p0_leg)
     return res
 
 
@@ -416,6 +421,85 @@ def longctx_leg(args):
 
 
 # ---------------------------------------------------------------------------
+# pi0-style policy step: Gemma-2B-shaped prefix model + 300M action expert, bf16
+P0_L, P0_H, P0_HQ, P0_D, P0_F = 18, 2048, 8, 256, 16384       # prefix (17 + K/V-only 18th)
+AE_H, AE_F, AE_N, AE_STEPS = 1024, 4096, 63, 10
+P0_PREFIX = 512                                                  # 2 views x 256 image tokens
+
+
+def pi0_prefix_flops():
+    qkv = (P0_HQ + 2) * P0_D * P0_H
+    full = qkv + P0_H * P0_HQ * P0_D + 3 * P0_F * P0_H
+    lin = 2 * P0_PREFIX * (full * (P0_L - 1) + 2 * P0_D * P0_H)     # 18th layer: K/V only
+    attn = (P0_L - 1) * P0_HQ * 2 * 2 * P0_D * (P0_PREFIX * (P0_PREFIX + 1) // 2)
+    return lin + attn
+
+
+def pi0_expert_bytes():
+    per = (P0_HQ + 2) * P0_D * AE_H + AE_H * P0_HQ * P0_D + 3 * AE_F * AE_H
+    return 2 * per * P0_L
+
+
+def pi0_leg(args):
+    """Prefill 2 x 256 image-token embeddings (N(0,1)) into the prefix model, then
+    10 Euler steps of the action expert on a 63-token N(0,1) chunk."""
+    import numpy as np
+    import torch
+
+    import kv_cached_gqa_decoder_amd as vla
+    import synth
+
+    stream = torch.cuda.current_stream()
+    sh = stream.cuda_stream
+    vp = vla.PRESETS["c4_pi0_vlm"]
+    ap = vla.PRESETS["c4_pi0_action_expert"]
+    log("[bench] pi0 leg: creating the prefix model and the action expert")
+    m = vla.Model(vla.make_config(**vp))
+    e = vla.Expert(m, vla.make_config(**ap), AE_N)
+    _, xs = synth.embeddings(vp["seed"], 0, P0_PREFIX, P0_H, "bf16")
+    img = torch.from_numpy(np.ascontiguousarray(xs).view(np.int16)).view(torch.bfloat16).cuda()
+    noise = torch.from_numpy(synth.action_noise(vp["seed"], 0, AE_N, AE_H)).cuda()
+    x = torch.empty_like(noise)
+
+    def step(ev=None):
+        m.kv_rollback(-1)
+        x.copy_(noise)
+        if ev:
+            ev[0].record(stream)
+        m.prefill_chunk(embeds=img, n=P0_PREFIX, stream=sh)
+        if ev:
+            ev[1].record(stream)
+        e.denoise(x, n_steps=AE_STEPS, stream=sh)
+        if ev:
+            ev[2].record(stream)
+
+    for _ in range(3):
+        step()
+    torch.cuda.synchronize()
+    reps = max(5, args.steps)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(reps)]
+    for i in range(reps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    e.close()
+    m.close()
+    pre = statistics.median(ev[0].elapsed_time(ev[1]) for ev in evs)
+    ae = statistics.median(ev[1].elapsed_time(ev[2]) for ev in evs)
+    fl = pi0_prefix_flops()
+    ab = pi0_expert_bytes()
+    it = ae / AE_STEPS
+    return {
+        "pi0_step_ms": round(pre + ae, 3),
+        "pi0_prefix_prefill_ms": round(pre, 3),
+        "pi0_prefix_prefill_mfma_frac": round(fl / (pre * 1e-3) / (PEAK_BF16_TFLOPS * 1e12), 4),
+        "pi0_prefix_prefill_flop": fl,
+        "pi0_expert_iteration_ms": round(it, 4),
+        "pi0_expert_iteration_hbm_frac": round(ab / (it * 1e-3) / (PEAK_HBM_GBS * 1e9), 4),
+        "pi0_expert_weight_bytes": ab,
+    }
+
+
+# ---------------------------------------------------------------------------
 def cpu_baseline(layers_sample: int):
     """The oracle (fp64 numpy) on a bounded sample of the prefill: the same 1024-token
     context and 256-token chunk, through the first `layers_sample` of the 28 layers, then
@@ -443,7 +527,7 @@ def cpu_baseline(layers_sample: int):
     x32, _ = synth.embeddings(cfg.seed, 0, CHUNK, H, "bf16")
     ctx_fid = sess.frames()[-1].frame_id
     runs = []
-    for _ in range(3):
+    for _ in range(5):
         sess.rollback(ctx_fid)
         t0 = time.perf_counter()
         sess.prefill_chunk(embeds=x32)
@@ -461,7 +545,7 @@ def cpu_baseline(layers_sample: int):
         "cores": threads,
         "kind": "oracle",
         "sample": f"256-token chunk prefill over a 1024-token cached context through "
-                  f"{layers_sample} of {L} layers plus the output head (median of 3: "
+                  f"{layers_sample} of {L} layers plus the output head (median of 5: "
                   f"{t_all:.2f} s); scaled per layer to {L} layers: est. {est:.2f} s",
     }
 
@@ -474,7 +558,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-eviction", action="store_true")
     ap.add_argument("--no-longctx", action="store_true")
-    ap.add_argument("--cpu-layers", type=int, default=2)
+    ap.add_argument("--no-pi0", action="store_true")
+    ap.add_argument("--cpu-layers", type=int, default=28)
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the decoder's hot path here runs on a single "

@@ -180,7 +180,8 @@ vla_status vla_kv_append_raw(vla_model* m, const void* k, const void* v, int32_t
 /* Drop every frame and decode tail created after frame keep_frame_id, newest
  * first, returning their blocks in reverse allocation order (this restores the
  * free-list exactly when nothing was evicted since), and reset the position
- * and frame-id counters to their values right after that frame. Host-only
+ * and frame-id counters to their values right after that frame. keep_frame_id
+ * -1 drops every frame and tail (position 0, frame id 0 next). Host-only
  * bookkeeping; enqueues no work. Errors: VLA_E_INVALID (no such frame). */
 vla_status vla_kv_rollback(vla_model* m, int32_t keep_frame_id);
 

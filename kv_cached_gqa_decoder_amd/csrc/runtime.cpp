@@ -894,11 +894,14 @@ vla_status vla_kv_append_raw(vla_model* m, const void* k, const void* v, int32_t
 vla_status vla_kv_rollback(vla_model* m, int32_t keep_frame_id) {
   return guarded([&] {
     if (!m) raise(VLA_E_INVALID, "null model");
+    // keep_frame_id -1: drop everything (back to the empty state)
     size_t keep = m->segs.size();
     for (size_t i = 0; i < m->segs.size(); ++i)
       if (m->segs[i].frame && m->segs[i].frame_id == keep_frame_id) keep = i;
-    if (keep == m->segs.size()) raise(VLA_E_INVALID, "no such resident frame");
-    while (m->segs.size() > keep + 1) {
+    if (keep == m->segs.size() && keep_frame_id != -1)
+      raise(VLA_E_INVALID, "no such resident frame");
+    const size_t n_keep = keep_frame_id == -1 ? 0 : keep + 1;
+    while (m->segs.size() > n_keep) {
       Segment s = m->segs.back();
       std::vector<int> rb(s.blocks.rbegin(), s.blocks.rend());
       if (!m->pool.release(rb.data(), (int)rb.size()))
@@ -906,8 +909,12 @@ vla_status vla_kv_rollback(vla_model* m, int32_t keep_frame_id) {
       if (s.frame) m->free_slots.push_back(s.slot);
       m->segs.pop_back();
     }
-    const Segment& k = m->segs[keep];
-    m->next_pos = k.start_pos + k.ntok;
+    if (n_keep == 0) {
+      m->next_pos = 0;
+    } else {
+      const Segment& k = m->segs[keep];
+      m->next_pos = k.start_pos + k.ntok;
+    }
     m->next_frame_id = keep_frame_id + 1;
     m->meta_dirty = true;
   });
