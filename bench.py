@@ -560,11 +560,28 @@ def main():
     ap.add_argument("--no-longctx", action="store_true")
     ap.add_argument("--no-pi0", action="store_true")
     ap.add_argument("--cpu-layers", type=int, default=28)
+    ap.add_argument("--only", choices=["eviction", "longctx", "pi0"],
+                    help="run one leg alone and print its numbers (for kernel traces)")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="first copy 256 MiB on the device three times (a plain copy of known "
+                         "size, the reference for scaling HBM counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the decoder's hot path here runs on a single "
               "MI355X (no multi-GPU path is built); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
+    if args.copy_probe:
+        import torch
+        a = torch.ones(64 << 20, dtype=torch.float32, device="cuda")
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
+    if args.only:
+        leg = {"eviction": eviction_leg, "longctx": longctx_leg, "pi0": pi0_leg}[args.only]
+        print(json.dumps(leg(args)), flush=True)
+        return
     res = gpu_leg(args)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(args.cpu_layers)
