@@ -9,8 +9,8 @@
 //
 // bf16 path (matrix cores). Query rows are (token, q head of the group) pairs,
 // so the g heads sharing a KV head consume each K/V block together and a block
-// is read once per KV-head group rather than once per query head. One 16-row
-// tile is one wavefront's set of query columns. Per 32-key step (two blocks):
+// is read once per KV-head group rather than once per query head. A 16-row
+// tile is a set of MFMA query columns. Per 32-key step (two blocks):
 //   S^T = K Q^T        v_mfma_f32_16x16x32_bf16, A = 16 keys x 32 dims (K rows),
 //                      B = Q^T held in registers for the whole loop; the
 //                      accumulator gives each lane 4 keys of one query.
@@ -19,12 +19,17 @@
 //   O^T += V^T P^T     A = V^T (the pool stores V transposed inside a block, so
 //                      4 consecutive keys of one dimension are contiguous),
 //                      B = P^T, which is exactly the lane's own probabilities.
-// Two workgroup shapes (4 wavefronts each):
-//   key split (decode, <= 16 query rows): the 4 wavefronts share one row tile
-//     and take interleaved block pairs straight from memory; their partial
-//     (m, l, o) are merged through LDS.
-//   row tiles (prefill): each wavefront owns 16 rows; the workgroup stages each
-//     block pair in LDS once (double buffered) for all 64 rows.
+// Two kernels:
+//   decode (<= 16 query rows): 4 wavefronts share one row tile and take
+//     interleaved block pairs straight from memory (one pair prefetched); their
+//     partial (m, l, o) are merged through LDS.
+//   rows (prefill): 8 wavefronts, each owning 2 row tiles (1 at d = 256), so a
+//     workgroup covers 256 (128) rows; every block pair goes through a 3-stage
+//     LDS ring filled by direct-to-LDS DMA (16 bytes per lane; K rows XOR-
+//     swizzled in 16-byte chunks against bank conflicts) and is read by all
+//     rows of the workgroup. Workgroups are numbered so that all row tiles of
+//     one (KV head, key split) run on one XCD and stream the same blocks
+//     through its L2.
 // The resident blocks are split over workgroups (split-K). Each workgroup
 // writes its partial (m, l, o); a second kernel merges the splits in split
 // order (deterministic). Merging inside the first kernel would need an
@@ -37,9 +42,9 @@
 
 namespace vla {
 
-constexpr int kAttnWaves = 4;
-constexpr int kMaxSplitsKey = 128;  // key-split shape: 16 rows per workgroup
-constexpr int kMaxSplitsRow = 32;   // row-tile shape: 64 rows per workgroup
+constexpr int kAttnWaves = 4;       // decode kernel
+constexpr int kMaxSplitsKey = 128;  // decode: 16 rows per workgroup
+constexpr int kMaxSplitsRow = 32;   // rows kernel
 constexpr float kLog2e = 1.4426950408889634f;
 
 __device__ __forceinline__ bool key_visible(const AttnArgs& a, int b, int slot, int ntok, int tq) {
@@ -49,8 +54,15 @@ __device__ __forceinline__ bool key_visible(const AttnArgs& a, int b, int slot, 
   return ck <= tq;
 }
 
-__device__ __forceinline__ int block_ntok(const AttnArgs& a, int b) {
-  return b == a.nlb - 1 ? a.last_ntok : a.blk_ntok[b];
+// Table reads with a wave-uniform index through the constant address space, so
+// they become scalar loads: the tables are not written while a kernel runs, and
+// vector loads would count in vmcnt and break the DMA ring's wait depths.
+typedef const __attribute__((address_space(4))) int* const_int_p;
+__device__ __forceinline__ int uniform_ld(const int* p, int i) {
+  return ((const_int_p)(const void*)p)[i];
+}
+__device__ __forceinline__ int block_ntok_s(const AttnArgs& a, int b) {
+  return b == a.nlb - 1 ? a.last_ntok : uniform_ld(a.blk_ntok, b);
 }
 
 // Operands of one 32-key step held by a lane: K rows (A of S^T = K Q^T) for the
@@ -76,7 +88,59 @@ __device__ __forceinline__ void state_init(SoftmaxState<D>& st) {
   for (int i = 0; i < D / 16; ++i) st.o[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 }
 
-// one online-softmax step over blocks b (and b+1 when has1) for query column (tq)
+// Online-softmax update of one query column (tq) for the scores of blocks b and
+// b+1 (s0, s1: keys 4jq..4jq+3 of each; has1: block b+1 exists). `masked`:
+// some key of the pair may be invisible (ragged block, causal region);
+// otherwise every key is visible. Returns the bf16 probabilities as the MFMA B
+// operand (the running sum uses the rounded values) and the rescale factor of
+// the running output.
+__device__ __forceinline__ bf16x8_t softmax_pair(const AttnArgs& a, float& m, float& l,
+                                                 const f32x4_t& s0, const f32x4_t& s1, int b,
+                                                 bool has1, bool masked, int tq, int jq,
+                                                 float sl2, float& alpha) {
+  float p0[4], p1[4];
+  float mx = -INFINITY;
+  if (masked) {
+    const int nt0 = block_ntok_s(a, b);
+    const int nt1 = has1 ? block_ntok_s(a, b + 1) : 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int ks = 4 * jq + e;
+      p0[e] = key_visible(a, b, ks, nt0, tq) ? s0[e] * sl2 : -INFINITY;
+      p1[e] = (has1 && key_visible(a, b + 1, ks, nt1, tq)) ? s1[e] * sl2 : -INFINITY;
+      mx = fmaxf(mx, fmaxf(p0[e], p1[e]));
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      p0[e] = s0[e] * sl2;
+      p1[e] = s1[e] * sl2;
+      mx = fmaxf(mx, fmaxf(p0[e], p1[e]));
+    }
+  }
+  mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+  mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+  const float m_new = fmaxf(m, mx);
+  const float m_use = m_new == -INFINITY ? 0.f : m_new;
+  alpha = m == -INFINITY ? 0.f : exp2f(m - m_use);
+  u32x4_t pw;
+#pragma unroll
+  for (int e = 0; e < 2; ++e) {
+    pw[e] = pack_bf16x2(exp2f(p0[2 * e] - m_use), exp2f(p0[2 * e + 1] - m_use));
+    pw[2 + e] = pack_bf16x2(exp2f(p1[2 * e] - m_use), exp2f(p1[2 * e + 1] - m_use));
+  }
+  float sum = 0.f;
+#pragma unroll
+  for (int e = 0; e < 4; ++e)
+    sum += __uint_as_float(pw[e] << 16) + __uint_as_float(pw[e] & 0xffff0000u);
+  sum += __shfl_xor(sum, 16, 64);
+  sum += __shfl_xor(sum, 32, 64);
+  l = l * alpha + sum;
+  m = m_new;
+  return __builtin_bit_cast(bf16x8_t, pw);
+}
+
+// one online-softmax step of the decode kernel over blocks b (and b+1 when has1)
 template <int D>
 __device__ __forceinline__ void attn_step(const AttnArgs& a, SoftmaxState<D>& st,
                                           const bf16x8_t* qf, const PairFrags<D>& f, int b,
@@ -87,40 +151,9 @@ __device__ __forceinline__ void attn_step(const AttnArgs& a, SoftmaxState<D>& st
     s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f.k0[ds], qf[ds], s0, 0, 0, 0);
     s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f.k1[ds], qf[ds], s1, 0, 0, 0);
   }
-  const int nt0 = block_ntok(a, b);
-  const int nt1 = has1 ? block_ntok(a, b + 1) : 0;
-  float p0[4], p1[4];
-  float mx = -INFINITY;
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const int ks = 4 * jq + e;
-    p0[e] = key_visible(a, b, ks, nt0, tq) ? s0[e] * sl2 : -INFINITY;
-    p1[e] = (has1 && key_visible(a, b + 1, ks, nt1, tq)) ? s1[e] * sl2 : -INFINITY;
-    mx = fmaxf(mx, fmaxf(p0[e], p1[e]));
-  }
-  mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-  mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-  const float m_new = fmaxf(st.m, mx);
-  const float m_use = m_new == -INFINITY ? 0.f : m_new;
-  const float alpha = st.m == -INFINITY ? 0.f : exp2f(st.m - m_use);
-  // probabilities rounded to bf16 once; the sum uses the rounded values
-  u32x4_t pw;
-  float sum = 0.f;
-#pragma unroll
-  for (int e = 0; e < 2; ++e) {
-    const bf16_t a0 = f32_to_bf16(exp2f(p0[2 * e] - m_use));
-    const bf16_t a1 = f32_to_bf16(exp2f(p0[2 * e + 1] - m_use));
-    const bf16_t b0 = f32_to_bf16(exp2f(p1[2 * e] - m_use));
-    const bf16_t b1 = f32_to_bf16(exp2f(p1[2 * e + 1] - m_use));
-    sum += bf16_to_f32(a0) + bf16_to_f32(a1) + bf16_to_f32(b0) + bf16_to_f32(b1);
-    pw[e] = (uint32_t)a0 | ((uint32_t)a1 << 16);
-    pw[2 + e] = (uint32_t)b0 | ((uint32_t)b1 << 16);
-  }
-  sum += __shfl_xor(sum, 16, 64);
-  sum += __shfl_xor(sum, 32, 64);
-  st.l = st.l * alpha + sum;
-  st.m = m_new;
-  const bf16x8_t pf = __builtin_bit_cast(bf16x8_t, pw);
+  float alpha;
+  const bf16x8_t pf = softmax_pair(a, st.m, st.l, s0, s1, b, has1, /*masked=*/true, tq, jq, sl2,
+                                   alpha);
 #pragma unroll
   for (int dt = 0; dt < D / 16; ++dt) {
     st.o[dt] *= alpha;
@@ -154,103 +187,234 @@ __device__ __forceinline__ void load_pair_global(const AttnArgs& a, PairFrags<D>
   }
 }
 
-// LDS image of one block pair (row-tile shape). K rows: [32 keys][D + 8];
-// V^T rows: [D][40], where dim i holds at 8jq + 4blk + e the key 4jq + e of block blk.
+// ---------------------------------------------------------------------------
+// rows kernel (prefill)
+// ---------------------------------------------------------------------------
 template <int D>
-struct PairLds {
-  static constexpr int KP = D + 8;
-  static constexpr int VP = 40;
-  static constexpr int KELEMS = 32 * KP;
-  static constexpr int VELEMS = D * VP;
-  static constexpr int ELEMS = KELEMS + VELEMS;
-  static constexpr int KCH = 32 * D / 8;   // 16-byte chunks of K per pair
-  static constexpr int VCH = 2 * D * 2;    // 16-byte chunks of V per pair
-  static constexpr int CH = (KCH + VCH) / (kAttnWaves * 64);
+struct RowCfg {
+  static constexpr int QT = D <= 128 ? 2 : 1;        // 16-row tiles per wavefront
+  static constexpr int WAVES = 8;
+  static constexpr int ROWS = WAVES * QT * 16;       // rows per workgroup
+  static constexpr int NS = 3;                       // ring stages (block pairs)
+  static constexpr int BLK = 16 * D * 2;             // one block of K (or V) of one KV head
+  static constexpr int STAGE = 4 * BLK;              // K0 K1 V0 V1
+  static constexpr int LDS = NS * STAGE;
+  static constexpr int CPR = D / 8;                  // 16-byte chunks per K row
+  static constexpr int LOADS = STAGE / 1024 / WAVES; // 1 KB DMA instructions per wavefront per stage
+  static_assert(LOADS >= 1 && STAGE % (1024 * WAVES) == 0, "stage split");
 };
 
+// K rows in LDS: 16-byte chunk c of row r sits at chunk position c ^ (r & 15)
+// (within the row: D >= 128 has >= 16 chunks per row; D = 64 uses r & 7)
 template <int D>
-__device__ __forceinline__ void stage_load(const AttnArgs& a, u32x4_t* r, int b, bool has1,
-                                           int kvh) {
-  using P = PairLds<D>;
-  const bf16_t* kp = (const bf16_t*)a.kpool;
-  const bf16_t* vp = (const bf16_t*)a.vpool;
-  const int pb0 = a.blk_table[b];
-  const int pb1 = has1 ? a.blk_table[b + 1] : pb0;
+__device__ __forceinline__ int kswz(int r) {
+  return D >= 128 ? (r & 15) : (r & 7);
+}
+
+template <int D>
+__global__ __launch_bounds__(512) void attn_rows_kernel(AttnArgs a, int rgroups, int units) {
+  using C = RowCfg<D>;
+  constexpr int QT = C::QT, NS = C::NS, ROWS = C::ROWS;
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[C::LDS];
+
+  // XCD-aware numbering: workgroup i runs on XCD i % 8; unit u = (kvh, split)
+  // lives on XCD u % 8 with all of its row tiles
+  const int xcd = blockIdx.x % 8, slot = blockIdx.x / 8;
+  const int u = (slot / rgroups) * 8 + xcd;
+  const int rg = slot % rgroups;
+  if (u >= units) return;
+  const int splits = a.splits;
+  const int kvh = u / splits, split = u % splits;
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int jq = lane >> 4, cq = lane & 15;
+  const int grp = a.hq / a.g.hkv;
+  const int R = a.n * grp;
+  const float sl2 = a.scale * kLog2e;
+
+  // this wavefront's query tiles: rows rg*ROWS + wave*QT*16 + qt*16 + cq
+  bf16x8_t qf[QT][D / 32];
+  int tq[QT];
 #pragma unroll
-  for (int i = 0; i < P::CH; ++i) {
-    const int c = threadIdx.x + i * kAttnWaves * 64;
-    if (c < P::KCH) {
-      const int blk = c / (16 * D / 8);
-      const int row = (c / (D / 8)) % 16;
-      const int col8 = c % (D / 8);
-      r[i] = *(const u32x4_t*)(kp + a.g.kidx(a.layer, blk ? pb1 : pb0, kvh, row, col8 * 8));
+  for (int qt = 0; qt < QT; ++qt) {
+    const int r = rg * ROWS + (wave * QT + qt) * 16 + cq;
+    const bool ok = r < R;
+    tq[qt] = ok ? r / grp : 0;
+    const int h = kvh * grp + (ok ? r % grp : 0);
+    const bf16_t* qrow = (const bf16_t*)a.q + ((size_t)tq[qt] * a.hq + h) * D;
+#pragma unroll
+    for (int ds = 0; ds < D / 32; ++ds) {
+      const u32x4_t v = ok ? *(const u32x4_t*)(qrow + ds * 32 + 8 * jq) : u32x4_t{0, 0, 0, 0};
+      qf[qt][ds] = __builtin_bit_cast(bf16x8_t, v);
+    }
+  }
+
+  // blocks of this split; past the workgroup's last causal key nothing is visible
+  const int bps = (a.nlb + splits - 1) / splits;
+  const int b_begin = split * bps;
+  int b_end = min(a.nlb, b_begin + bps);
+  if (a.causal) {
+    const int rlast = min(R, rg * ROWS + ROWS) - 1;
+    b_end = min(b_end, a.cb0 + (rlast / grp + a.cslot0) / a.g.bt + 1);
+  }
+  const int np = b_end > b_begin ? (b_end - b_begin + 1) / 2 : 0;
+
+  float m[QT], l[QT];
+  f32x4_t o[QT][D / 16];
+#pragma unroll
+  for (int qt = 0; qt < QT; ++qt) {
+    m[qt] = -INFINITY;
+    l[qt] = 0.f;
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt) o[qt][dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  }
+
+  if (np > 0) {
+    const unsigned char* kp = (const unsigned char*)a.kpool;
+    const unsigned char* vp = (const unsigned char*)a.vpool;
+    // stage p -> ring slot p % NS; past the last pair the DMA re-loads it (every
+    // step then issues the same loads and every wait has one depth)
+    auto issue = [&](int p) {
+      const int pd = p < np ? p : np - 1;
+      const int b = b_begin + 2 * pd;
+      const int pb0 = uniform_ld(a.blk_table, b);
+      const int pb1 = uniform_ld(a.blk_table, b + 1 < b_end ? b + 1 : b);
+      unsigned char* st = smem + (p % NS) * C::STAGE;
+#pragma unroll
+      for (int j = 0; j < C::LOADS; ++j) {
+        const int q = wave * C::LOADS + j;            // 1 KB piece of the stage
+        const int which = q / (C::BLK / 1024);        // 0 K0, 1 K1, 2 V0, 3 V1
+        const int part = q % (C::BLK / 1024);
+        const int pb = (which & 1) ? pb1 : pb0;
+        const int pos = part * 64 + lane;             // 16-byte chunk inside the block
+        size_t src;
+        if (which < 2) {
+          const int r = pos / C::CPR, pc = pos % C::CPR;
+          src = (size_t)a.g.kidx(a.layer, pb, kvh, 0, 0) * 2 + (size_t)r * (D * 2) +
+                ((pc ^ kswz<D>(r)) << 4);
+        } else {
+          src = (size_t)a.g.vidx(a.layer, pb, kvh, 0, 0) * 2 + (size_t)pos * 16;
+        }
+        __builtin_amdgcn_global_load_lds(
+            (const void*)((which < 2 ? kp : vp) + src),
+            (__attribute__((address_space(3))) void*)(st + which * C::BLK + part * 1024), 16, 0,
+            0);
+      }
+    };
+#pragma unroll
+    for (int p0 = 0; p0 < NS - 1; ++p0) issue(p0);
+
+    for (int p = 0; p < np; ++p) {
+      wait_vmcnt_steps<C::LOADS>(NS - 2);
+      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      issue(p + NS - 1);
+      const unsigned char* st = smem + (p % NS) * C::STAGE;
+      const int b = b_begin + 2 * p;
+      const bool has1 = b + 1 < b_end;
+      // every key of the pair visible: both blocks full, none in the causal region
+      bool masked = !has1 || block_ntok_s(a, b) != a.g.bt || block_ntok_s(a, b + 1) != a.g.bt;
+      if (a.causal) masked = masked || b + 1 >= a.cb0;
+
+      f32x4_t s0[QT], s1[QT];
+#pragma unroll
+      for (int qt = 0; qt < QT; ++qt) {
+        s0[qt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        s1[qt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      }
+#pragma unroll
+      for (int ds = 0; ds < D / 32; ++ds) {
+        const int c = ds * 4 + jq;
+        const int off = cq * (D * 2) + ((c ^ kswz<D>(cq)) << 4);
+        const bf16x8_t k0 = *(const bf16x8_t*)(st + off);
+        const bf16x8_t k1 = *(const bf16x8_t*)(st + C::BLK + off);
+#pragma unroll
+        for (int qt = 0; qt < QT; ++qt) {
+          s0[qt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, qf[qt][ds], s0[qt], 0, 0, 0);
+          s1[qt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, qf[qt][ds], s1[qt], 0, 0, 0);
+        }
+      }
+      bf16x8_t pf[QT];
+      float alpha[QT];
+#pragma unroll
+      for (int qt = 0; qt < QT; ++qt)
+        pf[qt] = softmax_pair(a, m[qt], l[qt], s0[qt], s1[qt], b, has1, masked, tq[qt], jq, sl2,
+                              alpha[qt]);
+      // the running outputs only change scale when some column's maximum rose
+      bool rescale = false;
+#pragma unroll
+      for (int qt = 0; qt < QT; ++qt) rescale = rescale || alpha[qt] != 1.f;
+      if (__any(rescale)) {
+#pragma unroll
+        for (int qt = 0; qt < QT; ++qt)
+#pragma unroll
+          for (int dt = 0; dt < D / 16; ++dt) o[qt][dt] *= alpha[qt];
+      }
+#pragma unroll
+      for (int dt = 0; dt < D / 16; ++dt) {
+        // V^T rows: dim dt*16 + cq, keys 4jq..4jq+3 of block 0 then of block 1
+        const int voff = (dt * 16 + cq) * 32 + jq * 8;
+        const u32x2_t lo = *(const u32x2_t*)(st + 2 * C::BLK + voff);
+        const u32x2_t hi = *(const u32x2_t*)(st + 3 * C::BLK + voff);
+        const bf16x8_t vf = __builtin_bit_cast(bf16x8_t, u32x4_t{lo[0], lo[1], hi[0], hi[1]});
+#pragma unroll
+        for (int qt = 0; qt < QT; ++qt)
+          o[qt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf[qt], o[qt][dt], 0, 0, 0);
+      }
+    }
+  }
+
+  // results: the output rows directly, or this split's partial (m, l, o)
+  const int tile = kvh * rgroups + rg;
+  const size_t unit = (size_t)tile * splits + split;
+#pragma unroll
+  for (int qt = 0; qt < QT; ++qt) {
+    const int c = (wave * QT + qt) * 16 + cq;  // row inside the workgroup
+    const int r = rg * ROWS + c;
+    if (splits == 1) {
+      if (r < R) {
+        const float inv = l[qt] > 0.f ? 1.f / l[qt] : 0.f;
+        bf16_t* orow = (bf16_t*)a.out + ((size_t)(r / grp) * a.hq + kvh * grp + r % grp) * D;
+#pragma unroll
+        for (int dt = 0; dt < D / 16; ++dt) {
+          u32x2_t w;
+          w[0] = pack_bf16x2(o[qt][dt][0] * inv, o[qt][dt][1] * inv);
+          w[1] = pack_bf16x2(o[qt][dt][2] * inv, o[qt][dt][3] * inv);
+          *(u32x2_t*)(orow + dt * 16 + 4 * jq) = w;
+        }
+      }
     } else {
-      const int cv = c - P::KCH;
-      const int blk = cv / (2 * D);
-      const int dim = (cv % (2 * D)) / 2;
-      const int h = cv % 2;
-      r[i] = (blk && !has1) ? u32x4_t{0, 0, 0, 0}
-                            : *(const u32x4_t*)(vp + a.g.vidx(a.layer, blk ? pb1 : pb0, kvh,
-                                                               8 * h, dim));
+      float* po = a.part_o + (unit * ROWS + c) * D;
+#pragma unroll
+      for (int dt = 0; dt < D / 16; ++dt) *(f32x4_t*)(po + dt * 16 + 4 * jq) = o[qt][dt];
+      if (jq == 0) {
+        a.part_ml[unit * 2 * ROWS + c] = m[qt];
+        a.part_ml[unit * 2 * ROWS + ROWS + c] = l[qt];
+      }
     }
   }
 }
 
-template <int D>
-__device__ __forceinline__ void stage_store(bf16_t* lds, const u32x4_t* r) {
-  using P = PairLds<D>;
-  bf16_t* Ks = lds;
-  bf16_t* Vs = lds + P::KELEMS;
-#pragma unroll
-  for (int i = 0; i < P::CH; ++i) {
-    const int c = threadIdx.x + i * kAttnWaves * 64;
-    if (c < P::KCH) {
-      const int blk = c / (16 * D / 8);
-      const int row = (c / (D / 8)) % 16;
-      const int col8 = c % (D / 8);
-      *(u32x4_t*)(Ks + (blk * 16 + row) * P::KP + col8 * 8) = r[i];
-    } else {
-      const int cv = c - P::KCH;
-      const int blk = cv / (2 * D);
-      const int dim = (cv % (2 * D)) / 2;
-      const int h = cv % 2;
-      bf16_t* row = Vs + dim * P::VP + blk * 4;
-      *(u32x2_t*)(row + (2 * h) * 8) = u32x2_t{r[i][0], r[i][1]};
-      *(u32x2_t*)(row + (2 * h + 1) * 8) = u32x2_t{r[i][2], r[i][3]};
-    }
-  }
-}
-
-template <int D>
-__device__ __forceinline__ void load_pair_lds(const bf16_t* lds, PairFrags<D>& f, int cq, int jq) {
-  using P = PairLds<D>;
-  const bf16_t* Ks = lds;
-  const bf16_t* Vs = lds + P::KELEMS;
-#pragma unroll
-  for (int ds = 0; ds < D / 32; ++ds) {
-    f.k0[ds] = *(const bf16x8_t*)(Ks + cq * P::KP + ds * 32 + 8 * jq);
-    f.k1[ds] = *(const bf16x8_t*)(Ks + (16 + cq) * P::KP + ds * 32 + 8 * jq);
-  }
-#pragma unroll
-  for (int dt = 0; dt < D / 16; ++dt)
-    f.v[dt] = *(const bf16x8_t*)(Vs + (dt * 16 + cq) * P::VP + 8 * jq);
-}
-
+// ---------------------------------------------------------------------------
+// decode kernel (<= 16 query rows)
+// ---------------------------------------------------------------------------
 template <int D, bool KEYSPLIT>
-struct AttnShape {
-  static constexpr int ROWS = KEYSPLIT ? 16 : 16 * kAttnWaves;
-  // LDS: key split -> per-wave partials (4 x 16 x D fp32 + m, l); row tiles -> 2 pair images
-  static constexpr int LDS_BYTES =
-      KEYSPLIT ? kAttnWaves * 16 * (D + 2) * 4 : 2 * PairLds<D>::ELEMS * 2;
+struct AttnShape;
+template <int D>
+struct AttnShape<D, true> {
+  static constexpr int ROWS = 16;
+};
+template <int D>
+struct AttnShape<D, false> {
+  static constexpr int ROWS = RowCfg<D>::ROWS;
 };
 
-// partial layout: part_o[unit][ROWS][D], part_ml[unit][2][ROWS] with
+// partial layout (both kernels): part_o[unit][ROWS][D], part_ml[unit][2][ROWS] with
 // unit = (kvh * rgroups + rg) * splits + split
-template <int D, bool KEYSPLIT>
-__global__ __launch_bounds__(256) void attn_bf16_kernel(AttnArgs a, int rgroups) {
-  using S = AttnShape<D, KEYSPLIT>;
-  constexpr int ROWS = S::ROWS;
-  __shared__ __attribute__((aligned(16))) unsigned char smem[S::LDS_BYTES];
+template <int D>
+__global__ __launch_bounds__(256) void attn_decode_kernel(AttnArgs a, int rgroups) {
+  constexpr int ROWS = 16;
+  // LDS: the 4 wavefronts' partial (o, m, l) for the merge
+  __shared__ __attribute__((aligned(16))) float smem[kAttnWaves * 16 * (D + 2)];
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int split = blockIdx.x, rg = blockIdx.y, kvh = blockIdx.z;
@@ -260,8 +424,7 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(AttnArgs a, int rgroups)
   const int jq = lane >> 4, cq = lane & 15;
   const float sl2 = a.scale * kLog2e;
 
-  const int wrow0 = rg * ROWS + (KEYSPLIT ? 0 : wave * 16);
-  const int r = wrow0 + cq;
+  const int r = rg * ROWS + cq;
   const bool qvalid = r < R;
   const int tq = qvalid ? r / grp : 0;
   const int hq = kvh * grp + (qvalid ? r % grp : 0);
@@ -281,158 +444,118 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(AttnArgs a, int rgroups)
   int b_end = min(a.nlb, b_begin + bps);
   if (a.causal) {
     const int rlast = min(R, rg * ROWS + ROWS) - 1;
-    const int tmax = rlast / grp;
-    b_end = min(b_end, a.cb0 + (tmax + a.cslot0) / a.g.bt + 1);
+    b_end = min(b_end, a.cb0 + (rlast / grp + a.cslot0) / a.g.bt + 1);
   }
 
   SoftmaxState<D> st;
   state_init(st);
-  if constexpr (KEYSPLIT) {
-    PairFrags<D> cur, nxt;
-    int b = b_begin + 2 * wave;
-    if (b < b_end) load_pair_global(a, cur, b, b + 1 < b_end, kvh, cq, jq);
-    for (; b < b_end; b += 2 * kAttnWaves) {
-      const int bn = b + 2 * kAttnWaves;
-      if (bn < b_end) load_pair_global(a, nxt, bn, bn + 1 < b_end, kvh, cq, jq);
-      attn_step(a, st, qf, cur, b, b + 1 < b_end, tq, jq, sl2);
-      cur = nxt;
-    }
-    // merge the 4 wavefronts' states through LDS
-    float* Lo = (float*)smem;                       // [wave][16][D]
-    float* Lml = Lo + kAttnWaves * 16 * D;           // [wave][2][16]
+  PairFrags<D> cur, nxt;
+  int b = b_begin + 2 * wave;
+  if (b < b_end) load_pair_global(a, cur, b, b + 1 < b_end, kvh, cq, jq);
+  for (; b < b_end; b += 2 * kAttnWaves) {
+    const int bn = b + 2 * kAttnWaves;
+    if (bn < b_end) load_pair_global(a, nxt, bn, bn + 1 < b_end, kvh, cq, jq);
+    attn_step(a, st, qf, cur, b, b + 1 < b_end, tq, jq, sl2);
+    cur = nxt;
+  }
+  // merge the 4 wavefronts' states through LDS
+  float* Lo = smem;                          // [wave][16][D]
+  float* Lml = Lo + kAttnWaves * 16 * D;     // [wave][2][16]
 #pragma unroll
-    for (int dt = 0; dt < D / 16; ++dt)
+  for (int dt = 0; dt < D / 16; ++dt)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) Lo[(wave * 16 + cq) * D + dt * 16 + 4 * jq + e] = st.o[dt][e];
-    if (jq == 0) {
-      Lml[wave * 32 + cq] = st.m;
-      Lml[wave * 32 + 16 + cq] = st.l;
-    }
-    __syncthreads();
-    const int unit = (kvh * rgroups + rg) * splits + split;
-    for (int e = threadIdx.x; e < 16 * D; e += kAttnWaves * 64) {
-      const int c = e / D, dim = e % D;
-      float M = -INFINITY;
+    for (int e = 0; e < 4; ++e) Lo[(wave * 16 + cq) * D + dt * 16 + 4 * jq + e] = st.o[dt][e];
+  if (jq == 0) {
+    Lml[wave * 32 + cq] = st.m;
+    Lml[wave * 32 + 16 + cq] = st.l;
+  }
+  __syncthreads();
+  const int unit = (kvh * rgroups + rg) * splits + split;
+  for (int e = threadIdx.x; e < 16 * D; e += kAttnWaves * 64) {
+    const int c = e / D, dim = e % D;
+    float M = -INFINITY;
 #pragma unroll
-      for (int w = 0; w < kAttnWaves; ++w) M = fmaxf(M, Lml[w * 32 + c]);
-      float L = 0.f, acc = 0.f;
-      if (M != -INFINITY) {
+    for (int w = 0; w < kAttnWaves; ++w) M = fmaxf(M, Lml[w * 32 + c]);
+    float L = 0.f, acc = 0.f;
+    if (M != -INFINITY) {
 #pragma unroll
-        for (int w = 0; w < kAttnWaves; ++w) {
-          const float mw_ = Lml[w * 32 + c];
-          const float wt = mw_ == -INFINITY ? 0.f : exp2f(mw_ - M);
-          L += wt * Lml[w * 32 + 16 + c];
-          acc += wt * Lo[(w * 16 + c) * D + dim];
-        }
-      }
-      const int rr = rg * 16 + c;
-      if (splits == 1) {
-        if (rr < R)
-          ((bf16_t*)a.out)[((size_t)(rr / grp) * a.hq + kvh * grp + rr % grp) * D + dim] =
-              f32_to_bf16(L > 0.f ? acc / L : 0.f);
-      } else {
-        a.part_o[((size_t)unit * 16 + c) * D + dim] = acc;
-        if (dim == 0) {
-          a.part_ml[(size_t)unit * 32 + c] = M;
-          a.part_ml[(size_t)unit * 32 + 16 + c] = L;
-        }
+      for (int w = 0; w < kAttnWaves; ++w) {
+        const float mw_ = Lml[w * 32 + c];
+        const float wt = mw_ == -INFINITY ? 0.f : exp2f(mw_ - M);
+        L += wt * Lml[w * 32 + 16 + c];
+        acc += wt * Lo[(w * 16 + c) * D + dim];
       }
     }
-  } else {
-    using P = PairLds<D>;
-    bf16_t* buf = (bf16_t*)smem;
-    u32x4_t rs[P::CH];
-    const int npairs = b_end > b_begin ? (b_end - b_begin + 1) / 2 : 0;
-    if (npairs > 0) {
-      stage_load<D>(a, rs, b_begin, b_begin + 1 < b_end, kvh);
-      stage_store<D>(buf, rs);
-    }
-    __syncthreads();
-    for (int p = 0; p < npairs; ++p) {
-      const int b = b_begin + 2 * p;
-      const bool more = p + 1 < npairs;
-      if (more) stage_load<D>(a, rs, b + 2, b + 3 < b_end, kvh);
-      PairFrags<D> f;
-      load_pair_lds<D>(buf + (p & 1) * P::ELEMS, f, cq, jq);
-      attn_step(a, st, qf, f, b, b + 1 < b_end, tq, jq, sl2);
-      if (more) stage_store<D>(buf + ((p + 1) & 1) * P::ELEMS, rs);
-      __syncthreads();
-    }
-    const int unit = (kvh * rgroups + rg) * splits + split;
+    const int rr = rg * 16 + c;
     if (splits == 1) {
-      if (qvalid) {
-        const float inv = st.l > 0.f ? 1.f / st.l : 0.f;
-        bf16_t* orow = (bf16_t*)a.out + ((size_t)tq * a.hq + hq) * D;
-#pragma unroll
-        for (int dt = 0; dt < D / 16; ++dt) {
-          u32x2_t w;
-          w[0] = (uint32_t)f32_to_bf16(st.o[dt][0] * inv) |
-                 ((uint32_t)f32_to_bf16(st.o[dt][1] * inv) << 16);
-          w[1] = (uint32_t)f32_to_bf16(st.o[dt][2] * inv) |
-                 ((uint32_t)f32_to_bf16(st.o[dt][3] * inv) << 16);
-          *(u32x2_t*)(orow + dt * 16 + 4 * jq) = w;
-        }
-      }
+      if (rr < R)
+        ((bf16_t*)a.out)[((size_t)(rr / grp) * a.hq + kvh * grp + rr % grp) * D + dim] =
+            f32_to_bf16(L > 0.f ? acc / L : 0.f);
     } else {
-      const int c = wave * 16 + cq;  // row inside the workgroup
-      float* po = a.part_o + ((size_t)unit * ROWS + c) * D;
-#pragma unroll
-      for (int dt = 0; dt < D / 16; ++dt) *(f32x4_t*)(po + dt * 16 + 4 * jq) = st.o[dt];
-      if (jq == 0) {
-        a.part_ml[(size_t)unit * 2 * ROWS + c] = st.m;
-        a.part_ml[(size_t)unit * 2 * ROWS + ROWS + c] = st.l;
+      a.part_o[((size_t)unit * 16 + c) * D + dim] = acc;
+      if (dim == 0) {
+        a.part_ml[(size_t)unit * 32 + c] = M;
+        a.part_ml[(size_t)unit * 32 + 16 + c] = L;
       }
     }
   }
 }
 
-// Combines the splits of one (KV head, row group): with per-split running max
-// m_s (base 2), sum l_s and unnormalised o_s, o = sum_s 2^(m_s - M) o_s /
-// sum_s 2^(m_s - M) l_s, M = max_s m_s, taken in split order. One thread per
-// output element; the splits are read 8 at a time (24 loads in flight).
+// Combines the splits of one query row of one (KV head, row group) tile: with
+// per-split running max m_s (base 2), sum l_s and unnormalised o_s,
+// o = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s, M = max_s m_s. One
+// workgroup per row: the weights 2^(m_s - M) go to LDS first, then 256 / D
+// groups of threads sum interleaved splits for one dim each (independent loads,
+// many in flight) and the groups are added in group order (deterministic).
+constexpr int kMaxSplits = 128;
+
 template <int D, bool KEYSPLIT>
 __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a, int rgroups) {
   using S = AttnShape<D, KEYSPLIT>;
   constexpr int ROWS = S::ROWS;
-  constexpr int CHUNK = 8;
+  constexpr int G = 256 / D;  // split groups
+  static_assert(G >= 1 && 256 % D == 0, "head dim");
+  __shared__ float wgt[kMaxSplits];
+  __shared__ float red[256];
+  __shared__ float wred[4];
   const int tile = blockIdx.x;  // kvh * rgroups + rg
+  const int c = blockIdx.y;     // row inside the tile
   const int rg = tile % rgroups, kvh = tile / rgroups;
-  const int e = blockIdx.y * 256 + threadIdx.x;
-  if (e >= ROWS * D) return;
-  const int c = e / D, dim = e % D;
   const int grp = a.hq / a.g.hkv;
   const int rr = rg * ROWS + c;
-  if (rr >= a.n * grp) return;
+  if (rr >= a.n * grp) return;  // uniform over the workgroup
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int splits = a.splits;
-  const size_t unit0 = (size_t)tile * splits;
-  float M = -INFINITY, L = 0.f, acc = 0.f;
-  for (int s0 = 0; s0 < splits; s0 += CHUNK) {
-    float m[CHUNK], l[CHUNK], o[CHUNK];
+  const size_t u0 = (size_t)tile * splits;
+
+  // M = max over splits (splits <= 128 < 256: one value per thread at most)
+  float m = tid < splits ? a.part_ml[(u0 + tid) * 2 * ROWS + c] : -INFINITY;
+  float mw = wave_max(m);
+  if (lane == 0) wred[wave] = mw;
+  __syncthreads();
+  const float M = fmaxf(fmaxf(wred[0], wred[1]), fmaxf(wred[2], wred[3]));
+  const float w = (tid < splits && m != -INFINITY) ? exp2f(m - M) : 0.f;
+  if (tid < splits) wgt[tid] = w;
+  // L = sum_s w_s l_s, reduced in a fixed order
+  float lw = tid < splits ? w * a.part_ml[(u0 + tid) * 2 * ROWS + ROWS + c] : 0.f;
+  lw = wave_sum(lw);
+  __syncthreads();  // wred reads done; wgt visible
+  if (lane == 0) wred[wave] = lw;
+  const int dim = tid % D, g = tid / D;
+  float acc = 0.f;
+#pragma unroll 8
+  for (int sp = g; sp < splits; sp += G)
+    acc += wgt[sp] * a.part_o[((u0 + sp) * ROWS + c) * D + dim];
+  red[tid] = acc;
+  __syncthreads();
+  if (g == 0) {
+    float tot = acc;
 #pragma unroll
-    for (int i = 0; i < CHUNK; ++i) {
-      const size_t u = unit0 + s0 + i;
-      const bool ok = s0 + i < splits;
-      m[i] = ok ? a.part_ml[u * 2 * ROWS + c] : -INFINITY;
-      l[i] = ok ? a.part_ml[u * 2 * ROWS + ROWS + c] : 0.f;
-      o[i] = ok ? a.part_o[(u * ROWS + c) * D + dim] : 0.f;
-    }
-    float mc = M;
-#pragma unroll
-    for (int i = 0; i < CHUNK; ++i) mc = fmaxf(mc, m[i]);
-    if (mc == -INFINITY) continue;
-    const float sc = M == -INFINITY ? 0.f : exp2f(M - mc);
-    L *= sc;
-    acc *= sc;
-#pragma unroll
-    for (int i = 0; i < CHUNK; ++i) {
-      const float w = m[i] == -INFINITY ? 0.f : exp2f(m[i] - mc);
-      L += w * l[i];
-      acc += w * o[i];
-    }
-    M = mc;
+    for (int k = 1; k < G; ++k) tot += red[k * D + dim];
+    const float L = (wred[0] + wred[1]) + (wred[2] + wred[3]);
+    ((bf16_t*)a.out)[((size_t)(rr / grp) * a.hq + kvh * grp + rr % grp) * D + dim] =
+        f32_to_bf16(M != -INFINITY && L > 0.f ? tot / L : 0.f);
   }
-  ((bf16_t*)a.out)[((size_t)(rr / grp) * a.hq + kvh * grp + rr % grp) * D + dim] =
-      f32_to_bf16(L > 0.f ? acc / L : 0.f);
 }
 
 // ---------------------------------------------------------------------------
@@ -489,21 +612,30 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(AttnArgs a) {
   }
 }
 
-template <int D, bool KEYSPLIT>
-static void attn_bf16_launch(const AttnArgs& a, int rgroups, hipStream_t s) {
-  const dim3 grid(a.splits, rgroups, a.g.hkv);
-  launch_k(attn_bf16_kernel<D, KEYSPLIT>, grid, dim3(kAttnWaves * 64), 0, s, a, rgroups);
+template <int D>
+static void attn_bf16_go(const AttnArgs& a, bool keysplit, int rgroups, hipStream_t s) {
+  if (keysplit) {
+    launch_k(attn_decode_kernel<D>, dim3(a.splits, rgroups, a.g.hkv), dim3(kAttnWaves * 64), 0, s,
+             a, rgroups);
+  } else {
+    const int units = a.g.hkv * a.splits;
+    const int grid = (units + 7) / 8 * rgroups * 8;
+    launch_k(attn_rows_kernel<D>, dim3(grid), dim3(RowCfg<D>::WAVES * 64), 0, s, a, rgroups,
+             units);
+  }
   if (a.splits > 1) {
-    constexpr int ROWS = AttnShape<D, KEYSPLIT>::ROWS;
-    const dim3 mgrid(a.g.hkv * rgroups, (ROWS * D + 255) / 256);
-    launch_k(attn_merge_kernel<D, KEYSPLIT>, mgrid, dim3(256), 0, s, a, rgroups);
+    const int rows = keysplit ? AttnShape<D, true>::ROWS : AttnShape<D, false>::ROWS;
+    const dim3 mgrid(a.g.hkv * rgroups, rows);
+    if (keysplit)
+      launch_k(attn_merge_kernel<D, true>, mgrid, dim3(256), 0, s, a, rgroups);
+    else
+      launch_k(attn_merge_kernel<D, false>, mgrid, dim3(256), 0, s, a, rgroups);
   }
 }
 
 template <int D>
-static void attn_bf16_dispatch(const AttnArgs& a, bool keysplit, int rgroups, hipStream_t s) {
-  if (keysplit) attn_bf16_launch<D, true>(a, rgroups, s);
-  else attn_bf16_launch<D, false>(a, rgroups, s);
+static int rows_per_group(bool keysplit) {
+  return keysplit ? AttnShape<D, true>::ROWS : AttnShape<D, false>::ROWS;
 }
 
 hipError_t launch_attention(const AttnArgs& args, int dt, hipStream_t s) {
@@ -514,29 +646,34 @@ hipError_t launch_attention(const AttnArgs& args, int dt, hipStream_t s) {
     return hipGetLastError();
   }
   AttnArgs a = args;
-  // workgroup shape and split count: at least 8 blocks (4 pairs) per workgroup,
-  // about 4 (decode) or 2 (prefill) workgroups per CU at most, within the
-  // partial-buffer capacity
+  const int d = a.g.d;
+  if (d != 64 && d != 128 && d != 256) return hipErrorInvalidValue;
+  if (a.g.bt != 16) return hipErrorInvalidValue;
   const int R = a.n * (a.hq / a.g.hkv);
   const bool keysplit = R <= 16;
-  const int rows = keysplit ? 16 : 16 * kAttnWaves;
+  const int rows = d == 64 ? rows_per_group<64>(keysplit)
+                           : d == 128 ? rows_per_group<128>(keysplit) : rows_per_group<256>(keysplit);
   const int rgroups = (R + rows - 1) / rows;
   const int base = a.g.hkv * rgroups;
+  // split count: at least 8 blocks (4 pairs) per split; about one resident round
+  // of workgroups (decode: 2 per CU, 512 in all; rows: 1 per CU, 256 in all), so
+  // that workgroups run long and few partials are merged; within the
+  // partial-buffer capacity
   int splits = (a.nlb + 7) / 8;
-  splits = std::min(splits, std::max(1, (keysplit ? 1024 : 512) / base));
+  splits = std::min(splits, std::max(1, (keysplit ? 512 : 256) / base));
   splits = std::min(splits, keysplit ? kMaxSplitsKey : kMaxSplitsRow);
+  static_assert(kMaxSplitsKey <= kMaxSplits && kMaxSplitsRow <= kMaxSplits, "merge capacity");
   splits = std::min(splits, std::max(1, a.part_rows / (base * rows)));
   splits = std::max(splits, 1);
   const int bps = (a.nlb + splits - 1) / splits;
   a.splits = (a.nlb + bps - 1) / bps;
   if (a.splits > 1 &&
-      (a.part_o == nullptr || a.part_ml == nullptr || base * rows * a.splits > a.part_rows))
+      (a.part_o == nullptr || a.part_ml == nullptr || (size_t)base * rows * a.splits > (size_t)a.part_rows))
     return hipErrorInvalidValue;
-  switch (a.g.d) {
-    case 64: attn_bf16_dispatch<64>(a, keysplit, rgroups, s); break;
-    case 128: attn_bf16_dispatch<128>(a, keysplit, rgroups, s); break;
-    case 256: attn_bf16_dispatch<256>(a, keysplit, rgroups, s); break;
-    default: return hipErrorInvalidValue;
+  switch (d) {
+    case 64: attn_bf16_go<64>(a, keysplit, rgroups, s); break;
+    case 128: attn_bf16_go<128>(a, keysplit, rgroups, s); break;
+    default: attn_bf16_go<256>(a, keysplit, rgroups, s); break;
   }
   return hipGetLastError();
 }

@@ -55,6 +55,33 @@ __device__ __forceinline__ double wave_sum_d(double v) {
   return v;
 }
 
+// wait until at most steps * STEP of this wavefront's vector-memory operations are
+// outstanding (vector loads, including direct-to-LDS ones, count in issue order)
+template <int STEP>
+__device__ __forceinline__ void wait_vmcnt_steps(int steps) {
+  // s_waitcnt simm16: vmcnt[3:0], expcnt[6:4] (7 = no wait), lgkmcnt[11:8] (15 = no
+  // wait), vmcnt[5:4] in [15:14]
+#define VLA_WAITVM(v) __builtin_amdgcn_s_waitcnt(((v) & 0xF) | 0x70 | 0xF00 | (((v) >> 4) << 14))
+  switch (steps) {
+    case 0: VLA_WAITVM(0); break;
+    case 1: VLA_WAITVM(STEP); break;
+    case 2: VLA_WAITVM(2 * STEP); break;
+    case 3: VLA_WAITVM(3 * STEP); break;
+    case 4: VLA_WAITVM(4 * STEP); break;
+    case 5: VLA_WAITVM(5 * STEP); break;
+    case 6: VLA_WAITVM(6 * STEP); break;
+    default: VLA_WAITVM(0); break;
+  }
+#undef VLA_WAITVM
+}
+
+// two floats -> packed bfloat16 pair (round to nearest even; one v_cvt_pk_bf16_f32)
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  typedef __bf16 bf2_t __attribute__((ext_vector_type(2)));
+  typedef float f2_t __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f2_t){lo, hi}, bf2_t));
+}
+
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + __expf(-z)); }
 // exact GELU: z * Phi(z) = z/2 * (1 + erf(z / sqrt 2))
 __device__ __forceinline__ float gelu_erf(float z) { return 0.5f * z * (1.0f + erff(z * 0.70710678118654752f)); }

@@ -56,25 +56,6 @@ struct GemmTile {
   }
 };
 
-// wait until at most n of this wavefront's vector-memory operations are outstanding
-template <int STEP>
-__device__ __forceinline__ void wait_vmcnt_steps(int steps) {
-  // s_waitcnt simm16: vmcnt[3:0], expcnt[6:4] (7 = no wait), lgkmcnt[11:8] (15 = no
-  // wait), vmcnt[5:4] in [15:14]
-#define VLA_WAITVM(v) __builtin_amdgcn_s_waitcnt(((v) & 0xF) | 0x70 | 0xF00 | (((v) >> 4) << 14))
-  switch (steps) {
-    case 0: VLA_WAITVM(0); break;
-    case 1: VLA_WAITVM(STEP); break;
-    case 2: VLA_WAITVM(2 * STEP); break;
-    case 3: VLA_WAITVM(3 * STEP); break;
-    case 4: VLA_WAITVM(4 * STEP); break;
-    case 5: VLA_WAITVM(5 * STEP); break;
-    case 6: VLA_WAITVM(6 * STEP); break;
-    default: VLA_WAITVM(0); break;
-  }
-#undef VLA_WAITVM
-}
-
 // Epilogue of a wavefront's (MT x NT) tiles. Accumulator element e of tile
 // (mi, ni) is row 4*(lane/16)+e, column lane%16 of that 16 x 16 tile.
 template <int EPI, int MT, int NT, int WM, int WN>

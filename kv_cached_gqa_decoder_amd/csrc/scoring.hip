@@ -15,26 +15,51 @@
 
 namespace vla {
 
+// one lane per 8 consecutive dims of one (frame, layer): the frame's tokens are
+// added in token order (the same order for every dim and every run), two
+// blocks (32 tokens) of 16-byte loads in flight per step
 template <typename T>
-__global__ __launch_bounds__(256) void meankeys_kernel(const T* kp, KvGeom g, const int* blk_table,
-                                                       const int* fr_blk0, const int* fr_nblk,
-                                                       const int* fr_ntok, const int* fr_slot,
-                                                       int layer0, double* table, int max_frames) {
+__global__ __launch_bounds__(64) void meankeys_kernel(const T* kp, KvGeom g, const int* blk_table,
+                                                      const int* fr_blk0, const int* fr_nblk,
+                                                      const int* fr_ntok, const int* fr_slot,
+                                                      int layer0, double* table, int max_frames) {
+  constexpr int V = 16 / sizeof(T);  // elements per 16-byte load
   const int f = blockIdx.x;
   const int layer = layer0 + blockIdx.y;
   const int D = g.hkv * g.d;
+  const int i0 = (blockIdx.z * 64 + threadIdx.x) * V;  // first dim of this lane
+  if (i0 >= D) return;
+  const int h = i0 / g.d, dd = i0 % g.d;
   const int blk0 = fr_blk0[f], nblk = fr_nblk[f], ntok = fr_ntok[f];
-  double* out = table + ((size_t)layer * max_frames + fr_slot[f]) * D;
-  for (int i = threadIdx.x; i < D; i += blockDim.x) {
-    const int h = i / g.d, dd = i % g.d;
-    double s = 0.0;
-    for (int k = 0; k < nblk; ++k) {
-      const int b = blk_table[blk0 + k];
-      const int nt = min(g.bt, ntok - k * g.bt);
-      for (int sl = 0; sl < nt; ++sl) s += (double)St<T>::ld(kp, g.kidx(layer, b, h, sl, dd));
+  double acc[V];
+#pragma unroll
+  for (int e = 0; e < V; ++e) acc[e] = 0.0;
+  for (int k = 0; k < nblk; k += 2) {
+    u32x4_t w[2][16];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int kk = k + j < nblk ? k + j : k;
+      const int b = blk_table[blk0 + kk];
+#pragma unroll
+      for (int sl = 0; sl < 16; ++sl)
+        w[j][sl] = *(const u32x4_t*)(kp + g.kidx(layer, b, h, sl, dd));
     }
-    out[i] = s / (double)ntok;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      if (k + j >= nblk) break;
+      const int nt = min(g.bt, ntok - (k + j) * g.bt);
+#pragma unroll
+      for (int sl = 0; sl < 16; ++sl) {
+        if (sl >= nt) break;
+        const T* v = (const T*)&w[j][sl];
+#pragma unroll
+        for (int e = 0; e < V; ++e) acc[e] += (double)St<T>::ld(v, e);
+      }
+    }
   }
+  double* out = table + ((size_t)layer * max_frames + fr_slot[f]) * D + i0;
+#pragma unroll
+  for (int e = 0; e < V; ++e) out[e] = acc[e] / (double)ntok;
 }
 
 hipError_t launch_meankeys(const void* kpool, KvGeom g, const int* blk_table, const int* fr_blk0,
@@ -42,15 +67,16 @@ hipError_t launch_meankeys(const void* kpool, KvGeom g, const int* blk_table, co
                            int layer0, int nlayers, double* table, int max_frames, int dt,
                            hipStream_t s) {
   if (nframes <= 0 || nlayers <= 0) return hipSuccess;
-  dim3 grid(nframes, nlayers);
+  const int D = g.hkv * g.d;
+  const int V = dt == DT_F32 ? 4 : 8;
+  if (g.bt != 16 || g.d % V) return hipErrorInvalidValue;
+  dim3 grid(nframes, nlayers, (D / V + 63) / 64);
   if (dt == DT_F32)
-    launch_k(meankeys_kernel<float>, grid, dim3(256), 0, s, (const float*)kpool, g, blk_table, fr_blk0,
-                                                fr_nblk, fr_ntok, fr_slot, layer0, table,
-                                                max_frames);
+    launch_k(meankeys_kernel<float>, grid, dim3(64), 0, s, (const float*)kpool, g, blk_table,
+             fr_blk0, fr_nblk, fr_ntok, fr_slot, layer0, table, max_frames);
   else
-    launch_k(meankeys_kernel<bf16_t>, grid, dim3(256), 0, s, (const bf16_t*)kpool, g, blk_table, fr_blk0,
-                                                 fr_nblk, fr_ntok, fr_slot, layer0, table,
-                                                 max_frames);
+    launch_k(meankeys_kernel<bf16_t>, grid, dim3(64), 0, s, (const bf16_t*)kpool, g, blk_table,
+             fr_blk0, fr_nblk, fr_ntok, fr_slot, layer0, table, max_frames);
   return hipGetLastError();
 }
 
