@@ -25,8 +25,8 @@
 //     partial (m, l, o) are merged through LDS.
 //   rows (prefill): 8 wavefronts, each owning 2 row tiles (1 at d = 256), so a
 //     workgroup covers 256 (128) rows; every block pair goes through a 3-stage
-//     LDS ring filled by direct-to-LDS DMA (16 bytes per lane; K rows XOR-
-//     swizzled in 16-byte chunks against bank conflicts) and is read by all
+//     LDS ring filled by direct-to-LDS DMA (16 bytes per lane; K rows and V^T
+//     rows swizzled in 16-byte chunks against bank conflicts) and is read by all
 //     rows of the workgroup. Workgroups are numbered so that all row tiles of
 //     one (KV head, key split) run on one XCD and stream the same blocks
 //     through its L2.
@@ -88,54 +88,66 @@ __device__ __forceinline__ void state_init(SoftmaxState<D>& st) {
   for (int i = 0; i < D / 16; ++i) st.o[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 }
 
+// max / sum over the 4 lanes of one query column (lanes c, c+16, c+32, c+48), by
+// the gfx950 row-swap permutes (no LDS traffic); every lane gets the same value
+__device__ __forceinline__ float col_max4(float v) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                  false);
+  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                  false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float col_sum4(float v) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                  false);
+  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                  false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
 // Online-softmax update of one query column (tq) for the scores of blocks b and
 // b+1 (s0, s1: keys 4jq..4jq+3 of each; has1: block b+1 exists). `masked`:
 // some key of the pair may be invisible (ragged block, causal region);
-// otherwise every key is visible. Returns the bf16 probabilities as the MFMA B
-// operand (the running sum uses the rounded values) and the rescale factor of
-// the running output.
+// otherwise every key is visible. The running max m is in base-2 units
+// (score * sl2, sl2 = log2(e) / sqrt(d) > 0, so the max of the raw scores gives
+// it); p = 2^(s * sl2 - m) by one fma and the hardware exp2. Returns the bf16
+// probabilities as the MFMA B operand (the running sum uses the rounded values)
+// and the rescale factor of the running output.
 __device__ __forceinline__ bf16x8_t softmax_pair(const AttnArgs& a, float& m, float& l,
-                                                 const f32x4_t& s0, const f32x4_t& s1, int b,
-                                                 bool has1, bool masked, int tq, int jq,
-                                                 float sl2, float& alpha) {
-  float p0[4], p1[4];
-  float mx = -INFINITY;
+                                                 f32x4_t s0, f32x4_t s1, int b, bool has1,
+                                                 bool masked, int tq, int jq, float sl2,
+                                                 float& alpha) {
   if (masked) {
     const int nt0 = block_ntok_s(a, b);
     const int nt1 = has1 ? block_ntok_s(a, b + 1) : 0;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int ks = 4 * jq + e;
-      p0[e] = key_visible(a, b, ks, nt0, tq) ? s0[e] * sl2 : -INFINITY;
-      p1[e] = (has1 && key_visible(a, b + 1, ks, nt1, tq)) ? s1[e] * sl2 : -INFINITY;
-      mx = fmaxf(mx, fmaxf(p0[e], p1[e]));
-    }
-  } else {
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      p0[e] = s0[e] * sl2;
-      p1[e] = s1[e] * sl2;
-      mx = fmaxf(mx, fmaxf(p0[e], p1[e]));
+      if (!key_visible(a, b, ks, nt0, tq)) s0[e] = -INFINITY;
+      if (!(has1 && key_visible(a, b + 1, ks, nt1, tq))) s1[e] = -INFINITY;
     }
   }
-  mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-  mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+  float mx = fmaxf(fmaxf(fmaxf(s0[0], s0[1]), fmaxf(s0[2], s0[3])),
+                   fmaxf(fmaxf(s1[0], s1[1]), fmaxf(s1[2], s1[3])));
+  mx = col_max4(mx) * sl2;
   const float m_new = fmaxf(m, mx);
   const float m_use = m_new == -INFINITY ? 0.f : m_new;
-  alpha = m == -INFINITY ? 0.f : exp2f(m - m_use);
+  alpha = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m - m_use);
   u32x4_t pw;
 #pragma unroll
   for (int e = 0; e < 2; ++e) {
-    pw[e] = pack_bf16x2(exp2f(p0[2 * e] - m_use), exp2f(p0[2 * e + 1] - m_use));
-    pw[2 + e] = pack_bf16x2(exp2f(p1[2 * e] - m_use), exp2f(p1[2 * e + 1] - m_use));
+    pw[e] = pack_bf16x2(__builtin_amdgcn_exp2f(fmaf(s0[2 * e], sl2, -m_use)),
+                        __builtin_amdgcn_exp2f(fmaf(s0[2 * e + 1], sl2, -m_use)));
+    pw[2 + e] = pack_bf16x2(__builtin_amdgcn_exp2f(fmaf(s1[2 * e], sl2, -m_use)),
+                            __builtin_amdgcn_exp2f(fmaf(s1[2 * e + 1], sl2, -m_use)));
   }
   float sum = 0.f;
 #pragma unroll
   for (int e = 0; e < 4; ++e)
     sum += __uint_as_float(pw[e] << 16) + __uint_as_float(pw[e] & 0xffff0000u);
-  sum += __shfl_xor(sum, 16, 64);
-  sum += __shfl_xor(sum, 32, 64);
-  l = l * alpha + sum;
+  l = l * alpha + col_sum4(sum);
   m = m_new;
   return __builtin_bit_cast(bf16x8_t, pw);
 }
@@ -192,10 +204,10 @@ __device__ __forceinline__ void load_pair_global(const AttnArgs& a, PairFrags<D>
 // ---------------------------------------------------------------------------
 template <int D>
 struct RowCfg {
-  static constexpr int QT = D <= 128 ? 2 : 1;        // 16-row tiles per wavefront
   static constexpr int WAVES = 8;
+  static constexpr int QT = (D <= 128 ? 16 : 8) / WAVES;  // 16-row tiles per wavefront
   static constexpr int ROWS = WAVES * QT * 16;       // rows per workgroup
-  static constexpr int NS = 3;                       // ring stages (block pairs)
+  static constexpr int NS = D <= 128 ? 4 : 3;        // ring stages (block pairs)
   static constexpr int BLK = 16 * D * 2;             // one block of K (or V) of one KV head
   static constexpr int STAGE = 4 * BLK;              // K0 K1 V0 V1
   static constexpr int LDS = NS * STAGE;
@@ -211,8 +223,68 @@ __device__ __forceinline__ int kswz(int r) {
   return D >= 128 ? (r & 15) : (r & 7);
 }
 
+// one block pair for a wavefront's QT row tiles: S^T = K Q^T for every tile (each
+// K fragment read once from LDS), the softmax of every tile, then O^T += V^T P^T
+// (each V fragment read once). MASKED: some key of the pair may be invisible.
+// Straight-line code apart from the rarely taken rescale, so the scheduler can
+// overlap one tile's softmax with another tile's products.
+template <int D, int QT, bool MASKED>
+__device__ __forceinline__ void rows_step(const AttnArgs& a, const unsigned char* st,
+                                          const bf16x8_t (&qf)[QT][D / 32], const int (&tq)[QT],
+                                          float (&m)[QT], float (&l)[QT],
+                                          f32x4_t (&o)[QT][D / 16], int b, bool has1, int cq,
+                                          int jq, float sl2) {
+  constexpr int BLK = RowCfg<D>::BLK;
+  f32x4_t s0[QT], s1[QT];
+#pragma unroll
+  for (int qt = 0; qt < QT; ++qt) {
+    s0[qt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    s1[qt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  }
+#pragma unroll
+  for (int ds = 0; ds < D / 32; ++ds) {
+    const int c = ds * 4 + jq;
+    const int off = cq * (D * 2) + ((c ^ kswz<D>(cq)) << 4);
+    const bf16x8_t k0 = *(const bf16x8_t*)(st + off);
+    const bf16x8_t k1 = *(const bf16x8_t*)(st + BLK + off);
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt) {
+      s0[qt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, qf[qt][ds], s0[qt], 0, 0, 0);
+      s1[qt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, qf[qt][ds], s1[qt], 0, 0, 0);
+    }
+  }
+  bf16x8_t pf[QT];
+  float alpha[QT];
+  bool rescale = false;
+#pragma unroll
+  for (int qt = 0; qt < QT; ++qt) {
+    pf[qt] = softmax_pair(a, m[qt], l[qt], s0[qt], s1[qt], b, has1, MASKED, tq[qt], jq, sl2,
+                          alpha[qt]);
+    rescale = rescale || alpha[qt] != 1.f;
+  }
+  // the running outputs only change scale when some column's maximum rose
+  if (__any(rescale)) {
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt)
+#pragma unroll
+      for (int dt = 0; dt < D / 16; ++dt) o[qt][dt] *= alpha[qt];
+  }
+#pragma unroll
+  for (int dt = 0; dt < D / 16; ++dt) {
+    // V^T rows: dim dt*16 + cq, keys 4jq..4jq+3 of block 0 then of block 1
+    const int voff = (dt * 16 + cq) * 32 + (((jq >> 1) ^ ((cq >> 3) & 1)) << 4) + (jq & 1) * 8;
+    const u32x2_t lo = *(const u32x2_t*)(st + 2 * BLK + voff);
+    const u32x2_t hi = *(const u32x2_t*)(st + 3 * BLK + voff);
+    const bf16x8_t vf = __builtin_bit_cast(bf16x8_t, u32x4_t{lo[0], lo[1], hi[0], hi[1]});
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt)
+      o[qt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf[qt], o[qt][dt], 0, 0, 0);
+  }
+}
+
 template <int D>
-__global__ __launch_bounds__(512) void attn_rows_kernel(AttnArgs a, int rgroups, int units) {
+__global__ __launch_bounds__(RowCfg<D>::WAVES * 64) void attn_rows_kernel(AttnArgs a, int rgroups,
+                                                                        int units) {
   using C = RowCfg<D>;
   constexpr int QT = C::QT, NS = C::NS, ROWS = C::ROWS;
   __shared__ __attribute__((aligned(1024))) unsigned char smem[C::LDS];
@@ -293,7 +365,11 @@ __global__ __launch_bounds__(512) void attn_rows_kernel(AttnArgs a, int rgroups,
           src = (size_t)a.g.kidx(a.layer, pb, kvh, 0, 0) * 2 + (size_t)r * (D * 2) +
                 ((pc ^ kswz<D>(r)) << 4);
         } else {
-          src = (size_t)a.g.vidx(a.layer, pb, kvh, 0, 0) * 2 + (size_t)pos * 16;
+          // V^T row vr (one dim, 16 keys = two 16-byte halves); the halves swap
+          // places on bit 3 of the row, against bank conflicts of the P*V reads
+          const int vr = pos >> 1;
+          src = (size_t)a.g.vidx(a.layer, pb, kvh, 0, 0) * 2 + (size_t)vr * 32 +
+                (((pos & 1) ^ ((vr >> 3) & 1)) << 4);
         }
         __builtin_amdgcn_global_load_lds(
             (const void*)((which < 2 ? kp : vp) + src),
@@ -315,51 +391,10 @@ __global__ __launch_bounds__(512) void attn_rows_kernel(AttnArgs a, int rgroups,
       bool masked = !has1 || block_ntok_s(a, b) != a.g.bt || block_ntok_s(a, b + 1) != a.g.bt;
       if (a.causal) masked = masked || b + 1 >= a.cb0;
 
-      f32x4_t s0[QT], s1[QT];
-#pragma unroll
-      for (int qt = 0; qt < QT; ++qt) {
-        s0[qt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-        s1[qt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-      }
-#pragma unroll
-      for (int ds = 0; ds < D / 32; ++ds) {
-        const int c = ds * 4 + jq;
-        const int off = cq * (D * 2) + ((c ^ kswz<D>(cq)) << 4);
-        const bf16x8_t k0 = *(const bf16x8_t*)(st + off);
-        const bf16x8_t k1 = *(const bf16x8_t*)(st + C::BLK + off);
-#pragma unroll
-        for (int qt = 0; qt < QT; ++qt) {
-          s0[qt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, qf[qt][ds], s0[qt], 0, 0, 0);
-          s1[qt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, qf[qt][ds], s1[qt], 0, 0, 0);
-        }
-      }
-      bf16x8_t pf[QT];
-      float alpha[QT];
-#pragma unroll
-      for (int qt = 0; qt < QT; ++qt)
-        pf[qt] = softmax_pair(a, m[qt], l[qt], s0[qt], s1[qt], b, has1, masked, tq[qt], jq, sl2,
-                              alpha[qt]);
-      // the running outputs only change scale when some column's maximum rose
-      bool rescale = false;
-#pragma unroll
-      for (int qt = 0; qt < QT; ++qt) rescale = rescale || alpha[qt] != 1.f;
-      if (__any(rescale)) {
-#pragma unroll
-        for (int qt = 0; qt < QT; ++qt)
-#pragma unroll
-          for (int dt = 0; dt < D / 16; ++dt) o[qt][dt] *= alpha[qt];
-      }
-#pragma unroll
-      for (int dt = 0; dt < D / 16; ++dt) {
-        // V^T rows: dim dt*16 + cq, keys 4jq..4jq+3 of block 0 then of block 1
-        const int voff = (dt * 16 + cq) * 32 + jq * 8;
-        const u32x2_t lo = *(const u32x2_t*)(st + 2 * C::BLK + voff);
-        const u32x2_t hi = *(const u32x2_t*)(st + 3 * C::BLK + voff);
-        const bf16x8_t vf = __builtin_bit_cast(bf16x8_t, u32x4_t{lo[0], lo[1], hi[0], hi[1]});
-#pragma unroll
-        for (int qt = 0; qt < QT; ++qt)
-          o[qt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf[qt], o[qt][dt], 0, 0, 0);
-      }
+      if (masked)
+        rows_step<D, QT, true>(a, st, qf, tq, m, l, o, b, has1, cq, jq, sl2);
+      else
+        rows_step<D, QT, false>(a, st, qf, tq, m, l, o, b, has1, cq, jq, sl2);
     }
   }
 
@@ -660,7 +695,9 @@ hipError_t launch_attention(const AttnArgs& args, int dt, hipStream_t s) {
   // that workgroups run long and few partials are merged; within the
   // partial-buffer capacity
   int splits = (a.nlb + 7) / 8;
-  splits = std::min(splits, std::max(1, (keysplit ? 512 : 256) / base));
+  // (rows kernel: 8 wavefronts per CU in all, i.e. 8 / WAVES workgroups per CU)
+  const int resident = keysplit ? 512 : 256 * 8 / RowCfg<128>::WAVES;
+  splits = std::min(splits, std::max(1, resident / base));
   splits = std::min(splits, keysplit ? kMaxSplitsKey : kMaxSplitsRow);
   static_assert(kMaxSplitsKey <= kMaxSplits && kMaxSplitsRow <= kMaxSplits, "merge capacity");
   splits = std::min(splits, std::max(1, a.part_rows / (base * rows)));
