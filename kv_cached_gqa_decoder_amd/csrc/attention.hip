@@ -202,12 +202,15 @@ __device__ __forceinline__ void load_pair_global(const AttnArgs& a, PairFrags<D>
 // ---------------------------------------------------------------------------
 // rows kernel (prefill)
 // ---------------------------------------------------------------------------
-template <int D>
+// Two shapes. Long caches: 8 wavefronts of 2 row tiles (1 at d = 256), so each
+// block pair is read once per 256 (128) rows. Short caches (few pairs per
+// workgroup): 4 wavefronts of one tile, 64 rows, for more workgroups.
+template <int D, bool SHORT>
 struct RowCfg {
-  static constexpr int WAVES = 8;
-  static constexpr int QT = (D <= 128 ? 16 : 8) / WAVES;  // 16-row tiles per wavefront
+  static constexpr int WAVES = SHORT ? 4 : 8;
+  static constexpr int QT = SHORT ? 1 : (D <= 128 ? 16 : 8) / WAVES;  // 16-row tiles per wavefront
   static constexpr int ROWS = WAVES * QT * 16;       // rows per workgroup
-  static constexpr int NS = D <= 128 ? 4 : 3;        // ring stages (block pairs)
+  static constexpr int NS = D <= 128 && !SHORT ? 4 : 3;  // ring stages (block pairs)
   static constexpr int BLK = 16 * D * 2;             // one block of K (or V) of one KV head
   static constexpr int STAGE = 4 * BLK;              // K0 K1 V0 V1
   static constexpr int LDS = NS * STAGE;
@@ -234,7 +237,7 @@ __device__ __forceinline__ void rows_step(const AttnArgs& a, const unsigned char
                                           float (&m)[QT], float (&l)[QT],
                                           f32x4_t (&o)[QT][D / 16], int b, bool has1, int cq,
                                           int jq, float sl2) {
-  constexpr int BLK = RowCfg<D>::BLK;
+  constexpr int BLK = 16 * D * 2;
   f32x4_t s0[QT], s1[QT];
 #pragma unroll
   for (int qt = 0; qt < QT; ++qt) {
@@ -282,10 +285,11 @@ __device__ __forceinline__ void rows_step(const AttnArgs& a, const unsigned char
   }
 }
 
-template <int D>
-__global__ __launch_bounds__(RowCfg<D>::WAVES * 64) void attn_rows_kernel(AttnArgs a, int rgroups,
-                                                                        int units) {
-  using C = RowCfg<D>;
+template <int D, bool SHORT>
+__global__ __launch_bounds__(SHORT ? 256 : 512) void attn_rows_kernel(AttnArgs a, int rgroups,
+                                                                    int units) {
+  using C = RowCfg<D, SHORT>;
+  static_assert(C::WAVES * 64 == (SHORT ? 256 : 512), "launch bounds");
   constexpr int QT = C::QT, NS = C::NS, ROWS = C::ROWS;
   __shared__ __attribute__((aligned(1024))) unsigned char smem[C::LDS];
 
@@ -432,17 +436,6 @@ __global__ __launch_bounds__(RowCfg<D>::WAVES * 64) void attn_rows_kernel(AttnAr
 // ---------------------------------------------------------------------------
 // decode kernel (<= 16 query rows)
 // ---------------------------------------------------------------------------
-template <int D, bool KEYSPLIT>
-struct AttnShape;
-template <int D>
-struct AttnShape<D, true> {
-  static constexpr int ROWS = 16;
-};
-template <int D>
-struct AttnShape<D, false> {
-  static constexpr int ROWS = RowCfg<D>::ROWS;
-};
-
 // partial layout (both kernels): part_o[unit][ROWS][D], part_ml[unit][2][ROWS] with
 // unit = (kvh * rgroups + rg) * splits + split
 template <int D>
@@ -544,10 +537,8 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(AttnArgs a, int rgroup
 // many in flight) and the groups are added in group order (deterministic).
 constexpr int kMaxSplits = 128;
 
-template <int D, bool KEYSPLIT>
+template <int D, int ROWS>
 __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a, int rgroups) {
-  using S = AttnShape<D, KEYSPLIT>;
-  constexpr int ROWS = S::ROWS;
   constexpr int G = 256 / D;  // split groups
   static_assert(G >= 1 && 256 % D == 0, "head dim");
   __shared__ float wgt[kMaxSplits];
@@ -647,30 +638,39 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(AttnArgs a) {
   }
 }
 
+template <int D, int ROWS>
+static void attn_merge_go(const AttnArgs& a, int rgroups, hipStream_t s) {
+  if (a.splits > 1)
+    launch_k(attn_merge_kernel<D, ROWS>, dim3(a.g.hkv * rgroups, ROWS), dim3(256), 0, s, a,
+             rgroups);
+}
+
+template <int D, bool SHORT>
+static void attn_rows_go(const AttnArgs& a, int rgroups, hipStream_t s) {
+  using C = RowCfg<D, SHORT>;
+  const int units = a.g.hkv * a.splits;
+  const int grid = (units + 7) / 8 * rgroups * 8;
+  launch_k(attn_rows_kernel<D, SHORT>, dim3(grid), dim3(C::WAVES * 64), 0, s, a, rgroups, units);
+  attn_merge_go<D, C::ROWS>(a, rgroups, s);
+}
+
+// shape: 0 decode, 1 rows (short cache), 2 rows (long cache)
 template <int D>
-static void attn_bf16_go(const AttnArgs& a, bool keysplit, int rgroups, hipStream_t s) {
-  if (keysplit) {
+static void attn_bf16_go(const AttnArgs& a, int shape, int rgroups, hipStream_t s) {
+  if (shape == 0) {
     launch_k(attn_decode_kernel<D>, dim3(a.splits, rgroups, a.g.hkv), dim3(kAttnWaves * 64), 0, s,
              a, rgroups);
+    attn_merge_go<D, 16>(a, rgroups, s);
+  } else if (shape == 1) {
+    attn_rows_go<D, true>(a, rgroups, s);
   } else {
-    const int units = a.g.hkv * a.splits;
-    const int grid = (units + 7) / 8 * rgroups * 8;
-    launch_k(attn_rows_kernel<D>, dim3(grid), dim3(RowCfg<D>::WAVES * 64), 0, s, a, rgroups,
-             units);
-  }
-  if (a.splits > 1) {
-    const int rows = keysplit ? AttnShape<D, true>::ROWS : AttnShape<D, false>::ROWS;
-    const dim3 mgrid(a.g.hkv * rgroups, rows);
-    if (keysplit)
-      launch_k(attn_merge_kernel<D, true>, mgrid, dim3(256), 0, s, a, rgroups);
-    else
-      launch_k(attn_merge_kernel<D, false>, mgrid, dim3(256), 0, s, a, rgroups);
+    attn_rows_go<D, false>(a, rgroups, s);
   }
 }
 
 template <int D>
-static int rows_per_group(bool keysplit) {
-  return keysplit ? AttnShape<D, true>::ROWS : AttnShape<D, false>::ROWS;
+static int rows_per_group(int shape) {
+  return shape == 0 ? 16 : shape == 1 ? RowCfg<D, true>::ROWS : RowCfg<D, false>::ROWS;
 }
 
 hipError_t launch_attention(const AttnArgs& args, int dt, hipStream_t s) {
@@ -686,8 +686,10 @@ hipError_t launch_attention(const AttnArgs& args, int dt, hipStream_t s) {
   if (a.g.bt != 16) return hipErrorInvalidValue;
   const int R = a.n * (a.hq / a.g.hkv);
   const bool keysplit = R <= 16;
-  const int rows = d == 64 ? rows_per_group<64>(keysplit)
-                           : d == 128 ? rows_per_group<128>(keysplit) : rows_per_group<256>(keysplit);
+  // short caches (<= 256 blocks) take the 64-row workgroups
+  const int shape = keysplit ? 0 : a.nlb <= 256 ? 1 : 2;
+  const int rows = d == 64 ? rows_per_group<64>(shape)
+                           : d == 128 ? rows_per_group<128>(shape) : rows_per_group<256>(shape);
   const int rgroups = (R + rows - 1) / rows;
   const int base = a.g.hkv * rgroups;
   // split count: at least 8 blocks (4 pairs) per split; about one resident round
@@ -695,8 +697,8 @@ hipError_t launch_attention(const AttnArgs& args, int dt, hipStream_t s) {
   // that workgroups run long and few partials are merged; within the
   // partial-buffer capacity
   int splits = (a.nlb + 7) / 8;
-  // (rows kernel: 8 wavefronts per CU in all, i.e. 8 / WAVES workgroups per CU)
-  const int resident = keysplit ? 512 : 256 * 8 / RowCfg<128>::WAVES;
+  // (rows kernel: 8 wavefronts per CU, i.e. 1 long-cache or 2 short-cache workgroups)
+  const int resident = shape == 2 ? 256 : 512;
   splits = std::min(splits, std::max(1, resident / base));
   splits = std::min(splits, keysplit ? kMaxSplitsKey : kMaxSplitsRow);
   static_assert(kMaxSplitsKey <= kMaxSplits && kMaxSplitsRow <= kMaxSplits, "merge capacity");
@@ -708,9 +710,9 @@ hipError_t launch_attention(const AttnArgs& args, int dt, hipStream_t s) {
       (a.part_o == nullptr || a.part_ml == nullptr || (size_t)base * rows * a.splits > (size_t)a.part_rows))
     return hipErrorInvalidValue;
   switch (d) {
-    case 64: attn_bf16_go<64>(a, keysplit, rgroups, s); break;
-    case 128: attn_bf16_go<128>(a, keysplit, rgroups, s); break;
-    default: attn_bf16_go<256>(a, keysplit, rgroups, s); break;
+    case 64: attn_bf16_go<64>(a, shape, rgroups, s); break;
+    case 128: attn_bf16_go<128>(a, shape, rgroups, s); break;
+    default: attn_bf16_go<256>(a, shape, rgroups, s); break;
   }
   return hipGetLastError();
 }

@@ -93,3 +93,22 @@ def test_int4_llama3_8b_shape_one_layer():
     ref = t.decode(ref, 3, "llama3-8b-shape")
     log("llama3-8b shape: last logits cos %.6f rel %.2e" % metrics(logits_of(t.m), ref))
     t.m.close()
+
+
+def test_int4_llama3_8b_shape_full_120k_context_one_layer():
+    """The long-context workload at its full size on one layer: a 120,000-token raw
+    prefix (235 frames of up to 512 tokens, 7,500 blocks), the 512-token chunk of ids
+    and 2 decodes, in the launch configuration the benchmark times (the output head
+    aside, every kernel shape depends on the context and the layer width, not on the
+    layer count)."""
+    p = dict(vla.PRESETS["c5_llama3_8b_int4"], n_layers=1, vocab=4096)
+    t = _Pair(p, 0.02)
+    done, f = 0, 0
+    while done < 120000:
+        n = min(512, 120000 - done)
+        t.raw(31, f, n)
+        done += n
+        f += 1
+    ref = t.ids(512, "120K-context prefill 512")
+    ref = t.decode(ref, 2, "120K-context")
+    t.m.close()

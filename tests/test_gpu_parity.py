@@ -269,3 +269,31 @@ def test_bf16_long_context_split_attention():
         check_argmax(g, ref, "bf16", f"long-context decode {i}")
         tok = nxt
     m.close()
+
+
+def test_bf16_long_cache_prefill_shape():
+    """More than 256 resident blocks (300 blocks of raw frames, then a 120-token chunk),
+    so the prefill attention takes its long-cache shape (256-row workgroups, 4-stage
+    ring, split keys + merge); then 3 greedy decodes."""
+    p = dict(TINY_BF16, num_blocks=320, max_frames=80, max_chunk=120)
+    init_std = 0.08
+    ocfg = oracle_config(p, init_std=init_std)
+    sess = D.Session(ocfg)
+    m = _model(p, init_std)
+    L, hkv, d = p["n_layers"], p["n_kv_heads"], p["head_dim"]
+    for f in range(75):
+        (k32, v32), (ks, vs) = synth.raw_kv_frame(12, f, L, 64, hkv, d, "bf16")
+        fid = m.kv_append_raw(dev_from_storage(ks, "bf16"), dev_from_storage(vs, "bf16"), 64)
+        assert fid == sess.append_raw(k32, v32)
+    x32, xs = synth.embeddings(p["seed"], 0, 120, p["hidden"], "bf16")
+    m.prefill_chunk(embeds=dev_from_storage(xs, "bf16"), n=120)
+    _, ref = sess.prefill_chunk(embeds=x32)
+    check_logits(logits_of(m), ref, "bf16", "long-cache prefill")
+    tok = int(np.argmax(ref))
+    for i in range(3):
+        g = m.decode_step(tok)
+        nxt, ref = sess.decode_step(tok)
+        check_logits(logits_of(m), ref, "bf16", f"long-cache decode {i}")
+        check_argmax(g, ref, "bf16", f"long-cache decode {i}")
+        tok = nxt
+    m.close()
