@@ -120,13 +120,19 @@ __device__ __forceinline__ bf16x8_t softmax_pair(const AttnArgs& a, float& m, fl
                                                  bool masked, int tq, int jq, float sl2,
                                                  float& alpha) {
   if (masked) {
+    // visible: slot < ntok, and outside the causal region or at most the row's token
+    // (branch-free selects; b, ntok and the region bounds are wave-uniform)
     const int nt0 = block_ntok_s(a, b);
     const int nt1 = has1 ? block_ntok_s(a, b + 1) : 0;
+    const bool open0 = b < a.cb0 || !a.causal, open1 = b + 1 < a.cb0 || !a.causal;
+    const int ck0 = (b - a.cb0) * a.g.bt - a.cslot0, ck1 = ck0 + a.g.bt;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int ks = 4 * jq + e;
-      if (!key_visible(a, b, ks, nt0, tq)) s0[e] = -INFINITY;
-      if (!(has1 && key_visible(a, b + 1, ks, nt1, tq))) s1[e] = -INFINITY;
+      const bool v0 = (ks < nt0) & (open0 | (ck0 + ks <= tq));
+      const bool v1 = (ks < nt1) & (open1 | (ck1 + ks <= tq));
+      s0[e] = v0 ? s0[e] : -INFINITY;
+      s1[e] = v1 ? s1[e] : -INFINITY;
     }
   }
   float mx = fmaxf(fmaxf(fmaxf(s0[0], s0[1]), fmaxf(s0[2], s0[3])),
@@ -228,15 +234,15 @@ __device__ __forceinline__ int kswz(int r) {
 
 // one block pair for a wavefront's QT row tiles: S^T = K Q^T for every tile (each
 // K fragment read once from LDS), the softmax of every tile, then O^T += V^T P^T
-// (each V fragment read once). MASKED: some key of the pair may be invisible.
-// Straight-line code apart from the rarely taken rescale, so the scheduler can
-// overlap one tile's softmax with another tile's products.
-template <int D, int QT, bool MASKED>
+// (each V fragment read once). masked: some key of the pair may be invisible;
+// only the masking itself is conditional, so both cases share one instruction
+// stream (and one register assignment of the running outputs).
+template <int D, int QT>
 __device__ __forceinline__ void rows_step(const AttnArgs& a, const unsigned char* st,
                                           const bf16x8_t (&qf)[QT][D / 32], const int (&tq)[QT],
                                           float (&m)[QT], float (&l)[QT],
-                                          f32x4_t (&o)[QT][D / 16], int b, bool has1, int cq,
-                                          int jq, float sl2) {
+                                          f32x4_t (&o)[QT][D / 16], int b, bool has1,
+                                          bool masked, int cq, int jq, float sl2) {
   constexpr int BLK = 16 * D * 2;
   f32x4_t s0[QT], s1[QT];
 #pragma unroll
@@ -261,7 +267,7 @@ __device__ __forceinline__ void rows_step(const AttnArgs& a, const unsigned char
   bool rescale = false;
 #pragma unroll
   for (int qt = 0; qt < QT; ++qt) {
-    pf[qt] = softmax_pair(a, m[qt], l[qt], s0[qt], s1[qt], b, has1, MASKED, tq[qt], jq, sl2,
+    pf[qt] = softmax_pair(a, m[qt], l[qt], s0[qt], s1[qt], b, has1, masked, tq[qt], jq, sl2,
                           alpha[qt]);
     rescale = rescale || alpha[qt] != 1.f;
   }
@@ -395,10 +401,7 @@ __global__ __launch_bounds__(SHORT ? 256 : 512) void attn_rows_kernel(AttnArgs a
       bool masked = !has1 || block_ntok_s(a, b) != a.g.bt || block_ntok_s(a, b + 1) != a.g.bt;
       if (a.causal) masked = masked || b + 1 >= a.cb0;
 
-      if (masked)
-        rows_step<D, QT, true>(a, st, qf, tq, m, l, o, b, has1, cq, jq, sl2);
-      else
-        rows_step<D, QT, false>(a, st, qf, tq, m, l, o, b, has1, cq, jq, sl2);
+      rows_step<D, QT>(a, st, qf, tq, m, l, o, b, has1, masked, cq, jq, sl2);
     }
   }
 
