@@ -542,9 +542,9 @@ static hipError_t gemm_w4(const GemmArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-// Shapes, measured at the 256-row chunks of the Qwen2.5-1.5B shape: the wide gated
-// projection takes 128 x 128 tiles with 32-deep K steps in a 4-stage ring (one
-// weight read per two 128-row tiles, sharing an XCD's L2); every other
+// Shapes, measured with the weights cold in HBM: the gated projection takes 64 x 128
+// tiles up to 64 rows and 64 x 64 tiles up to 511 rows (64-deep K steps), 128 x 128
+// tiles with 32-deep steps from 512 rows, in a 4-stage ring; every other
 // projection takes 64 x 64 tiles with 64-deep K steps in a 4-stage ring and, when
 // that leaves fewer than about 384 workgroups, splits K (at least 4 steps per
 // split). Split projections reduce their fp32 partials in a second kernel: the
@@ -553,7 +553,11 @@ static hipError_t gemm_bf16(const GemmArgs& a, hipStream_t s) {
   if (a.K % 64 != 0 || a.N % 64 != 0 || a.M < 1) return hipErrorInvalidValue;
   if (a.wf == WF_INT4) return gemm_w4(a, s);
   if (a.epi == EPI_SWIGLU) {
-    if (a.M > 64 && a.N % 128 == 0)
+    // measured with weights cold in HBM: at most 64 rows -> 64 x 128 tiles; up to
+    // 511 rows -> 64 x 64 (64-deep K steps); from 512 rows -> 128 x 128 (32-deep)
+    if (a.M <= 64 && a.N % 128 == 0)
+      gemm_bf16_go<EPI_SWIGLU, 64, 128, 64, 4>(a, 1, a.K / 64, s);
+    else if (a.M >= 512 && a.N % 128 == 0)
       gemm_bf16_go<EPI_SWIGLU, 128, 128, 32, 4>(a, 1, a.K / 32, s);
     else
       gemm_bf16_go<EPI_SWIGLU, 64, 64, 64, 4>(a, 1, a.K / 64, s);
