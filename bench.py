@@ -173,6 +173,19 @@ def gpu_leg(args):
         de[i + 1].record(stream)
     torch.cuda.synchronize()
     per_dec = [de[i].elapsed_time(de[i + 1]) for i in range(DECODES)]
+    # greedy decodes chained on the device (the token never visits the host)
+    chained = []
+    for _ in range(3):
+        m.kv_rollback(ctx_fid)
+        m.prefill_chunk(embeds=chunk, n=CHUNK, stream=sh)
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(DECODES):
+            m.decode_step(vla.VLA_TOKEN_DEVICE, stream=sh, want_token=False)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        chained.append(e0.elapsed_time(e1) / DECODES)
     m.close()
     del chunk
     torch.cuda.synchronize()
@@ -217,6 +230,7 @@ def gpu_leg(args):
             "decode_ms_per_step": round(dec_ms, 4),
             "decode_ms_per_step_median": round(statistics.median(per_dec), 4),
             "decode_ms_per_step_max": round(max(per_dec), 4),
+            "decode_ms_per_step_device_tokens": round(statistics.median(chained), 4),
             "decode_hbm_frac": round(dbytes / (dec_ms * 1e-3) / (PEAK_HBM_GBS * 1e9), 4),
             "decode_bytes_per_step": dbytes,
             "frame_step_ms": round(pre_ms + DECODES * dec_ms, 4),

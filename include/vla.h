@@ -138,8 +138,13 @@ vla_status vla_prefill_chunk(vla_model* m, const int32_t* tokens, const void* em
 /* One decode token at the next position: embedding row `token`, full forward,
  * logits kept, and the greedy next token (argmax over the vocabulary, ties to
  * the lowest id) written to *out_next_token (host, nullable; non-NULL
- * synchronises the stream). Errors: VLA_E_INVALID (token out of range),
+ * synchronises the stream). token VLA_TOKEN_DEVICE: the greedy token of the
+ * previous forward (prefill or decode), read on the device; with
+ * out_next_token NULL nothing synchronises, so greedy decode steps can be
+ * enqueued back to back without a host round trip. Errors: VLA_E_INVALID
+ * (token out of range), VLA_E_STATE (VLA_TOKEN_DEVICE before any forward),
  * VLA_E_NO_BLOCKS (the tail needs a new block and none is free). */
+#define VLA_TOKEN_DEVICE (-1)
 vla_status vla_decode_step(vla_model* m, int32_t token, int32_t* out_next_token, void* stream);
 
 /* Score the resident frames on `layer` and evict the most redundant one

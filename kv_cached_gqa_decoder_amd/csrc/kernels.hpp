@@ -154,8 +154,9 @@ hipError_t launch_action_begin(const float* xa, float* h, int rows, int H, doubl
                                hipStream_t s);
 hipError_t launch_euler_step(float* xa, const float* h, const float* g, int rows, int H,
                              float eps, float dt, hipStream_t s);
-hipError_t launch_embed(const int* tokens, int token_scalar, int n, const void* E, void* x,
-                        int H, int dt, unsigned long long* reset_cell, hipStream_t s);
+hipError_t launch_embed(const int* tokens, int token_scalar, const unsigned long long* token_key,
+                        int n, const void* E, void* x, int H, int dt,
+                        unsigned long long* reset_cell, hipStream_t s);
 hipError_t launch_rmsnorm(const void* x, const float* g, void* u, int rows, int H, float eps,
                           int dt, hipStream_t s);
 hipError_t launch_gemm(const GemmArgs& a, int dt, hipStream_t s);

@@ -232,24 +232,29 @@ hipError_t launch_fill_f32(float* p, float v, int64_t n, hipStream_t s) {
 // embedding rows (activation type) -> fp32 residual rows; block 0 also clears
 // the argmax cell of this pass
 template <typename T>
-__global__ void embed_kernel(const int* tokens, int token_scalar, int n, const T* E, float* x,
-                             int H, unsigned long long* reset_cell) {
+__global__ void embed_kernel(const int* tokens, int token_scalar, const unsigned long long* token_key,
+                             int n, const T* E, float* x, int H, unsigned long long* reset_cell) {
   if (reset_cell && blockIdx.x == 0 && threadIdx.x == 0) *reset_cell = 0ull;
   for (int t = blockIdx.x; t < n; t += gridDim.x) {
-    const int64_t id = tokens ? tokens[t] : token_scalar;
+    // token_key: an argmax key of the output head (the token id is stored as its
+    // complement in the low 32 bits, so that ties go to the lowest id)
+    const int64_t id = tokens      ? tokens[t]
+                       : token_key ? (int64_t)(0xffffffffu - (uint32_t)(*token_key & 0xffffffffull))
+                                   : token_scalar;
     for (int i = threadIdx.x; i < H; i += blockDim.x)
       x[(int64_t)t * H + i] = St<T>::ld(E, id * H + i);
   }
 }
-hipError_t launch_embed(const int* tokens, int token_scalar, int n, const void* E, void* x, int H,
-                        int dt, unsigned long long* reset_cell, hipStream_t s) {
+hipError_t launch_embed(const int* tokens, int token_scalar, const unsigned long long* token_key,
+                        int n, const void* E, void* x, int H, int dt,
+                        unsigned long long* reset_cell, hipStream_t s) {
   const int g = n < 1024 ? n : 1024;
   if (dt == DT_F32)
-    embed_kernel<float><<<g, 256, 0, s>>>(tokens, token_scalar, n, (const float*)E, (float*)x, H,
-                                          reset_cell);
+    embed_kernel<float><<<g, 256, 0, s>>>(tokens, token_scalar, token_key, n, (const float*)E,
+                                          (float*)x, H, reset_cell);
   else
-    embed_kernel<bf16_t><<<g, 256, 0, s>>>(tokens, token_scalar, n, (const bf16_t*)E, (float*)x,
-                                           H, reset_cell);
+    embed_kernel<bf16_t><<<g, 256, 0, s>>>(tokens, token_scalar, token_key, n, (const bf16_t*)E,
+                                           (float*)x, H, reset_cell);
   return hipGetLastError();
 }
 

@@ -733,7 +733,8 @@ vla_status vla_prefill_chunk(vla_model* m, const int32_t* tokens, const void* em
         int* h = (int*)staging_acquire(m->st_tok);
         memcpy(h, tokens, (size_t)n * sizeof(int));
         staging_upload(m->st_tok, m->d_tokens, (size_t)n * sizeof(int), st);
-        HIPCHK(launch_embed(m->d_tokens, 0, n, m->embed, m->x, m->cfg.hidden, m->dt, nullptr, st));
+        HIPCHK(launch_embed(m->d_tokens, 0, nullptr, n, m->embed, m->x, m->cfg.hidden, m->dt,
+                            nullptr, st));
       } else {
         HIPCHK(launch_to_f32(embeds, (float*)m->x, (int64_t)n * m->cfg.hidden, m->dt, st));
       }
@@ -758,7 +759,12 @@ vla_status vla_prefill_chunk(vla_model* m, const int32_t* tokens, const void* em
 vla_status vla_decode_step(vla_model* m, int32_t token, int32_t* out_next_token, void* stream) {
   return guarded([&] {
     if (!m) raise(VLA_E_INVALID, "null model");
-    if (token < 0 || token >= m->cfg.vocab) raise(VLA_E_INVALID, "token id out of range");
+    if (token == VLA_TOKEN_DEVICE) {
+      if (!m->have_logits || m->cfg.vocab == 0)
+        raise(VLA_E_STATE, "no previous forward to take the device-resident token from");
+    } else if (token < 0 || token >= m->cfg.vocab) {
+      raise(VLA_E_INVALID, "token id out of range");
+    }
     HIPCHK(hipSetDevice(m->dev));
     const hipStream_t st = (hipStream_t)stream;
     const int bt = bt_of(m);
@@ -784,7 +790,9 @@ vla_status vla_decode_step(vla_model* m, int32_t token, int32_t* out_next_token,
     try {
       sync_meta(m, st);
       const int cb0 = logical_blocks(m) - 1;
-      HIPCHK(launch_embed(nullptr, token, 1, m->embed, m->x, m->cfg.hidden, m->dt, nullptr, st));
+      // VLA_TOKEN_DEVICE: the previous forward's greedy token, read on the device
+      HIPCHK(launch_embed(nullptr, token, token == VLA_TOKEN_DEVICE ? m->amax_res : nullptr, 1,
+                          m->embed, m->x, m->cfg.hidden, m->dt, nullptr, st));
       run_layers(m, model_view(m), 1, pos, cb0, off % bt, /*decode=*/true, st);
       run_head(m, 0, st);
     } catch (...) {

@@ -19,6 +19,7 @@ VLA_OK, VLA_E_INVALID, VLA_E_NO_BLOCKS, VLA_E_NOTHING_TO_EVICT, VLA_E_HIP, VLA_E
     0, -1, -2, -3, -4, -5
 VLA_F32, VLA_BF16, VLA_INT4_G128 = 0, 1, 2
 VLA_SWIGLU, VLA_GEGLU = 0, 1
+VLA_TOKEN_DEVICE = -1   # decode input: the previous forward's greedy token, on the device
 
 # kernel classes for vla_profile_enable
 K_CLASSES = {

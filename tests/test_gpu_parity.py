@@ -297,3 +297,27 @@ def test_bf16_long_cache_prefill_shape():
         check_argmax(g, ref, "bf16", f"long-cache decode {i}")
         tok = nxt
     m.close()
+
+
+def test_device_resident_tokens_chain_like_host_tokens():
+    """Greedy decoding with the token kept on the device (no host round trip, no
+    synchronisation per step) gives bit-identical logits and the same cache as
+    decoding with host tokens."""
+    p = TINY_BF16
+    x32, xs = synth.embeddings(p["seed"], 3, 50, p["hidden"], "bf16")
+    a, b = _model(p, 0.08), _model(p, 0.08)
+    for m in (a, b):
+        m.prefill_chunk(embeds=dev_from_storage(xs, "bf16"), n=50)
+    tok = int(np.argmax(logits_of(a)))
+    for _ in range(20):
+        tok = a.decode_step(tok)
+        assert b.decode_step(vla.VLA_TOKEN_DEVICE, want_token=False) is None
+    assert np.array_equal(logits_of(a), logits_of(b))
+    assert a.state() == b.state()
+    # the device token needs a previous forward
+    c = _model(p, 0.08)
+    with pytest.raises(vla.VlaError) as e:
+        c.decode_step(vla.VLA_TOKEN_DEVICE)
+    assert e.value.status == vla.VLA_E_STATE and c.state()["n_frames"] == 0
+    for m in (a, b, c):
+        m.close()
