@@ -321,3 +321,72 @@ def test_device_resident_tokens_chain_like_host_tokens():
     assert e.value.status == vla.VLA_E_STATE and c.state()["n_frames"] == 0
     for m in (a, b, c):
         m.close()
+
+
+# ---------------------------------------------------------------------------
+# properties of the GPU path
+def test_mha_config_kv_heads_equal_heads():
+    """Hkv = Hq (no grouping: one query row per KV head and token) against the oracle."""
+    p = dict(TINY_BF16, n_heads=2, n_kv_heads=2, seed=91)
+    ocfg = oracle_config(p, init_std=0.08)
+    sess = D.Session(ocfg)
+    m = _model(p, 0.08)
+    x32, xs = synth.embeddings(p["seed"], 0, 70, p["hidden"], "bf16")
+    m.prefill_chunk(embeds=dev_from_storage(xs, "bf16"), n=70)
+    _, ref = sess.prefill_chunk(embeds=x32)
+    check_logits(logits_of(m), ref, "bf16", "mha prefill")
+    tok = int(np.argmax(ref))
+    for i in range(5):
+        g = m.decode_step(tok)
+        nxt, ref = sess.decode_step(tok)
+        check_logits(logits_of(m), ref, "bf16", f"mha decode {i}")
+        check_argmax(g, ref, "bf16", f"mha decode {i}")
+        tok = nxt
+    m.close()
+
+
+def test_physical_block_placement_is_invisible():
+    """The same frames placed in other physical blocks (a free-list reordered by earlier
+    frames, an eviction and a rollback) give bit-identical logits: every kernel reads the
+    cache in logical order through the block table."""
+    p = TINY_BF16
+    fresh = _model(p, 0.08)
+    moved = _model(p, 0.08)
+    H = p["hidden"]
+    # reorder moved's free-list: frames of various lengths, evict one, roll back
+    junk = [synth.embeddings(77, i, n, H, "bf16")[1] for i, n in enumerate((33, 50, 17))]
+    moved.prefill_chunk(embeds=dev_from_storage(junk[0], "bf16"), n=33)
+    moved.prefill_chunk(embeds=dev_from_storage(junk[1], "bf16"), n=50)
+    moved.prefill_chunk(embeds=dev_from_storage(junk[2], "bf16"), n=17)
+    moved.kv_score_and_evict(0)
+    moved.kv_rollback(-1)
+    assert moved.state()["free_blocks"] == p["num_blocks"]
+    chunks = [synth.embeddings(78, i, n, H, "bf16")[1] for i, n in enumerate((45, 20))]
+    for m in (fresh, moved):
+        for xs in chunks:
+            m.prefill_chunk(embeds=dev_from_storage(xs, "bf16"), n=xs.shape[0])
+    assert not np.array_equal(fresh.block_table()[0], moved.block_table()[0])
+    assert np.array_equal(logits_of(fresh), logits_of(moved))
+    t1 = fresh.decode_step(5)
+    t2 = moved.decode_step(5)
+    assert t1 == t2 and np.array_equal(logits_of(fresh), logits_of(moved))
+    fresh.close()
+    moved.close()
+
+
+def test_chunking_changes_only_rounding():
+    """One 96-token chunk, or the same tokens as 40 + 16 + 40: both match the oracle (which
+    is exactly chunking-invariant) and each other within the bf16 tolerance."""
+    p = dict(TINY_BF16, seed=92)
+    ocfg = oracle_config(p, init_std=0.08)
+    ids = synth.token_ids(p["seed"], 0, 96, p["vocab"])
+    one, three = _model(p, 0.08), _model(p, 0.08)
+    one.prefill_chunk(tokens=ids)
+    for a, b in ((0, 40), (40, 56), (56, 96)):
+        three.prefill_chunk(tokens=ids[a:b])
+    _, ref = D.Session(ocfg).prefill_chunk(tokens=ids)
+    check_logits(logits_of(one), ref, "bf16", "one chunk")
+    check_logits(logits_of(three), ref, "bf16", "three chunks")
+    check_logits(logits_of(three), logits_of(one), "bf16", "three vs one")
+    one.close()
+    three.close()
