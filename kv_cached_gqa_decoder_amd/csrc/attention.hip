@@ -225,37 +225,142 @@ struct RowCfg {
   static_assert(LOADS >= 1 && STAGE % (1024 * WAVES) == 0, "stage split");
 };
 
-// K rows in LDS: 16-byte chunk c of row r sits at chunk position c ^ (r & 15)
-// (within the row: D >= 128 has >= 16 chunks per row; D = 64 uses r & 7)
-template <int D>
-__device__ __forceinline__ int kswz(int r) {
-  return D >= 128 ? (r & 15) : (r & 7);
+// Ring layout of one block pair (K0 K1 V0 V1, one BLK each), chosen so that every
+// LDS read of the loop is one 16-byte load at a fixed offset and every 16 lanes
+// that read together cover 16 distinct 16-byte bank slots.
+//
+// K, chunk-major: the 16-byte chunk c (dims 8c..8c+7) of key r of block w sits
+// at slot c*16 + krow_slot(w, r) (bits 2 and 3 of r swapped, bit 3 flipped for
+// block 1). The S MFMA of half h (0, 1) takes as A-row i the key
+// 8*((i>>2)&1) + 4h + (i&3) of block i>>3; its slot is then i ^ 8h, and the
+// accumulator leaves lane (cq, jq) the scores of keys 8*(jq&1) + 4h + e of
+// block jq>>1: over both halves, 8 consecutive keys of one block.
+__device__ __forceinline__ int swap23(int x) {
+  return (x & ~12) | ((x & 4) << 1) | ((x & 8) >> 1);
+}
+// V^T, row-major as in the pool (dimension vr: 16 keys = two 16-byte halves);
+// the halves of a row trade places when bit 2 xor bit 3 of the row is set.
+__device__ __forceinline__ int vhalf_swz(int vr) { return ((vr >> 2) ^ (vr >> 3)) & 1; }
+
+// Reference maximum of the rows kernel. The base-2 running max m of a query
+// column moves only when a score exceeds it by more than kRefSlack, so most
+// steps skip the column max and the rescale; the probabilities 2^(s*sl2 - m)
+// then stay below 2^kRefSlack (exact in fp32 and bf16 range). m starts at a
+// finite floor so that no step needs a test for infinities: a column with no
+// visible key yet keeps m at the floor, a floor-to-score move rescales by
+// exp2(-huge) = 0, and fully masked lanes give 2^-inf = 0.
+constexpr float kRefSlack = 8.f;
+constexpr float kRefFloor = -1e30f;
+
+__device__ __forceinline__ float max8(const f32x4_t& x, const f32x4_t& y) {
+  // fmaximum: no NaN can occur here (finite scores, -inf for masked keys), and it
+  // maps to v_maximum3_f32 without operand canonicalisation
+  const float a = __builtin_elementwise_maximum(__builtin_elementwise_maximum(x[0], x[1]), x[2]);
+  const float b = __builtin_elementwise_maximum(__builtin_elementwise_maximum(x[3], y[0]), y[1]);
+  return __builtin_elementwise_maximum(__builtin_elementwise_maximum(a, b),
+                                       __builtin_elementwise_maximum(y[2], y[3]));
+}
+
+// sum of the two bf16 values of a packed pair added to acc (v_dot2c_f32_bf16)
+__device__ __forceinline__ float add_bf16x2(uint32_t w, float acc) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  const bf16x2_t one = {(__bf16)1.0f, (__bf16)1.0f};
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w), one, acc, false);
+}
+
+// Online softmax of one block pair for a wavefront's QT row tiles. s0/s1: the
+// raw scores of halves 0 and 1 (lane (cq, jq): keys 8*(jq&1) + 4h + e of block
+// b + (jq>>1)). Leaves the bf16 probabilities as the P^T MFMA operands; l holds
+// per-lane partial sums (the 4 lanes of a column are added at the end).
+template <int D, int QT>
+__device__ __forceinline__ void rows_softmax(const AttnArgs& a, f32x4_t (&s0)[QT],
+                                             f32x4_t (&s1)[QT], float (&m)[QT],
+                                             float (&thr)[QT], float (&l)[QT],
+                                             f32x4_t (&o)[QT][D / 16], bf16x8_t (&pf)[QT],
+                                             const int (&tq)[QT], int b, bool has1, bool masked,
+                                             int jq, float sl2, float isl2) {
+  if (masked) {
+    // visible: slot < ntok, and outside the causal region or at most the row's token
+    const int w = jq >> 1;
+    const int nt0 = block_ntok_s(a, b);
+    const int nt1 = has1 ? block_ntok_s(a, b + 1) : 0;
+    const int nt = w ? nt1 : nt0;
+    const bool open = b + w < a.cb0 || !a.causal;
+    const int k0 = 8 * (jq & 1);
+    const int ck = (b + w - a.cb0) * a.g.bt - a.cslot0 + k0;  // causal index of key k0
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const bool v0 = (k0 + e < nt) & (open | (ck + e <= tq[qt]));
+        const bool v1 = (k0 + 4 + e < nt) & (open | (ck + 4 + e <= tq[qt]));
+        s0[qt][e] = v0 ? s0[qt][e] : -INFINITY;
+        s1[qt][e] = v1 ? s1[qt][e] : -INFINITY;
+      }
+  }
+  float mx[QT];
+  bool need = false;
+#pragma unroll
+  for (int qt = 0; qt < QT; ++qt) {
+    mx[qt] = max8(s0[qt], s1[qt]);
+    need = need || mx[qt] > thr[qt];
+  }
+  if (__any(need)) {  // wave-uniform: move every column's reference to its max
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt) {
+      const float m_new = fmaxf(m[qt], col_max4(mx[qt]) * sl2);
+      const float alpha = __builtin_amdgcn_exp2f(m[qt] - m_new);
+      m[qt] = m_new;
+      thr[qt] = (m_new + kRefSlack) * isl2;
+      l[qt] *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < D / 16; ++dt) o[qt][dt] *= alpha;
+    }
+  }
+#pragma unroll
+  for (int qt = 0; qt < QT; ++qt) {
+    const float nm = -m[qt];
+    u32x4_t pw;
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      pw[e] = pack_bf16x2(__builtin_amdgcn_exp2f(fmaf(s0[qt][2 * e], sl2, nm)),
+                          __builtin_amdgcn_exp2f(fmaf(s0[qt][2 * e + 1], sl2, nm)));
+      pw[2 + e] = pack_bf16x2(__builtin_amdgcn_exp2f(fmaf(s1[qt][2 * e], sl2, nm)),
+                              __builtin_amdgcn_exp2f(fmaf(s1[qt][2 * e + 1], sl2, nm)));
+    }
+    // the running sum adds the rounded probabilities the P*V product uses
+#pragma unroll
+    for (int e = 0; e < 4; ++e) l[qt] = add_bf16x2(pw[e], l[qt]);
+    pf[qt] = __builtin_bit_cast(bf16x8_t, pw);
+  }
 }
 
 // one block pair for a wavefront's QT row tiles: S^T = K Q^T for every tile (each
 // K fragment read once from LDS), the softmax of every tile, then O^T += V^T P^T
-// (each V fragment read once). masked: some key of the pair may be invisible;
-// only the masking itself is conditional, so both cases share one instruction
-// stream (and one register assignment of the running outputs).
+// (each V fragment read once). koff / voff: the lane's K slot of half 0 and V^T
+// slot of dt = 0 inside a stage (byte offsets). masked: some key of the pair may
+// be invisible; only the masking itself is conditional, so both cases share one
+// instruction stream.
 template <int D, int QT>
 __device__ __forceinline__ void rows_step(const AttnArgs& a, const unsigned char* st,
                                           const bf16x8_t (&qf)[QT][D / 32], const int (&tq)[QT],
-                                          float (&m)[QT], float (&l)[QT],
+                                          float (&m)[QT], float (&thr)[QT], float (&l)[QT],
                                           f32x4_t (&o)[QT][D / 16], int b, bool has1,
-                                          bool masked, int cq, int jq, float sl2) {
-  constexpr int BLK = 16 * D * 2;
+                                          bool masked, int koff, int voff, int jq, float sl2,
+                                          float isl2) {
   f32x4_t s0[QT], s1[QT];
 #pragma unroll
   for (int qt = 0; qt < QT; ++qt) {
     s0[qt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     s1[qt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   }
+  const unsigned char* k0p = st + koff;
+  const unsigned char* k1p = st + (koff ^ (8 * 16));  // half 1: slot i ^ 8
 #pragma unroll
   for (int ds = 0; ds < D / 32; ++ds) {
-    const int c = ds * 4 + jq;
-    const int off = cq * (D * 2) + ((c ^ kswz<D>(cq)) << 4);
-    const bf16x8_t k0 = *(const bf16x8_t*)(st + off);
-    const bf16x8_t k1 = *(const bf16x8_t*)(st + BLK + off);
+    // chunk 4*ds + jq: 4 chunks of 16 slots further per ds
+    const bf16x8_t k0 = *(const bf16x8_t*)(k0p + ds * 1024);
+    const bf16x8_t k1 = *(const bf16x8_t*)(k1p + ds * 1024);
 #pragma unroll
     for (int qt = 0; qt < QT; ++qt) {
       s0[qt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, qf[qt][ds], s0[qt], 0, 0, 0);
@@ -263,28 +368,12 @@ __device__ __forceinline__ void rows_step(const AttnArgs& a, const unsigned char
     }
   }
   bf16x8_t pf[QT];
-  float alpha[QT];
-  bool rescale = false;
-#pragma unroll
-  for (int qt = 0; qt < QT; ++qt) {
-    pf[qt] = softmax_pair(a, m[qt], l[qt], s0[qt], s1[qt], b, has1, masked, tq[qt], jq, sl2,
-                          alpha[qt]);
-    rescale = rescale || alpha[qt] != 1.f;
-  }
-  // the running outputs only change scale when some column's maximum rose
-  if (__any(rescale)) {
-#pragma unroll
-    for (int qt = 0; qt < QT; ++qt)
-#pragma unroll
-      for (int dt = 0; dt < D / 16; ++dt) o[qt][dt] *= alpha[qt];
-  }
+  rows_softmax<D, QT>(a, s0, s1, m, thr, l, o, pf, tq, b, has1, masked, jq, sl2, isl2);
+  const unsigned char* vp = st + voff;
 #pragma unroll
   for (int dt = 0; dt < D / 16; ++dt) {
-    // V^T rows: dim dt*16 + cq, keys 4jq..4jq+3 of block 0 then of block 1
-    const int voff = (dt * 16 + cq) * 32 + (((jq >> 1) ^ ((cq >> 3) & 1)) << 4) + (jq & 1) * 8;
-    const u32x2_t lo = *(const u32x2_t*)(st + 2 * BLK + voff);
-    const u32x2_t hi = *(const u32x2_t*)(st + 3 * BLK + voff);
-    const bf16x8_t vf = __builtin_bit_cast(bf16x8_t, u32x4_t{lo[0], lo[1], hi[0], hi[1]});
+    // V^T row dt*16 + cq: keys 8*(jq&1)..+7 of block jq>>1, the order of P^T
+    const bf16x8_t vf = *(const bf16x8_t*)(vp + dt * 512);
 #pragma unroll
     for (int qt = 0; qt < QT; ++qt)
       o[qt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf[qt], o[qt][dt], 0, 0, 0);
@@ -308,11 +397,12 @@ __global__ __launch_bounds__(SHORT ? 256 : 512) void attn_rows_kernel(AttnArgs a
   const int splits = a.splits;
   const int kvh = u / splits, split = u % splits;
 
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int jq = lane >> 4, cq = lane & 15;
   const int grp = a.hq / a.g.hkv;
   const int R = a.n * grp;
-  const float sl2 = a.scale * kLog2e;
+  const float sl2 = a.scale * kLog2e, isl2 = 1.f / sl2;
 
   // this wavefront's query tiles: rows rg*ROWS + wave*QT*16 + qt*16 + cq
   bf16x8_t qf[QT][D / 32];
@@ -341,11 +431,12 @@ __global__ __launch_bounds__(SHORT ? 256 : 512) void attn_rows_kernel(AttnArgs a
   }
   const int np = b_end > b_begin ? (b_end - b_begin + 1) / 2 : 0;
 
-  float m[QT], l[QT];
+  float m[QT], thr[QT], l[QT];
   f32x4_t o[QT][D / 16];
 #pragma unroll
   for (int qt = 0; qt < QT; ++qt) {
-    m[qt] = -INFINITY;
+    m[qt] = kRefFloor;
+    thr[qt] = (kRefFloor + kRefSlack) * isl2;
     l[qt] = 0.f;
 #pragma unroll
     for (int dt = 0; dt < D / 16; ++dt) o[qt][dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -354,6 +445,27 @@ __global__ __launch_bounds__(SHORT ? 256 : 512) void attn_rows_kernel(AttnArgs a
   if (np > 0) {
     const unsigned char* kp = (const unsigned char*)a.kpool;
     const unsigned char* vp = (const unsigned char*)a.vpool;
+    // DMA: each wavefront moves LOADS 1 KB pieces of a stage; lane `lane` of a
+    // piece fills slot part*64 + lane of its block, so its source offset inside
+    // the block is fixed for the whole loop (the block base is wave-uniform)
+    uint32_t doff[C::LOADS];
+#pragma unroll
+    for (int j = 0; j < C::LOADS; ++j) {
+      const int q = wave * C::LOADS + j;
+      const int which = q / (C::BLK / 1024), part = q % (C::BLK / 1024);
+      const int ls = part * 64 + lane;  // 16-byte slot inside the block
+      if (which < 2) {
+        const int r = swap23((ls & 15) ^ (which << 3));
+        doff[j] = r * (D * 2) + (ls >> 4) * 16;
+      } else {
+        const int vr = ls >> 1;
+        doff[j] = vr * 32 + (((ls & 1) ^ vhalf_swz(vr)) << 4);
+      }
+    }
+    // the lane's read slots: K of half 0 (block cq>>3, chunk jq, slot cq), and
+    // V^T of dt = 0 (block jq>>1, row cq)
+    const int koff = (cq >> 3) * C::BLK + (jq * 16 + cq) * 16;
+    const int voff = (2 + (jq >> 1)) * C::BLK + (2 * cq + ((jq & 1) ^ vhalf_swz(cq))) * 16;
     // stage p -> ring slot p % NS; past the last pair the DMA re-loads it (every
     // step then issues the same loads and every wait has one depth)
     auto issue = [&](int p) {
@@ -368,21 +480,11 @@ __global__ __launch_bounds__(SHORT ? 256 : 512) void attn_rows_kernel(AttnArgs a
         const int which = q / (C::BLK / 1024);        // 0 K0, 1 K1, 2 V0, 3 V1
         const int part = q % (C::BLK / 1024);
         const int pb = (which & 1) ? pb1 : pb0;
-        const int pos = part * 64 + lane;             // 16-byte chunk inside the block
-        size_t src;
-        if (which < 2) {
-          const int r = pos / C::CPR, pc = pos % C::CPR;
-          src = (size_t)a.g.kidx(a.layer, pb, kvh, 0, 0) * 2 + (size_t)r * (D * 2) +
-                ((pc ^ kswz<D>(r)) << 4);
-        } else {
-          // V^T row vr (one dim, 16 keys = two 16-byte halves); the halves swap
-          // places on bit 3 of the row, against bank conflicts of the P*V reads
-          const int vr = pos >> 1;
-          src = (size_t)a.g.vidx(a.layer, pb, kvh, 0, 0) * 2 + (size_t)vr * 32 +
-                (((pos & 1) ^ ((vr >> 3) & 1)) << 4);
-        }
+        const unsigned char* base =
+            which < 2 ? kp + a.g.kidx(a.layer, pb, kvh, 0, 0) * 2
+                      : vp + a.g.vidx(a.layer, pb, kvh, 0, 0) * 2;
         __builtin_amdgcn_global_load_lds(
-            (const void*)((which < 2 ? kp : vp) + src),
+            (const void*)(base + doff[j]),
             (__attribute__((address_space(3))) void*)(st + which * C::BLK + part * 1024), 16, 0,
             0);
       }
@@ -401,9 +503,11 @@ __global__ __launch_bounds__(SHORT ? 256 : 512) void attn_rows_kernel(AttnArgs a
       bool masked = !has1 || block_ntok_s(a, b) != a.g.bt || block_ntok_s(a, b + 1) != a.g.bt;
       if (a.causal) masked = masked || b + 1 >= a.cb0;
 
-      rows_step<D, QT>(a, st, qf, tq, m, l, o, b, has1, masked, cq, jq, sl2);
+      rows_step<D, QT>(a, st, qf, tq, m, thr, l, o, b, has1, masked, koff, voff, jq, sl2, isl2);
     }
   }
+#pragma unroll
+  for (int qt = 0; qt < QT; ++qt) l[qt] = col_sum4(l[qt]);
 
   // results: the output rows directly, or this split's partial (m, l, o)
   const int tile = kvh * rgroups + rg;
