@@ -466,44 +466,73 @@ __global__ __launch_bounds__(SHORT ? 256 : 512) void attn_rows_kernel(AttnArgs a
     // V^T of dt = 0 (block jq>>1, row cq)
     const int koff = (cq >> 3) * C::BLK + (jq * 16 + cq) * 16;
     const int voff = (2 + (jq >> 1)) * C::BLK + (2 * cq + ((jq & 1) ^ vhalf_swz(cq))) * 16;
-    // stage p -> ring slot p % NS; past the last pair the DMA re-loads it (every
+    // block bases: one layer's K (V) blocks of this KV head lie bstride bytes apart
+    const unsigned char* kb = kp + a.g.kidx(a.layer, 0, kvh, 0, 0) * 2;
+    const unsigned char* vb = vp + a.g.vidx(a.layer, 0, kvh, 0, 0) * 2;
+    const uint32_t bstride = (uint32_t)a.g.hkv * a.g.bt * D * 2;
+    // physical blocks of pair p; past the last pair the DMA re-loads it (every
     // step then issues the same loads and every wait has one depth)
-    auto issue = [&](int p) {
+    auto ids = [&](int p, int& pb0, int& pb1) {
       const int pd = p < np ? p : np - 1;
       const int b = b_begin + 2 * pd;
-      const int pb0 = uniform_ld(a.blk_table, b);
-      const int pb1 = uniform_ld(a.blk_table, b + 1 < b_end ? b + 1 : b);
+      pb0 = uniform_ld(a.blk_table, b);
+      pb1 = uniform_ld(a.blk_table, b + 1 < b_end ? b + 1 : b);
+    };
+    // pair p (< np) has a key that may be invisible: a missing or partial block,
+    // or a block in the causal region
+    // (both table entries read unconditionally, from indices inside the table, so
+    // that no branch waits on a load)
+    auto pair_masked = [&](int p) {
+      const int b = b_begin + 2 * p;
+      const int b1 = min(b + 1, a.nlb - 1);
+      const int t0 = uniform_ld(a.blk_ntok, b), t1 = uniform_ld(a.blk_ntok, b1);
+      const int n0 = b == a.nlb - 1 ? a.last_ntok : t0;
+      const int n1 = b1 == a.nlb - 1 ? a.last_ntok : t1;
+      bool mk = (b + 1 >= b_end) | (n0 != a.g.bt) | (n1 != a.g.bt);
+      if (a.causal) mk = mk | (b + 1 >= a.cb0);
+      return mk;
+    };
+    // stage p -> ring slot p % NS
+    auto issue = [&](int p, int pb0, int pb1) {
       unsigned char* st = smem + (p % NS) * C::STAGE;
 #pragma unroll
       for (int j = 0; j < C::LOADS; ++j) {
         const int q = wave * C::LOADS + j;            // 1 KB piece of the stage
         const int which = q / (C::BLK / 1024);        // 0 K0, 1 K1, 2 V0, 3 V1
         const int part = q % (C::BLK / 1024);
-        const int pb = (which & 1) ? pb1 : pb0;
-        const unsigned char* base =
-            which < 2 ? kp + a.g.kidx(a.layer, pb, kvh, 0, 0) * 2
-                      : vp + a.g.vidx(a.layer, pb, kvh, 0, 0) * 2;
+        const uint32_t pb = (which & 1) ? pb1 : pb0;
+        const unsigned char* base = (which < 2 ? kb : vb) + (size_t)pb * bstride;
         __builtin_amdgcn_global_load_lds(
             (const void*)(base + doff[j]),
             (__attribute__((address_space(3))) void*)(st + which * C::BLK + part * 1024), 16, 0,
             0);
       }
     };
+    int pb0, pb1;
 #pragma unroll
-    for (int p0 = 0; p0 < NS - 1; ++p0) issue(p0);
+    for (int p0 = 0; p0 < NS - 1; ++p0) {
+      ids(p0, pb0, pb1);
+      issue(p0, pb0, pb1);
+    }
+    // the scalars a step needs (the blocks its DMA fetches, whether it masks) are
+    // requested one step ahead, so their latency is hidden behind a whole step
+    ids(NS - 1, pb0, pb1);
+    bool mk_next = pair_masked(0);
 
     for (int p = 0; p < np; ++p) {
       wait_vmcnt_steps<C::LOADS>(NS - 2);
       asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-      issue(p + NS - 1);
+      issue(p + NS - 1, pb0, pb1);
       const unsigned char* st = smem + (p % NS) * C::STAGE;
       const int b = b_begin + 2 * p;
       const bool has1 = b + 1 < b_end;
-      // every key of the pair visible: both blocks full, none in the causal region
-      bool masked = !has1 || block_ntok_s(a, b) != a.g.bt || block_ntok_s(a, b + 1) != a.g.bt;
-      if (a.causal) masked = masked || b + 1 >= a.cb0;
+      const bool masked = mk_next;
 
       rows_step<D, QT>(a, st, qf, tq, m, thr, l, o, b, has1, masked, koff, voff, jq, sl2, isl2);
+      // after this step's LDS reads, so that their waits do not include these loads
+      __builtin_amdgcn_sched_barrier(0);
+      ids(p + NS, pb0, pb1);
+      mk_next = pair_masked(min(p + 1, np - 1));
     }
   }
 #pragma unroll
