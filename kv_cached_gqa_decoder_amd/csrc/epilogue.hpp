@@ -14,16 +14,32 @@ namespace vla {
 // pairing), read from the pass's (cos, sin) table; q goes to the query buffer,
 // k and v to the paged pool at the token's block and slot (the cache stores
 // post-RoPE keys).
+// The pair's operands that do not depend on the projection (its rotation and,
+// for k/v heads, the physical block of the token), so a kernel can request them
+// before its sums are ready.
+struct QkvPre {
+  float2 cs = {1.f, 0.f};
+  int blk = 0;
+};
+__device__ __forceinline__ QkvPre epi_qkv_prefetch(const FwdCtx& c, int t, int col) {
+  QkvPre p;
+  const int d = c.g.d;
+  const int head = col / d;
+  const int j = (col % d) >> 1;
+  if (head < c.hq + c.g.hkv) p.cs = c.rope[(size_t)t * (d / 2) + j];
+  if (head >= c.hq) p.blk = c.blk_table[c.cb0 + (c.cslot0 + t) / c.g.bt];
+  return p;
+}
 template <typename T>
-__device__ __forceinline__ void epi_qkv_pair(const FwdCtx& c, int t, int col, float lo, float hi) {
+__device__ __forceinline__ void epi_qkv_store(const FwdCtx& c, int t, int col, const QkvPre& p,
+                                              float lo, float hi) {
   const int d = c.g.d;
   const int head = col / d;
   const int j = (col % d) >> 1;
   const int hkv = c.g.hkv;
   if (head < c.hq + hkv) {
-    const float2 cs = c.rope[(size_t)t * (d / 2) + j];
-    const float rlo = lo * cs.x - hi * cs.y;
-    const float rhi = hi * cs.x + lo * cs.y;
+    const float rlo = lo * p.cs.x - hi * p.cs.y;
+    const float rhi = hi * p.cs.x + lo * p.cs.y;
     lo = rlo;
     hi = rhi;
   }
@@ -33,20 +49,22 @@ __device__ __forceinline__ void epi_qkv_pair(const FwdCtx& c, int t, int col, fl
     St<T>::st(q, j + d / 2, hi);
     return;
   }
-  const int ls = c.cslot0 + t;
-  const int b = c.blk_table[c.cb0 + ls / c.g.bt];
-  const int s = ls % c.g.bt;
+  const int s = (c.cslot0 + t) % c.g.bt;
   if (head < c.hq + hkv) {
     const int h = head - c.hq;
     T* kp = (T*)c.kpool;
-    St<T>::st(kp, c.g.kidx(c.layer, b, h, s, j), lo);
-    St<T>::st(kp, c.g.kidx(c.layer, b, h, s, j + d / 2), hi);
+    St<T>::st(kp, c.g.kidx(c.layer, p.blk, h, s, j), lo);
+    St<T>::st(kp, c.g.kidx(c.layer, p.blk, h, s, j + d / 2), hi);
   } else {
     const int h = head - c.hq - hkv;
     T* vp = (T*)c.vpool;
-    St<T>::st(vp, c.g.vidx(c.layer, b, h, s, j), lo);
-    St<T>::st(vp, c.g.vidx(c.layer, b, h, s, j + d / 2), hi);
+    St<T>::st(vp, c.g.vidx(c.layer, p.blk, h, s, j), lo);
+    St<T>::st(vp, c.g.vidx(c.layer, p.blk, h, s, j + d / 2), hi);
   }
+}
+template <typename T>
+__device__ __forceinline__ void epi_qkv_pair(const FwdCtx& c, int t, int col, float lo, float hi) {
+  epi_qkv_store<T>(c, t, col, epi_qkv_prefetch(c, t, col), lo, hi);
 }
 
 // order-preserving map of an fp32 value to uint32 (larger float -> larger key)

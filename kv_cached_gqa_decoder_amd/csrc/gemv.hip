@@ -173,6 +173,174 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(GemvArgs a, int ngro
   }
 }
 
+// One-shot decode GEMV, bf16 weights. Every wavefront requests all it needs at
+// once -- the chunks of its rows, the matching input chunks (and RMSNorm gains),
+// the epilogue's RoPE operands -- so the kernel costs one memory round trip and
+// no workgroup barrier before its weights arrive. KS = 1: a wavefront owns a
+// group of RW rows and whole rows of CPL chunks per lane; it then holds the whole
+// input row across its lanes, so the RMSNorm statistic is a wavefront sum.
+// KS = 4 (residual projections with long rows): the workgroup owns RW rows and
+// its 4 wavefronts split K; their sums meet in LDS and are added in wavefront
+// order.
+template <int EPI, int RW, int CPL, int KS>
+__global__ __launch_bounds__(kGemvThreads) void gemv1_kernel(GemvArgs a, int ngroups) {
+  static_assert(KS == 1 || (KS == kGemvWaves && EPI == EPI_RESID), "K split: residual inputs only");
+  __shared__ float part[kGemvWaves][RW];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int g = KS == 1 ? blockIdx.x * kGemvWaves + wave : blockIdx.x;
+  const bool live = g < ngroups;  // wave-uniform
+  const int K = a.K, nch = K / 8;
+  const int q = KS == 1 ? nch : (nch + KS - 1) / KS;  // chunks of this wavefront's K range
+  const int cbeg = KS == 1 ? 0 : wave * q;
+  const int cend = min(nch, cbeg + q);
+
+  const bf16_t* W = (const bf16_t*)a.W;
+  u32x4_t w[CPL][RW];
+#pragma unroll
+  for (int r = 0; r < RW; ++r) {
+    const int64_t row = live ? gemv_row<EPI, RW>(g, r) : 0;
+    const bf16_t* wr = W + (row < a.N ? row : (int64_t)a.N - 1) * K;
+#pragma unroll
+    for (int u = 0; u < CPL; ++u) {
+      const int c = cbeg + lane + 64 * u;
+      w[u][r] = live && c < cend ? *(const u32x4_t*)(wr + (size_t)c * 8) : u32x4_t{0, 0, 0, 0};
+    }
+  }
+  float xv[CPL][8];
+  if constexpr (EPI != EPI_RESID) {
+    // the fp32 residual row (and the RMSNorm gains): 8 values per chunk
+    const f32x4_t* xf4 = (const f32x4_t*)a.x;
+    const f32x4_t* g4 = (const f32x4_t*)a.norm_g;
+    f32x4_t xr[CPL][2], gr[CPL][2];
+#pragma unroll
+    for (int u = 0; u < CPL; ++u) {
+      const int c = lane + 64 * u;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        xr[u][h] = c < nch ? xf4[2 * c + h] : f32x4_t{0.f, 0.f, 0.f, 0.f};
+        gr[u][h] = a.norm_g && c < nch ? g4[2 * c + h] : f32x4_t{0.f, 0.f, 0.f, 0.f};
+      }
+    }
+    float rn = 1.f;
+    if (a.norm_g) {
+      float ss = 0.f;
+#pragma unroll
+      for (int u = 0; u < CPL; ++u)
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) ss += xr[u][h][e] * xr[u][h][e];
+      rn = rsqrtf(wave_sum(ss) / (float)K + a.eps);
+    }
+#pragma unroll
+    for (int u = 0; u < CPL; ++u)
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          xv[u][4 * h + e] = a.norm_g ? xr[u][h][e] * rn * gr[u][h][e] : xr[u][h][e];
+  } else {
+    const bf16_t* x = (const bf16_t*)a.x;
+#pragma unroll
+    for (int u = 0; u < CPL; ++u) {
+      const int c = cbeg + lane + 64 * u;
+      const u32x4_t v = c < cend ? *(const u32x4_t*)(x + (size_t)c * 8) : u32x4_t{0, 0, 0, 0};
+      unpack8(v, xv[u]);
+    }
+  }
+  QkvPre pre;
+  if constexpr (EPI == EPI_QKV) {
+    if (live && lane < RW / 2) pre = epi_qkv_prefetch(a.ctx, 0, (int)gemv_row<EPI, RW>(g, 2 * lane));
+  }
+
+  float acc[RW];
+#pragma unroll
+  for (int r = 0; r < RW; ++r) {
+    acc[r] = 0.f;
+#pragma unroll
+    for (int u = 0; u < CPL; ++u) {
+      float wf[8];
+      unpack8(w[u][r], wf);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[r] += wf[i] * xv[u][i];
+    }
+    acc[r] = wave_sum(acc[r]);
+  }
+  if constexpr (KS > 1) {
+    if (lane == 0)
+#pragma unroll
+      for (int r = 0; r < RW; ++r) part[wave][r] = acc[r];
+    __syncthreads();
+    if (wave != 0) return;
+#pragma unroll
+    for (int r = 0; r < RW; ++r) {
+      float t = part[0][r];
+#pragma unroll
+      for (int v = 1; v < KS; ++v) t += part[v][r];
+      acc[r] = t;
+    }
+  }
+  if (!live) return;
+
+  if constexpr (EPI == EPI_QKV) {
+#pragma unroll
+    for (int p = 0; p < RW / 2; ++p)
+      if (lane == p)
+        epi_qkv_store<bf16_t>(a.ctx, 0, (int)gemv_row<EPI, RW>(g, 2 * p), pre, acc[2 * p],
+                              acc[2 * p + 1]);
+  } else if constexpr (EPI == EPI_RESID) {
+#pragma unroll
+    for (int r = 0; r < RW; ++r) {
+      const int64_t row = gemv_row<EPI, RW>(g, r);
+      if (lane == r && row < a.N) ((float*)a.out)[row] += acc[r];
+    }
+  } else if constexpr (EPI == EPI_SWIGLU) {
+#pragma unroll
+    for (int i = 0; i < RW / 2; ++i)
+      if (lane == i)
+        St<bf16_t>::st((bf16_t*)a.out, g * (RW / 2) + i, glu_act(a.glu, acc[i], acc[RW / 2 + i]));
+  }
+}
+
+template <int EPI, int RW, int CPL, int KS>
+static hipError_t gemv1_go(const GemvArgs& a, hipStream_t s, int* grid_out) {
+  const int ngroups = (EPI == EPI_SWIGLU) ? a.N / RW : (a.N + RW - 1) / RW;
+  const int grid = KS == 1 ? (ngroups + kGemvWaves - 1) / kGemvWaves : ngroups;
+  if (grid_out) *grid_out = grid;
+  launch_k(gemv1_kernel<EPI, RW, CPL, KS>, dim3(grid), dim3(kGemvThreads), 0, s, a, ngroups);
+  return hipGetLastError();
+}
+
+// Shapes of the one-shot kernel: whole rows of up to 4 chunks per lane (K <= 2048)
+// two rows per wavefront; residual rows up to 8 chunks per lane per wavefront of
+// a K split (K <= 16384), one row per workgroup. Returns false when K fits neither.
+template <int EPI>
+static bool gemv1_launch(const GemvArgs& a, hipStream_t s, int* grid_out, hipError_t* err) {
+  const int nch = a.K / 8;
+  const int cpl = (nch + 63) / 64;
+  if (cpl <= 4) {
+    switch (cpl) {
+      case 1: *err = gemv1_go<EPI, 2, 1, 1>(a, s, grid_out); return true;
+      case 2: *err = gemv1_go<EPI, 2, 2, 1>(a, s, grid_out); return true;
+      case 3: *err = gemv1_go<EPI, 2, 3, 1>(a, s, grid_out); return true;
+      case 4: *err = gemv1_go<EPI, 2, 4, 1>(a, s, grid_out); return true;
+    }
+  }
+  if constexpr (EPI == EPI_RESID) {
+    const int ks = ((nch + kGemvWaves - 1) / kGemvWaves + 63) / 64;
+    switch (ks) {
+      case 2: *err = gemv1_go<EPI, 1, 2, kGemvWaves>(a, s, grid_out); return true;
+      case 3: *err = gemv1_go<EPI, 1, 3, kGemvWaves>(a, s, grid_out); return true;
+      case 4: *err = gemv1_go<EPI, 1, 4, kGemvWaves>(a, s, grid_out); return true;
+      case 5: *err = gemv1_go<EPI, 1, 5, kGemvWaves>(a, s, grid_out); return true;
+      case 6: *err = gemv1_go<EPI, 1, 6, kGemvWaves>(a, s, grid_out); return true;
+      case 7: *err = gemv1_go<EPI, 1, 7, kGemvWaves>(a, s, grid_out); return true;
+      case 8: *err = gemv1_go<EPI, 1, 8, kGemvWaves>(a, s, grid_out); return true;
+    }
+  }
+  return false;
+}
+
 template <typename T, int EPI, int RW>
 static hipError_t gemv_launch_rw(const GemvArgs& a, hipStream_t s, int* grid_out) {
   // rows of the residual and head projections may end in a partial group
@@ -193,6 +361,10 @@ static hipError_t gemv_launch(const GemvArgs& a, hipStream_t s, int* grid_out) {
     if (a.N % 8) return hipErrorInvalidValue;
   } else if constexpr (EPI == EPI_SWIGLU) {
     if (a.N % 32) return hipErrorInvalidValue;
+  }
+  if constexpr (sizeof(T) == 2 && EPI != EPI_HEAD) {
+    hipError_t err;
+    if (gemv1_launch<EPI>(a, s, grid_out, &err)) return err;
   }
   if (a.N / 8 >= 2048) return gemv_launch_rw<T, EPI, 8>(a, s, grid_out);
   if (a.N / 4 >= 1024) return gemv_launch_rw<T, EPI, 4>(a, s, grid_out);
