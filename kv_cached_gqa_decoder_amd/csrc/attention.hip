@@ -792,11 +792,11 @@ static void attn_rows_go(const AttnArgs& a, int rgroups, hipStream_t s) {
 
 // shape: 0 decode, 1 rows (short cache), 2 rows (long cache)
 template <int D>
-static void attn_bf16_go(const AttnArgs& a, int shape, int rgroups, hipStream_t s) {
+static void attn_bf16_go(const AttnArgs& a, int shape, int rgroups, hipStream_t s, bool fold) {
   if (shape == 0) {
     launch_k(attn_decode_kernel<D>, dim3(a.splits, rgroups, a.g.hkv), dim3(kAttnWaves * 64), 0, s,
              a, rgroups);
-    attn_merge_go<D, 16>(a, rgroups, s);
+    if (!fold) attn_merge_go<D, 16>(a, rgroups, s);
   } else if (shape == 1) {
     attn_rows_go<D, true>(a, rgroups, s);
   } else {
@@ -809,7 +809,8 @@ static int rows_per_group(int shape) {
   return shape == 0 ? 16 : shape == 1 ? RowCfg<D, true>::ROWS : RowCfg<D, false>::ROWS;
 }
 
-hipError_t launch_attention(const AttnArgs& args, int dt, hipStream_t s) {
+hipError_t launch_attention(const AttnArgs& args, int dt, hipStream_t s, int* fold_splits) {
+  if (fold_splits) *fold_splits = 0;
   if (args.nlb <= 0 || args.n <= 0) return hipErrorInvalidValue;
   if (dt == DT_F32) {
     if (args.nlb * args.g.bt > kF32MaxKeys) return hipErrorInvalidValue;
@@ -845,10 +846,14 @@ hipError_t launch_attention(const AttnArgs& args, int dt, hipStream_t s) {
   if (a.splits > 1 &&
       (a.part_o == nullptr || a.part_ml == nullptr || (size_t)base * rows * a.splits > (size_t)a.part_rows))
     return hipErrorInvalidValue;
+  // one-token decode with few splits: the consumer merges the partials
+  const bool fold = fold_splits && shape == 0 && a.n == 1 && a.splits > 1 &&
+                    a.splits <= kFoldMaxSplits && a.hq <= kFoldMaxHeads;
+  if (fold) *fold_splits = a.splits;
   switch (d) {
-    case 64: attn_bf16_go<64>(a, shape, rgroups, s); break;
-    case 128: attn_bf16_go<128>(a, shape, rgroups, s); break;
-    default: attn_bf16_go<256>(a, shape, rgroups, s); break;
+    case 64: attn_bf16_go<64>(a, shape, rgroups, s, fold); break;
+    case 128: attn_bf16_go<128>(a, shape, rgroups, s, fold); break;
+    default: attn_bf16_go<256>(a, shape, rgroups, s, fold); break;
   }
   return hipGetLastError();
 }

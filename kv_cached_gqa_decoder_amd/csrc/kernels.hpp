@@ -105,7 +105,18 @@ struct GemvArgs {
   void* out = nullptr;          // RESID fp32 x[N] (+=); SWIGLU act[N/2]; HEAD logits fp32[N]
   unsigned long long* argmax_part = nullptr;  // HEAD: one key per workgroup
   FwdCtx ctx;
+  // RESID with part_o set: the input row is the one-token decode attention
+  // output, given as its split partials (launch_attention with a fold request),
+  // part_o [unit][16][hd], part_ml [unit][2][16], unit = kv head * splits + split;
+  // grp query heads per KV head, K = heads * hd
+  const float* part_o = nullptr;
+  const float* part_ml = nullptr;
+  int splits = 0, grp = 0, hd = 0;
 };
+
+// limits of the decode attention merge folded into the output projection
+constexpr int kFoldMaxSplits = 16;
+constexpr int kFoldMaxHeads = 16;
 
 struct AttnArgs {
   const void* q = nullptr;   // [n][Hq][d]
@@ -163,7 +174,12 @@ hipError_t launch_gemm(const GemmArgs& a, int dt, hipStream_t s);
 hipError_t launch_gemv(const GemvArgs& a, int dt, hipStream_t s, int* grid_out);
 hipError_t launch_argmax_final(const unsigned long long* part, int nparts,
                                unsigned long long* result, hipStream_t s);
-hipError_t launch_attention(const AttnArgs& a, int dt, hipStream_t s);
+// fold_splits non-null (one-token decode): when the key splits would need the
+// merge kernel and their count is within kFoldMaxSplits, the merge is left to
+// the consumer and *fold_splits receives the split count (the partials are in
+// a.part_o / a.part_ml); otherwise the output is written as usual and
+// *fold_splits is 0.
+hipError_t launch_attention(const AttnArgs& a, int dt, hipStream_t s, int* fold_splits = nullptr);
 hipError_t launch_kv_scatter(const void* k, const void* v, int n, void* kpool, void* vpool,
                              KvGeom g, const int* blk_table, int cb0, int dt, hipStream_t s);
 hipError_t launch_kv_gather(const void* kpool, const void* vpool, KvGeom g, int layer,

@@ -366,7 +366,12 @@ void run_layers(vla_model* m, const KvView& view, int n, int64_t pos0, int cb0, 
       g.ctx = ctx;
       LAUNCH(m, VLA_K_GEMV_QKV, st, launch_gemv(g, m->dt, st, nullptr));
       if (kv_only) break;
-      LAUNCH(m, VLA_K_ATTN_DECODE, st, launch_attention(at, m->dt, st));
+      // bf16 output projections of up to 2048 inputs take the attention's
+      // split partials directly (no merge kernel)
+      const bool can_fold = m->dt == DT_BF16 && m->wf == WF_ACT && qd <= 2048;
+      int fold_splits = 0;
+      LAUNCH(m, VLA_K_ATTN_DECODE, st,
+             launch_attention(at, m->dt, st, can_fold ? &fold_splits : nullptr));
       GemvArgs o;
       o.x = m->ao;
       o.W = m->wo[l];
@@ -375,6 +380,13 @@ void run_layers(vla_model* m, const KvView& view, int n, int64_t pos0, int cb0, 
       o.K = qd;
       o.epi = EPI_RESID;
       o.out = m->x;
+      if (fold_splits > 0) {
+        o.part_o = m->part_o;
+        o.part_ml = m->part_ml;
+        o.splits = fold_splits;
+        o.grp = c.n_heads / c.n_kv_heads;
+        o.hd = c.head_dim;
+      }
       LAUNCH(m, VLA_K_GEMV_O, st, launch_gemv(o, m->dt, st, nullptr));
       GemvArgs gu;
       gu.x = m->x;
