@@ -622,43 +622,56 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(AttnArgs a, int rgroup
     attn_step(a, st, qf, cur, b, b + 1 < b_end, tq, jq, sl2);
     cur = nxt;
   }
-  // merge the 4 wavefronts' states through LDS
+  // merge the 4 wavefronts' states through LDS: the row weights 2^(m_w - M) and
+  // the row sums first (one thread per row), then the rows' elements; rows past
+  // the pass's query rows are padding and are neither merged nor stored
   float* Lo = smem;                          // [wave][16][D]
   float* Lml = Lo + kAttnWaves * 16 * D;     // [wave][2][16]
+  __shared__ float wts[kAttnWaves][16], rowM[16], rowL[16];
+  const int nrow = min(ROWS, R - rg * ROWS);  // real rows of this tile
+  if (cq < nrow) {
 #pragma unroll
-  for (int dt = 0; dt < D / 16; ++dt)
+    for (int dt = 0; dt < D / 16; ++dt)
 #pragma unroll
-    for (int e = 0; e < 4; ++e) Lo[(wave * 16 + cq) * D + dt * 16 + 4 * jq + e] = st.o[dt][e];
-  if (jq == 0) {
-    Lml[wave * 32 + cq] = st.m;
-    Lml[wave * 32 + 16 + cq] = st.l;
+      for (int e = 0; e < 4; ++e) Lo[(wave * 16 + cq) * D + dt * 16 + 4 * jq + e] = st.o[dt][e];
+    if (jq == 0) {
+      Lml[wave * 32 + cq] = st.m;
+      Lml[wave * 32 + 16 + cq] = st.l;
+    }
   }
   __syncthreads();
-  const int unit = (kvh * rgroups + rg) * splits + split;
-  for (int e = threadIdx.x; e < 16 * D; e += kAttnWaves * 64) {
-    const int c = e / D, dim = e % D;
+  if (threadIdx.x < nrow) {
+    const int c = threadIdx.x;
     float M = -INFINITY;
 #pragma unroll
     for (int w = 0; w < kAttnWaves; ++w) M = fmaxf(M, Lml[w * 32 + c]);
-    float L = 0.f, acc = 0.f;
-    if (M != -INFINITY) {
+    float L = 0.f;
 #pragma unroll
-      for (int w = 0; w < kAttnWaves; ++w) {
-        const float mw_ = Lml[w * 32 + c];
-        const float wt = mw_ == -INFINITY ? 0.f : exp2f(mw_ - M);
-        L += wt * Lml[w * 32 + 16 + c];
-        acc += wt * Lo[(w * 16 + c) * D + dim];
-      }
+    for (int w = 0; w < kAttnWaves; ++w) {
+      const float mw_ = Lml[w * 32 + c];
+      const float wt = (M == -INFINITY || mw_ == -INFINITY) ? 0.f : exp2f(mw_ - M);
+      wts[w][c] = wt;
+      L += wt * Lml[w * 32 + 16 + c];
     }
+    rowM[c] = M;
+    rowL[c] = L;
+  }
+  __syncthreads();
+  const int unit = (kvh * rgroups + rg) * splits + split;
+  for (int e = threadIdx.x; e < nrow * D; e += kAttnWaves * 64) {
+    const int c = e / D, dim = e % D;
+    float acc = 0.f;
+#pragma unroll
+    for (int w = 0; w < kAttnWaves; ++w) acc += wts[w][c] * Lo[(w * 16 + c) * D + dim];
+    const float L = rowL[c];
     const int rr = rg * 16 + c;
     if (splits == 1) {
-      if (rr < R)
-        ((bf16_t*)a.out)[((size_t)(rr / grp) * a.hq + kvh * grp + rr % grp) * D + dim] =
-            f32_to_bf16(L > 0.f ? acc / L : 0.f);
+      ((bf16_t*)a.out)[((size_t)(rr / grp) * a.hq + kvh * grp + rr % grp) * D + dim] =
+          f32_to_bf16(L > 0.f ? acc / L : 0.f);
     } else {
       a.part_o[((size_t)unit * 16 + c) * D + dim] = acc;
       if (dim == 0) {
-        a.part_ml[(size_t)unit * 32 + c] = M;
+        a.part_ml[(size_t)unit * 32 + c] = rowM[c];
         a.part_ml[(size_t)unit * 32 + 16 + c] = L;
       }
     }
