@@ -145,7 +145,6 @@ def gpu_leg(args):
     torch.cuda.synchronize()
 
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
-    m.profile_enable("gemv_gateup")
     log(f"[bench] timing {args.steps} steps")
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -153,8 +152,12 @@ def gpu_leg(args):
         step(evs[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    gu_ms, gu_n = m.profile_read()
-    m.profile_enable(0)
+    # the roofline kernel (decode gate/up GEMV): replayed over the 28 layers' weights
+    # back to back between two stream events, on the decode state of the last step
+    # (events in each dispatch would lengthen a 12 us kernel by about 1.3 us)
+    gu_reps = 8
+    gu_avg = m.profile_replay("gemv_gateup", reps=gu_reps, stream=sh)
+    gu_n = gu_reps * L
 
     pre = [e[0].elapsed_time(e[1]) for e in evs]
     dec = [e[1].elapsed_time(e[2]) / DECODES for e in evs]
@@ -196,7 +199,6 @@ def gpu_leg(args):
 
     fl = prefill_flops()
     dbytes = decode_bytes(CONTEXT + CHUNK + DECODES // 2)
-    gu_avg = gu_ms / max(gu_n, 1)
     gu_gbs = gateup_bytes() / (gu_avg * 1e-3) / 1e9
     kernel_src = os.path.join(ROOT, "kv_cached_gqa_decoder_amd", "csrc", "gemv.hip")
     traffic = read_traffic(kernel_src)

@@ -249,6 +249,17 @@ enum {
 vla_status vla_profile_enable(vla_model* m, int32_t kernel_class);
 vla_status vla_profile_read(vla_model* m, double* total_ms, int32_t* launches);
 
+/* Kernel timing by replay, for kernels too short to carry events of their own
+ * without changing their duration: launches the one-token projection of
+ * `kernel_class` for every layer, `reps` times, back to back on `stream`
+ * between two stream events, synchronises, and returns the mean time per
+ * launch (ms) in *ms_per_launch. Only VLA_K_GEMV_GATEUP (the gated FFN
+ * projection of a decode step): it reads the residual row and rewrites only
+ * the FFN activation scratch, so the model's state and results are unchanged.
+ * Errors: VLA_E_INVALID (other class, reps outside 1..1000, no gated layer). */
+vla_status vla_profile_replay(vla_model* m, int32_t kernel_class, int32_t reps, void* stream,
+                              double* ms_per_launch);
+
 /* Action expert of a pi0-style policy ("Running VLAs at Real-time Speed",
  * section 2: a vision-language prefix model plus an expert that predicts an
  * action chunk by flow matching). The expert is a decoder of its own (cfg:

@@ -14,27 +14,28 @@
 //   S^T = K Q^T        v_mfma_f32_16x16x32_bf16, A = 16 keys x 32 dims (K rows),
 //                      B = Q^T held in registers for the whole loop; the
 //                      accumulator gives each lane 4 keys of one query.
-//   online softmax     per query column: in-lane max/sum + 2 cross-lane steps,
-//                      in base 2 (scores pre-multiplied by log2 e / sqrt(d)).
+//   online softmax     per query column, in base 2 (scores times log2 e / sqrt(d)).
 //   O^T += V^T P^T     A = V^T (the pool stores V transposed inside a block, so
-//                      4 consecutive keys of one dimension are contiguous),
+//                      consecutive keys of one dimension are contiguous),
 //                      B = P^T, which is exactly the lane's own probabilities.
 // Two kernels:
 //   decode (<= 16 query rows): 4 wavefronts share one row tile and take
 //     interleaved block pairs straight from memory (one pair prefetched); their
 //     partial (m, l, o) are merged through LDS.
 //   rows (prefill): 8 wavefronts, each owning 2 row tiles (1 at d = 256), so a
-//     workgroup covers 256 (128) rows; every block pair goes through a 3-stage
-//     LDS ring filled by direct-to-LDS DMA (16 bytes per lane; K rows and V^T
-//     rows swizzled in 16-byte chunks against bank conflicts) and is read by all
-//     rows of the workgroup. Workgroups are numbered so that all row tiles of
-//     one (KV head, key split) run on one XCD and stream the same blocks
-//     through its L2.
+//     workgroup covers 256 (128) rows; every block pair goes through a 3-4 stage
+//     LDS ring filled by direct-to-LDS DMA and is read by all rows of the
+//     workgroup. Its softmax keeps a lazy reference max and per-lane row sums,
+//     and its ring layout lets every operand read be one 16-byte load (see the
+//     layout and softmax comments below). Workgroups are numbered so that all
+//     row tiles of one (KV head, key split) run on one XCD and stream the same
+//     blocks through its L2.
 // The resident blocks are split over workgroups (split-K). Each workgroup
 // writes its partial (m, l, o); a second kernel merges the splits in split
-// order (deterministic). Merging inside the first kernel would need an
-// agent-scope release/acquire per workgroup, which on this chip writes back
-// and invalidates the whole L2 of the workgroup's XCD.
+// order (deterministic) -- or, for one-token decode with few splits, the output
+// projection merges them as it reads its input. Merging inside the first
+// kernel would need an agent-scope release/acquire per workgroup, which on
+// this chip writes back and invalidates the whole L2 of the workgroup's XCD.
 #include <algorithm>
 
 #include "common.hpp"

@@ -317,6 +317,24 @@ FwdCtx make_ctx(vla_model* m, const KvView& v, int layer, int cb0, int cslot0) {
   return c;
 }
 
+// one-token gated projection of layer l: the normalised residual row -> the
+// FFN activations (decode, and its timing replay)
+GemvArgs decode_gateup_args(vla_model* m, int l) {
+  const vla_config& c = m->cfg;
+  GemvArgs gu;
+  gu.x = m->x;
+  gu.norm_g = m->norm_ones;
+  gu.eps = c.rms_eps;
+  gu.W = m->wgu[l];
+  gu.wf = m->wf;
+  gu.N = 2 * c.ffn;
+  gu.K = c.hidden;
+  gu.epi = EPI_SWIGLU;
+  gu.glu = c.ffn_kind == VLA_GEGLU ? 1 : 0;
+  gu.out = m->act;
+  return gu;
+}
+
 // the per-layer launches of one pass over n rows whose K/V go to logical slots
 // (cb0, cslot0 ...); rows = prefill chunk (n >= 1, matrix path) or decode (GEMV path)
 void run_layers(vla_model* m, const KvView& view, int n, int64_t pos0, int cb0, int cslot0,
@@ -388,18 +406,7 @@ void run_layers(vla_model* m, const KvView& view, int n, int64_t pos0, int cb0, 
         o.hd = c.head_dim;
       }
       LAUNCH(m, VLA_K_GEMV_O, st, launch_gemv(o, m->dt, st, nullptr));
-      GemvArgs gu;
-      gu.x = m->x;
-      gu.norm_g = m->norm_ones;
-      gu.eps = c.rms_eps;
-      gu.W = m->wgu[l];
-      gu.wf = m->wf;
-      gu.N = 2 * c.ffn;
-      gu.K = H;
-      gu.epi = EPI_SWIGLU;
-      gu.glu = glu;
-      gu.out = m->act;
-      LAUNCH(m, VLA_K_GEMV_GATEUP, st, launch_gemv(gu, m->dt, st, nullptr));
+      LAUNCH(m, VLA_K_GEMV_GATEUP, st, launch_gemv(decode_gateup_args(m, l), m->dt, st, nullptr));
       GemvArgs dn;
       dn.x = m->act;
       dn.W = m->wdown[l];
@@ -1082,6 +1089,33 @@ vla_status vla_profile_enable(vla_model* m, int32_t kernel_class) {
     m->prof_cls = kernel_class;
     m->prof.used = 0;
     m->prof.calls = 0;
+  });
+}
+
+vla_status vla_profile_replay(vla_model* m, int32_t kernel_class, int32_t reps, void* stream,
+                              double* ms_per_launch) {
+  return guarded([&] {
+    if (!m) raise(VLA_E_INVALID, "null model");
+    if (kernel_class != VLA_K_GEMV_GATEUP) raise(VLA_E_INVALID, "replay: gated projection only");
+    if (m->cfg.n_layers < 1 || m->cfg.ffn < 1) raise(VLA_E_INVALID, "model has no gated projection");
+    if (reps < 1 || reps > 1000) raise(VLA_E_INVALID, "reps out of range");
+    const hipStream_t st = (hipStream_t)stream;
+    // the K/V-only last layer of a prefix model has no FFN
+    const int nl = m->cfg.kv_only_last ? m->cfg.n_layers - 1 : m->cfg.n_layers;
+    if (nl < 1) raise(VLA_E_INVALID, "model has no gated projection");
+    hipEvent_t e0, e1;
+    HIPCHK(hipEventCreate(&e0));
+    HIPCHK(hipEventCreate(&e1));
+    HIPCHK(hipEventRecord(e0, st));
+    for (int r = 0; r < reps; ++r)
+      for (int l = 0; l < nl; ++l) HIPCHK(launch_gemv(decode_gateup_args(m, l), m->dt, st, nullptr));
+    HIPCHK(hipEventRecord(e1, st));
+    HIPCHK(hipEventSynchronize(e1));
+    float ms = 0.f;
+    HIPCHK(hipEventElapsedTime(&ms, e0, e1));
+    HIPCHK(hipEventDestroy(e0));
+    HIPCHK(hipEventDestroy(e1));
+    if (ms_per_launch) *ms_per_launch = (double)ms / ((double)reps * nl);
   });
 }
 

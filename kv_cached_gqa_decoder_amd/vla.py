@@ -78,6 +78,7 @@ _SIGS = {
     "vla_weight_out": (c_int32, [c_void_p, c_int32, c_int32, c_void_p, c_int64, c_void_p]),
     "vla_profile_enable": (c_int32, [c_void_p, c_int32]),
     "vla_profile_read": (c_int32, [c_void_p, POINTER(c_double), POINTER(c_int32)]),
+    "vla_profile_replay": (c_int32, [c_void_p, c_int32, c_int32, c_void_p, POINTER(c_double)]),
     "vla_expert_create": (c_int32, [c_void_p, POINTER(vla_config), c_int32, POINTER(c_void_p)]),
     "vla_expert_destroy": (None, [c_void_p]),
     "vla_expert_denoise": (c_int32, [c_void_p, c_void_p, c_int32, c_double, c_void_p]),
@@ -247,6 +248,12 @@ def vla_profile_read(m: int):
     ms, n = c_double(0.0), c_int32(0)
     _check(load().vla_profile_read(m, byref(ms), byref(n)))
     return ms.value, n.value
+
+
+def vla_profile_replay(m: int, kernel_class: int, reps: int, stream=None) -> float:
+    ms = c_double(0.0)
+    _check(load().vla_profile_replay(m, kernel_class, reps, _stream(stream), byref(ms)))
+    return ms.value
 
 
 def vla_expert_create(prefix: int, cfg: vla_config, n_actions: int) -> int:
@@ -422,6 +429,11 @@ class Model:
 
     def profile_read(self):
         return vla_profile_read(self.h)
+
+    def profile_replay(self, kernel_class, reps=4, stream=None):
+        """Mean ms per launch of `kernel_class` replayed over all layers, back to back."""
+        return vla_profile_replay(self.h, K_CLASSES.get(kernel_class, kernel_class)
+                                  if isinstance(kernel_class, str) else kernel_class, reps, stream)
 
 
 class Expert:

@@ -241,6 +241,31 @@ def test_rollback_repeats_bit_identically():
     m.close()
 
 
+def test_profile_replay_leaves_results_unchanged():
+    """Replaying the decode gate/up projection for timing changes no result: decodes
+    after a replay give bit-identical logits and tokens to decodes without one; other
+    classes and out-of-range repeat counts are refused."""
+    p = TINY_BF16
+    runs = []
+    for replay in (False, True):
+        m = _model(p, 0.08)
+        _, xs = synth.embeddings(6, 0, 40, p["hidden"], "bf16")
+        m.prefill_chunk(embeds=dev_from_storage(xs, "bf16"), n=40)
+        toks = [m.decode_step(7)]
+        if replay:
+            ms = m.profile_replay("gemv_gateup", reps=3)
+            assert ms > 0.0
+            for bad in (("gemv_o", 3), ("gemv_gateup", 0), ("gemv_gateup", 1001)):
+                with pytest.raises(vla.VlaError) as err:
+                    m.profile_replay(bad[0], reps=bad[1])
+                assert err.value.status == vla.VLA_E_INVALID
+        for _ in range(4):
+            toks.append(m.decode_step(toks[-1]))
+        runs.append((logits_of(m), toks))
+        m.close()
+    assert np.array_equal(runs[0][0], runs[1][0]) and runs[0][1] == runs[1][1]
+
+
 # ---------------------------------------------------------------------------
 def test_bf16_long_context_split_attention():
     """A 1,920-token cached context (30 raw frames, 120 blocks) so that both the
