@@ -679,59 +679,83 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(AttnArgs a, int rgroup
   }
 }
 
-// Combines the splits of one query row of one (KV head, row group) tile: with
+// Combines the splits of query rows of one (KV head, row group) tile: with
 // per-split running max m_s (base 2), sum l_s and unnormalised o_s,
 // o = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s, M = max_s m_s. One
-// workgroup per row: the weights 2^(m_s - M) go to LDS first, then 256 / D
-// groups of threads sum interleaved splits for one dim each (independent loads,
-// many in flight) and the groups are added in group order (deterministic).
+// wavefront per row, D/64 dims per lane; the splits go in chunks (32 splits, 16
+// at d = 256 where a split carries 4 values per lane) whose loads are all issued
+// together (one memory round trip per chunk), with
+// a running max across chunks (the sums are rescaled when it rises). Splits
+// are added in order, so the result is deterministic. No LDS, no barrier.
 constexpr int kMaxSplits = 128;
 
 template <int D, int ROWS>
 __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a, int rgroups) {
-  constexpr int G = 256 / D;  // split groups
-  static_assert(G >= 1 && 256 % D == 0, "head dim");
-  __shared__ float wgt[kMaxSplits];
-  __shared__ float red[256];
-  __shared__ float wred[4];
-  const int tile = blockIdx.x;  // kvh * rgroups + rg
-  const int c = blockIdx.y;     // row inside the tile
+  constexpr int V = D / 64;  // dims per lane
+  constexpr int kMergeChunk = V >= 4 ? 16 : 32;
+  static_assert(V >= 1 && D % 64 == 0 && ROWS % 4 == 0, "head dim, rows");
+  const int tile = blockIdx.x;                                  // kvh * rgroups + rg
+  const int c = blockIdx.y * 4 + (int)(threadIdx.x >> 6);       // row inside the tile
+  const int lane = threadIdx.x & 63;
   const int rg = tile % rgroups, kvh = tile / rgroups;
   const int grp = a.hq / a.g.hkv;
   const int rr = rg * ROWS + c;
-  if (rr >= a.n * grp) return;  // uniform over the workgroup
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  if (rr >= a.n * grp) return;  // wave-uniform; no barrier follows
   const int splits = a.splits;
   const size_t u0 = (size_t)tile * splits;
 
-  // M = max over splits (splits <= 128 < 256: one value per thread at most)
-  float m = tid < splits ? a.part_ml[(u0 + tid) * 2 * ROWS + c] : -INFINITY;
-  float mw = wave_max(m);
-  if (lane == 0) wred[wave] = mw;
-  __syncthreads();
-  const float M = fmaxf(fmaxf(wred[0], wred[1]), fmaxf(wred[2], wred[3]));
-  const float w = (tid < splits && m != -INFINITY) ? exp2f(m - M) : 0.f;
-  if (tid < splits) wgt[tid] = w;
-  // L = sum_s w_s l_s, reduced in a fixed order
-  float lw = tid < splits ? w * a.part_ml[(u0 + tid) * 2 * ROWS + ROWS + c] : 0.f;
-  lw = wave_sum(lw);
-  __syncthreads();  // wred reads done; wgt visible
-  if (lane == 0) wred[wave] = lw;
-  const int dim = tid % D, g = tid / D;
-  float acc = 0.f;
-#pragma unroll 8
-  for (int sp = g; sp < splits; sp += G)
-    acc += wgt[sp] * a.part_o[((u0 + sp) * ROWS + c) * D + dim];
-  red[tid] = acc;
-  __syncthreads();
-  if (g == 0) {
-    float tot = acc;
+  float M = -INFINITY, L = 0.f;
+  float acc[V];
 #pragma unroll
-    for (int k = 1; k < G; ++k) tot += red[k * D + dim];
-    const float L = (wred[0] + wred[1]) + (wred[2] + wred[3]);
-    ((bf16_t*)a.out)[((size_t)(rr / grp) * a.hq + kvh * grp + rr % grp) * D + dim] =
-        f32_to_bf16(M != -INFINITY && L > 0.f ? tot / L : 0.f);
+  for (int v = 0; v < V; ++v) acc[v] = 0.f;
+  for (int s0 = 0; s0 < splits; s0 += kMergeChunk) {
+    float mv[kMergeChunk], lv[kMergeChunk], ov[kMergeChunk][V];
+#pragma unroll
+    for (int j = 0; j < kMergeChunk; ++j) {
+      const int sp = s0 + j;
+      mv[j] = -INFINITY;
+      lv[j] = 0.f;
+#pragma unroll
+      for (int v = 0; v < V; ++v) ov[j][v] = 0.f;
+      if (sp < splits) {  // wave-uniform
+        const size_t u = u0 + sp;
+        mv[j] = a.part_ml[u * 2 * ROWS + c];
+        lv[j] = a.part_ml[u * 2 * ROWS + ROWS + c];
+        const float* po = a.part_o + (u * ROWS + c) * D + lane * V;
+        if constexpr (V == 4) {
+          const f32x4_t q = *(const f32x4_t*)po;
+#pragma unroll
+          for (int v = 0; v < 4; ++v) ov[j][v] = q[v];
+        } else if constexpr (V == 2) {
+          const float2 q = *(const float2*)po;
+          ov[j][0] = q.x;
+          ov[j][1] = q.y;
+        } else {
+          ov[j][0] = po[0];
+        }
+      }
+    }
+    float Mc = M;
+#pragma unroll
+    for (int j = 0; j < kMergeChunk; ++j) Mc = fmaxf(Mc, mv[j]);
+    if (Mc != -INFINITY) {
+      const float sc = M == -INFINITY ? 0.f : exp2f(M - Mc);  // earlier chunks to the new max
+      L *= sc;
+#pragma unroll
+      for (int v = 0; v < V; ++v) acc[v] *= sc;
+#pragma unroll
+      for (int j = 0; j < kMergeChunk; ++j) {
+        const float w = mv[j] == -INFINITY ? 0.f : exp2f(mv[j] - Mc);
+        L += w * lv[j];
+#pragma unroll
+        for (int v = 0; v < V; ++v) acc[v] += w * ov[j][v];
+      }
+      M = Mc;
+    }
   }
+  bf16_t* orow = (bf16_t*)a.out + ((size_t)(rr / grp) * a.hq + kvh * grp + rr % grp) * D + lane * V;
+#pragma unroll
+  for (int v = 0; v < V; ++v) orow[v] = f32_to_bf16(M != -INFINITY && L > 0.f ? acc[v] / L : 0.f);
 }
 
 // ---------------------------------------------------------------------------
@@ -791,7 +815,7 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(AttnArgs a) {
 template <int D, int ROWS>
 static void attn_merge_go(const AttnArgs& a, int rgroups, hipStream_t s) {
   if (a.splits > 1)
-    launch_k(attn_merge_kernel<D, ROWS>, dim3(a.g.hkv * rgroups, ROWS), dim3(256), 0, s, a,
+    launch_k(attn_merge_kernel<D, ROWS>, dim3(a.g.hkv * rgroups, ROWS / 4), dim3(256), 0, s, a,
              rgroups);
 }
 
