@@ -681,34 +681,40 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(AttnArgs a, int rgroup
 
 // Combines the splits of query rows of one (KV head, row group) tile: with
 // per-split running max m_s (base 2), sum l_s and unnormalised o_s,
-// o = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s, M = max_s m_s. One
-// wavefront per row, D/64 dims per lane; the splits go in chunks (32 splits, 16
-// at d = 256 where a split carries 4 values per lane) whose loads are all issued
-// together (one memory round trip per chunk), with
-// a running max across chunks (the sums are rescaled when it rises). Splits
-// are added in order, so the result is deterministic. No LDS, no barrier.
+// o = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s, M = max_s m_s. D/64 dims per
+// lane; splits go in chunks (32 splits, 16 at d = 256 where a split carries 4
+// values per lane) whose loads are all issued together (one memory round trip
+// per chunk), with a running max across chunks (the sums are rescaled when it
+// rises). WAVES = 1: one wavefront per row, no LDS, no barrier. WAVES = 4 (many
+// splits, few rows: long-context decode): the 4 wavefronts of a workgroup take
+// consecutive quarters of one row's splits and are combined through LDS in
+// wavefront order. Splits are added in order, so the result is deterministic.
 constexpr int kMaxSplits = 128;
 
-template <int D, int ROWS>
+template <int D, int ROWS, int WAVES>
 __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a, int rgroups) {
   constexpr int V = D / 64;  // dims per lane
   constexpr int kMergeChunk = V >= 4 ? 16 : 32;
-  static_assert(V >= 1 && D % 64 == 0 && ROWS % 4 == 0, "head dim, rows");
-  const int tile = blockIdx.x;                                  // kvh * rgroups + rg
-  const int c = blockIdx.y * 4 + (int)(threadIdx.x >> 6);       // row inside the tile
-  const int lane = threadIdx.x & 63;
+  static_assert(V >= 1 && D % 64 == 0 && ROWS % 4 == 0 && (WAVES == 1 || WAVES == 4), "shape");
+  __shared__ float comb[WAVES == 4 ? 4 : 1][64][V + 2];
+  const int tile = blockIdx.x;  // kvh * rgroups + rg
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int c = WAVES == 1 ? (int)blockIdx.y * 4 + wave : (int)blockIdx.y;  // row inside the tile
   const int rg = tile % rgroups, kvh = tile / rgroups;
   const int grp = a.hq / a.g.hkv;
   const int rr = rg * ROWS + c;
-  if (rr >= a.n * grp) return;  // wave-uniform; no barrier follows
+  if (rr >= a.n * grp) return;  // uniform over the row's wavefronts (all of a workgroup at WAVES 4)
   const int splits = a.splits;
+  const int per = (splits + WAVES - 1) / WAVES;
+  const int sb = WAVES == 1 ? 0 : min(splits, wave * per);
+  const int se = WAVES == 1 ? splits : min(splits, sb + per);
   const size_t u0 = (size_t)tile * splits;
 
   float M = -INFINITY, L = 0.f;
   float acc[V];
 #pragma unroll
   for (int v = 0; v < V; ++v) acc[v] = 0.f;
-  for (int s0 = 0; s0 < splits; s0 += kMergeChunk) {
+  for (int s0 = sb; s0 < se; s0 += kMergeChunk) {
     float mv[kMergeChunk], lv[kMergeChunk], ov[kMergeChunk][V];
 #pragma unroll
     for (int j = 0; j < kMergeChunk; ++j) {
@@ -717,7 +723,7 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a, int rgroups
       lv[j] = 0.f;
 #pragma unroll
       for (int v = 0; v < V; ++v) ov[j][v] = 0.f;
-      if (sp < splits) {  // wave-uniform
+      if (sp < se) {  // wave-uniform
         const size_t u = u0 + sp;
         mv[j] = a.part_ml[u * 2 * ROWS + c];
         lv[j] = a.part_ml[u * 2 * ROWS + ROWS + c];
@@ -752,6 +758,31 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a, int rgroups
       }
       M = Mc;
     }
+  }
+  if constexpr (WAVES == 4) {
+    comb[wave][lane][0] = M;
+    comb[wave][lane][1] = L;
+#pragma unroll
+    for (int v = 0; v < V; ++v) comb[wave][lane][2 + v] = acc[v];
+    __syncthreads();
+    if (wave != 0) return;
+    float Mt = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) Mt = fmaxf(Mt, comb[w][lane][0]);
+    L = 0.f;
+#pragma unroll
+    for (int v = 0; v < V; ++v) acc[v] = 0.f;
+    if (Mt != -INFINITY) {
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const float mw = comb[w][lane][0];
+        const float sc = mw == -INFINITY ? 0.f : exp2f(mw - Mt);
+        L += sc * comb[w][lane][1];
+#pragma unroll
+        for (int v = 0; v < V; ++v) acc[v] += sc * comb[w][lane][2 + v];
+      }
+    }
+    M = Mt;
   }
   bf16_t* orow = (bf16_t*)a.out + ((size_t)(rr / grp) * a.hq + kvh * grp + rr % grp) * D + lane * V;
 #pragma unroll
@@ -814,8 +845,13 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(AttnArgs a) {
 
 template <int D, int ROWS>
 static void attn_merge_go(const AttnArgs& a, int rgroups, hipStream_t s) {
-  if (a.splits > 1)
-    launch_k(attn_merge_kernel<D, ROWS>, dim3(a.g.hkv * rgroups, ROWS / 4), dim3(256), 0, s, a,
+  if (a.splits <= 1) return;
+  // more than 32 splits (long-context decode): 4 wavefronts per row
+  if (a.splits > 32)
+    launch_k(attn_merge_kernel<D, ROWS, 4>, dim3(a.g.hkv * rgroups, ROWS), dim3(256), 0, s, a,
+             rgroups);
+  else
+    launch_k(attn_merge_kernel<D, ROWS, 1>, dim3(a.g.hkv * rgroups, ROWS / 4), dim3(256), 0, s, a,
              rgroups);
 }
 
