@@ -18,54 +18,99 @@
 
 namespace vla {
 
-// one lane per V consecutive dims (8 or 16 bytes) of one (frame, layer): the
-// frame's tokens are added in token order (the same order for every dim and
-// every run), two blocks (32 tokens) of loads in flight per step
+// one lane per V consecutive dims (8 or 16 bytes) of one (frame, layer); the 4
+// wavefronts of a workgroup take the frame's blocks round-robin, one block (16
+// token loads per lane) per step, the next step's block id requested before the
+// current step's keys are added; few registers, so many workgroups are resident. fp64 sums of bf16 or fp32
+// keys are exact here, so the 4 partial sums (added through LDS) give the same
+// table whatever the split.
 template <typename T, int V>
 struct KeyVec {
   static_assert(V * sizeof(T) == 8 || V * sizeof(T) == 16, "8- or 16-byte loads");
   using type = typename std::conditional<V * sizeof(T) == 16, u32x4_t, u32x2_t>::type;
 };
 
+// element e of a loaded key vector (bf16 pairs or fp32 words), without going
+// through memory
+template <typename T, typename W>
+__device__ __forceinline__ float key_elem(const W& w, int e) {
+  if constexpr (sizeof(T) == 2)
+    return __uint_as_float((e & 1) ? (w[e >> 1] & 0xffff0000u) : (w[e >> 1] << 16));
+  else
+    return __uint_as_float(w[e]);
+}
+
+typedef const __attribute__((address_space(4))) int* mk_const_int_p;
+__device__ __forceinline__ int mk_uniform_ld(const int* p, int i) {
+  return ((mk_const_int_p)(const void*)p)[i];
+}
+
 template <typename T, int V>
-__global__ __launch_bounds__(64) void meankeys_kernel(const T* kp, KvGeom g, const int* blk_table,
-                                                      const int* fr_blk0, const int* fr_nblk,
-                                                      const int* fr_ntok, const int* fr_slot,
-                                                      int layer0, double* table, int max_frames) {
+__global__ __launch_bounds__(256) void meankeys_kernel(const T* kp, KvGeom g, const int* blk_table,
+                                                       const int* fr_blk0, const int* fr_nblk,
+                                                       const int* fr_ntok, const int* fr_slot,
+                                                       int layer0, double* table, int max_frames) {
   using W = typename KeyVec<T, V>::type;
+  constexpr int BPS = 1;  // blocks per wavefront step: few registers, many resident wavefronts
+  __shared__ double red[4][64][V];
   const int f = blockIdx.x;
   const int layer = layer0 + blockIdx.y;
   const int D = g.hkv * g.d;
-  const int i0 = (blockIdx.z * 64 + threadIdx.x) * V;  // first dim of this lane
-  if (i0 >= D) return;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int i0 = min((int)(blockIdx.z * 64 + lane) * V, D - V);  // first dim of this lane
   const int h = i0 / g.d, dd = i0 % g.d;
-  const int blk0 = fr_blk0[f], nblk = fr_nblk[f], ntok = fr_ntok[f];
+  const int blk0 = mk_uniform_ld(fr_blk0, f), nblk = mk_uniform_ld(fr_nblk, f);
+  const int ntok = mk_uniform_ld(fr_ntok, f);
+  const int mine = nblk > wave ? (nblk - 1 - wave) / 4 + 1 : 0;  // this wavefront's blocks
   double acc[V];
 #pragma unroll
   for (int e = 0; e < V; ++e) acc[e] = 0.0;
-  for (int k = 0; k < nblk; k += 2) {
-    W w[2][16];
+  // block i of this wavefront: frame block wave + 4 i (ids past `mine` re-read a valid one)
+  auto ids = [&](int i0b, int (&b)[BPS]) {
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int kk = k + j < nblk ? k + j : k;
-      const int b = blk_table[blk0 + kk];
-#pragma unroll
-      for (int sl = 0; sl < 16; ++sl) w[j][sl] = *(const W*)(kp + g.kidx(layer, b, h, sl, dd));
+    for (int j = 0; j < BPS; ++j) {
+      const int i = min(i0b + j, mine - 1);
+      b[j] = mk_uniform_ld(blk_table, blk0 + wave + 4 * i);
     }
+  };
+  int bcur[BPS], bnext[BPS];
+  if (mine > 0) ids(0, bcur);
+  for (int i = 0; i < mine; i += BPS) {
+    W w[BPS][16];
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      if (k + j >= nblk) break;
-      const int nt = min(g.bt, ntok - (k + j) * g.bt);
+    for (int j = 0; j < BPS; ++j) {
+      if (i + j < mine) {  // wave-uniform: only this wavefront's own blocks
 #pragma unroll
-      for (int sl = 0; sl < 16; ++sl) {
-        if (sl >= nt) break;
-        const T* v = (const T*)&w[j][sl];
+        for (int sl = 0; sl < 16; ++sl) w[j][sl] = *(const W*)(kp + g.kidx(layer, bcur[j], h, sl, dd));
+      } else {
 #pragma unroll
-        for (int e = 0; e < V; ++e) acc[e] += (double)St<T>::ld(v, e);
+        for (int sl = 0; sl < 16; ++sl) w[j][sl] = W{};
       }
     }
+    if (i + BPS < mine) ids(i + BPS, bnext);
+    // valid tokens of each block (0 past this wavefront's blocks); predicated adds,
+    // no loop exits, so the loaded vectors stay in registers
+#pragma unroll
+    for (int j = 0; j < BPS; ++j) {
+      const int kb = wave + 4 * (i + j);
+      const int nt = i + j < mine ? min(g.bt, ntok - kb * g.bt) : 0;
+#pragma unroll
+      for (int sl = 0; sl < 16; ++sl) {
+        const bool on = sl < nt;
+#pragma unroll
+        for (int e = 0; e < V; ++e) acc[e] += on ? (double)key_elem<T>(w[j][sl], e) : 0.0;
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < BPS; ++j) bcur[j] = bnext[j];
   }
-  double* out = table + ((size_t)layer * max_frames + fr_slot[f]) * D + i0;
+#pragma unroll
+  for (int e = 0; e < V; ++e) red[wave][lane][e] = acc[e];
+  __syncthreads();
+  if (wave != 0 || (int)(blockIdx.z * 64 + lane) * V >= D) return;
+#pragma unroll
+  for (int e = 0; e < V; ++e) acc[e] = ((red[0][lane][e] + red[1][lane][e]) + red[2][lane][e]) + red[3][lane][e];
+  double* out = table + ((size_t)layer * max_frames + mk_uniform_ld(fr_slot, f)) * D + i0;
 #pragma unroll
   for (int e = 0; e < V; ++e) out[e] = acc[e] / (double)ntok;
 }
@@ -76,7 +121,7 @@ static void meankeys_go(const void* kpool, KvGeom g, const int* blk_table, const
                         int layer0, int nlayers, double* table, int max_frames, hipStream_t s) {
   const int D = g.hkv * g.d;
   dim3 grid(nframes, nlayers, (D / V + 63) / 64);
-  launch_k(meankeys_kernel<T, V>, grid, dim3(64), 0, s, (const T*)kpool, g, blk_table, fr_blk0,
+  launch_k(meankeys_kernel<T, V>, grid, dim3(256), 0, s, (const T*)kpool, g, blk_table, fr_blk0,
            fr_nblk, fr_ntok, fr_slot, layer0, table, max_frames);
 }
 
