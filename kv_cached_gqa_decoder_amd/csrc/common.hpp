@@ -90,6 +90,19 @@ __device__ __forceinline__ float glu_act(int glu, float gate, float up) {
   return (glu ? gelu_erf(gate) : silu(gate)) * up;
 }
 
+// gated activation with the hardware exp2 and reciprocal (no IEEE divide, no
+// branches): SwiGLU silu(g) * u, or GeGLU gelu(g) * u with the exact-erf GELU
+template <bool GELU>
+__device__ __forceinline__ float glu_fast(float g, float u) {
+  if constexpr (GELU) return gelu_erf(g) * u;
+  return g * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(g * -1.4426950408889634f)) * u;
+}
+
+// float -> bfloat16 bits, round to nearest even, in one v_cvt_pk_bf16_f32
+__device__ __forceinline__ bf16_t bf16_rne(float v) {
+  return static_cast<bf16_t>(pack_bf16x2(v, 0.0f) & 0xffffu);
+}
+
 // 8 bf16 values held in a 16-byte register quad, unpacked to fp32
 __device__ __forceinline__ void unpack8(const u32x4_t& w, float* f) {
 #pragma unroll

@@ -37,17 +37,23 @@ namespace vla {
 // a reduction kernel adds them to the residual in split order.
 // ---------------------------------------------------------------------------
 constexpr int kXcds = 8;
+// kernel-side epilogue id of the gated product with the GELU gate (the host
+// arguments say EPI_SWIGLU with glu = 1)
+constexpr int EPI_GEGLU_K = 16;
+template <int EPI> constexpr bool kGated = EPI == EPI_SWIGLU || EPI == EPI_GEGLU_K;
 
-template <int BM, int BN, int BK, int NS>
+template <int BM, int BN, int BK, int NS, int WGM = 2, int WGN = 2>
 struct GemmTile {
-  static constexpr int WM = BM / 2, WN = BN / 2;
+  static constexpr int NW = WGM * WGN;               // wavefronts per workgroup
+  static constexpr int WM = BM / WGM, WN = BN / WGN;
   static constexpr int MT = WM / 16, NT = WN / 16;
   static constexpr int ROWB = BK * 2;                // bytes of one LDS row (one K step)
   static constexpr int CPR = BK / 8;                 // 16-byte chunks per row
   static constexpr int RPI = 64 / CPR;               // rows filled by one DMA load
   static constexpr int ROWS = BM + BN;               // LDS rows per stage
   static constexpr int STAGE = ROWS * ROWB;          // bytes
-  static constexpr int LOADS = ROWS / RPI / 4;       // DMA loads per wavefront per stage
+  static constexpr int LOADS = ROWS / RPI / NW;      // DMA loads per wavefront per stage
+  static_assert(LOADS * RPI * NW == ROWS && WM % 16 == 0 && WN % 16 == 0, "tile shape");
   static constexpr int LDS = NS * STAGE;
   // chunk position of K chunk kc in LDS row r: 8 consecutive rows read at one chunk
   // column land in 8 distinct 16-byte bank groups (32 or 64 banks)
@@ -67,14 +73,13 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& a, f32x4_t (&acc)[
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int row = m0 + wm * WM + mi * 16 + 4 * (lane >> 4) + e;
-      if constexpr (EPI == EPI_SWIGLU) {
+      if constexpr (kGated<EPI>) {
         // tiles (ni, ni+1), ni even: gate rows f and the matching up rows (LAYOUT_GATEUP)
 #pragma unroll
         for (int ni = 0; ni < NT; ni += 2) {
           const int f = (n0 + wn * WN + ni * 16) / 2 + (lane & 15);
-          if (row < M)
-            St<bf16_t>::st((bf16_t*)a.C, (size_t)row * (a.N / 2) + f,
-                           glu_act(a.glu, acc[mi][ni][e], acc[mi][ni + 1][e]));
+          const bf16_t o = bf16_rne(glu_fast<EPI == EPI_GEGLU_K>(acc[mi][ni][e], acc[mi][ni + 1][e]));
+          if (row < M) ((bf16_t*)a.C)[(size_t)row * (a.N / 2) + f] = o;
         }
       } else {
 #pragma unroll
@@ -93,10 +98,10 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& a, f32x4_t (&acc)[
   }
 }
 
-template <int EPI, int BM, int BN, int BK, int NS>
-__global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs a, int tiles_m, int tiles,
-                                                        int ksteps) {
-  using G = GemmTile<BM, BN, BK, NS>;
+template <int EPI, int BM, int BN, int BK, int NS, int WGM, int WGN>
+__global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_kernel(GemmArgs a, int tiles_m,
+                                                                   int tiles, int ksteps) {
+  using G = GemmTile<BM, BN, BK, NS, WGM, WGN>;
   constexpr int MT = G::MT, NT = G::NT, LOADS = G::LOADS;
   static_assert(LOADS * (NS - 1) <= 63 && NS - 2 <= 6, "vmcnt range");
   __shared__ __attribute__((aligned(1024))) unsigned char smem[G::LDS];
@@ -112,7 +117,7 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs a, int tiles_m,
   const int nk = min(K / BK - kt0, ksteps);
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / WGN, wn = wave % WGN;
 
   // this lane's source pointers for its LOADS DMA loads (rows past M re-read row M-1)
   const bf16_t* src[LOADS];
@@ -131,7 +136,7 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs a, int tiles_m,
     unsigned char* st = smem + (kt % NS) * G::STAGE + wave * LOADS * 1024;
 #pragma unroll
     for (int j = 0; j < LOADS; ++j)
-      __builtin_amdgcn_global_load_lds((const void*)(src[j] + kt * BK),
+      __builtin_amdgcn_global_load_lds((const void*)(src[j] + (int64_t)kt * BK),
                                        (__attribute__((address_space(3))) void*)(st + j * 1024),
                                        16, 0, 0);
   };
@@ -504,13 +509,13 @@ __global__ __launch_bounds__(256) void qkv_reduce_kernel(GemmArgs a, int splits)
   }
 }
 
-template <int EPI, int BM, int BN, int BK, int NS>
+template <int EPI, int BM, int BN, int BK, int NS, int WGM = 2, int WGN = 2>
 static void gemm_bf16_go(const GemmArgs& a, int splits, int ksteps, hipStream_t s) {
   const int tiles_m = (a.M + BM - 1) / BM;
   const int tiles = tiles_m * (a.N / BN);
   const int per_xcd = (tiles + kXcds - 1) / kXcds;
-  launch_k(gemm_bf16_kernel<EPI, BM, BN, BK, NS>, dim3(kXcds * per_xcd * splits), dim3(256), 0,
-           s, a, tiles_m, tiles, ksteps);
+  launch_k(gemm_bf16_kernel<EPI, BM, BN, BK, NS, WGM, WGN>, dim3(kXcds * per_xcd * splits),
+           dim3(64 * WGM * WGN), 0, s, a, tiles_m, tiles, ksteps);
 }
 
 // INT4 projections: 64 x 64 tiles over 128-wide groups; residual projections split
@@ -520,7 +525,8 @@ static hipError_t gemm_w4(const GemmArgs& a, hipStream_t s) {
   if (a.K % 128 != 0 || a.N % 64 != 0) return hipErrorInvalidValue;
   const int ngk = a.K / 128;
   if (a.epi == EPI_SWIGLU) {
-    gemm_w4_go<EPI_SWIGLU>(a, 1, ngk, s);
+    if (a.glu) gemm_w4_go<EPI_GEGLU_K>(a, 1, ngk, s);
+    else gemm_w4_go<EPI_SWIGLU>(a, 1, ngk, s);
     return hipGetLastError();
   }
   if (a.epi == EPI_QKV) {
@@ -542,31 +548,46 @@ static hipError_t gemm_w4(const GemmArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-// Shapes, measured with the weights cold in HBM: the gated projection takes 64 x 128
-// tiles up to 64 rows and 64 x 64 tiles up to 511 rows (64-deep K steps), 128 x 128
-// tiles with 32-deep steps from 512 rows, in a 4-stage ring; every other
-// projection takes 64 x 64 tiles with 64-deep K steps in a 4-stage ring and, when
-// that leaves fewer than about 384 workgroups, splits K (at least 4 steps per
-// split). Split projections reduce their fp32 partials in a second kernel: the
-// residual add (+ next RMSNorm), or RoPE + K/V write for q/k/v.
+// Tile shapes, measured with the weights cold in HBM (rotated over more than the
+// last-level cache between launches):
+//  gated projection (SwiGLU or GeGLU epilogue): at most 64 rows -> 64 x 128 tiles;
+//    up to 511 rows -> 128 x 64 in a 3-stage ring (37 us against 41 us for 64 x 64 at
+//    256 x 17920 x 1536); from 512 rows -> 256 x 128 with 8 wavefronts (4 x 2 grid of
+//    64 x 64 wavefront tiles), 32-deep steps (100 us against 110 us for 128 x 128 at
+//    512 x 32768 x 2048);
+//  residual and q/k/v projections: 64 x 64 tiles, 64-deep steps, 3-stage ring; K is
+//    split into pieces of about 24 steps and into enough splits for about 192
+//    workgroups (at least 4 steps per split, at most 8 splits): the 256 x 1536 x 8960
+//    down projection takes 6 splits (21.5 us with its reduction, against 23.9 us
+//    for 4). From 512 rows with at least 128 K steps: 256 x 64 tiles with 8
+//    wavefronts and K in pieces of 64 steps (512 x 2048 x 16384: 61 us against 74).
+// Split projections reduce their fp32 partials in split order in a second kernel:
+// the residual add (+ next RMSNorm), or RoPE + K/V write for q/k/v.
+template <int EPI>
+static void gated_go(const GemmArgs& a, hipStream_t s) {
+  if (a.M <= 64 && a.N % 128 == 0)
+    gemm_bf16_go<EPI, 64, 128, 64, 4>(a, 1, a.K / 64, s);
+  else if (a.M >= 512 && a.N % 128 == 0)
+    gemm_bf16_go<EPI, 256, 128, 32, 4, 4, 2>(a, 1, a.K / 32, s);
+  else
+    gemm_bf16_go<EPI, 128, 64, 64, 3>(a, 1, a.K / 64, s);
+}
+
 static hipError_t gemm_bf16(const GemmArgs& a, hipStream_t s) {
   if (a.K % 64 != 0 || a.N % 64 != 0 || a.M < 1) return hipErrorInvalidValue;
   if (a.wf == WF_INT4) return gemm_w4(a, s);
   if (a.epi == EPI_SWIGLU) {
-    // measured with weights cold in HBM: at most 64 rows -> 64 x 128 tiles; up to
-    // 511 rows -> 64 x 64 (64-deep K steps); from 512 rows -> 128 x 128 (32-deep)
-    if (a.M <= 64 && a.N % 128 == 0)
-      gemm_bf16_go<EPI_SWIGLU, 64, 128, 64, 4>(a, 1, a.K / 64, s);
-    else if (a.M >= 512 && a.N % 128 == 0)
-      gemm_bf16_go<EPI_SWIGLU, 128, 128, 32, 4>(a, 1, a.K / 32, s);
-    else
-      gemm_bf16_go<EPI_SWIGLU, 64, 64, 64, 4>(a, 1, a.K / 64, s);
+    if (a.glu) gated_go<EPI_GEGLU_K>(a, s);
+    else gated_go<EPI_SWIGLU>(a, s);
     return hipGetLastError();
   }
   if (a.epi != EPI_QKV && a.epi != EPI_RESID) return hipErrorInvalidValue;
-  const int tiles = ((a.M + 63) / 64) * (a.N / 64);
   const int ksteps_all = a.K / 64;
-  int splits = std::max(1, std::min(8, (384 + tiles - 1) / tiles));
+  const bool tall = a.M >= 512 && ksteps_all >= 128;  // 256 x 64 tiles, 8 wavefronts
+  const int tiles = tall ? ((a.M + 255) / 256) * (a.N / 64) : ((a.M + 63) / 64) * (a.N / 64);
+  int splits = tall ? (ksteps_all + 63) / 64
+                    : std::max((192 + tiles - 1) / tiles, (ksteps_all + 23) / 24);
+  splits = std::max(1, std::min(8, splits));
   while (splits > 1 && ksteps_all / splits < 4) --splits;
   while (splits > 1 && (size_t)splits * a.M * a.N > a.ws_elems) --splits;
   if (a.ws == nullptr || (size_t)a.M * a.N > a.ws_elems) splits = 1;
@@ -574,9 +595,10 @@ static hipError_t gemm_bf16(const GemmArgs& a, hipStream_t s) {
   splits = (ksteps_all + ksteps - 1) / ksteps;
   if (a.epi == EPI_QKV) {
     if (splits == 1) {
-      gemm_bf16_go<EPI_QKV, 64, 64, 64, 4>(a, 1, ksteps_all, s);
+      gemm_bf16_go<EPI_QKV, 64, 64, 64, 3>(a, 1, ksteps_all, s);
     } else {
-      gemm_bf16_go<EPI_PARTIAL, 64, 64, 64, 4>(a, splits, ksteps, s);
+      if (tall) gemm_bf16_go<EPI_PARTIAL, 256, 64, 64, 3, 4, 2>(a, splits, ksteps, s);
+      else gemm_bf16_go<EPI_PARTIAL, 64, 64, 64, 3>(a, splits, ksteps, s);
       launch_k(qkv_reduce_kernel, dim3(a.M), dim3(256), 0, s, a, splits);
     }
     return hipGetLastError();
@@ -584,7 +606,8 @@ static hipError_t gemm_bf16(const GemmArgs& a, hipStream_t s) {
   // residual projection: always through the partial buffer and the reduction kernel
   if (a.ws == nullptr || (size_t)a.M * a.N > a.ws_elems) return hipErrorInvalidValue;
   if (a.N % 8 != 0 || a.N / 8 > 256 * kResidMaxChunks) return hipErrorInvalidValue;
-  gemm_bf16_go<EPI_PARTIAL, 64, 64, 64, 4>(a, splits, ksteps, s);
+  if (tall) gemm_bf16_go<EPI_PARTIAL, 256, 64, 64, 3, 4, 2>(a, splits, ksteps, s);
+  else gemm_bf16_go<EPI_PARTIAL, 64, 64, 64, 3>(a, splits, ksteps, s);
   launch_k(resid_norm_kernel, dim3(a.M), dim3(256), 0, s, (const float*)a.ws, splits, a.M, a.N,
            (float*)a.C, (bf16_t*)a.norm_out, a.norm_g, a.eps);
   return hipGetLastError();
