@@ -186,6 +186,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_kernel(GemmArgs a, i
 // then, if u is given, u[row] = RMSNorm(x[row]) in bf16 with fp32 statistics.
 // One workgroup per row; each thread keeps up to 4 chunks of 8 columns in registers.
 constexpr int kResidMaxChunks = 4;
+constexpr int kResidMaxSplits = 8;
 __global__ __launch_bounds__(256) void resid_norm_kernel(const float* ws, int splits, int M, int N,
                                                          float* x, bf16_t* u, const float* g,
                                                          float eps) {
@@ -205,15 +206,24 @@ __global__ __launch_bounds__(256) void resid_norm_kernel(const float* ws, int sp
       v[j][i] = x0[i];
       v[j][4 + i] = x1[i];
     }
-    for (int s = 0; s < splits; ++s) {
-      const float* p = ws + ((size_t)s * M + row) * N + c * 8;
-      const f32x4_t p0 = *(const f32x4_t*)p, p1 = *(const f32x4_t*)(p + 4);
+    // every split's partial of this chunk is requested before the sum (split order)
+    f32x4_t p0[kResidMaxSplits], p1[kResidMaxSplits];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        v[j][i] += p0[i];
-        v[j][4 + i] += p1[i];
+    for (int s = 0; s < kResidMaxSplits; ++s)
+      if (s < splits) {
+        const float* p = ws + ((size_t)s * M + row) * N + c * 8;
+        p0[s] = *(const f32x4_t*)p;
+        p1[s] = *(const f32x4_t*)(p + 4);
       }
-    }
+#pragma unroll
+    for (int s = 0; s < kResidMaxSplits; ++s)
+      if (s < splits) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          v[j][i] += p0[s][i];
+          v[j][4 + i] += p1[s][i];
+        }
+      }
     *(f32x4_t*)xp = f32x4_t{v[j][0], v[j][1], v[j][2], v[j][3]};
     *(f32x4_t*)(xp + 4) = f32x4_t{v[j][4], v[j][5], v[j][6], v[j][7]};
 #pragma unroll
@@ -495,18 +505,26 @@ static void gemm_w4_go(const GemmArgs& a, int splits, int ksteps, hipStream_t s)
 
 // q/k/v split-K reduction: sums the partials of each RoPE pair (split order) and
 // applies the same epilogue as the unsplit kernel (rotation, query buffer, paged
-// K/V). One workgroup per row.
+// K/V). One thread per pair (grid: pair blocks x rows); the rotation, the block id
+// and every split's partial are requested together before the sum.
+constexpr int kQkvReduceMaxSplits = kResidMaxSplits;
 __global__ __launch_bounds__(256) void qkv_reduce_kernel(GemmArgs a, int splits) {
-  const int row = blockIdx.x;
-  for (int cp = threadIdx.x; cp < a.N / 2; cp += 256) {
-    float lo = 0.f, hi = 0.f;
-    for (int s = 0; s < splits; ++s) {
-      const float2 v = *(const float2*)(a.ws + ((size_t)s * a.M + row) * a.N + 2 * cp);
-      lo += v.x;
-      hi += v.y;
+  const int row = blockIdx.y;
+  const int cp = blockIdx.x * 256 + threadIdx.x;
+  if (cp >= a.N / 2) return;
+  const QkvPre pre = epi_qkv_prefetch(a.ctx, row, 2 * cp);
+  float2 v[kQkvReduceMaxSplits];
+#pragma unroll
+  for (int s = 0; s < kQkvReduceMaxSplits; ++s)
+    if (s < splits) v[s] = *(const float2*)(a.ws + ((size_t)s * a.M + row) * a.N + 2 * cp);
+  float lo = 0.f, hi = 0.f;
+#pragma unroll
+  for (int s = 0; s < kQkvReduceMaxSplits; ++s)
+    if (s < splits) {
+      lo += v[s].x;
+      hi += v[s].y;
     }
-    epi_qkv_pair<bf16_t>(a.ctx, row, 2 * cp, lo, hi);
-  }
+  epi_qkv_store<bf16_t>(a.ctx, row, 2 * cp, pre, lo, hi);
 }
 
 template <int EPI, int BM, int BN, int BK, int NS, int WGM = 2, int WGN = 2>
@@ -537,7 +555,7 @@ static hipError_t gemm_w4(const GemmArgs& a, hipStream_t s) {
   if (a.ws == nullptr || (size_t)a.M * a.N > a.ws_elems) return hipErrorInvalidValue;
   if (a.N % 8 != 0 || a.N / 8 > 256 * kResidMaxChunks) return hipErrorInvalidValue;
   const int tiles = ((a.M + 63) / 64) * (a.N / 64);
-  int splits = std::max(1, std::min(8, (384 + tiles - 1) / tiles));
+  int splits = std::max(1, std::min(kResidMaxSplits, (384 + tiles - 1) / tiles));
   while (splits > 1 && ngk / splits < 4) --splits;
   while (splits > 1 && (size_t)splits * a.M * a.N > a.ws_elems) --splits;
   const int ksteps = (ngk + splits - 1) / splits;
@@ -587,7 +605,7 @@ static hipError_t gemm_bf16(const GemmArgs& a, hipStream_t s) {
   const int tiles = tall ? ((a.M + 255) / 256) * (a.N / 64) : ((a.M + 63) / 64) * (a.N / 64);
   int splits = tall ? (ksteps_all + 63) / 64
                     : std::max((192 + tiles - 1) / tiles, (ksteps_all + 23) / 24);
-  splits = std::max(1, std::min(8, splits));
+  splits = std::max(1, std::min(kResidMaxSplits, splits));
   while (splits > 1 && ksteps_all / splits < 4) --splits;
   while (splits > 1 && (size_t)splits * a.M * a.N > a.ws_elems) --splits;
   if (a.ws == nullptr || (size_t)a.M * a.N > a.ws_elems) splits = 1;
@@ -599,7 +617,7 @@ static hipError_t gemm_bf16(const GemmArgs& a, hipStream_t s) {
     } else {
       if (tall) gemm_bf16_go<EPI_PARTIAL, 256, 64, 64, 3, 4, 2>(a, splits, ksteps, s);
       else gemm_bf16_go<EPI_PARTIAL, 64, 64, 64, 3>(a, splits, ksteps, s);
-      launch_k(qkv_reduce_kernel, dim3(a.M), dim3(256), 0, s, a, splits);
+      launch_k(qkv_reduce_kernel, dim3((a.N / 2 + 255) / 256, a.M), dim3(256), 0, s, a, splits);
     }
     return hipGetLastError();
   }
