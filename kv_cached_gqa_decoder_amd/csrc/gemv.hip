@@ -524,26 +524,55 @@ static hipError_t gemv_launch(const GemvArgs& a, hipStream_t s, int* grid_out) {
 // INT4 group-128 weights: a 16-byte chunk holds the 32 codes of K positions
 // 32c .. 32c+31 (even k in the low nibble), inside group c / 4 whose fp16 scale
 // (scales stored [K/128][N]) multiplies the chunk's partial sum in fp32.
-// Same row groups, grid and epilogues as the 16-bit kernel; the input row is
-// always kept in fp32 in LDS.
+// Unpacking: flipping each nibble's sign bit turns a code q into u = q + 8
+// (0..15); two nibbles masked into a bf16 pair with the exponent of 128 are the
+// values 128 + u, and v_dot2c_f32_bf16 adds two products to an fp32 sum per
+// instruction. Per 32-code chunk, sum_k q_k x_k = sum_k (128 + u_k) x_k -
+// 136 sum_k x_k, the second sum shared by all rows that use the chunk's inputs.
+// The input is rounded to bf16 (as the matrix-core path does) and kept as bf16
+// pairs in the order the nibbles come out of a 32-bit word: for its 8 codes
+// k0..k7, pairs (k0, k4), (k1, k5), (k2, k6), (k3, k7).
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ float dot32_w4(const u32x4_t& w, const float* x) {
-  float s = 0.f;
+typedef __bf16 bf16x2v_t __attribute__((ext_vector_type(2)));
+
+// the 8 inputs x0..x7 of one word's codes, as the 4 pairs of that order
+__device__ __forceinline__ void w4_pairs(const float (&x)[8], uint32_t (&pr)[4]) {
+#pragma unroll
+  for (int p = 0; p < 4; ++p) pr[p] = pack_bf16x2(x[p], x[p + 4]);
+}
+// (x0, x1), (x2, x3), (x4, x5), (x6, x7) as bf16 words -> the 4 pairs of that order
+__device__ __forceinline__ void w4_pairs_bf16(const u32x4_t& n, uint32_t (&pr)[4]) {
+  pr[0] = __builtin_amdgcn_perm(n[2], n[0], 0x05040100u);  // (x0, x4)
+  pr[1] = __builtin_amdgcn_perm(n[2], n[0], 0x07060302u);  // (x1, x5)
+  pr[2] = __builtin_amdgcn_perm(n[3], n[1], 0x05040100u);  // (x2, x6)
+  pr[3] = __builtin_amdgcn_perm(n[3], n[1], 0x07060302u);  // (x3, x7)
+}
+__device__ __forceinline__ float w4_dot2(uint32_t a, uint32_t b, float acc) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2v_t, a),
+                                         __builtin_bit_cast(bf16x2v_t, b), acc, false);
+}
+// sum over one chunk (4 words of codes) of (128 + u_k) x_k
+__device__ __forceinline__ float w4_chunk(const u32x4_t& w, const uint32_t (&xp)[16]) {
+  float acc = 0.f;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
+    const uint32_t v = w[i] ^ 0x88888888u;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int q = (int)(w[i] << (28 - 4 * j)) >> 28;  // sign-extended nibble j
-      s += (float)q * x[8 * i + j];
-    }
+    for (int p = 0; p < 4; ++p)
+      acc = w4_dot2(((v >> (4 * p)) & 0x000F000Fu) | 0x43004300u, xp[4 * i + p], acc);
   }
-  return s;
+  return acc;
 }
 
+
+// Streaming INT4 GEMV: same row groups, grid and epilogues as the 16-bit
+// kernel; the input row is staged once per workgroup in LDS as bf16 pairs (the
+// normalised residual, or the bf16 activations), and each chunk's input pairs
+// and their sum are read once for the wavefront's RW rows.
 template <int EPI, int RW>
 __global__ __launch_bounds__(kGemvThreads) void gemv_w4_kernel(GemvArgs a, int ngroups) {
   extern __shared__ __attribute__((aligned(16))) unsigned char gsmem[];
-  f32x4_t* xs4 = (f32x4_t*)gsmem;
+  uint32_t* xsh = (uint32_t*)gsmem;  // K/2 words: the input as bf16 pairs
   __shared__ float ssq[kGemvWaves];
   __shared__ unsigned long long wbest[kGemvWaves];
   constexpr int UNR = RW >= 8 ? 1 : (RW >= 4 ? 2 : 4);  // 8 chunk loads (256 codes) in flight
@@ -551,34 +580,43 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_w4_kernel(GemvArgs a, int n
   const int K = a.K;
   const int nch = K / 32;
 
-  // input row -> LDS in fp32 (the normalised residual, or the bf16 activations widened)
+  // input row -> LDS as bf16 pairs (the normalised residual, or the bf16 activations)
   if constexpr (EPI != EPI_RESID) {
     const f32x4_t* xf4 = (const f32x4_t*)a.x;
-    float ss = 0.f;
-    for (int i = tid; i < K / 4; i += kGemvThreads) {
-      const f32x4_t v = xf4[i];
-      xs4[i] = v;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) ss += v[e] * v[e];
-    }
+    const f32x4_t* g4 = (const f32x4_t*)a.norm_g;
+    float rn = 1.f;
     if (a.norm_g) {
+      float ss = 0.f;
+      for (int i = tid; i < K / 4; i += kGemvThreads) {
+        const f32x4_t v = xf4[i];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) ss += v[e] * v[e];
+      }
       ss = wave_sum(ss);
       if (lane == 0) ssq[wave] = ss;
       __syncthreads();
       float tot = 0.f;
 #pragma unroll
       for (int w = 0; w < kGemvWaves; ++w) tot += ssq[w];
-      const float rn = rsqrtf(tot / (float)K + a.eps);
-      const f32x4_t* g4 = (const f32x4_t*)a.norm_g;
-      for (int i = tid; i < K / 4; i += kGemvThreads) xs4[i] = xs4[i] * rn * g4[i];  // own elements
+      rn = rsqrtf(tot / (float)K + a.eps);
+    }
+    for (int gi = tid; gi < K / 8; gi += kGemvThreads) {
+      f32x4_t v0 = xf4[2 * gi], v1 = xf4[2 * gi + 1];
+      if (a.norm_g) {
+        v0 = v0 * rn * g4[2 * gi];
+        v1 = v1 * rn * g4[2 * gi + 1];
+      }
+      const float xv8[8] = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+      uint32_t pr[4];
+      w4_pairs(xv8, pr);
+      *(u32x4_t*)(xsh + 4 * gi) = u32x4_t{pr[0], pr[1], pr[2], pr[3]};
     }
   } else {
     const bf16_t* x = (const bf16_t*)a.x;
-    for (int c = tid; c < K / 8; c += kGemvThreads) {
-      float f[8];
-      unpack8(*(const u32x4_t*)(x + (size_t)c * 8), f);
-      xs4[2 * c] = f32x4_t{f[0], f[1], f[2], f[3]};
-      xs4[2 * c + 1] = f32x4_t{f[4], f[5], f[6], f[7]};
+    for (int gi = tid; gi < K / 8; gi += kGemvThreads) {
+      uint32_t pr[4];
+      w4_pairs_bf16(*(const u32x4_t*)(x + (size_t)gi * 8), pr);
+      *(u32x4_t*)(xsh + 4 * gi) = u32x4_t{pr[0], pr[1], pr[2], pr[3]};
     }
   }
   __syncthreads();
@@ -612,18 +650,18 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_w4_kernel(GemvArgs a, int n
 #pragma unroll
       for (int u = 0; u < UNR; ++u) {
         const int c = c0 + 64 * u;
-        float xv[32];
-        const f32x4_t* xp = xs4 + (size_t)c * 8;
+        uint32_t xp[16];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const f32x4_t q = c < nch ? xp[i] : f32x4_t{0.f, 0.f, 0.f, 0.f};
-          xv[4 * i] = q[0];
-          xv[4 * i + 1] = q[1];
-          xv[4 * i + 2] = q[2];
-          xv[4 * i + 3] = q[3];
+        for (int i = 0; i < 4; ++i) {
+          const u32x4_t v = c < nch ? *(const u32x4_t*)(xsh + 16 * c + 4 * i) : u32x4_t{0, 0, 0, 0};
+#pragma unroll
+          for (int p = 0; p < 4; ++p) xp[4 * i + p] = v[p];
         }
+        float sx = 0.f;
 #pragma unroll
-        for (int r = 0; r < RW; ++r) acc[r] += sc[u][r] * dot32_w4(w[u][r], xv);
+        for (int j = 0; j < 16; ++j) sx = w4_dot2(xp[j], 0x3f803f80u, sx);  // (1, 1)
+#pragma unroll
+        for (int r = 0; r < RW; ++r) acc[r] += sc[u][r] * (w4_chunk(w[u][r], xp) - 136.f * sx);
       }
     }
 #pragma unroll
@@ -672,46 +710,8 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_w4_kernel(GemvArgs a, int n
 // One-shot INT4 decode GEMV: the one-shot structure of the bf16 kernel (input
 // side first, then every weight chunk of the wavefront's rows; 2 whole rows per
 // wavefront, or one row per workgroup with K split over its 4 wavefronts for long
-// residual rows) with a cheaper unpacking. Flipping each nibble's sign bit turns
-// a code q into u = q + 8 (0..15); two nibbles masked into a bf16 pair with the
-// exponent of 128 are the values 128 + u, and v_dot2c_f32_bf16 adds two products
-// to an fp32 sum per instruction. Per 32-code chunk, sum_k q_k x_k =
-// sum_k (128 + u_k) x_k - 136 sum_k x_k, the second sum shared by all rows of the
-// wavefront; the chunk's group scale multiplies the difference. The input is
-// rounded to bf16 (as the matrix-core path does) and kept as bf16 pairs in the
-// order the nibbles come out of a 32-bit word: for its 8 codes k0..k7, pairs
-// (k0, k4), (k1, k5), (k2, k6), (k3, k7).
-typedef __bf16 bf16x2v_t __attribute__((ext_vector_type(2)));
-
-// the 8 inputs x0..x7 of one word's codes, as the 4 pairs of that order
-__device__ __forceinline__ void w4_pairs(const float (&x)[8], uint32_t (&pr)[4]) {
-#pragma unroll
-  for (int p = 0; p < 4; ++p) pr[p] = pack_bf16x2(x[p], x[p + 4]);
-}
-// (x0, x1), (x2, x3), (x4, x5), (x6, x7) as bf16 words -> the 4 pairs of that order
-__device__ __forceinline__ void w4_pairs_bf16(const u32x4_t& n, uint32_t (&pr)[4]) {
-  pr[0] = __builtin_amdgcn_perm(n[2], n[0], 0x05040100u);  // (x0, x4)
-  pr[1] = __builtin_amdgcn_perm(n[2], n[0], 0x07060302u);  // (x1, x5)
-  pr[2] = __builtin_amdgcn_perm(n[3], n[1], 0x05040100u);  // (x2, x6)
-  pr[3] = __builtin_amdgcn_perm(n[3], n[1], 0x07060302u);  // (x3, x7)
-}
-__device__ __forceinline__ float w4_dot2(uint32_t a, uint32_t b, float acc) {
-  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2v_t, a),
-                                         __builtin_bit_cast(bf16x2v_t, b), acc, false);
-}
-// sum over one chunk (4 words of codes) of (128 + u_k) x_k
-__device__ __forceinline__ float w4_chunk(const u32x4_t& w, const uint32_t (&xp)[16]) {
-  float acc = 0.f;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const uint32_t v = w[i] ^ 0x88888888u;
-#pragma unroll
-    for (int p = 0; p < 4; ++p)
-      acc = w4_dot2(((v >> (4 * p)) & 0x000F000Fu) | 0x43004300u, xp[4 * i + p], acc);
-  }
-  return acc;
-}
-
+// residual rows) with the unpacking above; the chunk input sums are shared by the
+// wavefront's rows.
 template <int EPI, int RW, int CPL, int KS>
 __global__ __launch_bounds__(kGemvThreads) void gemv1_w4_kernel(GemvArgs a, int ngroups) {
   static_assert(KS == 1 || (KS == kGemvWaves && EPI == EPI_RESID), "K split: residual inputs only");
@@ -931,7 +931,7 @@ static hipError_t gemv_w4_launch_rw(const GemvArgs& a, hipStream_t s, int* grid_
   int grid = (ngroups + kGemvWaves - 1) / kGemvWaves;
   grid = grid < kGemvMaxGrid ? grid : kGemvMaxGrid;
   if (grid_out) *grid_out = grid;
-  launch_k(gemv_w4_kernel<EPI, RW>, dim3(grid), dim3(kGemvThreads), (uint32_t)(a.K * 4), s, a,
+  launch_k(gemv_w4_kernel<EPI, RW>, dim3(grid), dim3(kGemvThreads), (uint32_t)(a.K * 2), s, a,
            ngroups);
   return hipGetLastError();
 }
