@@ -132,11 +132,15 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_kernel(GemmArgs a, i
       src[j] = (const bf16_t*)a.W + (int64_t)(n0 + row - BM) * K + (int64_t)kt0 * BK + kc * 8;
     }
   }
+  // stage kt -> ring slot kt % NS. Past the last step the DMA re-loads the last
+  // step's data into the slot just freed (never read), so every step issues the
+  // same loads and every wait has one constant depth
   auto issue = [&](int kt) {
     unsigned char* st = smem + (kt % NS) * G::STAGE + wave * LOADS * 1024;
+    const int kd = kt < nk ? kt : nk - 1;
 #pragma unroll
     for (int j = 0; j < LOADS; ++j)
-      __builtin_amdgcn_global_load_lds((const void*)(src[j] + (int64_t)kt * BK),
+      __builtin_amdgcn_global_load_lds((const void*)(src[j] + (int64_t)kd * BK),
                                        (__attribute__((address_space(3))) void*)(st + j * 1024),
                                        16, 0, 0);
   };
@@ -147,17 +151,20 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_kernel(GemmArgs a, i
 #pragma unroll
     for (int j = 0; j < NT; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
+  if (nk <= 0) {  // (the host never splits K into an empty piece)
+    gemm_epilogue<EPI, MT, NT, G::WM, G::WN>(a, acc, m0, n0, z, wm, wn, lane);
+    return;
+  }
 #pragma unroll
-  for (int s = 0; s < NS - 1; ++s)
-    if (s < nk) issue(s);
+  for (int s = 0; s < NS - 1; ++s) issue(s);
   for (int kt = 0; kt < nk; ++kt) {
-    // stage kt has landed once at most (issued - kt - 1) stages are outstanding
-    wait_vmcnt_steps<LOADS>(min(nk, NS - 1 + kt) - kt - 1);
+    // stage kt has landed once at most NS-2 younger stages are outstanding
+    wait_vmcnt_steps<LOADS>(NS - 2);
     // every wavefront's loads of stage kt are in LDS, and every wavefront's reads of
     // stage kt-1 have returned (lgkmcnt), so that stage may be refilled. A bare
     // barrier: a fenced one would also drain the loads still in flight.
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    if (kt + NS - 1 < nk) issue(kt + NS - 1);
+    issue(kt + NS - 1);
     const unsigned char* st = smem + (kt % NS) * G::STAGE;
 #pragma unroll
     for (int ks = 0; ks < BK / 32; ++ks) {
@@ -569,23 +576,24 @@ static hipError_t gemm_w4(const GemmArgs& a, hipStream_t s) {
 // Tile shapes, measured with the weights cold in HBM (rotated over more than the
 // last-level cache between launches):
 //  gated projection (SwiGLU or GeGLU epilogue): at most 64 rows -> 64 x 128 tiles;
-//    up to 511 rows -> 128 x 64 in a 3-stage ring (37 us against 41 us for 64 x 64 at
-//    256 x 17920 x 1536); from 512 rows -> 256 x 128 with 8 wavefronts (4 x 2 grid of
-//    64 x 64 wavefront tiles), 32-deep steps (100 us against 110 us for 128 x 128 at
-//    512 x 32768 x 2048);
+//    up to 128 rows -> 128 x 64 in a 3-stage ring; more rows -> 256 x 128 with 8
+//    wavefronts (4 x 2 grid of 64 x 64 wavefront tiles), 32-deep steps (256 x 17920 x
+//    1536: 34 us against 37 us for 128 x 64 and 39 us for 64 x 64; 512 x 32768 x 2048:
+//    95 us against 118 us for 128 x 128);
 //  residual and q/k/v projections: 64 x 64 tiles, 64-deep steps, 3-stage ring; K is
-//    split into pieces of about 24 steps and into enough splits for about 192
-//    workgroups (at least 4 steps per split, at most 8 splits): the 256 x 1536 x 8960
-//    down projection takes 6 splits (21.5 us with its reduction, against 23.9 us
-//    for 4). From 512 rows with at least 128 K steps: 256 x 64 tiles with 8
-//    wavefronts and K in pieces of 64 steps (512 x 2048 x 16384: 61 us against 74).
+//    split into pieces of about 36 steps and into enough splits for about 192
+//    workgroups (at least 4 steps per split, at most 8 splits): 256 x 2048 x 1536
+//    q/k/v 12.0 us and 256 x 1536 x 1536 O 11.1 us with 2 splits, 256 x 1536 x 8960
+//    down 21.4 us with 4 (times include the reduction kernel). From 512 rows with at
+//    least 128 K steps: 256 x 64 tiles with 8 wavefronts and K in pieces of 64 steps
+//    (512 x 2048 x 16384: 57 us against 75 us for 64 x 64).
 // Split projections reduce their fp32 partials in split order in a second kernel:
 // the residual add (+ next RMSNorm), or RoPE + K/V write for q/k/v.
 template <int EPI>
 static void gated_go(const GemmArgs& a, hipStream_t s) {
   if (a.M <= 64 && a.N % 128 == 0)
     gemm_bf16_go<EPI, 64, 128, 64, 4>(a, 1, a.K / 64, s);
-  else if (a.M >= 512 && a.N % 128 == 0)
+  else if (a.M > 128 && a.N % 128 == 0)
     gemm_bf16_go<EPI, 256, 128, 32, 4, 4, 2>(a, 1, a.K / 32, s);
   else
     gemm_bf16_go<EPI, 128, 64, 64, 3>(a, 1, a.K / 64, s);
@@ -604,7 +612,7 @@ static hipError_t gemm_bf16(const GemmArgs& a, hipStream_t s) {
   const bool tall = a.M >= 512 && ksteps_all >= 128;  // 256 x 64 tiles, 8 wavefronts
   const int tiles = tall ? ((a.M + 255) / 256) * (a.N / 64) : ((a.M + 63) / 64) * (a.N / 64);
   int splits = tall ? (ksteps_all + 63) / 64
-                    : std::max((192 + tiles - 1) / tiles, (ksteps_all + 23) / 24);
+                    : std::max((192 + tiles - 1) / tiles, (ksteps_all + 35) / 36);
   splits = std::max(1, std::min(kResidMaxSplits, splits));
   while (splits > 1 && ksteps_all / splits < 4) --splits;
   while (splits > 1 && (size_t)splits * a.M * a.N > a.ws_elems) --splits;

@@ -951,6 +951,10 @@ static hipError_t gemv_w4_launch(const GemvArgs& a, hipStream_t s, int* grid_out
     hipError_t err;
     if ((a.K / 32 + 63) / 64 <= 4 && gemv1_w4_launch<EPI>(a, s, grid_out, &err)) return err;
   }
+  // residual rows too long for the one-shot kernel: 2 rows per wavefront (more
+  // wavefronts, fewer dependent steps each; Llama-3-8B down projection 16.5 ->
+  // about 14.5 us against 4 rows)
+  if constexpr (EPI == EPI_RESID) return gemv_w4_launch_rw<EPI, 2>(a, s, grid_out);
   if (a.N / 8 >= 2048) return gemv_w4_launch_rw<EPI, 8>(a, s, grid_out);
   if (a.N / 4 >= 1024) return gemv_w4_launch_rw<EPI, 4>(a, s, grid_out);
   return gemv_w4_launch_rw<EPI, 2>(a, s, grid_out);
