@@ -575,8 +575,11 @@ static hipError_t gemm_w4(const GemmArgs& a, hipStream_t s) {
 
 // Tile shapes, measured with the weights cold in HBM (rotated over more than the
 // last-level cache between launches):
-//  gated projection (SwiGLU or GeGLU epilogue): at most 64 rows -> 64 x 128 tiles;
-//    up to 128 rows -> 128 x 64 in a 3-stage ring; more rows -> 256 x 128 with 8
+//  gated projection (SwiGLU or GeGLU epilogue): at most 64 rows -> 64 x 128 tiles
+//    when that makes at least 128 workgroups (64 x 17920 x 1536: 17.7 us against
+//    20.3 us for 64 x 64), else 64 x 32 tiles with 4 wavefronts along M (63 x 8192 x
+//    1024: 6.2 us against 10.1 us for 64 x 128); up to 128 rows -> 128 x 64 in a
+//    3-stage ring; more rows -> 256 x 128 with 8
 //    wavefronts (4 x 2 grid of 64 x 64 wavefront tiles), 32-deep steps (256 x 17920 x
 //    1536: 34 us against 37 us for 128 x 64 and 39 us for 64 x 64; 512 x 32768 x 2048:
 //    95 us against 118 us for 128 x 128);
@@ -586,13 +589,17 @@ static hipError_t gemm_w4(const GemmArgs& a, hipStream_t s) {
 //    q/k/v 12.0 us and 256 x 1536 x 1536 O 11.1 us with 2 splits, 256 x 1536 x 8960
 //    down 21.4 us with 4 (times include the reduction kernel). From 512 rows with at
 //    least 128 K steps: 256 x 64 tiles with 8 wavefronts and K in pieces of 64 steps
-//    (512 x 2048 x 16384: 57 us against 75 us for 64 x 64).
+//    (512 x 2048 x 16384: 57 us against 75 us for 64 x 64). At most 64 rows: 64 x 32
+//    tiles with 4 wavefronts along M, splits for about 384 workgroups (63 x 1024 x
+//    2048: 7.9 us against 8.3 us; 63 x 1024 x 4096: 8.9 against 9.5).
 // Split projections reduce their fp32 partials in split order in a second kernel:
 // the residual add (+ next RMSNorm), or RoPE + K/V write for q/k/v.
 template <int EPI>
 static void gated_go(const GemmArgs& a, hipStream_t s) {
-  if (a.M <= 64 && a.N % 128 == 0)
+  if (a.M <= 64 && a.N % 128 == 0 && a.N / 128 >= 128)
     gemm_bf16_go<EPI, 64, 128, 64, 4>(a, 1, a.K / 64, s);
+  else if (a.M <= 64)
+    gemm_bf16_go<EPI, 64, 32, 64, 4, 4, 1>(a, 1, a.K / 64, s);
   else if (a.M > 128 && a.N % 128 == 0)
     gemm_bf16_go<EPI, 256, 128, 32, 4, 4, 2>(a, 1, a.K / 32, s);
   else
@@ -610,9 +617,12 @@ static hipError_t gemm_bf16(const GemmArgs& a, hipStream_t s) {
   if (a.epi != EPI_QKV && a.epi != EPI_RESID) return hipErrorInvalidValue;
   const int ksteps_all = a.K / 64;
   const bool tall = a.M >= 512 && ksteps_all >= 128;  // 256 x 64 tiles, 8 wavefronts
-  const int tiles = tall ? ((a.M + 255) / 256) * (a.N / 64) : ((a.M + 63) / 64) * (a.N / 64);
+  const bool skinny = !tall && a.M <= 64;               // 64 x 32 tiles, 4 wavefronts along M
+  const int tiles = tall ? ((a.M + 255) / 256) * (a.N / 64)
+                         : skinny ? a.N / 32 : ((a.M + 63) / 64) * (a.N / 64);
+  const int target = skinny ? 384 : 192;
   int splits = tall ? (ksteps_all + 63) / 64
-                    : std::max((192 + tiles - 1) / tiles, (ksteps_all + 35) / 36);
+                    : std::max((target + tiles - 1) / tiles, (ksteps_all + 35) / 36);
   splits = std::max(1, std::min(kResidMaxSplits, splits));
   while (splits > 1 && ksteps_all / splits < 4) --splits;
   while (splits > 1 && (size_t)splits * a.M * a.N > a.ws_elems) --splits;
@@ -621,9 +631,11 @@ static hipError_t gemm_bf16(const GemmArgs& a, hipStream_t s) {
   splits = (ksteps_all + ksteps - 1) / ksteps;
   if (a.epi == EPI_QKV) {
     if (splits == 1) {
-      gemm_bf16_go<EPI_QKV, 64, 64, 64, 3>(a, 1, ksteps_all, s);
+      if (skinny) gemm_bf16_go<EPI_QKV, 64, 32, 64, 3, 4, 1>(a, 1, ksteps_all, s);
+      else gemm_bf16_go<EPI_QKV, 64, 64, 64, 3>(a, 1, ksteps_all, s);
     } else {
       if (tall) gemm_bf16_go<EPI_PARTIAL, 256, 64, 64, 3, 4, 2>(a, splits, ksteps, s);
+      else if (skinny) gemm_bf16_go<EPI_PARTIAL, 64, 32, 64, 3, 4, 1>(a, splits, ksteps, s);
       else gemm_bf16_go<EPI_PARTIAL, 64, 64, 64, 3>(a, splits, ksteps, s);
       launch_k(qkv_reduce_kernel, dim3((a.N / 2 + 255) / 256, a.M), dim3(256), 0, s, a, splits);
     }
@@ -633,6 +645,7 @@ static hipError_t gemm_bf16(const GemmArgs& a, hipStream_t s) {
   if (a.ws == nullptr || (size_t)a.M * a.N > a.ws_elems) return hipErrorInvalidValue;
   if (a.N % 8 != 0 || a.N / 8 > 256 * kResidMaxChunks) return hipErrorInvalidValue;
   if (tall) gemm_bf16_go<EPI_PARTIAL, 256, 64, 64, 3, 4, 2>(a, splits, ksteps, s);
+  else if (skinny) gemm_bf16_go<EPI_PARTIAL, 64, 32, 64, 3, 4, 1>(a, splits, ksteps, s);
   else gemm_bf16_go<EPI_PARTIAL, 64, 64, 64, 3>(a, splits, ksteps, s);
   launch_k(resid_norm_kernel, dim3(a.M), dim3(256), 0, s, (const float*)a.ws, splits, a.M, a.N,
            (float*)a.C, (bf16_t*)a.norm_out, a.norm_g, a.eps);
