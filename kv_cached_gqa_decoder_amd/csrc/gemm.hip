@@ -349,39 +349,37 @@ static hipError_t gemm_f32_launch(const GemmArgs& a, hipStream_t s) {
 // products into a temporary, and s (fp16, widened) scales it into the fp32 sum,
 // so no product q * s is ever rounded to bf16.
 // ---------------------------------------------------------------------------
-template <int BM, int BN, int NS, int WGM = 2, int WGN = 2, bool RU = false>
+template <int BM, int BN, int NS, int WGM, int WGN>
 struct GemmW4Tile {
   static constexpr int WM = BM / WGM, WN = BN / WGN;
   static constexpr int MT = WM / 16, NT = WN / 16;
   static_assert(WGM * WGN == 4 && MT >= 1 && NT >= 1, "four wavefronts");
   // a stage: A tile, W codes, and one 1 KiB slot whose first BN * 2 bytes are the
-  // group's scales for the tile's columns (8 copies of the 128 bytes)
+  // group's scales for the tile's columns
   static constexpr int ASTAGE = BM * 256, WSTAGE = BN * 64, STAGE = ASTAGE + WSTAGE + 1024;
   static constexpr int ALOADS = BM / 4 / 4, WLOADS = BN / 16 / 4;  // DMA loads per wavefront
   static constexpr int LOADS = ALOADS + WLOADS;  // wavefront 0 adds the scale load
   // one scale DMA (16 bytes per lane) covers the tile's BN columns: lane % (BN / 8)
   // picks a 16-byte piece, repeated across the 1 KiB slot
   static_assert(BN % 64 == 0 && BN <= 512, "one scale DMA covers the tile's columns");
-  static constexpr int WBP = 128 + 8;  // bf16 pitch of the widened W tile
-  static constexpr int LDS = NS * STAGE + (RU ? 0 : BN * WBP * 2);
+  static constexpr int LDS = NS * STAGE;
 };
 
-// RU (register unpack): no widened tile. Each lane reads its 8 codes of a B
-// fragment as one 32-bit word and unpacks them in registers as in the decode
-// GEMV: u = q + 8 (sign bit flipped), a pair of nibbles masked into a bf16 pair
-// with the exponent of 128 is (128 + u_k, 128 + u_k+4), so the fragment holds the
-// pairs (k0, k4), (k1, k5), (k2, k6), (k3, k7); the A fragment is permuted to the
-// same order (the product over a K slice does not depend on the order of k).
-// Per group, P = sum_k a (128 + u) and S = sum_k a (one more MFMA against ones)
-// give sum_k a q = P - 136 S, scaled by the column's fp16 scale in fp32.
-template <int EPI, int BM, int BN, int NS, int WGM = 2, int WGN = 2, bool RU = false>
+// The codes are unpacked in registers: each lane reads the 8 codes of its B
+// fragment as one 32-bit word and unpacks them as in the decode GEMV: u = q + 8
+// (sign bit flipped), a pair of nibbles masked into a bf16 pair with the exponent
+// of 128 is (128 + u_k, 128 + u_k+4), so the fragment holds the pairs (k0, k4),
+// (k1, k5), (k2, k6), (k3, k7); the A fragment is permuted to the same order (the
+// product over a K slice does not depend on the order of k). Per group,
+// P = sum_k a (128 + u) and S = sum_k a (one more MFMA against ones) give
+// sum_k a q = P - 136 S, scaled by the column's fp16 scale in fp32.
+template <int EPI, int BM, int BN, int NS, int WGM, int WGN>
 __global__ __launch_bounds__(256) void gemm_w4_kernel(GemmArgs a, int tiles_m, int tiles,
                                                       int ksteps) {
-  using G = GemmW4Tile<BM, BN, NS, WGM, WGN, RU>;
+  using G = GemmW4Tile<BM, BN, NS, WGM, WGN>;
   constexpr int MT = G::MT, NT = G::NT, LOADS = G::LOADS;
   static_assert(LOADS * (NS - 1) <= 63 && NS - 2 <= 6 && G::WLOADS >= 1, "shape");
   __shared__ __attribute__((aligned(1024))) unsigned char smem[G::LDS];
-  bf16_t* wb = (bf16_t*)(smem + NS * G::STAGE);  // widened W tile (not with RU)
 
   const int per_xcd = (tiles + kXcds - 1) / kXcds;
   const int slot = blockIdx.x % (kXcds * per_xcd);
@@ -465,106 +463,60 @@ __global__ __launch_bounds__(256) void gemm_w4_kernel(GemmArgs a, int tiles_m, i
       sc[ni] = __half2float(
           *(const __half*)(st + G::ASTAGE + G::WSTAGE + (wn * G::WN + ni * 16 + (lane & 15)) * 2));
     issue(kt + NS - 1);
-    if constexpr (RU) {
-      f32x4_t tmp[MT][NT], tsum[MT];
+    f32x4_t tmp[MT][NT], tsum[MT];
 #pragma unroll
-      for (int i = 0; i < MT; ++i) {
-        tsum[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int i = 0; i < MT; ++i) {
+      tsum[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int j = 0; j < NT; ++j) tmp[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      for (int j = 0; j < NT; ++j) tmp[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    }
+    const bf16x8_t ones = __builtin_bit_cast(
+        bf16x8_t, u32x4_t{0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u});
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      // B: the 8 codes of K positions ks*32 + 8*(lane/16) .. +7 of column lane%16
+      bf16x8_t bf[NT];
+#pragma unroll
+      for (int ni = 0; ni < NT; ++ni) {
+        const int r = wn * G::WN + ni * 16 + (lane & 15);
+        const uint32_t v = *(const uint32_t*)(st + G::ASTAGE + r * 64 + ((ks ^ ((r >> 1) & 3)) << 4) +
+                                              4 * (lane >> 4)) ^ 0x88888888u;
+        bf[ni] = __builtin_bit_cast(
+            bf16x8_t, u32x4_t{(v & 0x000F000Fu) | 0x43004300u, ((v >> 4) & 0x000F000Fu) | 0x43004300u,
+                              ((v >> 8) & 0x000F000Fu) | 0x43004300u,
+                              ((v >> 12) & 0x000F000Fu) | 0x43004300u});
       }
-      const bf16x8_t ones = __builtin_bit_cast(
-          bf16x8_t, u32x4_t{0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u});
+      const int kc = ks * 4 + (lane >> 4);
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        // B: the 8 codes of K positions ks*32 + 8*(lane/16) .. +7 of column lane%16
-        bf16x8_t bf[NT];
-#pragma unroll
-        for (int ni = 0; ni < NT; ++ni) {
-          const int r = wn * G::WN + ni * 16 + (lane & 15);
-          const uint32_t v = *(const uint32_t*)(st + G::ASTAGE + r * 64 + ((ks ^ ((r >> 1) & 3)) << 4) +
-                                                4 * (lane >> 4)) ^ 0x88888888u;
-          bf[ni] = __builtin_bit_cast(
-              bf16x8_t, u32x4_t{(v & 0x000F000Fu) | 0x43004300u, ((v >> 4) & 0x000F000Fu) | 0x43004300u,
-                                ((v >> 8) & 0x000F000Fu) | 0x43004300u,
-                                ((v >> 12) & 0x000F000Fu) | 0x43004300u});
-        }
-        const int kc = ks * 4 + (lane >> 4);
-#pragma unroll
-        for (int mi = 0; mi < MT; ++mi) {
-          const int r = wm * G::WM + mi * 16 + (lane & 15);
-          const u32x4_t n = *(const u32x4_t*)(st + r * 256 + ((kc ^ (r & 15)) << 4));
-          // (x0, x1), (x2, x3), (x4, x5), (x6, x7) -> (x0, x4), (x1, x5), (x2, x6), (x3, x7)
-          const bf16x8_t af = __builtin_bit_cast(
-              bf16x8_t, u32x4_t{__builtin_amdgcn_perm(n[2], n[0], 0x05040100u),
-                                __builtin_amdgcn_perm(n[2], n[0], 0x07060302u),
-                                __builtin_amdgcn_perm(n[3], n[1], 0x05040100u),
-                                __builtin_amdgcn_perm(n[3], n[1], 0x07060302u)});
-#pragma unroll
-          for (int ni = 0; ni < NT; ++ni)
-            tmp[mi][ni] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bf[ni], tmp[mi][ni], 0, 0, 0);
-          tsum[mi] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, ones, tsum[mi], 0, 0, 0);
-        }
-      }
-#pragma unroll
-      for (int mi = 0; mi < MT; ++mi)
-#pragma unroll
-        for (int ni = 0; ni < NT; ++ni) acc[mi][ni] += sc[ni] * (tmp[mi][ni] - 136.f * tsum[mi]);
-    } else {
-      // widen the stage's W codes to bf16 (one 16-byte chunk = 32 codes per thread per pass)
-      for (int c = tid; c < BN * 4; c += 256) {
-        const int r = c >> 2, kc = c & 3;
-        const u32x4_t w = *(const u32x4_t*)(st + G::ASTAGE + r * 64 + ((kc ^ ((r >> 1) & 3)) << 4));
-        u32x4_t o[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const int q0 = (int)(w[i] << (28 - 8 * j)) >> 28;
-            const int q1 = (int)(w[i] << (24 - 8 * j)) >> 28;
-            o[i][j] = (__float_as_uint((float)q0) >> 16) | (__float_as_uint((float)q1) & 0xffff0000u);
-          }
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) *(u32x4_t*)(wb + r * G::WBP + kc * 32 + 8 * i) = o[i];
-      }
-      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-      f32x4_t tmp[MT][NT];
-#pragma unroll
-      for (int i = 0; i < MT; ++i)
-#pragma unroll
-        for (int j = 0; j < NT; ++j) tmp[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        const int kc = ks * 4 + (lane >> 4);
-        bf16x8_t bf[NT];
+      for (int mi = 0; mi < MT; ++mi) {
+        const int r = wm * G::WM + mi * 16 + (lane & 15);
+        const u32x4_t n = *(const u32x4_t*)(st + r * 256 + ((kc ^ (r & 15)) << 4));
+        // (x0, x1), (x2, x3), (x4, x5), (x6, x7) -> (x0, x4), (x1, x5), (x2, x6), (x3, x7)
+        const bf16x8_t af = __builtin_bit_cast(
+            bf16x8_t, u32x4_t{__builtin_amdgcn_perm(n[2], n[0], 0x05040100u),
+                              __builtin_amdgcn_perm(n[2], n[0], 0x07060302u),
+                              __builtin_amdgcn_perm(n[3], n[1], 0x05040100u),
+                              __builtin_amdgcn_perm(n[3], n[1], 0x07060302u)});
 #pragma unroll
         for (int ni = 0; ni < NT; ++ni)
-          bf[ni] = *(const bf16x8_t*)(wb + (wn * G::WN + ni * 16 + (lane & 15)) * G::WBP + kc * 8);
-#pragma unroll
-        for (int mi = 0; mi < MT; ++mi) {
-          const int r = wm * G::WM + mi * 16 + (lane & 15);
-          const bf16x8_t af = *(const bf16x8_t*)(st + r * 256 + ((kc ^ (r & 15)) << 4));
-#pragma unroll
-          for (int ni = 0; ni < NT; ++ni)
-            tmp[mi][ni] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bf[ni], tmp[mi][ni], 0, 0, 0);
-        }
+          tmp[mi][ni] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bf[ni], tmp[mi][ni], 0, 0, 0);
+        tsum[mi] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, ones, tsum[mi], 0, 0, 0);
       }
-#pragma unroll
-      for (int mi = 0; mi < MT; ++mi)
-#pragma unroll
-        for (int ni = 0; ni < NT; ++ni) acc[mi][ni] += sc[ni] * tmp[mi][ni];
     }
+#pragma unroll
+    for (int mi = 0; mi < MT; ++mi)
+#pragma unroll
+      for (int ni = 0; ni < NT; ++ni) acc[mi][ni] += sc[ni] * (tmp[mi][ni] - 136.f * tsum[mi]);
   }
   gemm_epilogue<EPI, MT, NT, G::WM, G::WN>(a, acc, m0, n0, z, wm, wn, lane);
 }
 
-template <int EPI, int BM = 64, int NS = 3, int WGM = 2, int WGN = 2, bool RU = false, int BN = 64>
+template <int EPI, int BM, int BN, int NS, int WGM, int WGN>
 static void gemm_w4_go(const GemmArgs& a, int splits, int ksteps, hipStream_t s) {
   const int tiles_m = (a.M + BM - 1) / BM;
   const int tiles = tiles_m * (a.N / BN);
   const int per_xcd = (tiles + kXcds - 1) / kXcds;
-  launch_k(gemm_w4_kernel<EPI, BM, BN, NS, WGM, WGN, RU>, dim3(kXcds * per_xcd * splits), dim3(256), 0, s, a,
+  launch_k(gemm_w4_kernel<EPI, BM, BN, NS, WGM, WGN>, dim3(kXcds * per_xcd * splits), dim3(256), 0, s, a,
            tiles_m, tiles, ksteps);
 }
 
@@ -601,22 +553,21 @@ static void gemm_bf16_go(const GemmArgs& a, int splits, int ksteps, hipStream_t 
            dim3(64 * WGM * WGN), 0, s, a, tiles_m, tiles, ksteps);
 }
 
-// INT4 projections. Column counts divisible by 128: 64 x 128 tiles, four
-// wavefronts along N (64 x 32 wavefront tiles), codes unpacked in
-// registers. Measured at the Llama-3-8B shape with 512 rows (cold weights):
-// gate/up 240 us against 309 us for 64 x 64 tiles widened in LDS (the activation
-// tile is re-read once per column tile, so wider tiles cut the dominant traffic),
-// down 117 us against 143 us, O 37 us against 46 us. Other column counts: 64 x 64
-// tiles with the widened LDS tile. Residual projections split the groups when
+// INT4 projections: 64 x 128 tiles, four wavefronts along N (64 x 32 wavefront
+// tiles). Every INT4 projection has N divisible by 128 (each K is a multiple of
+// 128 and N is one of those sizes or twice one). Measured at the Llama-3-8B shape
+// with 512 rows (cold weights): gate/up 240 us against 309 us for 64 x 64 tiles
+// whose codes were widened to bf16 in LDS (the activation tile is re-read once
+// per column tile, so wider tiles cut the dominant traffic), down 117 us against
+// 143 us, O 37 us against 46 us. Residual projections split the groups when
 // fewer than about 384 workgroups would run (at least 4 groups per split) and
 // reduce like the 16-bit path.
 template <int EPI>
 static void gemm_w4_pick(const GemmArgs& a, int splits, int ksteps, hipStream_t s) {
-  if (a.N % 128 == 0) gemm_w4_go<EPI, 64, 3, 1, 4, true, 128>(a, splits, ksteps, s);
-  else gemm_w4_go<EPI>(a, splits, ksteps, s);
+  gemm_w4_go<EPI, 64, 128, 3, 1, 4>(a, splits, ksteps, s);
 }
 static hipError_t gemm_w4(const GemmArgs& a, hipStream_t s) {
-  if (a.K % 128 != 0 || a.N % 64 != 0) return hipErrorInvalidValue;
+  if (a.K % 128 != 0 || a.N % 128 != 0) return hipErrorInvalidValue;
   const int ngk = a.K / 128;
   if (a.epi == EPI_SWIGLU) {
     if (a.glu) gemm_w4_pick<EPI_GEGLU_K>(a, 1, ngk, s);
@@ -630,7 +581,7 @@ static hipError_t gemm_w4(const GemmArgs& a, hipStream_t s) {
   if (a.epi != EPI_RESID) return hipErrorInvalidValue;
   if (a.ws == nullptr || (size_t)a.M * a.N > a.ws_elems) return hipErrorInvalidValue;
   if (a.N % 8 != 0 || a.N / 8 > 256 * kResidMaxChunks) return hipErrorInvalidValue;
-  const int tiles = ((a.M + 63) / 64) * (a.N / (a.N % 128 == 0 ? 128 : 64));
+  const int tiles = ((a.M + 63) / 64) * (a.N / 128);
   int splits = std::max(1, std::min(kResidMaxSplits, (384 + tiles - 1) / tiles));
   while (splits > 1 && ngk / splits < 4) --splits;
   while (splits > 1 && (size_t)splits * a.M * a.N > a.ws_elems) --splits;

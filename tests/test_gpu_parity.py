@@ -324,6 +324,34 @@ def test_bf16_long_cache_prefill_shape():
     m.close()
 
 
+def test_qwen_shape_one_layer_chunk_sizes():
+    """One layer at the Qwen2.5-1.5B shape (hidden 1536, 12/2 heads, FFN 8960; a
+    4,096-entry vocabulary): a 64-token chunk (the gated projection's 64 x 128 tiles,
+    which it takes from 128 column tiles on, and the 64 x 32 split tiles of the other
+    projections), a 256-token chunk (256 x 128 gated tiles of eight wavefronts, split
+    q/k/v and residual projections) and 2 greedy decodes."""
+    p = dict(vla.PRESETS["c2_qwen1p5b_bf16"], n_layers=1, vocab=4096, num_blocks=24,
+             max_frames=4)
+    init_std = 0.02
+    sess = D.Session(oracle_config(p, init_std=init_std))
+    m = _model(p, init_std)
+    ref = None
+    for call, n in enumerate((64, 256)):
+        x32, xs = synth.embeddings(p["seed"], call, n, p["hidden"], "bf16")
+        m.prefill_chunk(embeds=dev_from_storage(xs, "bf16"), n=n)
+        _, ref = sess.prefill_chunk(embeds=x32)
+        log("qwen-shape prefill %d cos %.6f rel %.2e" % ((n,) + metrics(logits_of(m), ref)))
+        check_logits(logits_of(m), ref, "bf16", f"qwen-shape prefill {n}")
+    tok = int(np.argmax(ref))
+    for i in range(2):
+        g = m.decode_step(tok)
+        nxt, ref = sess.decode_step(tok)
+        check_logits(logits_of(m), ref, "bf16", f"qwen-shape decode {i}")
+        check_argmax(g, ref, "bf16", f"qwen-shape decode {i}")
+        tok = nxt
+    m.close()
+
+
 def test_device_resident_tokens_chain_like_host_tokens():
     """Greedy decoding with the token kept on the device (no host round trip, no
     synchronisation per step) gives bit-identical logits and the same cache as
