@@ -641,7 +641,7 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(AttnArgs a, int rgroup
     }
   }
   __syncthreads();
-  if (threadIdx.x < nrow) {
+  if ((int)threadIdx.x < nrow) {
     const int c = threadIdx.x;
     float M = -INFINITY;
 #pragma unroll
