@@ -165,6 +165,11 @@ hipError_t launch_action_begin(const float* xa, float* h, int rows, int H, doubl
                                hipStream_t s);
 hipError_t launch_euler_step(float* xa, const float* h, const float* g, int rows, int H,
                              float eps, float dt, hipStream_t s);
+// one decode row: the token's embedding row (token_key non-null: the token is the
+// argmax key's id) and the RoPE table of position pos, in one launch
+hipError_t launch_embed_rope1(int token_scalar, const unsigned long long* token_key, const void* E,
+                              void* x, int H, int dt, int64_t pos, const double* inv_freq, int half,
+                              float2* tab, hipStream_t s);
 hipError_t launch_embed(const int* tokens, int token_scalar, const unsigned long long* token_key,
                         int n, const void* E, void* x, int H, int dt,
                         unsigned long long* reset_cell, hipStream_t s);

@@ -198,19 +198,23 @@ hipError_t launch_weight_logical(const void* phys, void* out, int dt, int layout
 }
 
 // ---------------------------------------------------------------------------
+// entry p = t * half + j of the table: (cos, sin) of (pos0 + t) * inv_freq[j]
+__device__ __forceinline__ void rope_entry(int64_t p, int64_t pos0, const double* inv_freq,
+                                           int half, float2* tab) {
+  const int64_t t = p / half;
+  const int j = (int)(p % half);
+  const double ang = (double)(pos0 + t) * inv_freq[j];
+  const double red = fma(-rint(ang * 0.15915494309189535), 6.283185307179586, ang);
+  float sn, cs;
+  sincosf((float)red, &sn, &cs);
+  tab[p] = make_float2(cs, sn);
+}
 __global__ void rope_table_kernel(int64_t pos0, int n, const double* inv_freq, int half,
                                   float2* tab) {
   const int64_t total = (int64_t)n * half;
   for (int64_t p = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; p < total;
-       p += (int64_t)gridDim.x * blockDim.x) {
-    const int64_t t = p / half;
-    const int j = (int)(p % half);
-    const double ang = (double)(pos0 + t) * inv_freq[j];
-    const double red = fma(-rint(ang * 0.15915494309189535), 6.283185307179586, ang);
-    float sn, cs;
-    sincosf((float)red, &sn, &cs);
-    tab[p] = make_float2(cs, sn);
-  }
+       p += (int64_t)gridDim.x * blockDim.x)
+    rope_entry(p, pos0, inv_freq, half, tab);
 }
 hipError_t launch_rope_table(int64_t pos0, int n, const double* inv_freq, int half, float2* tab,
                              hipStream_t s) {
@@ -244,6 +248,31 @@ __global__ void embed_kernel(const int* tokens, int token_scalar, const unsigned
     for (int i = threadIdx.x; i < H; i += blockDim.x)
       x[(int64_t)t * H + i] = St<T>::ld(E, id * H + i);
   }
+}
+// one decode row: block 0 gathers the token's embedding row, block 1 writes the
+// row's RoPE table (one launch instead of two at the start of a decode step)
+template <typename T>
+__global__ void embed_rope1_kernel(int token_scalar, const unsigned long long* token_key,
+                                   const T* E, float* x, int H, int64_t pos, const double* inv_freq,
+                                   int half, float2* tab) {
+  if (blockIdx.x == 0) {
+    const int64_t id = token_key ? (int64_t)(0xffffffffu - (uint32_t)(*token_key & 0xffffffffull))
+                                 : token_scalar;
+    for (int i = threadIdx.x; i < H; i += blockDim.x) x[i] = St<T>::ld(E, id * H + i);
+  } else {
+    for (int p = threadIdx.x; p < half; p += blockDim.x) rope_entry(p, pos, inv_freq, half, tab);
+  }
+}
+hipError_t launch_embed_rope1(int token_scalar, const unsigned long long* token_key, const void* E,
+                              void* x, int H, int dt, int64_t pos, const double* inv_freq, int half,
+                              float2* tab, hipStream_t s) {
+  if (dt == DT_F32)
+    embed_rope1_kernel<float><<<2, 256, 0, s>>>(token_scalar, token_key, (const float*)E, (float*)x,
+                                                H, pos, inv_freq, half, tab);
+  else
+    embed_rope1_kernel<bf16_t><<<2, 256, 0, s>>>(token_scalar, token_key, (const bf16_t*)E,
+                                                 (float*)x, H, pos, inv_freq, half, tab);
+  return hipGetLastError();
 }
 hipError_t launch_embed(const int* tokens, int token_scalar, const unsigned long long* token_key,
                         int n, const void* E, void* x, int H, int dt,

@@ -338,13 +338,14 @@ GemvArgs decode_gateup_args(vla_model* m, int l) {
 // the per-layer launches of one pass over n rows whose K/V go to logical slots
 // (cb0, cslot0 ...); rows = prefill chunk (n >= 1, matrix path) or decode (GEMV path)
 void run_layers(vla_model* m, const KvView& view, int n, int64_t pos0, int cb0, int cslot0,
-                bool decode, hipStream_t st) {
+                bool decode, hipStream_t st, bool rope_ready = false) {
   const vla_config& c = m->cfg;
   const int H = c.hidden, qd = c.n_heads * c.head_dim;
   const int nqkv = (c.n_heads + 2 * c.n_kv_heads) * c.head_dim;
   const int glu = c.ffn_kind == VLA_GEGLU ? 1 : 0;
-  // the rows' RoPE (cos, sin), shared by every layer of this pass
-  HIPCHK(launch_rope_table(pos0, n, m->inv_freq, c.head_dim / 2, m->rope_tab, st));
+  // the rows' RoPE (cos, sin), shared by every layer of this pass (a decode step
+  // writes it in its embedding launch)
+  if (!rope_ready) HIPCHK(launch_rope_table(pos0, n, m->inv_freq, c.head_dim / 2, m->rope_tab, st));
   AttnArgs at;
   at.q = m->qbuf;
   at.out = m->ao;
@@ -809,10 +810,12 @@ vla_status vla_decode_step(vla_model* m, int32_t token, int32_t* out_next_token,
     try {
       sync_meta(m, st);
       const int cb0 = logical_blocks(m) - 1;
-      // VLA_TOKEN_DEVICE: the previous forward's greedy token, read on the device
-      HIPCHK(launch_embed(nullptr, token, token == VLA_TOKEN_DEVICE ? m->amax_res : nullptr, 1,
-                          m->embed, m->x, m->cfg.hidden, m->dt, nullptr, st));
-      run_layers(m, model_view(m), 1, pos, cb0, off % bt, /*decode=*/true, st);
+      // VLA_TOKEN_DEVICE: the previous forward's greedy token, read on the device;
+      // the same launch writes the position's RoPE table
+      HIPCHK(launch_embed_rope1(token, token == VLA_TOKEN_DEVICE ? m->amax_res : nullptr, m->embed,
+                                m->x, m->cfg.hidden, m->dt, pos, m->inv_freq,
+                                m->cfg.head_dim / 2, m->rope_tab, st));
+      run_layers(m, model_view(m), 1, pos, cb0, off % bt, /*decode=*/true, st, /*rope_ready=*/true);
       run_head(m, 0, st);
     } catch (...) {
       tail.ntok -= 1;
