@@ -189,6 +189,194 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_kernel(GemmArgs a, i
   gemm_epilogue<EPI, MT, NT, G::WM, G::WN>(a, acc, m0, n0, z, wm, wn, lane);
 }
 
+// ---------------------------------------------------------------------------
+// Two-stream GEMM for 256-row M tiles with a wide N (the gated projection of a
+// 256-token prefill). The activation tile (L2-resident, re-read by every column
+// group) and the weight tile (streamed from HBM once) travel in two LDS rings of
+// different depths, each filled by its own two producer wavefronts with
+// global_load_lds DMA. Vector-memory counters retire in issue order per
+// wavefront, so a ring's producers wait only for their own stream: the weight
+// ring keeps NSW-1 32-deep steps in flight (the HBM latency needs about 100 KB per
+// CU) while the activation ring stays short. Four consumer wavefronts (64 rows
+// each, every column of the group) read both operands from LDS; one barrier per
+// K step hands both stages over. Columns are dealt out in units of 32 (one
+// interleaved gate/up block, or 16 RoPE pairs), each workgroup taking a
+// contiguous run of floor or ceil of units/groups, so a launch covers every
+// column in about one round of workgroups.
+// ---------------------------------------------------------------------------
+template <int NTM, int NSA, int NSW>
+struct Ws2Tile {
+  static constexpr int ASTAGE = 256 * 64;            // 256 rows x 32 bf16
+  static constexpr int WROWS = NTM * 16;
+  static constexpr int WSTAGE = WROWS * 64;          // WROWS x 32 bf16
+  static constexpr int ALOADS = ASTAGE / 1024 / 2;   // DMA loads per activation producer
+  static constexpr int WLOADS = WSTAGE / 1024 / 2;   // DMA loads per weight producer
+  static constexpr int LDS = NSA * ASTAGE + NSW * WSTAGE;
+  static_assert(WSTAGE % 2048 == 0 && ALOADS * (NSA - 2) <= 63 && WLOADS * (NSW - 2) <= 63 &&
+                    LDS <= 160 * 1024,
+                "ring shape");
+  static_assert(NTM == 2 || NTM == 4 || NTM == 6, "tile counts");
+  // chunk position of K chunk kc (0..3) in LDS row r: 16 rows read at one chunk
+  // column fall in distinct 16-byte bank groups
+  static __device__ __forceinline__ int pos(int r, int kc) { return kc ^ ((r >> 1) & 3); }
+};
+
+// wait until at most N of this wavefront's vector-memory operations are outstanding
+template <int N>
+__device__ __forceinline__ void wait_vmcnt_le() {
+  static_assert(N >= 0 && N <= 63, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | 0x70 | 0xF00 | ((N >> 4) << 14));
+}
+
+// producer wavefront of one ring: rows [row0, row0 + LOADS*16) of each stage; a
+// DMA load fills 1 KiB = 16 rows of 64 bytes, lane i writing chunk position i % 4
+// of row i / 4 with the K chunk that position holds
+template <int LOADS, int NS, int STAGE>
+__device__ __forceinline__ void ws2_produce(unsigned char* ring, const bf16_t* (&src)[LOADS],
+                                            int lds_off, int nk) {
+  auto issue = [&](int kt) {
+    unsigned char* st = ring + (kt % NS) * STAGE + lds_off;
+    const int kd = kt < nk ? kt : nk - 1;  // past the end: the last step again (never read)
+#pragma unroll
+    for (int j = 0; j < LOADS; ++j)
+      __builtin_amdgcn_global_load_lds((const void*)(src[j] + (int64_t)kd * 32),
+                                       (__attribute__((address_space(3))) void*)(st + j * 1024),
+                                       16, 0, 0);
+  };
+#pragma unroll
+  for (int s0 = 0; s0 < NS - 1; ++s0) issue(s0);
+  for (int kt = 0; kt < nk; ++kt) {
+    wait_vmcnt_le<LOADS * (NS - 2)>();  // stage kt of this ring has landed
+    asm volatile("s_barrier" ::: "memory");
+    issue(kt + NS - 1);                 // into the slot of stage kt-1, read before this barrier
+  }
+  __builtin_amdgcn_s_waitcnt(0);        // no DMA outstanding at exit
+}
+
+// consumer wavefront c of CW: rows (256/CW)c .. of the M tile, NTC 16-column tiles
+template <int EPI, int NTC, int NTM, int NSA, int NSW, int CW>
+__device__ __forceinline__ void ws2_consume(const GemmArgs& a, const unsigned char* smem, int nk,
+                                            int n0, int m0, int c, int lane) {
+  using T = Ws2Tile<NTM, NSA, NSW>;
+  constexpr int RPW = 256 / CW, MT = RPW / 16;  // rows and 16-row tiles per consumer
+  f32x4_t acc[MT][NTC];
+#pragma unroll
+  for (int i = 0; i < MT; ++i)
+#pragma unroll
+    for (int j = 0; j < NTC; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  const int kc = lane >> 4;
+  for (int kt = 0; kt < nk; ++kt) {
+    asm volatile("s_barrier" ::: "memory");  // both stages of step kt are in LDS
+    const unsigned char* sa = smem + (kt % NSA) * T::ASTAGE;
+    const unsigned char* sw = smem + NSA * T::ASTAGE + (kt % NSW) * T::WSTAGE;
+    bf16x8_t bf[NTC];
+#pragma unroll
+    for (int ni = 0; ni < NTC; ++ni) {
+      const int r = ni * 16 + (lane & 15);
+      bf[ni] = *(const bf16x8_t*)(sw + r * 64 + (T::pos(r, kc) << 4));
+    }
+#pragma unroll
+    for (int mi = 0; mi < MT; ++mi) {
+      const int r = RPW * c + 16 * mi + (lane & 15);
+      const bf16x8_t af = *(const bf16x8_t*)(sa + r * 64 + (T::pos(r, kc) << 4));
+#pragma unroll
+      for (int ni = 0; ni < NTC; ++ni)
+        acc[mi][ni] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bf[ni], acc[mi][ni], 0, 0, 0);
+    }
+    // this step's LDS reads are complete before the barrier that lets them be refilled
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  }
+  // accumulator element e of tile (mi, ni) is row 4*(lane/16)+e, column lane%16
+  const int M = a.M;
+#pragma unroll
+  for (int mi = 0; mi < MT; ++mi) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int row = m0 + RPW * c + 16 * mi + 4 * (lane >> 4) + e;
+#pragma unroll
+      for (int ni = 0; ni < NTC; ++ni) {
+        const float v = acc[mi][ni][e];
+        if constexpr (kGated<EPI>) {
+          // tiles (ni, ni+1), ni even: 16 gate columns, then the 16 matching up columns
+          if ((ni & 1) == 0) {
+            const bf16_t o =
+                bf16_rne(glu_fast<EPI == EPI_GEGLU_K>(v, acc[mi][ni + 1 < NTC ? ni + 1 : ni][e]));
+            if (row < M) ((bf16_t*)a.C)[(size_t)row * (a.N / 2) + (n0 + ni * 16) / 2 + (lane & 15)] = o;
+          }
+        } else {  // EPI_QKV
+          const int col = n0 + ni * 16 + (lane & 15);
+          const float partner = __shfl_xor(v, 1, 64);
+          if (row < M && (col & 1) == 0) epi_qkv_pair<bf16_t>(a.ctx, row, col, v, partner);
+        }
+      }
+    }
+  }
+}
+
+template <int EPI, int NTM, int NSA, int NSW, int CW>
+__global__ __launch_bounds__(64 * (CW + 4)) void gemm_ws2_kernel(GemmArgs a, int units, int groups,
+                                                                 int tiles_m) {
+  using T = Ws2Tile<NTM, NSA, NSW>;
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[T::LDS];
+  // workgroup -> (M tile mt, column group g); the M tiles of one group sit 8
+  // workgroups apart, i.e. on one XCD, where they share the weights
+  const int g8 = (groups + 7) & ~7;
+  const int r = blockIdx.x % (g8 * tiles_m);
+  const int mt = (r % (8 * tiles_m)) / 8;
+  const int g = (r / (8 * tiles_m)) * 8 + r % 8;
+  if (g >= groups) return;  // the whole workgroup
+  const int u0 = (int)((int64_t)g * units / groups), u1 = (int)((int64_t)(g + 1) * units / groups);
+  const int n0 = u0 * 32, nc = (u1 - u0) * 32;
+  const int M = a.M, K = a.K, nk = K / 32, m0 = mt * 256;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (wave >= CW + 2) {  // weight producers: rows of the group (past its columns: a row inside it)
+    const int p = wave - CW - 2;
+    const bf16_t* src[T::WLOADS];
+#pragma unroll
+    for (int j = 0; j < T::WLOADS; ++j) {
+      const int row = (p * T::WLOADS + j) * 16 + (lane >> 2);
+      src[j] = (const bf16_t*)a.W + (int64_t)(n0 + row % nc) * K + T::pos(row, lane & 3) * 8;
+    }
+    ws2_produce<T::WLOADS, NSW, T::WSTAGE>(smem + NSA * T::ASTAGE, src, p * T::WLOADS * 1024, nk);
+    return;
+  }
+  if (wave >= CW) {  // activation producers: the M tile's rows (past M: row M-1)
+    const int p = wave - CW;
+    const bf16_t* src[T::ALOADS];
+#pragma unroll
+    for (int j = 0; j < T::ALOADS; ++j) {
+      const int row = (p * T::ALOADS + j) * 16 + (lane >> 2);
+      src[j] = (const bf16_t*)a.A + (int64_t)min(m0 + row, M - 1) * K + T::pos(row, lane & 3) * 8;
+    }
+    ws2_produce<T::ALOADS, NSA, T::ASTAGE>(smem, src, p * T::ALOADS * 1024, nk);
+    return;
+  }
+  switch (nc / 16) {
+    case NTM: ws2_consume<EPI, NTM, NTM, NSA, NSW, CW>(a, smem, nk, n0, m0, wave, lane); break;
+    case (NTM > 2 ? NTM - 2 : NTM):
+      ws2_consume<EPI, (NTM > 2 ? NTM - 2 : NTM), NTM, NSA, NSW, CW>(a, smem, nk, n0, m0, wave,
+                                                                     lane);
+      break;
+    default:
+      ws2_consume<EPI, (NTM > 4 ? NTM - 4 : 2), NTM, NSA, NSW, CW>(a, smem, nk, n0, m0, wave, lane);
+      break;
+  }
+}
+
+// about `target` workgroups over (M tiles x column groups); a group holds at most
+// NTM*16 columns
+template <int EPI, int NTM, int NSA, int NSW, int CW = 4>
+static void gemm_ws2_go(const GemmArgs& a, int target, hipStream_t s) {
+  const int units = a.N / 32;
+  const int tiles_m = (a.M + 255) / 256;
+  int groups = std::max(1, target / tiles_m);
+  groups = std::max(groups, (units + NTM / 2 - 1) / (NTM / 2));
+  groups = std::min(groups, units);
+  const int g8 = (groups + 7) & ~7;
+  launch_k(gemm_ws2_kernel<EPI, NTM, NSA, NSW, CW>, dim3(tiles_m * g8), dim3(64 * (CW + 4)), 0, s,
+           a, units, groups, tiles_m);
+}
+
 // x[row] += sum over splits of the partials (split order), x the fp32 residual;
 // then, if u is given, u[row] = RMSNorm(x[row]) in bf16 with fp32 statistics.
 // One workgroup per row; each thread keeps up to 4 chunks of 8 columns in registers.
@@ -599,7 +787,8 @@ static hipError_t gemm_w4(const GemmArgs& a, hipStream_t s) {
 //    when that makes at least 128 workgroups (64 x 17920 x 1536: 17.7 us against
 //    20.3 us for 64 x 64), else 64 x 32 tiles with 4 wavefronts along M (63 x 8192 x
 //    1024: 6.2 us against 10.1 us for 64 x 128); up to 128 rows -> 128 x 64 in a
-//    3-stage ring; more rows -> 256 x 128 with 8
+//    3-stage ring; 129 to 256 rows -> the two-stream kernel (separate activation and
+//    weight rings, 256 x 17920 x 1536: 30.9 us against 34.5 us); more rows -> 256 x 128 with 8
 //    wavefronts (4 x 2 grid of 64 x 64 wavefront tiles), 32-deep steps (256 x 17920 x
 //    1536: 34 us against 37 us for 128 x 64 and 39 us for 64 x 64), or 256 x 256 (64 x
 //    128 wavefront tiles, 3-stage ring) when that still makes about 192 workgroups:
@@ -622,6 +811,8 @@ static void gated_go(const GemmArgs& a, hipStream_t s) {
     gemm_bf16_go<EPI, 64, 128, 64, 4>(a, 1, a.K / 64, s);
   else if (a.M <= 64)
     gemm_bf16_go<EPI, 64, 32, 64, 4, 4, 1>(a, 1, a.K / 64, s);
+  else if (a.M > 128 && a.M <= 256 && a.N % 32 == 0)
+    gemm_ws2_go<EPI, 6, 4, 8>(a, 256, s);
   else if (a.M > 128 && a.N % 256 == 0 && ((a.M + 255) / 256) * (a.N / 256) >= 192)
     gemm_bf16_go<EPI, 256, 256, 32, 3, 4, 2>(a, 1, a.K / 32, s);
   else if (a.M > 128 && a.N % 128 == 0)
