@@ -190,8 +190,8 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_kernel(GemmArgs a, i
 }
 
 // ---------------------------------------------------------------------------
-// Two-stream GEMM for 256-row M tiles with a wide N (the gated projection of a
-// 256-token prefill). The activation tile (L2-resident, re-read by every column
+// Two-stream GEMM for 256-row M tiles with a wide N: the gated projection of a
+// 129- to 256-token prefill. The activation tile (L2-resident, re-read by every column
 // group) and the weight tile (streamed from HBM once) travel in two LDS rings of
 // different depths, each filled by its own two producer wavefronts with
 // global_load_lds DMA. Vector-memory counters retire in issue order per
@@ -257,6 +257,7 @@ __device__ __forceinline__ void ws2_produce(unsigned char* ring, const bf16_t* (
 template <int EPI, int NTC, int NTM, int NSA, int NSW, int CW>
 __device__ __forceinline__ void ws2_consume(const GemmArgs& a, const unsigned char* smem, int nk,
                                             int n0, int m0, int c, int lane) {
+  static_assert(kGated<EPI>, "gated projections (the SwiGLU / GeGLU epilogue) only");
   using T = Ws2Tile<NTM, NSA, NSW>;
   constexpr int RPW = 256 / CW, MT = RPW / 16;  // rows and 16-row tiles per consumer
   f32x4_t acc[MT][NTC];
@@ -296,17 +297,11 @@ __device__ __forceinline__ void ws2_consume(const GemmArgs& a, const unsigned ch
 #pragma unroll
       for (int ni = 0; ni < NTC; ++ni) {
         const float v = acc[mi][ni][e];
-        if constexpr (kGated<EPI>) {
-          // tiles (ni, ni+1), ni even: 16 gate columns, then the 16 matching up columns
-          if ((ni & 1) == 0) {
-            const bf16_t o =
-                bf16_rne(glu_fast<EPI == EPI_GEGLU_K>(v, acc[mi][ni + 1 < NTC ? ni + 1 : ni][e]));
-            if (row < M) ((bf16_t*)a.C)[(size_t)row * (a.N / 2) + (n0 + ni * 16) / 2 + (lane & 15)] = o;
-          }
-        } else {  // EPI_QKV
-          const int col = n0 + ni * 16 + (lane & 15);
-          const float partner = __shfl_xor(v, 1, 64);
-          if (row < M && (col & 1) == 0) epi_qkv_pair<bf16_t>(a.ctx, row, col, v, partner);
+        // tiles (ni, ni+1), ni even: 16 gate columns, then the 16 matching up columns
+        if ((ni & 1) == 0) {
+          const bf16_t o =
+              bf16_rne(glu_fast<EPI == EPI_GEGLU_K>(v, acc[mi][ni + 1 < NTC ? ni + 1 : ni][e]));
+          if (row < M) ((bf16_t*)a.C)[(size_t)row * (a.N / 2) + (n0 + ni * 16) / 2 + (lane & 15)] = o;
         }
       }
     }
