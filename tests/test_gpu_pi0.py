@@ -114,6 +114,29 @@ def test_geglu_head_dim_256_prefill_and_decode():
     m.close()
 
 
+def test_geglu_gated_tile_shapes():
+    """GeGLU through the gated projection's 65-128-row (128 x 64 tiles) and 129-256-row
+    (two-stream kernel) paths: chunks of 100 and 160 tokens, then 3 greedy decodes."""
+    p = dict(TINY_VLM, vocab=800, kv_only_last=0, num_blocks=24, max_chunk=160, seed=63)
+    ocfg = _ocfg(p, "geglu_tiles", 0.05)
+    sess = D.Session(ocfg)
+    m = vla.Model(vla.make_config(**p, init_std=0.05))
+    ref = None
+    for call, n in enumerate((100, 160)):
+        ids = synth.token_ids(p["seed"], call, n, p["vocab"])
+        m.prefill_chunk(tokens=ids)
+        _, ref = sess.prefill_chunk(tokens=ids)
+        check_logits(logits_of(m), ref, "bf16", f"geglu prefill {n}")
+    tok = int(np.argmax(ref))
+    for i in range(3):
+        g = m.decode_step(tok)
+        nxt, ref = sess.decode_step(tok)
+        check_logits(logits_of(m), ref, "bf16", f"geglu tiles decode {i}")
+        check_argmax(g, ref, "bf16", f"geglu tiles decode {i}")
+        tok = nxt
+    m.close()
+
+
 def test_pi0_full_shape_policy_step():
     """The workload's own shapes: Gemma-2B-shaped prefix (17 layers + K/V-only 18th)
     over 2 x 256 image-token embeddings, the 300M expert on a 63-token chunk, 10
