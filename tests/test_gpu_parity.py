@@ -297,10 +297,11 @@ def test_bf16_long_context_split_attention():
 
 
 def test_bf16_long_cache_prefill_shape():
-    """More than 256 resident blocks (300 blocks of raw frames, then a 120-token chunk),
-    so the prefill attention takes its long-cache shape (256-row workgroups, 4-stage
-    ring, split keys + merge); then 3 greedy decodes."""
-    p = dict(TINY_BF16, num_blocks=320, max_frames=80, max_chunk=120)
+    """More than 256 resident blocks (300 blocks of raw frames), then a 120-token chunk
+    (360 query rows per KV head: the 64-row workgroups with many key splits) and a
+    180-token chunk (540 rows: the long-cache shape, 256-row workgroups, 4-stage ring);
+    each splits the keys and merges; then 3 greedy decodes."""
+    p = dict(TINY_BF16, num_blocks=330, max_frames=80, max_chunk=180)
     init_std = 0.08
     ocfg = oracle_config(p, init_std=init_std)
     sess = D.Session(ocfg)
@@ -310,10 +311,12 @@ def test_bf16_long_cache_prefill_shape():
         (k32, v32), (ks, vs) = synth.raw_kv_frame(12, f, L, 64, hkv, d, "bf16")
         fid = m.kv_append_raw(dev_from_storage(ks, "bf16"), dev_from_storage(vs, "bf16"), 64)
         assert fid == sess.append_raw(k32, v32)
-    x32, xs = synth.embeddings(p["seed"], 0, 120, p["hidden"], "bf16")
-    m.prefill_chunk(embeds=dev_from_storage(xs, "bf16"), n=120)
-    _, ref = sess.prefill_chunk(embeds=x32)
-    check_logits(logits_of(m), ref, "bf16", "long-cache prefill")
+    ref = None
+    for call, n in enumerate((120, 180)):
+        x32, xs = synth.embeddings(p["seed"], call, n, p["hidden"], "bf16")
+        m.prefill_chunk(embeds=dev_from_storage(xs, "bf16"), n=n)
+        _, ref = sess.prefill_chunk(embeds=x32)
+        check_logits(logits_of(m), ref, "bf16", f"long-cache prefill {n}")
     tok = int(np.argmax(ref))
     for i in range(3):
         g = m.decode_step(tok)
