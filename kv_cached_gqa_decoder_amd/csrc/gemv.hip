@@ -551,118 +551,188 @@ __device__ __forceinline__ float w4_dot2(uint32_t a, uint32_t b, float acc) {
   return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2v_t, a),
                                          __builtin_bit_cast(bf16x2v_t, b), acc, false);
 }
-// sum over one chunk (4 words of codes) of (128 + u_k) x_k
+// sum over one chunk (4 words of codes) of (128 + u_k) x_k; one v_bitop3 per
+// pair masks the two nibbles into place and, in the same operation, flips their
+// sign bits and sets the bf16 exponent of 128 ((t & 0x000F000F) ^ 0x43084308)
 __device__ __forceinline__ float w4_chunk(const u32x4_t& w, const uint32_t (&xp)[16]) {
   float acc = 0.f;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const uint32_t v = w[i] ^ 0x88888888u;
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int p = 0; p < 4; ++p)
-      acc = w4_dot2(((v >> (4 * p)) & 0x000F000Fu) | 0x43004300u, xp[4 * i + p], acc);
-  }
+    for (int p = 0; p < 4; ++p) {
+      const uint32_t t = p ? w[i] >> (4 * p) : w[i];
+      acc = w4_dot2(__builtin_amdgcn_bitop3_b32(t, 0x43084308u, 0x000F000Fu, 0x6C), xp[4 * i + p], acc);
+    }
   return acc;
 }
 
 
-// Streaming INT4 GEMV: same row groups, grid and epilogues as the 16-bit
-// kernel; the input row is staged once per workgroup in LDS as bf16 pairs (the
-// normalised residual, or the bf16 activations), and each chunk's input pairs
-// and their sum are read once for the wavefront's RW rows.
-template <int EPI, int RW>
-__global__ __launch_bounds__(kGemvThreads) void gemv_w4_kernel(GemvArgs a, int ngroups) {
+// Streaming INT4 GEMV: same row groups and epilogues as the 16-bit kernel. A
+// wavefront walks its (row group, block of 64 * UNR chunks per row) steps; per
+// step every code and scale load of the step is issued before any is used
+// (chunk indexes past the row are clamped, their scale zeroed at use, so the
+// loads carry no branches). The input row is read once into registers (XG groups
+// of 8 per thread), the first step's loads go out right behind it, and the row
+// is then staged in LDS as bf16 pairs (normalised residual, or bf16 activations)
+// while those loads are in flight. ONE: exactly one row group per wavefront and
+// one step per row (the whole row in flight at once, no loop).
+template <int UNR, int RW>
+struct W4Step {
+  u32x4_t w[UNR][RW];
+  uint16_t sc[UNR][RW];  // fp16 bits
+};
+
+template <int EPI, int RW, int UNR, int NW, int XG, bool ONE>
+__global__ __launch_bounds__(64 * NW) void gemv_w4_kernel(GemvArgs a, int ngroups) {
   extern __shared__ __attribute__((aligned(16))) unsigned char gsmem[];
   uint32_t* xsh = (uint32_t*)gsmem;  // K/2 words: the input as bf16 pairs
-  __shared__ float ssq[kGemvWaves];
-  __shared__ unsigned long long wbest[kGemvWaves];
-  constexpr int UNR = RW >= 8 ? 1 : (RW >= 4 ? 2 : 4);  // 8 chunk loads (256 codes) in flight
+  __shared__ float ssq[NW];
+  __shared__ unsigned long long wbest[NW];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int K = a.K;
-  const int nch = K / 32;
+  const int K = a.K, nch = K / 32, ng8 = K / 8;
+  constexpr int PER = 64 * UNR;  // chunks per row per step
+  const int nit = ONE ? 1 : (nch + PER - 1) / PER;
+  const int stride = gridDim.x * NW;
+  const uint8_t* W = (const uint8_t*)a.W;
+  const uint16_t* Sc16 = (const uint16_t*)(W + (size_t)a.N * K / 2);
 
-  // input row -> LDS as bf16 pairs (the normalised residual, or the bf16 activations)
+  // ---- the input row, one load round trip ----
+  f32x4_t xr[XG][2], gr[XG][2];
+  u32x4_t xb[XG];
+#pragma unroll
+  for (int k = 0; k < XG; ++k) {
+    int gi = tid + k * 64 * NW;
+    gi = gi < ng8 ? gi : ng8 - 1;
+    if constexpr (EPI != EPI_RESID) {
+      const f32x4_t* xf4 = (const f32x4_t*)a.x;
+      xr[k][0] = xf4[2 * gi];
+      xr[k][1] = xf4[2 * gi + 1];
+      if (a.norm_g) {
+        const f32x4_t* g4 = (const f32x4_t*)a.norm_g;
+        gr[k][0] = g4[2 * gi];
+        gr[k][1] = g4[2 * gi + 1];
+      }
+    } else {
+      xb[k] = *(const u32x4_t*)((const bf16_t*)a.x + (size_t)gi * 8);
+    }
+  }
+
+  // ---- load cursor: (group lg, chunk block lit) ----
+  int lg = blockIdx.x * NW + wave, lit = 0;
+  W4Step<UNR, RW> st;
+  auto load = [&]() {
+    const int gg = __builtin_amdgcn_readfirstlane(lg < ngroups ? lg : ngroups - 1);
+    const uint8_t* wrow[RW];
+    const uint16_t* srow[RW];
+#pragma unroll
+    for (int r = 0; r < RW; ++r) {  // rows past N (a partial last group) re-read row N-1
+      const int64_t row0 = gemv_row<EPI, RW>(gg, r);
+      const int64_t row = row0 < a.N ? row0 : (int64_t)a.N - 1;
+      wrow[r] = W + row * (K / 2);
+      srow[r] = Sc16 + row;
+    }
+#pragma unroll
+    for (int u = 0; u < UNR; ++u) {
+      int c = lane + lit * PER + 64 * u;
+      c = c < nch ? c : nch - 1;
+      const uint32_t wo = (uint32_t)c * 16u, so = (uint32_t)(c / 4) * (uint32_t)a.N;
+#pragma unroll
+      for (int r = 0; r < RW; ++r) {
+        st.w[u][r] = *(const u32x4_t*)(wrow[r] + wo);
+        st.sc[u][r] = srow[r][so];
+      }
+    }
+    if (++lit == nit) {
+      lit = 0;
+      lg += stride;
+    }
+  };
+  load();
+
+  // ---- input -> LDS as bf16 pairs ----
   if constexpr (EPI != EPI_RESID) {
-    const f32x4_t* xf4 = (const f32x4_t*)a.x;
-    const f32x4_t* g4 = (const f32x4_t*)a.norm_g;
     float rn = 1.f;
     if (a.norm_g) {
       float ss = 0.f;
-      for (int i = tid; i < K / 4; i += kGemvThreads) {
-        const f32x4_t v = xf4[i];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) ss += v[e] * v[e];
-      }
+      for (int k = 0; k < XG; ++k)
+        if (tid + k * 64 * NW < ng8)
+#pragma unroll
+          for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) ss += xr[k][h][e] * xr[k][h][e];
       ss = wave_sum(ss);
       if (lane == 0) ssq[wave] = ss;
       __syncthreads();
       float tot = 0.f;
 #pragma unroll
-      for (int w = 0; w < kGemvWaves; ++w) tot += ssq[w];
+      for (int w = 0; w < NW; ++w) tot += ssq[w];
       rn = rsqrtf(tot / (float)K + a.eps);
     }
-    for (int gi = tid; gi < K / 8; gi += kGemvThreads) {
-      f32x4_t v0 = xf4[2 * gi], v1 = xf4[2 * gi + 1];
-      if (a.norm_g) {
-        v0 = v0 * rn * g4[2 * gi];
-        v1 = v1 * rn * g4[2 * gi + 1];
+#pragma unroll
+    for (int k = 0; k < XG; ++k) {
+      const int gi = tid + k * 64 * NW;
+      if (gi < ng8) {
+        f32x4_t v0 = xr[k][0], v1 = xr[k][1];
+        if (a.norm_g) {
+          v0 = v0 * rn * gr[k][0];
+          v1 = v1 * rn * gr[k][1];
+        }
+        const float xv8[8] = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+        uint32_t pr[4];
+        w4_pairs(xv8, pr);
+        *(u32x4_t*)(xsh + 4 * gi) = u32x4_t{pr[0], pr[1], pr[2], pr[3]};
       }
-      const float xv8[8] = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
-      uint32_t pr[4];
-      w4_pairs(xv8, pr);
-      *(u32x4_t*)(xsh + 4 * gi) = u32x4_t{pr[0], pr[1], pr[2], pr[3]};
     }
   } else {
-    const bf16_t* x = (const bf16_t*)a.x;
-    for (int gi = tid; gi < K / 8; gi += kGemvThreads) {
-      uint32_t pr[4];
-      w4_pairs_bf16(*(const u32x4_t*)(x + (size_t)gi * 8), pr);
-      *(u32x4_t*)(xsh + 4 * gi) = u32x4_t{pr[0], pr[1], pr[2], pr[3]};
+#pragma unroll
+    for (int k = 0; k < XG; ++k) {
+      const int gi = tid + k * 64 * NW;
+      if (gi < ng8) {
+        uint32_t pr[4];
+        w4_pairs_bf16(xb[k], pr);
+        *(u32x4_t*)(xsh + 4 * gi) = u32x4_t{pr[0], pr[1], pr[2], pr[3]};
+      }
     }
   }
   __syncthreads();
 
-  const uint8_t* W = (const uint8_t*)a.W;
-  const __half* Sc = (const __half*)(W + (size_t)a.N * K / 2);
+  // ---- compute cursor: same walk as the loads ----
+  int cg = blockIdx.x * NW + wave, cit = 0;
+  float acc[RW];
+#pragma unroll
+  for (int r = 0; r < RW; ++r) acc[r] = 0.f;
   unsigned long long best = 0ull;
-  for (int g = blockIdx.x * kGemvWaves + wave; g < ngroups; g += gridDim.x * kGemvWaves) {
-    int64_t prow[RW];
+  while (cg < ngroups) {
 #pragma unroll
-    for (int r = 0; r < RW; ++r) {  // rows past N (a partial last group) re-read row N-1
-      const int64_t row = gemv_row<EPI, RW>(g, r);
-      prow[r] = row < a.N ? row : (int64_t)a.N - 1;
+    for (int u = 0; u < UNR; ++u) {
+      const int c0 = lane + cit * PER + 64 * u;
+      const int c = c0 < nch ? c0 : nch - 1;
+      uint32_t xp[16];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const u32x4_t v = *(const u32x4_t*)(xsh + 16 * c + 4 * i);
+#pragma unroll
+        for (int p = 0; p < 4; ++p) xp[4 * i + p] = v[p];
+      }
+      float sx = 0.f;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) sx = w4_dot2(xp[j], 0x3f803f80u, sx);  // (1, 1)
+#pragma unroll
+      for (int r = 0; r < RW; ++r) {
+        const float scv = c0 < nch ? __half2float(__builtin_bit_cast(__half, st.sc[u][r])) : 0.f;
+        acc[r] += scv * (w4_chunk(st.w[u][r], xp) - 136.f * sx);
+      }
     }
-    float acc[RW];
-#pragma unroll
-    for (int r = 0; r < RW; ++r) acc[r] = 0.f;
-    for (int c0 = lane; c0 < nch; c0 += 64 * UNR) {
-      u32x4_t w[UNR][RW];
-      float sc[UNR][RW];
-#pragma unroll
-      for (int u = 0; u < UNR; ++u) {
-        const int c = c0 + 64 * u;
-#pragma unroll
-        for (int r = 0; r < RW; ++r) {
-          w[u][r] = c < nch ? *(const u32x4_t*)(W + prow[r] * (K / 2) + (size_t)c * 16)
-                            : u32x4_t{0, 0, 0, 0};
-          sc[u][r] = c < nch ? __half2float(Sc[(size_t)(c / 4) * a.N + prow[r]]) : 0.f;
-        }
-      }
-#pragma unroll
-      for (int u = 0; u < UNR; ++u) {
-        const int c = c0 + 64 * u;
-        uint32_t xp[16];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const u32x4_t v = c < nch ? *(const u32x4_t*)(xsh + 16 * c + 4 * i) : u32x4_t{0, 0, 0, 0};
-#pragma unroll
-          for (int p = 0; p < 4; ++p) xp[4 * i + p] = v[p];
-        }
-        float sx = 0.f;
-#pragma unroll
-        for (int j = 0; j < 16; ++j) sx = w4_dot2(xp[j], 0x3f803f80u, sx);  // (1, 1)
-#pragma unroll
-        for (int r = 0; r < RW; ++r) acc[r] += sc[u][r] * (w4_chunk(w[u][r], xp) - 136.f * sx);
-      }
+    const int g = cg;
+    const bool last = ++cit == nit;
+    if (last) {
+      cit = 0;
+      cg += stride;
+    }
+    if constexpr (!ONE) {
+      if (cg < ngroups) load();
+      if (!last) continue;
     }
 #pragma unroll
     for (int r = 0; r < RW; ++r) acc[r] = wave_sum(acc[r]);
@@ -694,6 +764,9 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_w4_kernel(GemvArgs a, int n
         }
       }
     }
+#pragma unroll
+    for (int r = 0; r < RW; ++r) acc[r] = 0.f;
+    if constexpr (ONE) break;
   }
   if constexpr (EPI == EPI_HEAD) {
     if (lane == 0) wbest[wave] = best;
@@ -701,7 +774,7 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_w4_kernel(GemvArgs a, int n
     if (tid == 0) {
       unsigned long long b = wbest[0];
 #pragma unroll
-      for (int w = 1; w < kGemvWaves; ++w) b = wbest[w] > b ? wbest[w] : b;
+      for (int w = 1; w < NW; ++w) b = wbest[w] > b ? wbest[w] : b;
       a.argmax_part[blockIdx.x] = b;
     }
   }
@@ -925,15 +998,32 @@ static bool gemv1_w4_launch(const GemvArgs& a, hipStream_t s, int* grid_out, hip
   return false;
 }
 
-template <int EPI, int RW>
-static hipError_t gemv_w4_launch_rw(const GemvArgs& a, hipStream_t s, int* grid_out) {
-  const int ngroups = (EPI == EPI_SWIGLU) ? a.N / RW : (a.N + RW - 1) / RW;
-  int grid = (ngroups + kGemvWaves - 1) / kGemvWaves;
-  grid = grid < kGemvMaxGrid ? grid : kGemvMaxGrid;
-  if (grid_out) *grid_out = grid;
-  launch_k(gemv_w4_kernel<EPI, RW>, dim3(grid), dim3(kGemvThreads), (uint32_t)(a.K * 2), s, a,
-           ngroups);
+template <int EPI, int RW, int UNR, bool ONE, int XG>
+static hipError_t gemv_w4_go(const GemvArgs& a, int ngroups, int grid, hipStream_t s) {
+  launch_k(gemv_w4_kernel<EPI, RW, UNR, kGemvWaves, XG, ONE>, dim3(grid), dim3(kGemvThreads),
+           (uint32_t)(a.K * 2), s, a, ngroups);
   return hipGetLastError();
+}
+
+// RW rows per wavefront, 64 * UNR chunks per row per step; ONE: one row group per
+// wavefront and the whole row in one step (needs K <= 2048 * UNR), else a grid of
+// at most kGemvMaxGrid workgroups striding over the groups
+template <int EPI, int RW, int UNR, bool ONE>
+static hipError_t gemv_w4_launch_rw(const GemvArgs& a, hipStream_t s, int* grid_out) {
+  static_assert(!(ONE && EPI == EPI_HEAD), "the output head's argmax partials need a bounded grid");
+  const int ngroups = (EPI == EPI_SWIGLU) ? a.N / RW : (a.N + RW - 1) / RW;
+  if (ngroups <= 0) return hipErrorInvalidValue;
+  if (ONE && a.K / 32 > 64 * UNR) return hipErrorInvalidValue;
+  int grid = (ngroups + kGemvWaves - 1) / kGemvWaves;
+  if (!ONE) grid = grid < kGemvMaxGrid ? grid : kGemvMaxGrid;
+  if (grid_out) *grid_out = grid;
+  // input groups of 8 per thread: K / 8 <= XG * kGemvThreads (K <= 16384 checked by the caller)
+  const int xg = (a.K / 8 + kGemvThreads - 1) / kGemvThreads;
+  if (xg <= 1) return gemv_w4_go<EPI, RW, UNR, ONE, 1>(a, ngroups, grid, s);
+  if (xg <= 2) return gemv_w4_go<EPI, RW, UNR, ONE, 2>(a, ngroups, grid, s);
+  if (xg <= 4) return gemv_w4_go<EPI, RW, UNR, ONE, 4>(a, ngroups, grid, s);
+  if (xg <= 8) return gemv_w4_go<EPI, RW, UNR, ONE, 8>(a, ngroups, grid, s);
+  return hipErrorInvalidValue;
 }
 
 template <int EPI>
@@ -944,20 +1034,26 @@ static hipError_t gemv_w4_launch(const GemvArgs& a, hipStream_t s, int* grid_out
   } else if constexpr (EPI == EPI_SWIGLU) {
     if (a.N % 32) return hipErrorInvalidValue;
   }
-  // one-shot kernel for the q/k/v and whole-row residual projections; the gated and
-  // the long-row residual projections measured faster with the streaming kernel
-  // (Llama-3-8B shape: gate/up 22.5 against 30.1 us, down 20.2 against 21.7)
+  // one-shot kernel for the q/k/v and whole-row residual projections (the q/k/v
+  // epilogue writes RoPE'd keys and values into the paged cache); the gated and the
+  // long-row residual projections go to the streaming kernel
   if constexpr (EPI == EPI_QKV || EPI == EPI_RESID) {
     hipError_t err;
     if ((a.K / 32 + 63) / 64 <= 4 && gemv1_w4_launch<EPI>(a, s, grid_out, &err)) return err;
   }
-  // residual rows too long for the one-shot kernel: 2 rows per wavefront (more
-  // wavefronts, fewer dependent steps each; Llama-3-8B down projection 16.5 ->
-  // about 14.5 us against 4 rows)
-  if constexpr (EPI == EPI_RESID) return gemv_w4_launch_rw<EPI, 2>(a, s, grid_out);
-  if (a.N / 8 >= 2048) return gemv_w4_launch_rw<EPI, 8>(a, s, grid_out);
-  if (a.N / 4 >= 1024) return gemv_w4_launch_rw<EPI, 4>(a, s, grid_out);
-  return gemv_w4_launch_rw<EPI, 2>(a, s, grid_out);
+  // streaming kernel, measured at the Llama-3-8B shape: down projection (14336 ->
+  // 4096, 2 rows per wavefront, 64 chunks per row per step) 9.4 us; gated
+  // projection (4096 -> 2 x 14336, one row group of 4 rows per wavefront, whole
+  // rows in flight) 14.6 us; output head (4096 -> 128256, 8 rows) 53 us
+  if constexpr (EPI == EPI_RESID) return gemv_w4_launch_rw<EPI, 2, 1, false>(a, s, grid_out);
+  if constexpr (EPI == EPI_SWIGLU) {
+    if (a.K <= 2048) return gemv_w4_launch_rw<EPI, 4, 1, true>(a, s, grid_out);
+    if (a.K <= 4096) return gemv_w4_launch_rw<EPI, 4, 2, true>(a, s, grid_out);
+    return gemv_w4_launch_rw<EPI, 8, 1, false>(a, s, grid_out);
+  }
+  if (a.N / 8 >= 2048) return gemv_w4_launch_rw<EPI, 8, 1, false>(a, s, grid_out);
+  if (a.N / 4 >= 1024) return gemv_w4_launch_rw<EPI, 4, 1, false>(a, s, grid_out);
+  return gemv_w4_launch_rw<EPI, 2, 1, false>(a, s, grid_out);
 }
 
 static hipError_t gemv_w4_dispatch(const GemvArgs& a, hipStream_t s, int* grid_out) {
