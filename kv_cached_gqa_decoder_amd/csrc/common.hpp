@@ -92,6 +92,14 @@ __device__ __forceinline__ float glu_act(int glu, float gate, float up) {
 
 // gated activation with the hardware exp2 and reciprocal (no IEEE divide, no
 // branches): SwiGLU silu(g) * u, or GeGLU gelu(g) * u with the exact-erf GELU
+// INT4 offset-binary unpacking: the two nibbles of t at bits 0..3 and 16..19
+// (two's-complement codes q) as a bf16 pair of 128 + (q + 8), in one v_bitop3:
+// (t & 0x000F000F) ^ 0x43084308 keeps the nibbles, flips their sign bits and
+// sets the exponent of 128 (truth table 0x6C = (a & c) ^ b)
+__device__ __forceinline__ uint32_t w4_pair_bits(uint32_t t) {
+  return __builtin_amdgcn_bitop3_b32(t, 0x43084308u, 0x000F000Fu, 0x6C);
+}
+
 template <bool GELU>
 __device__ __forceinline__ float glu_fast(float g, float u) {
   if constexpr (GELU) return gelu_erf(g) * u;

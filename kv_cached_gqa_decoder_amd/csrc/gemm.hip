@@ -663,11 +663,9 @@ __global__ __launch_bounds__(256) void gemm_w4_kernel(GemmArgs a, int tiles_m, i
       for (int ni = 0; ni < NT; ++ni) {
         const int r = wn * G::WN + ni * 16 + (lane & 15);
         const uint32_t v = *(const uint32_t*)(st + G::ASTAGE + r * 64 + ((ks ^ ((r >> 1) & 3)) << 4) +
-                                              4 * (lane >> 4)) ^ 0x88888888u;
-        bf[ni] = __builtin_bit_cast(
-            bf16x8_t, u32x4_t{(v & 0x000F000Fu) | 0x43004300u, ((v >> 4) & 0x000F000Fu) | 0x43004300u,
-                              ((v >> 8) & 0x000F000Fu) | 0x43004300u,
-                              ((v >> 12) & 0x000F000Fu) | 0x43004300u});
+                                              4 * (lane >> 4));
+        bf[ni] = __builtin_bit_cast(bf16x8_t, u32x4_t{w4_pair_bits(v), w4_pair_bits(v >> 4),
+                                                      w4_pair_bits(v >> 8), w4_pair_bits(v >> 12)});
       }
       const int kc = ks * 4 + (lane >> 4);
 #pragma unroll

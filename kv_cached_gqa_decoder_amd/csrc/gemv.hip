@@ -551,18 +551,13 @@ __device__ __forceinline__ float w4_dot2(uint32_t a, uint32_t b, float acc) {
   return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2v_t, a),
                                          __builtin_bit_cast(bf16x2v_t, b), acc, false);
 }
-// sum over one chunk (4 words of codes) of (128 + u_k) x_k; one v_bitop3 per
-// pair masks the two nibbles into place and, in the same operation, flips their
-// sign bits and sets the bf16 exponent of 128 ((t & 0x000F000F) ^ 0x43084308)
+// sum over one chunk (4 words of codes) of (128 + u_k) x_k
 __device__ __forceinline__ float w4_chunk(const u32x4_t& w, const uint32_t (&xp)[16]) {
   float acc = 0.f;
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      const uint32_t t = p ? w[i] >> (4 * p) : w[i];
-      acc = w4_dot2(__builtin_amdgcn_bitop3_b32(t, 0x43084308u, 0x000F000Fu, 0x6C), xp[4 * i + p], acc);
-    }
+    for (int p = 0; p < 4; ++p) acc = w4_dot2(w4_pair_bits(w[i] >> (4 * p)), xp[4 * i + p], acc);
   return acc;
 }
 
