@@ -14,7 +14,6 @@ constexpr int kGemvThreads = 256;
 constexpr int kGemvWaves = kGemvThreads / 64;
 constexpr int kGemvMaxGrid = 2048;  // also the capacity of the argmax partials
 constexpr int kGemv1MaxK = 2048;    // one-shot kernel: longest whole row (4 chunks per lane)
-constexpr int kGemv1W4MaxK = 8192;  // one-shot INT4 kernel: longest whole row (4 chunks per lane)
 
 // Row group g of a wave: RW physical rows. For the gated projection the group
 // is RW/2 gate rows f0 .. f0+RW/2-1 and their RW/2 up rows (LAYOUT_GATEUP puts
@@ -775,224 +774,6 @@ __global__ __launch_bounds__(64 * NW) void gemv_w4_kernel(GemvArgs a, int ngroup
   }
 }
 
-// One-shot INT4 decode GEMV: the one-shot structure of the bf16 kernel (input
-// side first, then every weight chunk of the wavefront's rows; 2 whole rows per
-// wavefront, or one row per workgroup with K split over its 4 wavefronts for long
-// residual rows) with the unpacking above; the chunk input sums are shared by the
-// wavefront's rows.
-template <int EPI, int RW, int CPL, int KS>
-__global__ __launch_bounds__(kGemvThreads) void gemv1_w4_kernel(GemvArgs a, int ngroups) {
-  static_assert(KS == 1 || (KS == kGemvWaves && EPI == EPI_RESID), "K split: residual inputs only");
-  constexpr int XG = kGemv1W4MaxK / 8 / kGemvThreads;  // groups of 8 inputs per thread (staging)
-  __shared__ float part[kGemvWaves][RW];
-  __shared__ uint32_t xsh[kGemv1W4MaxK / 2];             // the input as bf16 pairs
-  __shared__ float ssq[kGemvWaves];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int g = KS == 1 ? blockIdx.x * kGemvWaves + wave : blockIdx.x;
-  const bool live = g < ngroups;  // wave-uniform
-  const int K = a.K, nch = K / 32;  // 16-byte chunks of codes per row
-  const int q = KS == 1 ? nch : (nch + KS - 1) / KS;
-  const int cbeg = KS == 1 ? 0 : wave * q;
-  const int cend = min(nch, cbeg + q);
-
-  // ---- input side ----
-  f32x4_t xr[XG][2], gr[XG][2];
-  u32x4_t xb[CPL][4];
-  if constexpr (EPI != EPI_RESID) {
-    const f32x4_t* xf4 = (const f32x4_t*)a.x;
-    const f32x4_t* g4 = (const f32x4_t*)a.norm_g;
-#pragma unroll
-    for (int k = 0; k < XG; ++k) {
-      const int gi = tid + k * kGemvThreads;  // group of 8 inputs
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        xr[k][h] = gi < K / 8 ? xf4[2 * gi + h] : f32x4_t{0.f, 0.f, 0.f, 0.f};
-        gr[k][h] = a.norm_g && gi < K / 8 ? g4[2 * gi + h] : f32x4_t{0.f, 0.f, 0.f, 0.f};
-      }
-    }
-  } else {
-    const bf16_t* x = (const bf16_t*)a.x;
-#pragma unroll
-    for (int u = 0; u < CPL; ++u) {
-      const int c = cbeg + lane + 64 * u;
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        xb[u][i] = c < cend ? *(const u32x4_t*)(x + (size_t)c * 32 + 8 * i) : u32x4_t{0, 0, 0, 0};
-    }
-  }
-
-  // ---- weights: codes, then the chunks' group scales ----
-  const uint8_t* W = (const uint8_t*)a.W;
-  const __half* Sc = (const __half*)(W + (size_t)a.N * K / 2);
-  u32x4_t w[CPL][RW];
-  float sc[CPL][RW];
-#pragma unroll
-  for (int r = 0; r < RW; ++r) {
-    const int64_t row0 = live ? gemv_row<EPI, RW>(g, r) : 0;
-    const int64_t row = row0 < a.N ? row0 : (int64_t)a.N - 1;
-#pragma unroll
-    for (int u = 0; u < CPL; ++u) {
-      const int c = cbeg + lane + 64 * u;
-      const bool ok = live && c < cend;
-      w[u][r] = ok ? *(const u32x4_t*)(W + row * (K / 2) + (size_t)c * 16) : u32x4_t{0, 0, 0, 0};
-      sc[u][r] = ok ? __half2float(Sc[(size_t)(c / 4) * a.N + row]) : 0.f;
-    }
-  }
-  QkvPre pre;
-  if constexpr (EPI == EPI_QKV) {
-    if (live && lane < RW / 2) pre = epi_qkv_prefetch(a.ctx, 0, (int)gemv_row<EPI, RW>(g, 2 * lane));
-  }
-
-  // ---- the lane's input pairs per chunk ----
-  uint32_t xp[CPL][16];
-  if constexpr (EPI != EPI_RESID) {
-    // RMSNorm (fp32 statistics) once per workgroup, rounded to bf16 pairs in LDS
-    if (a.norm_g) {
-      float ss = 0.f;
-#pragma unroll
-      for (int k = 0; k < XG; ++k)
-#pragma unroll
-        for (int h = 0; h < 2; ++h)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) ss += xr[k][h][e] * xr[k][h][e];
-      ss = wave_sum(ss);
-      if (lane == 0) ssq[wave] = ss;
-      __syncthreads();
-      float tot = 0.f;
-#pragma unroll
-      for (int v = 0; v < kGemvWaves; ++v) tot += ssq[v];
-      const float rn = rsqrtf(tot / (float)K + a.eps);
-#pragma unroll
-      for (int k = 0; k < XG; ++k)
-#pragma unroll
-        for (int h = 0; h < 2; ++h) xr[k][h] = xr[k][h] * rn * gr[k][h];
-    }
-#pragma unroll
-    for (int k = 0; k < XG; ++k) {
-      const int gi = tid + k * kGemvThreads;
-      if (gi < K / 8) {
-        const float xv8[8] = {xr[k][0][0], xr[k][0][1], xr[k][0][2], xr[k][0][3],
-                              xr[k][1][0], xr[k][1][1], xr[k][1][2], xr[k][1][3]};
-        uint32_t pr[4];
-        w4_pairs(xv8, pr);
-        *(u32x4_t*)(xsh + 4 * gi) = u32x4_t{pr[0], pr[1], pr[2], pr[3]};
-      }
-    }
-    __syncthreads();
-#pragma unroll
-    for (int u = 0; u < CPL; ++u) {
-      const int c = lane + 64 * u;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const u32x4_t v = c < nch ? *(const u32x4_t*)(xsh + 16 * c + 4 * i) : u32x4_t{0, 0, 0, 0};
-#pragma unroll
-        for (int p = 0; p < 4; ++p) xp[u][4 * i + p] = v[p];
-      }
-    }
-  } else {
-#pragma unroll
-    for (int u = 0; u < CPL; ++u)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        uint32_t pr[4];
-        w4_pairs_bf16(xb[u][i], pr);
-#pragma unroll
-        for (int p = 0; p < 4; ++p) xp[u][4 * i + p] = pr[p];
-      }
-  }
-
-  // ---- sums: per chunk sum (128 + u) x - 136 sum x, times the group scale ----
-  float sx[CPL];
-#pragma unroll
-  for (int u = 0; u < CPL; ++u) {
-    float t = 0.f;
-#pragma unroll
-    for (int j = 0; j < 16; ++j) t = w4_dot2(xp[u][j], 0x3f803f80u, t);  // (1, 1)
-    sx[u] = t;
-  }
-  float acc[RW];
-#pragma unroll
-  for (int r = 0; r < RW; ++r) {
-    acc[r] = 0.f;
-#pragma unroll
-    for (int u = 0; u < CPL; ++u) acc[r] += sc[u][r] * (w4_chunk(w[u][r], xp[u]) - 136.f * sx[u]);
-    acc[r] = wave_sum(acc[r]);
-  }
-  if constexpr (KS > 1) {
-    if (lane == 0)
-#pragma unroll
-      for (int r = 0; r < RW; ++r) part[wave][r] = acc[r];
-    __syncthreads();
-    if (wave != 0) return;
-#pragma unroll
-    for (int r = 0; r < RW; ++r) {
-      float t = part[0][r];
-#pragma unroll
-      for (int v = 1; v < KS; ++v) t += part[v][r];
-      acc[r] = t;
-    }
-  }
-  if (!live) return;
-
-  if constexpr (EPI == EPI_QKV) {
-#pragma unroll
-    for (int p = 0; p < RW / 2; ++p)
-      if (lane == p)
-        epi_qkv_store<bf16_t>(a.ctx, 0, (int)gemv_row<EPI, RW>(g, 2 * p), pre, acc[2 * p],
-                              acc[2 * p + 1]);
-  } else if constexpr (EPI == EPI_RESID) {
-#pragma unroll
-    for (int r = 0; r < RW; ++r) {
-      const int64_t row = gemv_row<EPI, RW>(g, r);
-      if (lane == r && row < a.N) ((float*)a.out)[row] += acc[r];
-    }
-  } else if constexpr (EPI == EPI_SWIGLU) {
-#pragma unroll
-    for (int i = 0; i < RW / 2; ++i)
-      if (lane == i)
-        St<bf16_t>::st((bf16_t*)a.out, g * (RW / 2) + i, glu_act(a.glu, acc[i], acc[RW / 2 + i]));
-  }
-}
-
-template <int EPI, int RW, int CPL, int KS>
-static hipError_t gemv1_w4_go(const GemvArgs& a, hipStream_t s, int* grid_out) {
-  const int ngroups = (EPI == EPI_SWIGLU) ? a.N / RW : (a.N + RW - 1) / RW;
-  const int grid = KS == 1 ? (ngroups + kGemvWaves - 1) / kGemvWaves : ngroups;
-  if (grid_out) *grid_out = grid;
-  launch_k(gemv1_w4_kernel<EPI, RW, CPL, KS>, dim3(grid), dim3(kGemvThreads), 0, s, a, ngroups);
-  return hipGetLastError();
-}
-
-// whole rows of up to 4 chunks per lane (K <= 8192), 2 rows per wavefront;
-// residual rows up to 8 chunks per lane per wavefront of a K split (K <= 65536)
-template <int EPI>
-static bool gemv1_w4_launch(const GemvArgs& a, hipStream_t s, int* grid_out, hipError_t* err) {
-  static_assert(kGemv1W4MaxK == 4 * 64 * 32, "whole rows of up to 4 chunks per lane");
-  const int nch = a.K / 32;
-  const int cpl = (nch + 63) / 64;
-  if (cpl <= 4) {
-    switch (cpl) {
-      case 1: *err = gemv1_w4_go<EPI, 2, 1, 1>(a, s, grid_out); return true;
-      case 2: *err = gemv1_w4_go<EPI, 2, 2, 1>(a, s, grid_out); return true;
-      case 3: *err = gemv1_w4_go<EPI, 2, 3, 1>(a, s, grid_out); return true;
-      case 4: *err = gemv1_w4_go<EPI, 2, 4, 1>(a, s, grid_out); return true;
-    }
-  }
-  if constexpr (EPI == EPI_RESID) {
-    const int ks = ((nch + kGemvWaves - 1) / kGemvWaves + 63) / 64;
-    switch (ks) {
-      case 2: *err = gemv1_w4_go<EPI, 1, 2, kGemvWaves>(a, s, grid_out); return true;
-      case 3: *err = gemv1_w4_go<EPI, 1, 3, kGemvWaves>(a, s, grid_out); return true;
-      case 4: *err = gemv1_w4_go<EPI, 1, 4, kGemvWaves>(a, s, grid_out); return true;
-      case 5: *err = gemv1_w4_go<EPI, 1, 5, kGemvWaves>(a, s, grid_out); return true;
-      case 6: *err = gemv1_w4_go<EPI, 1, 6, kGemvWaves>(a, s, grid_out); return true;
-      case 7: *err = gemv1_w4_go<EPI, 1, 7, kGemvWaves>(a, s, grid_out); return true;
-      case 8: *err = gemv1_w4_go<EPI, 1, 8, kGemvWaves>(a, s, grid_out); return true;
-    }
-  }
-  return false;
-}
-
 template <int EPI, int RW, int UNR, bool ONE, int XG>
 static hipError_t gemv_w4_go(const GemvArgs& a, int ngroups, int grid, hipStream_t s) {
   launch_k(gemv_w4_kernel<EPI, RW, UNR, kGemvWaves, XG, ONE>, dim3(grid), dim3(kGemvThreads),
@@ -1029,17 +810,22 @@ static hipError_t gemv_w4_launch(const GemvArgs& a, hipStream_t s, int* grid_out
   } else if constexpr (EPI == EPI_SWIGLU) {
     if (a.N % 32) return hipErrorInvalidValue;
   }
-  // one-shot kernel for the q/k/v and whole-row residual projections (the q/k/v
-  // epilogue writes RoPE'd keys and values into the paged cache); the gated and the
-  // long-row residual projections go to the streaming kernel
+  // q/k/v (epilogue: RoPE'd keys and values into the paged cache) and residual rows
+  // up to 4096: one row group of 2 rows per wavefront with the whole row in flight
+  // (Llama-3-8B shape, in the decode step: q/k/v 9.7 -> 7.1 us and O 6.7 -> 5.5 us
+  // against a one-shot kernel whose 2-row wavefronts each took a whole workgroup's
+  // input staging)
   if constexpr (EPI == EPI_QKV || EPI == EPI_RESID) {
-    hipError_t err;
-    if ((a.K / 32 + 63) / 64 <= 4 && gemv1_w4_launch<EPI>(a, s, grid_out, &err)) return err;
+    if (a.K <= 2048) return gemv_w4_launch_rw<EPI, 2, 1, true>(a, s, grid_out);
+    if (a.K <= 4096) return gemv_w4_launch_rw<EPI, 2, 2, true>(a, s, grid_out);
   }
-  // streaming kernel, measured at the Llama-3-8B shape: down projection (14336 ->
-  // 4096, 2 rows per wavefront, 64 chunks per row per step) 9.4 us; gated
-  // projection (4096 -> 2 x 14336, one row group of 4 rows per wavefront, whole
-  // rows in flight) 14.6 us; output head (4096 -> 128256, 8 rows) 53 us
+  if constexpr (EPI == EPI_QKV) {
+    if (a.K <= 8192) return gemv_w4_launch_rw<EPI, 2, 4, true>(a, s, grid_out);
+  }
+  // streaming kernel, measured at the Llama-3-8B shape in the decode step: down
+  // projection (14336 -> 4096, 2 rows per wavefront, 64 chunks per row per step)
+  // 10.8 us; gated projection (4096 -> 2 x 14336, one row group of 4 rows per
+  // wavefront, whole rows in flight) 15.9 us; output head (4096 -> 128256, 8 rows) 53 us
   if constexpr (EPI == EPI_RESID) return gemv_w4_launch_rw<EPI, 2, 1, false>(a, s, grid_out);
   if constexpr (EPI == EPI_SWIGLU) {
     if (a.K <= 2048) return gemv_w4_launch_rw<EPI, 4, 1, true>(a, s, grid_out);

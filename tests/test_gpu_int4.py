@@ -95,6 +95,22 @@ def test_int4_llama3_8b_shape_one_layer():
     t.m.close()
 
 
+def test_int4_wide_rows_one_layer():
+    """Rows wider than 4096 on one layer (hidden 5120, 40/8 heads, FFN 13824): the
+    q/k/v projection takes whole 5120-wide rows per wavefront (4 blocks of 64
+    chunks), the gated projection the grid-stride loop over 8-row groups, the O
+    projection (K 5120) and the down projection (K 13824) the 2-row streaming loop
+    with a short last block; chunks of 70 and 1 rows, then 3 decodes."""
+    p = dict(vla.PRESETS["c5_llama3_8b_int4"], n_layers=1, hidden=5120, n_heads=40, n_kv_heads=8,
+             ffn=13824, vocab=4096, num_blocks=40, max_frames=8, max_chunk=128)
+    t = _Pair(p, 0.02)
+    ref = t.embeds(70, "wide-rows prefill 70")
+    ref = t.embeds(1, "wide-rows prefill 1")
+    ref = t.decode(ref, 3, "wide-rows")
+    log("wide rows: last logits cos %.6f rel %.2e" % metrics(logits_of(t.m), ref))
+    t.m.close()
+
+
 def test_int4_llama3_8b_shape_full_120k_context_one_layer():
     """The long-context workload at its full size on one layer: a 120,000-token raw
     prefix (235 frames of up to 512 tokens, 7,500 blocks), the 512-token chunk of ids
