@@ -268,8 +268,13 @@ __global__ __launch_bounds__(kGemvThreads) void gemv1_kernel(GemvArgs a, int ngr
   }
 
   // ---- weights ----
+  // Unconditional loads: chunks past the wavefront's range re-read its last chunk
+  // (their inputs are zero, so they add nothing), and a wavefront past the last
+  // group reads row N-1 (its sums are dropped). With no guarded load after them,
+  // the input-side loads above can be waited for alone while these are in flight.
   const bf16_t* W = (const bf16_t*)a.W;
   u32x4_t w[CPL][RW];
+  const int clast = cend > 0 ? cend - 1 : 0;
 #pragma unroll
   for (int r = 0; r < RW; ++r) {
     const int64_t row = live ? gemv_row<EPI, RW>(g, r) : 0;
@@ -277,9 +282,12 @@ __global__ __launch_bounds__(kGemvThreads) void gemv1_kernel(GemvArgs a, int ngr
 #pragma unroll
     for (int u = 0; u < CPL; ++u) {
       const int c = cbeg + lane + 64 * u;
-      w[u][r] = live && c < cend ? *(const u32x4_t*)(wr + (size_t)c * 8) : u32x4_t{0, 0, 0, 0};
+      w[u][r] = *(const u32x4_t*)(wr + (size_t)(c < cend ? c : clast) * 8);
     }
   }
+  // every load above is issued before any of them is used (the scheduler would
+  // otherwise start converting the input between the weight loads and wait there)
+  __builtin_amdgcn_sched_barrier(0);
   QkvPre pre;
   if constexpr (EPI == EPI_QKV) {
     if (live && lane < RW / 2) pre = epi_qkv_prefetch(a.ctx, 0, (int)gemv_row<EPI, RW>(g, 2 * lane));
