@@ -186,8 +186,11 @@ __device__ __forceinline__ void load_pair_global(const AttnArgs& a, PairFrags<D>
                                                  bool has1, int kvh, int cq, int jq) {
   const bf16_t* kp = (const bf16_t*)a.kpool;
   const bf16_t* vp = (const bf16_t*)a.vpool;
-  const int pb0 = a.blk_table[b];
-  const int pb1 = has1 ? a.blk_table[b + 1] : pb0;
+  // b is wave-uniform: scalar table loads, which count in lgkmcnt, so waiting for
+  // them does not wait for the previous pair's K/V loads still in flight
+  const int bu = __builtin_amdgcn_readfirstlane(b);
+  const int pb0 = uniform_ld(a.blk_table, bu);
+  const int pb1 = has1 ? uniform_ld(a.blk_table, bu + 1) : pb0;
   const bf16_t* k0 = kp + a.g.kidx(a.layer, pb0, kvh, cq, 0) + 8 * jq;
   const bf16_t* k1 = kp + a.g.kidx(a.layer, pb1, kvh, cq, 0) + 8 * jq;
 #pragma unroll
@@ -200,8 +203,11 @@ __device__ __forceinline__ void load_pair_global(const AttnArgs& a, PairFrags<D>
 #pragma unroll
   for (int dt = 0; dt < D / 16; ++dt) {
     const size_t off = (size_t)(dt * 16 + cq) * a.g.bt;
+    // without a second block pb1 = pb0: the load stays unconditional (a guarded
+    // load would make every wait on earlier loads a full drain) and its keys get
+    // P = 0 in the softmax, so these values add nothing
     const u32x2_t lo = *(const u32x2_t*)(v0 + off);
-    const u32x2_t hi = has1 ? *(const u32x2_t*)(v1 + off) : u32x2_t{0, 0};
+    const u32x2_t hi = *(const u32x2_t*)(v1 + off);
     f.v[dt] = __builtin_bit_cast(bf16x8_t, u32x4_t{lo[0], lo[1], hi[0], hi[1]});
   }
 }
@@ -615,11 +621,16 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(AttnArgs a, int rgroup
   SoftmaxState<D> st;
   state_init(st);
   PairFrags<D> cur, nxt;
-  int b = b_begin + 2 * wave;
+  // wave-uniform block index, known as such to the compiler: the block table and
+  // token counts are then read with scalar loads, which leave vmcnt to the K/V loads
+  int b = __builtin_amdgcn_readfirstlane(b_begin + 2 * wave);
   if (b < b_end) load_pair_global(a, cur, b, b + 1 < b_end, kvh, cq, jq);
   for (; b < b_end; b += 2 * kAttnWaves) {
+    // the next pair's loads are unconditional (past the end they re-load the current
+    // pair, cache-hot and unused), so the step below waits only for its own pair
     const int bn = b + 2 * kAttnWaves;
-    if (bn < b_end) load_pair_global(a, nxt, bn, bn + 1 < b_end, kvh, cq, jq);
+    const int bl = bn < b_end ? bn : b;
+    load_pair_global(a, nxt, bl, bl + 1 < b_end, kvh, cq, jq);
     attn_step(a, st, qf, cur, b, b + 1 < b_end, tq, jq, sl2);
     cur = nxt;
   }
