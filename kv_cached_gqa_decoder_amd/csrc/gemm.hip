@@ -384,12 +384,17 @@ __global__ __launch_bounds__(256) void resid_norm_kernel(const float* ws, int sp
   const int row = blockIdx.x, tid = threadIdx.x;
   const int nch = N / 8;
   float v[kResidMaxChunks][8];
+  f32x4_t gv[kResidMaxChunks][2];  // the chunk's RMSNorm gains, requested with its partials
   float ss = 0.f;
 #pragma unroll
   for (int j = 0; j < kResidMaxChunks; ++j) {
     const int c = tid + 256 * j;
     if (c >= nch) continue;
     float* xp = x + (size_t)row * N + c * 8;
+    if (u != nullptr) {
+      gv[j][0] = *(const f32x4_t*)(g + c * 8);
+      gv[j][1] = *(const f32x4_t*)(g + c * 8 + 4);
+    }
     const f32x4_t x0 = *(const f32x4_t*)xp, x1 = *(const f32x4_t*)(xp + 4);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -431,8 +436,8 @@ __global__ __launch_bounds__(256) void resid_norm_kernel(const float* ws, int sp
     u32x4_t o;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      o[i] = (uint32_t)f32_to_bf16(v[j][2 * i] * r * g[c * 8 + 2 * i]) |
-             ((uint32_t)f32_to_bf16(v[j][2 * i + 1] * r * g[c * 8 + 2 * i + 1]) << 16);
+      o[i] = (uint32_t)f32_to_bf16(v[j][2 * i] * r * gv[j][i >> 1][2 * (i & 1)]) |
+             ((uint32_t)f32_to_bf16(v[j][2 * i + 1] * r * gv[j][i >> 1][2 * (i & 1) + 1]) << 16);
     *(u32x4_t*)(u + (size_t)row * N + c * 8) = o;
   }
 }
