@@ -30,6 +30,16 @@ __device__ __forceinline__ QkvPre epi_qkv_prefetch(const FwdCtx& c, int t, int c
   if (head >= c.hq) p.blk = c.blk_table[c.cb0 + (c.cslot0 + t) / c.g.bt];
   return p;
 }
+// The same factors for any head, loaded unconditionally (row t < the chunk's rows):
+// a guarded load is waited for before its default value can be written to the
+// same registers, so many guarded prefetches cost one round trip each.
+__device__ __forceinline__ QkvPre epi_qkv_prefetch_all(const FwdCtx& c, int t, int col) {
+  QkvPre p;
+  const int d = c.g.d;
+  p.cs = c.rope[(size_t)t * (d / 2) + ((col % d) >> 1)];
+  p.blk = c.blk_table[c.cb0 + (c.cslot0 + t) / c.g.bt];
+  return p;
+}
 template <typename T>
 __device__ __forceinline__ void epi_qkv_store(const FwdCtx& c, int t, int col, const QkvPre& p,
                                               float lo, float hi) {

@@ -68,6 +68,37 @@ template <int EPI, int MT, int NT, int WM, int WN>
 __device__ __forceinline__ void gemm_epilogue(const GemmArgs& a, f32x4_t (&acc)[MT][NT], int m0,
                                               int n0, int z, int wm, int wn, int lane) {
   const int M = a.M;
+  if constexpr (EPI == EPI_QKV) {
+    // every pair's RoPE factors and K/V block id are requested, unconditionally,
+    // before the first store (loads cannot move past the stores, so per-pair
+    // load-then-store cost one memory round trip per pair)
+    QkvPre pre[MT][4][NT];
+#pragma unroll
+    for (int mi = 0; mi < MT; ++mi)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+#pragma unroll
+        for (int ni = 0; ni < NT; ++ni) {
+          const int row = m0 + wm * WM + mi * 16 + 4 * (lane >> 4) + e;
+          const int col = n0 + wn * WN + ni * 16 + (lane & 15);
+          pre[mi][e][ni] = epi_qkv_prefetch_all(a.ctx, row < M ? row : M - 1, col);
+        }
+    __builtin_amdgcn_sched_barrier(0);  // keep the loads ahead of every store
+#pragma unroll
+    for (int mi = 0; mi < MT; ++mi)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+#pragma unroll
+        for (int ni = 0; ni < NT; ++ni) {
+          const int row = m0 + wm * WM + mi * 16 + 4 * (lane >> 4) + e;
+          const int col = n0 + wn * WN + ni * 16 + (lane & 15);
+          const float v = acc[mi][ni][e];
+          const float partner = __shfl_xor(v, 1, 64);
+          if (row < M && (col & 1) == 0)
+            epi_qkv_store<bf16_t>(a.ctx, row, col, pre[mi][e][ni], v, partner);
+        }
+    return;
+  }
 #pragma unroll
   for (int mi = 0; mi < MT; ++mi) {
 #pragma unroll
@@ -86,12 +117,7 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& a, f32x4_t (&acc)[
         for (int ni = 0; ni < NT; ++ni) {
           const int col = n0 + wn * WN + ni * 16 + (lane & 15);
           const float v = acc[mi][ni][e];
-          if constexpr (EPI == EPI_QKV) {
-            const float partner = __shfl_xor(v, 1, 64);
-            if (row < M && (col & 1) == 0) epi_qkv_pair<bf16_t>(a.ctx, row, col, v, partner);
-          } else {  // EPI_PARTIAL
-            if (row < M) a.ws[((size_t)z * M + row) * a.N + col] = v;
-          }
+          if (row < M) a.ws[((size_t)z * M + row) * a.N + col] = v;  // EPI_PARTIAL
         }
       }
     }
@@ -715,7 +741,7 @@ __global__ __launch_bounds__(256) void qkv_reduce_kernel(GemmArgs a, int splits)
   const int row = blockIdx.y;
   const int cp = blockIdx.x * 256 + threadIdx.x;
   if (cp >= a.N / 2) return;
-  const QkvPre pre = epi_qkv_prefetch(a.ctx, row, 2 * cp);
+  const QkvPre pre = epi_qkv_prefetch_all(a.ctx, row, 2 * cp);
   float2 v[kQkvReduceMaxSplits];
 #pragma unroll
   for (int s = 0; s < kQkvReduceMaxSplits; ++s)
