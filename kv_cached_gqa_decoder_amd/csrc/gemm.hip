@@ -737,23 +737,41 @@ static void gemm_w4_go(const GemmArgs& a, int splits, int ksteps, hipStream_t s)
 // K/V). One thread per pair (grid: pair blocks x rows); the rotation, the block id
 // and every split's partial are requested together before the sum.
 constexpr int kQkvReduceMaxSplits = kResidMaxSplits;
-__global__ __launch_bounds__(256) void qkv_reduce_kernel(GemmArgs a, int splits) {
+// S splits as a template argument: every load is unconditional, so the sum waits
+// for its own loads only (a runtime split count made each load a guarded one)
+template <int S>
+__global__ __launch_bounds__(256) void qkv_reduce_kernel(GemmArgs a) {
   const int row = blockIdx.y;
   const int cp = blockIdx.x * 256 + threadIdx.x;
   if (cp >= a.N / 2) return;
   const QkvPre pre = epi_qkv_prefetch_all(a.ctx, row, 2 * cp);
-  float2 v[kQkvReduceMaxSplits];
+  float2 v[S];
 #pragma unroll
-  for (int s = 0; s < kQkvReduceMaxSplits; ++s)
-    if (s < splits) v[s] = *(const float2*)(a.ws + ((size_t)s * a.M + row) * a.N + 2 * cp);
+  for (int s = 0; s < S; ++s) v[s] = *(const float2*)(a.ws + ((size_t)s * a.M + row) * a.N + 2 * cp);
   float lo = 0.f, hi = 0.f;
 #pragma unroll
-  for (int s = 0; s < kQkvReduceMaxSplits; ++s)
-    if (s < splits) {
-      lo += v[s].x;
-      hi += v[s].y;
-    }
+  for (int s = 0; s < S; ++s) {
+    lo += v[s].x;
+    hi += v[s].y;
+  }
   epi_qkv_store<bf16_t>(a.ctx, row, 2 * cp, pre, lo, hi);
+}
+
+static hipError_t launch_qkv_reduce(const GemmArgs& a, int splits, hipStream_t s) {
+  static_assert(kQkvReduceMaxSplits == 8, "one instantiation per split count");
+  const dim3 grid((a.N / 2 + 255) / 256, a.M), block(256);
+  switch (splits) {
+    case 1: launch_k(qkv_reduce_kernel<1>, grid, block, 0, s, a); break;
+    case 2: launch_k(qkv_reduce_kernel<2>, grid, block, 0, s, a); break;
+    case 3: launch_k(qkv_reduce_kernel<3>, grid, block, 0, s, a); break;
+    case 4: launch_k(qkv_reduce_kernel<4>, grid, block, 0, s, a); break;
+    case 5: launch_k(qkv_reduce_kernel<5>, grid, block, 0, s, a); break;
+    case 6: launch_k(qkv_reduce_kernel<6>, grid, block, 0, s, a); break;
+    case 7: launch_k(qkv_reduce_kernel<7>, grid, block, 0, s, a); break;
+    case 8: launch_k(qkv_reduce_kernel<8>, grid, block, 0, s, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
 }
 
 template <int EPI, int BM, int BN, int BK, int NS, int WGM = 2, int WGN = 2>
@@ -876,7 +894,7 @@ static hipError_t gemm_bf16(const GemmArgs& a, hipStream_t s) {
       if (tall) gemm_bf16_go<EPI_PARTIAL, 256, 64, 64, 3, 4, 2>(a, splits, ksteps, s);
       else if (skinny) gemm_bf16_go<EPI_PARTIAL, 64, 32, 64, 3, 4, 1>(a, splits, ksteps, s);
       else gemm_bf16_go<EPI_PARTIAL, 64, 64, 64, 3>(a, splits, ksteps, s);
-      launch_k(qkv_reduce_kernel, dim3((a.N / 2 + 255) / 256, a.M), dim3(256), 0, s, a, splits);
+      if (hipError_t e = launch_qkv_reduce(a, splits, s); e != hipSuccess) return e;
     }
     return hipGetLastError();
   }
