@@ -135,7 +135,11 @@ void vla_model_destroy(vla_model* m);
 vla_status vla_prefill_chunk(vla_model* m, const int32_t* tokens, const void* embeds,
                              int32_t n, int32_t* out_frame_id, void* stream);
 
-/* One decode token at the next position: embedding row `token`, full forward,
+/* One decode token at the next position ("CSR: Infinite-Horizon Real-Time
+ * Policies with Massive Cached State Representations", III-A: with the K/V of
+ * earlier tokens cached, each new token only computes its own q, k, v and
+ * attends to the cache; "Can an LLM Forget the Right Things?", section 4: one
+ * greedy argmax token per decode step): embedding row `token`, full forward,
  * logits kept, and the greedy next token (argmax over the vocabulary, ties to
  * the lowest id) written to *out_next_token (host, nullable; non-NULL
  * synchronises the stream). token VLA_TOKEN_DEVICE: the greedy token of the
@@ -166,7 +170,10 @@ vla_status vla_kv_score_and_evict(vla_model* m, int32_t layer, int32_t* out_fram
 vla_status vla_kv_score(vla_model* m, int32_t layer, int32_t* out_frame_id, double* out_score,
                         void* stream);
 
-/* Copy the last computed logits (fp32[vocab], from the last prefill row or
+/* Output head ("CSR: Infinite-Horizon Real-Time Policies with Massive Cached
+ * State Representations", III-A: the distribution over the vocabulary comes from
+ * W_Y applied to the last hidden state; here before the softmax, after the final
+ * RMSNorm). Copy the last computed logits (fp32[vocab], from the last prefill row or
  * decode step) into `out` (host or device memory; n must equal vocab).
  * Synchronises the stream. Errors: VLA_E_INVALID (n != vocab, out NULL),
  * VLA_E_STATE (no forward has run yet). */
@@ -210,6 +217,13 @@ vla_status vla_get_state(const vla_model* m, vla_state* out);
  * entries; *n_out receives the number of entries. */
 vla_status vla_kv_block_table(const vla_model* m, int32_t* blocks, int32_t* ntok, int32_t cap,
                               int32_t* n_out);
+
+/* The KV free-list as a stack, bottom first: out[n-1] is the block the next
+ * allocation pops ("Rebuilding Kshipra Around Memory", section 1: LIFO reuse
+ * of freed blocks). Host array of cap entries; *n_out receives the number of
+ * free blocks (entries past cap are not written). Host-only; enqueues no work.
+ * Errors: VLA_E_INVALID (null m or n_out). */
+vla_status vla_kv_free_list(const vla_model* m, int32_t* out, int32_t cap, int32_t* n_out);
 
 /* Resident frame ids in arrival order (host array of cap entries). */
 vla_status vla_kv_frames(const vla_model* m, int32_t* frame_ids, int32_t cap, int32_t* n_out);
@@ -296,6 +310,8 @@ vla_status vla_pool_alloc(vla_pool* p, int32_t n, int32_t* out);
 /* Push n blocks in the order given; VLA_E_INVALID for an id out of range or already free. */
 vla_status vla_pool_release(vla_pool* p, const int32_t* blocks, int32_t n);
 int32_t vla_pool_free_count(const vla_pool* p);
+/* The pool's free-list bottom first (out[n-1] is popped next), as vla_kv_free_list. */
+vla_status vla_pool_free_list(const vla_pool* p, int32_t* out, int32_t cap, int32_t* n_out);
 
 #ifdef __cplusplus
 }

@@ -1,6 +1,9 @@
 // Prefill projections C[M][N] = A[M][K] * W[N][K]^T with fused epilogues.
-//  bf16: matrix-core kernel on v_mfma_f32_16x16x32_bf16 (fp32 accumulate),
-//        LDS-staged 64-deep K tiles with register prefetch of the next tile.
+//  bf16: matrix-core kernels on v_mfma_f32_16x16x32_bf16 (fp32 accumulate),
+//        operands streamed into a multi-stage LDS ring by global_load_lds
+//        (direct-to-LDS DMA, no register staging); gated projections of
+//        129-256 rows on a two-stream kernel (separate activation and weight
+//        rings, each with its own producer wavefronts).
 //  fp32: FMA kernel (the fp32 configuration never touches bf16 matrix cores).
 // Epilogues: plain store, residual add (x += C), RoPE + paged K/V write on the
 // fused q/k/v projection, SwiGLU on the interleaved gate/up projection

@@ -992,6 +992,21 @@ vla_status vla_kv_block_table(const vla_model* m, int32_t* blocks, int32_t* ntok
   });
 }
 
+static void copy_free_list(const BlockPool& p, int32_t* out, int32_t cap, int32_t* n_out) {
+  const std::vector<int>& fl = p.free_list();
+  const int n = (int)fl.size();
+  if (out)
+    for (int i = 0; i < n && i < cap; ++i) out[i] = fl[i];
+  *n_out = n;
+}
+
+vla_status vla_kv_free_list(const vla_model* m, int32_t* out, int32_t cap, int32_t* n_out) {
+  return guarded([&] {
+    if (!m || !n_out) raise(VLA_E_INVALID, "null argument");
+    copy_free_list(m->pool, out, cap, n_out);
+  });
+}
+
 vla_status vla_kv_frames(const vla_model* m, int32_t* frame_ids, int32_t cap, int32_t* n_out) {
   return guarded([&] {
     if (!m || !n_out) raise(VLA_E_INVALID, "null argument");
@@ -1257,5 +1272,11 @@ vla_status vla_pool_release(vla_pool* p, const int32_t* blocks, int32_t n) {
   });
 }
 int32_t vla_pool_free_count(const vla_pool* p) { return p ? p->p.free_count() : 0; }
+vla_status vla_pool_free_list(const vla_pool* p, int32_t* out, int32_t cap, int32_t* n_out) {
+  return guarded([&] {
+    if (!p || !n_out) raise(VLA_E_INVALID, "null argument");
+    copy_free_list(p->p, out, cap, n_out);
+  });
+}
 
 }  // extern "C"

@@ -3,8 +3,13 @@
 // cosine is a dot product over two norms, 0 below a 1e-8 denominator).
 //
 // mean keys   fp64 mean over a frame's tokens of its stored keys, per layer,
-//             all KV heads concatenated. A sum of bf16 or fp32 values in fp64
-//             is exact here, so the result does not depend on the order.
+//             all KV heads concatenated. For bf16 keys (8 significant bits) a
+//             sum of up to 2^45 values is exact in fp64 whenever the exponents
+//             of the summed values span at most 45 - log2(count) binades, so it
+//             does not depend on the order: the device and a plain left-to-right
+//             sum agree bit for bit. For fp32 keys (24 bits) that span shrinks to
+//             29 - log2(count) binades; outside it the 4-way split below and a
+//             sequential sum may round differently (last-bit differences).
 // scoring     one workgroup per frame i computes s_ij for every j != i and
 //             m_i = max_j s_ij; the pair value is a pure function of the
 //             unordered pair (the dot product is symmetric in its operands
@@ -21,8 +26,8 @@ namespace vla {
 // one lane per V consecutive dims (8 or 16 bytes) of one (frame, layer); the 4
 // wavefronts of a workgroup take the frame's blocks round-robin, one block (16
 // token loads per lane) per step, the next step's block id requested before the
-// current step's keys are added; few registers, so many workgroups are resident. fp64 sums of bf16 or fp32
-// keys are exact here, so the 4 partial sums (added through LDS) give the same
+// current step's keys are added; few registers, so many workgroups are resident. fp64 sums of bf16 keys
+// are exact (see above), so the 4 partial sums (added through LDS) give the same
 // table whatever the split.
 template <typename T, int V>
 struct KeyVec {

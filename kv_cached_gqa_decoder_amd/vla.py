@@ -71,6 +71,8 @@ _SIGS = {
     "vla_get_state": (c_int32, [c_void_p, POINTER(vla_state)]),
     "vla_kv_block_table": (c_int32, [c_void_p, c_void_p, c_void_p, c_int32, POINTER(c_int32)]),
     "vla_kv_frames": (c_int32, [c_void_p, c_void_p, c_int32, POINTER(c_int32)]),
+    "vla_kv_free_list": (c_int32, [c_void_p, c_void_p, c_int32, POINTER(c_int32)]),
+    "vla_pool_free_list": (c_int32, [c_void_p, c_void_p, c_int32, POINTER(c_int32)]),
     "vla_mean_keys_out": (c_int32, [c_void_p, c_int32, c_void_p, c_int32, POINTER(c_int32),
                                     c_void_p]),
     "vla_kv_gather": (c_int32, [c_void_p, c_int32, c_void_p, c_void_p, c_int32,
@@ -218,6 +220,24 @@ def vla_kv_frames(m: int):
     ids = np.zeros(max(n.value, 1), dtype=np.int32)
     _check(load().vla_kv_frames(m, ids.ctypes.data, n.value, byref(n)))
     return ids[: n.value]
+
+
+def _free_list(fn, h):
+    import numpy as np
+    n = c_int32(0)
+    _check(fn(h, None, 0, byref(n)))
+    out = np.zeros(max(n.value, 1), dtype=np.int32)
+    _check(fn(h, out.ctypes.data, n.value, byref(n)))
+    return [int(b) for b in out[: n.value]]
+
+
+def vla_kv_free_list(m: int):
+    """The free-list bottom first (the last entry is popped next)."""
+    return _free_list(load().vla_kv_free_list, m)
+
+
+def vla_pool_free_list(p: int):
+    return _free_list(load().vla_pool_free_list, p)
 
 
 def vla_mean_keys_out(m: int, layer: int, cap_frames: int, dim: int, stream=None):
@@ -412,6 +432,9 @@ class Model:
 
     def frames(self):
         return vla_kv_frames(self.h)
+
+    def free_list(self):
+        return vla_kv_free_list(self.h)
 
     def mean_keys(self, layer, stream=None):
         return vla_mean_keys_out(self.h, layer, self.cfg.max_frames,

@@ -76,3 +76,27 @@ def oracle_config(preset: dict, name="custom", init_std=0.02) -> D.Config:
                     rms_eps=preset.get("rms_eps", 1e-6), rope_theta=preset["rope_theta"],
                     wdtype=wd, act=act, num_blocks=preset["num_blocks"],
                     max_frames=preset["max_frames"], seed=preset["seed"], init_std=init_std)
+
+
+def eviction_margin(vectors: np.ndarray):
+    """The oracle's redundancy scoring of mean-key rows [F, D]: (winner index, the gap
+    between the winner's score and the best score of any frame outside the winning
+    pair, the pair matrix).
+
+    The winning pair is the winner and its most similar partner; both carry the
+    same score, so only frames outside the pair can compete with it.
+    """
+    from oracle.scoring import pair_matrix
+    s = pair_matrix(np.asarray(vectors, dtype=np.float64))
+    m = s.max(axis=1)
+    win = int(np.argmax(m))
+    partner = int(np.argmax(s[win]))
+    rest = [m[i] for i in range(len(m)) if i not in (win, partner)]
+    gap = float(m[win] - max(rest)) if rest else float("inf")
+    return win, gap, s
+
+
+# Eviction decisions that depend on keys the model computed (bf16-rounded on the
+# device, fp64 in the oracle) are only compared when the oracle's margin is outside
+# this band of cosine similarity.
+KEY_BAND = 1e-2

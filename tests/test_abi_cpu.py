@@ -71,6 +71,7 @@ def test_host_pool_matches_oracle_lifo(vla):
                 assert got == ref.alloc(k)
                 held += got
             assert vla.vla_pool_free_count(p) == len(ref.free)
+            assert vla.vla_pool_free_list(p) == ref.free
     finally:
         vla.vla_pool_destroy(p)
 

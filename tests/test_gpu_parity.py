@@ -12,8 +12,8 @@ import torch
 import kv_cached_gqa_decoder_amd as vla
 import synth
 from oracle import decoder as D
-from tests.gpu_util import (check_argmax, check_logits, dev_from_storage, log, logits_of,
-                            metrics, oracle_config)
+from tests.gpu_util import (KEY_BAND, check_argmax, check_logits, dev_from_storage,
+                            eviction_margin, log, logits_of, metrics, oracle_config)
 
 pytestmark = pytest.mark.gpu
 
@@ -149,15 +149,26 @@ def test_bf16_ragged_chunks_interleaved_decodes_and_eviction():
         omk = np.stack([v for _, v in sess.mean_keys(layer)])
         assert mk.shape == omk.shape
         assert metrics(mk.ravel(), omk.ravel())[1] < 2e-2
-    # eviction: the scorer on each side picks from its own keys
+    # eviction: each side scores its own keys (the device's are bf16-rounded), so
+    # the picks are compared only when the oracle's margin is outside the key band;
+    # the oracle always evicts its own pick and never takes the device's
+    gfid, _ = m.kv_score(0)
+    omk = [v for _, v in sess.mean_keys(0)]
+    win, gap, _ = eviction_margin(np.stack(omk))
+    ofid, oscore = sess.score_and_evict(0)
+    log(f"  eviction: oracle frame {ofid}, margin {gap:.3e} (band {KEY_BAND})")
+    if gap < KEY_BAND:
+        log("  eviction margin inside the key band: comparison stops here")
+        m.close()
+        return
+    assert gfid == ofid, (gfid, ofid)
     fid, score = m.kv_score_and_evict(0)
-    ofid, oscore, om = sess.score(0)
-    srt = np.sort(om)
-    assert fid == ofid or srt[-1] - srt[-3] < 1e-2, (fid, ofid, om)
-    sess.evict(fid)
+    assert fid == ofid and abs(score - oscore) < KEY_BAND
+    assert m.free_list() == sess.pool.free
     ref = prefill_embeds(40)       # reuses the freed blocks
     blocks, ntok = m.block_table()
     assert [(int(b), int(n)) for b, n in zip(blocks, ntok)] == sess.block_table()
+    assert m.free_list() == sess.pool.free
     decode(ref, 2)
     m.close()
 
@@ -187,6 +198,7 @@ def test_raw_frames_mean_keys_and_eviction_bit_exact():
         assert abs(score - oscore) < 1e-12
         blocks, ntok = m.block_table()
         assert [(int(b), int(n)) for b, n in zip(blocks, ntok)] == sess.block_table()
+        assert m.free_list() == sess.pool.free
     # the scoring on layer 1 (no cluster structure) also agrees
     assert m.kv_score(1)[0] == sess.score(1)[0]
     m.close()

@@ -96,3 +96,21 @@ def test_c_twin_matches_numpy(oracle_c_built):
     a = rng.normal_np(1236, 513, 0, 50_000)
     b = rng.normal_c(1236, 513, 0, 50_000, 1.0, "f64")
     assert np.max(np.abs(a - b) / np.maximum(np.abs(a), 1e-300)) < 1e-15
+
+
+def test_generator_pins_computed_independently(oracle_c_built):
+    """sm(0), sm(1), a stream key, the first normals and uniform ids of one stream,
+    as computed from the generator's definition by a separate implementation."""
+    pins = json.load(open(os.path.join(GOLDEN, "generator_pins.json")))
+    for x, want in pins["sm"].items():
+        assert int(rng.splitmix64(np.uint64(int(x)))) == int(want, 16), x
+    k = pins["key"]
+    assert int(rng.stream_key(k["seed"], k["stream"])) == int(k["value"], 16)
+    nrm = pins["normal"]
+    got = rng.normal_np(nrm["seed"], nrm["stream"], 0, len(nrm["first"]))
+    assert got.tolist() == nrm["first"]
+    # the C twin gives the same doubles (std 1, fp64 storage)
+    got_c = rng.normal_c(nrm["seed"], nrm["stream"], 0, len(nrm["first"]), 1.0, "f64")
+    assert np.max(np.abs(got_c - np.array(nrm["first"]))) <= 1e-15
+    u = pins["uniform_ids"]
+    assert rng.uniform_ids(u["seed"], u["stream"], len(u["first"]), u["vocab"]).tolist() == u["first"]
