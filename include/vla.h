@@ -170,6 +170,20 @@ vla_status vla_kv_score_and_evict(vla_model* m, int32_t layer, int32_t* out_fram
 vla_status vla_kv_score(vla_model* m, int32_t layer, int32_t* out_frame_id, double* out_score,
                         void* stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph capture,
+ * serving loops, harnesses that forbid allocation): the scoring of
+ * vla_kv_score on a caller-given mean-key table, with no handle and no
+ * allocation. mean_keys: device fp64 [n_frames][dim], one row per frame in
+ * arrival order. Writes the winning row's index (device int32) and its score
+ * (device fp64); asynchronous on `stream`, nothing synchronises. The per-frame
+ * scores live in a library-owned static device array of 4096 doubles per GPU,
+ * alive until the process ends: at most 4096 frames. Calls that overlap on one
+ * GPU share that array and race; serialise them (one stream, or events).
+ * Errors: VLA_E_INVALID (null pointer, n_frames > 4096, dim < 1),
+ * VLA_E_NOTHING_TO_EVICT (n_frames < 2), VLA_E_HIP (launch failure). */
+vla_status vla_kv_score_noalloc(const double* mean_keys, int32_t n_frames, int32_t dim,
+                                int32_t* out_index, double* out_score, void* stream);
+
 /* Output head ("CSR: Infinite-Horizon Real-Time Policies with Massive Cached
  * State Representations", III-A: the distribution over the vocabulary comes from
  * W_Y applied to the last hidden state; here before the softmax, after the final

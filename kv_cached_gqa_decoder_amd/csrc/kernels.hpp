@@ -196,5 +196,11 @@ hipError_t launch_meankeys(const void* kpool, KvGeom g, const int* blk_table,
                            double* table, int max_frames, int dt, hipStream_t s);
 hipError_t launch_score(const double* table_layer, const int* fr_slot, int nframes, int D,
                         double* m_out, double* result, hipStream_t s);
+// scoring of a dense fp64 table [nframes][D] (rows in frame order) with the
+// per-frame scores in a library-owned static device array (no allocation);
+// writes the winner's row index and score to device memory
+constexpr int kScoreNoAllocMaxFrames = 4096;
+hipError_t launch_score_noalloc(const double* table, int nframes, int D, int* out_idx,
+                                double* out_score, hipStream_t s);
 
 }  // namespace vla

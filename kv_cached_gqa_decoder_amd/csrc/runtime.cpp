@@ -882,6 +882,20 @@ vla_status vla_kv_score(vla_model* m, int32_t layer, int32_t* out_frame_id, doub
   return score_impl(m, layer, out_frame_id, out_score, stream, false);
 }
 
+vla_status vla_kv_score_noalloc(const double* mean_keys, int32_t n_frames, int32_t dim,
+                                int32_t* out_index, double* out_score, void* stream) {
+  return guarded([&] {
+    if (!mean_keys || !out_index || !out_score) raise(VLA_E_INVALID, "null argument");
+    if (n_frames < 2) raise(VLA_E_NOTHING_TO_EVICT, "fewer than 2 frames");
+    if (n_frames > kScoreNoAllocMaxFrames)
+      raise(VLA_E_INVALID, "n_frames " + std::to_string(n_frames) + " exceeds the maximum of " +
+                               std::to_string(kScoreNoAllocMaxFrames));
+    if (dim < 1) raise(VLA_E_INVALID, "dim must be >= 1");
+    HIPCHK(launch_score_noalloc(mean_keys, n_frames, dim, out_index, out_score,
+                                (hipStream_t)stream));
+  });
+}
+
 vla_status vla_logits_out(vla_model* m, float* out, int32_t n, void* stream) {
   return guarded([&] {
     if (!m || !out) raise(VLA_E_INVALID, "null argument");

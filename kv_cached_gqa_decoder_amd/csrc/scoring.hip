@@ -16,6 +16,7 @@
 //             (an fma's product is exact), the norms and the dot use one fixed
 //             summation shape), so s_ij == s_ji bit for bit. A second kernel
 //             takes argmax_i m_i with ties to the lowest index.
+#include <mutex>
 #include <type_traits>
 
 #include "common.hpp"
@@ -175,7 +176,8 @@ __global__ __launch_bounds__(kScoreWaves * 64) void score_rows_kernel(const doub
   __shared__ double wmax[kScoreWaves];
   const int i = blockIdx.x;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const double* a = tab + (size_t)fr_slot[i] * D;
+  // fr_slot null: the table rows are the frames themselves, in order
+  const double* a = tab + (size_t)(fr_slot ? fr_slot[i] : i) * D;
   // |row i|^2 (every wavefront computes it the same way)
   double aa = 0.0;
   for (int k = lane; k < D; k += 64) aa = fma(a[k], a[k], aa);
@@ -189,7 +191,7 @@ __global__ __launch_bounds__(kScoreWaves * 64) void score_rows_kernel(const doub
       ab[u] = 0.0;
       bb[u] = 0.0;
       const int j = min(j0 + u, F - 1);
-      b[u] = tab + (size_t)fr_slot[j] * D;
+      b[u] = tab + (size_t)(fr_slot ? fr_slot[j] : j) * D;
     }
 #pragma unroll 2
     for (int k = lane; k < D; k += 64) {
@@ -227,8 +229,10 @@ __global__ __launch_bounds__(kScoreWaves * 64) void score_rows_kernel(const doub
   }
 }
 
-// argmax over m[0..F), ties to the lowest index; result[0] = index, result[1] = value
-__global__ __launch_bounds__(256) void score_argmax_kernel(const double* m, int F, double* result) {
+// argmax over m[0..F), ties to the lowest index: result[0] = index, result[1] =
+// value (result non-null), or *out_idx = index, *out_val = value
+__global__ __launch_bounds__(256) void score_argmax_kernel(const double* m, int F, double* result,
+                                                           int* out_idx, double* out_val) {
   __shared__ double sv[256];
   __shared__ int si[256];
   double bv = -INFINITY;
@@ -251,8 +255,13 @@ __global__ __launch_bounds__(256) void score_argmax_kernel(const double* m, int 
     __syncthreads();
   }
   if (threadIdx.x == 0) {
-    result[0] = (double)si[0];
-    result[1] = sv[0];
+    if (result) {
+      result[0] = (double)si[0];
+      result[1] = sv[0];
+    } else {
+      *out_idx = si[0];
+      *out_val = sv[0];
+    }
   }
 }
 
@@ -261,7 +270,50 @@ hipError_t launch_score(const double* table_layer, const int* fr_slot, int nfram
   if (nframes < 2) return hipErrorInvalidValue;
   launch_k(score_rows_kernel, dim3(nframes), dim3(kScoreWaves * 64), 0, s, table_layer, fr_slot,
            nframes, D, m_out);
-  launch_k(score_argmax_kernel, dim3(1), dim3(256), 0, s, (const double*)m_out, nframes, result);
+  launch_k(score_argmax_kernel, dim3(1), dim3(256), 0, s, (const double*)m_out, nframes, result,
+           (int*)nullptr, (double*)nullptr);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Scoring that allocates nothing: the per-frame scores m_i live in a
+// file-scope device array (one copy per GPU, alive until the process ends)
+// instead of a model's scratch. Its device address is looked up once per GPU
+// with hipGetSymbolAddress and only that address is passed to the kernels (in
+// host code the array's name does not denote device memory). Every frame's
+// score is written before the argmax reads it, so nothing needs clearing; two
+// calls in flight on one GPU share the array and race.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) double scratch[kScoreNoAllocMaxFrames];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+double* g_scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+hipError_t launch_score_noalloc(const double* table, int nframes, int D, int* out_idx,
+                                double* out_score, hipStream_t s) {
+  if (nframes < 2 || nframes > kScoreNoAllocMaxFrames || D < 1) return hipErrorInvalidValue;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  double* ptr = nullptr;
+  {
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+      void* p = nullptr;
+      e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+      if (e != hipSuccess) return e;
+      g_scratch_ptr[dev] = (double*)p;
+    }
+    ptr = g_scratch_ptr[dev];
+  }
+  launch_k(score_rows_kernel, dim3(nframes), dim3(kScoreWaves * 64), 0, s, table,
+           (const int*)nullptr, nframes, D, ptr);
+  launch_k(score_argmax_kernel, dim3(1), dim3(256), 0, s, (const double*)ptr, nframes,
+           (double*)nullptr, out_idx, out_score);
   return hipGetLastError();
 }
 

@@ -63,6 +63,7 @@ _SIGS = {
                                          c_void_p]),
     "vla_kv_score": (c_int32, [c_void_p, c_int32, POINTER(c_int32), POINTER(c_double), c_void_p]),
     "vla_logits_out": (c_int32, [c_void_p, c_void_p, c_int32, c_void_p]),
+    "vla_kv_score_noalloc": (c_int32, [c_void_p, c_int32, c_int32, c_void_p, c_void_p, c_void_p]),
     "vla_last_error": (ctypes.c_char_p, []),
     "vla_kv_append_raw": (c_int32, [c_void_p, c_void_p, c_void_p, c_int32, POINTER(c_int32),
                                     c_void_p]),
@@ -172,6 +173,13 @@ def vla_kv_score(m: int, layer: int = 0, stream=None):
     fid, sc = c_int32(-1), c_double(0.0)
     _check(load().vla_kv_score(m, layer, byref(fid), byref(sc), _stream(stream)))
     return fid.value, sc.value
+
+
+def vla_kv_score_noalloc(mean_keys, n_frames: int, dim: int, out_index, out_score,
+                         stream=None) -> None:
+    """Device pointers: mean_keys fp64 [n_frames][dim], out_index int32[1], out_score fp64[1]."""
+    _check(load().vla_kv_score_noalloc(_ptr(mean_keys), n_frames, dim, _ptr(out_index),
+                                       _ptr(out_score), _stream(stream)))
 
 
 def vla_logits_out(m: int, out, n: int, stream=None) -> None:
