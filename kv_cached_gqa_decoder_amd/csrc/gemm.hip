@@ -45,7 +45,10 @@ constexpr int kXcds = 8;
 constexpr int EPI_GEGLU_K = 16;
 template <int EPI> constexpr bool kGated = EPI == EPI_SWIGLU || EPI == EPI_GEGLU_K;
 
-template <int BM, int BN, int BK, int NS, int WGM = 2, int WGN = 2>
+// LO: the activations come as a bf16 pair (A, A_lo); a stage holds the BM rows of
+// A, then the BM rows of A_lo, then the BN weight rows, and every weight fragment
+// meets both activation fragments (two MFMAs, the high part first)
+template <int BM, int BN, int BK, int NS, int WGM = 2, int WGN = 2, bool LO = false>
 struct GemmTile {
   static constexpr int NW = WGM * WGN;               // wavefronts per workgroup
   static constexpr int WM = BM / WGM, WN = BN / WGN;
@@ -53,11 +56,13 @@ struct GemmTile {
   static constexpr int ROWB = BK * 2;                // bytes of one LDS row (one K step)
   static constexpr int CPR = BK / 8;                 // 16-byte chunks per row
   static constexpr int RPI = 64 / CPR;               // rows filled by one DMA load
-  static constexpr int ROWS = BM + BN;               // LDS rows per stage
+  static constexpr int AROWS = LO ? 2 * BM : BM;     // activation rows per stage
+  static constexpr int ROWS = AROWS + BN;            // LDS rows per stage
   static constexpr int STAGE = ROWS * ROWB;          // bytes
   static constexpr int LOADS = ROWS / RPI / NW;      // DMA loads per wavefront per stage
   static_assert(LOADS * RPI * NW == ROWS && WM % 16 == 0 && WN % 16 == 0, "tile shape");
   static constexpr int LDS = NS * STAGE;
+  static_assert(LDS <= 160 * 1024, "LDS");
   // chunk position of K chunk kc in LDS row r: 8 consecutive rows read at one chunk
   // column land in 8 distinct 16-byte bank groups (32 or 64 banks)
   static __device__ __forceinline__ int pos(int r, int kc) {
@@ -127,10 +132,10 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& a, f32x4_t (&acc)[
   }
 }
 
-template <int EPI, int BM, int BN, int BK, int NS, int WGM, int WGN>
+template <int EPI, int BM, int BN, int BK, int NS, int WGM, int WGN, bool LO>
 __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_kernel(GemmArgs a, int tiles_m,
                                                                    int tiles, int ksteps) {
-  using G = GemmTile<BM, BN, BK, NS, WGM, WGN>;
+  using G = GemmTile<BM, BN, BK, NS, WGM, WGN, LO>;
   constexpr int MT = G::MT, NT = G::NT, LOADS = G::LOADS;
   static_assert(LOADS * (NS - 1) <= 63 && NS - 2 <= 6, "vmcnt range");
   __shared__ __attribute__((aligned(1024))) unsigned char smem[G::LDS];
@@ -154,11 +159,12 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_kernel(GemmArgs a, i
   for (int j = 0; j < LOADS; ++j) {
     const int row = (wave * LOADS + j) * G::RPI + lane / G::CPR;
     const int kc = G::pos(row, lane % G::CPR);  // pos() is an involution in kc
-    if (row < BM) {
-      const int ar = min(m0 + row, M - 1);
-      src[j] = (const bf16_t*)a.A + (int64_t)ar * K + (int64_t)kt0 * BK + kc * 8;
+    if (row < G::AROWS) {
+      const int ar = min(m0 + (row < BM ? row : row - BM), M - 1);
+      const bf16_t* base = (const bf16_t*)(row < BM ? a.A : a.A_lo);
+      src[j] = base + (int64_t)ar * K + (int64_t)kt0 * BK + kc * 8;
     } else {
-      src[j] = (const bf16_t*)a.W + (int64_t)(n0 + row - BM) * K + (int64_t)kt0 * BK + kc * 8;
+      src[j] = (const bf16_t*)a.W + (int64_t)(n0 + row - G::AROWS) * K + (int64_t)kt0 * BK + kc * 8;
     }
   }
   // stage kt -> ring slot kt % NS. Past the last step the DMA re-loads the last
@@ -201,7 +207,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_kernel(GemmArgs a, i
       bf16x8_t bf[NT];
 #pragma unroll
       for (int ni = 0; ni < NT; ++ni) {
-        const int r = BM + wn * G::WN + ni * 16 + (lane & 15);
+        const int r = G::AROWS + wn * G::WN + ni * 16 + (lane & 15);
         bf[ni] = *(const bf16x8_t*)(st + r * G::ROWB + (G::pos(r, kc) << 4));
       }
 #pragma unroll
@@ -211,6 +217,13 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_kernel(GemmArgs a, i
 #pragma unroll
         for (int ni = 0; ni < NT; ++ni)
           acc[mi][ni] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bf[ni], acc[mi][ni], 0, 0, 0);
+        if constexpr (LO) {
+          const int rl = BM + r;
+          const bf16x8_t al = *(const bf16x8_t*)(st + rl * G::ROWB + (G::pos(rl, kc) << 4));
+#pragma unroll
+          for (int ni = 0; ni < NT; ++ni)
+            acc[mi][ni] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bf[ni], acc[mi][ni], 0, 0, 0);
+        }
       }
     }
   }
@@ -233,9 +246,10 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_kernel(GemmArgs a, i
 // contiguous run of floor or ceil of units/groups, so a launch covers every
 // column in about one round of workgroups.
 // ---------------------------------------------------------------------------
-template <int NTM, int NSA, int NSW>
+template <int NTM, int NSA, int NSW, bool LO = false>
 struct Ws2Tile {
-  static constexpr int ASTAGE = 256 * 64;            // 256 rows x 32 bf16
+  // 256 rows x 32 bf16 of the activations (LO: then the 256 rows of their low part)
+  static constexpr int ASTAGE = (LO ? 2 : 1) * 256 * 64;
   static constexpr int WROWS = NTM * 16;
   static constexpr int WSTAGE = WROWS * 64;          // WROWS x 32 bf16
   static constexpr int ALOADS = ASTAGE / 1024 / 2;   // DMA loads per activation producer
@@ -283,11 +297,11 @@ __device__ __forceinline__ void ws2_produce(unsigned char* ring, const bf16_t* (
 }
 
 // consumer wavefront c of CW: rows (256/CW)c .. of the M tile, NTC 16-column tiles
-template <int EPI, int NTC, int NTM, int NSA, int NSW, int CW>
+template <int EPI, int NTC, int NTM, int NSA, int NSW, int CW, bool LO>
 __device__ __forceinline__ void ws2_consume(const GemmArgs& a, const unsigned char* smem, int nk,
                                             int n0, int m0, int c, int lane) {
   static_assert(kGated<EPI>, "gated projections (the SwiGLU / GeGLU epilogue) only");
-  using T = Ws2Tile<NTM, NSA, NSW>;
+  using T = Ws2Tile<NTM, NSA, NSW, LO>;
   constexpr int RPW = 256 / CW, MT = RPW / 16;  // rows and 16-row tiles per consumer
   f32x4_t acc[MT][NTC];
 #pragma unroll
@@ -312,6 +326,13 @@ __device__ __forceinline__ void ws2_consume(const GemmArgs& a, const unsigned ch
 #pragma unroll
       for (int ni = 0; ni < NTC; ++ni)
         acc[mi][ni] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bf[ni], acc[mi][ni], 0, 0, 0);
+      if constexpr (LO) {
+        const int rl = 256 + r;
+        const bf16x8_t al = *(const bf16x8_t*)(sa + rl * 64 + (T::pos(rl, kc) << 4));
+#pragma unroll
+        for (int ni = 0; ni < NTC; ++ni)
+          acc[mi][ni] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bf[ni], acc[mi][ni], 0, 0, 0);
+      }
     }
     // this step's LDS reads are complete before the barrier that lets them be refilled
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
@@ -337,10 +358,10 @@ __device__ __forceinline__ void ws2_consume(const GemmArgs& a, const unsigned ch
   }
 }
 
-template <int EPI, int NTM, int NSA, int NSW, int CW>
+template <int EPI, int NTM, int NSA, int NSW, int CW, bool LO>
 __global__ __launch_bounds__(64 * (CW + 4)) void gemm_ws2_kernel(GemmArgs a, int units, int groups,
                                                                  int tiles_m) {
-  using T = Ws2Tile<NTM, NSA, NSW>;
+  using T = Ws2Tile<NTM, NSA, NSW, LO>;
   __shared__ __attribute__((aligned(1024))) unsigned char smem[T::LDS];
   // workgroup -> (M tile mt, column group g); the M tiles of one group sit 8
   // workgroups apart, i.e. on one XCD, where they share the weights
@@ -364,32 +385,35 @@ __global__ __launch_bounds__(64 * (CW + 4)) void gemm_ws2_kernel(GemmArgs a, int
     ws2_produce<T::WLOADS, NSW, T::WSTAGE>(smem + NSA * T::ASTAGE, src, p * T::WLOADS * 1024, nk);
     return;
   }
-  if (wave >= CW) {  // activation producers: the M tile's rows (past M: row M-1)
+  if (wave >= CW) {  // activation producers: the M tile's rows (past M: row M-1), LO: then
+                     // the same rows of the low part
     const int p = wave - CW;
     const bf16_t* src[T::ALOADS];
 #pragma unroll
     for (int j = 0; j < T::ALOADS; ++j) {
       const int row = (p * T::ALOADS + j) * 16 + (lane >> 2);
-      src[j] = (const bf16_t*)a.A + (int64_t)min(m0 + row, M - 1) * K + T::pos(row, lane & 3) * 8;
+      const bf16_t* base = (const bf16_t*)(row < 256 ? a.A : a.A_lo);
+      src[j] = base + (int64_t)min(m0 + (row & 255), M - 1) * K + T::pos(row, lane & 3) * 8;
     }
     ws2_produce<T::ALOADS, NSA, T::ASTAGE>(smem, src, p * T::ALOADS * 1024, nk);
     return;
   }
   switch (nc / 16) {
-    case NTM: ws2_consume<EPI, NTM, NTM, NSA, NSW, CW>(a, smem, nk, n0, m0, wave, lane); break;
+    case NTM: ws2_consume<EPI, NTM, NTM, NSA, NSW, CW, LO>(a, smem, nk, n0, m0, wave, lane); break;
     case (NTM > 2 ? NTM - 2 : NTM):
-      ws2_consume<EPI, (NTM > 2 ? NTM - 2 : NTM), NTM, NSA, NSW, CW>(a, smem, nk, n0, m0, wave,
-                                                                     lane);
+      ws2_consume<EPI, (NTM > 2 ? NTM - 2 : NTM), NTM, NSA, NSW, CW, LO>(a, smem, nk, n0, m0,
+                                                                         wave, lane);
       break;
     default:
-      ws2_consume<EPI, (NTM > 4 ? NTM - 4 : 2), NTM, NSA, NSW, CW>(a, smem, nk, n0, m0, wave, lane);
+      ws2_consume<EPI, (NTM > 4 ? NTM - 4 : 2), NTM, NSA, NSW, CW, LO>(a, smem, nk, n0, m0, wave,
+                                                                       lane);
       break;
   }
 }
 
 // about `target` workgroups over (M tiles x column groups); a group holds at most
 // NTM*16 columns
-template <int EPI, int NTM, int NSA, int NSW, int CW = 4>
+template <int EPI, int NTM, int NSA, int NSW, bool LO, int CW = 4>
 static void gemm_ws2_go(const GemmArgs& a, int target, hipStream_t s) {
   const int units = a.N / 32;
   const int tiles_m = (a.M + 255) / 256;
@@ -397,8 +421,8 @@ static void gemm_ws2_go(const GemmArgs& a, int target, hipStream_t s) {
   groups = std::max(groups, (units + NTM / 2 - 1) / (NTM / 2));
   groups = std::min(groups, units);
   const int g8 = (groups + 7) & ~7;
-  launch_k(gemm_ws2_kernel<EPI, NTM, NSA, NSW, CW>, dim3(tiles_m * g8), dim3(64 * (CW + 4)), 0, s,
-           a, units, groups, tiles_m);
+  launch_k(gemm_ws2_kernel<EPI, NTM, NSA, NSW, CW, LO>, dim3(tiles_m * g8), dim3(64 * (CW + 4)),
+           0, s, a, units, groups, tiles_m);
 }
 
 // x[row] += sum over splits of the partials (split order), x the fp32 residual;
@@ -407,8 +431,8 @@ static void gemm_ws2_go(const GemmArgs& a, int target, hipStream_t s) {
 constexpr int kResidMaxChunks = 4;
 constexpr int kResidMaxSplits = 8;
 __global__ __launch_bounds__(256) void resid_norm_kernel(const float* ws, int splits, int M, int N,
-                                                         float* x, bf16_t* u, const float* g,
-                                                         float eps) {
+                                                         float* x, bf16_t* u, bf16_t* u_lo,
+                                                         const float* g, float eps) {
   __shared__ float red[4];
   const int row = blockIdx.x, tid = threadIdx.x;
   const int nch = N / 8;
@@ -462,12 +486,19 @@ __global__ __launch_bounds__(256) void resid_norm_kernel(const float* ws, int sp
   for (int j = 0; j < kResidMaxChunks; ++j) {
     const int c = tid + 256 * j;
     if (c >= nch) continue;
-    u32x4_t o;
+    u32x4_t o, ol;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      o[i] = (uint32_t)f32_to_bf16(v[j][2 * i] * r * gv[j][i >> 1][2 * (i & 1)]) |
-             ((uint32_t)f32_to_bf16(v[j][2 * i + 1] * r * gv[j][i >> 1][2 * (i & 1) + 1]) << 16);
+    for (int i = 0; i < 4; ++i) {
+      const float y0 = v[j][2 * i] * r * gv[j][i >> 1][2 * (i & 1)];
+      const float y1 = v[j][2 * i + 1] * r * gv[j][i >> 1][2 * (i & 1) + 1];
+      const bf16_t h0 = f32_to_bf16(y0), h1 = f32_to_bf16(y1);
+      o[i] = (uint32_t)h0 | ((uint32_t)h1 << 16);
+      // the low part: each value's rounding error, itself rounded to bf16
+      ol[i] = (uint32_t)f32_to_bf16(y0 - bf16_to_f32(h0)) |
+              ((uint32_t)f32_to_bf16(y1 - bf16_to_f32(h1)) << 16);
+    }
     *(u32x4_t*)(u + (size_t)row * N + c * 8) = o;
+    if (u_lo) *(u32x4_t*)(u_lo + (size_t)row * N + c * 8) = ol;
   }
 }
 
@@ -777,12 +808,12 @@ static hipError_t launch_qkv_reduce(const GemmArgs& a, int splits, hipStream_t s
   return hipGetLastError();
 }
 
-template <int EPI, int BM, int BN, int BK, int NS, int WGM = 2, int WGN = 2>
+template <int EPI, int BM, int BN, int BK, int NS, int WGM = 2, int WGN = 2, bool LO = false>
 static void gemm_bf16_go(const GemmArgs& a, int splits, int ksteps, hipStream_t s) {
   const int tiles_m = (a.M + BM - 1) / BM;
   const int tiles = tiles_m * (a.N / BN);
   const int per_xcd = (tiles + kXcds - 1) / kXcds;
-  launch_k(gemm_bf16_kernel<EPI, BM, BN, BK, NS, WGM, WGN>, dim3(kXcds * per_xcd * splits),
+  launch_k(gemm_bf16_kernel<EPI, BM, BN, BK, NS, WGM, WGN, LO>, dim3(kXcds * per_xcd * splits),
            dim3(64 * WGM * WGN), 0, s, a, tiles_m, tiles, ksteps);
 }
 
@@ -822,7 +853,7 @@ static hipError_t gemm_w4(const GemmArgs& a, hipStream_t s) {
   splits = (ngk + ksteps - 1) / ksteps;
   gemm_w4_pick<EPI_PARTIAL>(a, splits, ksteps, s);
   launch_k(resid_norm_kernel, dim3(a.M), dim3(256), 0, s, (const float*)a.ws, splits, a.M, a.N,
-           (float*)a.C, (bf16_t*)a.norm_out, a.norm_g, a.eps);
+           (float*)a.C, (bf16_t*)a.norm_out, (bf16_t*)a.norm_out_lo, a.norm_g, a.eps);
   return hipGetLastError();
 }
 
@@ -850,33 +881,60 @@ static hipError_t gemm_w4(const GemmArgs& a, hipStream_t s) {
 //    2048: 7.9 us against 8.3 us; 63 x 1024 x 4096: 8.9 against 9.5).
 // Split projections reduce their fp32 partials in split order in a second kernel:
 // the residual add (+ next RMSNorm), or RoPE + K/V write for q/k/v.
-template <int EPI>
+// LO: the activations carry a low part (A_lo); the same shapes, with one ring stage
+// less where the doubled activation rows would not fit the LDS
+template <int EPI, bool LO>
 static void gated_go(const GemmArgs& a, hipStream_t s) {
   if (a.M <= 64 && a.N % 128 == 0 && a.N / 128 >= 128)
-    gemm_bf16_go<EPI, 64, 128, 64, 4>(a, 1, a.K / 64, s);
+    gemm_bf16_go<EPI, 64, 128, 64, 4, 2, 2, LO>(a, 1, a.K / 64, s);
   else if (a.M <= 64)
-    gemm_bf16_go<EPI, 64, 32, 64, 4, 4, 1>(a, 1, a.K / 64, s);
+    gemm_bf16_go<EPI, 64, 32, 64, 4, 4, 1, LO>(a, 1, a.K / 64, s);
   else if (a.M > 128 && a.M <= 256 && a.N % 32 == 0)
-    gemm_ws2_go<EPI, 6, 4, 8>(a, 256, s);
+    gemm_ws2_go<EPI, 6, LO ? 3 : 4, 8, LO>(a, 256, s);
   else if (a.M > 128 && a.N % 256 == 0 && ((a.M + 255) / 256) * (a.N / 256) >= 192)
-    gemm_bf16_go<EPI, 256, 256, 32, 3, 4, 2>(a, 1, a.K / 32, s);
+    gemm_bf16_go<EPI, 256, 256, 32, 3, 4, 2, LO>(a, 1, a.K / 32, s);
   else if (a.M > 128 && a.N % 128 == 0)
-    gemm_bf16_go<EPI, 256, 128, 32, 4, 4, 2>(a, 1, a.K / 32, s);
+    gemm_bf16_go<EPI, 256, 128, 32, LO ? 3 : 4, 4, 2, LO>(a, 1, a.K / 32, s);
   else
-    gemm_bf16_go<EPI, 128, 64, 64, 3>(a, 1, a.K / 64, s);
+    gemm_bf16_go<EPI, 128, 64, 64, 3, 2, 2, LO>(a, 1, a.K / 64, s);
+}
+
+// the q/k/v projection: RoPE + K/V write in the epilogue, or split-K partials and
+// the q/k/v reduction
+template <bool LO>
+static hipError_t qkv_go(const GemmArgs& a, bool tall, bool skinny, int splits, int ksteps,
+                         int ksteps_all, hipStream_t s) {
+  if (splits == 1) {
+    if (skinny) gemm_bf16_go<EPI_QKV, 64, 32, 64, 3, 4, 1, LO>(a, 1, ksteps_all, s);
+    else gemm_bf16_go<EPI_QKV, 64, 64, 64, 3, 2, 2, LO>(a, 1, ksteps_all, s);
+  } else {
+    if (tall && !LO) gemm_bf16_go<EPI_PARTIAL, 256, 64, 64, 3, 4, 2>(a, splits, ksteps, s);
+    else if (skinny) gemm_bf16_go<EPI_PARTIAL, 64, 32, 64, 3, 4, 1, LO>(a, splits, ksteps, s);
+    else gemm_bf16_go<EPI_PARTIAL, 64, 64, 64, 3, 2, 2, LO>(a, splits, ksteps, s);
+    if (hipError_t e = launch_qkv_reduce(a, splits, s); e != hipSuccess) return e;
+  }
+  return hipGetLastError();
 }
 
 static hipError_t gemm_bf16(const GemmArgs& a, hipStream_t s) {
   if (a.K % 64 != 0 || a.N % 64 != 0 || a.M < 1) return hipErrorInvalidValue;
   if (a.wf == WF_INT4) return gemm_w4(a, s);
+  const bool lo = a.A_lo != nullptr;
   if (a.epi == EPI_SWIGLU) {
-    if (a.glu) gated_go<EPI_GEGLU_K>(a, s);
-    else gated_go<EPI_SWIGLU>(a, s);
+    if (a.glu) {
+      if (lo) gated_go<EPI_GEGLU_K, true>(a, s);
+      else gated_go<EPI_GEGLU_K, false>(a, s);
+    } else {
+      if (lo) gated_go<EPI_SWIGLU, true>(a, s);
+      else gated_go<EPI_SWIGLU, false>(a, s);
+    }
     return hipGetLastError();
   }
   if (a.epi != EPI_QKV && a.epi != EPI_RESID) return hipErrorInvalidValue;
+  if (lo && a.epi != EPI_QKV) return hipErrorInvalidValue;  // residual inputs carry no low part
   const int ksteps_all = a.K / 64;
-  const bool tall = a.M >= 512 && ksteps_all >= 128;  // 256 x 64 tiles, 8 wavefronts
+  // 256 x 64 tiles, 8 wavefronts (with a low part the doubled rows would not fit the LDS)
+  const bool tall = a.M >= 512 && ksteps_all >= 128 && !lo;
   const bool skinny = !tall && a.M <= 64;               // 64 x 32 tiles, 4 wavefronts along M
   const int tiles = tall ? ((a.M + 255) / 256) * (a.N / 64)
                          : skinny ? a.N / 32 : ((a.M + 63) / 64) * (a.N / 64);
@@ -889,18 +947,9 @@ static hipError_t gemm_bf16(const GemmArgs& a, hipStream_t s) {
   if (a.ws == nullptr || (size_t)a.M * a.N > a.ws_elems) splits = 1;
   const int ksteps = (ksteps_all + splits - 1) / splits;
   splits = (ksteps_all + ksteps - 1) / ksteps;
-  if (a.epi == EPI_QKV) {
-    if (splits == 1) {
-      if (skinny) gemm_bf16_go<EPI_QKV, 64, 32, 64, 3, 4, 1>(a, 1, ksteps_all, s);
-      else gemm_bf16_go<EPI_QKV, 64, 64, 64, 3>(a, 1, ksteps_all, s);
-    } else {
-      if (tall) gemm_bf16_go<EPI_PARTIAL, 256, 64, 64, 3, 4, 2>(a, splits, ksteps, s);
-      else if (skinny) gemm_bf16_go<EPI_PARTIAL, 64, 32, 64, 3, 4, 1>(a, splits, ksteps, s);
-      else gemm_bf16_go<EPI_PARTIAL, 64, 64, 64, 3>(a, splits, ksteps, s);
-      if (hipError_t e = launch_qkv_reduce(a, splits, s); e != hipSuccess) return e;
-    }
-    return hipGetLastError();
-  }
+  if (a.epi == EPI_QKV)
+    return lo ? qkv_go<true>(a, tall, skinny, splits, ksteps, ksteps_all, s)
+              : qkv_go<false>(a, tall, skinny, splits, ksteps, ksteps_all, s);
   // residual projection: always through the partial buffer and the reduction kernel
   if (a.ws == nullptr || (size_t)a.M * a.N > a.ws_elems) return hipErrorInvalidValue;
   if (a.N % 8 != 0 || a.N / 8 > 256 * kResidMaxChunks) return hipErrorInvalidValue;
@@ -908,7 +957,7 @@ static hipError_t gemm_bf16(const GemmArgs& a, hipStream_t s) {
   else if (skinny) gemm_bf16_go<EPI_PARTIAL, 64, 32, 64, 3, 4, 1>(a, splits, ksteps, s);
   else gemm_bf16_go<EPI_PARTIAL, 64, 64, 64, 3>(a, splits, ksteps, s);
   launch_k(resid_norm_kernel, dim3(a.M), dim3(256), 0, s, (const float*)a.ws, splits, a.M, a.N,
-           (float*)a.C, (bf16_t*)a.norm_out, a.norm_g, a.eps);
+           (float*)a.C, (bf16_t*)a.norm_out, (bf16_t*)a.norm_out_lo, a.norm_g, a.eps);
   return hipGetLastError();
 }
 

@@ -75,6 +75,10 @@ enum WeightFmt { WF_ACT = 0, WF_INT4 = 1 };  // weights in the activation type /
 
 struct GemmArgs {
   const void* A = nullptr;  // [M][K] activations
+  // bf16 only: the low part of the activations, A_lo = bf16(a - A) for the exact
+  // value a whose bf16 rounding is A; when set the product is (A + A_lo) W^T, i.e.
+  // the input carries about 16 significant bits (q/k/v and gated projections)
+  const void* A_lo = nullptr;
   const void* W = nullptr;  // [N][K] weights (physical layout); INT4: codes then scales
   int wf = WF_ACT;
   int M = 0, N = 0, K = 0;
@@ -88,6 +92,7 @@ struct GemmArgs {
   float* ws = nullptr;
   size_t ws_elems = 0;
   void* norm_out = nullptr;
+  void* norm_out_lo = nullptr;  // bf16: also the low part of norm_out (see A_lo)
   const float* norm_g = nullptr;
   float eps = 0.f;
 };
@@ -173,7 +178,9 @@ hipError_t launch_embed_rope1(int token_scalar, const unsigned long long* token_
 hipError_t launch_embed(const int* tokens, int token_scalar, const unsigned long long* token_key,
                         int n, const void* E, void* x, int H, int dt,
                         unsigned long long* reset_cell, hipStream_t s);
-hipError_t launch_rmsnorm(const void* x, const float* g, void* u, int rows, int H, float eps,
+// u = RMSNorm(x) rows; bf16: u_lo (nullable) receives the low part bf16(exact - u)
+hipError_t launch_rmsnorm(const void* x, const float* g, void* u, void* u_lo, int rows, int H,
+                          float eps,
                           int dt, hipStream_t s);
 hipError_t launch_gemm(const GemmArgs& a, int dt, hipStream_t s);
 hipError_t launch_gemv(const GemvArgs& a, int dt, hipStream_t s, int* grid_out);

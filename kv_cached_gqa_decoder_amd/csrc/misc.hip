@@ -305,7 +305,7 @@ hipError_t launch_to_f32(const void* in, float* out, int64_t n, int dt, hipStrea
 // row, fp32 statistics: u = x * (mean(x^2) + eps)^-1/2 * g. H is a multiple of 64.
 template <typename T>
 __global__ __launch_bounds__(256) void rmsnorm_kernel(const float* x, const float* g, T* u,
-                                                      int rows, int H, float eps) {
+                                                      T* u_lo, int rows, int H, float eps) {
   const int lane = threadIdx.x & 63;
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (row >= rows) return;
@@ -322,18 +322,25 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const float* x, const floa
   for (int c = lane; c < H / 4; c += 64) {
     const f32x4_t v = *(const f32x4_t*)(xr + c * 4);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) St<T>::st(ur, (size_t)c * 4 + i, v[i] * r * g[c * 4 + i]);
+    for (int i = 0; i < 4; ++i) {
+      const float y = v[i] * r * g[c * 4 + i];
+      St<T>::st(ur, (size_t)c * 4 + i, y);
+      if constexpr (sizeof(T) == 2) {
+        // low part: the rounding error of the stored value, itself rounded to bf16
+        if (u_lo) u_lo[(int64_t)row * H + c * 4 + i] = f32_to_bf16(y - bf16_to_f32(f32_to_bf16(y)));
+      }
+    }
   }
 }
-hipError_t launch_rmsnorm(const void* x, const float* g, void* u, int rows, int H, float eps,
-                          int dt, hipStream_t s) {
+hipError_t launch_rmsnorm(const void* x, const float* g, void* u, void* u_lo, int rows, int H,
+                          float eps, int dt, hipStream_t s) {
   const int grid = (rows + 3) / 4;
   if (dt == DT_F32)
     launch_k(rmsnorm_kernel<float>, dim3(grid), dim3(256), 0, s, (const float*)x, g, (float*)u,
-             rows, H, eps);
+             (float*)nullptr, rows, H, eps);
   else
     launch_k(rmsnorm_kernel<bf16_t>, dim3(grid), dim3(256), 0, s, (const float*)x, g, (bf16_t*)u,
-             rows, H, eps);
+             (bf16_t*)u_lo, rows, H, eps);
   return hipGetLastError();
 }
 

@@ -60,6 +60,7 @@ struct vla_pool {
   BlockPool p;
 };
 
+
 namespace vla {
 // event pairs of the profiled kernel launches since the last enable
 struct ProfSink {
@@ -115,6 +116,7 @@ struct vla_model {
   // scratch
   void* x = nullptr;
   void* u = nullptr;
+  void* u_lo = nullptr;         // bf16 weights: low part of the normalised rows (see GemmArgs)
   void* qbuf = nullptr;
   void* ao = nullptr;
   void* act = nullptr;
@@ -424,9 +426,10 @@ void run_layers(vla_model* m, const KvView& view, int n, int64_t pos0, int cb0, 
       const bool bf16 = m->dt == DT_BF16;
       if (!bf16 || l == 0)
         LAUNCH(m, VLA_K_RMSNORM, st,
-               launch_rmsnorm(m->x, m->norm_ones, m->u, n, H, c.rms_eps, m->dt, st));
+               launch_rmsnorm(m->x, m->norm_ones, m->u, m->u_lo, n, H, c.rms_eps, m->dt, st));
       GemmArgs q;
       q.A = m->u;
+      q.A_lo = m->u_lo;
       q.W = m->wqkv[l];
       q.wf = m->wf;
       q.M = n;
@@ -451,14 +454,16 @@ void run_layers(vla_model* m, const KvView& view, int n, int64_t pos0, int cb0, 
       o.ws = m->gemm_ws;
       o.ws_elems = m->gemm_ws_elems;
       o.norm_out = m->u;
+      o.norm_out_lo = m->u_lo;
       o.norm_g = m->norm_ones;
       o.eps = c.rms_eps;
       LAUNCH(m, VLA_K_GEMM_O, st, launch_gemm(o, m->dt, st));
       if (!bf16)
         LAUNCH(m, VLA_K_RMSNORM, st,
-               launch_rmsnorm(m->x, m->norm_ones, m->u, n, H, c.rms_eps, m->dt, st));
+               launch_rmsnorm(m->x, m->norm_ones, m->u, nullptr, n, H, c.rms_eps, m->dt, st));
       GemmArgs gu;
       gu.A = m->u;
+      gu.A_lo = m->u_lo;
       gu.W = m->wgu[l];
       gu.wf = m->wf;
       gu.M = n;
@@ -480,6 +485,7 @@ void run_layers(vla_model* m, const KvView& view, int n, int64_t pos0, int cb0, 
       dn.ws = m->gemm_ws;
       dn.ws_elems = m->gemm_ws_elems;
       dn.norm_out = l + 1 < c.n_layers ? m->u : nullptr;
+      dn.norm_out_lo = l + 1 < c.n_layers ? m->u_lo : nullptr;
       dn.norm_g = m->norm_ones;
       dn.eps = c.rms_eps;
       LAUNCH(m, VLA_K_GEMM_DOWN, st, launch_gemm(dn, m->dt, st));
@@ -679,6 +685,7 @@ void build_model(vla_model* m, const vla_config& cfg, const vla_model* borrow) {
   const size_t mc = c.max_chunk;
   m->x = dalloc(m, mc * H * sizeof(float));  // the residual stream is fp32
   m->u = dalloc(m, mc * H * e);
+  if (m->dt == DT_BF16 && m->wf == WF_ACT) m->u_lo = dalloc(m, mc * H * e);
   m->qbuf = dalloc(m, mc * hq * d * e);
   m->ao = dalloc(m, mc * hq * d * e);
   m->act = dalloc(m, mc * (size_t)c.ffn * e);

@@ -93,9 +93,11 @@ def test_pi0_tiny_prefix_cache_and_denoise():
 
 def test_geglu_head_dim_256_prefill_and_decode():
     """GeGLU FFN and head dim 256 with a vocabulary: prefill, then greedy decodes (the
-    decode attention's key-split shape at d = 256). Weights N(0, 0.05^2): at 0.08 this
-    two-head model's logits amplify the bf16 rounding of its activations to about the
-    tolerance band on some steps."""
+    decode attention's key-split shape at d = 256). Weights N(0, 0.05^2): at 0.08 an
+    exact model of this configuration's bf16 storage points (fp64 everywhere else)
+    already reaches a max relative error of 3.2e-2, over the 2e-2 bound, with no single
+    rounding point dominating (tests/test_precision_budget.py); at 0.05 it stays below
+    1e-2, so the bound is a real check of the kernels here."""
     p = dict(TINY_VLM, vocab=800, kv_only_last=0, num_blocks=16, seed=62)
     ocfg = _ocfg(p, "geglu", 0.05)
     sess = D.Session(ocfg)
