@@ -327,6 +327,61 @@ int32_t vla_pool_free_count(const vla_pool* p);
 /* The pool's free-list bottom first (out[n-1] is popped next), as vla_kv_free_list. */
 vla_status vla_pool_free_list(const vla_pool* p, int32_t* out, int32_t cap, int32_t* n_out);
 
+/* ---- Admission control of a real-time reasoning cycle ------------------------
+ * ("Can an LLM Forget the Right Things?", section 4: refuse to start a chunk
+ * whose estimated cost does not fit the rest of the cycle's deadline.) Host-only;
+ * no HIP calls; usable without a GPU. A handle is single-threaded.
+ *   estimate = ema_prefill_per_token * prefill_tokens + ema_decode_per_token * decode_tokens
+ *   admit    = no measurement recorded yet, or estimate <= deadline - elapsed - margin
+ *   ema     <- (1 - alpha) * ema + alpha * measured   (prefill and decode separately;
+ *              the first measurement initialises both)
+ * A refused cycle is the caller's fallback (e.g. repeat the last action). A cycle
+ * that ends after the deadline counts as a deadline miss. */
+typedef struct vla_admission vla_admission;
+typedef struct {
+  double deadline_ms;       /* cycle deadline, ms (> 0; 33 in the page's runtime) */
+  double safety_margin_ms;  /* kept free of estimated work, ms (>= 0; 2 on the page) */
+  double ema_alpha;         /* weight of a new measurement, (0, 1] (0.2 on the page) */
+  int32_t prefill_tokens;   /* tokens one admitted chunk prefills (>= 1) */
+  int32_t decode_tokens;    /* decode steps one admitted chunk runs (>= 0) */
+} vla_admission_config;
+typedef struct {
+  int64_t cycles;           /* cycles ended with vla_admission_cycle_end */
+  int64_t admitted;         /* ... whose chunk was admitted */
+  int64_t refused;          /* ... that fell back */
+  int64_t deadline_misses;  /* ... that ended after the deadline */
+  double worst_cycle_ms;    /* longest cycle */
+  double last_overrun_ms;   /* overrun of the latest missed cycle (0 if none) */
+  double ema_prefill_ms_per_token;
+  double ema_decode_ms_per_token;
+  int32_t has_sample;       /* 0 until the first vla_admission_record */
+} vla_admission_stats;
+/* Errors: VLA_E_INVALID (null out, sizes or rates outside the ranges above). */
+vla_status vla_admission_create(const vla_admission_config* cfg, vla_admission** out);
+void vla_admission_destroy(vla_admission* a);
+/* Start a cycle: the cycle clock (steady clock) restarts. */
+vla_status vla_admission_cycle_begin(vla_admission* a);
+/* Milliseconds since the cycle began. */
+vla_status vla_admission_elapsed_ms(const vla_admission* a, double* out_ms);
+/* The decision for a cycle `elapsed_ms` into its budget: *out_admit 1 or 0, and
+ * the current estimate (ms, nullable). */
+vla_status vla_admission_should_admit(const vla_admission* a, double elapsed_ms,
+                                      int32_t* out_admit, double* out_estimate_ms);
+/* Feed the measured cost of a finished chunk: prefill_ms over prefill_tokens (>= 1)
+ * and decode_ms over decode_tokens (>= 1). Errors: VLA_E_INVALID (token counts < 1,
+ * negative or non-finite times). */
+vla_status vla_admission_record(vla_admission* a, double prefill_ms, int32_t prefill_tokens,
+                                double decode_ms, int32_t decode_tokens);
+/* End the cycle: count it as admitted (1) or refused (0), and as a deadline miss when
+ * its duration on the cycle clock exceeds the deadline; the duration goes to
+ * *out_cycle_ms (nullable). */
+vla_status vla_admission_cycle_end(vla_admission* a, int32_t admitted, double* out_cycle_ms);
+/* Block until the cycle's deadline (cycle start + deadline): sleep through all but
+ * the last millisecond, then spin (same page, section 3: sleep is only accurate to
+ * about a millisecond). Returns at once when the deadline has passed. */
+vla_status vla_admission_sleep_until_deadline(const vla_admission* a);
+vla_status vla_admission_stats_out(const vla_admission* a, vla_admission_stats* out);
+
 #ifdef __cplusplus
 }
 #endif

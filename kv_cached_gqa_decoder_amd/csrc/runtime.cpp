@@ -10,6 +10,7 @@
 #include <vector>
 
 #include "../../include/vla.h"
+#include "admission.hpp"
 #include "block_pool.hpp"
 #include "kernels.hpp"
 
@@ -60,6 +61,9 @@ struct vla_pool {
   BlockPool p;
 };
 
+struct vla_admission {
+  Admission a;
+};
 
 namespace vla {
 // event pairs of the profiled kernel launches since the last enable
@@ -1297,6 +1301,83 @@ vla_status vla_pool_free_list(const vla_pool* p, int32_t* out, int32_t cap, int3
   return guarded([&] {
     if (!p || !n_out) raise(VLA_E_INVALID, "null argument");
     copy_free_list(p->p, out, cap, n_out);
+  });
+}
+
+// ---- admission control ("Can an LLM Forget the Right Things?", section 4) ----
+vla_status vla_admission_create(const vla_admission_config* cfg, vla_admission** out) {
+  return guarded([&] {
+    if (!out || !cfg) raise(VLA_E_INVALID, "null argument");
+    *out = nullptr;
+    if (!(cfg->deadline_ms > 0.0) || !std::isfinite(cfg->deadline_ms))
+      raise(VLA_E_INVALID, "deadline_ms must be finite and > 0");
+    if (!(cfg->safety_margin_ms >= 0.0) || !std::isfinite(cfg->safety_margin_ms))
+      raise(VLA_E_INVALID, "safety_margin_ms must be finite and >= 0");
+    if (!(cfg->ema_alpha > 0.0 && cfg->ema_alpha <= 1.0)) raise(VLA_E_INVALID, "ema_alpha in (0, 1]");
+    if (cfg->prefill_tokens < 1 || cfg->decode_tokens < 0)
+      raise(VLA_E_INVALID, "prefill_tokens >= 1, decode_tokens >= 0");
+    *out = new vla_admission{Admission(cfg->deadline_ms, cfg->safety_margin_ms, cfg->ema_alpha,
+                                       cfg->prefill_tokens, cfg->decode_tokens)};
+  });
+}
+void vla_admission_destroy(vla_admission* a) { delete a; }
+vla_status vla_admission_cycle_begin(vla_admission* a) {
+  return guarded([&] {
+    if (!a) raise(VLA_E_INVALID, "null argument");
+    a->a.cycle_begin();
+  });
+}
+vla_status vla_admission_elapsed_ms(const vla_admission* a, double* out_ms) {
+  return guarded([&] {
+    if (!a || !out_ms) raise(VLA_E_INVALID, "null argument");
+    *out_ms = a->a.elapsed_ms();
+  });
+}
+vla_status vla_admission_should_admit(const vla_admission* a, double elapsed_ms,
+                                      int32_t* out_admit, double* out_estimate_ms) {
+  return guarded([&] {
+    if (!a || !out_admit) raise(VLA_E_INVALID, "null argument");
+    if (!std::isfinite(elapsed_ms)) raise(VLA_E_INVALID, "elapsed_ms must be finite");
+    *out_admit = a->a.should_admit(elapsed_ms, out_estimate_ms) ? 1 : 0;
+  });
+}
+vla_status vla_admission_record(vla_admission* a, double prefill_ms, int32_t prefill_tokens,
+                                double decode_ms, int32_t decode_tokens) {
+  return guarded([&] {
+    if (!a) raise(VLA_E_INVALID, "null argument");
+    if (prefill_tokens < 1 || decode_tokens < 1) raise(VLA_E_INVALID, "token counts must be >= 1");
+    if (!(prefill_ms >= 0.0) || !(decode_ms >= 0.0) || !std::isfinite(prefill_ms) ||
+        !std::isfinite(decode_ms))
+      raise(VLA_E_INVALID, "times must be finite and >= 0");
+    a->a.record(prefill_ms, prefill_tokens, decode_ms, decode_tokens);
+  });
+}
+vla_status vla_admission_cycle_end(vla_admission* a, int32_t admitted, double* out_cycle_ms) {
+  return guarded([&] {
+    if (!a) raise(VLA_E_INVALID, "null argument");
+    const double ms = a->a.cycle_end(admitted != 0);
+    if (out_cycle_ms) *out_cycle_ms = ms;
+  });
+}
+vla_status vla_admission_sleep_until_deadline(const vla_admission* a) {
+  return guarded([&] {
+    if (!a) raise(VLA_E_INVALID, "null argument");
+    a->a.sleep_until_deadline();
+  });
+}
+vla_status vla_admission_stats_out(const vla_admission* a, vla_admission_stats* out) {
+  return guarded([&] {
+    if (!a || !out) raise(VLA_E_INVALID, "null argument");
+    const Admission& x = a->a;
+    out->cycles = x.cycles_;
+    out->admitted = x.admitted_;
+    out->refused = x.refused_;
+    out->deadline_misses = x.misses_;
+    out->worst_cycle_ms = x.worst_ms_;
+    out->last_overrun_ms = x.last_overrun_ms_;
+    out->ema_prefill_ms_per_token = x.ema_prefill_;
+    out->ema_decode_ms_per_token = x.ema_decode_;
+    out->has_sample = x.has_sample_ ? 1 : 0;
   });
 }
 

@@ -53,6 +53,18 @@ class vla_state(ctypes.Structure):
                 ("logical_blocks", c_int32)]
 
 
+class vla_admission_config(ctypes.Structure):
+    _fields_ = [("deadline_ms", c_double), ("safety_margin_ms", c_double), ("ema_alpha", c_double),
+                ("prefill_tokens", c_int32), ("decode_tokens", c_int32)]
+
+
+class vla_admission_stats(ctypes.Structure):
+    _fields_ = [("cycles", c_int64), ("admitted", c_int64), ("refused", c_int64),
+                ("deadline_misses", c_int64), ("worst_cycle_ms", c_double),
+                ("last_overrun_ms", c_double), ("ema_prefill_ms_per_token", c_double),
+                ("ema_decode_ms_per_token", c_double), ("has_sample", c_int32)]
+
+
 _SIGS = {
     "vla_model_create": (c_int32, [POINTER(vla_config), POINTER(c_void_p)]),
     "vla_model_destroy": (None, [c_void_p]),
@@ -90,6 +102,16 @@ _SIGS = {
     "vla_pool_alloc": (c_int32, [c_void_p, c_int32, c_void_p]),
     "vla_pool_release": (c_int32, [c_void_p, c_void_p, c_int32]),
     "vla_pool_free_count": (c_int32, [c_void_p]),
+    "vla_admission_create": (c_int32, [POINTER(vla_admission_config), POINTER(c_void_p)]),
+    "vla_admission_destroy": (None, [c_void_p]),
+    "vla_admission_cycle_begin": (c_int32, [c_void_p]),
+    "vla_admission_elapsed_ms": (c_int32, [c_void_p, POINTER(c_double)]),
+    "vla_admission_should_admit": (c_int32, [c_void_p, c_double, POINTER(c_int32),
+                                             POINTER(c_double)]),
+    "vla_admission_record": (c_int32, [c_void_p, c_double, c_int32, c_double, c_int32]),
+    "vla_admission_cycle_end": (c_int32, [c_void_p, c_int32, POINTER(c_double)]),
+    "vla_admission_sleep_until_deadline": (c_int32, [c_void_p]),
+    "vla_admission_stats_out": (c_int32, [c_void_p, POINTER(vla_admission_stats)]),
 }
 
 _lib = None
@@ -323,6 +345,57 @@ def vla_pool_release(p: int, blocks) -> None:
 
 def vla_pool_free_count(p: int) -> int:
     return load().vla_pool_free_count(p)
+
+
+def vla_admission_create(deadline_ms=33.0, safety_margin_ms=2.0, ema_alpha=0.2,
+                         prefill_tokens=32, decode_tokens=8) -> int:
+    cfg = vla_admission_config(deadline_ms, safety_margin_ms, ema_alpha, prefill_tokens,
+                               decode_tokens)
+    h = c_void_p()
+    _check(load().vla_admission_create(byref(cfg), byref(h)))
+    return h.value
+
+
+def vla_admission_destroy(a: int) -> None:
+    load().vla_admission_destroy(a)
+
+
+def vla_admission_cycle_begin(a: int) -> None:
+    _check(load().vla_admission_cycle_begin(a))
+
+
+def vla_admission_elapsed_ms(a: int) -> float:
+    v = c_double(0.0)
+    _check(load().vla_admission_elapsed_ms(a, byref(v)))
+    return v.value
+
+
+def vla_admission_should_admit(a: int, elapsed_ms: float):
+    """(admit?, estimate in ms)."""
+    ok, est = c_int32(0), c_double(0.0)
+    _check(load().vla_admission_should_admit(a, elapsed_ms, byref(ok), byref(est)))
+    return bool(ok.value), est.value
+
+
+def vla_admission_record(a: int, prefill_ms: float, prefill_tokens: int, decode_ms: float,
+                         decode_tokens: int) -> None:
+    _check(load().vla_admission_record(a, prefill_ms, prefill_tokens, decode_ms, decode_tokens))
+
+
+def vla_admission_cycle_end(a: int, admitted: bool) -> float:
+    ms = c_double(0.0)
+    _check(load().vla_admission_cycle_end(a, 1 if admitted else 0, byref(ms)))
+    return ms.value
+
+
+def vla_admission_sleep_until_deadline(a: int) -> None:
+    _check(load().vla_admission_sleep_until_deadline(a))
+
+
+def vla_admission_stats_out(a: int) -> dict:
+    st = vla_admission_stats()
+    _check(load().vla_admission_stats_out(a, byref(st)))
+    return {k: getattr(st, k) for k, _ in vla_admission_stats._fields_}
 
 
 # ---- configurations of the workloads --------------------------------------
