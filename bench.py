@@ -158,6 +158,17 @@ def gpu_leg(args):
     gu_reps = 8
     gu_avg = m.profile_replay("gemv_gateup", reps=gu_reps, stream=sh)
     gu_n = gu_reps * L
+    # the same kernel inside decode steps, with a start/stop event pair carried in each of
+    # its dispatches (the events lengthen a 12 us kernel by about 1.3 us)
+    m.kv_rollback(ctx_fid)
+    m.prefill_chunk(embeds=chunk, n=CHUNK, stream=sh)
+    m.profile_enable("gemv_gateup")
+    tok = 1
+    for _ in range(DECODES):
+        tok = m.decode_step(tok, stream=sh)
+    gi_ms, gi_n = m.profile_read()
+    m.profile_enable(0)
+    gu_in_step = gi_ms / max(gi_n, 1)
 
     pre = [e[0].elapsed_time(e[1]) for e in evs]
     dec = [e[1].elapsed_time(e[2]) / DECODES for e in evs]
@@ -193,6 +204,8 @@ def gpu_leg(args):
     del chunk
     torch.cuda.synchronize()
 
+    c1 = c1_leg(args)
+    peaks = measured_peaks()
     ev_leg = eviction_leg(args) if not args.no_eviction else None
     lc_leg = longctx_leg(args) if not args.no_longctx else None
     p0_leg = pi0_leg(args) if not args.no_pi0 else None
@@ -250,8 +263,24 @@ def gpu_leg(args):
             "algorithmic_bytes_per_launch": gateup_bytes(),
             "avg_launch_us": round(gu_avg * 1e3, 3),
             "launches": gu_n,
+            "timing": "replayed back to back over the 28 layers' weights between two stream "
+                      "events",
+            "in_step_avg_launch_us_with_events": round(gu_in_step * 1e3, 3),
+            "in_step_frac_with_events": round(gateup_bytes() / (gu_in_step * 1e-3)
+                                              / (PEAK_HBM_GBS * 1e9), 4),
+            "measured_peak_copy_gbs": peaks["copy_gbs"],
+            "measured_peak_read_gbs": peaks["read_gbs"],
+            "frac_of_measured_read_peak": round(gu_gbs / peaks["read_gbs"], 4),
         },
     }
+    res["phases"].update(c1)
+    res["phases"]["measured_peak_copy_gbs"] = peaks["copy_gbs"]
+    res["phases"]["measured_peak_read_gbs"] = peaks["read_gbs"]
+    res["phases"]["measured_peak_mfma_bf16_tflops"] = peaks["mfma_bf16_tflops"]
+    res["phases"]["prefill_frac_of_measured_mfma_peak"] = round(
+        fl / (pre_ms * 1e-3) / (peaks["mfma_bf16_tflops"] * 1e12), 4)
+    res["phases"]["decode_frac_of_measured_read_peak"] = round(
+        dbytes / (dec_ms * 1e-3) / (peaks["read_gbs"] * 1e9), 4)
     if ev_leg:
         res["phases"].update(ev_leg)
     if lc_leg:
@@ -276,10 +305,12 @@ def eviction_leg(args):
     p = vla.PRESETS["c3_semantic_eviction"]
     log("[bench] eviction leg: creating the model and 128 raw frames")
     m = vla.Model(vla.make_config(**p))
+    raw = []
     for f in range(128):
         _, (ks, vs) = synth.clustered_frame(p["seed"], f, L, 64, HKV, D)
         kt = torch.from_numpy(ks.view(np.int16)).view(torch.bfloat16).cuda()
         vt = torch.from_numpy(vs.view(np.int16)).view(torch.bfloat16).cuda()
+        raw.append((kt, vt))
         m.kv_append_raw(kt, vt, 64, stream=sh)
     embeds = []
     for c in range(32):
@@ -309,11 +340,34 @@ def eviction_leg(args):
         m.kv_refresh_mean_keys(stream=sh)
     r_ms, r_n = m.profile_read()
     m.profile_enable(0)
+    # the same 32 insert cycles under each eviction policy (evict-until-room, then the
+    # 64-token prefill): time per call, and how the 16 clusters' 8 frames each fare
+    ab = {}
+    for policy in ("semantic", "adjacent", "fifo"):
+        m.kv_rollback(-1)
+        for kt, vt in raw:
+            m.kv_append_raw(kt, vt, 64, stream=sh)
+        torch.cuda.synchronize()
+        t_us = []
+        for c in range(32):
+            torch.cuda.synchronize()       # the previous cycle's prefill is not timed here
+            t0 = time.perf_counter()
+            m.kv_make_room(policy, 64, stream=sh)
+            t_us.append((time.perf_counter() - t0) * 1e6)
+            m.prefill_chunk(embeds=embeds[c], n=64, stream=sh)
+        torch.cuda.synchronize()
+        kept = [int(f) for f in m.frames() if f < 128]
+        per = [sum(1 for f in kept if f % 16 == k) for k in range(16)]
+        ab[policy] = {"make_room_us_median": round(statistics.median(t_us), 2),
+                      "raw_frames_kept_per_cluster_min": min(per),
+                      "raw_frames_kept_per_cluster_max": max(per),
+                      "max_similarity_left": round(m.kv_score(0, stream=sh)[1], 9)}
     m.close()
     torch.cuda.synchronize()
     refresh_bytes = L * 128 * 64 * HKV * D * 2
     r_avg = r_ms / max(r_n, 1)
     return {
+        "eviction_policy_ab": ab,
         "evict_score_us_median": round(statistics.median(sc_us), 2),
         "evict_score_kernel_us": round(s_ms / max(s_n, 1) * 1e3, 2),
         "evict_cycle_prefill64_ms_median": round(statistics.median(pf_ms), 4),
@@ -321,6 +375,84 @@ def eviction_leg(args):
         "meankey_refresh_gbs": round(refresh_bytes / (r_avg * 1e-3) / 1e9, 1),
         "meankey_refresh_hbm_frac": round(refresh_bytes / (r_avg * 1e-3) / (PEAK_HBM_GBS * 1e9), 4),
     }
+
+
+# ---------------------------------------------------------------------------
+def c1_leg(args):
+    """The fp32 tiny decoder (2 layers, hidden 256, 4/2 heads, head dim 64, FFN 688, vocab
+    1024): a 64-token prompt of uniform ids prefilled, then 16 greedy decodes; median over
+    repeats (rolled back between them)."""
+    import torch
+
+    import kv_cached_gqa_decoder_amd as vla
+    import synth
+
+    stream = torch.cuda.current_stream()
+    sh = stream.cuda_stream
+    p = vla.PRESETS["c1_tiny_f32"]
+    m = vla.Model(vla.make_config(**p))
+    ids = synth.token_ids(p["seed"], 0, 64, p["vocab"])
+
+    def run(ev=None):
+        m.kv_rollback(-1)
+        if ev:
+            ev[0].record(stream)
+        m.prefill_chunk(tokens=ids, stream=sh)
+        if ev:
+            ev[1].record(stream)
+        tok = m.decode_step(1, stream=sh)
+        for _ in range(15):
+            tok = m.decode_step(tok, stream=sh)
+        if ev:
+            ev[2].record(stream)
+
+    for _ in range(3):
+        run()
+    reps = max(10, args.steps)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(reps)]
+    for i in range(reps):
+        run(evs[i])
+    torch.cuda.synchronize()
+    m.close()
+    return {
+        "c1_prefill_ms": round(statistics.median(e[0].elapsed_time(e[1]) for e in evs), 4),
+        "c1_decode_ms_per_step": round(statistics.median(e[1].elapsed_time(e[2]) / 16
+                                                         for e in evs), 4),
+    }
+
+
+def measured_peaks():
+    """This box's measured ceilings beside the published ones: a 1 GiB device-to-device
+    copy (read + write bytes) and a register-only bf16 MFMA loop."""
+    import torch
+
+    import kv_cached_gqa_decoder_amd as vla
+
+    stream = torch.cuda.current_stream()
+    a = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    a.fill_(1.0)
+    b.copy_(a)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(5):
+        b.copy_(a)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    copy_gbs = 5 * 2 * a.numel() * 4 / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    # a read-only stream of the same 1 GiB (a sum: the reads dominate, one scalar out)
+    a.sum()
+    e0.record(stream)
+    for _ in range(5):
+        a.sum()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    read_gbs = 5 * a.numel() * 4 / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del a, b
+    out = torch.empty(4096, dtype=torch.float32, device="cuda")
+    tf = vla.vla_probe_mfma_peak(out, 4096, 2000, stream.cuda_stream)
+    return {"copy_gbs": round(copy_gbs, 1), "read_gbs": round(read_gbs, 1),
+            "mfma_bf16_tflops": round(tf, 1)}
 
 
 # ---------------------------------------------------------------------------
@@ -516,10 +648,25 @@ def pi0_leg(args):
 
 
 # ---------------------------------------------------------------------------
+def _vm_hwm_kib():
+    try:
+        for ln in open("/proc/self/status"):
+            if ln.startswith("VmHWM:"):
+                return int(ln.split()[1])
+    except OSError:
+        pass
+    return None
+
+
 def cpu_baseline(layers_sample: int):
-    """The oracle (fp64 numpy) on a bounded sample of the prefill: the same 1024-token
-    context and 256-token chunk, through the first `layers_sample` of the 28 layers, then
-    the output head on the last row; scaled per layer to 28 layers for tokens/s."""
+    """The oracle (fp64 numpy) on the host cores, per phase, on bounded samples of the
+    same workloads: the Qwen2.5-1.5B-shaped 256-token chunk prefill over the 1024-token
+    context through the first `layers_sample` of the 28 layers plus the output head (the
+    reported value, scaled per layer to 28 layers), two decode steps after it, one
+    scoring cycle over 128 clustered frames, and the fp32 tiny decoder's prompt and
+    decode steps; the scoring cycle and the tiny decoder also on one thread. The BLAS
+    thread count is set to the cores this process may run on; peak host memory is
+    VmHWM."""
     import numpy as np
 
     import synth
@@ -529,24 +676,25 @@ def cpu_baseline(layers_sample: int):
     if not rng.have_c():
         from oracle import build as ob
         ob.build()
+    cores = len(os.sched_getaffinity(0))
     try:
         import threadpoolctl
-        threads = max(i["num_threads"] for i in threadpoolctl.threadpool_info()
-                      if i.get("user_api") == "blas")
-    except Exception:
-        threads = len(os.sched_getaffinity(0))
+        limit = threadpoolctl.threadpool_limits
+    except Exception:            # no control over the BLAS threads: report the default
+        limit = None
+    ctx = limit(cores) if limit else None
+    log(f"[bench] cpu baseline: oracle, {layers_sample} of {L} layers, {cores} cores")
     cfg = D_.C2.with_(n_layers=layers_sample)
-    log(f"[bench] cpu baseline: oracle, {layers_sample} of {L} layers, {threads} BLAS threads")
     sess = D_.Session(cfg)
     for c in range(CONTEXT // CHUNK):
         sess.prefill_chunk(tokens=synth.token_ids(cfg.seed, c, CHUNK, V))
     x32, _ = synth.embeddings(cfg.seed, 0, CHUNK, H, "bf16")
     ctx_fid = sess.frames()[-1].frame_id
     runs = []
-    for _ in range(5):
+    for _ in range(3):
         sess.rollback(ctx_fid)
         t0 = time.perf_counter()
-        sess.prefill_chunk(embeds=x32)
+        _, ref = sess.prefill_chunk(embeds=x32)
         runs.append(time.perf_counter() - t0)
     t_all = statistics.median(runs)
     h = np.asarray(x32[-1], dtype=np.float64)
@@ -555,14 +703,74 @@ def cpu_baseline(layers_sample: int):
     t_head = time.perf_counter() - t0
     per_layer = (t_all - t_head) / layers_sample
     est = per_layer * L + t_head
+    dec = []
+    tok = int(np.argmax(ref))
+    for _ in range(2):
+        t0 = time.perf_counter()
+        tok, _ = sess.decode_step(tok)
+        dec.append(time.perf_counter() - t0)
+    # per-layer part scaled to 28 layers, the output head once
+    dec_ms = ((statistics.median(dec) - t_head) / layers_sample * L + t_head) * 1e3
+    del sess
+
+    def scoring_cycle():
+        c3 = D_.C3.with_(n_layers=1)
+        s3 = D_.Session(c3)
+        for f in range(128):
+            (k32, v32), _ = synth.clustered_frame(c3.seed, f, 1, 64, HKV, D)
+            s3.append_raw(k32, v32)
+        t = []
+        for _ in range(3):
+            t0 = time.perf_counter()
+            s3.score(0)
+            t.append(time.perf_counter() - t0)
+        return statistics.median(t) * 1e3
+
+    w1 = D_.Weights(D_.C1)
+    ids1 = synth.token_ids(D_.C1.seed, 0, 64, D_.C1.vocab)
+    D_.Session(D_.C1, w1).prefill_chunk(tokens=ids1)     # generates the weights (untimed)
+
+    def tiny():
+        s1 = D_.Session(D_.C1, w1)
+        ids = ids1
+        t0 = time.perf_counter()
+        _, r = s1.prefill_chunk(tokens=ids)
+        tp = time.perf_counter() - t0
+        tok1 = int(np.argmax(r))
+        t0 = time.perf_counter()
+        for _ in range(16):
+            tok1, _ = s1.decode_step(tok1)
+        return tp * 1e3, (time.perf_counter() - t0) / 16 * 1e3
+
+    score_ms = scoring_cycle()
+    c1_pre, c1_dec = tiny()
+    if ctx is not None:
+        ctx.restore_original_limits()
+    one = limit(1) if limit else None
+    score_ms_1t = scoring_cycle()
+    c1_pre_1t, c1_dec_1t = tiny()
+    if one is not None:
+        one.restore_original_limits()
     return {
         "value": round(CHUNK / est, 3),
         "unit": "tok/s",
-        "cores": threads,
+        "cores": cores,
         "kind": "oracle",
         "sample": f"256-token chunk prefill over a 1024-token cached context through "
-                  f"{layers_sample} of {L} layers plus the output head (median of 5: "
+                  f"{layers_sample} of {L} layers plus the output head (median of 3: "
                   f"{t_all:.2f} s); scaled per layer to {L} layers: est. {est:.2f} s",
+        "phases_ms": {
+            "qwen_prefill_256": round(est * 1e3, 1),
+            "qwen_decode_step": round(dec_ms, 1),
+            "scoring_cycle_128_frames": round(score_ms, 2),
+            "scoring_cycle_128_frames_1_thread": round(score_ms_1t, 2),
+            "tiny_f32_prefill_64": round(c1_pre, 2),
+            "tiny_f32_decode_step": round(c1_dec, 2),
+            "tiny_f32_prefill_64_1_thread": round(c1_pre_1t, 2),
+            "tiny_f32_decode_step_1_thread": round(c1_dec_1t, 2),
+        },
+        "host_peak_rss_mib": round(_vm_hwm_kib() / 1024, 1) if _vm_hwm_kib() else None,
+        "blas_threads": cores if limit else "default",
     }
 
 

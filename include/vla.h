@@ -170,6 +170,35 @@ vla_status vla_kv_score_and_evict(vla_model* m, int32_t layer, int32_t* out_fram
 vla_status vla_kv_score(vla_model* m, int32_t layer, int32_t* out_frame_id, double* out_score,
                         void* stream);
 
+/* Eviction policies ("Can an LLM Forget the Right Things?", section 5):
+ *  VLA_EVICT_SEMANTIC  the all-pairs redundancy scoring of vla_kv_score_and_evict;
+ *  VLA_EVICT_FIFO      the oldest resident frame (the page's FIFO baseline; score 0);
+ *  VLA_EVICT_ADJACENT  the page's own semantic rule: the cosine of each frame's mean
+ *                      key with the next frame's (arrival order), and the older frame
+ *                      of the most similar pair (the first pair on ties); the score is
+ *                      that pair's cosine, the same fp64 value the all-pairs scoring
+ *                      gives the pair.
+ * A sliding window of W frames is FIFO with vla_kv_make_room's window W (with frames
+ * of one size the two evict the same frames, as the page notes). */
+typedef enum { VLA_EVICT_SEMANTIC = 0, VLA_EVICT_FIFO = 1, VLA_EVICT_ADJACENT = 2 } vla_evict_policy;
+
+/* Evict one frame chosen by `policy` on mean keys of `layer`; writes its frame id and
+ * score (host, nullable). Synchronises the stream (FIFO: no device work). Errors:
+ * VLA_E_INVALID (policy, layer), VLA_E_NOTHING_TO_EVICT (no frame; fewer than two for
+ * the scoring policies). */
+vla_status vla_kv_evict(vla_model* m, int32_t policy, int32_t layer, int32_t* out_frame_id,
+                        double* out_score, void* stream);
+
+/* Evict frames chosen by `policy` until a frame of n_tokens fits (its blocks and a frame
+ * slot are free) and, when window > 0, fewer than `window` frames are resident (at most
+ * `window` frames after the insert): the page's evict-until-room loop. With one frame
+ * left every policy takes it. Writes the number of frames evicted (host, nullable).
+ * Errors: VLA_E_INVALID (policy, layer, n_tokens outside 1..max_chunk, window < 0),
+ * VLA_E_NO_BLOCKS (evicting every frame would not free enough blocks; nothing is
+ * evicted). */
+vla_status vla_kv_make_room(vla_model* m, int32_t policy, int32_t layer, int32_t n_tokens,
+                            int32_t window, int32_t* out_evicted, void* stream);
+
 /* For callers that cannot allocate device memory (code under HIP graph capture,
  * serving loops, harnesses that forbid allocation): the scoring of
  * vla_kv_score on a caller-given mean-key table, with no handle and no
@@ -287,6 +316,15 @@ vla_status vla_profile_read(vla_model* m, double* total_ms, int32_t* launches);
  * Errors: VLA_E_INVALID (other class, reps outside 1..1000, no gated layer). */
 vla_status vla_profile_replay(vla_model* m, int32_t kernel_class, int32_t reps, void* stream,
                               double* ms_per_launch);
+
+/* Matrix-core throughput probe (a measured peak beside the published one): launches
+ * `blocks` workgroups of 4 wavefronts, each wavefront running iters x 8 independent
+ * v_mfma_f32_16x16x32_bf16 (16384 FLOP each) on register operands, times it with
+ * stream events and writes the achieved bf16 TFLOP/s. `out`: device float[blocks]
+ * (one kept value per workgroup). Synchronises the stream. Errors: VLA_E_INVALID
+ * (null pointers, blocks outside 1..65536, iters outside 1..1000000). */
+vla_status vla_probe_mfma_peak(float* out, int32_t blocks, int32_t iters, void* stream,
+                               double* out_tflops);
 
 /* Action expert of a pi0-style policy ("Running VLAs at Real-time Speed",
  * section 2: a vision-language prefix model plus an expert that predicts an

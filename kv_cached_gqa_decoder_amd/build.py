@@ -32,6 +32,10 @@ def _flags():
             "-Wall", "-Werror=uninitialized", "-Werror=shadow",
             # packed fp32 instructions are kept out of every kernel
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+            # matrix-core accumulators in ordinary VGPRs: with the accumulation registers
+            # the compiler rotated GEMM and attention accumulators through copies every
+            # loop iteration (e.g. 24 moves per 8 MFMAs in the split-K GEMM step)
+            "-mllvm", "-amdgpu-mfma-vgpr-form",
             "-I", os.path.join(HERE, "..", "include")]
 
 

@@ -201,31 +201,40 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_kernel(GemmArgs a, i
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     issue(kt + NS - 1);
     const unsigned char* st = smem + (kt % NS) * G::STAGE;
+    // all operand fragments of the step first, then each accumulator's MFMAs back to
+    // back (sub-step 0 high, low, sub-step 1 ...): one update chain per accumulator
+    // and step, so the compiler keeps every accumulator in place (two separate passes
+    // over the accumulators made it rotate them through other registers every step)
+    constexpr int KS = BK / 32;
+    bf16x8_t bf[KS][NT], af[KS][MT], al[KS][LO ? MT : 1];
 #pragma unroll
-    for (int ks = 0; ks < BK / 32; ++ks) {
+    for (int ks = 0; ks < KS; ++ks) {
       const int kc = ks * 4 + (lane >> 4);
-      bf16x8_t bf[NT];
 #pragma unroll
       for (int ni = 0; ni < NT; ++ni) {
         const int r = G::AROWS + wn * G::WN + ni * 16 + (lane & 15);
-        bf[ni] = *(const bf16x8_t*)(st + r * G::ROWB + (G::pos(r, kc) << 4));
+        bf[ks][ni] = *(const bf16x8_t*)(st + r * G::ROWB + (G::pos(r, kc) << 4));
       }
 #pragma unroll
       for (int mi = 0; mi < MT; ++mi) {
         const int r = wm * G::WM + mi * 16 + (lane & 15);
-        const bf16x8_t af = *(const bf16x8_t*)(st + r * G::ROWB + (G::pos(r, kc) << 4));
-#pragma unroll
-        for (int ni = 0; ni < NT; ++ni)
-          acc[mi][ni] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bf[ni], acc[mi][ni], 0, 0, 0);
+        af[ks][mi] = *(const bf16x8_t*)(st + r * G::ROWB + (G::pos(r, kc) << 4));
         if constexpr (LO) {
           const int rl = BM + r;
-          const bf16x8_t al = *(const bf16x8_t*)(st + rl * G::ROWB + (G::pos(rl, kc) << 4));
-#pragma unroll
-          for (int ni = 0; ni < NT; ++ni)
-            acc[mi][ni] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bf[ni], acc[mi][ni], 0, 0, 0);
+          al[ks][mi] = *(const bf16x8_t*)(st + rl * G::ROWB + (G::pos(rl, kc) << 4));
         }
       }
     }
+#pragma unroll
+    for (int mi = 0; mi < MT; ++mi)
+#pragma unroll
+      for (int ni = 0; ni < NT; ++ni)
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          acc[mi][ni] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[ks][mi], bf[ks][ni], acc[mi][ni], 0, 0, 0);
+          if constexpr (LO)
+            acc[mi][ni] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al[ks][mi], bf[ks][ni], acc[mi][ni], 0, 0, 0);
+        }
   }
 
   gemm_epilogue<EPI, MT, NT, G::WM, G::WN>(a, acc, m0, n0, z, wm, wn, lane);

@@ -159,6 +159,9 @@ hipError_t launch_weight_logical(const void* phys, void* out, int dt, int layout
                                  int64_t rows, int64_t cols, int hq, int hkv, int d,
                                  hipStream_t s);
 hipError_t launch_fill_f32(float* p, float v, int64_t n, hipStream_t s);
+// matrix-core throughput probe: `blocks` workgroups of 4 wavefronts, each wavefront
+// iters x 8 bf16 MFMAs of 16384 FLOP; out[blocks] receives one value per workgroup
+hipError_t launch_mfma_peak(float* out, int blocks, int iters, hipStream_t s);
 // (cos, sin) of pos * inv_freq[j] for rows t = 0..n-1 at positions pos0 + t: the
 // angle is formed in fp64 and reduced to [-pi, pi] in fp64, then fp32 sin/cos
 hipError_t launch_rope_table(int64_t pos0, int n, const double* inv_freq, int half,
@@ -203,6 +206,10 @@ hipError_t launch_meankeys(const void* kpool, KvGeom g, const int* blk_table,
                            double* table, int max_frames, int dt, hipStream_t s);
 hipError_t launch_score(const double* table_layer, const int* fr_slot, int nframes, int D,
                         double* m_out, double* result, hipStream_t s);
+// adjacent-pair scoring: s[i] = cos(frame i, frame i + 1), then the argmax over the
+// nframes - 1 pairs (ties to the first pair) into result[0] (pair index), result[1]
+hipError_t launch_score_adjacent(const double* table_layer, const int* fr_slot, int nframes, int D,
+                                 double* s_out, double* result, hipStream_t s);
 // scoring of a dense fp64 table [nframes][D] (rows in frame order) with the
 // per-frame scores in a library-owned static device array (no allocation);
 // writes the winner's row index and score to device memory

@@ -233,6 +233,33 @@ hipError_t launch_fill_f32(float* p, float v, int64_t n, hipStream_t s) {
 }
 
 // ---------------------------------------------------------------------------
+// Matrix-core throughput probe: every wavefront runs `iters` rounds of 8
+// independent v_mfma_f32_16x16x32_bf16 chains on register operands (no memory
+// traffic in the loop); one value per workgroup is stored so the work is kept.
+// 16384 FLOP per instruction.
+__global__ __launch_bounds__(256) void mfma_peak_kernel(float* out, int iters) {
+  // eight chains with distinct B operands and start values, so none can be merged
+  bf16x8_t a, b[8];
+  f32x4_t acc[8];
+  for (int i = 0; i < 8; ++i) a[i] = (__bf16)(0.001f * (float)((threadIdx.x + i) & 7));
+  for (int j = 0; j < 8; ++j) {
+    for (int i = 0; i < 8; ++i) b[j][i] = (__bf16)(0.002f * (float)((threadIdx.x * 3 + i + j) & 7));
+    acc[j] = f32x4_t{(float)j, 0.f, 0.f, 0.f};
+  }
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b[j], acc[j], 0, 0, 0);
+  }
+  float t = 0.f;
+  for (int j = 0; j < 8; ++j) t += acc[j][0] + acc[j][1] + acc[j][2] + acc[j][3];
+  if (threadIdx.x == 0) out[blockIdx.x] = t;
+}
+hipError_t launch_mfma_peak(float* out, int blocks, int iters, hipStream_t s) {
+  mfma_peak_kernel<<<blocks, 256, 0, s>>>(out, iters);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
 // embedding rows (activation type) -> fp32 residual rows; block 0 also clears
 // the argmax cell of this pass
 template <typename T>

@@ -845,39 +845,70 @@ vla_status vla_decode_step(vla_model* m, int32_t token, int32_t* out_next_token,
   });
 }
 
+// the resident frame (index in arrival order) that `policy` evicts next, and its
+// score; synchronises the stream when the choice is made on the device
+static int pick_frame(vla_model* m, int policy, int layer, hipStream_t st, double* score) {
+  const int F = n_frames(m);
+  if (policy == VLA_EVICT_FIFO) {
+    if (F < 1) raise(VLA_E_NOTHING_TO_EVICT, "no frame resident");
+    *score = 0.0;
+    return 0;
+  }
+  if (F < 2) raise(VLA_E_NOTHING_TO_EVICT, "fewer than 2 frames resident");
+  sync_meta(m, st);
+  const int D = m->cfg.n_kv_heads * m->cfg.head_dim;
+  const double* tab = m->meankeys + (size_t)layer * m->cfg.max_frames * D;
+  if (policy == VLA_EVICT_ADJACENT)
+    LAUNCH(m, VLA_K_SCORE, st, launch_score_adjacent(tab, m->d_fr_slot(), F, D, m->d_score_m,
+                                                     m->d_score_res, st));
+  else
+    LAUNCH(m, VLA_K_SCORE, st, launch_score(tab, m->d_fr_slot(), F, D, m->d_score_m,
+                                            m->d_score_res, st));
+  double* h = (double*)staging_acquire(m->st_read);
+  HIPCHK(hipMemcpyAsync(h, m->d_score_res, 2 * sizeof(double), hipMemcpyDeviceToHost, st));
+  HIPCHK(hipStreamSynchronize(st));
+  const int idx = (int)h[0];
+  *score = h[1];
+  // adjacent: pair i's older frame is frame i
+  if (idx < 0 || idx >= F) raise(VLA_E_STATE, "scoring returned an invalid index");
+  return idx;
+}
+
+// segment index of the idx-th resident frame (arrival order)
+static size_t frame_seg(const vla_model* m, int idx) {
+  size_t si = 0;
+  for (int f = -1; si < m->segs.size(); ++si)
+    if (m->segs[si].frame && ++f == idx) break;
+  return si;
+}
+
+// evict the idx-th resident frame: its blocks go onto the free-list in logical order
+static int evict_frame_index(vla_model* m, int idx) {
+  const size_t si = frame_seg(m, idx);
+  Segment s = m->segs[si];
+  if (!m->pool.release(s.blocks.data(), (int)s.blocks.size()))
+    raise(VLA_E_STATE, "block bookkeeping corrupted");
+  m->free_slots.push_back(s.slot);
+  m->segs.erase(m->segs.begin() + si);
+  m->meta_dirty = true;
+  return s.frame_id;
+}
+
+static void check_policy_layer(const vla_model* m, int policy, int layer) {
+  if (policy != VLA_EVICT_SEMANTIC && policy != VLA_EVICT_FIFO && policy != VLA_EVICT_ADJACENT)
+    raise(VLA_E_INVALID, "unknown eviction policy");
+  if (layer < 0 || layer >= m->cfg.n_layers) raise(VLA_E_INVALID, "layer out of range");
+}
+
 static vla_status score_impl(vla_model* m, int32_t layer, int32_t* out_frame_id, double* out_score,
                              void* stream, bool evict) {
   return guarded([&] {
     if (!m) raise(VLA_E_INVALID, "null model");
-    if (layer < 0 || layer >= m->cfg.n_layers) raise(VLA_E_INVALID, "layer out of range");
-    const int F = n_frames(m);
-    if (F < 2) raise(VLA_E_NOTHING_TO_EVICT, "fewer than 2 frames resident");
+    check_policy_layer(m, VLA_EVICT_SEMANTIC, layer);
     HIPCHK(hipSetDevice(m->dev));
-    const hipStream_t st = (hipStream_t)stream;
-    sync_meta(m, st);
-    const int D = m->cfg.n_kv_heads * m->cfg.head_dim;
-    const double* tab = m->meankeys + (size_t)layer * m->cfg.max_frames * D;
-    LAUNCH(m, VLA_K_SCORE, st, launch_score(tab, m->d_fr_slot(), F, D, m->d_score_m,
-                                            m->d_score_res, st));
-    double* h = (double*)staging_acquire(m->st_read);
-    HIPCHK(hipMemcpyAsync(h, m->d_score_res, 2 * sizeof(double), hipMemcpyDeviceToHost, st));
-    HIPCHK(hipStreamSynchronize(st));
-    const int idx = (int)h[0];
-    const double score = h[1];
-    if (idx < 0 || idx >= F) raise(VLA_E_STATE, "scoring returned an invalid index");
-    // idx-th resident frame in arrival order
-    size_t si = 0;
-    for (int f = -1; si < m->segs.size(); ++si)
-      if (m->segs[si].frame && ++f == idx) break;
-    const int fid = m->segs[si].frame_id;
-    if (evict) {
-      Segment s = m->segs[si];
-      if (!m->pool.release(s.blocks.data(), (int)s.blocks.size()))
-        raise(VLA_E_STATE, "block bookkeeping corrupted");
-      m->free_slots.push_back(s.slot);
-      m->segs.erase(m->segs.begin() + si);
-      m->meta_dirty = true;
-    }
+    double score = 0.0;
+    const int idx = pick_frame(m, VLA_EVICT_SEMANTIC, layer, (hipStream_t)stream, &score);
+    const int fid = evict ? evict_frame_index(m, idx) : m->segs[frame_seg(m, idx)].frame_id;
     if (out_frame_id) *out_frame_id = fid;
     if (out_score) *out_score = score;
   });
@@ -891,6 +922,50 @@ vla_status vla_kv_score_and_evict(vla_model* m, int32_t layer, int32_t* out_fram
 vla_status vla_kv_score(vla_model* m, int32_t layer, int32_t* out_frame_id, double* out_score,
                         void* stream) {
   return score_impl(m, layer, out_frame_id, out_score, stream, false);
+}
+
+vla_status vla_kv_evict(vla_model* m, int32_t policy, int32_t layer, int32_t* out_frame_id,
+                        double* out_score, void* stream) {
+  return guarded([&] {
+    if (!m) raise(VLA_E_INVALID, "null model");
+    check_policy_layer(m, policy, layer);
+    HIPCHK(hipSetDevice(m->dev));
+    double score = 0.0;
+    const int idx = pick_frame(m, policy, layer, (hipStream_t)stream, &score);
+    const int fid = evict_frame_index(m, idx);
+    if (out_frame_id) *out_frame_id = fid;
+    if (out_score) *out_score = score;
+  });
+}
+
+vla_status vla_kv_make_room(vla_model* m, int32_t policy, int32_t layer, int32_t n_tokens,
+                            int32_t window, int32_t* out_evicted, void* stream) {
+  return guarded([&] {
+    if (!m) raise(VLA_E_INVALID, "null model");
+    check_policy_layer(m, policy, layer);
+    if (n_tokens < 1 || n_tokens > m->cfg.max_chunk) raise(VLA_E_INVALID, "n_tokens out of range");
+    if (window < 0) raise(VLA_E_INVALID, "window must be >= 0");
+    HIPCHK(hipSetDevice(m->dev));
+    const int need = (n_tokens + bt_of(m) - 1) / bt_of(m);
+    int evictable = 0;
+    for (const auto& sg : m->segs)
+      if (sg.frame) evictable += (int)sg.blocks.size();
+    if (need > m->pool.free_count() + evictable)
+      raise(VLA_E_NO_BLOCKS, "need " + std::to_string(need) + " blocks; evicting every frame frees " +
+                                 std::to_string(evictable) + " of them");
+    int n = 0;
+    for (;;) {
+      const int F = n_frames(m);
+      const bool room = m->pool.free_count() >= need && F < m->cfg.max_frames &&
+                        (window == 0 || F < window);
+      if (room) break;
+      double score = 0.0;
+      const int idx = F == 1 ? 0 : pick_frame(m, policy, layer, (hipStream_t)stream, &score);
+      evict_frame_index(m, idx);
+      ++n;
+    }
+    if (out_evicted) *out_evicted = n;
+  });
 }
 
 vla_status vla_kv_score_noalloc(const double* mean_keys, int32_t n_frames, int32_t dim,
@@ -1159,6 +1234,30 @@ vla_status vla_profile_replay(vla_model* m, int32_t kernel_class, int32_t reps, 
     HIPCHK(hipEventDestroy(e0));
     HIPCHK(hipEventDestroy(e1));
     if (ms_per_launch) *ms_per_launch = (double)ms / ((double)reps * nl);
+  });
+}
+
+vla_status vla_probe_mfma_peak(float* out, int32_t blocks, int32_t iters, void* stream,
+                               double* out_tflops) {
+  return guarded([&] {
+    if (!out || !out_tflops) raise(VLA_E_INVALID, "null argument");
+    if (blocks < 1 || blocks > 65536 || iters < 1 || iters > 1000000)
+      raise(VLA_E_INVALID, "blocks in 1..65536, iters in 1..1000000");
+    const hipStream_t st = (hipStream_t)stream;
+    HIPCHK(launch_mfma_peak(out, blocks, 1, st));  // warm-up
+    hipEvent_t e0, e1;
+    HIPCHK(hipEventCreate(&e0));
+    HIPCHK(hipEventCreate(&e1));
+    HIPCHK(hipEventRecord(e0, st));
+    HIPCHK(launch_mfma_peak(out, blocks, iters, st));
+    HIPCHK(hipEventRecord(e1, st));
+    HIPCHK(hipEventSynchronize(e1));
+    float ms = 0.f;
+    HIPCHK(hipEventElapsedTime(&ms, e0, e1));
+    HIPCHK(hipEventDestroy(e0));
+    HIPCHK(hipEventDestroy(e1));
+    const double flop = (double)blocks * 4.0 * (double)iters * 8.0 * 16384.0;
+    *out_tflops = flop / ((double)ms * 1e-3) / 1e12;
   });
 }
 

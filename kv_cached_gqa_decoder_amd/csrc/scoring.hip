@@ -265,6 +265,43 @@ __global__ __launch_bounds__(256) void score_argmax_kernel(const double* m, int 
   }
 }
 
+// Adjacent pairs, the page's own rule ("Can an LLM Forget the Right Things?",
+// section 5: compare each retained frame with the next one and evict the older frame
+// of the most similar pair): s_i = cos(frame i, frame i + 1) in arrival order. The
+// sums have the all-pairs kernel's fixed shape (lane k adds dims k, k+64, ... by fma,
+// then the xor tree; |lo|^2 from frame i), so s_i equals that kernel's value of the
+// pair bit for bit. One wavefront per pair.
+__global__ __launch_bounds__(64) void score_adjacent_kernel(const double* tab, const int* fr_slot,
+                                                            int D, double* s_out) {
+  const int i = blockIdx.x, lane = threadIdx.x;
+  const double* a = tab + (size_t)fr_slot[i] * D;
+  const double* b = tab + (size_t)fr_slot[i + 1] * D;
+  double ab = 0.0, aa = 0.0, bb = 0.0;
+  for (int k = lane; k < D; k += 64) {
+    const double x = a[k], y = b[k];
+    ab = fma(x, y, ab);
+    aa = fma(x, x, aa);
+    bb = fma(y, y, bb);
+  }
+  ab = wave_sum_d(ab);
+  aa = wave_sum_d(aa);
+  bb = wave_sum_d(bb);
+  if (lane == 0) {
+    const double den = sqrt(aa) * sqrt(bb);
+    s_out[i] = den < 1e-8 ? 0.0 : ab / den;
+  }
+}
+
+hipError_t launch_score_adjacent(const double* table_layer, const int* fr_slot, int nframes, int D,
+                                 double* s_out, double* result, hipStream_t s) {
+  if (nframes < 2) return hipErrorInvalidValue;
+  launch_k(score_adjacent_kernel, dim3(nframes - 1), dim3(64), 0, s, table_layer, fr_slot, D,
+           s_out);
+  launch_k(score_argmax_kernel, dim3(1), dim3(256), 0, s, (const double*)s_out, nframes - 1, result,
+           (int*)nullptr, (double*)nullptr);
+  return hipGetLastError();
+}
+
 hipError_t launch_score(const double* table_layer, const int* fr_slot, int nframes, int D,
                         double* m_out, double* result, hipStream_t s) {
   if (nframes < 2) return hipErrorInvalidValue;

@@ -20,6 +20,9 @@ VLA_OK, VLA_E_INVALID, VLA_E_NO_BLOCKS, VLA_E_NOTHING_TO_EVICT, VLA_E_HIP, VLA_E
 VLA_F32, VLA_BF16, VLA_INT4_G128 = 0, 1, 2
 VLA_SWIGLU, VLA_GEGLU = 0, 1
 VLA_TOKEN_DEVICE = -1   # decode input: the previous forward's greedy token, on the device
+VLA_EVICT_SEMANTIC, VLA_EVICT_FIFO, VLA_EVICT_ADJACENT = 0, 1, 2
+EVICT_POLICIES = {"semantic": VLA_EVICT_SEMANTIC, "fifo": VLA_EVICT_FIFO,
+                  "adjacent": VLA_EVICT_ADJACENT}
 
 # kernel classes for vla_profile_enable
 K_CLASSES = {
@@ -74,6 +77,10 @@ _SIGS = {
     "vla_kv_score_and_evict": (c_int32, [c_void_p, c_int32, POINTER(c_int32), POINTER(c_double),
                                          c_void_p]),
     "vla_kv_score": (c_int32, [c_void_p, c_int32, POINTER(c_int32), POINTER(c_double), c_void_p]),
+    "vla_kv_evict": (c_int32, [c_void_p, c_int32, c_int32, POINTER(c_int32), POINTER(c_double),
+                               c_void_p]),
+    "vla_kv_make_room": (c_int32, [c_void_p, c_int32, c_int32, c_int32, c_int32, POINTER(c_int32),
+                                   c_void_p]),
     "vla_logits_out": (c_int32, [c_void_p, c_void_p, c_int32, c_void_p]),
     "vla_kv_score_noalloc": (c_int32, [c_void_p, c_int32, c_int32, c_void_p, c_void_p, c_void_p]),
     "vla_last_error": (ctypes.c_char_p, []),
@@ -94,6 +101,7 @@ _SIGS = {
     "vla_profile_enable": (c_int32, [c_void_p, c_int32]),
     "vla_profile_read": (c_int32, [c_void_p, POINTER(c_double), POINTER(c_int32)]),
     "vla_profile_replay": (c_int32, [c_void_p, c_int32, c_int32, c_void_p, POINTER(c_double)]),
+    "vla_probe_mfma_peak": (c_int32, [c_void_p, c_int32, c_int32, c_void_p, POINTER(c_double)]),
     "vla_expert_create": (c_int32, [c_void_p, POINTER(vla_config), c_int32, POINTER(c_void_p)]),
     "vla_expert_destroy": (None, [c_void_p]),
     "vla_expert_denoise": (c_int32, [c_void_p, c_void_p, c_int32, c_double, c_void_p]),
@@ -195,6 +203,19 @@ def vla_kv_score(m: int, layer: int = 0, stream=None):
     fid, sc = c_int32(-1), c_double(0.0)
     _check(load().vla_kv_score(m, layer, byref(fid), byref(sc), _stream(stream)))
     return fid.value, sc.value
+
+
+def vla_kv_evict(m: int, policy: int, layer: int = 0, stream=None):
+    fid, sc = c_int32(-1), c_double(0.0)
+    _check(load().vla_kv_evict(m, policy, layer, byref(fid), byref(sc), _stream(stream)))
+    return fid.value, sc.value
+
+
+def vla_kv_make_room(m: int, policy: int, layer: int, n_tokens: int, window: int = 0,
+                     stream=None) -> int:
+    n = c_int32(0)
+    _check(load().vla_kv_make_room(m, policy, layer, n_tokens, window, byref(n), _stream(stream)))
+    return n.value
 
 
 def vla_kv_score_noalloc(mean_keys, n_frames: int, dim: int, out_index, out_score,
@@ -304,6 +325,13 @@ def vla_profile_replay(m: int, kernel_class: int, reps: int, stream=None) -> flo
     ms = c_double(0.0)
     _check(load().vla_profile_replay(m, kernel_class, reps, _stream(stream), byref(ms)))
     return ms.value
+
+
+def vla_probe_mfma_peak(out, blocks: int, iters: int, stream=None) -> float:
+    """Achieved bf16 MFMA TFLOP/s of a register-only MFMA loop (out: device float[blocks])."""
+    t = c_double(0.0)
+    _check(load().vla_probe_mfma_peak(_ptr(out), blocks, iters, _stream(stream), byref(t)))
+    return t.value
 
 
 def vla_expert_create(prefix: int, cfg: vla_config, n_actions: int) -> int:
@@ -492,6 +520,13 @@ class Model:
 
     def kv_score(self, layer=0, stream=None):
         return vla_kv_score(self.h, layer, stream)
+
+    def kv_evict(self, policy, layer=0, stream=None):
+        return vla_kv_evict(self.h, EVICT_POLICIES.get(policy, policy), layer, stream)
+
+    def kv_make_room(self, policy, n_tokens, window=0, layer=0, stream=None):
+        return vla_kv_make_room(self.h, EVICT_POLICIES.get(policy, policy), layer, n_tokens,
+                                window, stream)
 
     def logits_out(self, out, stream=None):
         vla_logits_out(self.h, out, self.cfg.vocab, stream)

@@ -513,6 +513,54 @@ class Session:
         self.evict(fid)
         return fid, score
 
+    # -- baseline eviction policies ("Can an LLM Forget the Right Things?", section 5) --
+    def pick(self, policy: str, layer: int = 0):
+        """The frame a policy evicts next and its score: (frame id, score).
+
+        semantic: the all-pairs redundancy winner (``score``);
+        fifo:     the oldest resident frame (score 0);
+        adjacent: the older frame of the most similar pair of frames adjacent in
+                  arrival order (strict greater-than keeps the first pair on ties),
+                  scored by that pair's cosine.
+        """
+        from .scoring import adjacent_pair_pick, cosine
+        frames = self.frames()
+        if not frames:
+            raise NothingToEvict("no frame resident")
+        if policy == "fifo":
+            return frames[0].frame_id, 0.0
+        if policy == "semantic":
+            fid, score, _ = self.score(layer)
+            return fid, score
+        if policy == "adjacent":
+            mk = self.mean_keys(layer)
+            if len(mk) < 2:
+                raise NothingToEvict("fewer than 2 frames")
+            vecs = np.stack([v for _, v in mk])
+            i = adjacent_pair_pick(vecs)
+            return mk[i][0], cosine(vecs[i], vecs[i + 1])
+        raise ValueError(policy)
+
+    def make_room(self, policy: str, n_tokens: int, window: int = 0, layer: int = 0):
+        """Evict frames chosen by ``policy`` until a frame of n_tokens fits (its blocks and
+        a frame slot are free) and, with window > 0, fewer than ``window`` frames are
+        resident (a sliding window of at most ``window`` frames after the insert). With
+        one frame left every policy takes it. Returns the evicted frame ids; raises
+        NoBlocks (state unchanged) when even an empty cache would not make room."""
+        bt = self.cfg.block_tokens
+        need = -(-n_tokens // bt)
+        evictable = sum(len(s.blocks) for s in self.frames())
+        if need > len(self.pool.free) + evictable:
+            raise NoBlocks(f"need {need} blocks, at most {len(self.pool.free) + evictable}")
+        out = []
+        while (len(self.pool.free) < need or len(self.frames()) >= self.cfg.max_frames
+               or (window > 0 and len(self.frames()) >= window)):
+            frames = self.frames()
+            fid = frames[0].frame_id if len(frames) == 1 else self.pick(policy, layer)[0]
+            self.evict(fid)
+            out.append(fid)
+        return out
+
     def rollback(self, keep_frame_id: int) -> None:
         """Drop every segment created after frame ``keep_frame_id`` (newest first).
 
