@@ -200,6 +200,24 @@ def gpu_leg(args):
         e1.record(stream)
         torch.cuda.synchronize()
         chained.append(e0.elapsed_time(e1) / DECODES)
+    # the same greedy decodes as one persistent launch per step (phases separated by
+    # device-scope barriers), and the latency of such a barrier alone
+    m.set_option(vla.VLA_OPT_PERSISTENT_DECODE, 1)
+    pers = []
+    for _ in range(3):
+        m.kv_rollback(ctx_fid)
+        m.prefill_chunk(embeds=chunk, n=CHUNK, stream=sh)
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(DECODES):
+            m.decode_step(vla.VLA_TOKEN_DEVICE, stream=sh, want_token=False)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        pers.append(e0.elapsed_time(e1) / DECODES)
+    used_persistent = m.get_option(vla.VLA_INFO_LAST_DECODE_PERSISTENT)
+    m.set_option(vla.VLA_OPT_PERSISTENT_DECODE, 0)
+    bar_us = {g: round(vla.vla_probe_barrier(g, 200, sh), 2) for g in (64, 256)}
     m.close()
     del chunk
     torch.cuda.synchronize()
@@ -274,6 +292,10 @@ def gpu_leg(args):
         },
     }
     res["phases"].update(c1)
+    res["phases"]["decode_ms_per_step_persistent_kernel"] = (round(statistics.median(pers), 4)
+                                                             if used_persistent else None)
+    res["phases"]["device_barrier_us_64_workgroups"] = bar_us[64]
+    res["phases"]["device_barrier_us_256_workgroups"] = bar_us[256]
     res["phases"]["measured_peak_copy_gbs"] = peaks["copy_gbs"]
     res["phases"]["measured_peak_read_gbs"] = peaks["read_gbs"]
     res["phases"]["measured_peak_mfma_bf16_tflops"] = peaks["mfma_bf16_tflops"]

@@ -56,7 +56,9 @@ typedef enum {
   VLA_E_NO_BLOCKS = -2,        /* not enough free KV blocks (or frame slots) */
   VLA_E_NOTHING_TO_EVICT = -3, /* fewer than two evictable frames */
   VLA_E_HIP = -4,              /* a HIP runtime call failed */
-  VLA_E_STATE = -5             /* call not valid in the current state */
+  VLA_E_STATE = -5,            /* call not valid in the current state */
+  VLA_E_TIMEOUT = -6           /* a bounded wait between the workgroups of a persistent
+                                  kernel gave up (see vla_set_option) */
 } vla_status;
 
 typedef enum { VLA_F32 = 0, VLA_BF16 = 1, VLA_INT4_G128 = 2 } vla_dtype;
@@ -287,6 +289,40 @@ vla_status vla_kv_gather(vla_model* m, int32_t layer, void* k_out, void* v_out,
  * INT4 models: kinds 1-7 and 9 are written dequantised (q * s, fp32). */
 vla_status vla_weight_out(vla_model* m, int32_t kind, int32_t layer, void* out, int64_t bytes,
                           void* stream);
+
+/* Execution options of a handle.
+ *  VLA_OPT_PERSISTENT_DECODE (default 0): run a decode step's layers as one
+ *    persistent launch when the model's shape has that kernel (bf16 weights, head
+ *    dim 128, the Qwen2.5-1.5B projection shapes and the tiny test shapes): a fixed
+ *    grid of resident workgroups walks the phases of every layer, separated by
+ *    device-scope barriers ("Running VLAs at Real-time Speed", sections 3.1 and 5.2:
+ *    the step as one unit, and the cost of synchronising many small products).
+ *    0: one launch per projection and attention. While a kernel class is profiled
+ *    (vla_profile_enable) the per-kernel launches are used.
+ *  VLA_OPT_BARRIER_SPIN_LIMIT (default 1048576): polls of a barrier wait before it
+ *    gives up (>= 0). A workgroup that gives up sets an error flag and ends, every
+ *    other one ends at its next wait, and the call that reads the step's result
+ *    returns VLA_E_TIMEOUT (a decode step with out_next_token, else the next
+ *    vla_logits_out or such decode step); the decode step is then to be rolled back.
+ *  VLA_OPT_BARRIER_TEST_UNREACHABLE (default 0; for tests): 1 gives every barrier a
+ *    target the arrival counter never reaches, so each wait runs to its spin limit.
+ *  VLA_INFO_LAST_DECODE_PERSISTENT (read only): 1 when the last decode step ran the
+ *    persistent kernel.
+ * Errors: VLA_E_INVALID (unknown key, value out of range, setting a read-only key). */
+enum {
+  VLA_OPT_PERSISTENT_DECODE = 1,
+  VLA_OPT_BARRIER_SPIN_LIMIT = 2,
+  VLA_OPT_BARRIER_TEST_UNREACHABLE = 3,
+  VLA_INFO_LAST_DECODE_PERSISTENT = 100
+};
+vla_status vla_set_option(vla_model* m, int32_t key, int64_t value);
+/* The latency of that barrier alone: nbar barriers over `grid` resident workgroups of
+ * 256 threads (cooperative launch, one store per thread per phase), timed with stream
+ * events; writes microseconds per barrier. Allocates and frees its own buffers;
+ * synchronises the stream. Errors: VLA_E_INVALID (grid beyond what can be resident,
+ * nbar outside 1..100000), VLA_E_TIMEOUT. */
+vla_status vla_probe_barrier(int32_t grid, int32_t nbar, void* stream, double* out_us);
+vla_status vla_get_option(const vla_model* m, int32_t key, int64_t* value);
 
 /* Kernel timing with HIP events. While a kernel class is enabled, every
  * kernel that a call of that class launches carries a start/stop event pair

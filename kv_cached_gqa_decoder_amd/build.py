@@ -15,7 +15,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 OUT = os.path.join(HERE, "libvla.so")
-SOURCES = ["misc.hip", "gemv.hip", "gemm.hip", "attention.hip", "scoring.hip", "runtime.cpp"]
+SOURCES = ["misc.hip", "gemv.hip", "gemm.hip", "attention.hip", "scoring.hip", "decode_step.hip",
+           "runtime.cpp"]
 ARCH = "gfx950"
 
 

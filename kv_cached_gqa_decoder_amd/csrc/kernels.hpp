@@ -144,6 +144,51 @@ struct AttnArgs {
   float scale = 1.f;
 };
 
+// One decode step in one launch: the embedding row and RoPE table, then every
+// layer's q/k/v projection, attention, output projection, gated projection and
+// down projection, each phase spread over the persistent workgroups and separated
+// from the next by a device-scope barrier. The projections and the attention take
+// their per-layer weights from wtab and their layer index from the loop; everything
+// else is in the templates below.
+struct DecodeStepArgs {
+  // first phase
+  int token = 0;                              // token id, or ...
+  const unsigned long long* token_key = nullptr;  // ... the previous argmax key (device)
+  const void* E = nullptr;
+  float* x = nullptr;
+  int H = 0;
+  int64_t pos = 0;
+  const double* inv_freq = nullptr;
+  int half = 0;
+  float2* rope = nullptr;
+  // per-layer phases (W and the layer are set per layer)
+  GemvArgs qkv, o, gu, dn;
+  AttnArgs at;
+  const void* const* wtab = nullptr;          // [L][4]: q/k/v, O, gate/up, down weights
+  int n_layers = 0;
+  int ng_qkv = 0, ng_o = 0, ng_gu = 0, ng_dn = 0;   // row groups of each projection
+  int vg_qkv = 0, vg_o = 0, vg_gu = 0, vg_dn = 0;   // their virtual workgroups
+  // barriers: a monotonic arrival counter; barrier i of this launch completes when
+  // it reaches base + (i + 1) * gridDim.x. A wait gives up after spin_limit polls
+  // (or when another workgroup gave up), sets *err and ends the workgroup.
+  unsigned long long* bar = nullptr;
+  int* err = nullptr;
+  unsigned long long base = 0;
+  int spin_limit = 0;
+};
+// shapes with a persistent decode-step kernel (chunks per lane of the q/k/v, O and
+// gated projections; rows per wavefront, chunks and K split of the down projection)
+enum DecodeShape { DSHAPE_NONE = -1, DSHAPE_C3_3_3_D1_5_4 = 0, DSHAPE_C1_2_1_D2_1_1 = 1 };
+// barriers of one launch
+inline int decode_step_barriers(int n_layers) { return 5 * n_layers; }
+// persistent workgroups of the shape's kernel (all resident at once), 0 if unknown
+int decode_step_grid(int shape);
+hipError_t launch_decode_step(const DecodeStepArgs& p, int shape, int grid, hipStream_t s);
+// nbar barriers of that kind over `grid` resident workgroups (scratch: grid * 256 floats)
+hipError_t launch_barrier_probe(unsigned long long* bar, int* err, float* scratch, int grid,
+                                int nbar, int spin_limit, hipStream_t s);
+int barrier_probe_max_grid();
+
 // ---- launches (all return the launch status) ----
 hipError_t launch_init_weight(void* out, int dt, int layout, int64_t rows, int64_t cols,
                               uint64_t seed, uint64_t sa, uint64_t sb, uint64_t sc, int hq,

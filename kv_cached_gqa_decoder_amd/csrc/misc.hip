@@ -3,6 +3,7 @@
 
 #include "common.hpp"
 #include "kernels.hpp"
+#include "rope_body.hpp"
 
 namespace vla {
 
@@ -198,17 +199,6 @@ hipError_t launch_weight_logical(const void* phys, void* out, int dt, int layout
 }
 
 // ---------------------------------------------------------------------------
-// entry p = t * half + j of the table: (cos, sin) of (pos0 + t) * inv_freq[j]
-__device__ __forceinline__ void rope_entry(int64_t p, int64_t pos0, const double* inv_freq,
-                                           int half, float2* tab) {
-  const int64_t t = p / half;
-  const int j = (int)(p % half);
-  const double ang = (double)(pos0 + t) * inv_freq[j];
-  const double red = fma(-rint(ang * 0.15915494309189535), 6.283185307179586, ang);
-  float sn, cs;
-  sincosf((float)red, &sn, &cs);
-  tab[p] = make_float2(cs, sn);
-}
 __global__ void rope_table_kernel(int64_t pos0, int n, const double* inv_freq, int half,
                                   float2* tab) {
   const int64_t total = (int64_t)n * half;
@@ -282,13 +272,7 @@ template <typename T>
 __global__ void embed_rope1_kernel(int token_scalar, const unsigned long long* token_key,
                                    const T* E, float* x, int H, int64_t pos, const double* inv_freq,
                                    int half, float2* tab) {
-  if (blockIdx.x == 0) {
-    const int64_t id = token_key ? (int64_t)(0xffffffffu - (uint32_t)(*token_key & 0xffffffffull))
-                                 : token_scalar;
-    for (int i = threadIdx.x; i < H; i += blockDim.x) x[i] = St<T>::ld(E, id * H + i);
-  } else {
-    for (int p = threadIdx.x; p < half; p += blockDim.x) rope_entry(p, pos, inv_freq, half, tab);
-  }
+  embed_rope1_body<T>(token_scalar, token_key, E, x, H, pos, inv_freq, half, tab, blockIdx.x);
 }
 hipError_t launch_embed_rope1(int token_scalar, const unsigned long long* token_key, const void* E,
                               void* x, int H, int dt, int64_t pos, const double* inv_freq, int half,

@@ -146,6 +146,18 @@ struct vla_model {
   bool meta_dirty = true;
   bool have_logits = false;
 
+  // persistent decode step
+  int ds_shape = DSHAPE_NONE;   // its kernel shape for this model, DSHAPE_NONE if none
+  int ds_grid = 0;              // resident workgroups of that kernel (0: not queried yet)
+  const void** d_wtab = nullptr;          // [L][4] weight pointers (device)
+  unsigned long long* d_bar = nullptr;    // [0] arrival counter, [1] error flag
+  unsigned long long bar_base = 0;        // arrivals so far
+  bool ds_check = false;                  // a persistent step ran since the last check
+  bool last_persistent = false;
+  int opt_persistent = 0;
+  int opt_spin_limit = 1 << 20;
+  int opt_unreachable = 0;
+
   // profiling
   int prof_cls = VLA_K_NONE;
   ProfSink prof;
@@ -497,6 +509,111 @@ void run_layers(vla_model* m, const KvView& view, int n, int64_t pos0, int cb0, 
   }
 }
 
+// One decode step's embedding row, RoPE table and every layer as one persistent
+// launch (decode_step.hip). Returns false, having launched nothing, when this step
+// cannot take it (no kernel shape, a single cached block, no co-resident grid).
+bool run_decode_persistent(vla_model* m, const KvView& view, int32_t token, int64_t pos, int cb0,
+                           int cslot0, hipStream_t st) {
+  const vla_config& c = m->cfg;
+  if (m->ds_shape == DSHAPE_NONE || !m->opt_persistent || m->prof_cls != VLA_K_NONE ||
+      view.nlb < 2)
+    return false;
+  if (m->ds_grid == 0) m->ds_grid = decode_step_grid(m->ds_shape);
+  if (m->ds_grid < 1) return false;
+  const int H = c.hidden, qd = c.n_heads * c.head_dim, hkv = c.n_kv_heads;
+  const int nqkv = (c.n_heads + 2 * hkv) * c.head_dim;
+  DecodeStepArgs p;
+  p.token = token == VLA_TOKEN_DEVICE ? 0 : token;
+  p.token_key = token == VLA_TOKEN_DEVICE ? m->amax_res : nullptr;
+  p.E = m->embed;
+  p.x = (float*)m->x;
+  p.H = H;
+  p.pos = pos;
+  p.inv_freq = m->inv_freq;
+  p.half = c.head_dim / 2;
+  p.rope = m->rope_tab;
+  const FwdCtx ctx = make_ctx(m, view, 0, cb0, cslot0);
+  // q/k/v: the residual row, normalised per wavefront; RoPE + paged K/V write
+  p.qkv.x = m->x;
+  p.qkv.norm_g = m->norm_ones;
+  p.qkv.eps = c.rms_eps;
+  p.qkv.N = nqkv;
+  p.qkv.K = H;
+  p.qkv.epi = EPI_QKV;
+  p.qkv.ctx = ctx;
+  // attention: the key splits of the decode kernel, at least 2 (the output
+  // projection merges them) and at most the merge's limit
+  AttnArgs& at = p.at;
+  at.q = m->qbuf;
+  at.out = m->ao;
+  at.kpool = m->kpool;
+  at.vpool = m->vpool;
+  at.g = m->geom;
+  at.blk_table = view.blk;
+  at.blk_ntok = view.ntok;
+  at.nlb = view.nlb;
+  at.last_ntok = view.last_ntok;
+  at.causal = 1;
+  at.cb0 = cb0;
+  at.cslot0 = cslot0;
+  at.n = 1;
+  at.hq = c.n_heads;
+  at.part_o = m->part_o;
+  at.part_ml = m->part_ml;
+  at.part_rows = kPartRows;
+  at.scale = (float)(1.0 / std::sqrt((double)c.head_dim));
+  int splits = (view.nlb + 7) / 8;
+  splits = std::min(splits, std::max(1, 512 / hkv));
+  splits = std::min(splits, kFoldMaxSplits);
+  splits = std::min(splits, std::max(1, kPartRows / (hkv * 16)));
+  splits = std::max(splits, 2);
+  const int bps = (view.nlb + splits - 1) / splits;
+  at.splits = (view.nlb + bps - 1) / bps;
+  if (at.splits < 2) return false;
+  // output projection: merges the splits on the way in, adds to the residual
+  p.o.x = m->ao;
+  p.o.N = H;
+  p.o.K = qd;
+  p.o.epi = EPI_RESID;
+  p.o.out = m->x;
+  p.o.part_o = m->part_o;
+  p.o.part_ml = m->part_ml;
+  p.o.splits = at.splits;
+  p.o.grp = c.n_heads / hkv;
+  p.o.hd = c.head_dim;
+  p.gu = decode_gateup_args(m, 0);
+  p.dn.x = m->act;
+  p.dn.N = H;
+  p.dn.K = c.ffn;
+  p.dn.epi = EPI_RESID;
+  p.dn.out = m->x;
+  // row groups and virtual workgroups (as the separate kernels would launch them)
+  const bool dks = m->ds_shape == DSHAPE_C3_3_3_D1_5_4;  // down projection K split 4 ways
+  p.ng_qkv = nqkv / 2;
+  p.vg_qkv = (p.ng_qkv + 3) / 4;
+  p.ng_o = (H + 1) / 2;
+  p.vg_o = (p.ng_o + 3) / 4;
+  p.ng_gu = c.ffn;
+  p.vg_gu = (p.ng_gu + 3) / 4;
+  p.ng_dn = dks ? H : (H + 1) / 2;
+  p.vg_dn = dks ? p.ng_dn : (p.ng_dn + 3) / 4;
+  p.wtab = m->d_wtab;
+  p.n_layers = c.n_layers;
+  p.bar = m->d_bar;
+  p.err = (int*)(m->d_bar + 1);
+  p.base = m->bar_base + (m->opt_unreachable ? (1ull << 40) : 0ull);
+  p.spin_limit = m->opt_spin_limit;
+  const hipError_t e = launch_decode_step(p, m->ds_shape, m->ds_grid, st);
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    m->ds_shape = DSHAPE_NONE;  // e.g. the grid cannot be co-resident: per-kernel path from now on
+    return false;
+  }
+  m->bar_base += (unsigned long long)decode_step_barriers(c.n_layers) * (unsigned long long)m->ds_grid;
+  m->ds_check = true;
+  return true;
+}
+
 // final RMSNorm of the last row, output head, argmax
 void run_head(vla_model* m, int row, hipStream_t st) {
   const vla_config& c = m->cfg;
@@ -517,11 +634,47 @@ void run_head(vla_model* m, int row, hipStream_t st) {
   m->have_logits = true;
 }
 
+// after a persistent decode step: reads its error flag (synchronises) and, when a
+// barrier wait gave up, clears the barrier state and reports it
+void check_step_error(vla_model* m, hipStream_t st) {
+  if (!m->ds_check) return;
+  unsigned long long* h = (unsigned long long*)staging_acquire(m->st_read) + 4;
+  HIPCHK(hipMemcpyAsync(h, m->d_bar + 1, sizeof(unsigned long long), hipMemcpyDeviceToHost, st));
+  HIPCHK(hipStreamSynchronize(st));
+  m->ds_check = false;
+  if (*h != 0) {
+    HIPCHK(hipMemsetAsync(m->d_bar, 0, 2 * sizeof(unsigned long long), st));
+    HIPCHK(hipStreamSynchronize(st));
+    m->bar_base = 0;
+    raise(VLA_E_TIMEOUT, "a barrier wait of the persistent decode step gave up");
+  }
+}
+
 int read_argmax(vla_model* m, hipStream_t st) {
+  check_step_error(m, st);
   unsigned long long* h = (unsigned long long*)staging_acquire(m->st_read);
   HIPCHK(hipMemcpyAsync(h, m->amax_res, sizeof(unsigned long long), hipMemcpyDeviceToHost, st));
   HIPCHK(hipStreamSynchronize(st));
   return (int)(0xffffffffu - (uint32_t)(*h & 0xffffffffull));
+}
+
+// chunks per lane of a whole-row one-shot GEMV over K inputs
+int gemv1_cpl(int K) { return (K / 8 + 63) / 64; }
+
+// the persistent decode-step kernel shape of a model, or DSHAPE_NONE
+int decode_shape(const vla_config& c, int dt, int wf) {
+  if (dt != DT_BF16 || wf != WF_ACT || c.vocab < 1 || c.kv_only_last || c.head_dim != 128)
+    return DSHAPE_NONE;
+  const int grp = c.n_heads / c.n_kv_heads;
+  if (grp > 16 || c.n_heads > kFoldMaxHeads) return DSHAPE_NONE;
+  const int nqkv = (c.n_heads + 2 * c.n_kv_heads) * c.head_dim;
+  if (nqkv % 8 || (2 * c.ffn) % 32) return DSHAPE_NONE;
+  const int cq = gemv1_cpl(c.hidden), co = gemv1_cpl(c.n_heads * c.head_dim);
+  const int cg = gemv1_cpl(c.hidden), cd = gemv1_cpl(c.ffn);
+  const int dks = ((c.ffn / 8 + 3) / 4 + 63) / 64;  // chunks per lane of a 4-way K split
+  if (cq == 3 && co == 3 && cg == 3 && cd > 4 && dks == 5) return DSHAPE_C3_3_3_D1_5_4;
+  if (cq == 1 && co == 2 && cg == 1 && cd == 1) return DSHAPE_C1_2_1_D2_1_1;
+  return DSHAPE_NONE;
 }
 
 void mean_keys_for(vla_model* m, int frame_index, hipStream_t st) {
@@ -711,6 +864,20 @@ void build_model(vla_model* m, const vla_config& cfg, const vla_model* borrow) {
   staging_init(m->st_read, 64);
   m->pool.reset(c.num_blocks);
   for (int i = c.max_frames - 1; i >= 0; --i) m->free_slots.push_back(i);
+  m->ds_shape = decode_shape(c, m->dt, m->wf);
+  if (m->ds_shape != DSHAPE_NONE) {
+    std::vector<const void*> wt;
+    for (int l = 0; l < c.n_layers; ++l) {
+      wt.push_back(m->wqkv[l]);
+      wt.push_back(m->wo[l]);
+      wt.push_back(m->wgu[l]);
+      wt.push_back(m->wdown[l]);
+    }
+    m->d_wtab = (const void**)dalloc(m, wt.size() * sizeof(void*));
+    HIPCHK(hipMemcpy(m->d_wtab, wt.data(), wt.size() * sizeof(void*), hipMemcpyHostToDevice));
+    m->d_bar = (unsigned long long*)dalloc(m, 2 * sizeof(unsigned long long));
+    HIPCHK(hipMemset(m->d_bar, 0, 2 * sizeof(unsigned long long)));
+  }
   init_weights(m);
 }
 
@@ -821,13 +988,18 @@ vla_status vla_decode_step(vla_model* m, int32_t token, int32_t* out_next_token,
     try {
       sync_meta(m, st);
       const int cb0 = logical_blocks(m) - 1;
-      // VLA_TOKEN_DEVICE: the previous forward's greedy token, read on the device;
-      // the same launch writes the position's RoPE table
-      HIPCHK(launch_embed_rope1(token, token == VLA_TOKEN_DEVICE ? m->amax_res : nullptr, m->embed,
-                                m->x, m->cfg.hidden, m->dt, pos, m->inv_freq,
-                                m->cfg.head_dim / 2, m->rope_tab, st));
-      run_layers(m, model_view(m), 1, pos, cb0, off % bt, /*decode=*/true, st, /*rope_ready=*/true);
+      const KvView view = model_view(m);
+      m->last_persistent = run_decode_persistent(m, view, token, pos, cb0, off % bt, st);
+      if (!m->last_persistent) {
+        // VLA_TOKEN_DEVICE: the previous forward's greedy token, read on the device;
+        // the same launch writes the position's RoPE table
+        HIPCHK(launch_embed_rope1(token, token == VLA_TOKEN_DEVICE ? m->amax_res : nullptr,
+                                  m->embed, m->x, m->cfg.hidden, m->dt, pos, m->inv_freq,
+                                  m->cfg.head_dim / 2, m->rope_tab, st));
+        run_layers(m, view, 1, pos, cb0, off % bt, /*decode=*/true, st, /*rope_ready=*/true);
+      }
       run_head(m, 0, st);
+      if (out_next_token) *out_next_token = read_argmax(m, st);
     } catch (...) {
       tail.ntok -= 1;
       m->next_pos -= 1;
@@ -841,7 +1013,6 @@ vla_status vla_decode_step(vla_model* m, int32_t token, int32_t* out_next_token,
       m->meta_dirty = true;
       throw;
     }
-    if (out_next_token) *out_next_token = read_argmax(m, st);
   });
 }
 
@@ -989,6 +1160,7 @@ vla_status vla_logits_out(vla_model* m, float* out, int32_t n, void* stream) {
     if (!m->have_logits) raise(VLA_E_STATE, "no forward has run yet");
     HIPCHK(hipSetDevice(m->dev));
     const hipStream_t st = (hipStream_t)stream;
+    check_step_error(m, st);
     HIPCHK(hipMemcpyAsync(out, m->logits, (size_t)n * sizeof(float), hipMemcpyDefault, st));
     HIPCHK(hipStreamSynchronize(st));
   });
@@ -1200,6 +1372,41 @@ vla_status vla_weight_out(vla_model* m, int32_t kind, int32_t layer, void* out, 
   });
 }
 
+vla_status vla_set_option(vla_model* m, int32_t key, int64_t value) {
+  return guarded([&] {
+    if (!m) raise(VLA_E_INVALID, "null model");
+    switch (key) {
+      case VLA_OPT_PERSISTENT_DECODE:
+        if (value != 0 && value != 1) raise(VLA_E_INVALID, "value must be 0 or 1");
+        m->opt_persistent = (int)value;
+        break;
+      case VLA_OPT_BARRIER_SPIN_LIMIT:
+        if (value < 0 || value > (1ll << 30)) raise(VLA_E_INVALID, "spin limit outside 0..2^30");
+        m->opt_spin_limit = (int)value;
+        break;
+      case VLA_OPT_BARRIER_TEST_UNREACHABLE:
+        if (value != 0 && value != 1) raise(VLA_E_INVALID, "value must be 0 or 1");
+        m->opt_unreachable = (int)value;
+        break;
+      default:
+        raise(VLA_E_INVALID, "unknown or read-only option");
+    }
+  });
+}
+
+vla_status vla_get_option(const vla_model* m, int32_t key, int64_t* value) {
+  return guarded([&] {
+    if (!m || !value) raise(VLA_E_INVALID, "null argument");
+    switch (key) {
+      case VLA_OPT_PERSISTENT_DECODE: *value = m->opt_persistent; break;
+      case VLA_OPT_BARRIER_SPIN_LIMIT: *value = m->opt_spin_limit; break;
+      case VLA_OPT_BARRIER_TEST_UNREACHABLE: *value = m->opt_unreachable; break;
+      case VLA_INFO_LAST_DECODE_PERSISTENT: *value = m->last_persistent ? 1 : 0; break;
+      default: raise(VLA_E_INVALID, "unknown option");
+    }
+  });
+}
+
 vla_status vla_profile_enable(vla_model* m, int32_t kernel_class) {
   return guarded([&] {
     if (!m) raise(VLA_E_INVALID, "null model");
@@ -1258,6 +1465,47 @@ vla_status vla_probe_mfma_peak(float* out, int32_t blocks, int32_t iters, void* 
     HIPCHK(hipEventDestroy(e1));
     const double flop = (double)blocks * 4.0 * (double)iters * 8.0 * 16384.0;
     *out_tflops = flop / ((double)ms * 1e-3) / 1e12;
+  });
+}
+
+vla_status vla_probe_barrier(int32_t grid, int32_t nbar, void* stream, double* out_us) {
+  return guarded([&] {
+    if (!out_us) raise(VLA_E_INVALID, "null argument");
+    const int gmax = barrier_probe_max_grid();
+    if (grid < 1 || grid > gmax || nbar < 1 || nbar > 100000)
+      raise(VLA_E_INVALID, "grid outside 1.." + std::to_string(gmax) + " or nbar outside 1..100000");
+    const hipStream_t st = (hipStream_t)stream;
+    unsigned long long* bar = nullptr;
+    float* scratch = nullptr;
+    HIPCHK(hipMalloc(&bar, 64));
+    HIPCHK(hipMalloc(&scratch, (size_t)grid * 256 * sizeof(float)));
+    hipEvent_t e0 = nullptr, e1 = nullptr;
+    auto cleanup = [&] {
+      if (e0) (void)hipEventDestroy(e0);
+      if (e1) (void)hipEventDestroy(e1);
+      (void)hipFree(bar);
+      (void)hipFree(scratch);
+    };
+    try {
+      HIPCHK(hipMemsetAsync(bar, 0, 64, st));
+      HIPCHK(hipMemsetAsync(scratch, 0, (size_t)grid * 256 * sizeof(float), st));
+      HIPCHK(hipEventCreate(&e0));
+      HIPCHK(hipEventCreate(&e1));
+      HIPCHK(hipEventRecord(e0, st));
+      HIPCHK(launch_barrier_probe(bar, (int*)(bar + 1), scratch, grid, nbar, 1 << 20, st));
+      HIPCHK(hipEventRecord(e1, st));
+      HIPCHK(hipEventSynchronize(e1));
+      float ms = 0.f;
+      HIPCHK(hipEventElapsedTime(&ms, e0, e1));
+      int err = 0;
+      HIPCHK(hipMemcpy(&err, bar + 1, sizeof(int), hipMemcpyDeviceToHost));
+      if (err) raise(VLA_E_TIMEOUT, "a probe barrier gave up");
+      *out_us = (double)ms * 1e3 / nbar;
+    } catch (...) {
+      cleanup();
+      throw;
+    }
+    cleanup();
   });
 }
 

@@ -17,6 +17,9 @@ LIB_PATH = os.path.join(HERE, "libvla.so")
 
 VLA_OK, VLA_E_INVALID, VLA_E_NO_BLOCKS, VLA_E_NOTHING_TO_EVICT, VLA_E_HIP, VLA_E_STATE = \
     0, -1, -2, -3, -4, -5
+VLA_E_TIMEOUT = -6
+VLA_OPT_PERSISTENT_DECODE, VLA_OPT_BARRIER_SPIN_LIMIT, VLA_OPT_BARRIER_TEST_UNREACHABLE = 1, 2, 3
+VLA_INFO_LAST_DECODE_PERSISTENT = 100
 VLA_F32, VLA_BF16, VLA_INT4_G128 = 0, 1, 2
 VLA_SWIGLU, VLA_GEGLU = 0, 1
 VLA_TOKEN_DEVICE = -1   # decode input: the previous forward's greedy token, on the device
@@ -98,6 +101,9 @@ _SIGS = {
     "vla_kv_gather": (c_int32, [c_void_p, c_int32, c_void_p, c_void_p, c_int32,
                                 POINTER(c_int32), c_void_p]),
     "vla_weight_out": (c_int32, [c_void_p, c_int32, c_int32, c_void_p, c_int64, c_void_p]),
+    "vla_set_option": (c_int32, [c_void_p, c_int32, c_int64]),
+    "vla_probe_barrier": (c_int32, [c_int32, c_int32, c_void_p, POINTER(c_double)]),
+    "vla_get_option": (c_int32, [c_void_p, c_int32, POINTER(c_int64)]),
     "vla_profile_enable": (c_int32, [c_void_p, c_int32]),
     "vla_profile_read": (c_int32, [c_void_p, POINTER(c_double), POINTER(c_int32)]),
     "vla_profile_replay": (c_int32, [c_void_p, c_int32, c_int32, c_void_p, POINTER(c_double)]),
@@ -309,6 +315,23 @@ def vla_kv_gather(m: int, layer: int, k_out, v_out, cap_tokens: int, stream=None
 
 def vla_weight_out(m: int, kind: int, layer: int, out, nbytes: int, stream=None) -> None:
     _check(load().vla_weight_out(m, kind, layer, _ptr(out), nbytes, _stream(stream)))
+
+
+def vla_set_option(m: int, key: int, value: int) -> None:
+    _check(load().vla_set_option(m, key, int(value)))
+
+
+def vla_probe_barrier(grid: int, nbar: int, stream=None) -> float:
+    """Microseconds per device-scope barrier over `grid` resident workgroups."""
+    us = c_double(0.0)
+    _check(load().vla_probe_barrier(grid, nbar, _stream(stream), byref(us)))
+    return us.value
+
+
+def vla_get_option(m: int, key: int) -> int:
+    v = c_int64(0)
+    _check(load().vla_get_option(m, key, byref(v)))
+    return v.value
 
 
 def vla_profile_enable(m: int, kernel_class: int) -> None:
@@ -561,6 +584,12 @@ class Model:
 
     def weight_out(self, kind, layer, out, nbytes, stream=None):
         vla_weight_out(self.h, kind, layer, out, nbytes, stream)
+
+    def set_option(self, key, value):
+        vla_set_option(self.h, key, value)
+
+    def get_option(self, key):
+        return vla_get_option(self.h, key)
 
     def profile_enable(self, kernel_class):
         vla_profile_enable(self.h, K_CLASSES.get(kernel_class, kernel_class)
