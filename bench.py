@@ -462,15 +462,9 @@ def measured_peaks():
     e1.record(stream)
     torch.cuda.synchronize()
     copy_gbs = 5 * 2 * a.numel() * 4 / (e0.elapsed_time(e1) * 1e-3) / 1e9
-    # a read-only stream of the same 1 GiB (a sum: the reads dominate, one scalar out)
-    a.sum()
-    e0.record(stream)
-    for _ in range(5):
-        a.sum()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    read_gbs = 5 * a.numel() * 4 / (e0.elapsed_time(e1) * 1e-3) / 1e9
     del a, b
+    # a streaming read of 1 GiB (16-byte loads, 8 in flight per thread)
+    read_gbs = vla.vla_probe_read_bandwidth(1 << 30, 5, stream.cuda_stream)
     out = torch.empty(4096, dtype=torch.float32, device="cuda")
     tf = vla.vla_probe_mfma_peak(out, 4096, 2000, stream.cuda_stream)
     return {"copy_gbs": round(copy_gbs, 1), "read_gbs": round(read_gbs, 1),

@@ -362,6 +362,13 @@ vla_status vla_profile_replay(vla_model* m, int32_t kernel_class, int32_t reps, 
 vla_status vla_probe_mfma_peak(float* out, int32_t blocks, int32_t iters, void* stream,
                                double* out_tflops);
 
+/* HBM read probe (a measured streaming ceiling beside the published 8 TB/s): reads a
+ * device buffer of `bytes` (allocated, zeroed and freed by the call; a multiple of 16
+ * in 1 MiB..64 GiB) `reps` times (1..100) with 16-byte loads, 8 in flight per thread
+ * over 2048 workgroups, timed with stream events; writes GB/s. Synchronises. Errors:
+ * VLA_E_INVALID, VLA_E_HIP. */
+vla_status vla_probe_read_bandwidth(int64_t bytes, int32_t reps, void* stream, double* out_gbs);
+
 /* Action expert of a pi0-style policy ("Running VLAs at Real-time Speed",
  * section 2: a vision-language prefix model plus an expert that predicts an
  * action chunk by flow matching). The expert is a decoder of its own (cfg:

@@ -244,6 +244,33 @@ __global__ __launch_bounds__(256) void mfma_peak_kernel(float* out, int iters) {
   for (int j = 0; j < 8; ++j) t += acc[j][0] + acc[j][1] + acc[j][2] + acc[j][3];
   if (threadIdx.x == 0) out[blockIdx.x] = t;
 }
+// HBM read probe: 16-byte loads over n16 chunks, 8 independent loads in flight per
+// thread (indexes past the end re-read the last chunk), folded into one xor per thread
+// that is stored so that no load can be dropped
+__global__ __launch_bounds__(256) void read_probe_kernel(const u32x4_t* p, int64_t n16,
+                                                         uint32_t* out) {
+  constexpr int U = 8;
+  const int64_t stride = (int64_t)gridDim.x * 256;
+  u32x4_t acc = {0u, 0u, 0u, 0u};
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n16; i += stride * U) {
+    u32x4_t v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t j = i + u * stride;
+      v[u] = p[j < n16 ? j : n16 - 1];
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) acc ^= v[u];
+  }
+  out[(int64_t)blockIdx.x * 256 + threadIdx.x] = acc[0] ^ acc[1] ^ acc[2] ^ acc[3];
+}
+hipError_t launch_read_probe(const void* p, int64_t bytes, uint32_t* out, int blocks,
+                             hipStream_t s) {
+  if (bytes < 16 || bytes % 16 || blocks < 1) return hipErrorInvalidValue;
+  read_probe_kernel<<<blocks, 256, 0, s>>>((const u32x4_t*)p, bytes / 16, out);
+  return hipGetLastError();
+}
+
 hipError_t launch_mfma_peak(float* out, int blocks, int iters, hipStream_t s) {
   mfma_peak_kernel<<<blocks, 256, 0, s>>>(out, iters);
   return hipGetLastError();

@@ -1468,6 +1468,44 @@ vla_status vla_probe_mfma_peak(float* out, int32_t blocks, int32_t iters, void* 
   });
 }
 
+vla_status vla_probe_read_bandwidth(int64_t bytes, int32_t reps, void* stream, double* out_gbs) {
+  return guarded([&] {
+    if (!out_gbs) raise(VLA_E_INVALID, "null argument");
+    if (bytes < (1 << 20) || bytes > ((int64_t)1 << 36) || bytes % 16 || reps < 1 || reps > 100)
+      raise(VLA_E_INVALID, "bytes a multiple of 16 in 1 MiB..64 GiB, reps in 1..100");
+    const hipStream_t st = (hipStream_t)stream;
+    const int blocks = 2048;
+    void* buf = nullptr;
+    uint32_t* out = nullptr;
+    hipEvent_t e0 = nullptr, e1 = nullptr;
+    auto cleanup = [&] {
+      if (e0) (void)hipEventDestroy(e0);
+      if (e1) (void)hipEventDestroy(e1);
+      (void)hipFree(buf);
+      (void)hipFree(out);
+    };
+    try {
+      HIPCHK(hipMalloc(&buf, (size_t)bytes));
+      HIPCHK(hipMalloc(&out, (size_t)blocks * 256 * sizeof(uint32_t)));
+      HIPCHK(hipMemsetAsync(buf, 0, (size_t)bytes, st));
+      HIPCHK(launch_read_probe(buf, bytes, out, blocks, st));  // warm-up
+      HIPCHK(hipEventCreate(&e0));
+      HIPCHK(hipEventCreate(&e1));
+      HIPCHK(hipEventRecord(e0, st));
+      for (int r = 0; r < reps; ++r) HIPCHK(launch_read_probe(buf, bytes, out, blocks, st));
+      HIPCHK(hipEventRecord(e1, st));
+      HIPCHK(hipEventSynchronize(e1));
+      float ms = 0.f;
+      HIPCHK(hipEventElapsedTime(&ms, e0, e1));
+      *out_gbs = (double)bytes * reps / ((double)ms * 1e-3) / 1e9;
+    } catch (...) {
+      cleanup();
+      throw;
+    }
+    cleanup();
+  });
+}
+
 vla_status vla_probe_barrier(int32_t grid, int32_t nbar, void* stream, double* out_us) {
   return guarded([&] {
     if (!out_us) raise(VLA_E_INVALID, "null argument");

@@ -103,6 +103,7 @@ _SIGS = {
     "vla_weight_out": (c_int32, [c_void_p, c_int32, c_int32, c_void_p, c_int64, c_void_p]),
     "vla_set_option": (c_int32, [c_void_p, c_int32, c_int64]),
     "vla_probe_barrier": (c_int32, [c_int32, c_int32, c_void_p, POINTER(c_double)]),
+    "vla_probe_read_bandwidth": (c_int32, [c_int64, c_int32, c_void_p, POINTER(c_double)]),
     "vla_get_option": (c_int32, [c_void_p, c_int32, POINTER(c_int64)]),
     "vla_profile_enable": (c_int32, [c_void_p, c_int32]),
     "vla_profile_read": (c_int32, [c_void_p, POINTER(c_double), POINTER(c_int32)]),
@@ -326,6 +327,13 @@ def vla_probe_barrier(grid: int, nbar: int, stream=None) -> float:
     us = c_double(0.0)
     _check(load().vla_probe_barrier(grid, nbar, _stream(stream), byref(us)))
     return us.value
+
+
+def vla_probe_read_bandwidth(nbytes: int, reps: int = 5, stream=None) -> float:
+    """GB/s of a streaming read of an nbytes device buffer."""
+    g = c_double(0.0)
+    _check(load().vla_probe_read_bandwidth(int(nbytes), reps, _stream(stream), byref(g)))
+    return g.value
 
 
 def vla_get_option(m: int, key: int) -> int:
