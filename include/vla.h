@@ -372,8 +372,8 @@ vla_status vla_probe_read_bandwidth(int64_t bytes, int32_t reps, void* stream, d
 /* Action expert of a pi0-style policy ("Running VLAs at Real-time Speed",
  * section 2: a vision-language prefix model plus an expert that predicts an
  * action chunk by flow matching). The expert is a decoder of its own (cfg:
- * vocab 0, all layers full; n_layers, n_kv_heads, head_dim, act_dtype and
- * block_tokens equal to the prefix model's) whose layer l attends to the
+ * vocab 0, all layers full, hidden <= 4096; n_layers, n_kv_heads, head_dim,
+ * act_dtype and block_tokens equal to the prefix model's) whose layer l attends to the
  * prefix model's layer-l cache plus the n_actions tokens of the chunk, every
  * key visible to every chunk row (no causal mask inside the chunk). The
  * chunk's K/V live in ceil(n_actions / block_tokens) blocks popped from the
@@ -391,7 +391,9 @@ void vla_expert_destroy(vla_expert* e);
  *   h = the expert's layers over the chunk at positions P .. P+n_actions-1,
  *       P = the prefix model's next position (the prefix state is unchanged)
  *   x += dt * RMSNorm(h)   (the velocity: the final norm, no output projection)
- * Asynchronous on `stream`. Errors: VLA_E_INVALID (null x, n_steps < 1, dt <= 0). */
+ * Asynchronous on `stream`. The first call with more steps than any earlier call
+ * allocates the table of the n_steps time embeddings (n_steps * hidden floats,
+ * kept until destroy). Errors: VLA_E_INVALID (null x, n_steps < 1, dt <= 0). */
 vla_status vla_expert_denoise(vla_expert* e, float* x, int32_t n_steps, double dt, void* stream);
 
 /* Host-only LIFO block pool ("Rebuilding Kshipra Around Memory", section 1):

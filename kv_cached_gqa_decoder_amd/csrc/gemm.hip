@@ -13,6 +13,7 @@
 #include <hip/hip_fp16.h>
 
 #include <algorithm>
+#include <type_traits>
 
 #include "common.hpp"
 #include "epilogue.hpp"
@@ -241,24 +242,28 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_kernel(GemmArgs a, i
 }
 
 // ---------------------------------------------------------------------------
-// Two-stream GEMM for 256-row M tiles with a wide N: the gated projection of a
-// 129- to 256-token prefill. The activation tile (L2-resident, re-read by every column
-// group) and the weight tile (streamed from HBM once) travel in two LDS rings of
+// Two-stream GEMM for BMT-row M tiles (128 or 256) with a wide N: the gated
+// projection of a 129- to 256-token prefill, and the long-K residual projection
+// (down) of one, split along K. The activation tile (re-read by every column group)
+// and the weight tile (streamed from HBM once) travel in two LDS rings of
 // different depths, each filled by its own two producer wavefronts with
 // global_load_lds DMA. Vector-memory counters retire in issue order per
 // wavefront, so a ring's producers wait only for their own stream: the weight
 // ring keeps NSW-1 32-deep steps in flight (the HBM latency needs about 100 KB per
-// CU) while the activation ring stays short. Four consumer wavefronts (64 rows
+// CU) while the activation ring stays shorter. Four consumer wavefronts (BMT/4 rows
 // each, every column of the group) read both operands from LDS; one barrier per
 // K step hands both stages over. Columns are dealt out in units of 32 (one
-// interleaved gate/up block, or 16 RoPE pairs), each workgroup taking a
-// contiguous run of floor or ceil of units/groups, so a launch covers every
-// column in about one round of workgroups.
+// interleaved gate/up block), each workgroup taking a contiguous run of floor or
+// ceil of units/groups, so a launch covers every column in about one round of
+// workgroups. Unsplit launches put the M tiles of one column group on one XCD
+// (they share the weight tile through its L2); split launches put the column
+// groups of one (K piece, M tile) on one XCD (they share the activation piece).
 // ---------------------------------------------------------------------------
-template <int NTM, int NSA, int NSW, bool LO = false>
+template <int NTM, int NSA, int NSW, bool LO = false, int BMT = 256>
 struct Ws2Tile {
-  // 256 rows x 32 bf16 of the activations (LO: then the 256 rows of their low part)
-  static constexpr int ASTAGE = (LO ? 2 : 1) * 256 * 64;
+  // BMT rows x 32 bf16 of the activations (LO: then the BMT rows of their low part)
+  static constexpr int AROWS = (LO ? 2 : 1) * BMT;
+  static constexpr int ASTAGE = AROWS * 64;
   static constexpr int WROWS = NTM * 16;
   static constexpr int WSTAGE = WROWS * 64;          // WROWS x 32 bf16
   static constexpr int ALOADS = ASTAGE / 1024 / 2;   // DMA loads per activation producer
@@ -267,7 +272,8 @@ struct Ws2Tile {
   static_assert(WSTAGE % 2048 == 0 && ALOADS * (NSA - 2) <= 63 && WLOADS * (NSW - 2) <= 63 &&
                     LDS <= 160 * 1024,
                 "ring shape");
-  static_assert(NTM == 2 || NTM == 4 || NTM == 6, "tile counts");
+  static_assert(NTM % 2 == 0 && NTM >= 2 && NTM <= 12 && (BMT == 128 || BMT == 256),
+                "tile counts");
   // chunk position of K chunk kc (0..3) in LDS row r: 16 rows read at one chunk
   // column fall in distinct 16-byte bank groups
   static __device__ __forceinline__ int pos(int r, int kc) { return kc ^ ((r >> 1) & 3); }
@@ -305,13 +311,14 @@ __device__ __forceinline__ void ws2_produce(unsigned char* ring, const bf16_t* (
   __builtin_amdgcn_s_waitcnt(0);        // no DMA outstanding at exit
 }
 
-// consumer wavefront c of CW: rows (256/CW)c .. of the M tile, NTC 16-column tiles
-template <int EPI, int NTC, int NTM, int NSA, int NSW, int CW, bool LO>
+// consumer wavefront c of CW: rows (BMT/CW)c .. of the M tile, NTC 16-column tiles;
+// the gated product, or (EPI_PARTIAL) this K piece's fp32 partial [z][M][N]
+template <int EPI, int NTC, int NTM, int NSA, int NSW, int CW, bool LO, int BMT>
 __device__ __forceinline__ void ws2_consume(const GemmArgs& a, const unsigned char* smem, int nk,
-                                            int n0, int m0, int c, int lane) {
-  static_assert(kGated<EPI>, "gated projections (the SwiGLU / GeGLU epilogue) only");
-  using T = Ws2Tile<NTM, NSA, NSW, LO>;
-  constexpr int RPW = 256 / CW, MT = RPW / 16;  // rows and 16-row tiles per consumer
+                                            int n0, int m0, int c, int lane, int z) {
+  static_assert(kGated<EPI> || EPI == EPI_PARTIAL, "gated products or split-K partials");
+  using T = Ws2Tile<NTM, NSA, NSW, LO, BMT>;
+  constexpr int RPW = BMT / CW, MT = RPW / 16;  // rows and 16-row tiles per consumer
   f32x4_t acc[MT][NTC];
 #pragma unroll
   for (int i = 0; i < MT; ++i)
@@ -336,7 +343,7 @@ __device__ __forceinline__ void ws2_consume(const GemmArgs& a, const unsigned ch
       for (int ni = 0; ni < NTC; ++ni)
         acc[mi][ni] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bf[ni], acc[mi][ni], 0, 0, 0);
       if constexpr (LO) {
-        const int rl = 256 + r;
+        const int rl = BMT + r;
         const bf16x8_t al = *(const bf16x8_t*)(sa + rl * 64 + (T::pos(rl, kc) << 4));
 #pragma unroll
         for (int ni = 0; ni < NTC; ++ni)
@@ -356,8 +363,10 @@ __device__ __forceinline__ void ws2_consume(const GemmArgs& a, const unsigned ch
 #pragma unroll
       for (int ni = 0; ni < NTC; ++ni) {
         const float v = acc[mi][ni][e];
-        // tiles (ni, ni+1), ni even: 16 gate columns, then the 16 matching up columns
-        if ((ni & 1) == 0) {
+        if constexpr (EPI == EPI_PARTIAL) {
+          if (row < M) a.ws[((size_t)z * M + row) * a.N + n0 + ni * 16 + (lane & 15)] = v;
+        } else if ((ni & 1) == 0) {
+          // tiles (ni, ni+1), ni even: 16 gate columns, then the 16 matching up columns
           const bf16_t o =
               bf16_rne(glu_fast<EPI == EPI_GEGLU_K>(v, acc[mi][ni + 1 < NTC ? ni + 1 : ni][e]));
           if (row < M) ((bf16_t*)a.C)[(size_t)row * (a.N / 2) + (n0 + ni * 16) / 2 + (lane & 15)] = o;
@@ -367,21 +376,37 @@ __device__ __forceinline__ void ws2_consume(const GemmArgs& a, const unsigned ch
   }
 }
 
-template <int EPI, int NTM, int NSA, int NSW, int CW, bool LO>
+template <int EPI, int NTM, int NSA, int NSW, int CW, bool LO, int BMT>
 __global__ __launch_bounds__(64 * (CW + 4)) void gemm_ws2_kernel(GemmArgs a, int units, int groups,
-                                                                 int tiles_m) {
-  using T = Ws2Tile<NTM, NSA, NSW, LO>;
+                                                                 int tiles_m, int splits,
+                                                                 int ksteps) {
+  using T = Ws2Tile<NTM, NSA, NSW, LO, BMT>;
   __shared__ __attribute__((aligned(1024))) unsigned char smem[T::LDS];
-  // workgroup -> (M tile mt, column group g); the M tiles of one group sit 8
-  // workgroups apart, i.e. on one XCD, where they share the weights
   const int g8 = (groups + 7) & ~7;
-  const int r = blockIdx.x % (g8 * tiles_m);
-  const int mt = (r % (8 * tiles_m)) / 8;
-  const int g = (r / (8 * tiles_m)) * 8 + r % 8;
+  int mt, g, z;
+  if (splits == 1) {
+    // workgroup -> (M tile mt, column group g); the M tiles of one group sit 8
+    // workgroups apart, i.e. on one XCD
+    const int r = blockIdx.x;
+    mt = (r % (8 * tiles_m)) / 8;
+    g = (r / (8 * tiles_m)) * 8 + r % 8;
+    z = 0;
+  } else {
+    // workgroup -> (unit u = (K piece, M tile), column group g); unit u lives on
+    // XCD u % 8 with all of its column groups
+    const int xcd = blockIdx.x % 8, q = blockIdx.x / 8;
+    const int u = (q / groups) * 8 + xcd;
+    g = q % groups;
+    if (u >= splits * tiles_m) return;
+    z = u / tiles_m;
+    mt = u % tiles_m;
+  }
   if (g >= groups) return;  // the whole workgroup
   const int u0 = (int)((int64_t)g * units / groups), u1 = (int)((int64_t)(g + 1) * units / groups);
   const int n0 = u0 * 32, nc = (u1 - u0) * 32;
-  const int M = a.M, K = a.K, nk = K / 32, m0 = mt * 256;
+  const int M = a.M, K = a.K, m0 = mt * BMT;
+  const int kt0 = z * ksteps;
+  const int nk = min(K / 32 - kt0, ksteps);  // (the host never makes an empty piece)
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   if (wave >= CW + 2) {  // weight producers: rows of the group (past its columns: a row inside it)
     const int p = wave - CW - 2;
@@ -389,7 +414,8 @@ __global__ __launch_bounds__(64 * (CW + 4)) void gemm_ws2_kernel(GemmArgs a, int
 #pragma unroll
     for (int j = 0; j < T::WLOADS; ++j) {
       const int row = (p * T::WLOADS + j) * 16 + (lane >> 2);
-      src[j] = (const bf16_t*)a.W + (int64_t)(n0 + row % nc) * K + T::pos(row, lane & 3) * 8;
+      src[j] = (const bf16_t*)a.W + (int64_t)(n0 + row % nc) * K + (int64_t)kt0 * 32 +
+               T::pos(row, lane & 3) * 8;
     }
     ws2_produce<T::WLOADS, NSW, T::WSTAGE>(smem + NSA * T::ASTAGE, src, p * T::WLOADS * 1024, nk);
     return;
@@ -401,44 +427,51 @@ __global__ __launch_bounds__(64 * (CW + 4)) void gemm_ws2_kernel(GemmArgs a, int
 #pragma unroll
     for (int j = 0; j < T::ALOADS; ++j) {
       const int row = (p * T::ALOADS + j) * 16 + (lane >> 2);
-      const bf16_t* base = (const bf16_t*)(row < 256 ? a.A : a.A_lo);
-      src[j] = base + (int64_t)min(m0 + (row & 255), M - 1) * K + T::pos(row, lane & 3) * 8;
+      const bf16_t* base = (const bf16_t*)(row < BMT ? a.A : a.A_lo);
+      src[j] = base + (int64_t)min(m0 + row % BMT, M - 1) * K + (int64_t)kt0 * 32 +
+               T::pos(row, lane & 3) * 8;
     }
     ws2_produce<T::ALOADS, NSA, T::ASTAGE>(smem, src, p * T::ALOADS * 1024, nk);
     return;
   }
+  constexpr int N2 = NTM > 2 ? NTM - 2 : NTM, N4 = NTM > 4 ? NTM - 4 : N2;
+  auto consume = [&](auto ntc) {
+    constexpr int NTC = decltype(ntc)::value;
+    ws2_consume<EPI, NTC, NTM, NSA, NSW, CW, LO, BMT>(a, smem, nk, n0, m0, wave, lane, z);
+  };
   switch (nc / 16) {
-    case NTM: ws2_consume<EPI, NTM, NTM, NSA, NSW, CW, LO>(a, smem, nk, n0, m0, wave, lane); break;
-    case (NTM > 2 ? NTM - 2 : NTM):
-      ws2_consume<EPI, (NTM > 2 ? NTM - 2 : NTM), NTM, NSA, NSW, CW, LO>(a, smem, nk, n0, m0,
-                                                                         wave, lane);
-      break;
-    default:
-      ws2_consume<EPI, (NTM > 4 ? NTM - 4 : 2), NTM, NSA, NSW, CW, LO>(a, smem, nk, n0, m0, wave,
-                                                                       lane);
-      break;
+    case NTM: consume(std::integral_constant<int, NTM>{}); break;
+    case N2: consume(std::integral_constant<int, N2>{}); break;
+    default: consume(std::integral_constant<int, N4>{}); break;
   }
 }
 
-// about `target` workgroups over (M tiles x column groups); a group holds at most
-// NTM*16 columns
-template <int EPI, int NTM, int NSA, int NSW, bool LO, int CW = 4>
-static void gemm_ws2_go(const GemmArgs& a, int target, hipStream_t s) {
+// about `target` workgroups over (K pieces x M tiles x column groups); a group holds
+// NTM-4 .. NTM 16-column tiles (the consumer's shapes); false if no group count fits
+template <int EPI, int NTM, int NSA, int NSW, bool LO, int BMT = 256, int CW = 4>
+static bool gemm_ws2_go(const GemmArgs& a, int target, int splits, hipStream_t s) {
   const int units = a.N / 32;
-  const int tiles_m = (a.M + 255) / 256;
-  int groups = std::max(1, target / tiles_m);
-  groups = std::max(groups, (units + NTM / 2 - 1) / (NTM / 2));
-  groups = std::min(groups, units);
-  const int g8 = (groups + 7) & ~7;
-  launch_k(gemm_ws2_kernel<EPI, NTM, NSA, NSW, CW, LO>, dim3(tiles_m * g8), dim3(64 * (CW + 4)),
-           0, s, a, units, groups, tiles_m);
+  const int tiles_m = (a.M + BMT - 1) / BMT;
+  const int steps = a.K / 32;
+  const int ksteps = (steps + splits - 1) / splits;
+  splits = (steps + ksteps - 1) / ksteps;
+  const int gmin = (units + NTM / 2 - 1) / (NTM / 2);             // at most NTM tiles
+  const int gmax = NTM > 4 ? units / ((NTM - 4) / 2) : units;     // at least NTM-4 tiles
+  if (gmin > gmax) return false;
+  const int groups = std::min(gmax, std::max(gmin, target / (tiles_m * splits)));
+  const int grid = splits == 1 ? tiles_m * ((groups + 7) & ~7)
+                               : 8 * ((splits * tiles_m + 7) / 8) * groups;
+  launch_k(gemm_ws2_kernel<EPI, NTM, NSA, NSW, CW, LO, BMT>, dim3(grid), dim3(64 * (CW + 4)), 0,
+           s, a, units, groups, tiles_m, splits, ksteps);
+  return true;
 }
 
 // x[row] += sum over splits of the partials (split order), x the fp32 residual;
 // then, if u is given, u[row] = RMSNorm(x[row]) in bf16 with fp32 statistics.
 // One workgroup per row; each thread keeps up to 4 chunks of 8 columns in registers.
 constexpr int kResidMaxChunks = 4;
-constexpr int kResidMaxSplits = 8;
+constexpr int kResidMaxSplits = 8;        // K pieces of the one-stream split projections
+constexpr int kResidNormMaxSplits = 16;   // partials the reduction takes
 __global__ __launch_bounds__(256) void resid_norm_kernel(const float* ws, int splits, int M, int N,
                                                          float* x, bf16_t* u, bf16_t* u_lo,
                                                          const float* g, float eps) {
@@ -464,16 +497,16 @@ __global__ __launch_bounds__(256) void resid_norm_kernel(const float* ws, int sp
       v[j][4 + i] = x1[i];
     }
     // every split's partial of this chunk is requested before the sum (split order)
-    f32x4_t p0[kResidMaxSplits], p1[kResidMaxSplits];
+    f32x4_t p0[kResidNormMaxSplits], p1[kResidNormMaxSplits];
 #pragma unroll
-    for (int s = 0; s < kResidMaxSplits; ++s)
+    for (int s = 0; s < kResidNormMaxSplits; ++s)
       if (s < splits) {
         const float* p = ws + ((size_t)s * M + row) * N + c * 8;
         p0[s] = *(const f32x4_t*)p;
         p1[s] = *(const f32x4_t*)(p + 4);
       }
 #pragma unroll
-    for (int s = 0; s < kResidMaxSplits; ++s)
+    for (int s = 0; s < kResidNormMaxSplits; ++s)
       if (s < splits) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -873,7 +906,10 @@ static hipError_t gemm_w4(const GemmArgs& a, hipStream_t s) {
 //    20.3 us for 64 x 64), else 64 x 32 tiles with 4 wavefronts along M (63 x 8192 x
 //    1024: 6.2 us against 10.1 us for 64 x 128); up to 128 rows -> 128 x 64 in a
 //    3-stage ring; 129 to 256 rows -> the two-stream kernel (separate activation and
-//    weight rings, 256 x 17920 x 1536: 30.9 us against 34.5 us); more rows -> 256 x 128 with 8
+//    weight rings) on 128-row M tiles, groups of up to 160 columns (256 x 17920 x 1536
+//    with the activations' low part: 36 us against 44 us for one 256-row tile and
+//    96-column groups, whose activation re-reads were 7x the weight bytes, and against
+//    37 us with 32 x 32 x 16 matrix instructions); more rows -> 256 x 128 with 8
 //    wavefronts (4 x 2 grid of 64 x 64 wavefront tiles), 32-deep steps (256 x 17920 x
 //    1536: 34 us against 37 us for 128 x 64 and 39 us for 64 x 64), or 256 x 256 (64 x
 //    128 wavefront tiles, 3-stage ring) when that still makes about 192 workgroups:
@@ -883,7 +919,10 @@ static hipError_t gemm_w4(const GemmArgs& a, hipStream_t s) {
 //    split into pieces of about 36 steps and into enough splits for about 192
 //    workgroups (at least 4 steps per split, at most 8 splits): 256 x 2048 x 1536
 //    q/k/v 12.0 us and 256 x 1536 x 1536 O 11.1 us with 2 splits, 256 x 1536 x 8960
-//    down 21.4 us with 4 (times include the reduction kernel). From 512 rows with at
+//    down 21.4 us with 4 (times include the reduction kernel); 129 to 256 rows with
+//    K >= 4096 (down): the two-stream kernel split into up to 16 K pieces with
+//    128-column groups (256 x 1536 x 8960: 18.1 us against 23.8 us for 64 x 64 tiles in
+//    4 pieces, without the reduction). From 512 rows with at
 //    least 128 K steps: 256 x 64 tiles with 8 wavefronts and K in pieces of 64 steps
 //    (512 x 2048 x 16384: 57 us against 75 us for 64 x 64). At most 64 rows: 64 x 32
 //    tiles with 4 wavefronts along M, splits for about 384 workgroups (63 x 1024 x
@@ -898,8 +937,9 @@ static void gated_go(const GemmArgs& a, hipStream_t s) {
     gemm_bf16_go<EPI, 64, 128, 64, 4, 2, 2, LO>(a, 1, a.K / 64, s);
   else if (a.M <= 64)
     gemm_bf16_go<EPI, 64, 32, 64, 4, 4, 1, LO>(a, 1, a.K / 64, s);
-  else if (a.M > 128 && a.M <= 256 && a.N % 32 == 0)
-    gemm_ws2_go<EPI, 6, LO ? 3 : 4, 8, LO>(a, 256, s);
+  else if (a.M > 128 && a.M <= 256 && a.N % 32 == 0 &&
+           gemm_ws2_go<EPI, 10, 4, 8, LO, 128>(a, 256, 1, s))
+    return;
   else if (a.M > 128 && a.N % 256 == 0 && ((a.M + 255) / 256) * (a.N / 256) >= 192)
     gemm_bf16_go<EPI, 256, 256, 32, 3, 4, 2, LO>(a, 1, a.K / 32, s);
   else if (a.M > 128 && a.N % 128 == 0)
@@ -962,6 +1002,20 @@ static hipError_t gemm_bf16(const GemmArgs& a, hipStream_t s) {
   // residual projection: always through the partial buffer and the reduction kernel
   if (a.ws == nullptr || (size_t)a.M * a.N > a.ws_elems) return hipErrorInvalidValue;
   if (a.N % 8 != 0 || a.N / 8 > 256 * kResidMaxChunks) return hipErrorInvalidValue;
+  // 129 to 256 rows with a long K (the down projection): the two-stream kernel with
+  // 128-column groups, K in up to 16 pieces
+  if (a.M > 128 && a.M <= 256 && ksteps_all >= 64 && a.N % 128 == 0) {
+    const int steps = a.K / 32;
+    int sp = kResidNormMaxSplits;
+    while (sp > 1 && (size_t)sp * a.M * a.N > a.ws_elems) --sp;
+    const int ks = (steps + sp - 1) / sp;
+    sp = (steps + ks - 1) / ks;
+    if (gemm_ws2_go<EPI_PARTIAL, 8, 6, 6, false>(a, 192, sp, s)) {
+      launch_k(resid_norm_kernel, dim3(a.M), dim3(256), 0, s, (const float*)a.ws, sp, a.M, a.N,
+               (float*)a.C, (bf16_t*)a.norm_out, (bf16_t*)a.norm_out_lo, a.norm_g, a.eps);
+      return hipGetLastError();
+    }
+  }
   if (tall) gemm_bf16_go<EPI_PARTIAL, 256, 64, 64, 3, 4, 2>(a, splits, ksteps, s);
   else if (skinny) gemm_bf16_go<EPI_PARTIAL, 64, 32, 64, 3, 4, 1>(a, splits, ksteps, s);
   else gemm_bf16_go<EPI_PARTIAL, 64, 64, 64, 3>(a, splits, ksteps, s);

@@ -216,11 +216,13 @@ hipError_t launch_rope_table(int64_t pos0, int n, const double* inv_freq, int ha
                              float2* tab, hipStream_t s);
 // x: the fp32 residual rows [n][H]; E and u in the activation type
 hipError_t launch_to_f32(const void* in, float* out, int64_t n, int dt, hipStream_t s);
-// action expert: h = x + time embedding of tau; then x += dt * RMSNorm(h)
-hipError_t launch_action_begin(const float* xa, float* h, int rows, int H, double tau,
-                               hipStream_t s);
-hipError_t launch_euler_step(float* xa, const float* h, const float* g, int rows, int H,
-                             float eps, float dt, hipStream_t s);
+// action expert: the time-embedding rows of tau_k = k * dt (k < n_steps), and the
+// boundary of two flow-matching iterations: optionally x += dt * RMSNorm(h), then,
+// if temb is given, h = x + temb and u (u_lo) = RMSNorm(h) (H a multiple of 4, <= 4096)
+hipError_t launch_flow_temb(float* temb, int n_steps, int H, double dt, hipStream_t s);
+hipError_t launch_flow_step(float* xa, float* h, const float* temb, const float* g, void* u,
+                            void* u_lo, int rows, int H, float eps, float dt, bool euler, int dtype,
+                            hipStream_t s);
 // one decode row: the token's embedding row (token_key non-null: the token is the
 // argmax key's id) and the RoPE table of position pos, in one launch
 hipError_t launch_embed_rope1(int token_scalar, const unsigned long long* token_key, const void* E,

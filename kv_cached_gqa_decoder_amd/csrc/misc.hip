@@ -384,47 +384,128 @@ hipError_t launch_rmsnorm(const void* x, const float* g, void* u, void* u_lo, in
 
 // ---------------------------------------------------------------------------
 // action expert ("Running VLAs at Real-time Speed", section 2: flow matching on
-// the action chunk). Time embedding of tau, width H: sin(tau w_j) for j < H/2,
-// cos(tau w_{j-H/2}) after, w_j = 2 pi / p_j, p_j = 0.004 * 1000^(j / (H/2 - 1)),
-// evaluated in fp64. h = x + temb(tau), fp32 [rows][H].
-__global__ void action_begin_kernel(const float* xa, float* h, int rows, int H, double tau) {
+// the action chunk). Time embedding of tau_k = k * dt, width H: sin(tau w_j) for
+// j < H/2, cos(tau w_{j-H/2}) after, w_j = 2 pi / p_j, p_j = 0.004 * 1000^(j / (H/2 - 1)),
+// evaluated in fp64 and stored in fp32, one row per iteration k < n_steps.
+__global__ void flow_temb_kernel(float* temb, int n_steps, int H, double dt) {
   const int half = H / 2;
-  const int64_t total = (int64_t)rows * H;
+  const int64_t total = (int64_t)n_steps * H;
   for (int64_t p = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; p < total;
        p += (int64_t)gridDim.x * blockDim.x) {
-    const int j = (int)(p % H);
+    const int k = (int)(p / H), j = (int)(p % H);
     const int jj = j < half ? j : j - half;
     const double period = 0.004 * pow(1000.0, (double)jj / (double)(half - 1));
-    const double ang = tau * (6.283185307179586 / period);
-    h[p] = xa[p] + (float)(j < half ? sin(ang) : cos(ang));
+    const double ang = ((double)k * dt) * (6.283185307179586 / period);
+    temb[p] = (float)(j < half ? sin(ang) : cos(ang));
   }
 }
-hipError_t launch_action_begin(const float* xa, float* h, int rows, int H, double tau,
-                               hipStream_t s) {
-  if (H < 4 || H % 2) return hipErrorInvalidValue;
-  launch_k(action_begin_kernel, dim3(grid_for((int64_t)rows * H, 256)), dim3(256), 0, s, xa, h,
-           rows, H, tau);
+hipError_t launch_flow_temb(float* temb, int n_steps, int H, double dt, hipStream_t s) {
+  if (H < 4 || H % 2 || n_steps < 1) return hipErrorInvalidValue;
+  launch_k(flow_temb_kernel, dim3(grid_for((int64_t)n_steps * H, 256)), dim3(256), 0, s, temb,
+           n_steps, H, dt);
   return hipGetLastError();
 }
 
-// Euler step x += dt * v with the velocity v = RMSNorm(h) (the expert's final
-// norm, no output projection); one wavefront per row, fp32
-__global__ __launch_bounds__(256) void euler_step_kernel(float* xa, const float* h, const float* g,
-                                                         int rows, int H, float eps, float dt) {
+// The boundary between two flow-matching iterations, one wavefront per action row
+// with the whole row in registers (NC chunks of 4 per lane):
+//   euler: x += dt * RMSNorm(h) (the velocity: the expert's final norm, no output
+//          projection), fp32;
+//   temb:  h = x + temb (the next iteration's input), then u = RMSNorm(h) in the
+//          activation type (bf16: with its low part), the first layer's input.
+template <typename T, int NC>
+__global__ __launch_bounds__(256) void flow_step_kernel(float* xa, float* h, const float* temb,
+                                                        const float* g, T* u, T* u_lo, int rows,
+                                                        int H, float eps, float dt, int euler) {
   const int lane = threadIdx.x & 63;
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (row >= rows) return;
-  const float* hr = h + (int64_t)row * H;
+  const int nq = H / 4;
   float* xr = xa + (int64_t)row * H;
-  float ss = 0.f;
-  for (int c = lane; c < H; c += 64) ss += hr[c] * hr[c];
-  ss = wave_sum(ss);
-  const float r = rsqrtf(ss / (float)H + eps);
-  for (int c = lane; c < H; c += 64) xr[c] += dt * (hr[c] * r * g[c]);
+  float* hr = h + (int64_t)row * H;
+  f32x4_t xv[NC], hv[NC], gv[NC];
+  // every load of the row first
+#pragma unroll
+  for (int i = 0; i < NC; ++i) {
+    const int c = lane + 64 * i;
+    if (c < nq) {
+      xv[i] = *(const f32x4_t*)(xr + 4 * c);
+      gv[i] = *(const f32x4_t*)(g + 4 * c);
+      hv[i] = euler ? *(const f32x4_t*)(hr + 4 * c) : f32x4_t{0.f, 0.f, 0.f, 0.f};
+    }
+  }
+  if (euler) {
+    float ss = 0.f;
+#pragma unroll
+    for (int i = 0; i < NC; ++i)
+      if (lane + 64 * i < nq)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) ss += hv[i][e] * hv[i][e];
+    ss = wave_sum(ss);
+    const float r = rsqrtf(ss / (float)H + eps);
+#pragma unroll
+    for (int i = 0; i < NC; ++i) {
+      const int c = lane + 64 * i;
+      if (c < nq) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) xv[i][e] += dt * (hv[i][e] * r * gv[i][e]);
+        *(f32x4_t*)(xr + 4 * c) = xv[i];
+      }
+    }
+  }
+  if (temb) {
+    float ss = 0.f;
+#pragma unroll
+    for (int i = 0; i < NC; ++i) {
+      const int c = lane + 64 * i;
+      if (c < nq) {
+        const f32x4_t t = *(const f32x4_t*)(temb + 4 * c);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          hv[i][e] = xv[i][e] + t[e];
+          ss += hv[i][e] * hv[i][e];
+        }
+        *(f32x4_t*)(hr + 4 * c) = hv[i];
+      }
+    }
+    ss = wave_sum(ss);
+    const float r = rsqrtf(ss / (float)H + eps);
+    T* ur = u + (int64_t)row * H;
+#pragma unroll
+    for (int i = 0; i < NC; ++i) {
+      const int c = lane + 64 * i;
+      if (c < nq) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float y = hv[i][e] * r * gv[i][e];
+          St<T>::st(ur, (size_t)c * 4 + e, y);
+          if constexpr (sizeof(T) == 2) {
+            if (u_lo)
+              u_lo[(int64_t)row * H + c * 4 + e] = f32_to_bf16(y - bf16_to_f32(f32_to_bf16(y)));
+          }
+        }
+      }
+    }
+  }
 }
-hipError_t launch_euler_step(float* xa, const float* h, const float* g, int rows, int H,
-                             float eps, float dt, hipStream_t s) {
-  launch_k(euler_step_kernel, dim3((rows + 3) / 4), dim3(256), 0, s, xa, h, g, rows, H, eps, dt);
+template <typename T>
+static void flow_step_go(float* xa, float* h, const float* temb, const float* g, void* u,
+                         void* u_lo, int rows, int H, float eps, float dt, int euler, hipStream_t s) {
+  const dim3 grid((rows + 3) / 4), block(256);
+  if (H <= 1024)
+    launch_k(flow_step_kernel<T, 4>, grid, block, 0, s, xa, h, temb, g, (T*)u, (T*)u_lo, rows, H,
+             eps, dt, euler);
+  else
+    launch_k(flow_step_kernel<T, 16>, grid, block, 0, s, xa, h, temb, g, (T*)u, (T*)u_lo, rows, H,
+             eps, dt, euler);
+}
+hipError_t launch_flow_step(float* xa, float* h, const float* temb, const float* g, void* u,
+                            void* u_lo, int rows, int H, float eps, float dt, bool euler, int dtype,
+                            hipStream_t s) {
+  if (H % 4 || H > 4096 || rows < 1 || (!euler && !temb)) return hipErrorInvalidValue;
+  if (dtype == DT_F32)
+    flow_step_go<float>(xa, h, temb, g, u, nullptr, rows, H, eps, dt, euler ? 1 : 0, s);
+  else
+    flow_step_go<bf16_t>(xa, h, temb, g, u, u_lo, rows, H, eps, dt, euler ? 1 : 0, s);
   return hipGetLastError();
 }
 

@@ -35,7 +35,7 @@ struct Err {
 [[noreturn]] void raise(vla_status st, const std::string& msg) { throw Err{st, msg}; }
 
 constexpr int kPartRows = 65536;   // attention split partials capacity (query rows x splits)
-constexpr int kGemmSplitsMax = 8;  // split-K partial capacity of the prefill residual projections
+constexpr int kGemmSplitsMax = 16; // split-K partial capacity of the prefill residual projections
 constexpr int kArgmaxParts = 2048; // head GEMV workgroups at most
 
 struct Segment {
@@ -94,6 +94,8 @@ struct vla_expert {
   int n_actions = 0;
   int* d_view = nullptr;         // block list of a pass: blk | ntok (num_blocks each)
   Staging st_view;
+  float* temb = nullptr;         // time-embedding rows of one denoise call
+  int temb_cap = 0;              // rows it holds
 };
 
 struct vla_model {
@@ -356,7 +358,7 @@ GemvArgs decode_gateup_args(vla_model* m, int l) {
 // the per-layer launches of one pass over n rows whose K/V go to logical slots
 // (cb0, cslot0 ...); rows = prefill chunk (n >= 1, matrix path) or decode (GEMV path)
 void run_layers(vla_model* m, const KvView& view, int n, int64_t pos0, int cb0, int cslot0,
-                bool decode, hipStream_t st, bool rope_ready = false) {
+                bool decode, hipStream_t st, bool rope_ready = false, bool norm_ready = false) {
   const vla_config& c = m->cfg;
   const int H = c.hidden, qd = c.n_heads * c.head_dim;
   const int nqkv = (c.n_heads + 2 * c.n_kv_heads) * c.head_dim;
@@ -440,7 +442,8 @@ void run_layers(vla_model* m, const KvView& view, int n, int64_t pos0, int cb0, 
       // write the next projection's normalised input u in the same pass; only
       // the first layer's input norm is a kernel of its own. fp32: plain norms.
       const bool bf16 = m->dt == DT_BF16;
-      if (!bf16 || l == 0)
+      // (norm_ready: the first layer's input norm is already in u)
+      if ((!bf16 || l == 0) && !(l == 0 && norm_ready))
         LAUNCH(m, VLA_K_RMSNORM, st,
                launch_rmsnorm(m->x, m->norm_ones, m->u, m->u_lo, n, H, c.rms_eps, m->dt, st));
       GemmArgs q;
@@ -1580,6 +1583,7 @@ vla_status vla_expert_create(vla_model* prefix, const vla_config* cfg, int32_t n
         c.block_tokens != pc.block_tokens)
       raise(VLA_E_INVALID, "invalid config: layers, KV heads, head_dim, act_dtype and "
                            "block_tokens must match the prefix model");
+    if (c.hidden > 4096) raise(VLA_E_INVALID, "invalid config: an expert's hidden must be <= 4096");
     c.num_blocks = pc.num_blocks;
     c.max_frames = 1;
     c.max_chunk = n_actions;
@@ -1649,11 +1653,21 @@ vla_status vla_expert_denoise(vla_expert* e, float* x, int32_t n_steps, double d
     v.last_ntok = h[cap + nb - 1];
     v.causal = 0;
     staging_upload(e->st_view, e->d_view, 2 * (size_t)cap * sizeof(int), st);
+    if (e->temb_cap < n_steps) {  // (grown on demand; the old table stays until destroy)
+      e->temb = (float*)dalloc(m, (size_t)n_steps * H * sizeof(float));
+      e->temb_cap = n_steps;
+    }
+    HIPCHK(launch_flow_temb(e->temb, n_steps, H, dt, st));
+    const float eps = m->cfg.rms_eps;
+    // iteration k: h = x + temb(tau_k), the layers, x += dt * RMSNorm(h); each boundary
+    // (the Euler step of k and the input of k + 1) is one launch
+    HIPCHK(launch_flow_step(x, (float*)m->x, e->temb, m->norm_ones, m->u, m->u_lo, n, H, eps,
+                            (float)dt, false, m->dt, st));
     for (int k = 0; k < n_steps; ++k) {
-      HIPCHK(launch_action_begin(x, (float*)m->x, n, H, k * dt, st));
-      run_layers(m, v, n, p->next_pos, cb0, 0, /*decode=*/false, st);
-      HIPCHK(launch_euler_step(x, (const float*)m->x, m->norm_ones, n, H, m->cfg.rms_eps,
-                               (float)dt, st));
+      run_layers(m, v, n, p->next_pos, cb0, 0, /*decode=*/false, st, false, /*norm_ready=*/true);
+      const float* next = k + 1 < n_steps ? e->temb + (size_t)(k + 1) * H : nullptr;
+      HIPCHK(launch_flow_step(x, (float*)m->x, next, m->norm_ones, m->u, m->u_lo, n, H, eps,
+                              (float)dt, true, m->dt, st));
     }
   });
 }
