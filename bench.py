@@ -312,6 +312,47 @@ def gpu_leg(args):
     return res
 
 
+def frame_leg(args):
+    """The Qwen2.5-1.5B-shaped frame step alone (for kernel traces and counter passes):
+    the 1024-token context, then per step a 256-token chunk prefill, 16 greedy decodes
+    and the layer-0 frame scoring; prints the median phase times."""
+    import numpy as np
+    import torch
+
+    import kv_cached_gqa_decoder_amd as vla
+    import synth
+
+    stream = torch.cuda.current_stream()
+    sh = stream.cuda_stream
+    p = vla.PRESETS["c2_qwen1p5b_bf16"]
+    m = vla.Model(vla.make_config(**p))
+    ctx_fid = -1
+    for c in range(CONTEXT // CHUNK):
+        ctx_fid = m.prefill_chunk(tokens=synth.token_ids(p["seed"], c, CHUNK, V), stream=sh)
+    _, xs = synth.embeddings(p["seed"], 0, CHUNK, H, "bf16")
+    chunk = torch.from_numpy(np.ascontiguousarray(xs).view(np.int16)).view(torch.bfloat16).cuda()
+    evs = []
+    for i in range(args.warmup + args.steps):
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+        m.kv_rollback(ctx_fid)
+        ev[0].record(stream)
+        m.prefill_chunk(embeds=chunk, n=CHUNK, stream=sh)
+        ev[1].record(stream)
+        tok = m.decode_step(1, stream=sh)
+        for _ in range(DECODES - 1):
+            tok = m.decode_step(tok, stream=sh)
+        ev[2].record(stream)
+        m.kv_score(0, stream=sh)
+        ev[3].record(stream)
+        if i >= args.warmup:
+            evs.append(ev)
+    torch.cuda.synchronize()
+    m.close()
+    med = lambda a, b: round(statistics.median(e[a].elapsed_time(e[b]) for e in evs), 4)
+    return {"prefill_ms": med(0, 1), "decode_ms_per_step": round(med(1, 2) / DECODES, 4),
+            "score_ms": med(2, 3)}
+
+
 def eviction_leg(args):
     """Semantic eviction workload: 128 raw frames of 64 tokens (layer-0 keys clustered
     around 16 centres, sigma 0.1), 512-block budget, 32 cycles of score-and-evict followed
@@ -800,7 +841,7 @@ def main():
     ap.add_argument("--no-longctx", action="store_true")
     ap.add_argument("--no-pi0", action="store_true")
     ap.add_argument("--cpu-layers", type=int, default=28)
-    ap.add_argument("--only", choices=["eviction", "longctx", "pi0"],
+    ap.add_argument("--only", choices=["frame", "eviction", "longctx", "pi0"],
                     help="run one leg alone and print its numbers (for kernel traces)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="first copy 256 MiB on the device three times (a plain copy of known "
@@ -819,7 +860,8 @@ def main():
         torch.cuda.synchronize()
         del a, b
     if args.only:
-        leg = {"eviction": eviction_leg, "longctx": longctx_leg, "pi0": pi0_leg}[args.only]
+        leg = {"frame": frame_leg, "eviction": eviction_leg, "longctx": longctx_leg,
+               "pi0": pi0_leg}[args.only]
         print(json.dumps(leg(args)), flush=True)
         return
     res = gpu_leg(args)

@@ -354,8 +354,9 @@ vla_status vla_profile_replay(vla_model* m, int32_t kernel_class, int32_t reps, 
                               double* ms_per_launch);
 
 /* Matrix-core throughput probe (a measured peak beside the published one): launches
- * `blocks` workgroups of 4 wavefronts, each wavefront running iters x 8 independent
- * v_mfma_f32_16x16x32_bf16 (16384 FLOP each) on register operands, times it with
+ * `blocks` workgroups of 4 wavefronts, each wavefront running iters x 4 independent
+ * v_mfma_f32_32x32x16_bf16 (32768 FLOP each; the 16x16x32 form issues at about half
+ * that rate on gfx950) on register operands, times it with
  * stream events and writes the achieved bf16 TFLOP/s. `out`: device float[blocks]
  * (one kept value per workgroup). Synchronises the stream. Errors: VLA_E_INVALID
  * (null pointers, blocks outside 1..65536, iters outside 1..1000000). */

@@ -205,7 +205,7 @@ hipError_t launch_weight_logical(const void* phys, void* out, int dt, int layout
                                  hipStream_t s);
 hipError_t launch_fill_f32(float* p, float v, int64_t n, hipStream_t s);
 // matrix-core throughput probe: `blocks` workgroups of 4 wavefronts, each wavefront
-// iters x 8 bf16 MFMAs of 16384 FLOP; out[blocks] receives one value per workgroup
+// iters x 4 bf16 MFMAs of 32768 FLOP; out[blocks] receives one value per workgroup
 hipError_t launch_mfma_peak(float* out, int blocks, int iters, hipStream_t s);
 // HBM read probe over `bytes` (a multiple of 16) at p; out: blocks * 256 words
 hipError_t launch_read_probe(const void* p, int64_t bytes, uint32_t* out, int blocks,

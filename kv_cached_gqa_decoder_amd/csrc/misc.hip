@@ -228,20 +228,23 @@ hipError_t launch_fill_f32(float* p, float v, int64_t n, hipStream_t s) {
 // traffic in the loop); one value per workgroup is stored so the work is kept.
 // 16384 FLOP per instruction.
 __global__ __launch_bounds__(256) void mfma_peak_kernel(float* out, int iters) {
-  // eight chains with distinct B operands and start values, so none can be merged
-  bf16x8_t a, b[8];
-  f32x4_t acc[8];
+  // four chains of v_mfma_f32_32x32x16_bf16 (32768 flops each) with distinct B operands
+  // and start values, so none can be merged; the 16 x 16 x 32 form issues at about
+  // half this rate on gfx950
+  bf16x8_t a, b[4];
+  f32x16_t acc[4];
   for (int i = 0; i < 8; ++i) a[i] = (__bf16)(0.001f * (float)((threadIdx.x + i) & 7));
-  for (int j = 0; j < 8; ++j) {
+  for (int j = 0; j < 4; ++j) {
     for (int i = 0; i < 8; ++i) b[j][i] = (__bf16)(0.002f * (float)((threadIdx.x * 3 + i + j) & 7));
-    acc[j] = f32x4_t{(float)j, 0.f, 0.f, 0.f};
+    for (int e = 0; e < 16; ++e) acc[j][e] = (float)(j + e);
   }
   for (int it = 0; it < iters; ++it) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b[j], acc[j], 0, 0, 0);
+    for (int j = 0; j < 4; ++j) acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b[j], acc[j], 0, 0, 0);
   }
   float t = 0.f;
-  for (int j = 0; j < 8; ++j) t += acc[j][0] + acc[j][1] + acc[j][2] + acc[j][3];
+  for (int j = 0; j < 4; ++j)
+    for (int e = 0; e < 16; ++e) t += acc[j][e];
   if (threadIdx.x == 0) out[blockIdx.x] = t;
 }
 // HBM read probe: 16-byte loads over n16 chunks, 8 independent loads in flight per

@@ -1466,7 +1466,7 @@ vla_status vla_probe_mfma_peak(float* out, int32_t blocks, int32_t iters, void* 
     HIPCHK(hipEventElapsedTime(&ms, e0, e1));
     HIPCHK(hipEventDestroy(e0));
     HIPCHK(hipEventDestroy(e1));
-    const double flop = (double)blocks * 4.0 * (double)iters * 8.0 * 16384.0;
+    const double flop = (double)blocks * 4.0 * (double)iters * 4.0 * 32768.0;
     *out_tflops = flop / ((double)ms * 1e-3) / 1e12;
   });
 }
