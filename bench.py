@@ -686,6 +686,43 @@ def pi0_leg(args):
     for i in range(reps):
         step(evs[i])
     torch.cuda.synchronize()
+    # the same frames through the overlapped prefix / expert streams: frame t's prefill
+    # beside the expert's run on the newest finished prefix; wall time per frame with
+    # 1 and 2 expert runs per frame, and sequentially on one stream for comparison
+    pl = None
+
+    def frames(n, acts, piped):
+        t0 = time.perf_counter()
+        for _ in range(n):
+            if piped:
+                pl.prefill(img, P0_PREFIX, stream)
+            else:
+                m.kv_rollback(-1)
+                m.prefill_chunk(embeds=img, n=P0_PREFIX, stream=sh)
+            for _ in range(acts):
+                x.copy_(noise)
+                if piped:
+                    pl.act(x, n_steps=AE_STEPS, stream=stream)
+                else:
+                    e.denoise(x, n_steps=AE_STEPS, stream=sh)
+        if piped:
+            pl.sync()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) * 1e3 / n
+
+    overlap = {}
+    for acts in (1, 2):
+        overlap[f"{acts}_runs_per_frame"] = {
+            "one_stream_ms_per_frame": round(statistics.median(frames(8, acts, False)
+                                                               for _ in range(3)), 3)}
+    pl = vla.Pipeline(m, e)  # (the pair is used only through the pipeline from here)
+    for acts in (1, 2):
+        frames(2, acts, True)
+        overlap[f"{acts}_runs_per_frame"]["overlapped_ms_per_frame"] = round(
+            statistics.median(frames(8, acts, True) for _ in range(3)), 3)
+    overlap["runs_on_older_prefix"] = pl.stats()["acts_on_older"]
+    overlap["runs"] = pl.stats()["acts"]
+    pl.close()
     e.close()
     m.close()
     pre = statistics.median(ev[0].elapsed_time(ev[1]) for ev in evs)
@@ -694,6 +731,7 @@ def pi0_leg(args):
     ab = pi0_expert_bytes()
     it = ae / AE_STEPS
     return {
+        "pi0_overlapped_streams": overlap,
         "pi0_step_ms": round(pre + ae, 3),
         "pi0_prefix_prefill_ms": round(pre, 3),
         "pi0_prefix_prefill_mfma_frac": round(fl / (pre * 1e-3) / (PEAK_BF16_TFLOPS * 1e12), 4),

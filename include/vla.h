@@ -120,8 +120,18 @@ typedef struct vla_expert vla_expert;
  * VLA_E_HIP (allocation or launch failure). */
 vla_status vla_model_create(const vla_config* cfg, vla_model** out);
 
-/* Free everything the handle owns (synchronises the device). NULL is a no-op. */
+/* Free everything the handle owns (synchronises the device). NULL is a no-op.
+ * Weights shared with sibling models are freed with the last model using them. */
 void vla_model_destroy(vla_model* m);
+
+/* A second model over the same weights ("Running VLAs at Real-time Speed",
+ * section 6.1: a second prefix state, filled while the first one is read): the
+ * source's config, its own KV pool, tables and scratch, and the source's
+ * embedding, output head and projection weights, read-only and shared (kept
+ * until the last model using them is destroyed, in any order). The source is
+ * not modified. Synchronises the device. Errors: VLA_E_INVALID (NULL src or
+ * out), VLA_E_HIP. */
+vla_status vla_model_create_sibling(const vla_model* src, vla_model** out);
 
 /* Append one frame of n tokens at the next n positions and run the whole
  * forward over it ("Rebuilding Kshipra Around Memory", section 4).
@@ -383,6 +393,10 @@ vla_status vla_probe_read_bandwidth(int64_t bytes, int32_t reps, void* stream, d
  * shapes), VLA_E_NO_BLOCKS (no room in the prefix pool), VLA_E_HIP. */
 vla_status vla_expert_create(vla_model* prefix, const vla_config* cfg, int32_t n_actions,
                              vla_expert** out);
+/* An expert with src's config, chunk size and (shared, read-only) weights,
+ * bound to `prefix` (which must satisfy vla_expert_create's conditions, e.g. a
+ * sibling of src's prefix model). Errors as vla_expert_create. */
+vla_status vla_expert_create_sibling(vla_model* prefix, const vla_expert* src, vla_expert** out);
 void vla_expert_destroy(vla_expert* e);
 
 /* Flow-matching Euler loop on the action chunk x (device fp32 [n_actions][hidden],
@@ -396,6 +410,46 @@ void vla_expert_destroy(vla_expert* e);
  * allocates the table of the n_steps time embeddings (n_steps * hidden floats,
  * kept until destroy). Errors: VLA_E_INVALID (null x, n_steps < 1, dt <= 0). */
 vla_status vla_expert_denoise(vla_expert* e, float* x, int32_t n_steps, double dt, void* stream);
+
+/* ---- Overlapped prefix and expert streams ----------------------------------
+ * "Running VLAs at Real-time Speed", section 6.1: the compute-bound prefix model
+ * and the bandwidth-bound action expert run on two streams, the expert working
+ * from the newest prefix K/V that is complete while the next frame's prefill
+ * runs. A pipeline double-buffers the prefix state: the caller's (prefix,
+ * expert) pair and a sibling pair over the same weights (created here, freed by
+ * destroy). Frame t is prefilled (from scratch, positions 0..n-1) into buffer
+ * t % 2 on the pipeline's prefix stream, after every action run that read that
+ * buffer has finished. An action run (vla_expert_denoise on a caller chunk)
+ * goes on the pipeline's expert stream and uses the newest buffer whose
+ * prefill has finished, or, if none has, waits on the device for the older
+ * submitted one. Both streams are created with the default priority. Calls
+ * order themselves after the caller's `stream` (its inputs are ready there),
+ * and the caller's stream waits for each action run, so x can be read there
+ * right after vla_pipeline_act returns; embeds must stay unchanged until the
+ * next vla_pipeline_sync. The caller must not use the prefix model or the
+ * expert directly while the pipeline exists. One host thread at a time. */
+typedef struct vla_pipeline vla_pipeline;
+/* Errors: VLA_E_INVALID (NULL argument, expert not bound to prefix),
+ * VLA_E_NO_BLOCKS / VLA_E_HIP (the sibling pair could not be created). */
+vla_status vla_pipeline_create(vla_model* prefix, vla_expert* expert, vla_pipeline** out);
+/* Synchronises both streams, then frees the sibling pair, streams and events. */
+void vla_pipeline_destroy(vla_pipeline* p);
+/* Prefill n rows of device embeddings ([n][hidden], act_dtype) as a new frame;
+ * out_frame (nullable) receives its number (0, 1, ...). Asynchronous.
+ * Errors: VLA_E_INVALID (NULL, n outside 1..max_chunk), VLA_E_HIP. */
+vla_status vla_pipeline_prefill(vla_pipeline* p, const void* embeds, int32_t n, void* stream,
+                                int64_t* out_frame);
+/* One action run on the device fp32 chunk x (as vla_expert_denoise);
+ * out_frame (nullable) receives the frame whose prefix K/V it used.
+ * Errors: VLA_E_INVALID, VLA_E_STATE (no frame submitted yet), VLA_E_HIP. */
+vla_status vla_pipeline_act(vla_pipeline* p, float* x, int32_t n_steps, double dt, void* stream,
+                            int64_t* out_frame);
+/* Wait for both streams. */
+vla_status vla_pipeline_sync(vla_pipeline* p);
+/* Counts: prefills, action runs, and action runs that used a frame older than
+ * the newest one submitted (each pointer nullable). */
+vla_status vla_pipeline_stats(const vla_pipeline* p, int64_t* prefills, int64_t* acts,
+                              int64_t* acts_on_older);
 
 /* Host-only LIFO block pool ("Rebuilding Kshipra Around Memory", section 1):
  * the free-list starts as [0 .. n-1] so the first pop returns n-1; released

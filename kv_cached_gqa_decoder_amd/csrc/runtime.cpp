@@ -6,6 +6,7 @@
 
 #include <algorithm>
 #include <cmath>
+#include <memory>
 #include <string>
 #include <vector>
 
@@ -96,6 +97,30 @@ struct vla_expert {
   Staging st_view;
   float* temb = nullptr;         // time-embedding rows of one denoise call
   int temb_cap = 0;              // rows it holds
+  // a denoise loop captured as a graph (replayed while these arguments stay the same)
+  struct GraphKey {
+    const float* x = nullptr;
+    int n_steps = 0, nb = 0, last_ntok = 0, cb0 = 0;
+    double dt = 0.0;
+    int64_t pos = 0;
+    bool operator==(const GraphKey& o) const {
+      return x == o.x && n_steps == o.n_steps && nb == o.nb && last_ntok == o.last_ntok &&
+             cb0 == o.cb0 && dt == o.dt && pos == o.pos;
+    }
+  };
+  hipGraphExec_t gexec = nullptr;
+  GraphKey gkey;
+};
+
+// device memory of one set of weights: shared by every model built over it (sibling
+// models and experts) and freed with the last of them
+struct WeightStore {
+  int dev = 0;
+  std::vector<void*> allocs;
+  ~WeightStore() {
+    (void)hipSetDevice(dev);
+    for (void* p : allocs) (void)hipFree(p);
+  }
 };
 
 struct vla_model {
@@ -106,7 +131,8 @@ struct vla_model {
   size_t esz = 2;
   KvGeom geom{};
 
-  // weights (physical layouts, see kernels.hpp)
+  // weights (physical layouts, see kernels.hpp), in a store this model may share
+  std::shared_ptr<WeightStore> wstore;
   void* embed = nullptr;
   void* head = nullptr;
   std::vector<void*> wqkv, wo, wgu, wdown;
@@ -200,6 +226,13 @@ void* dalloc(vla_model* m, size_t bytes) {
   void* p = nullptr;
   HIPCHK(hipMalloc(&p, bytes < 256 ? 256 : bytes));
   m->allocs.push_back(p);
+  return p;
+}
+// weight memory: in the model's weight store
+void* walloc(vla_model* m, size_t bytes) {
+  void* p = nullptr;
+  HIPCHK(hipMalloc(&p, bytes < 256 ? 256 : bytes));
+  m->wstore->allocs.push_back(p);
   return p;
 }
 
@@ -756,7 +789,9 @@ void validate_cfg(const vla_config* c) {
   if ((int64_t)c->vocab * c->hidden > ((int64_t)1 << 40)) bad("vocab*hidden too large");
 }
 
-void init_weights(vla_model* m) {
+// the seeded projection, embedding and head weights (own_weights), then the norm
+// weights and the RoPE inverse frequencies
+void init_weights(vla_model* m, bool own_weights) {
   const vla_config& c = m->cfg;
   const int H = c.hidden, d = c.head_dim, hq = c.n_heads, hkv = c.n_kv_heads;
   const hipStream_t st = nullptr;
@@ -772,12 +807,12 @@ void init_weights(vla_model* m) {
       HIPCHK(launch_init_weight(out, m->dt, layout, rows, cols, c.seed, sa, sb, sc, hq, hkv, d,
                                 c.init_std, st));
   };
-  if (c.vocab > 0) {
+  if (own_weights && c.vocab > 0) {
     HIPCHK(launch_init_weight(m->embed, m->dt, LAYOUT_PLAIN, c.vocab, H, c.seed, 1, 1, 1, hq, hkv,
                               d, c.init_std, st));
     proj(m->head, LAYOUT_PLAIN, c.vocab, H, 2, 2, 2);
   }
-  for (int l = 0; l < c.n_layers; ++l) {
+  for (int l = 0; own_weights && l < c.n_layers; ++l) {
     proj(m->wqkv[l], LAYOUT_QKV, (int64_t)(hq + 2 * hkv) * d, H, sid(l, 1), sid(l, 2), sid(l, 3));
     proj(m->wo[l], LAYOUT_PLAIN, H, (int64_t)hq * d, sid(l, 4), sid(l, 4), sid(l, 4));
     proj(m->wgu[l], LAYOUT_GATEUP, 2 * (int64_t)c.ffn, H, sid(l, 5), sid(l, 6), sid(l, 6));
@@ -803,8 +838,10 @@ void destroy(vla_model* m) {
 }
 
 // allocate and initialise a model; `borrow` (non-null): the KV pool and its
-// geometry belong to that model (an action expert writing into its prefix's pool)
-void build_model(vla_model* m, const vla_config& cfg, const vla_model* borrow) {
+// geometry belong to that model (an action expert writing into its prefix's pool);
+// `share` (non-null, same config): the weights are that model's (a sibling)
+void build_model(vla_model* m, const vla_config& cfg, const vla_model* borrow,
+                 const vla_model* share = nullptr) {
   m->cfg = cfg;
   HIPCHK(hipGetDevice(&m->dev));
   const vla_config& c = m->cfg;
@@ -819,13 +856,25 @@ void build_model(vla_model* m, const vla_config& cfg, const vla_model* borrow) {
   auto wbytes = [&](size_t rows, size_t cols) {
     return m->wf == WF_INT4 ? rows * cols / 2 + rows * (cols / 128) * 2 : rows * cols * e;
   };
-  m->embed = dalloc(m, (size_t)c.vocab * H * e);
-  m->head = dalloc(m, wbytes(c.vocab, H));
-  for (int l = 0; l < c.n_layers; ++l) {
-    m->wqkv.push_back(dalloc(m, wbytes((hq + 2 * hkv) * d, H)));
-    m->wo.push_back(dalloc(m, wbytes(H, hq * d)));
-    m->wgu.push_back(dalloc(m, wbytes(2 * (size_t)c.ffn, H)));
-    m->wdown.push_back(dalloc(m, wbytes(H, c.ffn)));
+  if (share) {
+    m->wstore = share->wstore;
+    m->embed = share->embed;
+    m->head = share->head;
+    m->wqkv = share->wqkv;
+    m->wo = share->wo;
+    m->wgu = share->wgu;
+    m->wdown = share->wdown;
+  } else {
+    m->wstore = std::make_shared<WeightStore>();
+    m->wstore->dev = m->dev;
+    m->embed = walloc(m, (size_t)c.vocab * H * e);
+    m->head = walloc(m, wbytes(c.vocab, H));
+    for (int l = 0; l < c.n_layers; ++l) {
+      m->wqkv.push_back(walloc(m, wbytes((hq + 2 * hkv) * d, H)));
+      m->wo.push_back(walloc(m, wbytes(H, hq * d)));
+      m->wgu.push_back(walloc(m, wbytes(2 * (size_t)c.ffn, H)));
+      m->wdown.push_back(walloc(m, wbytes(H, c.ffn)));
+    }
   }
   m->norm_ones = (float*)dalloc(m, H * sizeof(float));
   m->inv_freq = (double*)dalloc(m, d / 2 * sizeof(double));
@@ -881,7 +930,7 @@ void build_model(vla_model* m, const vla_config& cfg, const vla_model* borrow) {
     m->d_bar = (unsigned long long*)dalloc(m, 2 * sizeof(unsigned long long));
     HIPCHK(hipMemset(m->d_bar, 0, 2 * sizeof(unsigned long long)));
   }
-  init_weights(m);
+  init_weights(m, share == nullptr);
 }
 
 }  // namespace
@@ -901,6 +950,25 @@ vla_status vla_model_create(const vla_config* cfg, vla_model** out) {
     validate_cfg(cfg);
     m = new vla_model();
     build_model(m, *cfg, nullptr);
+    *out = m;
+  });
+  if (st != VLA_OK && m) {
+    std::string keep = g_err;
+    destroy(m);
+    g_err = keep;
+  }
+  return st;
+}
+
+vla_status vla_model_create_sibling(const vla_model* src, vla_model** out) {
+  vla_model* m = nullptr;
+  vla_status st = guarded([&] {
+    if (!out) raise(VLA_E_INVALID, "out is NULL");
+    *out = nullptr;
+    if (!src) raise(VLA_E_INVALID, "null source model");
+    HIPCHK(hipSetDevice(src->dev));
+    m = new vla_model();
+    build_model(m, src->cfg, nullptr, src);
     *out = m;
   });
   if (st != VLA_OK && m) {
@@ -1566,8 +1634,10 @@ vla_status vla_profile_read(vla_model* m, double* total_ms, int32_t* launches) {
 }
 
 // ---- action expert ("Running VLAs at Real-time Speed", section 2) ----
-vla_status vla_expert_create(vla_model* prefix, const vla_config* cfg, int32_t n_actions,
-                             vla_expert** out) {
+namespace {
+// an expert bound to `prefix`; `share` (non-null): with that expert's weights
+vla_status expert_create(vla_model* prefix, const vla_config* cfg, int32_t n_actions,
+                         const vla_expert* share, vla_expert** out) {
   vla_expert* e = nullptr;
   vla_status st = guarded([&] {
     if (!out) raise(VLA_E_INVALID, "out is NULL");
@@ -1593,7 +1663,7 @@ vla_status vla_expert_create(vla_model* prefix, const vla_config* cfg, int32_t n
     e->prefix = prefix;
     e->n_actions = n_actions;
     e->m = new vla_model();
-    build_model(e->m, c, prefix);
+    build_model(e->m, c, prefix, share ? share->m : nullptr);
     const int nres = (n_actions + c.block_tokens - 1) / c.block_tokens;
     if (!prefix->pool.alloc(nres, &e->reserved))
       raise(VLA_E_NO_BLOCKS, "no free blocks in the prefix pool for the action chunk's K/V");
@@ -1608,9 +1678,25 @@ vla_status vla_expert_create(vla_model* prefix, const vla_config* cfg, int32_t n
   }
   return st;
 }
+}  // namespace
+
+vla_status vla_expert_create(vla_model* prefix, const vla_config* cfg, int32_t n_actions,
+                             vla_expert** out) {
+  return expert_create(prefix, cfg, n_actions, nullptr, out);
+}
+
+vla_status vla_expert_create_sibling(vla_model* prefix, const vla_expert* src, vla_expert** out) {
+  if (!src) {
+    g_err = "null source expert";
+    if (out) *out = nullptr;
+    return VLA_E_INVALID;
+  }
+  return expert_create(prefix, &src->m->cfg, src->n_actions, src, out);
+}
 
 void vla_expert_destroy(vla_expert* e) {
   if (!e) return;
+  if (e->gexec) (void)hipGraphExecDestroy(e->gexec);
   if (e->m) destroy(e->m);
   staging_free(e->st_view);
   if (!e->reserved.empty()) {
@@ -1620,55 +1706,263 @@ void vla_expert_destroy(vla_expert* e) {
   delete e;
 }
 
-vla_status vla_expert_denoise(vla_expert* e, float* x, int32_t n_steps, double dt, void* stream) {
-  return guarded([&] {
-    if (!e || !x) raise(VLA_E_INVALID, "null argument");
-    if (n_steps < 1 || !(dt > 0.0) || !std::isfinite(dt))
-      raise(VLA_E_INVALID, "need n_steps >= 1 and a finite dt > 0");
-    vla_model* p = e->prefix;
-    vla_model* m = e->m;
-    HIPCHK(hipSetDevice(m->dev));
-    const hipStream_t st = (hipStream_t)stream;
-    const int bt = bt_of(p), n = e->n_actions, H = m->cfg.hidden, cap = p->cfg.num_blocks;
-    // the blocks of every pass: the prefix's resident blocks in logical order, then
-    // the chunk's own (its K/V are rewritten by every pass)
-    int* h = (int*)staging_acquire(e->st_view);
-    int nb = 0;
-    for (const auto& sg : p->segs)
-      for (size_t i = 0; i < sg.blocks.size(); ++i) {
-        h[nb] = sg.blocks[i];
-        h[cap + nb] = std::min(bt, sg.ntok - (int)i * bt);
-        ++nb;
-      }
-    const int cb0 = nb;
-    for (size_t i = 0; i < e->reserved.size(); ++i) {
-      h[nb] = e->reserved[i];
-      h[cap + nb] = std::min(bt, n - (int)i * bt);
+namespace {
+// The Euler loop on x. graph: the launches are captured once into a graph on `st`
+// (not the null stream) and replayed while the loop's arguments stay the same; the
+// block list is uploaded outside the graph on every call (the kernels read it).
+void expert_denoise(vla_expert* e, float* x, int32_t n_steps, double dt, hipStream_t st,
+                    bool graph) {
+  if (!e || !x) raise(VLA_E_INVALID, "null argument");
+  if (n_steps < 1 || !(dt > 0.0) || !std::isfinite(dt))
+    raise(VLA_E_INVALID, "need n_steps >= 1 and a finite dt > 0");
+  vla_model* p = e->prefix;
+  vla_model* m = e->m;
+  HIPCHK(hipSetDevice(m->dev));
+  const int bt = bt_of(p), n = e->n_actions, H = m->cfg.hidden, cap = p->cfg.num_blocks;
+  // the blocks of every pass: the prefix's resident blocks in logical order, then
+  // the chunk's own (its K/V are rewritten by every pass)
+  int* h = (int*)staging_acquire(e->st_view);
+  int nb = 0;
+  for (const auto& sg : p->segs)
+    for (size_t i = 0; i < sg.blocks.size(); ++i) {
+      h[nb] = sg.blocks[i];
+      h[cap + nb] = std::min(bt, sg.ntok - (int)i * bt);
       ++nb;
     }
-    KvView v;
-    v.blk = e->d_view;
-    v.ntok = e->d_view + cap;
-    v.nlb = nb;
-    v.last_ntok = h[cap + nb - 1];
-    v.causal = 0;
-    staging_upload(e->st_view, e->d_view, 2 * (size_t)cap * sizeof(int), st);
-    if (e->temb_cap < n_steps) {  // (grown on demand; the old table stays until destroy)
-      e->temb = (float*)dalloc(m, (size_t)n_steps * H * sizeof(float));
-      e->temb_cap = n_steps;
+  const int cb0 = nb;
+  for (size_t i = 0; i < e->reserved.size(); ++i) {
+    h[nb] = e->reserved[i];
+    h[cap + nb] = std::min(bt, n - (int)i * bt);
+    ++nb;
+  }
+  KvView v;
+  v.blk = e->d_view;
+  v.ntok = e->d_view + cap;
+  v.nlb = nb;
+  v.last_ntok = h[cap + nb - 1];
+  v.causal = 0;
+  staging_upload(e->st_view, e->d_view, 2 * (size_t)cap * sizeof(int), st);
+  if (e->temb_cap < n_steps) {  // (grown on demand; the old table stays until destroy)
+    if (e->gexec) {              // a captured loop may refer to the old table
+      HIPCHK(hipGraphExecDestroy(e->gexec));
+      e->gexec = nullptr;
     }
+    e->temb = (float*)dalloc(m, (size_t)n_steps * H * sizeof(float));
+    e->temb_cap = n_steps;
+  }
+  const float eps = m->cfg.rms_eps;
+  const int64_t pos = p->next_pos;
+  auto enqueue = [&] {
     HIPCHK(launch_flow_temb(e->temb, n_steps, H, dt, st));
-    const float eps = m->cfg.rms_eps;
     // iteration k: h = x + temb(tau_k), the layers, x += dt * RMSNorm(h); each boundary
     // (the Euler step of k and the input of k + 1) is one launch
     HIPCHK(launch_flow_step(x, (float*)m->x, e->temb, m->norm_ones, m->u, m->u_lo, n, H, eps,
                             (float)dt, false, m->dt, st));
     for (int k = 0; k < n_steps; ++k) {
-      run_layers(m, v, n, p->next_pos, cb0, 0, /*decode=*/false, st, false, /*norm_ready=*/true);
+      run_layers(m, v, n, pos, cb0, 0, /*decode=*/false, st, false, /*norm_ready=*/true);
       const float* next = k + 1 < n_steps ? e->temb + (size_t)(k + 1) * H : nullptr;
       HIPCHK(launch_flow_step(x, (float*)m->x, next, m->norm_ones, m->u, m->u_lo, n, H, eps,
                               (float)dt, true, m->dt, st));
     }
+  };
+  if (!graph || st == nullptr || m->prof_cls != VLA_K_NONE) {
+    enqueue();
+    return;
+  }
+  vla_expert::GraphKey key;
+  key.x = x;
+  key.n_steps = n_steps;
+  key.nb = nb;
+  key.last_ntok = v.last_ntok;
+  key.cb0 = cb0;
+  key.dt = dt;
+  key.pos = pos;
+  if (!e->gexec || !(key == e->gkey)) {
+    if (e->gexec) {
+      HIPCHK(hipGraphExecDestroy(e->gexec));
+      e->gexec = nullptr;
+    }
+    hipGraph_t g = nullptr;
+    HIPCHK(hipStreamBeginCapture(st, hipStreamCaptureModeThreadLocal));
+    try {
+      enqueue();
+    } catch (...) {
+      hipGraph_t junk = nullptr;
+      (void)hipStreamEndCapture(st, &junk);
+      if (junk) (void)hipGraphDestroy(junk);
+      throw;
+    }
+    HIPCHK(hipStreamEndCapture(st, &g));
+    const hipError_t ie = hipGraphInstantiate(&e->gexec, g, nullptr, nullptr, 0);
+    (void)hipGraphDestroy(g);
+    if (ie != hipSuccess) e->gexec = nullptr;
+    HIPCHK(ie);
+    e->gkey = key;
+  }
+  HIPCHK(hipGraphLaunch(e->gexec, st));
+}
+}  // namespace
+
+vla_status vla_expert_denoise(vla_expert* e, float* x, int32_t n_steps, double dt, void* stream) {
+  return guarded([&] { expert_denoise(e, x, n_steps, dt, (hipStream_t)stream, false); });
+}
+
+// ---- overlapped prefix and expert streams ("Running VLAs at Real-time Speed",
+// section 6.1: the bandwidth-bound expert and the compute-bound prefix model on two
+// streams, the expert iterating on the newest finished prefix K/V) ----
+struct vla_pipeline {
+  vla_model* P[2] = {nullptr, nullptr};   // [0] the caller's prefix model, [1] its sibling
+  vla_expert* E[2] = {nullptr, nullptr};  // [0] the caller's expert, [1] its sibling on P[1]
+  hipStream_t sv = nullptr, sa = nullptr; // prefix stream, expert stream (default priority)
+  hipEvent_t pre_done[2] = {nullptr, nullptr};  // the latest prefill into buffer b has finished
+  hipEvent_t act_done[2] = {nullptr, nullptr};  // the latest action run on buffer b has finished
+  hipEvent_t in_ready = nullptr;                // the caller's inputs are ready (caller's stream)
+  int64_t frame[2] = {-1, -1};                  // frame held (or being written) by buffer b
+  bool acted[2] = {false, false};               // act_done[b] has been recorded
+  int64_t next_frame = 0;
+  int64_t prefills = 0, acts = 0, acts_on_older = 0;
+};
+
+namespace {
+void pipeline_free(vla_pipeline* p) {
+  if (!p) return;
+  if (p->sv) (void)hipStreamSynchronize(p->sv);
+  if (p->sa) (void)hipStreamSynchronize(p->sa);
+  if (p->E[1]) vla_expert_destroy(p->E[1]);
+  if (p->P[1]) destroy(p->P[1]);
+  for (int b = 0; b < 2; ++b) {
+    if (p->pre_done[b]) (void)hipEventDestroy(p->pre_done[b]);
+    if (p->act_done[b]) (void)hipEventDestroy(p->act_done[b]);
+  }
+  if (p->in_ready) (void)hipEventDestroy(p->in_ready);
+  if (p->sv) (void)hipStreamDestroy(p->sv);
+  if (p->sa) (void)hipStreamDestroy(p->sa);
+  delete p;
+}
+}  // namespace
+
+vla_status vla_pipeline_create(vla_model* prefix, vla_expert* expert, vla_pipeline** out) {
+  vla_pipeline* p = nullptr;
+  vla_status st = guarded([&] {
+    if (!out) raise(VLA_E_INVALID, "out is NULL");
+    *out = nullptr;
+    if (!prefix || !expert) raise(VLA_E_INVALID, "null argument");
+    if (expert->prefix != prefix) raise(VLA_E_INVALID, "the expert is not bound to this prefix model");
+    HIPCHK(hipSetDevice(prefix->dev));
+    p = new vla_pipeline();
+    p->P[0] = prefix;
+    p->E[0] = expert;
+    {
+      vla_model* m = nullptr;
+      const vla_status ms = vla_model_create_sibling(prefix, &m);
+      if (ms != VLA_OK) raise(ms, g_err);
+      p->P[1] = m;
+      vla_expert* e = nullptr;
+      const vla_status es = vla_expert_create_sibling(m, expert, &e);
+      if (es != VLA_OK) raise(es, g_err);
+      p->E[1] = e;
+    }
+    HIPCHK(hipStreamCreateWithFlags(&p->sv, hipStreamNonBlocking));
+    HIPCHK(hipStreamCreateWithFlags(&p->sa, hipStreamNonBlocking));
+    for (int b = 0; b < 2; ++b) {
+      HIPCHK(hipEventCreateWithFlags(&p->pre_done[b], hipEventDisableTiming));
+      HIPCHK(hipEventCreateWithFlags(&p->act_done[b], hipEventDisableTiming));
+    }
+    HIPCHK(hipEventCreateWithFlags(&p->in_ready, hipEventDisableTiming));
+    *out = p;
+  });
+  if (st != VLA_OK && p) {
+    std::string keep = g_err;
+    pipeline_free(p);
+    g_err = keep;
+  }
+  return st;
+}
+
+void vla_pipeline_destroy(vla_pipeline* p) { pipeline_free(p); }
+
+vla_status vla_pipeline_prefill(vla_pipeline* p, const void* embeds, int32_t n, void* stream,
+                                int64_t* out_frame) {
+  return guarded([&] {
+    if (!p || !embeds) raise(VLA_E_INVALID, "null argument");
+    if (n < 1 || n > p->P[0]->cfg.max_chunk) raise(VLA_E_INVALID, "chunk length out of range");
+    HIPCHK(hipSetDevice(p->P[0]->dev));
+    const int b = (int)(p->next_frame & 1);
+    // the caller's embeddings are ready; no action run still reads this buffer
+    HIPCHK(hipEventRecord(p->in_ready, (hipStream_t)stream));
+    HIPCHK(hipStreamWaitEvent(p->sv, p->in_ready, 0));
+    if (p->acted[b]) HIPCHK(hipStreamWaitEvent(p->sv, p->act_done[b], 0));
+    vla_model* m = p->P[b];
+    p->frame[b] = -1;  // (no frame here until this prefill is enqueued)
+    vla_status s = vla_kv_rollback(m, -1);
+    if (s != VLA_OK) raise(s, g_err);
+    int32_t fid = -1;
+    s = vla_prefill_chunk(m, nullptr, embeds, n, &fid, p->sv);
+    if (s != VLA_OK) raise(s, g_err);
+    HIPCHK(hipEventRecord(p->pre_done[b], p->sv));
+    p->frame[b] = p->next_frame++;
+    ++p->prefills;
+    if (out_frame) *out_frame = p->frame[b];
+  });
+}
+
+vla_status vla_pipeline_act(vla_pipeline* p, float* x, int32_t n_steps, double dt, void* stream,
+                            int64_t* out_frame) {
+  return guarded([&] {
+    if (!p || !x) raise(VLA_E_INVALID, "null argument");
+    if (p->frame[0] < 0 && p->frame[1] < 0) raise(VLA_E_STATE, "no prefix submitted yet");
+    HIPCHK(hipSetDevice(p->P[0]->dev));
+    // the newest buffer whose prefill has finished; if neither has, the older one,
+    // waited for on the expert stream
+    int order[2];
+    const bool first_newer = p->frame[0] > p->frame[1];
+    order[0] = first_newer ? 0 : 1;
+    order[1] = 1 - order[0];
+    int b = -1;
+    for (int i = 0; i < 2 && b < 0; ++i) {
+      const int c = order[i];
+      if (p->frame[c] < 0) continue;
+      const hipError_t q = hipEventQuery(p->pre_done[c]);
+      if (q == hipSuccess) b = c;
+      else if (q != hipErrorNotReady) HIPCHK(q);
+    }
+    bool wait = false;
+    if (b < 0) {
+      b = p->frame[order[1]] >= 0 ? order[1] : order[0];
+      wait = true;
+    }
+    HIPCHK(hipEventRecord(p->in_ready, (hipStream_t)stream));
+    HIPCHK(hipStreamWaitEvent(p->sa, p->in_ready, 0));
+    if (wait) HIPCHK(hipStreamWaitEvent(p->sa, p->pre_done[b], 0));
+    // the loop's ~1,600 launches from one graph: the host would otherwise spend about as
+    // long enqueueing them as the device spends running them, and fall behind
+    expert_denoise(p->E[b], x, n_steps, dt, p->sa, /*graph=*/true);
+    HIPCHK(hipEventRecord(p->act_done[b], p->sa));
+    p->acted[b] = true;
+    // the caller's stream sees x after the run
+    HIPCHK(hipStreamWaitEvent((hipStream_t)stream, p->act_done[b], 0));
+    ++p->acts;
+    if (p->frame[b] < p->next_frame - 1) ++p->acts_on_older;
+    if (out_frame) *out_frame = p->frame[b];
+  });
+}
+
+vla_status vla_pipeline_sync(vla_pipeline* p) {
+  return guarded([&] {
+    if (!p) raise(VLA_E_INVALID, "null pipeline");
+    HIPCHK(hipSetDevice(p->P[0]->dev));
+    HIPCHK(hipStreamSynchronize(p->sv));
+    HIPCHK(hipStreamSynchronize(p->sa));
+  });
+}
+
+vla_status vla_pipeline_stats(const vla_pipeline* p, int64_t* prefills, int64_t* acts,
+                              int64_t* acts_on_older) {
+  return guarded([&] {
+    if (!p) raise(VLA_E_INVALID, "null pipeline");
+    if (prefills) *prefills = p->prefills;
+    if (acts) *acts = p->acts;
+    if (acts_on_older) *acts_on_older = p->acts_on_older;
   });
 }
 

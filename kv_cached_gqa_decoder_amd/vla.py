@@ -74,6 +74,7 @@ class vla_admission_stats(ctypes.Structure):
 _SIGS = {
     "vla_model_create": (c_int32, [POINTER(vla_config), POINTER(c_void_p)]),
     "vla_model_destroy": (None, [c_void_p]),
+    "vla_model_create_sibling": (c_int32, [c_void_p, POINTER(c_void_p)]),
     "vla_prefill_chunk": (c_int32, [c_void_p, c_void_p, c_void_p, c_int32, POINTER(c_int32),
                                     c_void_p]),
     "vla_decode_step": (c_int32, [c_void_p, c_int32, POINTER(c_int32), c_void_p]),
@@ -111,6 +112,15 @@ _SIGS = {
     "vla_probe_mfma_peak": (c_int32, [c_void_p, c_int32, c_int32, c_void_p, POINTER(c_double)]),
     "vla_expert_create": (c_int32, [c_void_p, POINTER(vla_config), c_int32, POINTER(c_void_p)]),
     "vla_expert_destroy": (None, [c_void_p]),
+    "vla_expert_create_sibling": (c_int32, [c_void_p, c_void_p, POINTER(c_void_p)]),
+    "vla_pipeline_create": (c_int32, [c_void_p, c_void_p, POINTER(c_void_p)]),
+    "vla_pipeline_destroy": (None, [c_void_p]),
+    "vla_pipeline_prefill": (c_int32, [c_void_p, c_void_p, c_int32, c_void_p, POINTER(c_int64)]),
+    "vla_pipeline_act": (c_int32, [c_void_p, c_void_p, c_int32, c_double, c_void_p,
+                                   POINTER(c_int64)]),
+    "vla_pipeline_sync": (c_int32, [c_void_p]),
+    "vla_pipeline_stats": (c_int32, [c_void_p, POINTER(c_int64), POINTER(c_int64),
+                                     POINTER(c_int64)]),
     "vla_expert_denoise": (c_int32, [c_void_p, c_void_p, c_int32, c_double, c_void_p]),
     "vla_pool_create": (c_int32, [c_int32, POINTER(c_void_p)]),
     "vla_pool_destroy": (None, [c_void_p]),
@@ -375,6 +385,50 @@ def vla_expert_destroy(e: int) -> None:
     load().vla_expert_destroy(e)
 
 
+def vla_model_create_sibling(src: int) -> int:
+    h = c_void_p()
+    _check(load().vla_model_create_sibling(src, byref(h)))
+    return h.value
+
+
+def vla_expert_create_sibling(prefix: int, src: int) -> int:
+    h = c_void_p()
+    _check(load().vla_expert_create_sibling(prefix, src, byref(h)))
+    return h.value
+
+
+def vla_pipeline_create(prefix: int, expert: int) -> int:
+    h = c_void_p()
+    _check(load().vla_pipeline_create(prefix, expert, byref(h)))
+    return h.value
+
+
+def vla_pipeline_destroy(p: int) -> None:
+    load().vla_pipeline_destroy(p)
+
+
+def vla_pipeline_prefill(p: int, embeds, n: int, stream=None) -> int:
+    f = c_int64(-1)
+    _check(load().vla_pipeline_prefill(p, _ptr(embeds), n, _stream(stream), byref(f)))
+    return f.value
+
+
+def vla_pipeline_act(p: int, x, n_steps: int, dt: float, stream=None) -> int:
+    f = c_int64(-1)
+    _check(load().vla_pipeline_act(p, _ptr(x), n_steps, dt, _stream(stream), byref(f)))
+    return f.value
+
+
+def vla_pipeline_sync(p: int) -> None:
+    _check(load().vla_pipeline_sync(p))
+
+
+def vla_pipeline_stats(p: int) -> dict:
+    a, b, c = c_int64(0), c_int64(0), c_int64(0)
+    _check(load().vla_pipeline_stats(p, byref(a), byref(b), byref(c)))
+    return {"prefills": a.value, "acts": b.value, "acts_on_older": c.value}
+
+
 def vla_expert_denoise(e: int, x, n_steps: int, dt: float, stream=None) -> None:
     _check(load().vla_expert_denoise(e, _ptr(x), n_steps, dt, _stream(stream)))
 
@@ -525,9 +579,13 @@ def preset(name: str, **overrides) -> vla_config:
 class Model:
     """Owns one handle; methods forward to the C entry points of the same names."""
 
-    def __init__(self, cfg: vla_config):
+    def __init__(self, cfg: vla_config, _handle=None):
         self.cfg = cfg
-        self.h = vla_model_create(cfg)
+        self.h = _handle if _handle is not None else vla_model_create(cfg)
+
+    def sibling(self):
+        """A second model over the same (shared) weights: vla_model_create_sibling."""
+        return Model(self.cfg, _handle=vla_model_create_sibling(self.h))
 
     def close(self):
         if self.h:
@@ -615,11 +673,16 @@ class Model:
 class Expert:
     """An action expert bound to a prefix Model; forwards to the vla_expert_* entry points."""
 
-    def __init__(self, prefix: Model, cfg: vla_config, n_actions: int):
+    def __init__(self, prefix: Model, cfg: vla_config, n_actions: int, _handle=None):
         self.prefix = prefix
         self.cfg = cfg
         self.n_actions = n_actions
-        self.h = vla_expert_create(prefix.h, cfg, n_actions)
+        self.h = _handle if _handle is not None else vla_expert_create(prefix.h, cfg, n_actions)
+
+    def sibling(self, prefix: Model):
+        """An expert with these (shared) weights bound to `prefix`: vla_expert_create_sibling."""
+        return Expert(prefix, self.cfg, self.n_actions,
+                      _handle=vla_expert_create_sibling(prefix.h, self.h))
 
     def close(self):
         if self.h:
@@ -634,3 +697,35 @@ class Expert:
 
     def denoise(self, x, n_steps=10, dt=None, stream=None):
         vla_expert_denoise(self.h, x, n_steps, 1.0 / n_steps if dt is None else dt, stream)
+
+
+class Pipeline:
+    """Overlapped prefix and expert streams over a (Model, Expert) pair: vla_pipeline_*."""
+
+    def __init__(self, prefix: Model, expert: Expert):
+        self.prefix = prefix
+        self.expert = expert
+        self.h = vla_pipeline_create(prefix.h, expert.h)
+
+    def close(self):
+        if self.h:
+            vla_pipeline_destroy(self.h)
+            self.h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def prefill(self, embeds, n, stream=None):
+        return vla_pipeline_prefill(self.h, embeds, n, stream)
+
+    def act(self, x, n_steps=10, dt=None, stream=None):
+        return vla_pipeline_act(self.h, x, n_steps, 1.0 / n_steps if dt is None else dt, stream)
+
+    def sync(self):
+        vla_pipeline_sync(self.h)
+
+    def stats(self):
+        return vla_pipeline_stats(self.h)
