@@ -227,6 +227,7 @@ def gpu_leg(args):
     ev_leg = eviction_leg(args) if not args.no_eviction else None
     lc_leg = longctx_leg(args) if not args.no_longctx else None
     p0_leg = pi0_leg(args) if not args.no_pi0 else None
+    as_leg = asr_leg(args)
 
     fl = prefill_flops()
     dbytes = decode_bytes(CONTEXT + CHUNK + DECODES // 2)
@@ -309,6 +310,7 @@ def gpu_leg(args):
         res["phases"].update(lc_leg)
     if p0_leg:
         res["phases"].update(p0_leg)
+    res["phases"].update(as_leg)
     return res
 
 
@@ -351,6 +353,54 @@ def frame_leg(args):
     med = lambda a, b: round(statistics.median(e[a].elapsed_time(e[b]) for e in evs), 4)
     return {"prefill_ms": med(0, 1), "decode_ms_per_step": round(med(1, 2) / DECODES, 4),
             "score_ms": med(2, 3)}
+
+
+def asr_leg(args):
+    """Reconciliation on a second state at the Qwen2.5-1.5B shape: 5 frames of 256 ids
+    through the reconciler, one all-pairs eviction, then the spare re-prefills the 4 kept
+    frames (1,024 tokens) on its own stream while the serving model prefills a new
+    256-token frame; times: the reconciliation (begin to swap), and the serving prefill
+    alone and during the reconciliation (events on the caller's stream)."""
+    import torch
+
+    import kv_cached_gqa_decoder_amd as vla
+    import synth
+
+    stream = torch.cuda.current_stream()
+    p = vla.PRESETS["c2_qwen1p5b_bf16"]
+    m = vla.Model(vla.make_config(**p))
+    ids = [synth.token_ids(p["seed"], 100 + i, CHUNK, V) for i in range(8)]
+    rows = {"alone": [], "during": [], "reconcile": []}
+    for rep in range(3):
+        rec = vla.Reconciler(m)
+        for i in range(5):
+            rec.prefill(tokens=ids[i], stream=stream)
+        rec.evict("semantic", 0, stream)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        rec.prefill(tokens=ids[5], stream=stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        rows["alone"].append(e0.elapsed_time(e1))
+        rec.evict("fifo", 0, stream)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        rec.begin(stream)
+        e0.record(stream)
+        rec.prefill(tokens=ids[6], stream=stream)
+        e1.record(stream)
+        while not rec.try_swap(stream):
+            time.sleep(0.0002)
+        torch.cuda.synchronize()
+        rows["reconcile"].append((time.perf_counter() - t0) * 1e3)
+        rows["during"].append(e0.elapsed_time(e1))
+        rec.close()
+        m.kv_rollback(-1)
+    m.close()
+    med = lambda k: round(statistics.median(rows[k]), 3)
+    return {"asr_reconcile_ms_5_frames_1280_tokens": med("reconcile"),
+            "asr_serving_prefill_ms_alone": med("alone"),
+            "asr_serving_prefill_ms_during_reconcile": med("during")}
 
 
 def eviction_leg(args):
@@ -879,7 +929,7 @@ def main():
     ap.add_argument("--no-longctx", action="store_true")
     ap.add_argument("--no-pi0", action="store_true")
     ap.add_argument("--cpu-layers", type=int, default=28)
-    ap.add_argument("--only", choices=["frame", "eviction", "longctx", "pi0"],
+    ap.add_argument("--only", choices=["frame", "eviction", "longctx", "pi0", "asr"],
                     help="run one leg alone and print its numbers (for kernel traces)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="first copy 256 MiB on the device three times (a plain copy of known "
@@ -899,7 +949,7 @@ def main():
         del a, b
     if args.only:
         leg = {"frame": frame_leg, "eviction": eviction_leg, "longctx": longctx_leg,
-               "pi0": pi0_leg}[args.only]
+               "pi0": pi0_leg, "asr": asr_leg}[args.only]
         print(json.dumps(leg(args)), flush=True)
         return
     res = gpu_leg(args)

@@ -451,6 +451,56 @@ vla_status vla_pipeline_sync(vla_pipeline* p);
 vla_status vla_pipeline_stats(const vla_pipeline* p, int64_t* prefills, int64_t* acts,
                               int64_t* acts_on_older);
 
+/* ---- Reconciliation on a second state ---------------------------------------
+ * "CSR: Infinite-Horizon Real-Time Policies with Massive Cached State
+ * Representations", section III-E and Appendix D: after evictions, a second
+ * resource re-prefills the kept state while the first keeps serving, catches up
+ * on the chunks that arrived meanwhile, and the two swap roles. Here the second
+ * resource is a sibling model (same weights, its own KV pool) on a second
+ * stream of the same GPU. Every frame is prefilled through the reconciler,
+ * which logs its input (host token ids are copied; device embeddings are copied
+ * into a log of 2 x max_frames chunks, allocated on first use), so that the
+ * spare model can recompute the kept frames' K/V from scratch at contiguous
+ * positions. Frames are named by reconciler ids (0, 1, ... in arrival order),
+ * which stay valid across swaps. The caller decodes and scores on
+ * vla_asr_model() but prefills and evicts only through the reconciler, and
+ * passes one stream to every call. The spare stream has the default priority. */
+typedef struct vla_asr vla_asr;
+/* primary must hold no frame yet. Errors: VLA_E_INVALID, VLA_E_STATE (primary
+ * not empty), VLA_E_HIP. */
+vla_status vla_asr_create(vla_model* primary, vla_asr** out);
+/* Waits for the spare stream, frees the sibling model, the log and the stream.
+ * The caller's model stays valid (it may be the spare at that point). */
+void vla_asr_destroy(vla_asr* a);
+/* The model serving now (the primary, or the sibling after an odd number of swaps). */
+vla_model* vla_asr_model(const vla_asr* a);
+/* vla_prefill_chunk on the serving model, logging the input; out_id (nullable)
+ * receives the frame's reconciler id. Errors: as vla_prefill_chunk, and
+ * VLA_E_NO_BLOCKS when the embeddings log is full. */
+vla_status vla_asr_prefill(vla_asr* a, const int32_t* tokens, const void* embeds, int32_t n,
+                           void* stream, int64_t* out_id);
+/* vla_kv_evict on the serving model (and on the spare, if it already holds the
+ * frame); out_id / out_score (nullable) receive the frame and its score. */
+vla_status vla_asr_evict(vla_asr* a, int32_t policy, int32_t layer, void* stream, int64_t* out_id,
+                         double* out_score);
+/* Start re-prefilling every resident frame, in arrival order, into the emptied
+ * spare model on the spare stream (after the work already on `stream`).
+ * Errors: VLA_E_STATE (one is already running). */
+vla_status vla_asr_reconcile_begin(vla_asr* a, void* stream);
+/* Catch the spare up on frames prefilled since, then, if all of its work has
+ * finished, swap: *swapped = 1 and the spare serves from now on (`stream` is
+ * ordered after its work); else *swapped = 0 and nothing changes. Never waits
+ * on the host. Errors: VLA_E_STATE (no reconciliation running). */
+vla_status vla_asr_try_swap(vla_asr* a, void* stream, int32_t* swapped);
+/* Wait for the spare stream. */
+vla_status vla_asr_sync(vla_asr* a);
+/* The resident frames' reconciler ids in arrival order (the first cap); n_out: their count. */
+vla_status vla_asr_frames(const vla_asr* a, int64_t* ids, int32_t cap, int32_t* n_out);
+/* Counts (each pointer nullable): reconciliations begun, swaps, frames re-prefilled
+ * by the spare, and whether a reconciliation is running. */
+vla_status vla_asr_stats(const vla_asr* a, int64_t* reconciliations, int64_t* swaps,
+                         int64_t* frames_replayed, int32_t* reconciling);
+
 /* Host-only LIFO block pool ("Rebuilding Kshipra Around Memory", section 1):
  * the free-list starts as [0 .. n-1] so the first pop returns n-1; released
  * blocks are pushed in the order given and popped first. The model uses the

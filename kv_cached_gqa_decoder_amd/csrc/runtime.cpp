@@ -1966,6 +1966,271 @@ vla_status vla_pipeline_stats(const vla_pipeline* p, int64_t* prefills, int64_t*
   });
 }
 
+// ---- reconciliation on a second state ("CSR: Infinite-Horizon Real-Time
+// Policies with Massive Cached State Representations", section III-E and
+// Appendix D: after an eviction, a second resource re-prefills the kept state
+// while the first keeps serving, then catches up on the chunks that arrived
+// meanwhile and the two swap roles). On one GPU: a sibling model over the same
+// weights and a second stream. Frames are logged with their inputs so that the
+// spare model can recompute their K/V at contiguous positions. ----
+struct AsrFrame {
+  int64_t id = -1;               // reconciler frame id (monotonic)
+  int n = 0;
+  std::vector<int32_t> tokens;   // host ids (tokens input), or
+  int eslot = -1;                // a slot of the embeddings log (device)
+  int fid[2] = {-1, -1};         // the frame's id in model 0 / model 1 (-1: not there)
+  bool alive = true;             // still resident in the serving model
+};
+
+struct vla_asr {
+  vla_model* M[2] = {nullptr, nullptr};  // [0] the caller's model, [1] its sibling (owned)
+  int serving = 0;
+  hipStream_t sr = nullptr;               // the spare model's stream (default priority)
+  hipEvent_t rec_done = nullptr, in_ready = nullptr;
+  std::vector<AsrFrame> log;              // frames in arrival order
+  void* elog = nullptr;                   // embeddings log: n_eslots x max_chunk x hidden
+  size_t eslot_bytes = 0;
+  int n_eslots = 0;
+  std::vector<int> free_eslots;
+  bool reconciling = false;
+  int64_t next_id = 0;
+  int64_t reconciliations = 0, swaps = 0, replayed = 0;
+};
+
+namespace {
+// drop log entries that no model needs any more (their embedding slots are free again)
+void asr_compact(vla_asr* a) {
+  std::vector<AsrFrame> keep;
+  for (auto& f : a->log) {
+    if (f.alive || f.fid[0] >= 0 || f.fid[1] >= 0) {
+      keep.push_back(std::move(f));
+    } else if (f.eslot >= 0) {
+      a->free_eslots.push_back(f.eslot);
+    }
+  }
+  a->log.swap(keep);
+}
+// prefill every live frame the spare does not hold yet, in arrival order, on the spare stream
+void asr_replay(vla_asr* a) {
+  const int sp = 1 - a->serving;
+  vla_model* m = a->M[sp];
+  for (auto& f : a->log) {
+    if (!f.alive || f.fid[sp] >= 0) continue;
+    const void* emb = f.eslot >= 0 ? (const char*)a->elog + (size_t)f.eslot * a->eslot_bytes : nullptr;
+    int32_t fid = -1;
+    const vla_status s = vla_prefill_chunk(m, emb ? nullptr : f.tokens.data(), emb, f.n, &fid, a->sr);
+    if (s != VLA_OK) raise(s, g_err);
+    f.fid[sp] = fid;
+    ++a->replayed;
+  }
+}
+void asr_free(vla_asr* a) {
+  if (!a) return;
+  if (a->sr) (void)hipStreamSynchronize(a->sr);
+  if (a->M[1]) destroy(a->M[1]);
+  if (a->elog) (void)hipFree(a->elog);
+  if (a->rec_done) (void)hipEventDestroy(a->rec_done);
+  if (a->in_ready) (void)hipEventDestroy(a->in_ready);
+  if (a->sr) (void)hipStreamDestroy(a->sr);
+  delete a;
+}
+}  // namespace
+
+vla_status vla_asr_create(vla_model* primary, vla_asr** out) {
+  vla_asr* a = nullptr;
+  vla_status st = guarded([&] {
+    if (!out) raise(VLA_E_INVALID, "out is NULL");
+    *out = nullptr;
+    if (!primary) raise(VLA_E_INVALID, "null model");
+    if (!primary->segs.empty()) raise(VLA_E_STATE, "the model must be empty (no logged inputs)");
+    HIPCHK(hipSetDevice(primary->dev));
+    a = new vla_asr();
+    a->M[0] = primary;
+    vla_model* s = nullptr;
+    const vla_status ms = vla_model_create_sibling(primary, &s);
+    if (ms != VLA_OK) raise(ms, g_err);
+    a->M[1] = s;
+    HIPCHK(hipStreamCreateWithFlags(&a->sr, hipStreamNonBlocking));
+    HIPCHK(hipEventCreateWithFlags(&a->rec_done, hipEventDisableTiming));
+    HIPCHK(hipEventCreateWithFlags(&a->in_ready, hipEventDisableTiming));
+    *out = a;
+  });
+  if (st != VLA_OK && a) {
+    std::string keep = g_err;
+    asr_free(a);
+    g_err = keep;
+  }
+  return st;
+}
+
+void vla_asr_destroy(vla_asr* a) { asr_free(a); }
+
+vla_model* vla_asr_model(const vla_asr* a) { return a ? a->M[a->serving] : nullptr; }
+
+vla_status vla_asr_prefill(vla_asr* a, const int32_t* tokens, const void* embeds, int32_t n,
+                           void* stream, int64_t* out_id) {
+  return guarded([&] {
+    if (!a) raise(VLA_E_INVALID, "null reconciler");
+    vla_model* m = a->M[a->serving];
+    if ((tokens == nullptr) == (embeds == nullptr))
+      raise(VLA_E_INVALID, "exactly one of tokens / embeds must be given");
+    if (n < 1 || n > m->cfg.max_chunk) raise(VLA_E_INVALID, "chunk length out of range");
+    HIPCHK(hipSetDevice(m->dev));
+    AsrFrame f;
+    f.n = n;
+    if (tokens) {
+      f.tokens.assign(tokens, tokens + n);
+    } else {
+      if (!a->elog) {  // the embeddings log, on first use: 2 x max_frames chunks
+        a->eslot_bytes = (size_t)m->cfg.max_chunk * m->cfg.hidden * m->esz;
+        a->n_eslots = 2 * m->cfg.max_frames;
+        HIPCHK(hipMalloc(&a->elog, a->eslot_bytes * a->n_eslots));
+        for (int i = a->n_eslots - 1; i >= 0; --i) a->free_eslots.push_back(i);
+      }
+      if (a->free_eslots.empty()) raise(VLA_E_NO_BLOCKS, "the embeddings log is full");
+      f.eslot = a->free_eslots.back();
+      HIPCHK(hipMemcpyAsync((char*)a->elog + (size_t)f.eslot * a->eslot_bytes, embeds,
+                            (size_t)n * m->cfg.hidden * m->esz, hipMemcpyDeviceToDevice,
+                            (hipStream_t)stream));
+    }
+    int32_t fid = -1;
+    const vla_status s = vla_prefill_chunk(m, f.tokens.empty() ? nullptr : f.tokens.data(),
+                                           embeds, n, &fid, stream);
+    if (s != VLA_OK) raise(s, g_err);
+    if (f.eslot >= 0) a->free_eslots.pop_back();
+    f.fid[a->serving] = fid;
+    f.id = a->next_id++;
+    a->log.push_back(std::move(f));
+    if (out_id) *out_id = a->log.back().id;
+  });
+}
+
+vla_status vla_asr_evict(vla_asr* a, int32_t policy, int32_t layer, void* stream, int64_t* out_id,
+                         double* out_score) {
+  return guarded([&] {
+    if (!a) raise(VLA_E_INVALID, "null reconciler");
+    vla_model* m = a->M[a->serving];
+    int32_t fid = -1;
+    const vla_status s = vla_kv_evict(m, policy, layer, &fid, out_score, stream);
+    if (s != VLA_OK) raise(s, g_err);
+    const int sp = 1 - a->serving;
+    int64_t id = -1;
+    for (auto& f : a->log)
+      if (f.fid[a->serving] == fid) {
+        id = f.id;
+        f.alive = false;
+        f.fid[a->serving] = -1;
+        // a spare that already holds it rolls back to the last live frame before it, so
+        // that the next catch-up recomputes the later frames at contiguous positions (its
+        // work is ordered on the spare stream)
+        if (a->reconciling && f.fid[sp] >= 0) {
+          int keep = -1;
+          for (const auto& g : a->log) {
+            if (&g == &f) break;
+            if (g.fid[sp] >= 0) keep = g.fid[sp];
+          }
+          const vla_status rs = vla_kv_rollback(a->M[sp], keep);
+          if (rs != VLA_OK) raise(rs, g_err);
+          bool after = false;
+          for (auto& g : a->log) {
+            after = after || &g == &f;
+            if (after) g.fid[sp] = -1;
+          }
+        }
+        break;
+      }
+    if (!a->reconciling) asr_compact(a);
+    if (out_id) *out_id = id;
+  });
+}
+
+vla_status vla_asr_reconcile_begin(vla_asr* a, void* stream) {
+  return guarded([&] {
+    if (!a) raise(VLA_E_INVALID, "null reconciler");
+    if (a->reconciling) raise(VLA_E_STATE, "a reconciliation is already running");
+    const int sp = 1 - a->serving;
+    vla_model* m = a->M[sp];
+    HIPCHK(hipSetDevice(m->dev));
+    // the spare's earlier work (as the serving model) and the logged inputs are ordered
+    // before its re-prefill
+    HIPCHK(hipEventRecord(a->in_ready, (hipStream_t)stream));
+    HIPCHK(hipStreamWaitEvent(a->sr, a->in_ready, 0));
+    const vla_status s = vla_kv_rollback(m, -1);
+    if (s != VLA_OK) raise(s, g_err);
+    for (auto& f : a->log) f.fid[sp] = -1;
+    asr_compact(a);
+    a->reconciling = true;
+    ++a->reconciliations;
+    asr_replay(a);
+    HIPCHK(hipEventRecord(a->rec_done, a->sr));
+  });
+}
+
+vla_status vla_asr_try_swap(vla_asr* a, void* stream, int32_t* swapped) {
+  return guarded([&] {
+    if (!a) raise(VLA_E_INVALID, "null reconciler");
+    if (swapped) *swapped = 0;
+    if (!a->reconciling) raise(VLA_E_STATE, "no reconciliation is running");
+    HIPCHK(hipSetDevice(a->M[0]->dev));
+    // catch up on the frames that arrived since the last replay (their inputs are
+    // ready on the caller's stream); rec_done marks the end of the spare's work so far
+    const int sp = 1 - a->serving;
+    bool behind = false;
+    for (const auto& f : a->log) behind = behind || (f.alive && f.fid[sp] < 0);
+    if (behind) {
+      HIPCHK(hipEventRecord(a->in_ready, (hipStream_t)stream));
+      HIPCHK(hipStreamWaitEvent(a->sr, a->in_ready, 0));
+      asr_replay(a);
+      HIPCHK(hipEventRecord(a->rec_done, a->sr));
+    }
+    const hipError_t q = hipEventQuery(a->rec_done);
+    if (q == hipErrorNotReady) return;
+    HIPCHK(q);
+    // the spare holds every live frame at contiguous positions: it becomes the serving
+    // model, and the caller's stream is ordered after its work
+    HIPCHK(hipStreamWaitEvent((hipStream_t)stream, a->rec_done, 0));
+    const int old = a->serving;
+    a->serving = 1 - old;
+    for (auto& f : a->log) f.fid[old] = -1;
+    a->reconciling = false;
+    ++a->swaps;
+    asr_compact(a);
+    if (swapped) *swapped = 1;
+  });
+}
+
+vla_status vla_asr_sync(vla_asr* a) {
+  return guarded([&] {
+    if (!a) raise(VLA_E_INVALID, "null reconciler");
+    HIPCHK(hipSetDevice(a->M[0]->dev));
+    HIPCHK(hipStreamSynchronize(a->sr));
+  });
+}
+
+vla_status vla_asr_frames(const vla_asr* a, int64_t* ids, int32_t cap, int32_t* n_out) {
+  return guarded([&] {
+    if (!a || !n_out || (!ids && cap > 0) || cap < 0) raise(VLA_E_INVALID, "bad argument");
+    int n = 0;
+    for (const auto& f : a->log)
+      if (f.alive) {
+        if (n < cap) ids[n] = f.id;
+        ++n;
+      }
+    *n_out = n;
+  });
+}
+
+vla_status vla_asr_stats(const vla_asr* a, int64_t* reconciliations, int64_t* swaps,
+                         int64_t* frames_replayed, int32_t* reconciling) {
+  return guarded([&] {
+    if (!a) raise(VLA_E_INVALID, "null reconciler");
+    if (reconciliations) *reconciliations = a->reconciliations;
+    if (swaps) *swaps = a->swaps;
+    if (frames_replayed) *frames_replayed = a->replayed;
+    if (reconciling) *reconciling = a->reconciling ? 1 : 0;
+  });
+}
+
 // ---- host-only pool ----
 vla_status vla_pool_create(int32_t num_blocks, vla_pool** out) {
   return guarded([&] {

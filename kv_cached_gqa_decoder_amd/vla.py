@@ -121,6 +121,19 @@ _SIGS = {
     "vla_pipeline_sync": (c_int32, [c_void_p]),
     "vla_pipeline_stats": (c_int32, [c_void_p, POINTER(c_int64), POINTER(c_int64),
                                      POINTER(c_int64)]),
+    "vla_asr_create": (c_int32, [c_void_p, POINTER(c_void_p)]),
+    "vla_asr_destroy": (None, [c_void_p]),
+    "vla_asr_model": (c_void_p, [c_void_p]),
+    "vla_asr_prefill": (c_int32, [c_void_p, c_void_p, c_void_p, c_int32, c_void_p,
+                                  POINTER(c_int64)]),
+    "vla_asr_evict": (c_int32, [c_void_p, c_int32, c_int32, c_void_p, POINTER(c_int64),
+                                POINTER(c_double)]),
+    "vla_asr_reconcile_begin": (c_int32, [c_void_p, c_void_p]),
+    "vla_asr_try_swap": (c_int32, [c_void_p, c_void_p, POINTER(c_int32)]),
+    "vla_asr_sync": (c_int32, [c_void_p]),
+    "vla_asr_frames": (c_int32, [c_void_p, c_void_p, c_int32, POINTER(c_int32)]),
+    "vla_asr_stats": (c_int32, [c_void_p, POINTER(c_int64), POINTER(c_int64), POINTER(c_int64),
+                                POINTER(c_int32)]),
     "vla_expert_denoise": (c_int32, [c_void_p, c_void_p, c_int32, c_double, c_void_p]),
     "vla_pool_create": (c_int32, [c_int32, POINTER(c_void_p)]),
     "vla_pool_destroy": (None, [c_void_p]),
@@ -421,6 +434,68 @@ def vla_pipeline_act(p: int, x, n_steps: int, dt: float, stream=None) -> int:
 
 def vla_pipeline_sync(p: int) -> None:
     _check(load().vla_pipeline_sync(p))
+
+
+def vla_asr_create(primary: int) -> int:
+    h = c_void_p()
+    _check(load().vla_asr_create(primary, byref(h)))
+    return h.value
+
+
+def vla_asr_destroy(a: int) -> None:
+    load().vla_asr_destroy(a)
+
+
+def vla_asr_model(a: int) -> int:
+    return load().vla_asr_model(a)
+
+
+def vla_asr_prefill(a: int, tokens=None, embeds=None, n: int = 0, stream=None) -> int:
+    f = c_int64(-1)
+    if tokens is not None:
+        import numpy as np
+        arr = np.ascontiguousarray(tokens, dtype=np.int32)
+        n = len(arr)
+        _check(load().vla_asr_prefill(a, arr.ctypes.data, None, n, _stream(stream), byref(f)))
+    else:
+        _check(load().vla_asr_prefill(a, None, _ptr(embeds), n, _stream(stream), byref(f)))
+    return f.value
+
+
+def vla_asr_evict(a: int, policy: int, layer: int = 0, stream=None):
+    f, sc = c_int64(-1), c_double(0.0)
+    _check(load().vla_asr_evict(a, policy, layer, _stream(stream), byref(f), byref(sc)))
+    return f.value, sc.value
+
+
+def vla_asr_reconcile_begin(a: int, stream=None) -> None:
+    _check(load().vla_asr_reconcile_begin(a, _stream(stream)))
+
+
+def vla_asr_try_swap(a: int, stream=None) -> bool:
+    s = c_int32(0)
+    _check(load().vla_asr_try_swap(a, _stream(stream), byref(s)))
+    return bool(s.value)
+
+
+def vla_asr_sync(a: int) -> None:
+    _check(load().vla_asr_sync(a))
+
+
+def vla_asr_frames(a: int):
+    import numpy as np
+    n = c_int32(0)
+    _check(load().vla_asr_frames(a, None, 0, byref(n)))
+    ids = np.zeros(max(n.value, 1), dtype=np.int64)
+    _check(load().vla_asr_frames(a, ids.ctypes.data, n.value, byref(n)))
+    return [int(i) for i in ids[:n.value]]
+
+
+def vla_asr_stats(a: int) -> dict:
+    r, s, f, on = c_int64(0), c_int64(0), c_int64(0), c_int32(0)
+    _check(load().vla_asr_stats(a, byref(r), byref(s), byref(f), byref(on)))
+    return {"reconciliations": r.value, "swaps": s.value, "frames_replayed": f.value,
+            "reconciling": bool(on.value)}
 
 
 def vla_pipeline_stats(p: int) -> dict:
@@ -729,3 +804,48 @@ class Pipeline:
 
     def stats(self):
         return vla_pipeline_stats(self.h)
+
+
+class Reconciler:
+    """Reconciliation on a sibling state (vla_asr_*); the serving model changes on a swap."""
+
+    def __init__(self, primary: Model):
+        self.primary = primary
+        self.h = vla_asr_create(primary.h)
+
+    def close(self):
+        if self.h:
+            vla_asr_destroy(self.h)
+            self.h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def model_handle(self) -> int:
+        return vla_asr_model(self.h)
+
+    def prefill(self, tokens=None, embeds=None, n=0, stream=None):
+        return vla_asr_prefill(self.h, tokens, embeds, n, stream)
+
+    def evict(self, policy, layer=0, stream=None):
+        if isinstance(policy, str):
+            policy = EVICT_POLICIES[policy]
+        return vla_asr_evict(self.h, policy, layer, stream)
+
+    def begin(self, stream=None):
+        vla_asr_reconcile_begin(self.h, stream)
+
+    def try_swap(self, stream=None):
+        return vla_asr_try_swap(self.h, stream)
+
+    def sync(self):
+        vla_asr_sync(self.h)
+
+    def frames(self):
+        return vla_asr_frames(self.h)
+
+    def stats(self):
+        return vla_asr_stats(self.h)
