@@ -48,17 +48,18 @@ namespace vla {
 // rows kernel (prefill)
 // ---------------------------------------------------------------------------
 // Two shapes. Long caches: 128 rows per workgroup, each block pair read once per
-// 128 rows: at d <= 128 4 wavefronts of 2 row tiles, two workgroups per CU whose
-// per-pair barriers need not line up (a 512-token chunk over 120,000 keys: 30.8 ms
-// of attention against 32.3 ms for one workgroup of 8 wavefronts x 2 tiles), at
-// d = 256 8 wavefronts of one tile. Short caches (few pairs per workgroup): 4
-// wavefronts of one tile, 64 rows, for more workgroups.
+// 128 rows: at d <= 128 4 wavefronts of 2 row tiles in a 3-stage ring (48 KB), three
+// workgroups per CU whose per-pair barriers need not line up (a 512-token chunk over
+// 120,000 keys: 29.8 ms of attention against 30.8 ms with a 4-stage ring and two
+// per CU, and 32.3 ms for one workgroup of 8 wavefronts x 2 tiles), at d = 256 8
+// wavefronts of one tile. Short caches (few pairs per workgroup): 4 wavefronts of
+// one tile, 64 rows, for more workgroups.
 template <int D, bool SHORT>
 struct RowCfg {
   static constexpr int WAVES = SHORT || D <= 128 ? 4 : 8;
   static constexpr int QT = SHORT || D > 128 ? 1 : 2;  // 16-row tiles per wavefront
   static constexpr int ROWS = WAVES * QT * 16;       // rows per workgroup
-  static constexpr int NS = D <= 128 && !SHORT ? 4 : 3;  // ring stages (block pairs)
+  static constexpr int NS = 3;                       // ring stages (block pairs)
   static constexpr int BLK = 16 * D * 2;             // one block of K (or V) of one KV head
   static constexpr int STAGE = 4 * BLK;              // K0 K1 V0 V1
   static constexpr int LDS = NS * STAGE;
@@ -648,8 +649,9 @@ hipError_t launch_attention(const AttnArgs& args, int dt, hipStream_t s, int* fo
   // that workgroups run long and few partials are merged; within the
   // partial-buffer capacity
   int splits = (a.nlb + 7) / 8;
-  // (rows kernel: 8 wavefronts per CU, i.e. 2 workgroups of 4, or 1 of 8 at d = 256)
-  const int resident = shape == 2 && d > 128 ? 256 : 512;
+  // (rows kernel: 12 wavefronts per CU, 3 long-cache workgroups of 4, or 8: 2 short-cache
+  // workgroups, 1 long-cache workgroup of 8 at d = 256)
+  const int resident = shape == 2 ? (d > 128 ? 256 : 768) : 512;
   splits = std::min(splits, std::max(1, resident / base));
   splits = std::min(splits, keysplit ? kMaxSplitsKey : kMaxSplitsRow);
   static_assert(kMaxSplitsKey <= kMaxSplits && kMaxSplitsRow <= kMaxSplits, "merge capacity");

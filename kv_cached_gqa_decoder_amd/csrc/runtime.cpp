@@ -35,7 +35,7 @@ struct Err {
 
 [[noreturn]] void raise(vla_status st, const std::string& msg) { throw Err{st, msg}; }
 
-constexpr int kPartRows = 65536;   // attention split partials capacity (query rows x splits)
+constexpr int kPartRows = 131072;  // attention split partials capacity (query rows x splits)
 constexpr int kGemmSplitsMax = 16; // split-K partial capacity of the prefill residual projections
 constexpr int kArgmaxParts = 2048; // head GEMV workgroups at most
 
