@@ -390,13 +390,24 @@ __global__ __launch_bounds__((RowCfg<D, SHORT>::WAVES * 64)) void attn_rows_kern
     if (splits == 1) {
       if (r < R) {
         const float inv = l[qt] > 0.f ? 1.f / l[qt] : 0.f;
-        bf16_t* orow = (bf16_t*)a.out + ((size_t)(r / grp) * a.hq + kvh * grp + r % grp) * D;
+        const size_t ro = ((size_t)(r / grp) * a.hq + kvh * grp + r % grp) * D;
+        bf16_t* orow = (bf16_t*)a.out + ro;
 #pragma unroll
         for (int dt = 0; dt < D / 16; ++dt) {
           u32x2_t w;
           w[0] = pack_bf16x2(o[qt][dt][0] * inv, o[qt][dt][1] * inv);
           w[1] = pack_bf16x2(o[qt][dt][2] * inv, o[qt][dt][3] * inv);
           *(u32x2_t*)(orow + dt * 16 + 4 * jq) = w;
+          if (a.out_lo) {
+            u32x2_t wl;
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+              const float y0 = o[qt][dt][2 * h] * inv, y1 = o[qt][dt][2 * h + 1] * inv;
+              wl[h] = pack_bf16x2(y0 - bf16_to_f32((bf16_t)(w[h] & 0xffffu)),
+                                  y1 - bf16_to_f32((bf16_t)(w[h] >> 16)));
+            }
+            *(u32x2_t*)((bf16_t*)a.out_lo + ro + dt * 16 + 4 * jq) = wl;
+          }
         }
       }
     } else {
@@ -521,9 +532,15 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a, int rgroups
     }
     M = Mt;
   }
-  bf16_t* orow = (bf16_t*)a.out + ((size_t)(rr / grp) * a.hq + kvh * grp + rr % grp) * D + lane * V;
+  const size_t ro = ((size_t)(rr / grp) * a.hq + kvh * grp + rr % grp) * D + lane * V;
+  bf16_t* orow = (bf16_t*)a.out + ro;
 #pragma unroll
-  for (int v = 0; v < V; ++v) orow[v] = f32_to_bf16(M != -INFINITY && L > 0.f ? acc[v] / L : 0.f);
+  for (int v = 0; v < V; ++v) {
+    const float y = M != -INFINITY && L > 0.f ? acc[v] / L : 0.f;
+    const bf16_t h = f32_to_bf16(y);
+    orow[v] = h;
+    if (a.out_lo) ((bf16_t*)a.out_lo)[ro + v] = f32_to_bf16(y - bf16_to_f32(h));
+  }
 }
 
 // ---------------------------------------------------------------------------

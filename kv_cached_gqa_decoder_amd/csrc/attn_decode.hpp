@@ -281,8 +281,11 @@ __device__ __forceinline__ void attn_decode_body(const AttnArgs& a, int rgroups,
     const float L = rowL[c];
     const int rr = rg * 16 + c;
     if (splits == 1) {
-      ((bf16_t*)a.out)[((size_t)(rr / grp) * a.hq + kvh * grp + rr % grp) * D + dim] =
-          f32_to_bf16(L > 0.f ? acc / L : 0.f);
+      const size_t oi = ((size_t)(rr / grp) * a.hq + kvh * grp + rr % grp) * D + dim;
+      const float y = L > 0.f ? acc / L : 0.f;
+      const bf16_t h = f32_to_bf16(y);
+      ((bf16_t*)a.out)[oi] = h;
+      if (a.out_lo) ((bf16_t*)a.out_lo)[oi] = f32_to_bf16(y - bf16_to_f32(h));
     } else {
       a.part_o[((size_t)unit * 16 + c) * D + dim] = acc;
       if (dim == 0) {

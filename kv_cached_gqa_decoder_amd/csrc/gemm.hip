@@ -906,10 +906,11 @@ static hipError_t gemm_w4(const GemmArgs& a, hipStream_t s) {
 //    20.3 us for 64 x 64), else 64 x 32 tiles with 4 wavefronts along M (63 x 8192 x
 //    1024: 6.2 us against 10.1 us for 64 x 128); up to 128 rows -> 128 x 64 in a
 //    3-stage ring; 129 to 256 rows -> the two-stream kernel (separate activation and
-//    weight rings) on 128-row M tiles, groups of up to 160 columns (256 x 17920 x 1536
-//    with the activations' low part: 36 us against 44 us for one 256-row tile and
-//    96-column groups, whose activation re-reads were 7x the weight bytes, and against
-//    37 us with 32 x 32 x 16 matrix instructions); more rows -> 256 x 128 with 8
+//    weight rings): one 256-row M tile with groups of up to 96 columns (256 x 17920 x
+//    1536: 0.7 us per layer faster than two 128-row tiles), with the activations' low
+//    part two 128-row M tiles with groups of up to 160 columns (36 us against 44 us for
+//    one 256-row tile, whose doubled activation re-reads were 7x the weight bytes); more
+//    rows -> 256 x 128 with 8
 //    wavefronts (4 x 2 grid of 64 x 64 wavefront tiles), 32-deep steps (256 x 17920 x
 //    1536: 34 us against 37 us for 128 x 64 and 39 us for 64 x 64), or 256 x 256 (64 x
 //    128 wavefront tiles, 3-stage ring) when that still makes about 192 workgroups:
@@ -931,14 +932,24 @@ static hipError_t gemm_w4(const GemmArgs& a, hipStream_t s) {
 // the residual add (+ next RMSNorm), or RoPE + K/V write for q/k/v.
 // LO: the activations carry a low part (A_lo); the same shapes, with one ring stage
 // less where the doubled activation rows would not fit the LDS
+// the two-stream gated projection: one 256-row M tile with up to 96-column groups, or
+// with the activations' low part (twice the activation rows) two 128-row M tiles with
+// up to 160-column groups
+template <int EPI, bool LO>
+static bool ws2_gated(const GemmArgs& a, hipStream_t s) {
+  if constexpr (LO)
+    return gemm_ws2_go<EPI, 10, 4, 8, true, 128>(a, 256, 1, s);
+  else
+    return gemm_ws2_go<EPI, 6, 4, 8, false, 256>(a, 256, 1, s);
+}
+
 template <int EPI, bool LO>
 static void gated_go(const GemmArgs& a, hipStream_t s) {
   if (a.M <= 64 && a.N % 128 == 0 && a.N / 128 >= 128)
     gemm_bf16_go<EPI, 64, 128, 64, 4, 2, 2, LO>(a, 1, a.K / 64, s);
   else if (a.M <= 64)
     gemm_bf16_go<EPI, 64, 32, 64, 4, 4, 1, LO>(a, 1, a.K / 64, s);
-  else if (a.M > 128 && a.M <= 256 && a.N % 32 == 0 &&
-           gemm_ws2_go<EPI, 10, 4, 8, LO, 128>(a, 256, 1, s))
+  else if (a.M > 128 && a.M <= 256 && a.N % 32 == 0 && ws2_gated<EPI, LO>(a, s))
     return;
   else if (a.M > 128 && a.N % 256 == 0 && ((a.M + 255) / 256) * (a.N / 256) >= 192)
     gemm_bf16_go<EPI, 256, 256, 32, 3, 4, 2, LO>(a, 1, a.K / 32, s);
@@ -980,7 +991,6 @@ static hipError_t gemm_bf16(const GemmArgs& a, hipStream_t s) {
     return hipGetLastError();
   }
   if (a.epi != EPI_QKV && a.epi != EPI_RESID) return hipErrorInvalidValue;
-  if (lo && a.epi != EPI_QKV) return hipErrorInvalidValue;  // residual inputs carry no low part
   const int ksteps_all = a.K / 64;
   // 256 x 64 tiles, 8 wavefronts (with a low part the doubled rows would not fit the LDS)
   const bool tall = a.M >= 512 && ksteps_all >= 128 && !lo;
@@ -1004,7 +1014,7 @@ static hipError_t gemm_bf16(const GemmArgs& a, hipStream_t s) {
   if (a.N % 8 != 0 || a.N / 8 > 256 * kResidMaxChunks) return hipErrorInvalidValue;
   // 129 to 256 rows with a long K (the down projection): the two-stream kernel with
   // 128-column groups, K in up to 16 pieces
-  if (a.M > 128 && a.M <= 256 && ksteps_all >= 64 && a.N % 128 == 0) {
+  if (a.M > 128 && a.M <= 256 && ksteps_all >= 64 && a.N % 128 == 0 && !lo) {
     const int steps = a.K / 32;
     int sp = kResidNormMaxSplits;
     while (sp > 1 && (size_t)sp * a.M * a.N > a.ws_elems) --sp;
@@ -1017,7 +1027,9 @@ static hipError_t gemm_bf16(const GemmArgs& a, hipStream_t s) {
     }
   }
   if (tall) gemm_bf16_go<EPI_PARTIAL, 256, 64, 64, 3, 4, 2>(a, splits, ksteps, s);
+  else if (skinny && lo) gemm_bf16_go<EPI_PARTIAL, 64, 32, 64, 3, 4, 1, true>(a, splits, ksteps, s);
   else if (skinny) gemm_bf16_go<EPI_PARTIAL, 64, 32, 64, 3, 4, 1>(a, splits, ksteps, s);
+  else if (lo) gemm_bf16_go<EPI_PARTIAL, 64, 64, 64, 3, 2, 2, true>(a, splits, ksteps, s);
   else gemm_bf16_go<EPI_PARTIAL, 64, 64, 64, 3>(a, splits, ksteps, s);
   launch_k(resid_norm_kernel, dim3(a.M), dim3(256), 0, s, (const float*)a.ws, splits, a.M, a.N,
            (float*)a.C, (bf16_t*)a.norm_out, (bf16_t*)a.norm_out_lo, a.norm_g, a.eps);

@@ -77,7 +77,7 @@ struct GemmArgs {
   const void* A = nullptr;  // [M][K] activations
   // bf16 only: the low part of the activations, A_lo = bf16(a - A) for the exact
   // value a whose bf16 rounding is A; when set the product is (A + A_lo) W^T, i.e.
-  // the input carries about 16 significant bits (q/k/v and gated projections)
+  // the input carries about 16 significant bits (q/k/v and output projections)
   const void* A_lo = nullptr;
   const void* W = nullptr;  // [N][K] weights (physical layout); INT4: codes then scales
   int wf = WF_ACT;
@@ -126,6 +126,7 @@ constexpr int kFoldMaxHeads = 16;
 struct AttnArgs {
   const void* q = nullptr;   // [n][Hq][d]
   void* out = nullptr;       // [n][Hq][d]
+  void* out_lo = nullptr;    // bf16, nullable: the low part of out, bf16(exact - out) (see A_lo)
   const void* kpool = nullptr;
   const void* vpool = nullptr;
   KvGeom g{};

@@ -148,7 +148,8 @@ struct vla_model {
   // scratch
   void* x = nullptr;
   void* u = nullptr;
-  void* u_lo = nullptr;         // bf16 weights: low part of the normalised rows (see GemmArgs)
+  void* u_lo = nullptr;         // bf16 weights: low part of the q/k/v input rows (see GemmArgs)
+  void* ao_lo = nullptr;        // bf16 weights: low part of the attention output rows
   void* qbuf = nullptr;
   void* ao = nullptr;
   void* act = nullptr;
@@ -493,9 +494,12 @@ void run_layers(vla_model* m, const KvView& view, int n, int64_t pos0, int cb0, 
       q.ws_elems = m->gemm_ws_elems;
       LAUNCH(m, VLA_K_GEMM_QKV, st, launch_gemm(q, m->dt, st));
       if (kv_only) break;
+      // the output projection's input as a bf16 pair (bf16 projection weights)
+      at.out_lo = m->ao_lo;
       LAUNCH(m, VLA_K_ATTN_PREFILL, st, launch_attention(at, m->dt, st));
       GemmArgs o;
       o.A = m->ao;
+      o.A_lo = m->ao_lo;
       o.W = m->wo[l];
       o.wf = m->wf;
       o.M = n;
@@ -506,7 +510,6 @@ void run_layers(vla_model* m, const KvView& view, int n, int64_t pos0, int cb0, 
       o.ws = m->gemm_ws;
       o.ws_elems = m->gemm_ws_elems;
       o.norm_out = m->u;
-      o.norm_out_lo = m->u_lo;
       o.norm_g = m->norm_ones;
       o.eps = c.rms_eps;
       LAUNCH(m, VLA_K_GEMM_O, st, launch_gemm(o, m->dt, st));
@@ -515,7 +518,6 @@ void run_layers(vla_model* m, const KvView& view, int n, int64_t pos0, int cb0, 
                launch_rmsnorm(m->x, m->norm_ones, m->u, nullptr, n, H, c.rms_eps, m->dt, st));
       GemmArgs gu;
       gu.A = m->u;
-      gu.A_lo = m->u_lo;
       gu.W = m->wgu[l];
       gu.wf = m->wf;
       gu.M = n;
@@ -894,7 +896,10 @@ void build_model(vla_model* m, const vla_config& cfg, const vla_model* borrow,
   const size_t mc = c.max_chunk;
   m->x = dalloc(m, mc * H * sizeof(float));  // the residual stream is fp32
   m->u = dalloc(m, mc * H * e);
-  if (m->dt == DT_BF16 && m->wf == WF_ACT) m->u_lo = dalloc(m, mc * H * e);
+  if (m->dt == DT_BF16 && m->wf == WF_ACT) {
+    m->u_lo = dalloc(m, mc * H * e);
+    m->ao_lo = dalloc(m, mc * hq * d * e);
+  }
   m->qbuf = dalloc(m, mc * hq * d * e);
   m->ao = dalloc(m, mc * hq * d * e);
   m->act = dalloc(m, mc * (size_t)c.ffn * e);
