@@ -932,15 +932,17 @@ static hipError_t gemm_w4(const GemmArgs& a, hipStream_t s) {
 // the residual add (+ next RMSNorm), or RoPE + K/V write for q/k/v.
 // LO: the activations carry a low part (A_lo); the same shapes, with one ring stage
 // less where the doubled activation rows would not fit the LDS
-// the two-stream gated projection: one 256-row M tile with up to 96-column groups, or
-// with the activations' low part (twice the activation rows) two 128-row M tiles with
-// up to 160-column groups
+// the two-stream gated projection: one 256-row M tile with up to 96-column groups and
+// eight consumer wavefronts of 32 rows (two per SIMD: 29.2 us against 29.5 us with four
+// of 64 rows; a consumer on 32 x 32 x 16 instructions, deeper activation or weight rings
+// and K walks staggered per workgroup gave nothing), or with the activations' low part
+// (twice the activation rows) two 128-row M tiles with up to 160-column groups
 template <int EPI, bool LO>
 static bool ws2_gated(const GemmArgs& a, hipStream_t s) {
   if constexpr (LO)
     return gemm_ws2_go<EPI, 10, 4, 8, true, 128>(a, 256, 1, s);
   else
-    return gemm_ws2_go<EPI, 6, 4, 8, false, 256>(a, 256, 1, s);
+    return gemm_ws2_go<EPI, 6, 4, 8, false, 256, 8>(a, 256, 1, s);
 }
 
 template <int EPI, bool LO>
