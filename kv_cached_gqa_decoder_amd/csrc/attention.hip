@@ -666,6 +666,11 @@ hipError_t launch_attention(const AttnArgs& args, int dt, hipStream_t s, int* fo
   // that workgroups run long and few partials are merged; within the
   // partial-buffer capacity
   int splits = (a.nlb + 7) / 8;
+  // one-token decode over a short cache: splits of 4 blocks while the output projection
+  // can still merge them as it reads its input (1,300 keys: 16 splits, decode step 1.080
+  // -> 1.067 ms)
+  if (keysplit && a.n == 1)
+    splits = std::max(splits, std::min(kFoldMaxSplits, (a.nlb + 3) / 4));
   // (rows kernel: 12 wavefronts per CU, 3 long-cache workgroups of 4, or 8: 2 short-cache
   // workgroups, 1 long-cache workgroup of 8 at d = 256)
   const int resident = shape == 2 ? (d > 128 ? 256 : 768) : 512;

@@ -600,7 +600,8 @@ bool run_decode_persistent(vla_model* m, const KvView& view, int32_t token, int6
   at.part_ml = m->part_ml;
   at.part_rows = kPartRows;
   at.scale = (float)(1.0 / std::sqrt((double)c.head_dim));
-  int splits = (view.nlb + 7) / 8;
+  // the per-kernel step's rule (launch_attention), so that both steps split alike
+  int splits = std::max((view.nlb + 7) / 8, std::min(kFoldMaxSplits, (view.nlb + 3) / 4));
   splits = std::min(splits, std::max(1, 512 / hkv));
   splits = std::min(splits, kFoldMaxSplits);
   splits = std::min(splits, std::max(1, kPartRows / (hkv * 16)));
