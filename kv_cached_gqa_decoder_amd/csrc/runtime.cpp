@@ -148,8 +148,8 @@ struct vla_model {
   // scratch
   void* x = nullptr;
   void* u = nullptr;
-  void* u_lo = nullptr;         // bf16 weights: low part of the q/k/v input rows (see GemmArgs)
-  void* ao_lo = nullptr;        // bf16 weights: low part of the attention output rows
+  void* u_lo = nullptr;         // bf16 weights, logits out: low part of the q/k/v input rows
+  void* ao_lo = nullptr;        // ... and of the attention output rows (see GemmArgs)
   void* qbuf = nullptr;
   void* ao = nullptr;
   void* act = nullptr;
@@ -897,7 +897,10 @@ void build_model(vla_model* m, const vla_config& cfg, const vla_model* borrow,
   const size_t mc = c.max_chunk;
   m->x = dalloc(m, mc * H * sizeof(float));  // the residual stream is fp32
   m->u = dalloc(m, mc * H * e);
-  if (m->dt == DT_BF16 && m->wf == WF_ACT) {
+  // the q/k/v and output-projection inputs as bf16 pairs: for models whose output is
+  // logits (the precision budget that needs them is the logits'); a prefix model (K/V
+  // out) or an action expert computes those products from the rounded inputs alone
+  if (m->dt == DT_BF16 && m->wf == WF_ACT && c.vocab > 0) {
     m->u_lo = dalloc(m, mc * H * e);
     m->ao_lo = dalloc(m, mc * hq * d * e);
   }
