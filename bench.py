@@ -761,12 +761,12 @@ def pi0_leg(args):
         return (time.perf_counter() - t0) * 1e3 / n
 
     overlap = {}
-    for acts in (1, 2):
+    for acts in (() if getattr(args, "no_overlap", False) else (1, 2)):
         overlap[f"{acts}_runs_per_frame"] = {
             "one_stream_ms_per_frame": round(statistics.median(frames(8, acts, False)
                                                                for _ in range(3)), 3)}
     pl = vla.Pipeline(m, e)  # (the pair is used only through the pipeline from here)
-    for acts in (1, 2):
+    for acts in (() if getattr(args, "no_overlap", False) else (1, 2)):
         frames(2, acts, True)
         overlap[f"{acts}_runs_per_frame"]["overlapped_ms_per_frame"] = round(
             statistics.median(frames(8, acts, True) for _ in range(3)), 3)
@@ -928,6 +928,8 @@ def main():
     ap.add_argument("--no-eviction", action="store_true")
     ap.add_argument("--no-longctx", action="store_true")
     ap.add_argument("--no-pi0", action="store_true")
+    ap.add_argument("--no-overlap", action="store_true",
+                    help="pi0 leg: skip the overlapped-stream comparison (short profiling runs)")
     ap.add_argument("--cpu-layers", type=int, default=28)
     ap.add_argument("--only", choices=["frame", "eviction", "longctx", "pi0", "asr"],
                     help="run one leg alone and print its numbers (for kernel traces)")
