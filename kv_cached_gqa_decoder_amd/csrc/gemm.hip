@@ -288,16 +288,21 @@ __device__ __forceinline__ void wait_vmcnt_le() {
 
 // producer wavefront of one ring: rows [row0, row0 + LOADS*16) of each stage; a
 // DMA load fills 1 KiB = 16 rows of 64 bytes, lane i writing chunk position i % 4
-// of row i / 4 with the K chunk that position holds
+// of row i / 4 with the K chunk that position holds. Load j reads base[j] (uniform,
+// the K piece's first column) + off[j] (the lane's byte offset) + 64 bytes per K
+// step: the address is one scalar base and one 32-bit vector offset, and the LDS
+// destination is uniform, so a load needs no per-lane address arithmetic and no
+// register it shares with the next load
 template <int LOADS, int NS, int STAGE>
-__device__ __forceinline__ void ws2_produce(unsigned char* ring, const bf16_t* (&src)[LOADS],
-                                            int lds_off, int nk) {
+__device__ __forceinline__ void ws2_produce(unsigned char* ring,
+                                            const unsigned char* const (&base)[LOADS],
+                                            const uint32_t (&off)[LOADS], int lds_off, int nk) {
   auto issue = [&](int kt) {
     unsigned char* st = ring + (kt % NS) * STAGE + lds_off;
     const int kd = kt < nk ? kt : nk - 1;  // past the end: the last step again (never read)
 #pragma unroll
     for (int j = 0; j < LOADS; ++j)
-      __builtin_amdgcn_global_load_lds((const void*)(src[j] + (int64_t)kd * 32),
+      __builtin_amdgcn_global_load_lds((const void*)(base[j] + kd * 64 + off[j]),
                                        (__attribute__((address_space(3))) void*)(st + j * 1024),
                                        16, 0, 0);
   };
@@ -407,31 +412,35 @@ __global__ __launch_bounds__(64 * (CW + 4)) void gemm_ws2_kernel(GemmArgs a, int
   const int M = a.M, K = a.K, m0 = mt * BMT;
   const int kt0 = z * ksteps;
   const int nk = min(K / 32 - kt0, ksteps);  // (the host never makes an empty piece)
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   if (wave >= CW + 2) {  // weight producers: rows of the group (past its columns: a row inside it)
     const int p = wave - CW - 2;
-    const bf16_t* src[T::WLOADS];
+    const unsigned char* base[T::WLOADS];
+    uint32_t off[T::WLOADS];
 #pragma unroll
     for (int j = 0; j < T::WLOADS; ++j) {
       const int row = (p * T::WLOADS + j) * 16 + (lane >> 2);
-      src[j] = (const bf16_t*)a.W + (int64_t)(n0 + row % nc) * K + (int64_t)kt0 * 32 +
-               T::pos(row, lane & 3) * 8;
+      base[j] = (const unsigned char*)a.W + (int64_t)kt0 * 64;
+      off[j] = (uint32_t)(((n0 + row % nc) * K + T::pos(row, lane & 3) * 8) * 2);
     }
-    ws2_produce<T::WLOADS, NSW, T::WSTAGE>(smem + NSA * T::ASTAGE, src, p * T::WLOADS * 1024, nk);
+    ws2_produce<T::WLOADS, NSW, T::WSTAGE>(smem + NSA * T::ASTAGE, base, off,
+                                           p * T::WLOADS * 1024, nk);
     return;
   }
   if (wave >= CW) {  // activation producers: the M tile's rows (past M: row M-1), LO: then
-                     // the same rows of the low part
+                     // the same rows of the low part (a whole 16-row piece lies on one side)
     const int p = wave - CW;
-    const bf16_t* src[T::ALOADS];
+    const unsigned char* base[T::ALOADS];
+    uint32_t off[T::ALOADS];
 #pragma unroll
     for (int j = 0; j < T::ALOADS; ++j) {
       const int row = (p * T::ALOADS + j) * 16 + (lane >> 2);
-      const bf16_t* base = (const bf16_t*)(row < BMT ? a.A : a.A_lo);
-      src[j] = base + (int64_t)min(m0 + row % BMT, M - 1) * K + (int64_t)kt0 * 32 +
-               T::pos(row, lane & 3) * 8;
+      base[j] = (const unsigned char*)((p * T::ALOADS + j) * 16 < BMT ? a.A : a.A_lo) +
+                (int64_t)kt0 * 64;
+      off[j] = (uint32_t)((min(m0 + row % BMT, M - 1) * K + T::pos(row, lane & 3) * 8) * 2);
     }
-    ws2_produce<T::ALOADS, NSA, T::ASTAGE>(smem, src, p * T::ALOADS * 1024, nk);
+    ws2_produce<T::ALOADS, NSA, T::ASTAGE>(smem, base, off, p * T::ALOADS * 1024, nk);
     return;
   }
   constexpr int N2 = NTM > 2 ? NTM - 2 : NTM, N4 = NTM > 4 ? NTM - 4 : N2;
