@@ -151,21 +151,28 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_kernel(GemmArgs a, i
   const int kt0 = z * ksteps;
   const int nk = min(K / BK - kt0, ksteps);
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / WGN, wn = wave % WGN;
 
-  // this lane's source pointers for its LOADS DMA loads (rows past M re-read row M-1)
-  const bf16_t* src[LOADS];
+  // this lane's sources for its LOADS DMA loads (rows past M re-read row M-1): load j
+  // reads a uniform base (its 1 KiB piece lies wholly in the activation rows, their low
+  // part or the weight rows) plus the lane's 32-bit byte offset
+  const unsigned char* base[LOADS];
+  uint32_t off[LOADS];
 #pragma unroll
   for (int j = 0; j < LOADS; ++j) {
-    const int row = (wave * LOADS + j) * G::RPI + lane / G::CPR;
+    const int row0 = (wave * LOADS + j) * G::RPI;  // the piece's first row (uniform)
+    const int row = row0 + lane / G::CPR;
     const int kc = G::pos(row, lane % G::CPR);  // pos() is an involution in kc
-    if (row < G::AROWS) {
+    if (row0 < G::AROWS) {
       const int ar = min(m0 + (row < BM ? row : row - BM), M - 1);
-      const bf16_t* base = (const bf16_t*)(row < BM ? a.A : a.A_lo);
-      src[j] = base + (int64_t)ar * K + (int64_t)kt0 * BK + kc * 8;
+      base[j] = (const unsigned char*)(row0 < BM ? a.A : a.A_lo) +
+                ((int64_t)m0 * K + (int64_t)kt0 * BK) * 2;
+      off[j] = (uint32_t)(((ar - m0) * K + kc * 8) * 2);
     } else {
-      src[j] = (const bf16_t*)a.W + (int64_t)(n0 + row - G::AROWS) * K + (int64_t)kt0 * BK + kc * 8;
+      base[j] = (const unsigned char*)a.W + ((int64_t)n0 * K + (int64_t)kt0 * BK) * 2;
+      off[j] = (uint32_t)(((row - G::AROWS) * K + kc * 8) * 2);
     }
   }
   // stage kt -> ring slot kt % NS. Past the last step the DMA re-loads the last
@@ -176,7 +183,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_kernel(GemmArgs a, i
     const int kd = kt < nk ? kt : nk - 1;
 #pragma unroll
     for (int j = 0; j < LOADS; ++j)
-      __builtin_amdgcn_global_load_lds((const void*)(src[j] + (int64_t)kd * BK),
+      __builtin_amdgcn_global_load_lds((const void*)(base[j] + kd * (BK * 2) + off[j]),
                                        (__attribute__((address_space(3))) void*)(st + j * 1024),
                                        16, 0, 0);
   };
@@ -421,8 +428,8 @@ __global__ __launch_bounds__(64 * (CW + 4)) void gemm_ws2_kernel(GemmArgs a, int
 #pragma unroll
     for (int j = 0; j < T::WLOADS; ++j) {
       const int row = (p * T::WLOADS + j) * 16 + (lane >> 2);
-      base[j] = (const unsigned char*)a.W + (int64_t)kt0 * 64;
-      off[j] = (uint32_t)(((n0 + row % nc) * K + T::pos(row, lane & 3) * 8) * 2);
+      base[j] = (const unsigned char*)a.W + ((int64_t)n0 * K + (int64_t)kt0 * 32) * 2;
+      off[j] = (uint32_t)(((row % nc) * K + T::pos(row, lane & 3) * 8) * 2);
     }
     ws2_produce<T::WLOADS, NSW, T::WSTAGE>(smem + NSA * T::ASTAGE, base, off,
                                            p * T::WLOADS * 1024, nk);
@@ -437,8 +444,8 @@ __global__ __launch_bounds__(64 * (CW + 4)) void gemm_ws2_kernel(GemmArgs a, int
     for (int j = 0; j < T::ALOADS; ++j) {
       const int row = (p * T::ALOADS + j) * 16 + (lane >> 2);
       base[j] = (const unsigned char*)((p * T::ALOADS + j) * 16 < BMT ? a.A : a.A_lo) +
-                (int64_t)kt0 * 64;
-      off[j] = (uint32_t)((min(m0 + row % BMT, M - 1) * K + T::pos(row, lane & 3) * 8) * 2);
+                ((int64_t)m0 * K + (int64_t)kt0 * 32) * 2;
+      off[j] = (uint32_t)(((min(m0 + row % BMT, M - 1) - m0) * K + T::pos(row, lane & 3) * 8) * 2);
     }
     ws2_produce<T::ALOADS, NSA, T::ASTAGE>(smem, base, off, p * T::ALOADS * 1024, nk);
     return;
