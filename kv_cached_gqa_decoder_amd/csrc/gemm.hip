@@ -490,7 +490,8 @@ constexpr int kResidMaxSplits = 8;        // K pieces of the one-stream split pr
 constexpr int kResidNormMaxSplits = 16;   // partials the reduction takes
 __global__ __launch_bounds__(256) void resid_norm_kernel(const float* ws, int splits, int M, int N,
                                                          float* x, bf16_t* u, bf16_t* u_lo,
-                                                         const float* g, float eps) {
+                                                         const float* g, float eps, float* usum,
+                                                         int sum_ld) {
   __shared__ float red[4];
   const int row = blockIdx.x, tid = threadIdx.x;
   const int nch = N / 8;
@@ -540,9 +541,11 @@ __global__ __launch_bounds__(256) void resid_norm_kernel(const float* ws, int sp
   if ((tid & 63) == 0) red[tid >> 6] = ss;
   __syncthreads();
   const float r = rsqrtf((red[0] + red[1] + red[2] + red[3]) / (float)N + eps);
+  float gs[kResidMaxChunks];  // each chunk's sum of its 8 rounded values, in order
 #pragma unroll
   for (int j = 0; j < kResidMaxChunks; ++j) {
     const int c = tid + 256 * j;
+    gs[j] = 0.f;
     if (c >= nch) continue;
     u32x4_t o, ol;
 #pragma unroll
@@ -550,6 +553,8 @@ __global__ __launch_bounds__(256) void resid_norm_kernel(const float* ws, int sp
       const float y0 = v[j][2 * i] * r * gv[j][i >> 1][2 * (i & 1)];
       const float y1 = v[j][2 * i + 1] * r * gv[j][i >> 1][2 * (i & 1) + 1];
       const bf16_t h0 = f32_to_bf16(y0), h1 = f32_to_bf16(y1);
+      gs[j] += bf16_to_f32(h0);
+      gs[j] += bf16_to_f32(h1);
       o[i] = (uint32_t)h0 | ((uint32_t)h1 << 16);
       // the low part: each value's rounding error, itself rounded to bf16
       ol[i] = (uint32_t)f32_to_bf16(y0 - bf16_to_f32(h0)) |
@@ -557,6 +562,19 @@ __global__ __launch_bounds__(256) void resid_norm_kernel(const float* ws, int sp
     }
     *(u32x4_t*)(u + (size_t)row * N + c * 8) = o;
     if (u_lo) *(u32x4_t*)(u_lo + (size_t)row * N + c * 8) = ol;
+  }
+  if (usum == nullptr) return;
+  // the sums of the rounded values per 128-column group (16 chunks on 16 consecutive
+  // lanes: each chunk's 8 values in order, then a fixed tree over the lanes)
+#pragma unroll
+  for (int j = 0; j < kResidMaxChunks; ++j) {
+    const int c = tid + 256 * j;
+    float t = gs[j];
+    t += __shfl_xor(t, 8);
+    t += __shfl_xor(t, 4);
+    t += __shfl_xor(t, 2);
+    t += __shfl_xor(t, 1);
+    if (c < nch && (c & 15) == 0) usum[(size_t)(c >> 4) * sum_ld + row] = t;
   }
 }
 
@@ -660,14 +678,16 @@ struct GemmW4Tile {
   static constexpr int WM = BM / WGM, WN = BN / WGN;
   static constexpr int MT = WM / 16, NT = WN / 16;
   static_assert(WGM * WGN == 4 && MT >= 1 && NT >= 1, "four wavefronts");
-  // a stage: A tile, W codes, and one 1 KiB slot whose first BN * 2 bytes are the
-  // group's scales for the tile's columns
-  static constexpr int ASTAGE = BM * 256, WSTAGE = BN * 64, STAGE = ASTAGE + WSTAGE + 1024;
+  // a stage: A tile, W codes, one 1 KiB slot whose first BN * 2 bytes are the group's
+  // scales for the tile's columns (the scale DMA fills the whole slot), and one 1 KiB
+  // slot whose first BM * 4 bytes are the group's activation sums of the tile's rows
+  static constexpr int ASTAGE = BM * 256, WSTAGE = BN * 64, STAGE = ASTAGE + WSTAGE + 2048;
   static constexpr int ALOADS = BM / 4 / 4, WLOADS = BN / 16 / 4;  // DMA loads per wavefront
   static constexpr int LOADS = ALOADS + WLOADS;  // wavefront 0 adds the scale load
   // one scale DMA (16 bytes per lane) covers the tile's BN columns: lane % (BN / 8)
   // picks a 16-byte piece, repeated across the 1 KiB slot
-  static_assert(BN % 64 == 0 && BN <= 512, "one scale DMA covers the tile's columns");
+  static_assert(BN % 64 == 0 && BN <= 512 && BM == 64,
+                "one scale DMA covers the tile's columns, one 4-byte sum DMA its rows");
   static constexpr int LDS = NS * STAGE;
 };
 
@@ -677,9 +697,12 @@ struct GemmW4Tile {
 // of 128 is (128 + u_k, 128 + u_k+4), so the fragment holds the pairs (k0, k4),
 // (k1, k5), (k2, k6), (k3, k7); the A fragment is permuted to the same order (the
 // product over a K slice does not depend on the order of k). Per group,
-// P = sum_k a (128 + u) and S = sum_k a (one more MFMA against ones) give
-// sum_k a q = P - 136 S, scaled by the column's fp16 scale in fp32.
-template <int EPI, int BM, int BN, int NS, int WGM, int WGN>
+// P = sum_k a (128 + u) and S = sum_k a give sum_k a q = P - 136 S, scaled by the
+// column's fp16 scale in fp32. S is one more MFMA against ones per 16-row tile and
+// 32-wide K slice (a third of the matrix-core work at 64 x 128 tiles, repeated by
+// every wavefront along N), or, with SUMS, read from the per-(group, row) sums that
+// the kernel producing the activations wrote (a_sum).
+template <int EPI, int BM, int BN, int NS, int WGM, int WGN, bool SUMS>
 __global__ __launch_bounds__(256) void gemm_w4_kernel(GemmArgs a, int tiles_m, int tiles,
                                                       int ksteps) {
   using G = GemmW4Tile<BM, BN, NS, WGM, WGN>;
@@ -742,6 +765,12 @@ __global__ __launch_bounds__(256) void gemm_w4_kernel(GemmArgs a, int tiles_m, i
       __builtin_amdgcn_global_load_lds(
           (const void*)(srcS + (size_t)kd * a.N * 2),
           (__attribute__((address_space(3))) void*)(st + G::ASTAGE + G::WSTAGE), 16, 0, 0);
+    // SUMS: the group's activation sums of the tile's BM rows, 4 bytes per lane, into
+    // the sum slot (rows past M read the padded table, never stored)
+    if (SUMS && wave == 1)
+      __builtin_amdgcn_global_load_lds(
+          (const void*)(a.a_sum + (size_t)(kt0 + kd) * a.sum_ld + m0 + lane),
+          (__attribute__((address_space(3))) void*)(st + G::ASTAGE + G::WSTAGE + 1024), 4, 0, 0);
   };
 
   f32x4_t acc[MT][NT];
@@ -768,11 +797,19 @@ __global__ __launch_bounds__(256) void gemm_w4_kernel(GemmArgs a, int tiles_m, i
     for (int ni = 0; ni < NT; ++ni)
       sc[ni] = __half2float(
           *(const __half*)(st + G::ASTAGE + G::WSTAGE + (wn * G::WN + ni * 16 + (lane & 15)) * 2));
-    issue(kt + NS - 1);
     f32x4_t tmp[MT][NT], tsum[MT];
+    if constexpr (SUMS) {
+      // the group's activation sums of the accumulator rows 4 (lane / 16) .. +3 of each
+      // 16-row tile (from the stage)
+#pragma unroll
+      for (int mi = 0; mi < MT; ++mi)
+        tsum[mi] = *(const f32x4_t*)(st + G::ASTAGE + G::WSTAGE + 1024 +
+                                     (wm * G::WM + mi * 16 + 4 * (lane >> 4)) * 4);
+    }
+    issue(kt + NS - 1);
 #pragma unroll
     for (int i = 0; i < MT; ++i) {
-      tsum[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      if constexpr (!SUMS) tsum[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int j = 0; j < NT; ++j) tmp[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     }
@@ -804,7 +841,8 @@ __global__ __launch_bounds__(256) void gemm_w4_kernel(GemmArgs a, int tiles_m, i
 #pragma unroll
         for (int ni = 0; ni < NT; ++ni)
           tmp[mi][ni] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bf[ni], tmp[mi][ni], 0, 0, 0);
-        tsum[mi] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, ones, tsum[mi], 0, 0, 0);
+        if constexpr (!SUMS)
+          tsum[mi] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, ones, tsum[mi], 0, 0, 0);
       }
     }
 #pragma unroll
@@ -820,8 +858,12 @@ static void gemm_w4_go(const GemmArgs& a, int splits, int ksteps, hipStream_t s)
   const int tiles_m = (a.M + BM - 1) / BM;
   const int tiles = tiles_m * (a.N / BN);
   const int per_xcd = (tiles + kXcds - 1) / kXcds;
-  launch_k(gemm_w4_kernel<EPI, BM, BN, NS, WGM, WGN>, dim3(kXcds * per_xcd * splits), dim3(256), 0, s, a,
-           tiles_m, tiles, ksteps);
+  if (a.a_sum)
+    launch_k(gemm_w4_kernel<EPI, BM, BN, NS, WGM, WGN, true>, dim3(kXcds * per_xcd * splits),
+             dim3(256), 0, s, a, tiles_m, tiles, ksteps);
+  else
+    launch_k(gemm_w4_kernel<EPI, BM, BN, NS, WGM, WGN, false>, dim3(kXcds * per_xcd * splits),
+             dim3(256), 0, s, a, tiles_m, tiles, ksteps);
 }
 
 // q/k/v split-K reduction: sums the partials of each RoPE pair (split order) and
@@ -890,6 +932,9 @@ static void gemm_w4_pick(const GemmArgs& a, int splits, int ksteps, hipStream_t 
 }
 static hipError_t gemm_w4(const GemmArgs& a, hipStream_t s) {
   if (a.K % 128 != 0 || a.N % 128 != 0) return hipErrorInvalidValue;
+  // the sum table's rows: every 64-row tile whole (the DMA reads rows past M)
+  if (a.a_sum && (a.sum_ld % 4 != 0 || a.sum_ld < (a.M + 63) / 64 * 64))
+    return hipErrorInvalidValue;
   const int ngk = a.K / 128;
   if (a.epi == EPI_SWIGLU) {
     if (a.glu) gemm_w4_pick<EPI_GEGLU_K>(a, 1, ngk, s);
@@ -911,7 +956,8 @@ static hipError_t gemm_w4(const GemmArgs& a, hipStream_t s) {
   splits = (ngk + ksteps - 1) / ksteps;
   gemm_w4_pick<EPI_PARTIAL>(a, splits, ksteps, s);
   launch_k(resid_norm_kernel, dim3(a.M), dim3(256), 0, s, (const float*)a.ws, splits, a.M, a.N,
-           (float*)a.C, (bf16_t*)a.norm_out, (bf16_t*)a.norm_out_lo, a.norm_g, a.eps);
+           (float*)a.C, (bf16_t*)a.norm_out, (bf16_t*)a.norm_out_lo, a.norm_g, a.eps,
+           a.norm_sum, a.sum_ld);
   return hipGetLastError();
 }
 
@@ -1040,7 +1086,8 @@ static hipError_t gemm_bf16(const GemmArgs& a, hipStream_t s) {
     sp = (steps + ks - 1) / ks;
     if (gemm_ws2_go<EPI_PARTIAL, 8, 6, 6, false>(a, 192, sp, s)) {
       launch_k(resid_norm_kernel, dim3(a.M), dim3(256), 0, s, (const float*)a.ws, sp, a.M, a.N,
-               (float*)a.C, (bf16_t*)a.norm_out, (bf16_t*)a.norm_out_lo, a.norm_g, a.eps);
+               (float*)a.C, (bf16_t*)a.norm_out, (bf16_t*)a.norm_out_lo, a.norm_g, a.eps,
+           a.norm_sum, a.sum_ld);
       return hipGetLastError();
     }
   }
@@ -1050,7 +1097,8 @@ static hipError_t gemm_bf16(const GemmArgs& a, hipStream_t s) {
   else if (lo) gemm_bf16_go<EPI_PARTIAL, 64, 64, 64, 3, 2, 2, true>(a, splits, ksteps, s);
   else gemm_bf16_go<EPI_PARTIAL, 64, 64, 64, 3>(a, splits, ksteps, s);
   launch_k(resid_norm_kernel, dim3(a.M), dim3(256), 0, s, (const float*)a.ws, splits, a.M, a.N,
-           (float*)a.C, (bf16_t*)a.norm_out, (bf16_t*)a.norm_out_lo, a.norm_g, a.eps);
+           (float*)a.C, (bf16_t*)a.norm_out, (bf16_t*)a.norm_out_lo, a.norm_g, a.eps,
+           a.norm_sum, a.sum_ld);
   return hipGetLastError();
 }
 

@@ -95,6 +95,13 @@ struct GemmArgs {
   void* norm_out_lo = nullptr;  // bf16: also the low part of norm_out (see A_lo)
   const float* norm_g = nullptr;
   float eps = 0.f;
+  // INT4 weights: per-(128-column group, row) sums of the bf16 activations, fp32,
+  // [K/128][sum_ld] (a_sum: this product's input, read instead of summing it with
+  // the matrix cores; norm_sum: written with norm_out, for the next projection;
+  // N % 128 == 0)
+  const float* a_sum = nullptr;
+  float* norm_sum = nullptr;
+  int sum_ld = 0;
 };
 
 struct GemvArgs {

@@ -150,6 +150,8 @@ struct vla_model {
   void* u = nullptr;
   void* u_lo = nullptr;         // bf16 weights, logits out: low part of the q/k/v input rows
   void* ao_lo = nullptr;        // ... and of the attention output rows (see GemmArgs)
+  float* usum = nullptr;        // INT4 weights: per-(128-group, row) sums of u (see GemmArgs)
+  int usum_ld = 0;
   void* qbuf = nullptr;
   void* ao = nullptr;
   void* act = nullptr;
@@ -483,6 +485,9 @@ void run_layers(vla_model* m, const KvView& view, int n, int64_t pos0, int cb0, 
       GemmArgs q;
       q.A = m->u;
       q.A_lo = m->u_lo;
+      // INT4: the previous layer's residual reduction wrote u's group sums
+      q.a_sum = l > 0 ? m->usum : nullptr;
+      q.sum_ld = m->usum_ld;
       q.W = m->wqkv[l];
       q.wf = m->wf;
       q.M = n;
@@ -510,6 +515,8 @@ void run_layers(vla_model* m, const KvView& view, int n, int64_t pos0, int cb0, 
       o.ws = m->gemm_ws;
       o.ws_elems = m->gemm_ws_elems;
       o.norm_out = m->u;
+      o.norm_sum = m->usum;
+      o.sum_ld = m->usum_ld;
       o.norm_g = m->norm_ones;
       o.eps = c.rms_eps;
       LAUNCH(m, VLA_K_GEMM_O, st, launch_gemm(o, m->dt, st));
@@ -518,6 +525,8 @@ void run_layers(vla_model* m, const KvView& view, int n, int64_t pos0, int cb0, 
                launch_rmsnorm(m->x, m->norm_ones, m->u, nullptr, n, H, c.rms_eps, m->dt, st));
       GemmArgs gu;
       gu.A = m->u;
+      gu.a_sum = m->usum;
+      gu.sum_ld = m->usum_ld;
       gu.W = m->wgu[l];
       gu.wf = m->wf;
       gu.M = n;
@@ -540,6 +549,8 @@ void run_layers(vla_model* m, const KvView& view, int n, int64_t pos0, int cb0, 
       dn.ws_elems = m->gemm_ws_elems;
       dn.norm_out = l + 1 < c.n_layers ? m->u : nullptr;
       dn.norm_out_lo = l + 1 < c.n_layers ? m->u_lo : nullptr;
+      dn.norm_sum = l + 1 < c.n_layers ? m->usum : nullptr;
+      dn.sum_ld = m->usum_ld;
       dn.norm_g = m->norm_ones;
       dn.eps = c.rms_eps;
       LAUNCH(m, VLA_K_GEMM_DOWN, st, launch_gemm(dn, m->dt, st));
@@ -903,6 +914,12 @@ void build_model(vla_model* m, const vla_config& cfg, const vla_model* borrow,
   if (m->dt == DT_BF16 && m->wf == WF_ACT && c.vocab > 0) {
     m->u_lo = dalloc(m, mc * H * e);
     m->ao_lo = dalloc(m, mc * hq * d * e);
+  }
+  if (m->wf == WF_INT4 && H % 128 == 0) {
+    m->usum_ld = (int)((mc + 63) / 64 * 64);
+    const size_t sb = (size_t)(H / 128) * m->usum_ld * sizeof(float);
+    m->usum = (float*)dalloc(m, sb);
+    HIPCHK(hipMemset(m->usum, 0, sb));  // padded rows stay finite
   }
   m->qbuf = dalloc(m, mc * hq * d * e);
   m->ao = dalloc(m, mc * hq * d * e);
