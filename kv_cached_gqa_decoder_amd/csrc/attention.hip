@@ -674,6 +674,10 @@ hipError_t launch_attention(const AttnArgs& args, int dt, hipStream_t s, int* fo
   // (rows kernel: 12 wavefronts per CU, 3 long-cache workgroups of 4, or 8: 2 short-cache
   // workgroups, 1 long-cache workgroup of 8 at d = 256)
   const int resident = shape == 2 ? (d > 128 ? 256 : 768) : 512;
+  // few row tiles over a short cache: splits of 4 blocks for more workgroups (the
+  // 63-token action chunk over 575 keys: 9 splits instead of 5, expert iteration
+  // 0.916 -> 0.892 ms; 2-block splits 0.908)
+  if (shape == 1 && base * splits < 128) splits = std::max(splits, (a.nlb + 3) / 4);
   splits = std::min(splits, std::max(1, resident / base));
   splits = std::min(splits, keysplit ? kMaxSplitsKey : kMaxSplitsRow);
   static_assert(kMaxSplitsKey <= kMaxSplits && kMaxSplitsRow <= kMaxSplits, "merge capacity");
