@@ -266,24 +266,30 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_kernel(GemmArgs a, i
 // (they share the weight tile through its L2); split launches put the column
 // groups of one (K piece, M tile) on one XCD (they share the activation piece).
 // ---------------------------------------------------------------------------
-template <int NTM, int NSA, int NSW, bool LO = false, int BMT = 256>
+template <int NTM, int NSA, int NSW, bool LO = false, int BMT = 256, int KB = 64>
 struct Ws2Tile {
-  // BMT rows x 32 bf16 of the activations (LO: then the BMT rows of their low part)
+  // a stage holds KB bytes (KB / 2 bf16 of K) of each row: BMT activation rows (LO: then
+  // the BMT rows of their low part) and NTM * 16 weight rows
+  static constexpr int CPR = KB / 16;                // 16-byte chunks per row
+  static constexpr int RPI = 1024 / KB;              // rows one DMA load fills
+  static constexpr int KSTEP = KB / 2;               // K per stage
   static constexpr int AROWS = (LO ? 2 : 1) * BMT;
-  static constexpr int ASTAGE = AROWS * 64;
+  static constexpr int ASTAGE = AROWS * KB;
   static constexpr int WROWS = NTM * 16;
-  static constexpr int WSTAGE = WROWS * 64;          // WROWS x 32 bf16
+  static constexpr int WSTAGE = WROWS * KB;
   static constexpr int ALOADS = ASTAGE / 1024 / 2;   // DMA loads per activation producer
   static constexpr int WLOADS = WSTAGE / 1024 / 2;   // DMA loads per weight producer
   static constexpr int LDS = NSA * ASTAGE + NSW * WSTAGE;
-  static_assert(WSTAGE % 2048 == 0 && ALOADS * (NSA - 2) <= 63 && WLOADS * (NSW - 2) <= 63 &&
-                    LDS <= 160 * 1024,
+  static_assert((KB == 64 || KB == 128) && WSTAGE % 2048 == 0 && ALOADS * (NSA - 2) <= 63 &&
+                    WLOADS * (NSW - 2) <= 63 && LDS <= 160 * 1024,
                 "ring shape");
   static_assert(NTM % 2 == 0 && NTM >= 2 && NTM <= 12 && (BMT == 128 || BMT == 256),
                 "tile counts");
-  // chunk position of K chunk kc (0..3) in LDS row r: 16 rows read at one chunk
-  // column fall in distinct 16-byte bank groups
-  static __device__ __forceinline__ int pos(int r, int kc) { return kc ^ ((r >> 1) & 3); }
+  // chunk position of K chunk kc in LDS row r: 16 rows read at one chunk column fall in
+  // distinct 16-byte bank groups (an involution in kc)
+  static __device__ __forceinline__ int pos(int r, int kc) {
+    return kc ^ ((r >> 1) & (CPR - 1));
+  }
 };
 
 // wait until at most N of this wavefront's vector-memory operations are outstanding
@@ -293,14 +299,14 @@ __device__ __forceinline__ void wait_vmcnt_le() {
   __builtin_amdgcn_s_waitcnt((N & 0xF) | 0x70 | 0xF00 | ((N >> 4) << 14));
 }
 
-// producer wavefront of one ring: rows [row0, row0 + LOADS*16) of each stage; a
-// DMA load fills 1 KiB = 16 rows of 64 bytes, lane i writing chunk position i % 4
-// of row i / 4 with the K chunk that position holds. Load j reads base[j] (uniform,
-// the K piece's first column) + off[j] (the lane's byte offset) + 64 bytes per K
+// producer wavefront of one ring: rows [row0, row0 + LOADS * RPI) of each stage; a
+// DMA load fills 1 KiB = RPI rows of KB bytes, lane i writing chunk position i % CPR
+// of row i / CPR with the K chunk that position holds. Load j reads base[j] (uniform,
+// the K piece's first column) + off[j] (the lane's byte offset) + KB bytes per K
 // step: the address is one scalar base and one 32-bit vector offset, and the LDS
 // destination is uniform, so a load needs no per-lane address arithmetic and no
 // register it shares with the next load
-template <int LOADS, int NS, int STAGE>
+template <int LOADS, int NS, int STAGE, int KB>
 __device__ __forceinline__ void ws2_produce(unsigned char* ring,
                                             const unsigned char* const (&base)[LOADS],
                                             const uint32_t (&off)[LOADS], int lds_off, int nk) {
@@ -309,7 +315,7 @@ __device__ __forceinline__ void ws2_produce(unsigned char* ring,
     const int kd = kt < nk ? kt : nk - 1;  // past the end: the last step again (never read)
 #pragma unroll
     for (int j = 0; j < LOADS; ++j)
-      __builtin_amdgcn_global_load_lds((const void*)(base[j] + kd * 64 + off[j]),
+      __builtin_amdgcn_global_load_lds((const void*)(base[j] + kd * KB + off[j]),
                                        (__attribute__((address_space(3))) void*)(st + j * 1024),
                                        16, 0, 0);
   };
@@ -325,41 +331,45 @@ __device__ __forceinline__ void ws2_produce(unsigned char* ring,
 
 // consumer wavefront c of CW: rows (BMT/CW)c .. of the M tile, NTC 16-column tiles;
 // the gated product, or (EPI_PARTIAL) this K piece's fp32 partial [z][M][N]
-template <int EPI, int NTC, int NTM, int NSA, int NSW, int CW, bool LO, int BMT>
+template <int EPI, int NTC, int NTM, int NSA, int NSW, int CW, bool LO, int BMT, int KB>
 __device__ __forceinline__ void ws2_consume(const GemmArgs& a, const unsigned char* smem, int nk,
                                             int n0, int m0, int c, int lane, int z) {
   static_assert(kGated<EPI> || EPI == EPI_PARTIAL, "gated products or split-K partials");
-  using T = Ws2Tile<NTM, NSA, NSW, LO, BMT>;
+  using T = Ws2Tile<NTM, NSA, NSW, LO, BMT, KB>;
   constexpr int RPW = BMT / CW, MT = RPW / 16;  // rows and 16-row tiles per consumer
   f32x4_t acc[MT][NTC];
 #pragma unroll
   for (int i = 0; i < MT; ++i)
 #pragma unroll
     for (int j = 0; j < NTC; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  const int kc = lane >> 4;
   for (int kt = 0; kt < nk; ++kt) {
     asm volatile("s_barrier" ::: "memory");  // both stages of step kt are in LDS
     const unsigned char* sa = smem + (kt % NSA) * T::ASTAGE;
     const unsigned char* sw = smem + NSA * T::ASTAGE + (kt % NSW) * T::WSTAGE;
-    bf16x8_t bf[NTC];
 #pragma unroll
-    for (int ni = 0; ni < NTC; ++ni) {
-      const int r = ni * 16 + (lane & 15);
-      bf[ni] = *(const bf16x8_t*)(sw + r * 64 + (T::pos(r, kc) << 4));
-    }
+    for (int sub = 0; sub < KB / 64; ++sub) {  // 32-wide K slices of the stage
+      const int kc = sub * 4 + (lane >> 4);
+      bf16x8_t bf[NTC];
 #pragma unroll
-    for (int mi = 0; mi < MT; ++mi) {
-      const int r = RPW * c + 16 * mi + (lane & 15);
-      const bf16x8_t af = *(const bf16x8_t*)(sa + r * 64 + (T::pos(r, kc) << 4));
+      for (int ni = 0; ni < NTC; ++ni) {
+        const int r = ni * 16 + (lane & 15);
+        bf[ni] = *(const bf16x8_t*)(sw + r * KB + (T::pos(r, kc) << 4));
+      }
 #pragma unroll
-      for (int ni = 0; ni < NTC; ++ni)
-        acc[mi][ni] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bf[ni], acc[mi][ni], 0, 0, 0);
-      if constexpr (LO) {
-        const int rl = BMT + r;
-        const bf16x8_t al = *(const bf16x8_t*)(sa + rl * 64 + (T::pos(rl, kc) << 4));
+      for (int mi = 0; mi < MT; ++mi) {
+        const int r = RPW * c + 16 * mi + (lane & 15);
+        const bf16x8_t af = *(const bf16x8_t*)(sa + r * KB + (T::pos(r, kc) << 4));
 #pragma unroll
         for (int ni = 0; ni < NTC; ++ni)
-          acc[mi][ni] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bf[ni], acc[mi][ni], 0, 0, 0);
+          acc[mi][ni] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bf[ni], acc[mi][ni], 0, 0, 0);
+        if constexpr (LO) {
+          const int rl = BMT + r;
+          const bf16x8_t al = *(const bf16x8_t*)(sa + rl * KB + (T::pos(rl, kc) << 4));
+#pragma unroll
+          for (int ni = 0; ni < NTC; ++ni)
+            acc[mi][ni] =
+                __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bf[ni], acc[mi][ni], 0, 0, 0);
+        }
       }
     }
     // this step's LDS reads are complete before the barrier that lets them be refilled
@@ -388,11 +398,11 @@ __device__ __forceinline__ void ws2_consume(const GemmArgs& a, const unsigned ch
   }
 }
 
-template <int EPI, int NTM, int NSA, int NSW, int CW, bool LO, int BMT>
+template <int EPI, int NTM, int NSA, int NSW, int CW, bool LO, int BMT, int KB>
 __global__ __launch_bounds__(64 * (CW + 4)) void gemm_ws2_kernel(GemmArgs a, int units, int groups,
                                                                  int tiles_m, int splits,
                                                                  int ksteps) {
-  using T = Ws2Tile<NTM, NSA, NSW, LO, BMT>;
+  using T = Ws2Tile<NTM, NSA, NSW, LO, BMT, KB>;
   __shared__ __attribute__((aligned(1024))) unsigned char smem[T::LDS];
   const int g8 = (groups + 7) & ~7;
   int mt, g, z;
@@ -418,7 +428,7 @@ __global__ __launch_bounds__(64 * (CW + 4)) void gemm_ws2_kernel(GemmArgs a, int
   const int n0 = u0 * 32, nc = (u1 - u0) * 32;
   const int M = a.M, K = a.K, m0 = mt * BMT;
   const int kt0 = z * ksteps;
-  const int nk = min(K / 32 - kt0, ksteps);  // (the host never makes an empty piece)
+  const int nk = min(K / T::KSTEP - kt0, ksteps);  // (the host never makes an empty piece)
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   if (wave >= CW + 2) {  // weight producers: rows of the group (past its columns: a row inside it)
@@ -427,12 +437,12 @@ __global__ __launch_bounds__(64 * (CW + 4)) void gemm_ws2_kernel(GemmArgs a, int
     uint32_t off[T::WLOADS];
 #pragma unroll
     for (int j = 0; j < T::WLOADS; ++j) {
-      const int row = (p * T::WLOADS + j) * 16 + (lane >> 2);
-      base[j] = (const unsigned char*)a.W + ((int64_t)n0 * K + (int64_t)kt0 * 32) * 2;
-      off[j] = (uint32_t)(((row % nc) * K + T::pos(row, lane & 3) * 8) * 2);
+      const int row = (p * T::WLOADS + j) * T::RPI + lane / T::CPR;
+      base[j] = (const unsigned char*)a.W + ((int64_t)n0 * K + (int64_t)kt0 * T::KSTEP) * 2;
+      off[j] = (uint32_t)(((row % nc) * K + T::pos(row, lane % T::CPR) * 8) * 2);
     }
-    ws2_produce<T::WLOADS, NSW, T::WSTAGE>(smem + NSA * T::ASTAGE, base, off,
-                                           p * T::WLOADS * 1024, nk);
+    ws2_produce<T::WLOADS, NSW, T::WSTAGE, KB>(smem + NSA * T::ASTAGE, base, off,
+                                               p * T::WLOADS * 1024, nk);
     return;
   }
   if (wave >= CW) {  // activation producers: the M tile's rows (past M: row M-1), LO: then
@@ -442,18 +452,19 @@ __global__ __launch_bounds__(64 * (CW + 4)) void gemm_ws2_kernel(GemmArgs a, int
     uint32_t off[T::ALOADS];
 #pragma unroll
     for (int j = 0; j < T::ALOADS; ++j) {
-      const int row = (p * T::ALOADS + j) * 16 + (lane >> 2);
-      base[j] = (const unsigned char*)((p * T::ALOADS + j) * 16 < BMT ? a.A : a.A_lo) +
-                ((int64_t)m0 * K + (int64_t)kt0 * 32) * 2;
-      off[j] = (uint32_t)(((min(m0 + row % BMT, M - 1) - m0) * K + T::pos(row, lane & 3) * 8) * 2);
+      const int row = (p * T::ALOADS + j) * T::RPI + lane / T::CPR;
+      base[j] = (const unsigned char*)((p * T::ALOADS + j) * T::RPI < BMT ? a.A : a.A_lo) +
+                ((int64_t)m0 * K + (int64_t)kt0 * T::KSTEP) * 2;
+      off[j] = (uint32_t)(((min(m0 + row % BMT, M - 1) - m0) * K +
+                           T::pos(row, lane % T::CPR) * 8) * 2);
     }
-    ws2_produce<T::ALOADS, NSA, T::ASTAGE>(smem, base, off, p * T::ALOADS * 1024, nk);
+    ws2_produce<T::ALOADS, NSA, T::ASTAGE, KB>(smem, base, off, p * T::ALOADS * 1024, nk);
     return;
   }
   constexpr int N2 = NTM > 2 ? NTM - 2 : NTM, N4 = NTM > 4 ? NTM - 4 : N2;
   auto consume = [&](auto ntc) {
     constexpr int NTC = decltype(ntc)::value;
-    ws2_consume<EPI, NTC, NTM, NSA, NSW, CW, LO, BMT>(a, smem, nk, n0, m0, wave, lane, z);
+    ws2_consume<EPI, NTC, NTM, NSA, NSW, CW, LO, BMT, KB>(a, smem, nk, n0, m0, wave, lane, z);
   };
   switch (nc / 16) {
     case NTM: consume(std::integral_constant<int, NTM>{}); break;
@@ -464,11 +475,13 @@ __global__ __launch_bounds__(64 * (CW + 4)) void gemm_ws2_kernel(GemmArgs a, int
 
 // about `target` workgroups over (K pieces x M tiles x column groups); a group holds
 // NTM-4 .. NTM 16-column tiles (the consumer's shapes); false if no group count fits
-template <int EPI, int NTM, int NSA, int NSW, bool LO, int BMT = 256, int CW = 4>
-static bool gemm_ws2_go(const GemmArgs& a, int target, int splits, hipStream_t s) {
+template <int EPI, int NTM, int NSA, int NSW, bool LO, int BMT = 256, int CW = 4, int KB = 64>
+static bool gemm_ws2_go(const GemmArgs& a, int target, int splits, hipStream_t s,
+                        int* used_splits = nullptr) {
   const int units = a.N / 32;
   const int tiles_m = (a.M + BMT - 1) / BMT;
-  const int steps = a.K / 32;
+  if (a.K % (KB / 2) != 0) return false;
+  const int steps = a.K / (KB / 2);
   const int ksteps = (steps + splits - 1) / splits;
   splits = (steps + ksteps - 1) / ksteps;
   const int gmin = (units + NTM / 2 - 1) / (NTM / 2);             // at most NTM tiles
@@ -477,7 +490,8 @@ static bool gemm_ws2_go(const GemmArgs& a, int target, int splits, hipStream_t s
   const int groups = std::min(gmax, std::max(gmin, target / (tiles_m * splits)));
   const int grid = splits == 1 ? tiles_m * ((groups + 7) & ~7)
                                : 8 * ((splits * tiles_m + 7) / 8) * groups;
-  launch_k(gemm_ws2_kernel<EPI, NTM, NSA, NSW, CW, LO, BMT>, dim3(grid), dim3(64 * (CW + 4)), 0,
+  if (used_splits) *used_splits = splits;
+  launch_k(gemm_ws2_kernel<EPI, NTM, NSA, NSW, CW, LO, BMT, KB>, dim3(grid), dim3(64 * (CW + 4)), 0,
            s, a, units, groups, tiles_m, splits, ksteps);
   return true;
 }
@@ -996,15 +1010,16 @@ static hipError_t gemm_w4(const GemmArgs& a, hipStream_t s) {
 // less where the doubled activation rows would not fit the LDS
 // the two-stream gated projection: one 256-row M tile with up to 96-column groups and
 // eight consumer wavefronts of 32 rows (two per SIMD: 29.2 us against 29.5 us with four
-// of 64 rows; a consumer on 32 x 32 x 16 instructions, deeper activation or weight rings
-// and K walks staggered per workgroup gave nothing), or with the activations' low part
-// (twice the activation rows) two 128-row M tiles with up to 160-column groups
+// of 64 rows), stages of 64 K (128-byte rows: every DMA request a whole cache line, 29.7
+// -> 24.9 us against stages of 32 K) in 3-stage activation and 4-stage weight rings; or
+// with the activations' low part (twice the activation rows) two 128-row M tiles with up
+// to 160-column groups
 template <int EPI, bool LO>
 static bool ws2_gated(const GemmArgs& a, hipStream_t s) {
   if constexpr (LO)
     return gemm_ws2_go<EPI, 10, 4, 8, true, 128>(a, 256, 1, s);
   else
-    return gemm_ws2_go<EPI, 6, 4, 8, false, 256, 8>(a, 256, 1, s);
+    return gemm_ws2_go<EPI, 6, 3, 4, false, 256, 8, 128>(a, 256, 1, s);
 }
 
 template <int EPI, bool LO>
@@ -1077,14 +1092,15 @@ static hipError_t gemm_bf16(const GemmArgs& a, hipStream_t s) {
   if (a.ws == nullptr || (size_t)a.M * a.N > a.ws_elems) return hipErrorInvalidValue;
   if (a.N % 8 != 0 || a.N / 8 > 256 * kResidMaxChunks) return hipErrorInvalidValue;
   // 129 to 256 rows with a long K (the down projection): the two-stream kernel with
-  // 128-column groups, K in up to 16 pieces
+  // 128-column groups, K in up to 16 pieces, stages of 64 K (128-byte rows: 18.6 ->
+  // 16.5 us against stages of 32 K)
   if (a.M > 128 && a.M <= 256 && ksteps_all >= 64 && a.N % 128 == 0 && !lo) {
     const int steps = a.K / 32;
     int sp = kResidNormMaxSplits;
     while (sp > 1 && (size_t)sp * a.M * a.N > a.ws_elems) --sp;
     const int ks = (steps + sp - 1) / sp;
     sp = (steps + ks - 1) / ks;
-    if (gemm_ws2_go<EPI_PARTIAL, 8, 6, 6, false>(a, 192, sp, s)) {
+    if (gemm_ws2_go<EPI_PARTIAL, 8, 3, 3, false, 256, 4, 128>(a, 192, sp, s, &sp)) {
       launch_k(resid_norm_kernel, dim3(a.M), dim3(256), 0, s, (const float*)a.ws, sp, a.M, a.N,
                (float*)a.C, (bf16_t*)a.norm_out, (bf16_t*)a.norm_out_lo, a.norm_g, a.eps,
            a.norm_sum, a.sum_ld);
