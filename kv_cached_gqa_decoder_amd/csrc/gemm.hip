@@ -989,9 +989,11 @@ static hipError_t gemm_w4(const GemmArgs& a, hipStream_t s) {
 //    rows -> 256 x 128 with 8
 //    wavefronts (4 x 2 grid of 64 x 64 wavefront tiles), 32-deep steps (256 x 17920 x
 //    1536: 34 us against 37 us for 128 x 64 and 39 us for 64 x 64), or 256 x 256 (64 x
-//    128 wavefront tiles, 3-stage ring) when that still makes about 192 workgroups:
-//    the activation tile is re-read once per column tile (512 x 32768 x 2048: 81 us
-//    against 98 us for 256 x 128 and 118 us for 128 x 128);
+//    128 wavefront tiles) when that still makes about 192 workgroups: the activation
+//    tile is re-read once per column tile (512 x 32768 x 2048: 81 us against 98 us for
+//    256 x 128 and 118 us for 128 x 128), in two stages of 64 K (128-byte rows: 77.7 us
+//    against 80.9 us for three of 32 K; 256 x 128 or 128 x 256 in three stages of 64 K:
+//    85.6, 87.8 us); with a low part three stages of 32 K;
 //  residual and q/k/v projections: 64 x 64 tiles, 64-deep steps, 3-stage ring; K is
 //    split into pieces of about 36 steps and into enough splits for about 192
 //    workgroups (at least 4 steps per split, at most 8 splits): 256 x 2048 x 1536
@@ -1030,6 +1032,8 @@ static void gated_go(const GemmArgs& a, hipStream_t s) {
     gemm_bf16_go<EPI, 64, 32, 64, 4, 4, 1, LO>(a, 1, a.K / 64, s);
   else if (a.M > 128 && a.M <= 256 && a.N % 32 == 0 && ws2_gated<EPI, LO>(a, s))
     return;
+  else if (!LO && a.M > 128 && a.N % 256 == 0 && ((a.M + 255) / 256) * (a.N / 256) >= 192)
+    gemm_bf16_go<EPI, 256, 256, 64, 2, 4, 2, false>(a, 1, a.K / 64, s);
   else if (a.M > 128 && a.N % 256 == 0 && ((a.M + 255) / 256) * (a.N / 256) >= 192)
     gemm_bf16_go<EPI, 256, 256, 32, 3, 4, 2, LO>(a, 1, a.K / 32, s);
   else if (a.M > 128 && a.N % 128 == 0)
