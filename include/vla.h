@@ -98,8 +98,9 @@ typedef struct {
 
 typedef struct vla_expert vla_expert;
 
-/* Create a model: validates cfg, allocates weights, KV pool (K and V, each
- * [L][num_blocks][Hkv][block_tokens][d] in act_dtype), the mean-key table
+/* Create a model: validates cfg, allocates weights, KV pool (K as
+ * [L][num_blocks][Hkv][d/c][block_tokens][c] with c = 64 bytes / element size,
+ * V as [L][num_blocks][Hkv][d][block_tokens], both in act_dtype), the mean-key table
  * ([L][max_frames][Hkv*d] fp64) and scratch on the current device, and fills
  * the weights from the seeded splitmix64 -> Box-Muller generator
  * ("Can an LLM Forget the Right Things?", section 6: untrained weights from a

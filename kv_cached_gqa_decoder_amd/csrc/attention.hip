@@ -297,8 +297,10 @@ __global__ __launch_bounds__((RowCfg<D, SHORT>::WAVES * 64)) void attn_rows_kern
       const int which = q / (C::BLK / 1024), part = q % (C::BLK / 1024);
       const int ls = part * 64 + lane;  // 16-byte slot inside the block
       if (which < 2) {
+        // 16-byte piece ls>>4 of key r: 64-byte chunk (ls>>4)/4 holds the block's 16
+        // keys in turn, so one 1 KB piece of the stage is one contiguous chunk
         const int r = swap23((ls & 15) ^ (which << 3));
-        doff[j] = r * (D * 2) + (ls >> 4) * 16;
+        doff[j] = (ls >> 6) * 1024 + r * 64 + ((ls >> 4) & 3) * 16;
       } else {
         const int vr = ls >> 1;
         doff[j] = vr * 32 + (((ls & 1) ^ vhalf_swz(vr)) << 4);
@@ -569,9 +571,9 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(AttnArgs a) {
     const int nt = (b == a.nlb - 1) ? last_ntok : a.blk_ntok[b];
     float v = -INFINITY;
     if (key_visible(a, b, s, nt, t)) {
-      const float* kr = kp + a.g.kidx(a.layer, a.blk_table[b], kvh, s, 0);
+      const int pb = a.blk_table[b];
       float dot = 0.f;
-      for (int j = 0; j < d; ++j) dot += q[j] * kr[j];
+      for (int j = 0; j < d; ++j) dot += q[j] * kp[a.g.kidx(a.layer, pb, kvh, s, j)];
       v = dot * a.scale;
     }
     sc[wave][i] = v;

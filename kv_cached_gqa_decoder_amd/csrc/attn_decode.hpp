@@ -157,12 +157,14 @@ __device__ __forceinline__ void load_pair_global(const AttnArgs& a, PairFrags<D>
   const int bu = __builtin_amdgcn_readfirstlane(b);
   const int pb0 = uniform_ld(a.blk_table, bu);
   const int pb1 = has1 ? uniform_ld(a.blk_table, bu + 1) : pb0;
-  const bf16_t* k0 = kp + a.g.kidx(layer, pb0, kvh, cq, 0) + 8 * jq;
-  const bf16_t* k1 = kp + a.g.kidx(layer, pb1, kvh, cq, 0) + 8 * jq;
+  // dims 32 ds + 8 jq.. of key cq: the 32-dim chunk ds of a block holds its 16 keys
+  // in turn, so each load reads one contiguous 1 KB run
+  const bf16_t* k0 = kp + a.g.kidx(layer, pb0, kvh, cq, 8 * jq);
+  const bf16_t* k1 = kp + a.g.kidx(layer, pb1, kvh, cq, 8 * jq);
 #pragma unroll
   for (int ds = 0; ds < D / 32; ++ds) {
-    f.k0[ds] = __builtin_bit_cast(bf16x8_t, *(const u32x4_t*)(k0 + ds * 32));
-    f.k1[ds] = __builtin_bit_cast(bf16x8_t, *(const u32x4_t*)(k1 + ds * 32));
+    f.k0[ds] = __builtin_bit_cast(bf16x8_t, *(const u32x4_t*)(k0 + ds * 32 * 16));
+    f.k1[ds] = __builtin_bit_cast(bf16x8_t, *(const u32x4_t*)(k1 + ds * 32 * 16));
   }
   const bf16_t* v0 = vp + a.g.vidx(layer, pb0, kvh, 4 * jq, 0);
   const bf16_t* v1 = vp + a.g.vidx(layer, pb1, kvh, 4 * jq, 0);

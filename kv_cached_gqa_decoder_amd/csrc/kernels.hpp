@@ -37,15 +37,20 @@ enum Dtype { DT_F32 = 0, DT_BF16 = 1 };
 //          rows, so one 32-column tile holds both operands of the gated product.
 enum Layout { LAYOUT_PLAIN = 0, LAYOUT_QKV = 1, LAYOUT_GATEUP = 2 };
 
-// Paged KV pool geometry. K element (l, b, h, s, i) lives at
-// (((l*nb + b)*hkv + h)*bt + s)*d + i; V is stored transposed inside a block,
-// element (l, b, h, s, i) at (((l*nb + b)*hkv + h)*d + i)*bt + s, so that a
-// 4-key run of one head dimension is contiguous (the operand order of the
-// P*V matrix-core product).
+// Paged KV pool geometry. Inside a block (l, b, h) K is split along the head
+// dimension into 64-byte chunks of kc = 2^kcs elements, each stored for all bt
+// keys in turn: element (l, b, h, s, i) lives at
+// ((l*nb + b)*hkv + h)*bt*d + (i/kc)*bt*kc + s*kc + i%kc. A matrix-core K operand
+// of 16 keys x 64 bytes is then one contiguous 1 KB run (whole 128-byte lines per
+// load). V is stored transposed inside a block, element (l, b, h, s, i) at
+// (((l*nb + b)*hkv + h)*d + i)*bt + s, so that a 4-key run of one head dimension
+// is contiguous (the operand order of the P*V matrix-core product).
 struct KvGeom {
   int L, nb, hkv, bt, d;
+  int kcs;  // log2 of the K chunk's elements: 4 for fp32, 5 for bf16
   __host__ __device__ size_t kidx(int l, int b, int h, int s, int i) const {
-    return ((((size_t)l * nb + b) * hkv + h) * bt + s) * d + i;
+    return ((((size_t)l * nb + b) * hkv + h) * d + (size_t)((i >> kcs) << kcs)) * bt +
+           ((size_t)s << kcs) + (i & ((1 << kcs) - 1));
   }
   __host__ __device__ size_t vidx(int l, int b, int h, int s, int i) const {
     return ((((size_t)l * nb + b) * hkv + h) * d + i) * bt + s;

@@ -863,7 +863,8 @@ void build_model(vla_model* m, const vla_config& cfg, const vla_model* borrow,
   m->wf = c.wdtype == VLA_INT4_G128 ? WF_INT4 : WF_ACT;
   m->esz = m->dt == DT_F32 ? 4 : 2;
   m->geom = borrow ? borrow->geom
-                   : KvGeom{c.n_layers, c.num_blocks, c.n_kv_heads, c.block_tokens, c.head_dim};
+                   : KvGeom{c.n_layers, c.num_blocks, c.n_kv_heads, c.block_tokens, c.head_dim,
+                            m->esz == 4 ? 4 : 5};
   const size_t H = c.hidden, d = c.head_dim, hq = c.n_heads, hkv = c.n_kv_heads;
   const size_t e = m->esz;
   // projection bytes: activation type, or INT4 codes (half a byte) + one fp16 per 128
