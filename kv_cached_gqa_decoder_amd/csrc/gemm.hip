@@ -283,7 +283,7 @@ struct Ws2Tile {
   static_assert((KB == 64 || KB == 128) && WSTAGE % 2048 == 0 && ALOADS * (NSA - 2) <= 63 &&
                     WLOADS * (NSW - 2) <= 63 && LDS <= 160 * 1024,
                 "ring shape");
-  static_assert(NTM % 2 == 0 && NTM >= 2 && NTM <= 12 && (BMT == 128 || BMT == 256),
+  static_assert(NTM % 2 == 0 && NTM >= 2 && NTM <= 12 && (BMT == 64 || BMT == 128 || BMT == 256),
                 "tile counts");
   // chunk position of K chunk kc in LDS row r: 16 rows read at one chunk column fall in
   // distinct 16-byte bank groups (an involution in kc)
@@ -1026,6 +1026,13 @@ static bool ws2_gated(const GemmArgs& a, hipStream_t s) {
 
 template <int EPI, bool LO>
 static void gated_go(const GemmArgs& a, hipStream_t s) {
+  // up to 64 rows, at least 128 column tiles of 128 (the Qwen-shaped gated projection of
+  // a 64-token chunk): the two-stream kernel with 64-row tiles keeps more weight stages
+  // in flight than the one-stream 64 x 128 tiles (64-token prefill 2.25 -> 2.18 ms); at
+  // 64 tiles (the action expert) it is slower (expert iteration 0.89 -> 0.92 ms)
+  if (!LO && a.M <= 64 && a.N % 128 == 0 && a.N / 128 >= 128 &&
+      gemm_ws2_go<EPI, 6, 3, 4, false, 64, 4, 128>(a, 256, 1, s))
+    return;
   if (a.M <= 64 && a.N % 128 == 0 && a.N / 128 >= 128)
     gemm_bf16_go<EPI, 64, 128, 64, 4, 2, 2, LO>(a, 1, a.K / 64, s);
   else if (a.M <= 64)
@@ -1108,6 +1115,20 @@ static hipError_t gemm_bf16(const GemmArgs& a, hipStream_t s) {
       launch_k(resid_norm_kernel, dim3(a.M), dim3(256), 0, s, (const float*)a.ws, sp, a.M, a.N,
                (float*)a.C, (bf16_t*)a.norm_out, (bf16_t*)a.norm_out_lo, a.norm_g, a.eps,
            a.norm_sum, a.sum_ld);
+      return hipGetLastError();
+    }
+  }
+  // up to 64 rows with K of 8192 or more (the Qwen-shaped down projection of a 64-token
+  // chunk): the two-stream kernel with 64-row tiles, K in pieces of at least 4 stages
+  // (64-token prefill 2.18 -> 2.12 ms); shorter K (the action expert's projections)
+  // stays on the one-stream split tiles, which were faster there
+  if (!lo && a.M <= 64 && ksteps_all >= 128 && a.N % 128 == 0) {
+    int sp = std::min(kResidNormMaxSplits, (a.K / 64) / 4);
+    while (sp > 1 && (size_t)sp * a.M * a.N > a.ws_elems) --sp;
+    if (gemm_ws2_go<EPI_PARTIAL, 8, 3, 4, false, 64, 4, 128>(a, 256, sp, s, &sp)) {
+      launch_k(resid_norm_kernel, dim3(a.M), dim3(256), 0, s, (const float*)a.ws, sp, a.M, a.N,
+               (float*)a.C, (bf16_t*)a.norm_out, (bf16_t*)a.norm_out_lo, a.norm_g, a.eps,
+               a.norm_sum, a.sum_ld);
       return hipGetLastError();
     }
   }

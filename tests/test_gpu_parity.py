@@ -367,6 +367,31 @@ def test_qwen_shape_one_layer_chunk_sizes():
     m.close()
 
 
+def test_qwen_shape_two_layers_64_token_chunks():
+    """Two layers at the Qwen2.5-1.5B shape, 64-token chunks: the gated projection
+    (17,920 columns) and the down projection (K 8,960) of up to 64 rows take the
+    two-stream kernel with 64-row tiles. With two layers every row's FFN output reaches
+    the logits through layer 1's keys and values, so a wrong row of the 64 shows."""
+    p = dict(vla.PRESETS["c2_qwen1p5b_bf16"], n_layers=2, vocab=4096, num_blocks=24,
+             max_frames=4)
+    init_std = 0.02
+    sess = D.Session(oracle_config(p, init_std=init_std))
+    m = _model(p, init_std)
+    ref = None
+    for call, n in enumerate((64, 37)):
+        x32, xs = synth.embeddings(p["seed"], 10 + call, n, p["hidden"], "bf16")
+        m.prefill_chunk(embeds=dev_from_storage(xs, "bf16"), n=n)
+        _, ref = sess.prefill_chunk(embeds=x32)
+        log("qwen-shape 2-layer prefill %d cos %.6f rel %.2e" % ((n,) + metrics(logits_of(m), ref)))
+        check_logits(logits_of(m), ref, "bf16", f"qwen-shape 2-layer prefill {n}")
+    tok = int(np.argmax(ref))
+    g = m.decode_step(tok)
+    _, ref = sess.decode_step(tok)
+    check_logits(logits_of(m), ref, "bf16", "qwen-shape 2-layer decode")
+    check_argmax(g, ref, "bf16", "qwen-shape 2-layer decode")
+    m.close()
+
+
 def test_device_resident_tokens_chain_like_host_tokens():
     """Greedy decoding with the token kept on the device (no host round trip, no
     synchronisation per step) gives bit-identical logits and the same cache as
