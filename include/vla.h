@@ -376,9 +376,10 @@ vla_status vla_probe_mfma_peak(float* out, int32_t blocks, int32_t iters, void* 
 
 /* HBM read probe (a measured streaming ceiling beside the published 8 TB/s): reads a
  * device buffer of `bytes` (allocated, zeroed and freed by the call; a multiple of 16
- * in 1 MiB..64 GiB) `reps` times (1..100) with 16-byte loads, 8 in flight per thread
- * over 2048 workgroups, timed with stream events; writes GB/s. Synchronises. Errors:
- * VLA_E_INVALID, VLA_E_HIP. */
+ * in 1 MiB..64 GiB) `reps` times (1..100) with 16-byte loads, each workgroup reading
+ * consecutive 4 KB pieces, in three grid shapes (512 workgroups x 4 pieces, 1024 x 1,
+ * 1024 x 2 per iteration), each timed with stream events; writes the best GB/s.
+ * Synchronises. Errors: VLA_E_INVALID, VLA_E_HIP. */
 vla_status vla_probe_read_bandwidth(int64_t bytes, int32_t reps, void* stream, double* out_gbs);
 
 /* Action expert of a pi0-style policy ("Running VLAs at Real-time Speed",

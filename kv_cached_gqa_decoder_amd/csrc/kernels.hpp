@@ -220,8 +220,9 @@ hipError_t launch_fill_f32(float* p, float v, int64_t n, hipStream_t s);
 // matrix-core throughput probe: `blocks` workgroups of 4 wavefronts, each wavefront
 // iters x 4 bf16 MFMAs of 32768 FLOP; out[blocks] receives one value per workgroup
 hipError_t launch_mfma_peak(float* out, int blocks, int iters, hipStream_t s);
-// HBM read probe over `bytes` (a multiple of 16) at p; out: blocks * 256 words
-hipError_t launch_read_probe(const void* p, int64_t bytes, uint32_t* out, int blocks,
+// HBM read probe over `bytes` (a multiple of 16) at p, `unroll` (1, 2, 4) consecutive 4 KB
+// pieces per workgroup and iteration; out: blocks * 256 words
+hipError_t launch_read_probe(const void* p, int64_t bytes, uint32_t* out, int blocks, int unroll,
                              hipStream_t s);
 // (cos, sin) of pos * inv_freq[j] for rows t = 0..n-1 at positions pos0 + t: the
 // angle is formed in fp64 and reduced to [-pi, pi] in fp64, then fp32 sin/cos
