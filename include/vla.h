@@ -307,7 +307,9 @@ vla_status vla_weight_out(vla_model* m, int32_t kind, int32_t layer, void* out, 
  *    dim 128, the Qwen2.5-1.5B projection shapes and the tiny test shapes): a fixed
  *    grid of resident workgroups walks the phases of every layer, separated by
  *    device-scope barriers ("Running VLAs at Real-time Speed", sections 3.1 and 5.2:
- *    the step as one unit, and the cost of synchronising many small products).
+ *    the step as one unit, and the cost of synchronising many small products); a
+ *    barrier counts the workgroups of each XCD first and writes each XCD's L2 back
+ *    once, from its last arrival.
  *    0: one launch per projection and attention. While a kernel class is profiled
  *    (vla_profile_enable) the per-kernel launches are used.
  *  VLA_OPT_BARRIER_SPIN_LIMIT (default 1048576): polls of a barrier wait before it
@@ -316,7 +318,7 @@ vla_status vla_weight_out(vla_model* m, int32_t kind, int32_t layer, void* out, 
  *    returns VLA_E_TIMEOUT (a decode step with out_next_token, else the next
  *    vla_logits_out or such decode step); the decode step is then to be rolled back.
  *  VLA_OPT_BARRIER_TEST_UNREACHABLE (default 0; for tests): 1 gives every barrier a
- *    target the arrival counter never reaches, so each wait runs to its spin limit.
+ *    target its generation never reaches, so each wait runs to its spin limit.
  *  VLA_INFO_LAST_DECODE_PERSISTENT (read only): 1 when the last decode step ran the
  *    persistent kernel.
  * Errors: VLA_E_INVALID (unknown key, value out of range, setting a read-only key). */
@@ -329,7 +331,7 @@ enum {
 vla_status vla_set_option(vla_model* m, int32_t key, int64_t value);
 /* The latency of that barrier alone: nbar barriers over `grid` resident workgroups of
  * 256 threads (cooperative launch, one store per thread per phase), timed with stream
- * events; writes microseconds per barrier. Allocates and frees its own buffers;
+ * events after one untimed launch of 10 barriers; writes microseconds per barrier. Allocates and frees its own buffers;
  * synchronises the stream. Errors: VLA_E_INVALID (grid beyond what can be resident,
  * nbar outside 1..100000), VLA_E_TIMEOUT. */
 vla_status vla_probe_barrier(int32_t grid, int32_t nbar, void* stream, double* out_us);

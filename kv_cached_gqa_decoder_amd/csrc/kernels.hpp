@@ -181,25 +181,34 @@ struct DecodeStepArgs {
   int n_layers = 0;
   int ng_qkv = 0, ng_o = 0, ng_gu = 0, ng_dn = 0;   // row groups of each projection
   int vg_qkv = 0, vg_o = 0, vg_gu = 0, vg_dn = 0;   // their virtual workgroups
-  // barriers: a monotonic arrival counter; barrier i of this launch completes when
-  // it reaches base + (i + 1) * gridDim.x. A wait gives up after spin_limit polls
-  // (or when another workgroup gave up), sets *err and ends the workgroup.
+  // barriers (grouped by XCD, decode_step.hip): the state words (kBarStateWords,
+  // zeroed when allocated; the error flag is the first word), the launch's sequence
+  // number (it uses state set seq & 1 and clears the other for the next launch) and
+  // an offset added to every generation target (0; 1 << 40 makes every barrier
+  // unreachable, a test of the error path). A wait gives up after spin_limit polls (or
+  // when another workgroup gave up), sets the error flag and ends the workgroup.
   unsigned long long* bar = nullptr;
-  int* err = nullptr;
-  unsigned long long base = 0;
+  int seq = 0;
+  unsigned long long gen_off = 0;
   int spin_limit = 0;
 };
+// barrier state: 256-byte lines of 32 words; line 0 the error flag, then two sets of
+// 20 lines (2 registration words, 8 XCD arrival counters, the top counter, 8 XCD
+// release flags, the generation)
+constexpr int kBarLineWords = 32;
+constexpr int kBarSetLines = 20;
+constexpr int kBarStateWords = (1 + 2 * kBarSetLines) * kBarLineWords;
 // shapes with a persistent decode-step kernel (chunks per lane of the q/k/v, O and
 // gated projections; rows per wavefront, chunks and K split of the down projection)
 enum DecodeShape { DSHAPE_NONE = -1, DSHAPE_C3_3_3_D1_5_4 = 0, DSHAPE_C1_2_1_D2_1_1 = 1 };
-// barriers of one launch
-inline int decode_step_barriers(int n_layers) { return 5 * n_layers; }
 // persistent workgroups of the shape's kernel (all resident at once), 0 if unknown
 int decode_step_grid(int shape);
 hipError_t launch_decode_step(const DecodeStepArgs& p, int shape, int grid, hipStream_t s);
-// nbar barriers of that kind over `grid` resident workgroups (scratch: grid * 256 floats)
-hipError_t launch_barrier_probe(unsigned long long* bar, int* err, float* scratch, int grid,
-                                int nbar, int spin_limit, hipStream_t s);
+// nbar barriers of that kind over `grid` resident workgroups (bar: kBarStateWords words,
+// zeroed before the first launch; seq: 0, 1, ... over consecutive launches on that
+// state; scratch: grid * 256 floats)
+hipError_t launch_barrier_probe(unsigned long long* bar, float* scratch, int grid, int nbar,
+                                int seq, int spin_limit, hipStream_t s);
 int barrier_probe_max_grid();
 
 // ---- launches (all return the launch status) ----
