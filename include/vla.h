@@ -309,7 +309,8 @@ vla_status vla_weight_out(vla_model* m, int32_t kind, int32_t layer, void* out, 
  *    device-scope barriers ("Running VLAs at Real-time Speed", sections 3.1 and 5.2:
  *    the step as one unit, and the cost of synchronising many small products); a
  *    barrier counts the workgroups of each XCD first and writes each XCD's L2 back
- *    once, from its last arrival.
+ *    once, from its last arrival (a device reporting an XCD id outside 0..7 makes
+ *    the step fail with VLA_E_HIP, reported like a barrier time-out).
  *    0: one launch per projection and attention. While a kernel class is profiled
  *    (vla_profile_enable) the per-kernel launches are used.
  *  VLA_OPT_BARRIER_SPIN_LIMIT (default 1048576): polls of a barrier wait before it
@@ -333,7 +334,7 @@ vla_status vla_set_option(vla_model* m, int32_t key, int64_t value);
  * 256 threads (cooperative launch, one store per thread per phase), timed with stream
  * events after one untimed launch of 10 barriers; writes microseconds per barrier. Allocates and frees its own buffers;
  * synchronises the stream. Errors: VLA_E_INVALID (grid beyond what can be resident,
- * nbar outside 1..100000), VLA_E_TIMEOUT. */
+ * nbar outside 1..100000), VLA_E_TIMEOUT, VLA_E_HIP (an XCD id outside 0..7). */
 vla_status vla_probe_barrier(int32_t grid, int32_t nbar, void* stream, double* out_us);
 vla_status vla_get_option(const vla_model* m, int32_t key, int64_t* value);
 

@@ -57,9 +57,10 @@ __device__ __forceinline__ bool bar_wait(const DecodeStepArgs& p, const u64* w, 
 __device__ __forceinline__ u64* bar_set(const DecodeStepArgs& p, int seq) {
   return p.bar + kBarLineWords * (1 + kBarSetLines * (seq & 1));
 }
-// the XCD this workgroup runs on (hardware register XCC_ID, bits 0..3)
+// the XCD this workgroup runs on (hardware register XCC_ID, bits 0..3; 0..7 on a
+// device of 8 XCDs)
 __device__ __forceinline__ int xcc_id() {
-  return __builtin_amdgcn_s_getreg((3 << 11) | (0 << 6) | 20) & 7;
+  return __builtin_amdgcn_s_getreg((3 << 11) | (0 << 6) | 20) & 15;
 }
 
 // thread 0's barrier state: its XCD, the workgroups on it, the XCDs in use (0 until
@@ -75,6 +76,12 @@ __device__ __forceinline__ void bar_start(const DecodeStepArgs& p, BarState& b) 
     bar_set(p, p.seq + 1)[threadIdx.x * kBarLineWords] = 0ull;
   if (threadIdx.x == 0) {
     b.x = xcc_id();
+    if (b.x > 7) {
+      // more than 8 XCDs: the groups would not match the L2s; error flag 2 (the
+      // first barrier then gives up)
+      __hip_atomic_store((int*)p.bar, 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      b.x = 0;
+    }
     __hip_atomic_fetch_add(bar_set(p, p.seq) + (b.x >> 2) * kBarLineWords,
                            1ull << (16 * (b.x & 3)), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
@@ -131,7 +138,8 @@ __device__ __forceinline__ bool step_barrier(const DecodeStepArgs& p, BarState& 
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
       }
     }
-    if (!ok) __hip_atomic_store((int*)p.bar, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (!ok && !bar_failed(p))
+      __hip_atomic_store((int*)p.bar, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     ok_s = ok;
   }
   __syncthreads();

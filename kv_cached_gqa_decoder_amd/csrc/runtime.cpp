@@ -696,6 +696,7 @@ void check_step_error(vla_model* m, hipStream_t st) {
     HIPCHK(hipMemsetAsync(m->d_bar, 0, kBarStateWords * sizeof(unsigned long long), st));
     HIPCHK(hipStreamSynchronize(st));
     m->ds_seq = 0;
+    if (*h == 2) raise(VLA_E_HIP, "the persistent decode step found an XCD id outside 0..7");
     raise(VLA_E_TIMEOUT, "a barrier wait of the persistent decode step gave up");
   }
 }
@@ -1645,6 +1646,7 @@ vla_status vla_probe_barrier(int32_t grid, int32_t nbar, void* stream, double* o
       HIPCHK(hipEventElapsedTime(&ms, e0, e1));
       int err = 0;
       HIPCHK(hipMemcpy(&err, bar, sizeof(int), hipMemcpyDeviceToHost));
+      if (err == 2) raise(VLA_E_HIP, "the barrier probe found an XCD id outside 0..7");
       if (err) raise(VLA_E_TIMEOUT, "a probe barrier gave up");
       *out_us = (double)ms * 1e3 / nbar;
     } catch (...) {
