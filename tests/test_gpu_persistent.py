@@ -100,3 +100,15 @@ def test_options_are_checked():
     assert b.get_option(vla.VLA_OPT_PERSISTENT_DECODE) == 0
     a.close()
     b.close()
+
+
+def test_read_probe_runs_and_checks_its_arguments():
+    """The streaming-read probe (the measured ceiling that the decode fractions are
+    given against): a positive rate below the published 8 TB/s, and its argument
+    checks (size outside 1 MiB..64 GiB or not a multiple of 16, reps outside 1..100)."""
+    gbs = vla.vla_probe_read_bandwidth(64 << 20, 3)
+    assert 0.0 < gbs < 8000.0
+    for nbytes, reps in (((1 << 20) - 16, 1), ((1 << 20) + 8, 1), (64 << 20, 0), (64 << 20, 101)):
+        with pytest.raises(vla.VlaError) as e:
+            vla.vla_probe_read_bandwidth(nbytes, reps)
+        assert e.value.status == vla.VLA_E_INVALID
