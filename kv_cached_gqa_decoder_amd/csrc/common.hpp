@@ -50,10 +50,46 @@ __device__ __forceinline__ float wave_max(float v) {
   for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
   return v;
 }
+// the two 32-bit halves of a double, and back
+__device__ __forceinline__ void split_d(double x, uint32_t& lo, uint32_t& hi) {
+  const unsigned long long u = __builtin_bit_cast(unsigned long long, x);
+  lo = (uint32_t)u;
+  hi = (uint32_t)(u >> 32);
+}
+__device__ __forceinline__ double join_d(uint32_t lo, uint32_t hi) {
+  return __builtin_bit_cast(double, ((unsigned long long)hi << 32) | lo);
+}
+// v + v of the lane K places away inside its row of 16 (DPP row rotation)
+template <int K>
+__device__ __forceinline__ double row_ror_add(double v) {
+  uint32_t lo, hi;
+  split_d(v, lo, hi);
+  const uint32_t plo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)lo, 0x120 + K, 0xF, 0xF, false);
+  const uint32_t phi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)hi, 0x120 + K, 0xF, 0xF, false);
+  return v + join_d(plo, phi);
+}
+// fp64 sum over the wavefront with no LDS traffic: lanes l ^ 32 and l ^ 16 by the
+// row-swap permutes, then rotations by 8, 4, 2 and 1 inside each row of 16 (after
+// the xor-8 step the values repeat with period 8 in a row, so each rotation pairs
+// the values the xor butterfly would: the same additions, every lane the same sum)
 __device__ __forceinline__ double wave_sum_d(double v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
-  return v;
+  uint32_t lo, hi;
+  split_d(v, lo, hi);
+  {
+    const auto a = __builtin_amdgcn_permlane32_swap(lo, lo, false, false);
+    const auto b = __builtin_amdgcn_permlane32_swap(hi, hi, false, false);
+    v = join_d(a[0], b[0]) + join_d(a[1], b[1]);
+  }
+  split_d(v, lo, hi);
+  {
+    const auto a = __builtin_amdgcn_permlane16_swap(lo, lo, false, false);
+    const auto b = __builtin_amdgcn_permlane16_swap(hi, hi, false, false);
+    v = join_d(a[0], b[0]) + join_d(a[1], b[1]);
+  }
+  v = row_ror_add<8>(v);
+  v = row_ror_add<4>(v);
+  v = row_ror_add<2>(v);
+  return row_ror_add<1>(v);
 }
 
 // wait until at most steps * STEP of this wavefront's vector-memory operations are

@@ -165,22 +165,37 @@ hipError_t launch_meankeys(const void* kpool, KvGeom g, const int* blk_table, co
 // D dims has one fixed shape whatever the workgroup: lane k adds dims k, k+64,
 // ... in order (fma), then a fixed xor tree across the 64 lanes. So s_ij, |a|^2
 // and |b|^2 come out bit-identical in the workgroups of i and of j, and the pair
-// value is the same for both rows. 16 wavefronts per row, 4 rows j in flight per
-// wavefront (independent loads and reductions).
+// value is the same for both rows. 16 wavefronts per row, 8 rows j in flight per
+// wavefront (independent loads and reductions; 128 frames take one batch per
+// wavefront). The frame slots are read with scalar loads (the index is uniform).
 constexpr int kScoreWaves = 16;
-constexpr int kScoreBatch = 4;
+constexpr int kScoreBatch = 8;
 
+// KD > 0: rows of at most 64 * KD dims, every load of a batch issued together (indexes
+// past the row clamped to its last element and masked in the sums); KD = 0: any D
+template <int KD>
 __global__ __launch_bounds__(kScoreWaves * 64) void score_rows_kernel(const double* tab,
                                                                       const int* fr_slot, int F,
                                                                       int D, double* m_out) {
   __shared__ double wmax[kScoreWaves];
   const int i = blockIdx.x;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   // fr_slot null: the table rows are the frames themselves, in order
-  const double* a = tab + (size_t)(fr_slot ? fr_slot[i] : i) * D;
+  const double* a = tab + (size_t)(fr_slot ? mk_uniform_ld(fr_slot, i) : i) * D;
   // |row i|^2 (every wavefront computes it the same way)
   double aa = 0.0;
-  for (int k = lane; k < D; k += 64) aa = fma(a[k], a[k], aa);
+  double av[KD > 0 ? KD : 1];
+  if constexpr (KD > 0) {
+#pragma unroll
+    for (int kk = 0; kk < KD; ++kk) {
+      const int k = lane + 64 * kk;
+      av[kk] = a[k < D ? k : D - 1];
+      av[kk] = k < D ? av[kk] : 0.0;
+      aa = fma(av[kk], av[kk], aa);
+    }
+  } else {
+    for (int k = lane; k < D; k += 64) aa = fma(a[k], a[k], aa);
+  }
   aa = wave_sum_d(aa);
   double best = -INFINITY;
   for (int j0 = wave * kScoreBatch; j0 < F; j0 += kScoreWaves * kScoreBatch) {
@@ -191,16 +206,35 @@ __global__ __launch_bounds__(kScoreWaves * 64) void score_rows_kernel(const doub
       ab[u] = 0.0;
       bb[u] = 0.0;
       const int j = min(j0 + u, F - 1);
-      b[u] = tab + (size_t)(fr_slot ? fr_slot[j] : j) * D;
+      b[u] = tab + (size_t)(fr_slot ? mk_uniform_ld(fr_slot, j) : j) * D;
     }
-#pragma unroll 2
-    for (int k = lane; k < D; k += 64) {
-      const double x = a[k];
+    if constexpr (KD > 0) {
+      double y[kScoreBatch][KD];
 #pragma unroll
-      for (int u = 0; u < kScoreBatch; ++u) {
-        const double y = b[u][k];
-        ab[u] = fma(x, y, ab[u]);
-        bb[u] = fma(y, y, bb[u]);
+      for (int u = 0; u < kScoreBatch; ++u)
+#pragma unroll
+        for (int kk = 0; kk < KD; ++kk) {
+          const int k = lane + 64 * kk;
+          y[u][kk] = b[u][k < D ? k : D - 1];
+        }
+#pragma unroll
+      for (int u = 0; u < kScoreBatch; ++u)
+#pragma unroll
+        for (int kk = 0; kk < KD; ++kk) {
+          const double yv = lane + 64 * kk < D ? y[u][kk] : 0.0;
+          ab[u] = fma(av[kk], yv, ab[u]);
+          bb[u] = fma(yv, yv, bb[u]);
+        }
+    } else {
+#pragma unroll 2
+      for (int k = lane; k < D; k += 64) {
+        const double x = a[k];
+#pragma unroll
+        for (int u = 0; u < kScoreBatch; ++u) {
+          const double yv = b[u][k];
+          ab[u] = fma(x, yv, ab[u]);
+          bb[u] = fma(yv, yv, bb[u]);
+        }
       }
     }
 #pragma unroll
@@ -227,6 +261,16 @@ __global__ __launch_bounds__(kScoreWaves * 64) void score_rows_kernel(const doub
     for (int w = 1; w < kScoreWaves; ++w) mx = wmax[w] > mx ? wmax[w] : mx;
     m_out[i] = mx;
   }
+}
+
+
+// rows of up to 256 dims (the Qwen shape's 2 x 128) take the fully issued batch
+static void launch_score_rows(dim3 grid, hipStream_t s, const double* tab, const int* fr_slot,
+                              int F, int D, double* m_out) {
+  if (D <= 256)
+    launch_k(score_rows_kernel<4>, grid, dim3(kScoreWaves * 64), 0, s, tab, fr_slot, F, D, m_out);
+  else
+    launch_k(score_rows_kernel<0>, grid, dim3(kScoreWaves * 64), 0, s, tab, fr_slot, F, D, m_out);
 }
 
 // argmax over m[0..F), ties to the lowest index: result[0] = index, result[1] =
@@ -305,7 +349,7 @@ hipError_t launch_score_adjacent(const double* table_layer, const int* fr_slot, 
 hipError_t launch_score(const double* table_layer, const int* fr_slot, int nframes, int D,
                         double* m_out, double* result, hipStream_t s) {
   if (nframes < 2) return hipErrorInvalidValue;
-  launch_k(score_rows_kernel, dim3(nframes), dim3(kScoreWaves * 64), 0, s, table_layer, fr_slot,
+  launch_score_rows(dim3(nframes), s, table_layer, fr_slot,
            nframes, D, m_out);
   launch_k(score_argmax_kernel, dim3(1), dim3(256), 0, s, (const double*)m_out, nframes, result,
            (int*)nullptr, (double*)nullptr);
@@ -347,7 +391,7 @@ hipError_t launch_score_noalloc(const double* table, int nframes, int D, int* ou
     }
     ptr = g_scratch_ptr[dev];
   }
-  launch_k(score_rows_kernel, dim3(nframes), dim3(kScoreWaves * 64), 0, s, table,
+  launch_score_rows(dim3(nframes), s, table,
            (const int*)nullptr, nframes, D, ptr);
   launch_k(score_argmax_kernel, dim3(1), dim3(256), 0, s, (const double*)ptr, nframes,
            (double*)nullptr, out_idx, out_score);
