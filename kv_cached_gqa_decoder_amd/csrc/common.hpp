@@ -40,15 +40,35 @@ template <> struct St<bf16_t> {
   static __device__ __forceinline__ void st(bf16_t* p, size_t i, float v) { p[i] = f32_to_bf16(v); }
 };
 
+// the value of the lane K places away inside its row of 16 (DPP row rotation)
+template <int K>
+__device__ __forceinline__ float row_ror(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x120 + K, 0xF, 0xF, false));
+}
+// sum / max over a whole wavefront (every lane active) with no LDS traffic: lanes
+// l ^ 32 and l ^ 16 by the row-swap permutes, then rotations by 8, 4, 2 and 1 inside
+// each row of 16 (after the xor-8 step the values repeat with period 8 in a row, so
+// each rotation pairs the values the xor butterfly would: the same operations,
+// every lane the same result)
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
-  return v;
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(b[0]) + __uint_as_float(b[1]);
+  v += row_ror<8>(v);
+  v += row_ror<4>(v);
+  v += row_ror<2>(v);
+  return v + row_ror<1>(v);
 }
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
-  return v;
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+  v = fmaxf(v, row_ror<8>(v));
+  v = fmaxf(v, row_ror<4>(v));
+  v = fmaxf(v, row_ror<2>(v));
+  return fmaxf(v, row_ror<1>(v));
 }
 // the two 32-bit halves of a double, and back
 __device__ __forceinline__ void split_d(double x, uint32_t& lo, uint32_t& hi) {
@@ -68,7 +88,7 @@ __device__ __forceinline__ double row_ror_add(double v) {
   const uint32_t phi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)hi, 0x120 + K, 0xF, 0xF, false);
   return v + join_d(plo, phi);
 }
-// fp64 sum over the wavefront with no LDS traffic: lanes l ^ 32 and l ^ 16 by the
+// fp64 sum over a whole wavefront (every lane active) with no LDS traffic: lanes l ^ 32 and l ^ 16 by the
 // row-swap permutes, then rotations by 8, 4, 2 and 1 inside each row of 16 (after
 // the xor-8 step the values repeat with period 8 in a row, so each rotation pairs
 // the values the xor butterfly would: the same additions, every lane the same sum)
