@@ -81,14 +81,23 @@ def gateup_bytes():
     return 2 * F * H * 2 + H * 2 + F * 2
 
 
-def file_sha(path):
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+# the sources the decode gate/up GEMV is built from (its own file, the one-shot body,
+# the shared device helpers, the epilogues, the argument structs)
+GEMV_SOURCES = ("gemv.hip", "gemv_body.hpp", "common.hpp", "epilogue.hpp", "kernels.hpp")
+
+
+def file_sha(paths):
+    """First 16 hex digits of the SHA-256 of the files' bytes, concatenated in order."""
+    h = hashlib.sha256()
+    for path in ([paths] if isinstance(paths, str) else paths):
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def read_traffic(kernel_src):
     """HBM traffic per launch of the gate/up GEMV from the committed counter summary,
-    or None when the summary is missing or the kernel source changed since."""
+    or None when the summary is missing or any of its kernel's sources changed since."""
     path = os.path.join(ROOT, "profiles", "gemv_gateup_qwen1p5b_decode_traffic.txt")
     if not os.path.exists(path):
         return None
@@ -232,7 +241,7 @@ def gpu_leg(args):
     fl = prefill_flops()
     dbytes = decode_bytes(CONTEXT + CHUNK + DECODES // 2)
     gu_gbs = gateup_bytes() / (gu_avg * 1e-3) / 1e9
-    kernel_src = os.path.join(ROOT, "kv_cached_gqa_decoder_amd", "csrc", "gemv.hip")
+    kernel_src = [os.path.join(ROOT, "kv_cached_gqa_decoder_amd", "csrc", f) for f in GEMV_SOURCES]
     traffic = read_traffic(kernel_src)
     res = {
         "metric": METRIC,
