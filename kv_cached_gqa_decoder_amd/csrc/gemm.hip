@@ -102,7 +102,9 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& a, f32x4_t (&acc)[
           const int row = m0 + wm * WM + mi * 16 + 4 * (lane >> 4) + e;
           const int col = n0 + wn * WN + ni * 16 + (lane & 15);
           const float v = acc[mi][ni][e];
-          const float partner = __shfl_xor(v, 1, 64);
+          // the neighbouring lane's value (DPP quad permute [1, 0, 3, 2]: no LDS round)
+          const float partner =
+              __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false));
           if (row < M && (col & 1) == 0)
             epi_qkv_store<bf16_t>(a.ctx, row, col, pre[mi][e][ni], v, partner);
         }
@@ -583,11 +585,12 @@ __global__ __launch_bounds__(256) void resid_norm_kernel(const float* ws, int sp
 #pragma unroll
   for (int j = 0; j < kResidMaxChunks; ++j) {
     const int c = tid + 256 * j;
+    // rotations by 8, 4, 2, 1 inside the 16-lane row pair the lanes as an xor tree would
     float t = gs[j];
-    t += __shfl_xor(t, 8);
-    t += __shfl_xor(t, 4);
-    t += __shfl_xor(t, 2);
-    t += __shfl_xor(t, 1);
+    t += row_ror<8>(t);
+    t += row_ror<4>(t);
+    t += row_ror<2>(t);
+    t += row_ror<1>(t);
     if (c < nch && (c & 15) == 0) usum[(size_t)(c >> 4) * sum_ld + row] = t;
   }
 }
